@@ -1,0 +1,405 @@
+"""CPU oracle for rotated INT2 KV-cache quantization with key centering.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, plain reference that the
+GPU path is checked against.  Only the test suite, the package smoke check and
+the benchmark's CPU-baseline leg may import or run it; the product path never
+calls it and shares no code with it.
+
+Sources.  "OptR" below is the page *Output-Oriented Rotation for INT2 KV-Cache
+Quantization* (arXiv 2608.02691):
+
+* §3, Eq. (1)-(2): GQA attention of query head j over KV head h,
+  a_s = <q_j, k_s>/sqrt(d), p = softmax_{s<=t}(a), o_j = sum_s p_s v_s.
+* §3.1, Eq. (4): the rotated INT2 quantizer D_R(z) = Q2(zR; c, G) R^T with an
+  orthogonal R; with Q2 replaced by the identity, D_R(z) = z.
+* §3.2, Eq. (5): attention on the effective (quantized) keys and values.
+* §3.2, Eq. (6)-(8): the exact split of the output error into a key-induced and
+  a value-induced term, Eq. (9)-(10): E_rec and E_out.
+* §1 (and the contributions list): keys are centred before rotation and
+  quantization; this shifts every logit of one query by the same constant, so
+  the softmax is unchanged.
+
+Readings where the page leaves a step open (each is listed with its reason in
+the design notes of the repository):
+
+* Q2 is asymmetric with clip ratio c = 1 and group size G = 32 consecutive
+  rotated channels of one token: scale s = (max - min)/3, zero z = min,
+  code = clamp(round_half_even((x - z)/s), 0, 3), level = z + s*code.
+  The exact fp32/fp16 operation order is fixed in ``int2_quantize``.
+* mu is an input; it is subtracted from keys only and never added back.
+* R^T is applied to the query (as qR) and once to the attention output, which
+  equals dequantize-then-rotate-back per token because R is orthogonal.
+* A sequence of length 0 attends to nothing and its output is zero.
+
+Packed page layout.  The pages fix only that rotation keeps a regular paged
+layout; the byte layout below is this repository's format, stated here in
+full so the oracle can be read without any other file.  One block holds the 16
+token slots of one (page p, KV head h) and starts at byte (p*H_kv + h)*1536:
+
+* bytes [0, 1024): 64 records of 16 bytes.  Record r = 16*a + b
+  (a in 0..3, b in 0..15) is four little-endian uint32 words at byte 16*r:
+  K0, K1, V0, V1.
+  - K code of slot s, channel c: kk = c // 32, a = (c % 32) // 8, e = c % 8;
+    record 16*a + s, word K[kk // 2], bit 2*(4*(kk % 2) + e // 2) + 16*(e % 2).
+  - V code of slot s, channel c: t = c // 16, b = c % 16, a = s // 4,
+    i = s % 4; record 16*a + b, word V[i // 2], bit 2*t + 16*(i % 2).
+  Each code occupies that bit and the one above it (low bit first).
+* bytes [1024, 1536): 16 records of 32 bytes.  Record m = 4*grp + a holds,
+  for the four slots s = 4*a + i (i in 0..3) and channel group grp
+  (channels 32*grp .. 32*grp+31): at byte 1024 + 32*m + 4*i the K pair and at
+  byte 1024 + 32*m + 16 + 4*i the V pair, each pair being the fp16 scale
+  (low two bytes) then the fp16 zero, little-endian.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+HEAD_DIM = 128
+GROUP = 32
+N_GROUPS = HEAD_DIM // GROUP
+PAGE = 16
+BLOCK_BYTES = 1536
+CODE_BYTES = 1024
+
+
+# --------------------------------------------------------------------- checks
+def check_orthogonal(r: np.ndarray, tol: float = 1e-6) -> None:
+    """OptR §3.1: R must be in O(d).  Asserts max|R^T R - I| <= tol."""
+    r64 = np.asarray(r, dtype=np.float64)
+    err = np.abs(r64.T @ r64 - np.eye(r64.shape[0])).max()
+    assert err <= tol, f"rotation is not orthogonal (max |R^T R - I| = {err:.3g})"
+
+
+# ---------------------------------------------- centering and rotation (fp64)
+def centre_keys(k: np.ndarray, mu: np.ndarray) -> np.ndarray:
+    """OptR §1: attention-equivalent key reparameterisation, k - mu (fp64).
+
+    ``k`` is [..., H_kv, d]; ``mu`` is [H_kv, d] and broadcasts over tokens.
+    """
+    return np.asarray(k, np.float64) - np.asarray(mu, np.float64)
+
+
+def rotate(z: np.ndarray, r: np.ndarray) -> np.ndarray:
+    """OptR §3.1, Eq. (4): row vector z maps to zR, per KV head (fp64).
+
+    ``z`` is [n, H_kv, d]; ``r`` is [H_kv, d, d]; out[n, h, j] = sum_i z[n,h,i] R[h,i,j].
+    """
+    z = np.asarray(z, np.float64)
+    r = np.asarray(r, np.float64)
+    return np.einsum("nhi,hij->nhj", z, r)
+
+
+def rotated_inputs(k, v, mu, r_k, r_v):
+    """fp32 inputs of the quantizer: x = fp32((k - mu) R_K), w = fp32(v R_V).
+
+    The products are formed in fp64 and rounded once to fp32 (OptR §1 centres
+    keys only; §3.1 Eq. (4) rotates both K and V).
+    """
+    x = rotate(centre_keys(k, mu), r_k).astype(np.float32)
+    w = rotate(np.asarray(v, np.float64), r_v).astype(np.float32)
+    return x, w
+
+
+# ---------------------------------------------------------- INT2 quantizer Q2
+def int2_quantize(x: np.ndarray):
+    """OptR §3.1: Q2(.; c=1, G=32), asymmetric, on fp32 rows of 128 channels.
+
+    ``x`` is float32 [..., 128].  Groups are 32 consecutive channels.  For each
+    group, with every operation in IEEE fp32 (round to nearest even) unless
+    stated:
+
+      mn, mx = min, max of the group
+      s32 = (mx - mn) / 3
+      s16 = fp16(s32), z16 = fp16(mn)          (round to nearest even)
+      s, z = float(s16), float(z16)
+      if s == 0: every code is 0
+      else code = clamp(round_half_even((x - z) / s), 0, 3)
+
+    Returns (codes uint8 [..., 128], scale float16 [..., 4], zero float16 [..., 4]).
+    Inputs must be finite with group ranges inside the fp16 range.
+    """
+    x = np.asarray(x)
+    assert x.dtype == np.float32 and x.shape[-1] == HEAD_DIM
+    assert np.isfinite(x).all(), "quantizer input must be finite"
+    xg = x.reshape(x.shape[:-1] + (N_GROUPS, GROUP))
+    mn = xg.min(axis=-1)
+    mx = xg.max(axis=-1)
+    rng = (mx - mn).astype(np.float32)
+    s32 = (rng / np.float32(3.0)).astype(np.float32)
+    s16 = s32.astype(np.float16)
+    z16 = mn.astype(np.float16)
+    assert np.isfinite(s16).all() and np.isfinite(z16).all(), "group range exceeds fp16"
+    s = s16.astype(np.float32)[..., None]
+    z = z16.astype(np.float32)[..., None]
+    t = (xg - z).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u = np.where(s > 0, t / np.where(s > 0, s, np.float32(1.0)), np.float32(0.0)).astype(np.float32)
+    codes = np.clip(np.rint(u), 0, 3).astype(np.uint8)
+    return codes.reshape(x.shape), s16, z16
+
+
+def int2_dequantize(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
+    """Level of each code, z + s*code, exact in fp64 (OptR §3.1, four levels per group)."""
+    c = np.asarray(codes, np.float64).reshape(codes.shape[:-1] + (N_GROUPS, GROUP))
+    lv = np.asarray(z16, np.float64)[..., None] + np.asarray(s16, np.float64)[..., None] * c
+    return lv.reshape(codes.shape)
+
+
+# ------------------------------------------------------------ pack / unpack
+def _k_position(slot: int, c: int):
+    kk, a, e = c // 32, (c % 32) // 8, c % 8
+    rec = 16 * a + slot
+    word = kk // 2
+    bit = 2 * (4 * (kk % 2) + e // 2) + 16 * (e % 2)
+    return rec, word, bit
+
+
+def _v_position(slot: int, c: int):
+    t, b, a, i = c // 16, c % 16, slot // 4, slot % 4
+    rec = 16 * a + b
+    word = 2 + i // 2
+    bit = 2 * t + 16 * (i % 2)
+    return rec, word, bit
+
+
+# Position tables [slot, channel] -> (record, word, bit), built by looping the
+# formulas above once.
+_K_POS = np.array([[_k_position(s, c) for c in range(HEAD_DIM)] for s in range(PAGE)], dtype=np.int64)
+_V_POS = np.array([[_v_position(s, c) for c in range(HEAD_DIM)] for s in range(PAGE)], dtype=np.int64)
+
+
+def pack_block(k_codes, k_s16, k_z16, v_codes, v_s16, v_z16, block: np.ndarray | None = None,
+               slots=None) -> np.ndarray:
+    """Write token slots of one (page, KV head) block in the layout above.
+
+    ``k_codes``/``v_codes`` are uint8 [n, 128]; scales/zeros float16 [n, 4];
+    ``slots`` (default 0..n-1, distinct) are the slot indices inside the page.
+    Bits of slots not written are left as they were in ``block``.
+    """
+    blk = np.zeros(BLOCK_BYTES, np.uint8) if block is None else block
+    assert blk.shape == (BLOCK_BYTES,) and blk.dtype == np.uint8
+    n = np.asarray(k_codes).shape[0]
+    slots = np.arange(n) if slots is None else np.asarray(slots, np.int64)
+    assert len(np.unique(slots)) == len(slots)
+    words = blk[:CODE_BYTES].view("<u4").reshape(-1)           # 64 records x 4 words
+    for codes, table in ((k_codes, _K_POS), (v_codes, _V_POS)):
+        pos = table[slots]                                      # [n, 128, (record, word, bit)]
+        idx = (pos[..., 0] * 4 + pos[..., 1]).reshape(-1)
+        bit = pos[..., 2].reshape(-1).astype(np.uint32)
+        val = np.asarray(codes, np.uint32).reshape(-1)
+        np.bitwise_and.at(words, idx, ~(np.uint32(3) << bit))
+        np.bitwise_or.at(words, idx, (val & np.uint32(3)) << bit)
+    meta = blk[CODE_BYTES:].view("<u2").reshape(16, 2, 4, 2)   # [record m][K/V][i][scale/zero]
+    for idx, s in enumerate(slots):
+        a, i = int(s) // 4, int(s) % 4
+        for grp in range(N_GROUPS):
+            m = 4 * grp + a
+            meta[m, 0, i, 0] = np.asarray(k_s16[idx, grp], np.float16).view(np.uint16)
+            meta[m, 0, i, 1] = np.asarray(k_z16[idx, grp], np.float16).view(np.uint16)
+            meta[m, 1, i, 0] = np.asarray(v_s16[idx, grp], np.float16).view(np.uint16)
+            meta[m, 1, i, 1] = np.asarray(v_z16[idx, grp], np.float16).view(np.uint16)
+    return blk
+
+
+def unpack_block(block: np.ndarray):
+    """Inverse of ``pack_block`` for all 16 slots.
+
+    Returns (k_codes, k_s16, k_z16, v_codes, v_s16, v_z16) with codes uint8
+    [16, 128] and scales/zeros float16 [16, 4].
+    """
+    blk = np.asarray(block, np.uint8)
+    assert blk.shape == (BLOCK_BYTES,)
+    words = blk[:CODE_BYTES].view("<u4").reshape(64, 4).astype(np.int64)
+    meta = blk[CODE_BYTES:].view("<u2").reshape(16, 2, 4, 2)
+
+    def gather(pos):
+        rec, word, bit = pos[..., 0], pos[..., 1], pos[..., 2]
+        return ((words[rec, word] >> bit) & 3).astype(np.uint8)
+
+    k_codes, v_codes = gather(_K_POS), gather(_V_POS)
+    k_s16 = np.zeros((PAGE, N_GROUPS), np.float16)
+    k_z16, v_s16, v_z16 = k_s16.copy(), k_s16.copy(), k_s16.copy()
+    for s in range(PAGE):
+        a, i = s // 4, s % 4
+        for grp in range(N_GROUPS):
+            m = 4 * grp + a
+            k_s16[s, grp] = meta[m, 0, i, 0:1].view(np.float16)[0]
+            k_z16[s, grp] = meta[m, 0, i, 1:2].view(np.float16)[0]
+            v_s16[s, grp] = meta[m, 1, i, 0:1].view(np.float16)[0]
+            v_z16[s, grp] = meta[m, 1, i, 1:2].view(np.float16)[0]
+    return k_codes, k_s16, k_z16, v_codes, v_s16, v_z16
+
+
+def pool_bytes(num_pages: int, num_kv_heads: int) -> int:
+    return int(num_pages) * int(num_kv_heads) * BLOCK_BYTES
+
+
+def block_view(pool: np.ndarray, page: int, h: int, num_kv_heads: int) -> np.ndarray:
+    off = (int(page) * num_kv_heads + int(h)) * BLOCK_BYTES
+    return pool[off:off + BLOCK_BYTES]
+
+
+# ------------------------------------------------------------- quantize-append
+def quantize_append(pool: np.ndarray, num_kv_heads: int, slots, x: np.ndarray, w: np.ndarray) -> None:
+    """Quantize rotated fp32 rows and store them at the given cache slots.
+
+    ``x``/``w`` are float32 [n, H_kv, 128] (already centred and rotated);
+    ``slots[n]`` = page*16 + offset, all distinct.  Writes ``pool`` (uint8) in place.
+    """
+    kc, ks, kz = int2_quantize(x)
+    vc, vs, vz = int2_quantize(w)
+    slots = np.asarray(slots, np.int64)
+    assert len(np.unique(slots)) == len(slots), "slots must be distinct"
+    pages = slots // PAGE
+    for page in np.unique(pages):
+        sel = np.nonzero(pages == page)[0]
+        offs = slots[sel] % PAGE
+        for h in range(num_kv_heads):
+            pack_block(kc[sel, h], ks[sel, h], kz[sel, h], vc[sel, h], vs[sel, h], vz[sel, h],
+                       block=block_view(pool, page, h, num_kv_heads), slots=offs)
+
+
+def append_tokens(pool, num_kv_heads, slots, k, v, mu, r_k, r_v) -> None:
+    """Full write path: centre keys, rotate K and V, quantize, pack (OptR §1, §3.1 Eq. (4))."""
+    check_orthogonal_all(r_k)
+    check_orthogonal_all(r_v)
+    x, w = rotated_inputs(k, v, mu, r_k, r_v)
+    quantize_append(pool, num_kv_heads, slots, x, w)
+
+
+def check_orthogonal_all(r: np.ndarray, tol: float = 1e-6) -> None:
+    for h in range(r.shape[0]):
+        check_orthogonal(r[h], tol)
+
+
+# ----------------------------------------------------------- reading the cache
+def gather_sequence(pool, num_kv_heads, table_row, seq_len, h):
+    """Dequantized rotated keys x_hat and values w_hat [T, 128] of one sequence and KV head (fp64)."""
+    T = int(seq_len)
+    if T == 0:
+        return np.zeros((0, HEAD_DIM)), np.zeros((0, HEAD_DIM))
+    n_pages = (T + PAGE - 1) // PAGE
+    xs, ws = [], []
+    for i in range(n_pages):
+        kc, ks, kz, vc, vs, vz = unpack_block(block_view(pool, table_row[i], h, num_kv_heads))
+        xs.append(int2_dequantize(kc, ks, kz))
+        ws.append(int2_dequantize(vc, vs, vz))
+    return np.concatenate(xs)[:T], np.concatenate(ws)[:T]
+
+
+def softmax_attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float) -> np.ndarray:
+    """OptR §3, Eq. (1)-(2) in fp64: softmax_s(<q, k_s> * scale) weighted sum of v_s.
+
+    ``q`` is [d] or [m, d]; keys/values [T, d].  T = 0 gives a zero output.
+    """
+    q = np.asarray(q, np.float64)
+    keys = np.asarray(keys, np.float64)
+    values = np.asarray(values, np.float64)
+    if keys.shape[0] == 0:
+        return np.zeros(q.shape[:-1] + (values.shape[-1],))
+    a = (q @ keys.T) * scale
+    a = a - a.max(axis=-1, keepdims=True)
+    p = np.exp(a)
+    p = p / p.sum(axis=-1, keepdims=True)
+    return p @ values
+
+
+def decode_attention(q, pool, num_kv_heads, page_table, seq_lens, r_k, r_v, sm_scale=None,
+                     heads=None, bypass=None) -> np.ndarray:
+    """Decode attention read from the packed cache (OptR §3.2 Eq. (5), §3.1 Eq. (4)).
+
+    For query head j of sequence b, with h = j // g:
+      q_hat = q_j R_K,h ;  a_s = <q_hat, x_hat_s> * sm_scale for s < T_b
+      p = softmax(a) ;     o_rot = sum_s p_s w_hat_s ;  o_j = o_rot R_V,h^T
+    x_hat, w_hat are the dequantized rotated cache rows.  Since R is
+    orthogonal, <q_hat, x_hat_s> = <q_j, x_hat_s R_K^T>: the key used is
+    D_R(k - mu), and the dropped <q_j, mu> shifts every logit of j equally.
+
+    ``q`` is [B, H_q, 128]; returns fp64 [B, H_q, 128] (only ``heads`` = list
+    of (b, j) pairs are filled when given; others stay zero).  ``bypass`` =
+    (x, w, tok_seq) replaces the packed cache with unquantized rotated rows.
+    """
+    q = np.asarray(q, np.float64)
+    B, Hq, d = q.shape
+    g = Hq // num_kv_heads
+    sm_scale = 1.0 / np.sqrt(d) if sm_scale is None else float(sm_scale)
+    out = np.zeros((B, Hq, d))
+    todo = [(b, j) for b in range(B) for j in range(Hq)] if heads is None else list(heads)
+    cache = {}
+    for b, j in todo:
+        h = j // g
+        if (b, h) not in cache:
+            if bypass is None:
+                cache[(b, h)] = gather_sequence(pool, num_kv_heads, page_table[b], seq_lens[b], h)
+            else:
+                x, w, tok_seq = bypass
+                sel = np.asarray(tok_seq) == b
+                cache[(b, h)] = (np.asarray(x, np.float64)[sel, h][:seq_lens[b]],
+                                 np.asarray(w, np.float64)[sel, h][:seq_lens[b]])
+        xh, wh = cache[(b, h)]
+        q_hat = q[b, j] @ np.asarray(r_k[h], np.float64)
+        o_rot = softmax_attention(q_hat, xh, wh, sm_scale)
+        out[b, j] = o_rot @ np.asarray(r_v[h], np.float64).T
+    return out
+
+
+# ------------------------------------------------------ split-K form (partials)
+def split_partials(q_hat: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float, bounds):
+    """Per-split softmax partials (m, l, acc) over token ranges ``bounds`` (fp64).
+
+    m = max logit of the split, l = sum exp(a - m), acc = sum exp(a - m) v.
+    An empty split has m = -inf, l = 0, acc = 0.
+    """
+    parts = []
+    for lo, hi in bounds:
+        if hi <= lo:
+            parts.append((-np.inf, 0.0, np.zeros(values.shape[-1])))
+            continue
+        a = (keys[lo:hi] @ q_hat) * scale
+        m = a.max()
+        e = np.exp(a - m)
+        parts.append((m, e.sum(), e @ values[lo:hi]))
+    return parts
+
+
+def merge_partials(parts) -> np.ndarray:
+    """Log-sum-exp merge of split partials into the normalised output (fp64)."""
+    ms = np.array([p[0] for p in parts])
+    if len(ms) == 0 or not np.isfinite(ms).any():
+        return np.zeros_like(parts[0][2]) if parts else np.zeros(HEAD_DIM)
+    m = ms[np.isfinite(ms)].max()
+    wts = np.where(np.isfinite(ms), np.exp(np.where(np.isfinite(ms), ms, 0.0) - m), 0.0)
+    l_tot = sum(w * p[1] for w, p in zip(wts, parts))
+    acc = sum(w * p[2] for w, p in zip(wts, parts))
+    return acc / l_tot
+
+
+# ------------------------------------------------- output-error decomposition
+def output_error_terms(q, keys, values, keys_q, values_q, w_o, scale=None):
+    """OptR §3.2 Eq. (6)-(10) for one query row (fp64).
+
+    Returns (dy, dy_k, dy_v, e_rec, e_out) with
+      dy   = y_tilde - y
+      dy_k = (sum_s (p_tilde_s - p_s) v_s) W_O^T      (key-induced)
+      dy_v = (sum_s p_tilde_s (v_tilde_s - v_s)) W_O^T  (value-induced)
+      e_rec = ||K - K_tilde||_F^2 + ||V - V_tilde||_F^2,  e_out = ||dy||^2.
+    """
+    q = np.asarray(q, np.float64)
+    d = q.shape[-1]
+    scale = 1.0 / np.sqrt(d) if scale is None else scale
+
+    def probs(kk):
+        a = (np.asarray(kk, np.float64) @ q) * scale
+        a = a - a.max()
+        e = np.exp(a)
+        return e / e.sum()
+
+    p, pt = probs(keys), probs(keys_q)
+    w_o = np.asarray(w_o, np.float64)
+    y = (p @ values) @ w_o.T
+    yt = (pt @ values_q) @ w_o.T
+    dy_k = ((pt - p) @ values) @ w_o.T
+    dy_v = (pt @ (np.asarray(values_q, np.float64) - values)) @ w_o.T
+    e_rec = float(((keys - keys_q) ** 2).sum() + ((values - values_q) ** 2).sum())
+    return yt - y, dy_k, dy_v, e_rec, float(((yt - y) ** 2).sum())

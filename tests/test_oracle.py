@@ -1,0 +1,409 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Every test here runs on the CPU.  None re-types the oracle's own formula: each
+checks a hand-derived worked example, a closed form, an invariant or a brute
+force search.
+"""
+
+import os
+
+import numpy as np
+import pytest
+
+import kvq_inputs as I
+from oracle import kvq_oracle as O
+
+
+# ------------------------------------------------------------------ helpers
+def _parse_runs(tokens, dtype):
+    out = []
+    for t in tokens:
+        if "*" in t:
+            val, cnt = t.split("*")
+            out += [dtype(val)] * int(cnt)
+        else:
+            out.append(dtype(t))
+    return out
+
+
+def _load_groups(golden_dir):
+    cases = {}
+    with open(os.path.join(golden_dir, "int2_groups.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, field, *rest = line.split()
+            c = cases.setdefault(name, {})
+            if field == "values":
+                c[field] = np.array(_parse_runs(rest, float), dtype=np.float32)
+            elif field == "codes":
+                c[field] = np.array(_parse_runs(rest, int), dtype=np.uint8)
+            else:
+                c[field] = float(rest[0])
+    return cases
+
+
+def _random_rows(rng, n, scale=1.0, offset=0.0):
+    return (rng.standard_normal((n, 128)) * scale + offset).astype(np.float32)
+
+
+# ---------------------------------------------------- Q2: worked examples
+def test_quantizer_golden_groups(golden_dir):
+    """OptR §3.1 Q2: hand-derived groups (ties to even, fp16 scale use, constant group)."""
+    cases = _load_groups(golden_dir)
+    assert set(cases) == {"A", "B", "C", "D"}
+    for name, c in cases.items():
+        assert c["values"].shape == (32,) and c["codes"].shape == (32,)
+        row = np.tile(c["values"], 4)[None, :]          # same group in all 4 positions
+        codes, s16, z16 = O.int2_quantize(row)
+        for grp in range(4):
+            assert float(s16[0, grp]) == c["scale"], (name, grp)
+            assert float(z16[0, grp]) == c["zero"], (name, grp)
+            np.testing.assert_array_equal(codes[0, 32 * grp:32 * grp + 32], c["codes"], err_msg=name)
+
+
+def test_quantizer_golden_groups_independent_positions(golden_dir):
+    """Each of the 4 groups of a row is quantized on its own (no cross-group leakage)."""
+    cases = _load_groups(golden_dir)
+    order = ["A", "B", "C", "D"]
+    row = np.concatenate([cases[n]["values"] for n in order])[None, :]
+    codes, s16, z16 = O.int2_quantize(row)
+    for grp, n in enumerate(order):
+        np.testing.assert_array_equal(codes[0, 32 * grp:32 * grp + 32], cases[n]["codes"])
+        assert float(s16[0, grp]) == cases[n]["scale"]
+        assert float(z16[0, grp]) == cases[n]["zero"]
+
+
+# ---------------------------------------------------- Q2: properties
+def test_quantizer_at_most_four_levels_and_nearest():
+    """OptR §1: only four INT2 levels per group; each code picks the nearest level.
+
+    Brute force over the four candidate levels in fp64.  Ties and fp32 rounding
+    of u allow a slack of a few fp32 ulps of the group's scale.
+    """
+    rng = np.random.default_rng(11)
+    x = np.concatenate([_random_rows(rng, 200), _random_rows(rng, 50, 20.0, 3.0),
+                        _random_rows(rng, 50, 1e-3, -2.0)])
+    codes, s16, z16 = O.int2_quantize(x)
+    lv = O.int2_dequantize(codes, s16, z16)
+    for n in range(x.shape[0]):
+        for grp in range(4):
+            sl = slice(32 * grp, 32 * grp + 32)
+            assert len(np.unique(lv[n, sl])) <= 4
+            s, z = float(s16[n, grp]), float(z16[n, grp])
+            cand = z + s * np.arange(4.0)
+            dist = np.abs(x[n, sl].astype(np.float64)[:, None] - cand[None, :])
+            chosen = dist[np.arange(32), codes[n, sl]]
+            assert np.all(chosen <= dist.min(axis=1) + 4 * np.spacing(np.float32(max(s, 1e-30))) + 1e-12)
+
+
+def test_quantizer_extremes_and_error_bound():
+    """Min element gets code 0, max gets 3; |x - level| <= s/2 (+ fp16 rounding of z and s)."""
+    rng = np.random.default_rng(12)
+    x = _random_rows(rng, 300, 4.0, 1.0)
+    codes, s16, z16 = O.int2_quantize(x)
+    xg = x.reshape(-1, 4, 32)
+    cg = codes.reshape(-1, 4, 32)
+    rows = np.arange(xg.shape[0])[:, None]
+    grps = np.arange(4)[None, :]
+    assert np.all(cg[rows, grps, xg.argmin(-1)] == 0)
+    assert np.all(cg[rows, grps, xg.argmax(-1)] == 3)
+    lv = O.int2_dequantize(codes, s16, z16).reshape(-1, 4, 32)
+    s = s16.astype(np.float64)
+    rng_true = (xg.max(-1) - xg.min(-1)).astype(np.float64)
+    # stored scale/zero differ from the exact ones by at most half an fp16 ulp (relative 2^-11)
+    slack = 2.0 ** -10 * (np.abs(z16.astype(np.float64)) + rng_true)
+    assert np.all(np.abs(xg - lv).max(-1) <= s / 2 + slack + 1e-7)
+
+
+def test_quantizer_arithmetic_progression_is_exact():
+    """A group already on an fp16-exact grid z + s*{0,1,2,3} reconstructs with zero error."""
+    rng = np.random.default_rng(13)
+    for _ in range(50):
+        z = float(np.float16(rng.uniform(-8, 8)))
+        s = float(2.0 ** rng.integers(-6, 3))
+        lvls = z + s * rng.integers(0, 4, size=(4, 32)).astype(np.float64)
+        lvls[:, 0], lvls[:, 1] = z, z + 3 * s                   # make min and max present
+        x = lvls.reshape(1, 128).astype(np.float32)
+        codes, s16, z16 = O.int2_quantize(x)
+        np.testing.assert_array_equal(O.int2_dequantize(codes, s16, z16), x.astype(np.float64))
+
+
+def test_quantizer_constant_and_degenerate_groups():
+    x = np.full((3, 128), 0.0, np.float32)
+    x[1] = -3.5
+    x[2, :32] = 1e-9                                           # range underflows fp16 scale
+    x[2, 1] = 2e-9
+    codes, s16, z16 = O.int2_quantize(x)
+    assert not codes.any()
+    assert float(z16[1, 0]) == -3.5
+    assert float(s16[2, 0]) == 0.0
+
+
+# ---------------------------------------------------- pack / unpack
+def test_block_layout_golden(golden_dir):
+    """Hand-derived byte positions of single codes and metadata in a block."""
+    with open(os.path.join(golden_dir, "block_layout.txt")) as f:
+        lines = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    z = np.zeros((1, 128), np.uint8)
+    zf = np.zeros((1, 4), np.float16)
+    n_checked = 0
+    for parts in lines:
+        if parts[0] in ("K", "V"):
+            tensor, slot, ch, code, byte, val = parts[0], *map(int, parts[1:])
+            kc, vc = z.copy(), z.copy()
+            (kc if tensor == "K" else vc)[0, ch] = code
+            blk = O.pack_block(kc, zf, zf, vc, zf, zf, slots=[slot])
+            nz = np.nonzero(blk)[0]
+            assert list(nz) == [byte] and blk[byte] == val, parts
+            n_checked += 1
+        elif parts[0] == "META":
+            tensor, slot, grp, byte = parts[1], int(parts[2]), int(parts[3]), int(parts[4])
+            sc = np.zeros((1, 4), np.float16)
+            zc = np.zeros((1, 4), np.float16)
+            sc[0, grp], zc[0, grp] = 1.5, -2.0                 # 0x3E00, 0xC000
+            args = (z, sc, zc, z, zf, zf) if tensor == "K" else (z, zf, zf, z, sc, zc)
+            blk = O.pack_block(*args, slots=[slot])
+            assert list(np.nonzero(blk)[0]) == [byte + 1, byte + 3], parts
+            assert blk[byte + 1] == 0x3E and blk[byte + 3] == 0xC0
+            n_checked += 1
+    assert n_checked == 10
+
+
+def test_pack_unpack_roundtrip_and_partial_writes():
+    rng = np.random.default_rng(14)
+    kc = rng.integers(0, 4, (16, 128)).astype(np.uint8)
+    vc = rng.integers(0, 4, (16, 128)).astype(np.uint8)
+    f = lambda: rng.standard_normal((16, 4)).astype(np.float16)
+    ks, kz, vs, vz = f(), f(), f(), f()
+    full = O.pack_block(kc, ks, kz, vc, vs, vz)
+    got = O.unpack_block(full)
+    for a, b in zip(got, (kc, ks, kz, vc, vs, vz)):
+        np.testing.assert_array_equal(a.view(np.uint8) if a.dtype == np.float16 else a,
+                                      b.view(np.uint8) if b.dtype == np.float16 else b)
+    # slot-by-slot writes in a scrambled order onto a dirty block give the same bytes
+    blk = rng.integers(0, 256, O.BLOCK_BYTES).astype(np.uint8)
+    for s in rng.permutation(16):
+        O.pack_block(kc[s:s + 1], ks[s:s + 1], kz[s:s + 1], vc[s:s + 1], vs[s:s + 1], vz[s:s + 1],
+                     block=blk, slots=[s])
+    np.testing.assert_array_equal(blk, full)
+
+
+def test_storage_arithmetic():
+    """OptR §1: INT2 codes take 1/8 of BF16 storage; with fp16 scale+zero per 32 the
+    block is 96 bytes per token per KV head (3 bits per element)."""
+    assert O.CODE_BYTES // 16 // 2 == 128 * 2 // 8            # K (or V) codes per token = bf16 bytes / 8
+    assert O.BLOCK_BYTES // 16 == 96
+    assert O.BLOCK_BYTES * 8 / (16 * 2 * 128) == 3.0
+
+
+# ---------------------------------------------------- attention pins
+def _brute_attention(q, keys, values, scale):
+    """Eq. (1)-(2) with explicit loops."""
+    T = len(keys)
+    a = [sum(float(q[c]) * float(keys[s][c]) for c in range(len(q))) * scale for s in range(T)]
+    m = max(a)
+    e = [np.exp(x - m) for x in a]
+    tot = sum(e)
+    return np.array([sum(e[s] / tot * float(values[s][c]) for s in range(T)) for c in range(values.shape[1])])
+
+
+def test_softmax_attention_matches_brute_force():
+    rng = np.random.default_rng(15)
+    for T in (1, 2, 7, 33):
+        q = rng.standard_normal(16)
+        k = rng.standard_normal((T, 16)) * 3
+        v = rng.standard_normal((T, 16))
+        np.testing.assert_allclose(O.softmax_attention(q, k, v, 0.25), _brute_attention(q, k, v, 0.25),
+                                   rtol=0, atol=1e-13)
+
+
+def test_split_merge_equals_one_pass():
+    rng = np.random.default_rng(16)
+    T = 37
+    q = rng.standard_normal(128)
+    k = rng.standard_normal((T, 128)) * 2
+    v = rng.standard_normal((T, 128))
+    ref = O.softmax_attention(q, k, v, 1 / np.sqrt(128))
+    for n_split in range(1, T + 1):
+        edges = np.linspace(0, T, n_split + 1).round().astype(int)
+        parts = O.split_partials(q, k, v, 1 / np.sqrt(128), list(zip(edges[:-1], edges[1:])))
+        np.testing.assert_allclose(O.merge_partials(parts), ref, rtol=0, atol=1e-13)
+    # empty splits are neutral
+    parts = O.split_partials(q, k, v, 1 / np.sqrt(128), [(0, 0), (0, T), (T, T)])
+    np.testing.assert_allclose(O.merge_partials(parts), ref, rtol=0, atol=1e-13)
+
+
+def test_key_centering_shift_invariance_fp64():
+    """OptR §1: centering shifts every logit of a query by one constant; softmax unchanged."""
+    rng = np.random.default_rng(17)
+    for _ in range(20):
+        q = rng.standard_normal(128)
+        k = rng.standard_normal((64, 128)) + rng.standard_normal(128) * 3
+        mu = k.mean(axis=0)
+        a = k @ q / np.sqrt(128)
+        ac = (k - mu) @ q / np.sqrt(128)
+        shift = ac - a
+        assert np.ptp(shift) <= 1e-12 * max(1.0, np.abs(a).max())
+        pa = np.exp(a - a.max()); pa /= pa.sum()
+        pc = np.exp(ac - ac.max()); pc /= pc.sum()
+        assert np.abs(pa - pc).max() <= 1e-14
+
+
+def _tiny(seed=1, **kw):
+    return I.make_case("t", seed, B=kw.pop("B", 1), Hq=kw.pop("Hq", 4), Hkv=kw.pop("Hkv", 1),
+                       seq_lens=kw.pop("seq_lens", [64]), dtype=kw.pop("dtype", "f32"), n_outliers=4,
+                       mu_tokens=kw.pop("mu_tokens", 64), table_policy=kw.pop("table_policy", "contiguous"),
+                       **kw)
+
+
+def _fp64_orthogonal(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        qm, rm = np.linalg.qr(rng.standard_normal((128, 128)))
+        out.append(qm * np.sign(np.diag(rm))[None, :])
+    return np.stack(out)
+
+
+def test_bypass_equals_plain_attention_any_rotation_and_mu():
+    """OptR §3.1 Eq. (4): with Q2 = identity, D_R(z) = z for orthogonal R, so the rotated,
+    centred path (q R_K against (k - mu) R_K, output mapped back by R_V^T) equals plain
+    Eq. (1)-(2) attention on the raw k, v.  The rotations are fp64-orthogonal so the
+    identity holds to fp64 rounding."""
+    c = _tiny(B=2, Hq=8, Hkv=2, seq_lens=[40, 23])
+    c.r_k, c.r_v = _fp64_orthogonal(101, 2), _fp64_orthogonal(102, 2)
+    x = O.rotate(O.centre_keys(c.k, c.mu), c.r_k)
+    w = O.rotate(c.v, c.r_v)
+    got = O.decode_attention(c.q, None, c.Hkv, c.page_table, c.seq_lens, c.r_k, c.r_v,
+                             bypass=(x, w, c.tok_seq))
+    for b in range(c.B):
+        kb = c.k[c.tok_seq == b].astype(np.float64)
+        vb = c.v[c.tok_seq == b].astype(np.float64)
+        for j in range(c.Hq):
+            ref = O.softmax_attention(c.q[b, j].astype(np.float64), kb[:, j // 4], vb[:, j // 4], 1 / np.sqrt(128))
+            np.testing.assert_allclose(got[b, j], ref, rtol=0, atol=1e-12)
+    # the rotations must be non-trivial for the test to mean anything
+    assert np.abs(c.r_k[0] - c.r_k[0].T).max() > 0.1 and np.abs(c.r_k[0] - np.eye(128)).max() > 0.1
+
+
+def test_orthogonal_rotation_preserves_norms_and_products():
+    c = _tiny()
+    O.check_orthogonal(c.r_k[0])
+    z = c.k[:, 0].astype(np.float64)
+    zr = O.rotate(c.k, c.r_k)[:, 0]
+    np.testing.assert_allclose(np.linalg.norm(zr, axis=1), np.linalg.norm(z, axis=1), rtol=1e-6)
+    with pytest.raises(AssertionError):
+        O.check_orthogonal(c.r_k[0] * 1.001)
+
+
+def test_identity_rotation_zero_mu_equals_direct_int2():
+    """R = I and mu = 0: the quantized cache equals INT2 applied directly to raw k and v (bit-exact)."""
+    c = _tiny(identity_rotation=True, mu_zero=True)
+    pool = np.zeros(O.pool_bytes(c.num_pages, c.Hkv), np.uint8)
+    O.append_tokens(pool, c.Hkv, c.slots, c.k, c.v, c.mu, c.r_k, c.r_v)
+    dk = O.int2_quantize(c.k.astype(np.float32))
+    dv = O.int2_quantize(c.v.astype(np.float32))
+    for n in range(c.n_tokens):
+        page, off = divmod(int(c.slots[n]), 16)
+        kc, ks, kz, vc, vs, vz = O.unpack_block(O.block_view(pool, page, 0, 1))
+        np.testing.assert_array_equal(kc[off], dk[0][n, 0])
+        np.testing.assert_array_equal(vc[off], dv[0][n, 0])
+        np.testing.assert_array_equal(ks[off], dk[1][n, 0])
+        np.testing.assert_array_equal(vz[off], dv[2][n, 0])
+
+
+def test_decode_from_pool_equals_attention_on_effective_kv():
+    """OptR §3.2 Eq. (5): decode over the packed cache equals Eq. (1)-(2) attention on the
+    effective keys k~ = Q2((k - mu) R_K) R_K^T + mu and values v~ = Q2(v R_V) R_V^T."""
+    c = _tiny(B=2, Hq=8, Hkv=2, seq_lens=[50, 33], table_policy="permuted")
+    pool = np.zeros(O.pool_bytes(c.num_pages, c.Hkv), np.uint8)
+    O.append_tokens(pool, c.Hkv, c.slots, c.k, c.v, c.mu, c.r_k, c.r_v)
+    got = O.decode_attention(c.q, pool, c.Hkv, c.page_table, c.seq_lens, c.r_k, c.r_v)
+    x, w = O.rotated_inputs(c.k, c.v, c.mu, c.r_k, c.r_v)
+    kq = O.int2_dequantize(*O.int2_quantize(x))
+    vq = O.int2_dequantize(*O.int2_quantize(w))
+    for b in range(c.B):
+        sel = c.tok_seq == b
+        for j in range(c.Hq):
+            h = j // 4
+            k_eff = kq[sel, h] @ c.r_k[h].astype(np.float64).T + c.mu[h]
+            v_eff = vq[sel, h] @ c.r_v[h].astype(np.float64).T
+            ref = O.softmax_attention(c.q[b, j], k_eff, v_eff, 1 / np.sqrt(128))
+            np.testing.assert_allclose(got[b, j], ref, rtol=0, atol=1e-11)
+
+
+def test_page_permutation_and_batch_independence():
+    """The result depends only on the tokens of each sequence, not on where pages live."""
+    base = dict(B=2, Hq=4, Hkv=1, seq_lens=[45, 70])
+    a = _tiny(table_policy="contiguous", **base)
+    b = _tiny(table_policy="interleaved", **base)
+    assert not np.array_equal(a.page_table, b.page_table)
+    outs = []
+    for c in (a, b):
+        pool = np.zeros(O.pool_bytes(c.num_pages, c.Hkv), np.uint8)
+        O.append_tokens(pool, c.Hkv, c.slots, c.k, c.v, c.mu, c.r_k, c.r_v)
+        outs.append(O.decode_attention(c.q, pool, c.Hkv, c.page_table, c.seq_lens, c.r_k, c.r_v))
+    np.testing.assert_array_equal(outs[0], outs[1])
+    # sequence 1 alone, in a pool of its own, gives the same output
+    c = a
+    sel = c.tok_seq == 1
+    table, npg = I.page_table_contiguous(np.array([70]))
+    pool = np.zeros(O.pool_bytes(npg, 1), np.uint8)
+    O.append_tokens(pool, 1, I.slots_for_positions(table, np.zeros(70, int), np.arange(70)),
+                    c.k[sel], c.v[sel], c.mu, c.r_k, c.r_v)
+    alone = O.decode_attention(c.q[1:2], pool, 1, table, np.array([70]), c.r_k, c.r_v)
+    np.testing.assert_array_equal(alone[0], outs[0][1])
+
+
+def test_gqa_group_of_one_is_mha():
+    """g = 1: every query head reads its own KV head (OptR §3, G_h = {h})."""
+    c = _tiny(Hq=2, Hkv=2)
+    c.r_k, c.r_v = _fp64_orthogonal(103, 2), _fp64_orthogonal(104, 2)
+    x = O.rotate(O.centre_keys(c.k, c.mu), c.r_k)
+    w = O.rotate(c.v, c.r_v)
+    got = O.decode_attention(c.q, None, 2, c.page_table, c.seq_lens, c.r_k, c.r_v, bypass=(x, w, c.tok_seq))
+    for j in range(2):
+        ref = O.softmax_attention(c.q[0, j], c.k[:, j], c.v[:, j], 1 / np.sqrt(128))
+        np.testing.assert_allclose(got[0, j], ref, rtol=0, atol=1e-12)
+
+
+def test_empty_sequence_gives_zero():
+    c = _tiny(B=2, seq_lens=[0, 20])
+    pool = np.zeros(O.pool_bytes(c.num_pages, 1), np.uint8)
+    O.append_tokens(pool, 1, c.slots, c.k, c.v, c.mu, c.r_k, c.r_v)
+    out = O.decode_attention(c.q, pool, 1, c.page_table, c.seq_lens, c.r_k, c.r_v)
+    assert not out[0].any() and np.abs(out[1]).max() > 0
+
+
+def test_output_error_decomposition_eq8():
+    """OptR §3.2 Eq. (8): dy = dy_K + dy_V exactly (random W_O), Eq. (10) E_out = ||dy||^2."""
+    rng = np.random.default_rng(18)
+    T, d = 40, 128
+    q = rng.standard_normal(d)
+    k = rng.standard_normal((T, d)) * 2
+    v = rng.standard_normal((T, d))
+    kq = k + rng.standard_normal((T, d)) * 0.3
+    vq = v + rng.standard_normal((T, d)) * 0.3
+    w_o = rng.standard_normal((64, d))
+    dy, dyk, dyv, e_rec, e_out = O.output_error_terms(q, k, v, kq, vq, w_o)
+    np.testing.assert_allclose(dy, dyk + dyv, rtol=0, atol=1e-12)
+    assert abs(e_out - float(dy @ dy)) <= 1e-9 * max(1.0, e_out)
+    assert abs(e_rec - (np.linalg.norm(k - kq) ** 2 + np.linalg.norm(v - vq) ** 2)) <= 1e-9 * e_rec
+    # no key error -> no key-induced term; no value error -> no value-induced term
+    _, dyk0, _, _, _ = O.output_error_terms(q, k, v, k, vq, w_o)
+    _, _, dyv0, _, _ = O.output_error_terms(q, k, v, kq, v, w_o)
+    assert np.abs(dyk0).max() == 0 and np.abs(dyv0).max() == 0
+
+
+def test_centering_reduces_int2_key_error_with_offsets():
+    """OptR §1: with large per-channel key offsets, centering before rotation shrinks the
+    INT2 key reconstruction error (a direction check on synthetic data)."""
+    c = I.tiny_case()
+    errs = []
+    for mu in (np.zeros_like(c.mu), c.mu):
+        x = O.rotate(O.centre_keys(c.k, mu), c.r_k).astype(np.float32)
+        xq = O.int2_dequantize(*O.int2_quantize(x))
+        errs.append(np.linalg.norm(x - xq))
+    assert errs[1] < errs[0]
