@@ -1,0 +1,193 @@
+/*
+ * kvq.h - C ABI of the rotated INT2 KV-cache library (libkvq.so), gfx950.
+ *
+ * What it computes.  The method is OptR, "Output-Oriented Rotation for INT2
+ * KV-Cache Quantization" (arXiv 2608.02691):
+ *   - write path (section 1 and section 3.1, Eq. (4)): a new key is centred by a
+ *     fixed per-channel mean mu (an attention-equivalent reparameterisation:
+ *     every logit of one query moves by the same constant, so softmax is
+ *     unchanged), rotated by a fixed orthogonal matrix R_K, and quantized to
+ *     INT2 with Q2(.; c, G); a new value is rotated by R_V and quantized;
+ *   - read path (section 3, Eq. (1)-(2); section 3.2, Eq. (5)): softmax
+ *     attention of every query head of a GQA group against the quantized
+ *     cache.  Because R is orthogonal, <q, x_hat R^T> = <q R, x_hat> and
+ *     sum_s p_s (w_hat_s R^T) = (sum_s p_s w_hat_s) R^T, so the kernels rotate
+ *     the query once, attend in the rotated basis straight from the packed
+ *     codes, and rotate the output back once.
+ * Q2 here is asymmetric with clip ratio 1 and G = 32 consecutive rotated
+ * channels of one token: scale = (max - min)/3 and zero = min, both stored as
+ * fp16 (round to nearest even); code = clamp(rint((x - zero)/scale), 0, 3)
+ * computed in IEEE fp32 from the stored fp16 scale and zero; a group whose
+ * stored scale is 0 gets all-zero codes.
+ *
+ * Geometry supported: head_dim 128, group 32, page 16 tokens, query heads per
+ * KV head g = num_q_heads / num_kv_heads with 1 <= g <= 16.
+ *
+ * Cache layout.  One device buffer ("pool") of num_pages * num_kv_heads blocks
+ * of 1536 bytes; block (page p, KV head h) starts at (p*num_kv_heads + h)*1536
+ * and holds the 16 token slots of that page.  Inside a block:
+ *   [0, 1024)    64 records of 16 bytes, record r = 16a + b (a < 4, b < 16)
+ *                = little-endian uint32 words K0, K1, V0, V1.
+ *                K code of slot s, channel c (kk = c/32, a = (c%32)/8, e = c%8):
+ *                  record 16a + s, word K[kk/2], bits 2*(4*(kk%2) + e/2) + 16*(e%2) (+1).
+ *                V code of slot s, channel c (t = c/16, b = c%16, a = s/4, i = s%4):
+ *                  record 16a + b, word V[i/2], bits 2*t + 16*(i%2) (+1).
+ *   [1024, 1536) 16 records of 32 bytes, record m = 4*grp + a: for slots
+ *                s = 4a + i, at +4i the K (fp16 scale, fp16 zero) pair of
+ *                channel group grp, at +16+4i the V pair.
+ * A slot index is page*16 + offset.  96 bytes per token per KV head.
+ *
+ * Conventions for every call.
+ *   - Pointers marked "device" are HIP device (or managed) memory; "host" are
+ *     CPU memory.  The library never allocates, frees or keeps caller memory.
+ *   - Calls validate their arguments on the host and return KVQ_OK or an error
+ *     code without launching anything; kvq_last_error() then describes it.
+ *     Kernels run asynchronously on `stream` (a hipStream_t; NULL = the null
+ *     stream).  No call synchronises the device.  A launch failure returns
+ *     KVQ_EHIP.
+ *   - The library never exits or aborts.  It holds no mutable global state
+ *     besides per-thread error text and a cached compute-unit count.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_EINVAL = 1,       /* null pointer, negative size, inconsistent sizes    */
+  KVQ_EUNSUPPORTED = 2, /* geometry other than d=128, G=32, page 16, g<=16    */
+  KVQ_ENOSPACE = 3,     /* page pool too small / workspace too small          */
+  KVQ_EHIP = 4          /* a HIP runtime call or kernel launch failed         */
+} kvq_status;
+
+typedef enum {
+  KVQ_BF16 = 0,        /* bfloat16                                              */
+  KVQ_F32 = 1,         /* float32                                               */
+  KVQ_F32_ROTATED = 2  /* append only: k, v are already centred and rotated fp32
+                          rows x = (k - mu) R_K and w = v R_V; only Q2 + packing
+                          run (mu, r_k, r_v are ignored and may be NULL)        */
+} kvq_dtype;
+
+/* Geometry of one layer's packed cache. */
+typedef struct {
+  int32_t num_kv_heads; /* H_kv >= 1                                          */
+  int32_t head_dim;     /* must be 128                                        */
+  int32_t group_size;   /* must be 32                                         */
+  int32_t page_size;    /* must be 16                                         */
+  int32_t num_pages;    /* pages in the pool                                  */
+  void* pool;           /* device, kvq_pool_bytes(cache) bytes, 16-byte aligned */
+} kvq_cache;
+
+/* Bytes of the pool: num_pages * num_kv_heads * 1536.  0 if `cache` is NULL
+ * or has non-positive sizes. */
+size_t kvq_pool_bytes(const kvq_cache* cache);
+
+/*
+ * kvq_quant_append - quantize-append n_tokens new tokens into the cache.
+ * OptR section 1 (key centering) and section 3.1, Eq. (4) (z -> Q2(zR)).
+ *
+ *   k, v      device [n_tokens][H_kv][128] of in_dtype (bf16 or fp32), or the
+ *             rotated fp32 rows when in_dtype == KVQ_F32_ROTATED.
+ *   slots     device int32 [n_tokens]: page*16 + offset of each token; all
+ *             distinct, each in [0, num_pages*16).  Out-of-range slots are
+ *             skipped by the kernel (never written).
+ *   mu        device fp32 [H_kv][128], the key centre; NULL means 0.
+ *   r_k, r_v  device fp32 [H_kv][128][128], row-major, x_rot[j] = sum_i x[i] R[i][j].
+ *             Must be orthogonal (not checked).
+ *   rot_out   optional device fp32 [n_tokens][H_kv][2][128]: receives the
+ *             fp32 quantizer inputs (index 0: centred rotated key, 1: rotated
+ *             value) exactly as the kernel quantized them.  NULL = not written.
+ * Writes the K/V codes and fp16 scale/zero of every (token, KV head) into its
+ * slot.  Other slots of the same page keep their contents.
+ * Errors: KVQ_EINVAL (NULL cache/pool/k/v/slots, NULL r_k or r_v unless
+ * pre-rotated, n_tokens < 0), KVQ_EUNSUPPORTED (geometry), KVQ_EHIP.
+ * n_tokens == 0 is a no-op.
+ */
+kvq_status kvq_quant_append(const kvq_cache* cache, const void* k, const void* v, kvq_dtype in_dtype,
+                            int32_t n_tokens, const int32_t* slots, const float* mu, const float* r_k,
+                            const float* r_v, float* rot_out, void* stream);
+
+/*
+ * kvq_decode_workspace_bytes - device workspace needed by kvq_decode_attn for
+ * the same (batch, num_q_heads, num_kv_heads, max_seq_len, num_splits).
+ * num_splits 0 selects the automatic split plan.  Returns 0 on invalid input.
+ */
+size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t max_seq_len, int32_t num_splits);
+
+/*
+ * kvq_decode_attn - one decode step of GQA attention over the packed cache.
+ * OptR section 3, Eq. (1)-(2) and section 3.2, Eq. (5): for query head j of
+ * sequence b, with KV head h = j / g and T = seq_lens[b],
+ *   o_j = ( sum_{s<T} softmax_s( <q_j R_K,h, x_hat_s> * sm_scale ) w_hat_s ) R_V,h^T
+ * where x_hat_s, w_hat_s are the dequantized rotated key/value of position s
+ * (the cached keys were centred; the dropped <q_j, mu> moves all logits of j
+ * equally).  T == 0 gives a zero output.
+ *
+ *   q           device [batch][num_q_heads][128] of q_dtype (KVQ_BF16 or KVQ_F32).
+ *   page_table  device int32 [batch][max_pages]; entry i of row b is the page
+ *               holding positions 16i..16i+15; entries for i < ceil(T/16) must
+ *               be in [0, num_pages) (not checked on the device).
+ *   seq_lens    device int32 [batch], each in [0, max_seq_len].
+ *   max_seq_len host bound on seq_lens; must satisfy ceil(max_seq_len/16) <= max_pages.
+ *   r_k, r_v    device fp32 [H_kv][128][128] as in kvq_quant_append.
+ *   sm_scale    logit scale; 0 selects 1/sqrt(128).
+ *   out         device [batch][num_q_heads][128] of out_dtype (KVQ_BF16 or
+ *               KVQ_F32).  The bf16 output is the fp32 result rounded to
+ *               nearest even.
+ *   workspace   device, >= kvq_decode_workspace_bytes(...) bytes, 16-byte
+ *               aligned; scratch for the split partials, overwritten.
+ *   num_splits  0 = automatic; otherwise the number of sequence splits per
+ *               (sequence, KV head), >= 1.
+ * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ENOSPACE (workspace too small),
+ * KVQ_EHIP.  batch == 0 is a no-op.
+ */
+kvq_status kvq_decode_attn(const kvq_cache* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
+                           int32_t num_q_heads, const int32_t* page_table, int32_t max_pages,
+                           const int32_t* seq_lens, int32_t max_seq_len, const float* r_k, const float* r_v,
+                           float sm_scale, void* out, kvq_dtype out_dtype, void* workspace,
+                           size_t workspace_bytes, int32_t num_splits, void* stream);
+
+/* Page-table policies for kvq_page_table. */
+typedef enum {
+  KVQ_PT_CONTIGUOUS = 0,  /* sequence b gets the next ceil(T_b/16) pages in order       */
+  KVQ_PT_PERMUTED = 1,    /* as contiguous, over a seeded random permutation of the pool */
+  KVQ_PT_INTERLEAVED = 2, /* free list = seeded permutation; for page index i = 0,1,...
+                             visit the sequences in a fresh seeded order and give one
+                             page to each sequence that needs page i                    */
+  KVQ_PT_VALIDATE = 3     /* do not write `table`: check it (entries of live pages in
+                             [0, num_pages), no page used twice)                       */
+} kvq_pt_policy;
+
+/*
+ * kvq_page_table - host-only helper that builds (or validates) a page table.
+ * The paged, regular cache layout is what rotation keeps compatible with
+ * paged serving systems (OptR section 1).
+ *
+ *   seq_lens   host int32 [batch], each >= 0.
+ *   table      host int32 [batch][max_pages]; written (unused entries = -1)
+ *              unless policy is KVQ_PT_VALIDATE, where it is only read.
+ *   slots_out  optional host int32 [batch]: slot of position seq_lens[b]-1
+ *              (-1 when seq_lens[b] == 0).
+ * The random stream is splitmix64 seeded with `seed`.
+ * Errors: KVQ_EINVAL (bad arguments, or an invalid table under
+ * KVQ_PT_VALIDATE), KVQ_ENOSPACE (pool or max_pages too small).
+ */
+kvq_status kvq_page_table(int32_t policy, uint64_t seed, const int32_t* seq_lens, int32_t batch,
+                          int32_t page_size, int32_t num_pages, int32_t max_pages, int32_t* table,
+                          int32_t* slots_out);
+
+/* Text describing the last non-OK status returned on the calling thread. */
+const char* kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

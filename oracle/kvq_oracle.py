@@ -202,33 +202,30 @@ def pack_block(k_codes, k_s16, k_z16, v_codes, v_s16, v_z16, block: np.ndarray |
     return blk
 
 
-def unpack_block(block: np.ndarray):
-    """Inverse of ``pack_block`` for all 16 slots.
+def unpack_blocks(blocks: np.ndarray):
+    """Inverse of ``pack_block`` for a stack of blocks [n, 1536] (all 16 slots each).
 
     Returns (k_codes, k_s16, k_z16, v_codes, v_s16, v_z16) with codes uint8
-    [16, 128] and scales/zeros float16 [16, 4].
+    [n, 16, 128] and scales/zeros float16 [n, 16, 4].
     """
-    blk = np.asarray(block, np.uint8)
-    assert blk.shape == (BLOCK_BYTES,)
-    words = blk[:CODE_BYTES].view("<u4").reshape(64, 4).astype(np.int64)
-    meta = blk[CODE_BYTES:].view("<u2").reshape(16, 2, 4, 2)
+    blk = np.ascontiguousarray(blocks, np.uint8).reshape(-1, BLOCK_BYTES)
+    words = blk[:, :CODE_BYTES].view("<u4").reshape(-1, 64, 4).astype(np.int64)
+    meta = blk[:, CODE_BYTES:].view("<f2").reshape(-1, 16, 2, 4, 2)   # [n][record m][K/V][i][scale/zero]
 
     def gather(pos):
-        rec, word, bit = pos[..., 0], pos[..., 1], pos[..., 2]
-        return ((words[rec, word] >> bit) & 3).astype(np.uint8)
+        rec, word, bit = pos[..., 0], pos[..., 1], pos[..., 2]      # [16, 128] each
+        return ((words[:, rec, word] >> bit[None]) & 3).astype(np.uint8)
 
-    k_codes, v_codes = gather(_K_POS), gather(_V_POS)
-    k_s16 = np.zeros((PAGE, N_GROUPS), np.float16)
-    k_z16, v_s16, v_z16 = k_s16.copy(), k_s16.copy(), k_s16.copy()
-    for s in range(PAGE):
-        a, i = s // 4, s % 4
-        for grp in range(N_GROUPS):
-            m = 4 * grp + a
-            k_s16[s, grp] = meta[m, 0, i, 0:1].view(np.float16)[0]
-            k_z16[s, grp] = meta[m, 0, i, 1:2].view(np.float16)[0]
-            v_s16[s, grp] = meta[m, 1, i, 0:1].view(np.float16)[0]
-            v_z16[s, grp] = meta[m, 1, i, 1:2].view(np.float16)[0]
-    return k_codes, k_s16, k_z16, v_codes, v_s16, v_z16
+    slots = np.arange(PAGE)
+    rec = 4 * np.arange(N_GROUPS)[None, :] + (slots // 4)[:, None]     # [slot, grp] -> record m
+    i = np.broadcast_to((slots % 4)[:, None], rec.shape)
+    return (gather(_K_POS), meta[:, rec, 0, i, 0], meta[:, rec, 0, i, 1],
+            gather(_V_POS), meta[:, rec, 1, i, 0], meta[:, rec, 1, i, 1])
+
+
+def unpack_block(block: np.ndarray):
+    """``unpack_blocks`` for a single block: codes [16, 128], scales/zeros [16, 4]."""
+    return tuple(x[0] for x in unpack_blocks(np.asarray(block, np.uint8)[None]))
 
 
 def pool_bytes(num_pages: int, num_kv_heads: int) -> int:
@@ -280,12 +277,13 @@ def gather_sequence(pool, num_kv_heads, table_row, seq_len, h):
     if T == 0:
         return np.zeros((0, HEAD_DIM)), np.zeros((0, HEAD_DIM))
     n_pages = (T + PAGE - 1) // PAGE
-    xs, ws = [], []
-    for i in range(n_pages):
-        kc, ks, kz, vc, vs, vz = unpack_block(block_view(pool, table_row[i], h, num_kv_heads))
-        xs.append(int2_dequantize(kc, ks, kz))
-        ws.append(int2_dequantize(vc, vs, vz))
-    return np.concatenate(xs)[:T], np.concatenate(ws)[:T]
+    pages = np.asarray(table_row[:n_pages], np.int64)
+    offs = (pages * num_kv_heads + int(h)) * BLOCK_BYTES
+    blocks = np.asarray(pool, np.uint8)[offs[:, None] + np.arange(BLOCK_BYTES)[None, :]]
+    kc, ks, kz, vc, vs, vz = unpack_blocks(blocks)
+    x = int2_dequantize(kc, ks, kz).reshape(-1, HEAD_DIM)[:T]
+    w = int2_dequantize(vc, vs, vz).reshape(-1, HEAD_DIM)[:T]
+    return x, w
 
 
 def softmax_attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray, scale: float) -> np.ndarray:

@@ -1,0 +1,280 @@
+// Host side of the C ABI declared in include/kvq.h: argument validation,
+// split planning, kernel launches and the host page-table helper.
+
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kvq.h"
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local std::string g_error = "no error";
+
+kvq_status fail(kvq_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+kvq_status hip_fail(hipError_t e, const char* what) {
+  return fail(KVQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kHeadDim = 128;
+constexpr int kGroup = 32;
+constexpr int kPage = 16;
+constexpr size_t kBlockBytes = 1536;
+constexpr int kRowStride = 132;  // floats per q_hat row and per split partial
+constexpr int kMaxGroup = 16;
+constexpr int kMinPagesPerSplit = 8;
+
+kvq_status check_cache(const kvq_cache* c) {
+  if (c == nullptr) return fail(KVQ_EINVAL, "cache is NULL");
+  if (c->head_dim != kHeadDim || c->group_size != kGroup || c->page_size != kPage)
+    return fail(KVQ_EUNSUPPORTED, "unsupported geometry head_dim=%d group_size=%d page_size=%d (need 128/32/16)",
+                c->head_dim, c->group_size, c->page_size);
+  if (c->num_kv_heads < 1) return fail(KVQ_EINVAL, "num_kv_heads=%d must be >= 1", c->num_kv_heads);
+  if (c->num_pages < 0) return fail(KVQ_EINVAL, "num_pages=%d must be >= 0", c->num_pages);
+  if (static_cast<long long>(c->num_pages) * kPage > 0x7fffffffLL)
+    return fail(KVQ_EUNSUPPORTED, "num_pages=%d exceeds the int32 slot range", c->num_pages);
+  if (c->pool == nullptr && c->num_pages > 0) return fail(KVQ_EINVAL, "cache pool is NULL");
+  if (reinterpret_cast<uintptr_t>(c->pool) % 16 != 0) return fail(KVQ_EINVAL, "cache pool must be 16-byte aligned");
+  return KVQ_OK;
+}
+
+// Compute units of the current device, cached per device id (256 when no
+// device can be queried, e.g. on a host without a GPU).
+int device_cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (dev < 0) return 256;
+  if (static_cast<size_t>(dev) >= cache.size()) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+      (void)hipGetLastError();
+      n = 256;
+    }
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+bool make_plan(int batch, int num_kv_heads, int max_seq_len, int num_splits, kvq::DecodePlan* plan) {
+  if (batch < 0 || num_kv_heads < 1 || max_seq_len < 0 || num_splits < 0) return false;
+  const int n_pages = (max_seq_len + kPage - 1) / kPage;
+  plan->n_pages_max = n_pages;
+  if (num_splits > 0) {
+    plan->pages_per_split = std::max(1, (n_pages + num_splits - 1) / num_splits);
+    plan->n_splits = num_splits;
+  } else {
+    // Aim at two 4-wave workgroups per compute unit over all (sequence, KV head).
+    const long long target = 2LL * device_cu_count();
+    const long long work = static_cast<long long>(std::max(batch, 1)) * num_kv_heads * std::max(n_pages, 1);
+    long long pps = (work + target - 1) / target;
+    pps = std::max<long long>(pps, kMinPagesPerSplit);
+    plan->pages_per_split = static_cast<int>(std::min<long long>(pps, std::max(n_pages, 1)));
+    plan->n_splits = std::max(1, (n_pages + plan->pages_per_split - 1) / plan->pages_per_split);
+  }
+  return true;
+}
+
+size_t workspace_bytes(int batch, int num_q_heads, const kvq::DecodePlan& plan) {
+  const size_t rows = static_cast<size_t>(batch) * num_q_heads;
+  return sizeof(float) * (rows * kRowStride + rows * static_cast<size_t>(plan.n_splits) * kRowStride);
+}
+
+// splitmix64 (Steele, Lea, Flood 2014) as the page allocator's random stream.
+struct SplitMix64 {
+  uint64_t s;
+  uint64_t next() {
+    uint64_t z = (s += 0x9e3779b97f4a7c15ULL);
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ULL;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebULL;
+    return z ^ (z >> 31);
+  }
+  uint64_t below(uint64_t n) { return next() % n; }  // n > 0; bias is irrelevant here
+};
+
+void shuffle(std::vector<int32_t>& v, SplitMix64& rng) {
+  for (size_t i = v.size(); i > 1; --i) std::swap(v[i - 1], v[rng.below(i)]);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvq_pool_bytes(const kvq_cache* cache) {
+  if (cache == nullptr || cache->num_kv_heads <= 0 || cache->num_pages <= 0) return 0;
+  return static_cast<size_t>(cache->num_pages) * static_cast<size_t>(cache->num_kv_heads) * kBlockBytes;
+}
+
+kvq_status kvq_quant_append(const kvq_cache* cache, const void* k, const void* v, kvq_dtype in_dtype,
+                            int32_t n_tokens, const int32_t* slots, const float* mu, const float* r_k,
+                            const float* r_v, float* rot_out, void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (n_tokens < 0) return fail(KVQ_EINVAL, "n_tokens=%d must be >= 0", n_tokens);
+  if (in_dtype != KVQ_BF16 && in_dtype != KVQ_F32 && in_dtype != KVQ_F32_ROTATED)
+    return fail(KVQ_EUNSUPPORTED, "unsupported input dtype %d", static_cast<int>(in_dtype));
+  if (n_tokens == 0) return KVQ_OK;
+  if (cache->num_pages == 0) return fail(KVQ_ENOSPACE, "cache has no pages");
+  if (k == nullptr || v == nullptr || slots == nullptr) return fail(KVQ_EINVAL, "k, v and slots must be non-NULL");
+  if (in_dtype != KVQ_F32_ROTATED && (r_k == nullptr || r_v == nullptr))
+    return fail(KVQ_EINVAL, "r_k and r_v must be non-NULL unless the input is pre-rotated");
+  const int kind = in_dtype == KVQ_BF16 ? 0 : (in_dtype == KVQ_F32 ? 1 : 2);
+  hipError_t e = kvq::launch_append(static_cast<uint8_t*>(cache->pool), cache->num_pages, cache->num_kv_heads, k, v,
+                                    kind, n_tokens, slots, mu, r_k, r_v, rot_out, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quant_append launch");
+  return KVQ_OK;
+}
+
+size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len,
+                                  int32_t num_splits) {
+  if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0) return 0;
+  kvq::DecodePlan plan;
+  if (!make_plan(batch, num_kv_heads, max_seq_len, num_splits, &plan)) return 0;
+  return workspace_bytes(batch, num_q_heads, plan);
+}
+
+kvq_status kvq_decode_attn(const kvq_cache* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
+                           int32_t num_q_heads, const int32_t* page_table, int32_t max_pages,
+                           const int32_t* seq_lens, int32_t max_seq_len, const float* r_k, const float* r_v,
+                           float sm_scale, void* out, kvq_dtype out_dtype, void* workspace, size_t workspace_bytes_,
+                           int32_t num_splits, void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (batch < 0) return fail(KVQ_EINVAL, "batch=%d must be >= 0", batch);
+  if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads != 0)
+    return fail(KVQ_EINVAL, "num_q_heads=%d must be a positive multiple of num_kv_heads=%d", num_q_heads,
+                cache->num_kv_heads);
+  const int g = num_q_heads / cache->num_kv_heads;
+  if (g > kMaxGroup) return fail(KVQ_EUNSUPPORTED, "query heads per KV head g=%d exceeds %d", g, kMaxGroup);
+  if (q_dtype != KVQ_BF16 && q_dtype != KVQ_F32) return fail(KVQ_EUNSUPPORTED, "q dtype must be bf16 or fp32");
+  if (out_dtype != KVQ_BF16 && out_dtype != KVQ_F32) return fail(KVQ_EUNSUPPORTED, "out dtype must be bf16 or fp32");
+  if (max_seq_len < 0) return fail(KVQ_EINVAL, "max_seq_len=%d must be >= 0", max_seq_len);
+  if (num_splits < 0) return fail(KVQ_EINVAL, "num_splits=%d must be >= 0", num_splits);
+  if (max_pages < (max_seq_len + kPage - 1) / kPage)
+    return fail(KVQ_EINVAL, "max_pages=%d cannot hold max_seq_len=%d", max_pages, max_seq_len);
+  if (batch > 0 && max_seq_len > 0 && cache->num_pages == 0) return fail(KVQ_ENOSPACE, "cache has no pages");
+  if (std::isnan(sm_scale) || std::isinf(sm_scale) || sm_scale < 0.0f)
+    return fail(KVQ_EINVAL, "sm_scale must be finite and >= 0");
+  if (batch == 0) return KVQ_OK;
+  if (q == nullptr || page_table == nullptr || seq_lens == nullptr || r_k == nullptr || r_v == nullptr ||
+      out == nullptr || workspace == nullptr)
+    return fail(KVQ_EINVAL, "q, page_table, seq_lens, r_k, r_v, out and workspace must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return fail(KVQ_EINVAL, "workspace must be 16-byte aligned");
+  if (static_cast<long long>(batch) * num_q_heads > 0x7fffffffLL / kRowStride)
+    return fail(KVQ_EUNSUPPORTED, "batch * num_q_heads too large");
+
+  kvq::DecodePlan plan;
+  if (!make_plan(batch, cache->num_kv_heads, max_seq_len, num_splits, &plan))
+    return fail(KVQ_EINVAL, "cannot plan the decode split");
+  const size_t need = workspace_bytes(batch, num_q_heads, plan);
+  if (workspace_bytes_ < need)
+    return fail(KVQ_ENOSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes_, need);
+  if (plan.n_splits > 65535) return fail(KVQ_EUNSUPPORTED, "too many splits (%d)", plan.n_splits);
+  if (batch > 65535 || cache->num_kv_heads > 65535) return fail(KVQ_EUNSUPPORTED, "batch or num_kv_heads too large");
+
+  const float scale = sm_scale == 0.0f ? 1.0f / std::sqrt(static_cast<float>(kHeadDim)) : sm_scale;
+  kvq::DecodeArgs a;
+  a.pool = static_cast<const uint8_t*>(cache->pool);
+  a.num_kv_heads = cache->num_kv_heads;
+  a.num_pages = cache->num_pages;
+  a.q = q;
+  a.q_kind = q_dtype == KVQ_BF16 ? 0 : 1;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.page_table = page_table;
+  a.max_pages = max_pages;
+  a.seq_lens = seq_lens;
+  a.r_k = r_k;
+  a.r_v = r_v;
+  a.logit_scale = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);  // log2(e)
+  a.out = out;
+  a.out_kind = out_dtype == KVQ_BF16 ? 0 : 1;
+  a.qhat = static_cast<float*>(workspace);
+  a.part = a.qhat + static_cast<size_t>(batch) * num_q_heads * kRowStride;
+  hipError_t e = kvq::launch_decode(a, plan, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "decode launch");
+  return KVQ_OK;
+}
+
+kvq_status kvq_page_table(int32_t policy, uint64_t seed, const int32_t* seq_lens, int32_t batch, int32_t page_size,
+                          int32_t num_pages, int32_t max_pages, int32_t* table, int32_t* slots_out) {
+  if (batch < 0 || num_pages < 0 || max_pages < 0) return fail(KVQ_EINVAL, "negative size");
+  if (page_size != kPage) return fail(KVQ_EUNSUPPORTED, "page_size must be 16");
+  if (batch > 0 && (seq_lens == nullptr || table == nullptr)) return fail(KVQ_EINVAL, "seq_lens and table required");
+  if (policy < KVQ_PT_CONTIGUOUS || policy > KVQ_PT_VALIDATE) return fail(KVQ_EINVAL, "unknown policy %d", policy);
+  std::vector<int32_t> need(batch);
+  long long total = 0;
+  int most = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (seq_lens[b] < 0) return fail(KVQ_EINVAL, "seq_lens[%d]=%d is negative", b, seq_lens[b]);
+    need[b] = (seq_lens[b] + kPage - 1) / kPage;
+    total += need[b];
+    most = std::max(most, need[b]);
+  }
+  if (most > max_pages) return fail(KVQ_ENOSPACE, "a sequence needs %d pages but max_pages=%d", most, max_pages);
+  if (total > num_pages) return fail(KVQ_ENOSPACE, "sequences need %lld pages but the pool has %d", total, num_pages);
+
+  if (policy == KVQ_PT_VALIDATE) {
+    std::vector<uint8_t> used(num_pages, 0);
+    for (int b = 0; b < batch; ++b)
+      for (int i = 0; i < need[b]; ++i) {
+        const int32_t p = table[static_cast<size_t>(b) * max_pages + i];
+        if (p < 0 || p >= num_pages)
+          return fail(KVQ_EINVAL, "table[%d][%d]=%d outside [0, %d)", b, i, p, num_pages);
+        if (used[p]) return fail(KVQ_EINVAL, "page %d is used twice (table[%d][%d])", p, b, i);
+        used[p] = 1;
+      }
+  } else {
+    std::vector<int32_t> order(num_pages);
+    for (int i = 0; i < num_pages; ++i) order[i] = i;
+    SplitMix64 rng{seed};
+    if (policy != KVQ_PT_CONTIGUOUS) shuffle(order, rng);
+    for (size_t i = 0; i < static_cast<size_t>(batch) * max_pages; ++i) table[i] = -1;
+    size_t next = 0;
+    if (policy == KVQ_PT_INTERLEAVED) {
+      std::vector<int32_t> seqs(batch);
+      for (int i = 0; i < most; ++i) {
+        for (int b = 0; b < batch; ++b) seqs[b] = b;
+        shuffle(seqs, rng);
+        for (int b : seqs)
+          if (i < need[b]) table[static_cast<size_t>(b) * max_pages + i] = order[next++];
+      }
+    } else {
+      for (int b = 0; b < batch; ++b)
+        for (int i = 0; i < need[b]; ++i) table[static_cast<size_t>(b) * max_pages + i] = order[next++];
+    }
+  }
+  if (slots_out != nullptr)
+    for (int b = 0; b < batch; ++b) {
+      const int32_t t = seq_lens[b] - 1;
+      slots_out[b] = t < 0 ? -1 : table[static_cast<size_t>(b) * max_pages + t / kPage] * kPage + t % kPage;
+    }
+  return KVQ_OK;
+}
+
+const char* kvq_last_error(void) { return g_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Device-side helpers shared by the kvq kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+// Cache geometry (the only one the kernels implement).
+constexpr int kHeadDim = 128;
+constexpr int kGroup = 32;
+constexpr int kPage = 16;
+constexpr int kBlockBytes = 1536;   // one (page, KV head) block
+constexpr int kCodeBytes = 1024;    // 64 records x 16 B of K/V code words
+constexpr int kMetaRecordBytes = 32;
+
+// Row strides (floats) of the decode workspace.
+constexpr int kQhatStride = 132;    // [0,128) scaled rotated query, [128] fp16 range factor
+constexpr int kPartStride = 132;    // [0,128) unnormalised rotated output, [128] max, [129] sum
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef uint32_t uint4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u) return static_cast<uint16_t>((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+// DPP move inside 16-lane rows (ctrl is a gfx9 DPP control word).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+template <int kLane>
+struct QuadBcast { static constexpr int ctrl = kLane | (kLane << 2) | (kLane << 4) | (kLane << 6); };
+
+// Sum over the lanes {n, n^4, n^8, n^12} of each 16-lane row (lane bits 2..3).
+__device__ __forceinline__ float row_sum_stride4(float x) {
+  x += dpp_f32<kDppRowRor8>(x);
+  x += dpp_f32<kDppRowRor4>(x);
+  return x;
+}
+
+// Pair lanes l and l^16 / l^32 with the gfx950 permlane swaps: the two returned
+// words are x[l] and x[l ^ 16] (resp. ^32), in some order.
+__device__ __forceinline__ void swap16(float x, float& u, float& v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  u = __uint_as_float(r[0]);
+  v = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float x, float& u, float& v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  u = __uint_as_float(r[0]);
+  v = __uint_as_float(r[1]);
+}
+// Max / sum over the four 16-lane rows (lane bits 4..5).
+__device__ __forceinline__ float rows_max(float x) {
+  float u, v;
+  swap16(x, u, v);
+  x = fmaxf(u, v);
+  swap32(x, u, v);
+  return fmaxf(u, v);
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  float u, v;
+  swap16(x, u, v);
+  x = u + v;
+  swap32(x, u, v);
+  return u + v;
+}
+
+}  // namespace kvq

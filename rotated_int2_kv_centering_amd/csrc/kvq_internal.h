@@ -1,0 +1,41 @@
+// Kernel launchers used by the C ABI (internal to libkvq).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const void* k, const void* v, int in_kind,
+                         int n_tokens, const int32_t* slots, const float* mu, const float* r_k, const float* r_v,
+                         float* rot_out, hipStream_t stream);
+
+struct DecodePlan {
+  int n_pages_max;      // ceil(max_seq_len / 16)
+  int pages_per_split;  // pages handled by one workgroup
+  int n_splits;         // splits per (sequence, KV head)
+};
+
+struct DecodeArgs {
+  const uint8_t* pool;
+  int num_kv_heads;
+  int num_pages;
+  const void* q;
+  int q_kind;  // 0 bf16, 1 fp32
+  int batch;
+  int num_q_heads;
+  const int32_t* page_table;
+  int max_pages;
+  const int32_t* seq_lens;
+  const float* r_k;
+  const float* r_v;
+  float logit_scale;  // sm_scale * log2(e)
+  void* out;
+  int out_kind;  // 0 bf16, 1 fp32
+  float* qhat;   // workspace: [batch][num_q_heads][kQhatStride]
+  float* part;   // workspace: [batch][num_q_heads][n_splits][kPartStride]
+};
+
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+
+}  // namespace kvq

@@ -1,0 +1,158 @@
+"""GPU parity of the quantize-append kernel against the oracle (through the C ABI)."""
+
+import numpy as np
+import pytest
+
+import kvq_inputs as I
+from oracle import kvq_oracle as O
+from tests.gpu_util import DeviceCase, dev_tensor, require_gpu, rotation_error_bound
+
+pytestmark = pytest.mark.gpu
+
+
+def _prerotated_append(dc: DeviceCase, x: np.ndarray, w: np.ndarray, slots: np.ndarray):
+    from rotated_int2_kv_centering_amd import kvq
+    import torch
+    xt = dev_tensor(x.astype(np.float32), dc.dev)
+    wt = dev_tensor(w.astype(np.float32), dc.dev)
+    st = dev_tensor(slots.astype(np.int32), dc.dev)
+    kvq.kvq_quant_append(dc.cache, xt, wt, kvq.KVQ_F32_ROTATED, len(slots), st, None, None, None, None)
+    torch.cuda.synchronize()
+
+
+def _oracle_pool(case, num_pages, slots, x, w, base=None):
+    pool = np.zeros(O.pool_bytes(num_pages, case.Hkv), np.uint8) if base is None else base.copy()
+    O.quantize_append(pool, case.Hkv, slots, x.astype(np.float32), w.astype(np.float32))
+    return pool
+
+
+@pytest.mark.parametrize("which", ["tiny", "llama_small"])
+def test_prerotated_codes_and_scales_bit_exact(which):
+    """Given the same rotated fp32 input, INT2 codes and fp16 scale/zero are bit-exact."""
+    dev = require_gpu()
+    case = I.tiny_case() if which == "tiny" else I.make_case("s", 21, B=2, Hq=32, Hkv=8, seq_lens=[100, 37])
+    x, w = O.rotated_inputs(case.k, case.v, case.mu, case.r_k, case.r_v)
+    dc = DeviceCase(case, dev)
+    _prerotated_append(dc, x, w, case.slots)
+    np.testing.assert_array_equal(dc.pool_np(), _oracle_pool(case, dc.num_pages, case.slots, x, w))
+
+
+def test_prerotated_ties_ranges_and_degenerate_groups():
+    """Rows built on exact ties (x - z)/s = k + 1/2, constant groups, tiny ranges and
+    large magnitudes: still bit-exact."""
+    dev = require_gpu()
+    rng = np.random.default_rng(31)
+    case = I.make_case("t", 32, B=1, Hq=4, Hkv=2, seq_lens=[48], dtype="f32", table_policy="permuted")
+    n = case.n_tokens
+    x = np.zeros((n, 2, 128), np.float32)
+    w = np.zeros((n, 2, 128), np.float32)
+    for t in range(n):
+        for h in range(2):
+            for grp in range(4):
+                kind = (t + h + grp) % 5
+                if kind == 0:    # s = 1, z = 0: ties at 0.5, 1.5, 2.5
+                    g = rng.choice([0.0, 0.5, 1.0, 1.5, 2.0, 2.5, 3.0], 32).astype(np.float32)
+                    g[0], g[1] = 0.0, 3.0
+                elif kind == 1:  # constant
+                    g = np.full(32, rng.standard_normal(), np.float32)
+                elif kind == 2:  # range that underflows the fp16 scale
+                    g = (1e-8 * rng.standard_normal(32)).astype(np.float32)
+                elif kind == 3:  # large magnitudes
+                    g = (3000.0 * rng.standard_normal(32)).astype(np.float32)
+                else:
+                    g = rng.standard_normal(32).astype(np.float32)
+                x[t, h, 32 * grp:32 * grp + 32] = g
+                w[t, h, 32 * grp:32 * grp + 32] = g[::-1]
+    dc = DeviceCase(case, dev)
+    _prerotated_append(dc, x, w, case.slots)
+    np.testing.assert_array_equal(dc.pool_np(), _oracle_pool(case, dc.num_pages, case.slots, x, w))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_raw_path_rotation_and_codes(dtype):
+    """Raw path: the kernel's fp32 rotation is within the derived rounding bound of the
+    oracle's fp64 rotation, and its codes/scales are bit-exact to the oracle's quantizer
+    run on the kernel's own rotated input (both decide codes in fp32)."""
+    dev = require_gpu()
+    case = I.make_case("r", 41, B=2, Hq=16, Hkv=4, seq_lens=[70, 45], dtype=dtype, table_policy="interleaved")
+    dc = DeviceCase(case, dev)
+    rot = dc.append(rot_out=True).cpu().numpy()
+    xg, wg = rot[:, :, 0, :], rot[:, :, 1, :]
+    x64 = O.rotate(O.centre_keys(case.k, case.mu), case.r_k)
+    w64 = O.rotate(case.v, case.r_v)
+    for h in range(case.Hkv):
+        a_k = O.centre_keys(case.k, case.mu)[:, h]
+        assert np.all(np.abs(xg[:, h] - x64[:, h]) <= rotation_error_bound(a_k, case.r_k[h]) + 1e-30)
+        assert np.all(np.abs(wg[:, h] - w64[:, h]) <= rotation_error_bound(case.v[:, h], case.r_v[h]) + 1e-30)
+    np.testing.assert_array_equal(dc.pool_np(), _oracle_pool(case, dc.num_pages, case.slots, xg, wg))
+    # codes from the oracle's own rotation differ only where u sits on a rounding boundary
+    ko = O.int2_quantize(x64.astype(np.float32))[0]
+    kg = O.int2_quantize(xg)[0]
+    assert np.mean(ko != kg) < 1e-3
+
+
+def test_same_page_tokens_in_one_call_any_order():
+    """Many tokens sharing pages, appended in one call in a scrambled order (concurrent
+    read-modify-write of shared value words) and then again over dirty pages."""
+    dev = require_gpu()
+    case = I.make_case("p", 51, B=3, Hq=8, Hkv=2, seq_lens=[64, 33, 17], table_policy="permuted")
+    x, w = O.rotated_inputs(case.k, case.v, case.mu, case.r_k, case.r_v)
+    perm = np.random.default_rng(5).permutation(case.n_tokens)
+    dc = DeviceCase(case, dev)
+    dc.pool.copy_(dev_tensor(np.random.default_rng(6).integers(0, 256, dc.pool.numel()).astype(np.uint8), dev))
+    dirty = dc.pool_np()
+    _prerotated_append(dc, x[perm], w[perm], case.slots[perm])
+    expect = _oracle_pool(case, dc.num_pages, case.slots, x, w, base=dirty)
+    np.testing.assert_array_equal(dc.pool_np(), expect)
+
+
+def test_invalid_slots_are_skipped_and_other_slots_kept():
+    dev = require_gpu()
+    case = I.make_case("i", 61, B=1, Hq=4, Hkv=1, seq_lens=[20], dtype="f32", table_policy="contiguous")
+    x, w = O.rotated_inputs(case.k, case.v, case.mu, case.r_k, case.r_v)
+    dc = DeviceCase(case, dev)
+    slots = case.slots.copy()
+    slots[3] = -1
+    slots[7] = dc.num_pages * 16        # one past the end
+    _prerotated_append(dc, x, w, slots)
+    keep = np.array([i for i in range(case.n_tokens) if i not in (3, 7)])
+    np.testing.assert_array_equal(dc.pool_np(), _oracle_pool(case, dc.num_pages, case.slots[keep], x[keep], w[keep]))
+
+
+def test_identity_rotation_zero_mu_matches_direct_int2():
+    """R = I, mu = 0: cache equals INT2 of the raw k, v (bit-exact, raw fp32 path)."""
+    dev = require_gpu()
+    case = I.make_case("e", 71, B=1, Hq=4, Hkv=1, seq_lens=[40], dtype="f32", identity_rotation=True, mu_zero=True)
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False)
+    np.testing.assert_array_equal(dc.pool_np(), _oracle_pool(case, dc.num_pages, case.slots, case.k, case.v))
+
+
+def test_full_size_append_sampled_tokens():
+    """8B shape at 128K context: bulk append of all tokens; sampled tokens bit-exact to the
+    oracle's quantizer on the kernel's rotated rows, and within the rotation bound."""
+    dev = require_gpu()
+    case = I.llama8b_case(131072)
+    dc = DeviceCase(case, dev)
+    rot = dc.append(rot_out=True)
+    pool = dc.pool_np()
+    rng = np.random.default_rng(7)
+    idx = np.sort(rng.choice(case.n_tokens, 512, replace=False))
+    import torch
+    rs = rot[torch.as_tensor(idx, device=rot.device)].cpu().numpy()
+    kc, ks, kz = O.int2_quantize(rs[:, :, 0])
+    vc, vs, vz = O.int2_quantize(rs[:, :, 1])
+    for n_i, n in enumerate(idx):
+        page, off = divmod(int(case.slots[n]), 16)
+        for h in range(case.Hkv):
+            got = O.unpack_block(O.block_view(pool, page, h, case.Hkv))
+            np.testing.assert_array_equal(got[0][off], kc[n_i, h])
+            np.testing.assert_array_equal(got[3][off], vc[n_i, h])
+            np.testing.assert_array_equal(got[1][off].view(np.uint16), ks[n_i, h].view(np.uint16))
+            np.testing.assert_array_equal(got[2][off].view(np.uint16), kz[n_i, h].view(np.uint16))
+            np.testing.assert_array_equal(got[4][off].view(np.uint16), vs[n_i, h].view(np.uint16))
+            np.testing.assert_array_equal(got[5][off].view(np.uint16), vz[n_i, h].view(np.uint16))
+    x64 = O.rotate(O.centre_keys(case.k[idx], case.mu), case.r_k)
+    for h in range(case.Hkv):
+        a_k = O.centre_keys(case.k[idx], case.mu)[:, h]
+        assert np.all(np.abs(rs[:, h, 0] - x64[:, h]) <= rotation_error_bound(a_k, case.r_k[h]) + 1e-30)

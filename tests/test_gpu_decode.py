@@ -1,0 +1,166 @@
+"""GPU parity of the fused decode attention against the oracle (through the C ABI).
+
+The oracle runs on the kernel's own pool bytes, so both sides read the same
+dequantized cache.  The gate is 2e-3 max-abs-relative per (sequence, head) row
+on the fp32 output; the bf16 output must equal the fp32 output rounded to
+nearest even.
+"""
+
+import numpy as np
+import pytest
+
+import kvq_inputs as I
+from oracle import kvq_oracle as O
+from tests.gpu_util import DeviceCase, dev_tensor, max_abs_rel, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _oracle_decode(case, pool, heads=None):
+    return O.decode_attention(case.q, pool, case.Hkv, case.page_table, case.seq_lens, case.r_k, case.r_v, heads=heads)
+
+
+def _rne_bf16(x: np.ndarray) -> np.ndarray:
+    """Reference fp32 -> bf16 rounding (nearest even) for the output-format check."""
+    return I.bf16_bits(np.asarray(x, np.float32))
+
+
+def test_tiny_case_parity_and_split_counts():
+    dev = require_gpu()
+    case = I.tiny_case()
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False)
+    ref = _oracle_decode(case, dc.pool_np())
+    for ns in (0, 1, 2, 3, 16):
+        got = dc.decode("f32", num_splits=ns)
+        err = max_abs_rel(got, ref)
+        assert err <= TOL, (ns, err)
+
+
+SHAPES = [
+    # (B, Hq, Hkv, seq_lens, policy)
+    (1, 4, 1, [1], "contiguous"),
+    (1, 4, 1, [15], "contiguous"),
+    (1, 4, 1, [16], "permuted"),
+    (1, 4, 1, [17], "permuted"),
+    (1, 8, 2, [31], "permuted"),
+    (1, 8, 2, [33], "permuted"),
+    (3, 8, 2, [0, 5, 100], "interleaved"),
+    (2, 2, 2, [77, 300], "interleaved"),        # g = 1
+    (2, 4, 2, [129, 64], "interleaved"),        # g = 2
+    (2, 32, 8, [1000, 257], "interleaved"),     # g = 4, Llama-3.1-8B heads
+    (2, 64, 8, [513, 1024], "interleaved"),     # g = 8, 70B-class heads
+    (1, 12, 1, [200], "permuted"),              # g = 12 (padded quad)
+    (1, 16, 1, [300], "permuted"),              # g = 16
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"B{s[0]}_Hq{s[1]}_Hkv{s[2]}_T{'-'.join(map(str, s[3]))}")
+def test_decode_parity_shapes(shape):
+    dev = require_gpu()
+    B, Hq, Hkv, lens, policy = shape
+    case = I.make_case("d", 100 + sum(lens) + Hq, B=B, Hq=Hq, Hkv=Hkv, seq_lens=lens, table_policy=policy)
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False)
+    ref = _oracle_decode(case, dc.pool_np())
+    for ns in (0, 1, 7):
+        got = dc.decode("f32", num_splits=ns)
+        assert np.isfinite(got).all()
+        err = max_abs_rel(got, ref)
+        assert err <= TOL, (ns, err)
+    for b in range(B):
+        if lens[b] == 0:
+            assert not got[b].any()
+
+
+def test_bf16_output_is_rounded_fp32_output():
+    dev = require_gpu()
+    case = I.make_case("o", 7, B=2, Hq=32, Hkv=8, seq_lens=[333, 4000], table_policy="interleaved")
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False)
+    f32 = dc.decode("f32")
+    b16 = dc.decode("bf16")
+    np.testing.assert_array_equal(b16, _rne_bf16(f32))
+    assert max_abs_rel(f32, _oracle_decode(case, dc.pool_np())) <= TOL
+
+
+def test_page_permutation_gives_identical_output():
+    """The same tokens under a different physical page placement: bit-identical output."""
+    dev = require_gpu()
+    base = dict(B=2, Hq=32, Hkv=8, seq_lens=[700, 1500])
+    a = I.make_case("q", 9, table_policy="contiguous", **base)
+    b = I.make_case("q", 9, table_policy="interleaved", **base)
+    assert not np.array_equal(a.page_table, b.page_table)
+    outs = []
+    for case in (a, b):
+        dc = DeviceCase(case, dev)
+        dc.append(rot_out=False)
+        outs.append(dc.decode("f32"))
+    np.testing.assert_array_equal(outs[0], outs[1])
+
+
+def test_repeated_calls_are_deterministic():
+    dev = require_gpu()
+    case = I.make_case("r", 11, B=1, Hq=32, Hkv=8, seq_lens=[5000])
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False)
+    first = dc.decode("f32")
+    for _ in range(3):
+        np.testing.assert_array_equal(dc.decode("f32"), first)
+
+
+def test_centering_is_invisible_to_attention_on_exact_cache():
+    """OptR section 1: centering shifts every logit of a query by <q, mu>, so softmax is
+    unchanged.  Keys k = mu + 0.5 * levels and values 0.25 * levels (R = I) quantize
+    exactly once centred, so the kernel's output must equal plain Eq. (1)-(2) attention
+    on the raw, uncentred k and v."""
+    dev = require_gpu()
+    rng = np.random.default_rng(12)
+    case = I.make_case("c", 13, B=1, Hq=4, Hkv=1, seq_lens=[64], dtype="f32", identity_rotation=True,
+                       mu_zero=True)
+
+    def levels():
+        lv = rng.integers(0, 4, size=(64, 1, 128)).astype(np.float32)
+        lv[:, :, 0::32] = 0
+        lv[:, :, 1::32] = 3
+        return lv
+
+    mu = (np.round(rng.standard_normal((1, 128)) * 4) / 4).astype(np.float32)
+    case.k = (levels() * np.float32(0.5) + mu[None]).astype(np.float32)
+    case.v = (levels() * np.float32(0.25)).astype(np.float32)
+    case.mu = mu
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False)
+    got = dc.decode("f32")
+    for j in range(case.Hq):
+        ref = O.softmax_attention(case.q[0, j], case.k[:, 0], case.v[:, 0], 1 / np.sqrt(128))
+        assert max_abs_rel(got[0, j], ref) <= TOL
+
+
+FULL = {
+    "llama8b_t32k": lambda: I.llama8b_case(32768),
+    "llama8b_t128k": lambda: I.llama8b_case(131072),
+    "llama8b_batch16": lambda: I.batched_case(),
+    "gqa70b_b4_t128k": lambda: I.seventy_b_case(),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled_heads(name):
+    """Workload sizes: bulk append of the whole context, one decode step, and the oracle
+    on sampled (sequence, head) rows over the kernel's own pool."""
+    dev = require_gpu()
+    case = FULL[name]()
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False, chunk=1 << 20)
+    got = dc.decode("f32")
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(3)
+    heads = sorted({(int(rng.integers(case.B)), int(rng.integers(case.Hq))) for _ in range(4)} |
+                   {(case.B - 1, case.Hq - 1), (0, 0)})
+    ref = _oracle_decode(case, dc.pool_np(), heads=heads)
+    for b, j in heads:
+        err = max_abs_rel(got[b, j], ref[b, j])
+        assert err <= TOL, (b, j, err)
