@@ -1,0 +1,325 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the rotated INT2 KV cache on one MI355X.
+
+One step = the whole hot path for one layer: quantize-append of the newest
+token of every sequence (position T-1 is re-appended so T stays fixed) and
+one fused decode-attention call over the packed cache.  Inputs are resident
+in HBM before timing starts.  Steps cycle over independent cache replicas
+("layers") whose total size exceeds twice the 256 MB Infinity Cache, so the
+cache read comes from HBM, not from the MALL.
+
+Prints ONE JSON line:
+  value      KV-tokens/s = sum_b T_b / step time (one GPU = whole job)
+  roofline   split-K attention kernel: algorithmic bytes per launch / its
+             average duration from HIP events recorded around it on its own
+             stream inside the timed region, against 8 TB/s
+  cpu_baseline  the oracle (NumPy, fp64) timed on a bounded sample of the same step
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0           # MI355X HBM3E peak
+MALL_BYTES = 256 * 1024 * 1024   # Infinity Cache
+BYTES_PER_TOKEN_HEAD = 96        # K+V codes (2 x 32 B) + K+V fp16 scale/zero (2 x 16 B)
+PAGE = 16
+
+WORKLOADS = {
+    "llama8b_t128k": ("Llama-3.1-8B-shaped decode, batch 1, context 131072 (32 q / 8 kv heads, d=128)",
+                      lambda I: I.llama8b_case(131072)),
+    "llama8b_t32k": ("Llama-3.1-8B-shaped decode, batch 1, context 32768 (32 q / 8 kv heads, d=128)",
+                     lambda I: I.llama8b_case(32768)),
+    "llama8b_batch16": ("Llama-3.1-8B-shaped decode, batch 16, contexts uniform in [4K, 64K]",
+                        lambda I: I.batched_case()),
+    "gqa70b_b4_t128k": ("70B-class GQA decode (64 q / 8 kv heads), batch 4, context 131072 each",
+                        lambda I: I.seventy_b_case()),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """hipEvent_* from the HIP runtime already loaded by torch (one runtime per process)."""
+
+    def __init__(self):
+        maps = open("/proc/self/maps").read()
+        paths = sorted({l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l})
+        if len(paths) != 1:
+            raise RuntimeError(f"expected one HIP runtime in the process, found {paths}")
+        self.lib = ctypes.CDLL(paths[0])
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self) -> int:
+        ev = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev.value
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+
+def counters_for(kernel_src: str, workload: str):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"split_kernel_{workload}_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_sha and m_b) or m_sha.group(1) != kernel_src:
+        return None
+    return float(m_b.group(1))
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for name in ("kvq_decode.hip", "kvq_device.h"):
+        with open(os.path.join(ROOT, "rotated_int2_kv_centering_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def cpu_baseline(case, pool_np, kv_heads_sample: int):
+    """Time the oracle (as it stands) on KV heads [0, kv_heads_sample) of the step:
+    the append of the newest token and the decode of their query heads, then scale
+    to the whole step.  BLAS is held to one thread, so cores = 1."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+    from oracle import kvq_oracle as O
+
+    hs = list(range(min(kv_heads_sample, case.Hkv)))
+    heads = [(b, j) for b in range(case.B) for j in range(case.Hq) if j // case.g in hs]
+    last = np.array([np.nonzero(case.tok_seq == b)[0][-1] for b in range(case.B)])
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        pool = pool_np.copy()
+        x, w = O.rotated_inputs(case.k[last], case.v[last], case.mu, case.r_k, case.r_v)
+        O.quantize_append(pool, case.Hkv, case.slots[last], x, w)
+        O.decode_attention(case.q, pool, case.Hkv, case.page_table, case.seq_lens, case.r_k, case.r_v, heads=heads)
+        dt = time.perf_counter() - t0
+    step_est = dt * case.Hkv / len(hs)
+    tokens = float(case.seq_lens.sum())
+    return {
+        "value": tokens / step_est,
+        "unit": "KV-tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"oracle (NumPy fp64) append of the newest token + decode of the {len(heads)} query heads on KV heads "
+                   f"{hs[0]}..{hs[-1]} of the same step ({dt:.1f} s), scaled by {case.Hkv}/{len(hs)} KV heads"),
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="llama8b_t128k", choices=sorted(WORKLOADS))
+    ap.add_argument("--replicas", type=int, default=0, help="cache replicas cycled per step (0 = auto, > 2x MALL)")
+    ap.add_argument("--hold-ms", type=float, default=60.0,
+                    help="length of the spin kernel that holds the stream while the timed steps are enqueued")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cpu-kv-heads", type=int, default=8, help="KV heads in the oracle's timed sample (0 = skip)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); the rotated INT2 "
+              f"decode path here is single-GPU and multi-GPU runs are not part of this build.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import kvq_inputs as I
+    from rotated_int2_kv_centering_amd import kvq
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    kvq.load()
+    hip = Hip()
+    dev = torch.device("cuda:0")
+    desc, make = WORKLOADS[args.workload]
+
+    t_gen = time.perf_counter()
+    case = make(I)
+    log(f"[bench] generated {case.name}: B={case.B} Hq={case.Hq} Hkv={case.Hkv} sum(T)={int(case.seq_lens.sum())} "
+        f"in {time.perf_counter() - t_gen:.1f}s")
+
+    def T(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def B16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    cache_bytes = int(case.seq_lens.sum()) * case.Hkv * BYTES_PER_TOKEN_HEAD
+    pool_bytes = case.num_pages * case.Hkv * 1536
+    n_rep = args.replicas or max(2, -(-2 * MALL_BYTES // pool_bytes) + 1)
+
+    # ---- replica 0: bulk quantize-append of the whole context
+    k_all, v_all = B16(case.k_bits), B16(case.v_bits)
+    slots_all = T(case.slots)
+    pools, caches, rks, rvs, mus = [], [], [], [], []
+    for r in range(n_rep):
+        pools.append(torch.zeros(pool_bytes, dtype=torch.uint8, device=dev))
+        caches.append(kvq.make_cache(case.Hkv, case.num_pages, pools[-1]))
+        rks.append(T(case.r_k))
+        rvs.append(T(case.r_v))
+        mus.append(T(case.mu))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    chunk = 1 << 20
+    for s in range(0, case.n_tokens, chunk):
+        e = min(case.n_tokens, s + chunk)
+        kvq.kvq_quant_append(caches[0], k_all[s:e], v_all[s:e], kvq.KVQ_BF16, e - s, slots_all[s:e], mus[0], rks[0],
+                             rvs[0], None)
+    torch.cuda.synchronize()
+    bulk_ms = (time.perf_counter() - t0) * 1e3
+    for r in range(1, n_rep):
+        pools[r].copy_(pools[0])
+    del k_all, v_all, slots_all
+    torch.cuda.synchronize()
+    log(f"[bench] bulk append of {case.n_tokens} tokens: {bulk_ms:.1f} ms; {n_rep} replicas x {pool_bytes / 1e6:.1f} MB")
+
+    # ---- per-step inputs: newest token of each sequence, queries, tables
+    last = np.array([np.nonzero(case.tok_seq == b)[0][-1] for b in range(case.B)])
+    k_new, v_new = B16(case.k_bits[last]), B16(case.v_bits[last])
+    slots_new = T(case.slots[last])
+    q = B16(case.q_bits)
+    table = T(case.page_table)
+    seq = T(case.seq_lens)
+    max_seq = int(case.seq_lens.max())
+    ws_bytes = kvq.kvq_decode_workspace_bytes(case.B, case.Hq, case.Hkv, max_seq, args.num_splits)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    outs = [torch.empty((case.B, case.Hq, 128), dtype=torch.bfloat16, device=dev) for _ in range(n_rep)]
+
+    def step(r, ev_b=None, ev_e=None):
+        kvq.kvq_quant_append(caches[r], k_new, v_new, kvq.KVQ_BF16, case.B, slots_new, mus[r], rks[r], rvs[r], None)
+        kvq.kvq_decode_attn_traced(caches[r], q, kvq.KVQ_BF16, case.B, case.Hq, table, table.shape[1], seq, max_seq,
+                                   rks[r], rvs[r], 0.0, outs[r], kvq.KVQ_BF16, ws, ws_bytes, args.num_splits, None,
+                                   ev_b, ev_e)
+
+    # eager reference output of every replica (also warms up the kernels)
+    for r in range(n_rep):
+        step(r)
+    torch.cuda.synchronize()
+    eager_out = [o.clone() for o in outs]
+
+    n_cycles = max(1, -(-args.steps // n_rep))
+    steps = n_cycles * n_rep
+    ev_b = [hip.event() for _ in range(steps)]
+    ev_e = [hip.event() for _ in range(steps)]
+
+    def run_all():
+        for i in range(steps):
+            step(i % n_rep, ev_b[i], ev_e[i])
+
+    # warm-up: at least `warmup` steps (whole passes of the step sequence)
+    warm_passes = max(1, -(-args.warmup // steps))
+    for _ in range(warm_passes):
+        run_all()
+    torch.cuda.synchronize()
+    for r in range(n_rep):
+        if not torch.equal(outs[r], eager_out[r]):
+            raise RuntimeError(f"warm-up output differs from the first output on replica {r}")
+
+    # ---- timed region: `steps` whole steps, no host synchronisation inside.
+    # A bounded spin kernel queued first holds the stream while the host enqueues
+    # every step, so the GPU then runs them back to back (no host launch gaps);
+    # the start event is recorded after the spin, so it is not timed.
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(args.hold_ms * 1e-3 * 2.4e9))
+    start.record()
+    t_wall = time.perf_counter()
+    run_all()
+    t_enqueue = (time.perf_counter() - t_wall) * 1e3
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / steps
+    split_ms = [hip.elapsed_ms(ev_b[i], ev_e[i]) for i in range(steps)]
+    split_avg_ms = float(np.mean(split_ms))
+    for r in range(n_rep):
+        if not torch.equal(outs[r], eager_out[r]):
+            raise RuntimeError(f"timed output differs from the first output on replica {r}")
+    log(f"[bench] {steps} steps: {ms_per_step * 1e3:.2f} us/step, split kernel {split_avg_ms * 1e3:.2f} us "
+        f"(min {min(split_ms) * 1e3:.2f}, max {max(split_ms) * 1e3:.2f}); host enqueue {t_enqueue:.1f} ms "
+        f"vs GPU {total_ms:.1f} ms")
+
+    tokens = float(case.seq_lens.sum())
+    n_pages = int(((case.seq_lens + PAGE - 1) // PAGE).sum())
+    alg_bytes = cache_bytes + 4 * n_pages  # packed cache + page-table entries read by the split kernel
+    achieved = alg_bytes / (split_avg_ms * 1e-3) / 1e9
+    traffic = counters_for(kernel_source_sha(), args.workload)
+
+    cpu = None
+    if args.cpu_kv_heads > 0:
+        log("[bench] timing the oracle on the CPU ...")
+        cpu = cpu_baseline(case, pools[0].cpu().numpy(), args.cpu_kv_heads)
+
+    res = {
+        "metric": "INT2 decode attention KV-tokens/s + HBM GB/s (% peak), 8B GQA shape @128K",
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "KV-tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm_passes * steps,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int2 cache, f16 MFMA operands, f32 accumulate",
+        "data": "synthetic (seeded bf16 q/k/v with outlier key channels and per-channel offsets, random orthogonal R)",
+        "config": {
+            "workload": desc,
+            "batch": case.B, "num_q_heads": case.Hq, "num_kv_heads": case.Hkv, "head_dim": 128,
+            "context_tokens": int(tokens), "group_size": 32, "page_size": PAGE,
+            "page_table": "seeded permutation" if case.B == 1 else "seeded interleaved allocator",
+            "cache_replicas": n_rep, "num_splits": args.num_splits or "auto",
+        },
+        "hbm_gbps_step": cache_bytes / (ms_per_step * 1e-3) / 1e9,
+        "pct_peak_step": cache_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        "split_kernel_us": split_avg_ms * 1e3,
+        "host_enqueue_ms": t_enqueue,
+        "bulk_append_ms": bulk_ms,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS,
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

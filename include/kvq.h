@@ -44,7 +44,8 @@
  *     code without launching anything; kvq_last_error() then describes it.
  *     Kernels run asynchronously on `stream` (a hipStream_t; NULL = the null
  *     stream).  No call synchronises the device.  A launch failure returns
- *     KVQ_EHIP.
+ *     KVQ_EHIP (an error left pending by an earlier, unrelated HIP call is
+ *     cleared first and not reported).
  *   - The library never exits or aborts.  It holds no mutable global state
  *     besides per-thread error text and a cached compute-unit count.
  */
@@ -133,7 +134,9 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
  *   q           device [batch][num_q_heads][128] of q_dtype (KVQ_BF16 or KVQ_F32).
  *   page_table  device int32 [batch][max_pages]; entry i of row b is the page
  *               holding positions 16i..16i+15; entries for i < ceil(T/16) must
- *               be in [0, num_pages) (not checked on the device).
+ *               be in [0, num_pages).  The kernel never reads outside the pool:
+ *               a page id outside [0, num_pages) contributes no tokens, and a
+ *               length beyond max_pages*16 is cut there.
  *   seq_lens    device int32 [batch], each in [0, max_seq_len].
  *   max_seq_len host bound on seq_lens; must satisfy ceil(max_seq_len/16) <= max_pages.
  *   r_k, r_v    device fp32 [H_kv][128][128] as in kvq_quant_append.
@@ -153,6 +156,22 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const void* q, kvq_dtype q_dt
                            const int32_t* seq_lens, int32_t max_seq_len, const float* r_k, const float* r_v,
                            float sm_scale, void* out, kvq_dtype out_dtype, void* workspace,
                            size_t workspace_bytes, int32_t num_splits, void* stream);
+
+/*
+ * kvq_decode_attn_traced - kvq_decode_attn plus timing events for measurement.
+ * Identical arguments, results and errors; in addition, when non-NULL,
+ * `ev_begin` and `ev_end` (hipEvent_t created by the caller) are recorded on
+ * `stream` immediately before and after the split-K attention kernel, the
+ * call's dominant (HBM-streaming) kernel, so the caller can read its duration
+ * with hipEventElapsedTime.  Meant for eager launches: inside a stream capture
+ * the records only order the graph and give no timing.
+ */
+kvq_status kvq_decode_attn_traced(const kvq_cache* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
+                                  int32_t num_q_heads, const int32_t* page_table, int32_t max_pages,
+                                  const int32_t* seq_lens, int32_t max_seq_len, const float* r_k, const float* r_v,
+                                  float sm_scale, void* out, kvq_dtype out_dtype, void* workspace,
+                                  size_t workspace_bytes, int32_t num_splits, void* stream, void* ev_begin,
+                                  void* ev_end);
 
 /* Page-table policies for kvq_page_table. */
 typedef enum {

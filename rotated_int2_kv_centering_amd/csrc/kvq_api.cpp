@@ -161,6 +161,17 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const void* q, kvq_dtype q_dt
                            const int32_t* seq_lens, int32_t max_seq_len, const float* r_k, const float* r_v,
                            float sm_scale, void* out, kvq_dtype out_dtype, void* workspace, size_t workspace_bytes_,
                            int32_t num_splits, void* stream) {
+  return kvq_decode_attn_traced(cache, q, q_dtype, batch, num_q_heads, page_table, max_pages, seq_lens, max_seq_len,
+                                r_k, r_v, sm_scale, out, out_dtype, workspace, workspace_bytes_, num_splits, stream,
+                                nullptr, nullptr);
+}
+
+kvq_status kvq_decode_attn_traced(const kvq_cache* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
+                                  int32_t num_q_heads, const int32_t* page_table, int32_t max_pages,
+                                  const int32_t* seq_lens, int32_t max_seq_len, const float* r_k, const float* r_v,
+                                  float sm_scale, void* out, kvq_dtype out_dtype, void* workspace,
+                                  size_t workspace_bytes_, int32_t num_splits, void* stream, void* ev_begin,
+                                  void* ev_end) {
   kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
   if (batch < 0) return fail(KVQ_EINVAL, "batch=%d must be >= 0", batch);
@@ -214,7 +225,8 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const void* q, kvq_dtype q_dt
   a.out_kind = out_dtype == KVQ_BF16 ? 0 : 1;
   a.qhat = static_cast<float*>(workspace);
   a.part = a.qhat + static_cast<size_t>(batch) * num_q_heads * kRowStride;
-  hipError_t e = kvq::launch_decode(a, plan, static_cast<hipStream_t>(stream));
+  hipError_t e = kvq::launch_decode(a, plan, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_begin),
+                                    static_cast<hipEvent_t>(ev_end));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return KVQ_OK;
 }

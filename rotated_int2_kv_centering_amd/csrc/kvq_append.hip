@@ -140,6 +140,7 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
                          float* rot_out, hipStream_t stream) {
   const dim3 grid((n_tokens + kAppendTile - 1) / kAppendTile, num_kv_heads, 2);
   const dim3 block(128);
+  (void)hipGetLastError();  // report only this call's launch errors, not stale ones
   switch (in_kind) {
     case 0:
       hipLaunchKernelGGL(append_kernel<0>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,

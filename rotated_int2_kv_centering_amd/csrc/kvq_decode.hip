@@ -402,8 +402,10 @@ static void launch_split(const DecodeArgs& a, const DecodePlan& plan, int g, hip
                      a.max_pages, a.seq_lens, a.num_q_heads, g, plan.pages_per_split, plan.n_splits, a.part);
 }
 
-hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream, hipEvent_t ev_begin,
+                         hipEvent_t ev_end) {
   const int g = a.num_q_heads / a.num_kv_heads;
+  (void)hipGetLastError();  // report only this call's launch errors, not stale ones
   const dim3 qgrid(a.batch * a.num_q_heads);
   if (a.q_kind == 0)
     hipLaunchKernelGGL(qrot_kernel<0>, qgrid, dim3(128), 0, stream, a.q, a.r_k, a.num_q_heads, g, a.logit_scale,
@@ -414,6 +416,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
+  if (ev_begin != nullptr && (err = hipEventRecord(ev_begin, stream)) != hipSuccess) return err;
   if (g <= 4)
     launch_split<1>(a, plan, g, stream);
   else if (g <= 8)
@@ -422,6 +425,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_
     launch_split<4>(a, plan, g, stream);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (ev_end != nullptr && (err = hipEventRecord(ev_end, stream)) != hipSuccess) return err;
 
   const dim3 mgrid(a.num_kv_heads, a.batch);
   if (a.out_kind == 0)

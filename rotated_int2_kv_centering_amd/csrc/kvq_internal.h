@@ -36,6 +36,7 @@ struct DecodeArgs {
   float* part;   // workspace: [batch][num_q_heads][n_splits][kPartStride]
 };
 
-hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream, hipEvent_t ev_begin,
+                         hipEvent_t ev_end);
 
 }  // namespace kvq

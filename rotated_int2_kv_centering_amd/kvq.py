@@ -64,6 +64,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_decode_workspace_bytes.restype = SZ
     lib.kvq_decode_attn.argtypes = [CP, P, I32, I32, I32, P, I32, P, I32, P, P, F, P, I32, P, SZ, I32, P]
     lib.kvq_decode_attn.restype = I32
+    lib.kvq_decode_attn_traced.argtypes = [CP, P, I32, I32, I32, P, I32, P, I32, P, P, F, P, I32, P, SZ, I32, P, P, P]
+    lib.kvq_decode_attn_traced.restype = I32
     lib.kvq_page_table.argtypes = [I32, U64, P, I32, I32, I32, I32, P, P]
     lib.kvq_page_table.restype = I32
     lib.kvq_last_error.argtypes = []
@@ -136,6 +138,17 @@ def kvq_decode_attn(cache: kvq_cache, q, q_dtype: int, batch: int, num_q_heads: 
                                   max_pages, _ptr(seq_lens), max_seq_len, _ptr(r_k), _ptr(r_v), float(sm_scale),
                                   _ptr(out), out_dtype, _ptr(workspace), int(workspace_bytes), num_splits,
                                   _stream(stream)))
+
+
+def kvq_decode_attn_traced(cache: kvq_cache, q, q_dtype: int, batch: int, num_q_heads: int, page_table,
+                           max_pages: int, seq_lens, max_seq_len: int, r_k, r_v, sm_scale: float, out, out_dtype: int,
+                           workspace, workspace_bytes: int, num_splits: int = 0, stream=None, ev_begin=None,
+                           ev_end=None) -> None:
+    """``ev_begin``/``ev_end`` are raw hipEvent_t addresses (or None)."""
+    _check(load().kvq_decode_attn_traced(ctypes.byref(cache), _ptr(q), q_dtype, batch, num_q_heads, _ptr(page_table),
+                                         max_pages, _ptr(seq_lens), max_seq_len, _ptr(r_k), _ptr(r_v),
+                                         float(sm_scale), _ptr(out), out_dtype, _ptr(workspace), int(workspace_bytes),
+                                         num_splits, _stream(stream), ev_begin, ev_end))
 
 
 def kvq_page_table(policy: int, seed: int, seq_lens, page_size: int, num_pages: int, max_pages: int, table=None):
