@@ -214,7 +214,7 @@ def main() -> int:
     seq = T(case.seq_lens)
     max_seq = int(case.seq_lens.max())
     ws_bytes = kvq.kvq_decode_workspace_bytes(case.B, case.Hq, case.Hkv, max_seq, args.num_splits)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     outs = [torch.empty((case.B, case.Hq, 128), dtype=torch.bfloat16, device=dev) for _ in range(n_rep)]
 
     def step(r, ev_b=None, ev_e=None):

@@ -118,6 +118,11 @@ kvq_status kvq_quant_append(const kvq_cache* cache, const void* k, const void* v
  * kvq_decode_workspace_bytes - device workspace needed by kvq_decode_attn for
  * the same (batch, num_q_heads, num_kv_heads, max_seq_len, num_splits).
  * num_splits 0 selects the automatic split plan.  Returns 0 on invalid input.
+ * The workspace holds per-(sequence, KV head) ticket counters and the split
+ * partials.  It must be zero-filled before its first use; every completed
+ * call leaves the counters at zero again, so a workspace is then reusable
+ * without clearing.  Calls that share one workspace must not overlap in time
+ * (same stream, or ordered by events).
  */
 size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t max_seq_len, int32_t num_splits);
@@ -145,9 +150,16 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
  *               KVQ_F32).  The bf16 output is the fp32 result rounded to
  *               nearest even.
  *   workspace   device, >= kvq_decode_workspace_bytes(...) bytes, 16-byte
- *               aligned; scratch for the split partials, overwritten.
- *   num_splits  0 = automatic; otherwise the number of sequence splits per
- *               (sequence, KV head), >= 1.
+ *               aligned, zero-filled before first use (see above).
+ *   num_splits  0 = automatic; otherwise the requested number of sequence
+ *               splits per (sequence, KV head).  The kernel caps a split at
+ *               2048 pages and uses at most 512 splits, so the count used can
+ *               differ; kvq_decode_workspace_bytes follows the same plan.
+ * Work decomposition: one kernel launch; one workgroup per compute unit
+ * (12 waves for g <= 4, else 4) streams a split's pages, and the last
+ * workgroup of each (sequence, KV head) merges the split partials
+ * (log-sum-exp) and applies R_V^T.
+ * Limits: max_seq_len <= 16777216 (512 splits x 2048 pages x 16 tokens).
  * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ENOSPACE (workspace too small),
  * KVQ_EHIP.  batch == 0 is a no-op.
  */

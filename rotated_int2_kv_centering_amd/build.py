@@ -19,10 +19,13 @@ SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip"]
 ARCH = "gfx950"
 
 # hipcc flags: no fast-math (the quantizer needs IEEE fp32 division and
-# round-to-nearest-even); packed fp32 instructions disabled in device code.
+# round-to-nearest-even); packed fp32 instructions disabled in device code;
+# MFMA accumulators in VGPRs (the online-softmax rescale works on them with
+# VALU ops, which cannot read AGPRs).
 HIP_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -37,9 +37,12 @@ constexpr int kHeadDim = 128;
 constexpr int kGroup = 32;
 constexpr int kPage = 16;
 constexpr size_t kBlockBytes = 1536;
-constexpr int kRowStride = 132;  // floats per q_hat row and per split partial
+constexpr int kRowStride = 132;  // floats per split partial (acc[128], max, sum, pad)
 constexpr int kMaxGroup = 16;
 constexpr int kMinPagesPerSplit = 8;
+constexpr int kMaxPagesPerSplit = 2048;  // page ids of one split staged in LDS
+constexpr int kMaxSplits = 512;         // merge weights of one (sequence, KV head) staged in LDS
+constexpr long long kMaxContext = static_cast<long long>(kMaxPagesPerSplit) * kMaxSplits * kPage;
 
 kvq_status check_cache(const kvq_cache* c) {
   if (c == nullptr) return fail(KVQ_EINVAL, "cache is NULL");
@@ -79,28 +82,39 @@ int device_cu_count() {
   return cache[dev];
 }
 
-bool make_plan(int batch, int num_kv_heads, int max_seq_len, int num_splits, kvq::DecodePlan* plan) {
+// Decode workgroups per compute unit: each workgroup has as many waves as a
+// compute unit holds for its group size (12 for g <= 4, else 4).
+int workgroups_per_cu(int) { return 1; }
+
+bool make_plan(int batch, int num_kv_heads, int g, int max_seq_len, int num_splits, kvq::DecodePlan* plan) {
   if (batch < 0 || num_kv_heads < 1 || max_seq_len < 0 || num_splits < 0) return false;
+  if (max_seq_len > kMaxContext) return false;
   const int n_pages = (max_seq_len + kPage - 1) / kPage;
   plan->n_pages_max = n_pages;
+  long long pps;
   if (num_splits > 0) {
-    plan->pages_per_split = std::max(1, (n_pages + num_splits - 1) / num_splits);
-    plan->n_splits = num_splits;
+    pps = (std::max(n_pages, 1) + num_splits - 1) / num_splits;
   } else {
-    // Aim at two 4-wave workgroups per compute unit over all (sequence, KV head).
-    const long long target = 2LL * device_cu_count();
+    // One resident wave of workgroups over all (sequence, KV head).
+    const long long target = static_cast<long long>(workgroups_per_cu(g)) * device_cu_count();
     const long long work = static_cast<long long>(std::max(batch, 1)) * num_kv_heads * std::max(n_pages, 1);
-    long long pps = (work + target - 1) / target;
-    pps = std::max<long long>(pps, kMinPagesPerSplit);
-    plan->pages_per_split = static_cast<int>(std::min<long long>(pps, std::max(n_pages, 1)));
-    plan->n_splits = std::max(1, (n_pages + plan->pages_per_split - 1) / plan->pages_per_split);
+    pps = std::max<long long>((work + target - 1) / target, kMinPagesPerSplit);
   }
+  pps = std::max<long long>(pps, (n_pages + kMaxSplits - 1) / kMaxSplits);
+  pps = std::min<long long>(pps, kMaxPagesPerSplit);
+  pps = std::max<long long>(1, std::min<long long>(pps, std::max(n_pages, 1)));
+  plan->pages_per_split = static_cast<int>(pps);
+  plan->n_splits = std::max(1, (n_pages + plan->pages_per_split - 1) / plan->pages_per_split);
   return true;
 }
 
-size_t workspace_bytes(int batch, int num_q_heads, const kvq::DecodePlan& plan) {
-  const size_t rows = static_cast<size_t>(batch) * num_q_heads;
-  return sizeof(float) * (rows * kRowStride + rows * static_cast<size_t>(plan.n_splits) * kRowStride);
+size_t counters_bytes(int batch, int num_kv_heads) {
+  return (static_cast<size_t>(batch) * num_kv_heads * sizeof(int32_t) + 255) / 256 * 256;
+}
+
+size_t workspace_bytes(int batch, int num_q_heads, int num_kv_heads, const kvq::DecodePlan& plan) {
+  return counters_bytes(batch, num_kv_heads) +
+         sizeof(float) * static_cast<size_t>(batch) * num_q_heads * plan.n_splits * kRowStride;
 }
 
 // splitmix64 (Steele, Lea, Flood 2014) as the page allocator's random stream.
@@ -152,8 +166,8 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
                                   int32_t num_splits) {
   if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0) return 0;
   kvq::DecodePlan plan;
-  if (!make_plan(batch, num_kv_heads, max_seq_len, num_splits, &plan)) return 0;
-  return workspace_bytes(batch, num_q_heads, plan);
+  if (!make_plan(batch, num_kv_heads, num_q_heads / num_kv_heads, max_seq_len, num_splits, &plan)) return 0;
+  return workspace_bytes(batch, num_q_heads, num_kv_heads, plan);
 }
 
 kvq_status kvq_decode_attn(const kvq_cache* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
@@ -197,17 +211,19 @@ kvq_status kvq_decode_attn_traced(const kvq_cache* cache, const void* q, kvq_dty
   if (static_cast<long long>(batch) * num_q_heads > 0x7fffffffLL / kRowStride)
     return fail(KVQ_EUNSUPPORTED, "batch * num_q_heads too large");
 
+  if (max_seq_len > kMaxContext)
+    return fail(KVQ_EUNSUPPORTED, "max_seq_len=%d exceeds the supported %lld", max_seq_len, kMaxContext);
   kvq::DecodePlan plan;
-  if (!make_plan(batch, cache->num_kv_heads, max_seq_len, num_splits, &plan))
+  if (!make_plan(batch, cache->num_kv_heads, g, max_seq_len, num_splits, &plan))
     return fail(KVQ_EINVAL, "cannot plan the decode split");
-  const size_t need = workspace_bytes(batch, num_q_heads, plan);
+  const size_t need = workspace_bytes(batch, num_q_heads, cache->num_kv_heads, plan);
   if (workspace_bytes_ < need)
     return fail(KVQ_ENOSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes_, need);
-  if (plan.n_splits > 65535) return fail(KVQ_EUNSUPPORTED, "too many splits (%d)", plan.n_splits);
-  if (batch > 65535 || cache->num_kv_heads > 65535) return fail(KVQ_EUNSUPPORTED, "batch or num_kv_heads too large");
+  if (static_cast<long long>(batch) * cache->num_kv_heads * plan.n_splits > 0x7fffffffLL)
+    return fail(KVQ_EUNSUPPORTED, "grid too large");
 
   const float scale = sm_scale == 0.0f ? 1.0f / std::sqrt(static_cast<float>(kHeadDim)) : sm_scale;
-  kvq::DecodeArgs a;
+  kvq::DecodeParams a;
   a.pool = static_cast<const uint8_t*>(cache->pool);
   a.num_kv_heads = cache->num_kv_heads;
   a.num_pages = cache->num_pages;
@@ -215,6 +231,7 @@ kvq_status kvq_decode_attn_traced(const kvq_cache* cache, const void* q, kvq_dty
   a.q_kind = q_dtype == KVQ_BF16 ? 0 : 1;
   a.batch = batch;
   a.num_q_heads = num_q_heads;
+  a.g = g;
   a.page_table = page_table;
   a.max_pages = max_pages;
   a.seq_lens = seq_lens;
@@ -223,9 +240,11 @@ kvq_status kvq_decode_attn_traced(const kvq_cache* cache, const void* q, kvq_dty
   a.logit_scale = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);  // log2(e)
   a.out = out;
   a.out_kind = out_dtype == KVQ_BF16 ? 0 : 1;
-  a.qhat = static_cast<float*>(workspace);
-  a.part = a.qhat + static_cast<size_t>(batch) * num_q_heads * kRowStride;
-  hipError_t e = kvq::launch_decode(a, plan, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_begin),
+  a.counters = static_cast<int32_t*>(workspace);
+  a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + counters_bytes(batch, cache->num_kv_heads));
+  a.pages_per_split = plan.pages_per_split;
+  a.n_splits = plan.n_splits;
+  hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_begin),
                                     static_cast<hipEvent_t>(ev_end));
   if (e != hipSuccess) return hip_fail(e, "decode launch");
   return KVQ_OK;

@@ -1,4 +1,4 @@
-// Decode attention read straight from the packed INT2 cache.
+// Decode attention read straight from the packed INT2 cache, in one kernel.
 //
 // OptR ("Output-Oriented Rotation for INT2 KV-Cache Quantization"), section 3,
 // Eq. (1)-(2) and section 3.2, Eq. (5): softmax attention of each query head
@@ -7,14 +7,24 @@
 // (q_hat = q R_K), logits are <q_hat, x_hat_s>, the value sum is formed in the
 // rotated basis and mapped back once with R_V^T (section 3.1, Eq. (4)).
 //
-// Three kernels per call:
-//   qrot_kernel   q_hat = q R_K * sm_scale * log2(e)  (fp32), plus a power of
-//                 two that brings max|q_hat| into [2^13, 2^14) for fp16.
-//   split_kernel  one workgroup (4 waves) per (split, KV head, sequence); each
-//                 wave streams page pairs, forms logits and the P.V product on
-//                 the matrix cores, keeps an online softmax, and the waves
-//                 merge through LDS into one partial (max, sum, acc[128]).
-//   merge_kernel  log-sum-exp merge of the partials, divide, o = o_rot R_V^T.
+// Work decomposition.  One workgroup of kW waves per (split, KV head h,
+// sequence b), sized so that one workgroup fills a compute unit; a split is a
+// contiguous range of the sequence's pages.  The workgroups of one KV head are
+// consecutive in the flattened grid with h fastest, so on an 8-XCD part the
+// workgroups of one KV head share an XCD's L2.
+//   prologue   load the split's page ids, the g query rows and R_K together;
+//              start streaming the first page pairs; compute
+//              q_hat = q R_K * sm_scale * log2(e) (fp32) and a per-head power
+//              of two f that brings max|q_hat*f| into [2^13, 2^14).
+//   main loop  wave w takes page pairs w, w+kW, ...: each pair is copied by
+//              direct global->LDS loads into a ring of kDepth slots per wave
+//              (kDepth - 1 pairs in flight while one is computed); logits and
+//              P.V run on the matrix cores, the online softmax in fp32.
+//   epilogue   the kW waves merge through LDS into one partial (max, sum,
+//              acc[128]) stored to the workspace with agent-scope (cross-XCD
+//              coherent) stores; the last workgroup of the (sequence, KV head)
+//              (atomic ticket) merges all partials with log-sum-exp weights,
+//              divides, applies R_V^T and stores the output.
 //
 // Logits on the matrix cores (per page, per quad of query heads).  A group's
 // dequantized key is z + s*c with codes c in {0..3}, so
@@ -24,7 +34,7 @@
 // column n = 4*grp + j holds q_hat_j on group grp's channels and 0 elsewhere,
 // so the four chunks of 32 channels fill all 16 columns.  Codes enter as the
 // raw fp16 bit patterns c (subnormals c * 2^-24, exact in the MFMA); the
-// query enters as an fp16 hi/lo pair of q_hat * 2^k, so the products carry
+// query enters as an fp16 hi/lo pair of q_hat * f, so the products carry
 // about 22 bits.  The per-group scale/zero are applied in fp32 and the 4
 // groups summed with two DPP row rotations.
 // P.V on the matrix cores (per page pair).  A = p * s_v as fp16 with rows
@@ -40,70 +50,213 @@ namespace kvq {
 
 constexpr float kNegBig = -3.0e38f;  // finite "minus infinity" for running maxima
 constexpr float kTwo24 = 16777216.0f;
+#ifndef KVQ_RING_DEPTH
+#define KVQ_RING_DEPTH 3
+#endif
+// Page pairs per wave staged in LDS by direct global->LDS loads; kDepth - 1
+// pairs are in flight while one is computed.
+constexpr int kDepth = KVQ_RING_DEPTH;
+constexpr int kDmaPerPair = 4;  // K/V codes of page 0, of page 1; metadata of page 0, of page 1
+static_assert(kDepth >= 2 && kDepth <= 4, "ring depth 2..4");
 
-// --------------------------------------------------------------- q rotation
-template <int kQIn>  // 0 bf16, 1 fp32
-__global__ __launch_bounds__(128) void qrot_kernel(const void* __restrict__ q, const float* __restrict__ r_k,
-                                                   int num_q_heads, int g, float logit_scale,
-                                                   float* __restrict__ qhat) {
-  const int row = blockIdx.x;  // b * num_q_heads + j
-  const int j = row % num_q_heads;
-  const int h = j / g;
-  const int c = threadIdx.x;
-  __shared__ float qs[kHeadDim];
-  __shared__ float wmax[2];
-  const size_t base = static_cast<size_t>(row) * kHeadDim;
-  qs[c] = kQIn == 0 ? bf16_bits_to_f32(static_cast<const uint16_t*>(q)[base + c]) : static_cast<const float*>(q)[base + c];
-  __syncthreads();
-  const float* R = r_k + static_cast<size_t>(h) * kHeadDim * kHeadDim;
-  float acc = 0.0f;
-  for (int i = 0; i < kHeadDim; ++i) acc = fmaf(qs[i], R[i * kHeadDim + c], acc);
-  acc *= logit_scale;
-  float am = fabsf(acc);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
-  if ((c & 63) == 0) wmax[c >> 6] = am;
-  __syncthreads();
-  am = fmaxf(wmax[0], wmax[1]);
-  float* dst = qhat + static_cast<size_t>(row) * kQhatStride;
-  dst[c] = acc;
-  if (c == 0) {
-    int e = 0;
-    frexpf(am, &e);  // am in [2^(e-1), 2^e)
-    dst[128] = am > 0.0f ? ldexpf(1.0f, 14 - e) : 1.0f;
-  }
+// Waves per workgroup and waves per SIMD the kernel is compiled for, by the
+// number of head quads: the g <= 4 kernel fits 3 waves per SIMD, so one
+// 12-wave workgroup fills a compute unit; the larger ones run 1 wave per SIMD.
+template <int kNQ> struct DecodeShape { static constexpr int waves = 4, waves_per_simd = 1; };
+template <> struct DecodeShape<1> { static constexpr int waves = 12, waves_per_simd = 3; };
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory straight into LDS: lane l reads
+// base + voff (base wave-uniform, in SGPRs) and its bytes land at lds + 16*l
+// (global_load_lds_dwordx4, LDS base in M0).  Issued as inline asm so the
+// compiler adds none of its own (whole-queue) waits for it; every read of a
+// ring slot is preceded by an explicit vmcnt wait instead.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, void* lds) {
+  const uint32_t lds_addr =
+      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(lds))));
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
+template <int kN>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kN) : "memory");
 }
 
-// ------------------------------------------------------------- split kernel
-template <int kNQ>  // quads of query heads per KV head: g <= 4 * kNQ
-__global__ __launch_bounds__(256) void split_kernel(const uint8_t* __restrict__ pool, int num_kv_heads,
-                                                    int num_pages, const float* __restrict__ qhat,
-                                                    const int32_t* __restrict__ page_table, int max_pages,
-                                                    const int32_t* __restrict__ seq_lens, int num_q_heads, int g,
-                                                    int pages_per_split, int n_splits, float* __restrict__ part) {
+struct PagePair {
+  uint4v rec0, rec1, km0, vm0, km1, vm1;
+};
+
+// Coherent (agent-scope) load of a value another workgroup stored with an agent-scope store.
+__device__ __forceinline__ float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int kNQ, int kW>  // quads of query heads (g <= 4 * kNQ), waves per workgroup
+__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(DecodeShape<kNQ>::waves_per_simd)))
+void decode_kernel(const DecodeParams p) {
   constexpr int kNH = 4 * kNQ;
-  __shared__ float s_acc[4][kNH][kHeadDim];
-  __shared__ float s_m[4][kNH];
-  __shared__ float s_l[4][kNH];
+  constexpr int kThreads = 64 * kW;
+  __shared__ int s_pages[kMaxPagesPerSplit];
+  __shared__ float s_q[kNH][kHeadDim];        // q rows -> q_hat -> o_rot
+  __shared__ float s_buf[kW][kNH][kHeadDim];  // q_hat parts / per-wave partials / merge weights / R_V^T parts
+  __shared__ float s_f[kNH];
+  __shared__ float s_m[kW][kNH];
+  __shared__ float s_l[kW][kNH];
+  __shared__ int s_ticket;
+  // One LDS object per ring slot (distinct objects: loads into one slot never
+  // alias reads of another): [wave][part][lane], part 0/1 = 64 x 16 B codes
+  // of page 0/1, part 2 = 32 x 16 B metadata of page 0 then of page 1.
+  __shared__ uint4v s_ring0[kW][3][64];
+  __shared__ uint4v s_ring1[kW][3][64];
+  __shared__ uint4v s_ring2[kDepth > 2 ? kW : 1][3][64];
+  __shared__ uint4v s_ring3[kDepth > 3 ? kW : 1][3][64];
 
-  const int split = blockIdx.x;
-  const int h = blockIdx.y;
-  const int b = blockIdx.z;
-  // Pages past the table row are never read (a length beyond max_pages*16 is cut).
-  const int T = min(seq_lens[b], max_pages * kPage);
-  const int n_pages = (T + kPage - 1) / kPage;
-  const int p0 = split * pages_per_split;
-  if (p0 >= n_pages) return;  // whole workgroup
-  const int p1 = min(p0 + pages_per_split, n_pages);
-  const int npairs = (p1 - p0 + 1) >> 1;
-
+  const int H = p.num_kv_heads;
+  const int g = p.g;
+  const int id = blockIdx.x;
+  const int h = id % H;
+  const int split = (id / H) % p.n_splits;
+  const int b = id / (H * p.n_splits);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
+  auto ring = [&](int slot) -> uint4v(*)[64] {
+    return slot == 0 ? s_ring0[wave] : slot == 1 ? s_ring1[wave] : slot == 2 ? s_ring2[wave] : s_ring3[wave];
+  };
+
+  // Pages past the table row are never read (a length beyond max_pages*16 is cut).
+  const int T = min(p.seq_lens[b], p.max_pages * kPage);
+  const int n_pages = T > 0 ? (T + kPage - 1) / kPage : 0;
+  const size_t out_row0 = static_cast<size_t>(b) * p.num_q_heads + static_cast<size_t>(h) * g;
+  if (n_pages == 0) {  // nothing to attend to: zero output, written once
+    if (split == 0) {
+      for (int idx = tid; idx < g * kHeadDim; idx += kThreads) {
+        if (p.out_kind == 0)
+          static_cast<uint16_t*>(p.out)[out_row0 * kHeadDim + idx] = 0;
+        else
+          static_cast<float*>(p.out)[out_row0 * kHeadDim + idx] = 0.0f;
+      }
+    }
+    return;
+  }
+  const int pps = p.pages_per_split;
+  const int n_valid = (n_pages + pps - 1) / pps;
+  const int p0 = split * pps;
+  if (p0 >= n_pages) return;  // whole workgroup
+  const int np = min(pps, n_pages - p0);
+  const int npairs = (np + 1) >> 1;
+
+  // ---- prologue loads, all issued before the first wait: this split's page
+  // ids, the g query rows and R_K.  Indices are clamped in bounds and values
+  // selected afterwards, so every load issues unconditionally.
+  constexpr int kPidPerThread = (kMaxPagesPerSplit + kThreads - 1) / kThreads;
+  const int32_t* pt = p.page_table + static_cast<size_t>(b) * p.max_pages + p0;
+  int pid[kPidPerThread];
+#pragma unroll
+  for (int u = 0; u < kPidPerThread; ++u) pid[u] = pt[min(tid + u * kThreads, np - 1)];
+  constexpr int kQPerThread = (kNH * kHeadDim + kThreads - 1) / kThreads;
+  float qld[kQPerThread];
+#pragma unroll
+  for (int u = 0; u < kQPerThread; ++u) {
+    const int idx = min(tid + u * kThreads, kNH * kHeadDim - 1);
+    const int jh = idx / kHeadDim;
+    const size_t qi = (out_row0 + min(jh, g - 1)) * kHeadDim + idx % kHeadDim;
+    const float qraw = p.q_kind == 0 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[qi])
+                                     : static_cast<const float*>(p.q)[qi];
+    qld[u] = jh < g ? qraw : 0.0f;
+  }
+  // q_hat partial sums: thread (column rc, part rpart) takes rows
+  // [kRows * rpart, +kRows) of R_K; threads past the last part repeat it.
+  constexpr int kParts = kThreads >= 4 * kHeadDim ? 4 : kThreads / kHeadDim;
+  constexpr int kRows = kHeadDim / kParts;
+  static_assert(kParts >= 1 && kParts <= kW, "row parts fit in s_buf");
+  const int rc = tid & (kHeadDim - 1);
+  const int rpart = min(tid / kHeadDim, kParts - 1);
+  float rv[kRows];
+  {
+    const float* R = p.r_k + (static_cast<size_t>(h) * kHeadDim + kRows * rpart) * kHeadDim + rc;
+#pragma unroll
+    for (int ii = 0; ii < kRows; ++ii) rv[ii] = R[ii * kHeadDim];
+  }
+#pragma unroll
+  for (int u = 0; u < kPidPerThread; ++u) {
+    const int i = tid + u * kThreads;
+    if (i < np) s_pages[i] = (pid[u] >= 0 && pid[u] < p.num_pages) ? pid[u] : -1;  // outside the pool: masked
+  }
+#pragma unroll
+  for (int u = 0; u < kQPerThread; ++u) {
+    const int idx = tid + u * kThreads;
+    if (idx < kNH * kHeadDim) s_q[idx / kHeadDim][idx % kHeadDim] = qld[u];
+  }
+  __syncthreads();
+
   const int a = lane >> 4;    // row of 16 lanes: token quad (QK) / channel octet
   const int col = lane & 15;  // MFMA column: 4*grp + jj
   const int grp = col >> 2;
   const int jj = col & 3;
+  const int meta_off = kMetaRecordBytes * (4 * grp + a);  // within a page's metadata
+  const uint8_t* pool_h = p.pool + static_cast<size_t>(h) * kBlockBytes;
+  const size_t page_stride = static_cast<size_t>(H) * kBlockBytes;
+
+  auto issue = [&](int slot, int pair) {
+    const int i0 = 2 * pair;
+    // page ids are wave-uniform: block addresses live in scalar registers
+    const int ph0 = __builtin_amdgcn_readfirstlane(s_pages[i0]);
+    const int ph1 = __builtin_amdgcn_readfirstlane(i0 + 1 < np ? s_pages[i0 + 1] : -1);
+    // a masked page reads page 0 (in bounds) and contributes no tokens
+    const uint8_t* blk0 = pool_h + static_cast<size_t>(ph0 < 0 ? 0 : ph0) * page_stride;
+    const uint8_t* blk1 = ph1 < 0 ? blk0 : pool_h + static_cast<size_t>(ph1) * page_stride;
+    uint4v(*r)[64] = ring(slot);
+    dma16(blk0, 16 * lane, &r[0][0]);
+    dma16(blk1, 16 * lane, &r[1][0]);
+    // metadata: lanes 0..31 take page 0's 512 B, lanes 32..63 page 1's
+    if (lane < 32)
+      dma16(blk0, kCodeBytes + 16 * lane, &r[2][0]);
+    else
+      dma16(blk1, kCodeBytes - 512 + 16 * lane, &r[2][0]);
+  };
+
+  // Every wave keeps kDepth - 1 page pairs in flight ahead of the one it
+  // computes (indices clamped to the last pair, so the wait counts are static;
+  // a wave near the end loads the last pair again and never uses it).
+#pragma unroll
+  for (int d = 0; d < kDepth - 1; ++d) issue(d, min(wave + kW * d, npairs - 1));
+
+  // ---- q_hat for the g query heads of this KV head
+  if (tid < kParts * kHeadDim) {
+    float accq[kNH];
+#pragma unroll
+    for (int jh = 0; jh < kNH; ++jh) accq[jh] = 0.0f;
+#pragma unroll
+    for (int ii = 0; ii < kRows; ++ii) {
+#pragma unroll
+      for (int jh = 0; jh < kNH; ++jh) accq[jh] = fmaf(s_q[jh][kRows * rpart + ii], rv[ii], accq[jh]);
+    }
+#pragma unroll
+    for (int jh = 0; jh < kNH; ++jh) s_buf[rpart][jh][rc] = accq[jh];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < kNH * kHeadDim; idx += kThreads) {
+    const int jh = idx / kHeadDim;
+    const int c = idx % kHeadDim;
+    float sum = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kParts; ++u) sum += s_buf[u][jh][c];
+    s_q[jh][c] = sum * p.logit_scale;
+  }
+  __syncthreads();
+  for (int jh = wave; jh < kNH; jh += kW) {
+    float am = fmaxf(fabsf(s_q[jh][lane]), fabsf(s_q[jh][lane + 64]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+    if (lane == 0) {
+      int e = 0;
+      frexpf(am, &e);  // am in [2^(e-1), 2^e)
+      s_f[jh] = am > 0.0f ? ldexpf(1.0f, 14 - e) : 1.0f;
+    }
+  }
+  __syncthreads();
 
   // ---- block-diagonal query operands (fp16 hi/lo of q_hat * f)
   half8 qhi[kNQ][4], qlo[kNQ][4];
@@ -111,30 +264,17 @@ __global__ __launch_bounds__(256) void split_kernel(const uint8_t* __restrict__ 
 #pragma unroll
   for (int Q = 0; Q < kNQ; ++Q) {
     const int jl = 4 * Q + jj;
-    float qv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qv[e] = 0.0f;
-    float f = 1.0f;
-    if (jl < g) {
-      const float* row = qhat + (static_cast<size_t>(b) * num_q_heads + h * g + jl) * kQhatStride;
-      f = row[128];
-      const float4v u0 = *reinterpret_cast<const float4v*>(row + 32 * grp + 8 * a);
-      const float4v u1 = *reinterpret_cast<const float4v*>(row + 32 * grp + 8 * a + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qv[e] = u0[e];
-        qv[e + 4] = u1[e];
-      }
-    }
+    const float f = s_f[jl];
     half8 hi, lo;
     float qsum = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float sc = qv[e] * f;
+      const float qv = s_q[jl][32 * grp + 8 * a + e];
+      const float sc = qv * f;
       const _Float16 hh = static_cast<_Float16>(sc);
       hi[e] = hh;
       lo[e] = static_cast<_Float16>(sc - static_cast<float>(hh));
-      qsum += qv[e];
+      qsum += qv;
     }
     qsum = rows_sum(qsum);  // sum of q_hat over group grp's 32 channels
     c1[Q] = kTwo24 / f;
@@ -158,42 +298,35 @@ __global__ __launch_bounds__(256) void split_kernel(const uint8_t* __restrict__ 
     for (int t = 0; t < 8; ++t) acc[Q][t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
   }
 
-  const int32_t* pt = page_table + static_cast<size_t>(b) * max_pages;
-  const int meta_off = kCodeBytes + kMetaRecordBytes * (4 * grp + a);
-
-  for (int pair = wave; pair < npairs; pair += 4) {
-    const int lp0 = p0 + 2 * pair;
-    int ph0 = pt[lp0];
-    int ph1 = lp0 + 1 < p1 ? pt[lp0 + 1] : ph0;
-    // A page id outside the pool is read as page 0 and all its tokens are masked.
-    const bool ok0 = ph0 >= 0 && ph0 < num_pages;
-    const bool has1 = lp0 + 1 < p1 && ph1 >= 0 && ph1 < num_pages;
-    ph0 = ok0 ? ph0 : 0;
-    ph1 = has1 ? ph1 : ph0;
-    const uint8_t* blk0 = pool + (static_cast<size_t>(ph0) * num_kv_heads + h) * kBlockBytes;
-    const uint8_t* blk1 = pool + (static_cast<size_t>(ph1) * num_kv_heads + h) * kBlockBytes;
-    const uint4v rec0 = *reinterpret_cast<const uint4v*>(blk0 + 16 * lane);
-    const uint4v rec1 = *reinterpret_cast<const uint4v*>(blk1 + 16 * lane);
-    const uint4v km0 = *reinterpret_cast<const uint4v*>(blk0 + meta_off);
-    const uint4v vm0 = *reinterpret_cast<const uint4v*>(blk0 + meta_off + 16);
-    const uint4v km1 = *reinterpret_cast<const uint4v*>(blk1 + meta_off);
-    const uint4v vm1 = *reinterpret_cast<const uint4v*>(blk1 + meta_off + 16);
-
-    // ---- logits (log2 units, divided by c1) for both pages
+  auto compute = [&](int slot, int pair) {
+    wait_vmcnt<kDmaPerPair * (kDepth - 1)>();  // this slot's loads have landed
+    PagePair P;
+    uint4v(*r)[64] = ring(slot);
+    P.rec0 = r[0][lane];
+    P.rec1 = r[1][lane];
+    const uint8_t* meta = reinterpret_cast<const uint8_t*>(&r[2][0]);
+    P.km0 = *reinterpret_cast<const uint4v*>(meta + meta_off);
+    P.vm0 = *reinterpret_cast<const uint4v*>(meta + meta_off + 16);
+    P.km1 = *reinterpret_cast<const uint4v*>(meta + 512 + meta_off);
+    P.vm1 = *reinterpret_cast<const uint4v*>(meta + 512 + meta_off + 16);
+    const int i0 = 2 * pair;
+    const bool ok0 = s_pages[i0] >= 0;
+    const bool has1 = i0 + 1 < np && s_pages[i0 + 1] >= 0;
+    // logits (log2 units, divided by c1) for both pages
     float sp[kNQ][2][4];
 #pragma unroll
     for (int X = 0; X < 2; ++X) {
-      const uint4v rec = X ? rec1 : rec0;
-      const uint4v km = X ? km1 : km0;
+      const uint4v rec = X ? P.rec1 : P.rec0;
+      const uint4v km = X ? P.km1 : P.km0;
       half8 kA[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const uint32_t w = kk < 2 ? rec[0] : rec[1];
         const int sh = 8 * (kk & 1);
-        uint4v r;
+        uint4v rr;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) r[q] = (w >> (sh + 2 * q)) & 0x00030003u;
-        kA[kk] = __builtin_bit_cast(half8, r);
+        for (int q = 0; q < 4; ++q) rr[q] = (w >> (sh + 2 * q)) & 0x00030003u;
+        kA[kk] = __builtin_bit_cast(half8, rr);
       }
       float sk[4], zk[4];
 #pragma unroll
@@ -201,7 +334,7 @@ __global__ __launch_bounds__(256) void split_kernel(const uint8_t* __restrict__ 
         sk[i] = f16_lo(km[i]);
         zk[i] = f16_hi(km[i]);
       }
-      const int pos0 = (lp0 + X) * kPage + 4 * a;
+      const int pos0 = (p0 + i0 + X) * kPage + 4 * a;
       const bool page_ok = X == 0 ? ok0 : has1;
 #pragma unroll
       for (int Q = 0; Q < kNQ; ++Q) {
@@ -220,27 +353,27 @@ __global__ __launch_bounds__(256) void split_kernel(const uint8_t* __restrict__ 
       }
     }
 
-    // ---- value operands: tile t holds channels 16t..16t+15
+    // value operands: tile t holds channels 16t..16t+15
     half8 vB[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      uint4v r;
-      r[0] = (rec0[2] >> (2 * t)) & 0x00030003u;
-      r[1] = (rec0[3] >> (2 * t)) & 0x00030003u;
-      r[2] = (rec1[2] >> (2 * t)) & 0x00030003u;
-      r[3] = (rec1[3] >> (2 * t)) & 0x00030003u;
-      vB[t] = __builtin_bit_cast(half8, r);
+      uint4v rr;
+      rr[0] = (P.rec0[2] >> (2 * t)) & 0x00030003u;
+      rr[1] = (P.rec0[3] >> (2 * t)) & 0x00030003u;
+      rr[2] = (P.rec1[2] >> (2 * t)) & 0x00030003u;
+      rr[3] = (P.rec1[3] >> (2 * t)) & 0x00030003u;
+      vB[t] = __builtin_bit_cast(half8, rr);
     }
     float sv[2][4], zv[2][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sv[0][i] = f16_lo(vm0[i]);
-      zv[0][i] = f16_hi(vm0[i]);
-      sv[1][i] = f16_lo(vm1[i]);
-      zv[1][i] = f16_hi(vm1[i]);
+      sv[0][i] = f16_lo(P.vm0[i]);
+      zv[0][i] = f16_hi(P.vm0[i]);
+      sv[1][i] = f16_lo(P.vm1[i]);
+      zv[1][i] = f16_hi(P.vm1[i]);
     }
 
-    // ---- online softmax and P.V per quad
+    // online softmax and P.V per quad
 #pragma unroll
     for (int Q = 0; Q < kNQ; ++Q) {
       float mloc = -INFINITY;
@@ -267,25 +400,32 @@ __global__ __launch_bounds__(256) void split_kernel(const uint8_t* __restrict__ 
         z_run[Q] *= alpha;
         m_run[Q] = m_new;
       }
-      float pv[2][4];
-#pragma unroll
-      for (int X = 0; X < 2; ++X)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sp[Q][X][i], c1[Q], -m_run[Q]));
-          l_run[Q] += p;
-          z_run[Q] = fmaf(p, zv[X][i], z_run[Q]);
-          pv[X][i] = p * sv[X][i];
-        }
       half8 pA;
 #pragma unroll
       for (int X = 0; X < 2; ++X)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pA[4 * X + i] = static_cast<_Float16>(pv[X][i]);
+        for (int i = 0; i < 4; ++i) {
+          const float pr = __builtin_amdgcn_exp2f(fmaf(sp[Q][X][i], c1[Q], -m_run[Q]));
+          l_run[Q] += pr;
+          z_run[Q] = fmaf(pr, zv[X][i], z_run[Q]);
+          pA[4 * X + i] = static_cast<_Float16>(pr * sv[X][i]);
+        }
 #pragma unroll
       for (int t = 0; t < 8; ++t) acc[Q][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pA, vB[t], acc[Q][t], 0, 0, 0);
     }
+  };
+
+  // ---- main loop
+  for (int pair = wave; pair < npairs;) {
+#pragma unroll
+    for (int k = 0; k < kDepth; ++k) {
+      issue((k + kDepth - 1) % kDepth, min(pair + kW * (kDepth - 1), npairs - 1));
+      compute(k, pair);
+      pair += kW;
+      if (pair >= npairs) break;
+    }
   }
+  wait_vmcnt<0>();  // no load into the ring outlives the loop
 
   // ---- per-wave results to LDS: lane (a, b) owns channels 32a + b and
   //      32a + 16 + b (tiles 2a, 2a+1) for the four heads of each quad.
@@ -298,7 +438,7 @@ __global__ __launch_bounds__(256) void split_kernel(const uint8_t* __restrict__ 
       const float zi = __shfl(zsum, 4 * a + i);  // zero part of head i, group a
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        if ((t >> 1) == a) s_acc[wave][4 * Q + i][16 * t + col] = acc[Q][t][i] * kTwo24 + zi;
+        if ((t >> 1) == a) s_buf[wave][4 * Q + i][16 * t + col] = acc[Q][t][i] * kTwo24 + zi;
       }
     }
     if (lane < 4) {
@@ -308,133 +448,154 @@ __global__ __launch_bounds__(256) void split_kernel(const uint8_t* __restrict__ 
   }
   __syncthreads();
 
-  for (int idx = tid; idx < kNH * kHeadDim; idx += 256) {
+  // ---- workgroup partial -> workspace (agent-scope stores: coherent across
+  //      XCDs without an L2 writeback)
+  const size_t head_base = (static_cast<size_t>(b) * H + h) * p.n_splits;  // first partial of (b, h)
+  for (int idx = tid; idx < g * kHeadDim; idx += kThreads) {
     const int jh = idx / kHeadDim;
     const int c = idx % kHeadDim;
-    if (jh >= g) continue;
     float M = kNegBig;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, s_m[w][jh]);
+    for (int w = 0; w < kW; ++w) M = fmaxf(M, s_m[w][jh]);
     float av = 0.0f, lv = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kW; ++w) {
       const float wt = __builtin_amdgcn_exp2f(s_m[w][jh] - M);
-      av = fmaf(wt, s_acc[w][jh][c], av);
+      av = fmaf(wt, s_buf[w][jh][c], av);
       lv = fmaf(wt, s_l[w][jh], lv);
     }
-    float* dst = part + ((static_cast<size_t>(b) * num_q_heads + h * g + jh) * n_splits + split) * kPartStride;
-    dst[c] = av;
+    float* dst = p.part + ((head_base + split) * g + jh) * kPartStride;
+    __hip_atomic_store(dst + c, av, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (c == 0) {
-      dst[128] = M;
-      dst[129] = lv;
+      __hip_atomic_store(dst + 128, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(dst + 129, lv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-}
 
-// ------------------------------------------------------------- merge kernel
-template <int kOut>  // 0 bf16, 1 fp32
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part,
-                                                    const int32_t* __restrict__ seq_lens, int max_pages,
-                                                    int num_q_heads, int g,
-                                                    int pages_per_split, int n_splits, const float* __restrict__ r_v,
-                                                    void* __restrict__ out) {
-  const int h = blockIdx.x;
-  const int b = blockIdx.y;
-  const int tid = threadIdx.x;
-  __shared__ float so[16][kHeadDim];
-  const int T = min(seq_lens[b], max_pages * kPage);
-  const int n_pages = (T + kPage - 1) / kPage;
-  const int nval = min(n_splits, (n_pages + pages_per_split - 1) / pages_per_split);
+  // ---- the last workgroup of (b, h) merges the splits.  The partial stores
+  // complete (vmcnt 0) before the ticket is taken; the merging workgroup reads
+  // them with agent-scope loads after seeing the last ticket.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0)
+    s_ticket = __hip_atomic_fetch_add(p.counters + b * H + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (s_ticket != n_valid - 1) return;
 
-  for (int idx = tid; idx < g * kHeadDim; idx += 256) {
+  // R_V rows for the output rotation, requested before the merge loads:
+  // thread (row oi, part oq) takes channels [kRows * oq, +kRows) of row oi
+  const int oi = tid & (kHeadDim - 1);
+  const int oq = rpart;
+  float4v rr[kRows / 4];
+  {
+    const float* Rrow = p.r_v + (static_cast<size_t>(h) * kHeadDim + oi) * kHeadDim + kRows * oq;
+#pragma unroll
+    for (int u = 0; u < kRows / 4; ++u) rr[u] = *reinterpret_cast<const float4v*>(Rrow + 4 * u);
+  }
+  // log-sum-exp weights of every (split, head): wave w takes heads w, w+kW, ...,
+  // each lane up to kMaxSplits/64 splits, all loads in one round.
+  // s_w aliases s_buf: n_valid * g <= kMaxSplits * kNH <= 4 * kNH * kHeadDim.
+  static_assert(kMaxSplits <= 4 * kHeadDim, "merge weights fit in s_buf");
+  float* s_w = &s_buf[0][0][0];
+  const float* pb = p.part + head_base * g * kPartStride;
+  constexpr int kSplitsPerLane = kMaxSplits / 64;
+  for (int jh = wave; jh < g; jh += kW) {
+    float ms[kSplitsPerLane], ls[kSplitsPerLane];
+#pragma unroll
+    for (int u = 0; u < kSplitsPerLane; ++u) {
+      const int sp_ = lane + 64 * u;
+      const float* ps = pb + (min(sp_, n_valid - 1) * g + jh) * kPartStride;
+      const float m_ld = ld_agent(ps + 128);
+      const float l_ld = ld_agent(ps + 129);
+      ms[u] = sp_ < n_valid ? m_ld : kNegBig;
+      ls[u] = sp_ < n_valid ? l_ld : 0.0f;
+    }
+    float M = kNegBig;
+#pragma unroll
+    for (int u = 0; u < kSplitsPerLane; ++u) M = fmaxf(M, ms[u]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float lv = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kSplitsPerLane; ++u) {
+      const int sp_ = lane + 64 * u;
+      const float wt = __builtin_amdgcn_exp2f(ms[u] - M);
+      if (sp_ < n_valid) s_w[sp_ * g + jh] = wt;
+      lv = fmaf(wt, ls[u], lv);
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) lv += __shfl_xor(lv, off);
+    if (lane == 0) s_f[jh] = lv > 0.0f ? 1.0f / lv : 0.0f;
+  }
+  __syncthreads();
+  // weighted sums, 32 partial rows in flight per thread
+  for (int idx = tid; idx < g * kHeadDim; idx += kThreads) {
     const int jh = idx / kHeadDim;
     const int c = idx % kHeadDim;
-    const float* src = part + (static_cast<size_t>(b) * num_q_heads + h * g + jh) * n_splits * kPartStride;
-    float M = kNegBig;
-    for (int s = 0; s < nval; ++s) M = fmaxf(M, src[s * kPartStride + 128]);
-    float av = 0.0f, lv = 0.0f;
-    for (int s = 0; s < nval; ++s) {
-      const float wt = __builtin_amdgcn_exp2f(src[s * kPartStride + 128] - M);
-      av = fmaf(wt, src[s * kPartStride + c], av);
-      lv = fmaf(wt, src[s * kPartStride + 129], lv);
+    float av = 0.0f;
+    for (int s0 = 0; s0 < n_valid; s0 += 32) {
+      float v[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) v[u] = ld_agent(pb + (min(s0 + u, n_valid - 1) * g + jh) * kPartStride + c);
+#pragma unroll
+      for (int u = 0; u < 32; ++u) av = fmaf(s0 + u < n_valid ? s_w[min(s0 + u, n_valid - 1) * g + jh] : 0.0f, v[u], av);
     }
-    so[jh][c] = lv > 0.0f ? av / lv : 0.0f;
+    s_q[jh][c] = av * s_f[jh];  // o_rot
   }
   __syncthreads();
 
-  if (tid < kHeadDim) {
-    const int i = tid;  // output channel: o[i] = sum_c o_rot[c] * R_V[i][c]
-    const float* Rrow = r_v + (static_cast<size_t>(h) * kHeadDim + i) * kHeadDim;
-    float o[16];
+  // o = o_rot R_V^T: o[i] = sum_c o_rot[c] R_V[i][c]; thread (i, part) sums kRows channels
+  if (tid < kParts * kHeadDim) {
+    float o[kNH];
 #pragma unroll
-    for (int jh = 0; jh < 16; ++jh) o[jh] = 0.0f;
-    for (int c = 0; c < kHeadDim; c += 4) {
-      const float4v r4 = *reinterpret_cast<const float4v*>(Rrow + c);
+    for (int jh = 0; jh < kNH; ++jh) o[jh] = 0.0f;
 #pragma unroll
-      for (int jh = 0; jh < 16; ++jh) {
-        if (jh < g) {
-          o[jh] = fmaf(so[jh][c + 0], r4[0], o[jh]);
-          o[jh] = fmaf(so[jh][c + 1], r4[1], o[jh]);
-          o[jh] = fmaf(so[jh][c + 2], r4[2], o[jh]);
-          o[jh] = fmaf(so[jh][c + 3], r4[3], o[jh]);
-        }
-      }
-    }
+    for (int u = 0; u < kRows / 4; ++u)
 #pragma unroll
-    for (int jh = 0; jh < 16; ++jh) {
-      if (jh < g) {
-        const size_t oi = (static_cast<size_t>(b) * num_q_heads + h * g + jh) * kHeadDim + i;
-        if (kOut == 0)
-          static_cast<uint16_t*>(out)[oi] = f32_to_bf16_bits(o[jh]);
-        else
-          static_cast<float*>(out)[oi] = o[jh];
-      }
-    }
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int jh = 0; jh < kNH; ++jh) o[jh] = fmaf(s_q[jh][kRows * oq + 4 * u + e], rr[u][e], o[jh]);
+#pragma unroll
+    for (int jh = 0; jh < kNH; ++jh) s_buf[oq][jh][oi] = o[jh];
   }
+  __syncthreads();
+  for (int idx = tid; idx < g * kHeadDim; idx += kThreads) {
+    const int jh = idx / kHeadDim;
+    const int i = idx % kHeadDim;
+    float o = 0.0f;
+#pragma unroll
+    for (int u = 0; u < kParts; ++u) o += s_buf[u][jh][i];
+    const size_t oidx = (out_row0 + jh) * kHeadDim + i;
+    if (p.out_kind == 0)
+      static_cast<uint16_t*>(p.out)[oidx] = f32_to_bf16_bits(o);
+    else
+      static_cast<float*>(p.out)[oidx] = o;
+  }
+  if (tid == 0) __hip_atomic_store(p.counters + b * H + h, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ----------------------------------------------------------------- launcher
 template <int kNQ>
-static void launch_split(const DecodeArgs& a, const DecodePlan& plan, int g, hipStream_t stream) {
-  const dim3 grid(plan.n_splits, a.num_kv_heads, a.batch);
-  hipLaunchKernelGGL(split_kernel<kNQ>, grid, dim3(256), 0, stream, a.pool, a.num_kv_heads, a.num_pages, a.qhat,
-                     a.page_table,
-                     a.max_pages, a.seq_lens, a.num_q_heads, g, plan.pages_per_split, plan.n_splits, a.part);
+static void launch_one(const DecodeParams& prm, hipStream_t stream) {
+  constexpr int kW = DecodeShape<kNQ>::waves;
+  const dim3 grid(prm.batch * prm.num_kv_heads * prm.n_splits);
+  hipLaunchKernelGGL((decode_kernel<kNQ, kW>), grid, dim3(64 * kW), 0, stream, prm);
 }
 
-hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream, hipEvent_t ev_begin,
-                         hipEvent_t ev_end) {
-  const int g = a.num_q_heads / a.num_kv_heads;
+hipError_t launch_decode(const DecodeParams& prm, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
   (void)hipGetLastError();  // report only this call's launch errors, not stale ones
-  const dim3 qgrid(a.batch * a.num_q_heads);
-  if (a.q_kind == 0)
-    hipLaunchKernelGGL(qrot_kernel<0>, qgrid, dim3(128), 0, stream, a.q, a.r_k, a.num_q_heads, g, a.logit_scale,
-                       a.qhat);
-  else
-    hipLaunchKernelGGL(qrot_kernel<1>, qgrid, dim3(128), 0, stream, a.q, a.r_k, a.num_q_heads, g, a.logit_scale,
-                       a.qhat);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-
+  hipError_t err;
   if (ev_begin != nullptr && (err = hipEventRecord(ev_begin, stream)) != hipSuccess) return err;
-  if (g <= 4)
-    launch_split<1>(a, plan, g, stream);
-  else if (g <= 8)
-    launch_split<2>(a, plan, g, stream);
+  if (prm.g <= 4)
+    launch_one<1>(prm, stream);
+  else if (prm.g <= 8)
+    launch_one<2>(prm, stream);
   else
-    launch_split<4>(a, plan, g, stream);
+    launch_one<4>(prm, stream);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (ev_end != nullptr && (err = hipEventRecord(ev_end, stream)) != hipSuccess) return err;
-
-  const dim3 mgrid(a.num_kv_heads, a.batch);
-  if (a.out_kind == 0)
-    hipLaunchKernelGGL(merge_kernel<0>, mgrid, dim3(256), 0, stream, a.part, a.seq_lens, a.max_pages, a.num_q_heads, g,
-                       plan.pages_per_split, plan.n_splits, a.r_v, a.out);
-  else
-    hipLaunchKernelGGL(merge_kernel<1>, mgrid, dim3(256), 0, stream, a.part, a.seq_lens, a.max_pages, a.num_q_heads, g,
-                       plan.pages_per_split, plan.n_splits, a.r_v, a.out);
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace kvq

@@ -14,9 +14,10 @@ constexpr int kBlockBytes = 1536;   // one (page, KV head) block
 constexpr int kCodeBytes = 1024;    // 64 records x 16 B of K/V code words
 constexpr int kMetaRecordBytes = 32;
 
-// Row strides (floats) of the decode workspace.
-constexpr int kQhatStride = 132;    // [0,128) scaled rotated query, [128] fp16 range factor
-constexpr int kPartStride = 132;    // [0,128) unnormalised rotated output, [128] max, [129] sum
+// Decode split limits and the partial-result row stride (floats).
+constexpr int kMaxPagesPerSplit = 2048;
+constexpr int kMaxSplits = 512;
+constexpr int kPartStride = 132;    // [0,128) unnormalised rotated output, [128] max (log2), [129] sum
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));

@@ -12,11 +12,12 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
 
 struct DecodePlan {
   int n_pages_max;      // ceil(max_seq_len / 16)
-  int pages_per_split;  // pages handled by one workgroup
-  int n_splits;         // splits per (sequence, KV head)
+  int pages_per_split;  // pages handled by one workgroup, <= kMaxPagesPerSplit
+  int n_splits;         // splits per (sequence, KV head), <= kMaxSplits
 };
 
-struct DecodeArgs {
+// Kernel arguments of the fused decode (passed by value).
+struct DecodeParams {
   const uint8_t* pool;
   int num_kv_heads;
   int num_pages;
@@ -24,6 +25,7 @@ struct DecodeArgs {
   int q_kind;  // 0 bf16, 1 fp32
   int batch;
   int num_q_heads;
+  int g;  // query heads per KV head
   const int32_t* page_table;
   int max_pages;
   const int32_t* seq_lens;
@@ -31,12 +33,13 @@ struct DecodeArgs {
   const float* r_v;
   float logit_scale;  // sm_scale * log2(e)
   void* out;
-  int out_kind;  // 0 bf16, 1 fp32
-  float* qhat;   // workspace: [batch][num_q_heads][kQhatStride]
-  float* part;   // workspace: [batch][num_q_heads][n_splits][kPartStride]
+  int out_kind;        // 0 bf16, 1 fp32
+  float* part;         // [batch][num_kv_heads][n_splits][g][kPartStride]
+  int32_t* counters;   // [batch][num_kv_heads], zero between calls
+  int pages_per_split;
+  int n_splits;
 };
 
-hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream, hipEvent_t ev_begin,
-                         hipEvent_t ev_end);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end);
 
 }  // namespace kvq

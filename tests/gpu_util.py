@@ -74,12 +74,16 @@ class DeviceCase:
         torch.cuda.synchronize()
         return rot
 
-    def decode(self, out_dtype="f32", num_splits=0, q=None, table=None):
+    def decode(self, out_dtype="f32", num_splits=0, q=None, table=None, ws=None):
         from rotated_int2_kv_centering_amd import kvq
         c = self.c
         max_seq = int(c.seq_lens.max(initial=0))
         ws_bytes = kvq.kvq_decode_workspace_bytes(c.B, c.Hq, c.Hkv, max_seq, num_splits)
-        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=self.dev)
+        if ws is None:
+            ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=self.dev)
+        else:
+            assert ws.numel() >= ws_bytes
+            ws_bytes = ws.numel()
         tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
         out = torch.full((c.B, c.Hq, 128), float("nan"), dtype=tdt, device=self.dev)
         table = self.table if table is None else table

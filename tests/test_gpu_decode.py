@@ -111,6 +111,21 @@ def test_repeated_calls_are_deterministic():
         np.testing.assert_array_equal(dc.decode("f32"), first)
 
 
+def test_one_workspace_reused_across_calls_and_shapes():
+    """The split tickets in the workspace return to zero after every call: one workspace
+    serves calls of different lengths and split counts, each equal to a fresh-workspace run."""
+    import torch
+    dev = require_gpu()
+    a = DeviceCase(I.make_case("wa", 15, B=2, Hq=32, Hkv=8, seq_lens=[3000, 100]), dev)
+    b = DeviceCase(I.make_case("wb", 16, B=1, Hq=32, Hkv=8, seq_lens=[9000]), dev)
+    for dc in (a, b):
+        dc.append(rot_out=False)
+    fresh = {(id(dc), ns): dc.decode("f32", num_splits=ns) for dc in (a, b) for ns in (0, 5)}
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=dev)
+    for dc, ns in [(a, 0), (b, 0), (a, 5), (b, 5), (a, 0), (b, 5), (a, 5)]:
+        np.testing.assert_array_equal(dc.decode("f32", num_splits=ns, ws=ws), fresh[(id(dc), ns)])
+
+
 def test_centering_is_invisible_to_attention_on_exact_cache():
     """OptR section 1: centering shifts every logit of a query by <q, mu>, so softmax is
     unchanged.  Keys k = mu + 0.5 * levels and values 0.25 * levels (R = I) quantize
