@@ -10,7 +10,7 @@ cache read comes from HBM, not from the MALL.
 
 Prints ONE JSON line:
   value      KV-tokens/s = sum_b T_b / step time (one GPU = whole job)
-  roofline   split-K attention kernel: algorithmic bytes per launch / its
+  roofline   the decode-attention kernel: algorithmic bytes per launch / its
              average duration from HIP events recorded around it on its own
              stream inside the timed region, against 8 TB/s
   cpu_baseline  the oracle (NumPy, fp64) timed on a bounded sample of the same step
@@ -83,7 +83,7 @@ class Hip:
 def counters_for(kernel_src: str, workload: str):
     """HBM traffic per launch from the committed rocprofv3 counter summary, if it was
     taken on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", f"split_kernel_{workload}_counters.md")
+    path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -267,7 +267,7 @@ def main() -> int:
     for r in range(n_rep):
         if not torch.equal(outs[r], eager_out[r]):
             raise RuntimeError(f"timed output differs from the first output on replica {r}")
-    log(f"[bench] {steps} steps: {ms_per_step * 1e3:.2f} us/step, split kernel {split_avg_ms * 1e3:.2f} us "
+    log(f"[bench] {steps} steps: {ms_per_step * 1e3:.2f} us/step, decode kernel {split_avg_ms * 1e3:.2f} us "
         f"(min {min(split_ms) * 1e3:.2f}, max {max(split_ms) * 1e3:.2f}); host enqueue {t_enqueue:.1f} ms "
         f"vs GPU {total_ms:.1f} ms")
 
@@ -304,7 +304,7 @@ def main() -> int:
         },
         "hbm_gbps_step": cache_bytes / (ms_per_step * 1e-3) / 1e9,
         "pct_peak_step": cache_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-        "split_kernel_us": split_avg_ms * 1e3,
+        "decode_kernel_us": split_avg_ms * 1e3,
         "host_enqueue_ms": t_enqueue,
         "bulk_append_ms": bulk_ms,
         "roofline": {

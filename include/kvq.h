@@ -172,11 +172,11 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const void* q, kvq_dtype q_dt
 /*
  * kvq_decode_attn_traced - kvq_decode_attn plus timing events for measurement.
  * Identical arguments, results and errors; in addition, when non-NULL,
- * `ev_begin` and `ev_end` (hipEvent_t created by the caller) are recorded on
- * `stream` immediately before and after the split-K attention kernel, the
- * call's dominant (HBM-streaming) kernel, so the caller can read its duration
- * with hipEventElapsedTime.  Meant for eager launches: inside a stream capture
- * the records only order the graph and give no timing.
+ * `ev_begin` and `ev_end` (hipEvent_t created by the caller, with timing)
+ * take the start and end timestamps of the attention kernel's own dispatch
+ * (the call launches exactly one kernel), so hipEventElapsedTime gives the
+ * kernel's duration without launch gaps.  Meant for eager launches; they give
+ * no timing inside a stream capture.
  */
 kvq_status kvq_decode_attn_traced(const kvq_cache* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
                                   int32_t num_q_heads, const int32_t* page_table, int32_t max_pages,

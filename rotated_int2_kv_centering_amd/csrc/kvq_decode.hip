@@ -43,6 +43,8 @@
 // rows whose group does not own the tile's channels are discarded.  The
 // zero-point part sum_s p_s z_v,s is accumulated in fp32.
 
+#include <hip/hip_ext.h>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -575,27 +577,29 @@ void decode_kernel(const DecodeParams p) {
 }
 
 // ----------------------------------------------------------------- launcher
+// hipExtLaunchKernel stamps the events with the dispatch's own start and end
+// times, so an event pair measures the kernel alone.
 template <int kNQ>
-static void launch_one(const DecodeParams& prm, hipStream_t stream) {
+static hipError_t launch_one(const DecodeParams& prm, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
   constexpr int kW = DecodeShape<kNQ>::waves;
-  const dim3 grid(prm.batch * prm.num_kv_heads * prm.n_splits);
-  hipLaunchKernelGGL((decode_kernel<kNQ, kW>), grid, dim3(64 * kW), 0, stream, prm);
+  DecodeParams arg = prm;
+  void* args[] = {&arg};
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<kNQ, kW>),
+                            dim3(prm.batch * prm.num_kv_heads * prm.n_splits), dim3(64 * kW), args, 0, stream,
+                            ev_begin, ev_end, 0);
 }
 
 hipError_t launch_decode(const DecodeParams& prm, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
   (void)hipGetLastError();  // report only this call's launch errors, not stale ones
   hipError_t err;
-  if (ev_begin != nullptr && (err = hipEventRecord(ev_begin, stream)) != hipSuccess) return err;
   if (prm.g <= 4)
-    launch_one<1>(prm, stream);
+    err = launch_one<1>(prm, stream, ev_begin, ev_end);
   else if (prm.g <= 8)
-    launch_one<2>(prm, stream);
+    err = launch_one<2>(prm, stream, ev_begin, ev_end);
   else
-    launch_one<4>(prm, stream);
-  err = hipGetLastError();
+    err = launch_one<4>(prm, stream, ev_begin, ev_end);
   if (err != hipSuccess) return err;
-  if (ev_end != nullptr && (err = hipEventRecord(ev_end, stream)) != hipSuccess) return err;
-  return hipSuccess;
+  return hipGetLastError();
 }
 
 }  // namespace kvq
