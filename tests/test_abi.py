@@ -1,0 +1,200 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports exactly
+the entry points include/kvq.h declares, and its host logic (sizes, page
+tables, argument validation) behaves as documented.  No call here reaches a
+kernel launch: every failing call is rejected by host validation first.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+@pytest.fixture(scope="module")
+def K():
+    from rotated_int2_kv_centering_amd import kvq
+
+    if not os.path.exists(kvq.LIB_PATH):  # fresh checkout: build once, as __graft_entry__.build() does
+        from rotated_int2_kv_centering_amd import build
+
+        build.build()
+    kvq.load()
+    return kvq
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(kvq_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(["kvq_pool_bytes", "kvq_quant_append", "kvq_decode_workspace_bytes", "kvq_decode_attn",
+                            "kvq_decode_attn_traced", "kvq_page_table", "kvq_last_error"]), names
+
+
+def test_library_exports_exactly_the_declared_symbols(K):
+    lib = K.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", K.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = sorted({l.split()[-1] for l in out.splitlines() if l.split()[-2:-1] == ["T"] and "kvq_" in l.split()[-1]})
+    assert exported == declared_functions()
+
+
+def test_python_binding_has_the_same_names(K):
+    for name in declared_functions():
+        assert callable(getattr(K, name)), name
+
+
+def test_pool_bytes(K):
+    assert K.kvq_pool_bytes(K.make_cache(8, 8192)) == 8192 * 8 * 1536
+    assert K.kvq_pool_bytes(K.make_cache(1, 16)) == 16 * 1536
+    assert K.kvq_pool_bytes(K.make_cache(0, 16)) == 0
+    assert K.kvq_pool_bytes(K.make_cache(8, 0)) == 0
+
+
+def test_workspace_bytes_with_explicit_splits(K):
+    # counters (B*Hkv int32, padded to 256 B) + B*Hq*n_splits partial rows of 132 floats
+    n_pages = (1000 + 15) // 16  # 63 pages; 7 splits of 9 pages
+    assert K.kvq_decode_workspace_bytes(2, 8, 2, 1000, 7) == 256 + 4 * 2 * 8 * 7 * 132
+    # a request of more splits than pages gives one page per split
+    assert K.kvq_decode_workspace_bytes(1, 4, 1, 40, 16) == 256 + 4 * 1 * 4 * 3 * 132
+    # at most 512 splits: pages per split grow instead
+    big = 600 * 16
+    assert K.kvq_decode_workspace_bytes(1, 4, 1, big, 600) == 256 + 4 * 4 * 300 * 132
+    assert n_pages == 63
+
+
+def test_workspace_bytes_rejects_bad_shapes(K):
+    assert K.kvq_decode_workspace_bytes(1, 6, 4, 100, 1) == 0   # Hq not a multiple of Hkv
+    assert K.kvq_decode_workspace_bytes(-1, 4, 1, 100, 1) == 0
+    assert K.kvq_decode_workspace_bytes(1, 4, 1, -5, 1) == 0
+    assert K.kvq_decode_workspace_bytes(1, 4, 1, 512 * 2048 * 16 + 1, 1) == 0  # beyond the longest context
+
+
+def test_page_table_contiguous_and_slots(K):
+    lens = [5, 33, 0, 16]
+    table, slots = K.kvq_page_table(K.KVQ_PT_CONTIGUOUS, 0, lens, 16, 10, 4)
+    assert table.tolist() == [[0, -1, -1, -1], [1, 2, 3, -1], [-1, -1, -1, -1], [4, -1, -1, -1]]
+    assert slots.tolist() == [4, 3 * 16 + 0, -1, 4 * 16 + 15]
+
+
+@pytest.mark.parametrize("policy", ["KVQ_PT_PERMUTED", "KVQ_PT_INTERLEAVED"])
+def test_page_table_random_policies_give_valid_tables(K, policy):
+    rng = np.random.default_rng(5)
+    lens = rng.integers(0, 400, size=9).astype(np.int32)
+    need = (lens + 15) // 16
+    table, slots = K.kvq_page_table(getattr(K, policy), 1234, lens, 16, int(need.sum()) + 7, int(need.max()))
+    used = np.concatenate([table[b, :need[b]] for b in range(len(lens))])
+    assert len(np.unique(used)) == len(used) == need.sum()
+    assert used.min() >= 0 and used.max() < need.sum() + 7
+    for b in range(len(lens)):
+        assert (table[b, need[b]:] == -1).all()
+        t = lens[b] - 1
+        assert slots[b] == (-1 if t < 0 else table[b, t // 16] * 16 + t % 16)
+    # the same seed gives the same table; the validator accepts it
+    again, _ = K.kvq_page_table(getattr(K, policy), 1234, lens, 16, int(need.sum()) + 7, int(need.max()))
+    assert (again == table).all()
+    K.kvq_page_table(K.KVQ_PT_VALIDATE, 0, lens, 16, int(need.sum()) + 7, int(need.max()), table)
+
+
+def test_page_table_validation_errors(K):
+    lens = [20, 20]
+    table = np.array([[0, 1], [2, 1]], dtype=np.int32)  # page 1 twice
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_page_table(K.KVQ_PT_VALIDATE, 0, lens, 16, 4, 2, table)
+    assert e.value.status == K.KVQ_EINVAL and "twice" in str(e.value)
+    table = np.array([[0, 1], [2, 4]], dtype=np.int32)  # page 4 outside a pool of 4
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_page_table(K.KVQ_PT_VALIDATE, 0, lens, 16, 4, 2, table)
+    assert e.value.status == K.KVQ_EINVAL
+    with pytest.raises(K.KvqError) as e:  # 4 pages needed, 3 in the pool
+        K.kvq_page_table(K.KVQ_PT_PERMUTED, 0, lens, 16, 3, 2)
+    assert e.value.status == K.KVQ_ENOSPACE
+    with pytest.raises(K.KvqError) as e:  # a row of 1 page cannot hold 20 tokens
+        K.kvq_page_table(K.KVQ_PT_PERMUTED, 0, lens, 16, 8, 1)
+    assert e.value.status == K.KVQ_ENOSPACE
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_page_table(K.KVQ_PT_CONTIGUOUS, 0, lens, 32, 8, 2)
+    assert e.value.status == K.KVQ_EUNSUPPORTED
+
+
+FAKE = 1 << 20  # a non-NULL, 16-byte aligned address; never dereferenced by rejected calls
+
+
+def test_append_argument_validation(K):
+    lib = K.load()
+    ok = K.make_cache(2, 4, FAKE)
+    assert lib.kvq_quant_append(None, FAKE, FAKE, K.KVQ_BF16, 1, FAKE, None, FAKE, FAKE, None, None) == K.KVQ_EINVAL
+    bad_geom = K.make_cache(2, 4, FAKE, head_dim=64)
+    assert lib.kvq_quant_append(ctypes.byref(bad_geom), FAKE, FAKE, K.KVQ_BF16, 1, FAKE, None, FAKE, FAKE, None,
+                                None) == K.KVQ_EUNSUPPORTED
+    assert "head_dim=64" in K.kvq_last_error()
+    assert lib.kvq_quant_append(ctypes.byref(ok), FAKE, FAKE, 7, 1, FAKE, None, FAKE, FAKE, None,
+                                None) == K.KVQ_EUNSUPPORTED
+    assert lib.kvq_quant_append(ctypes.byref(ok), FAKE, FAKE, K.KVQ_BF16, -1, FAKE, None, FAKE, FAKE, None,
+                                None) == K.KVQ_EINVAL
+    # zero tokens: nothing to do, OK without touching any pointer
+    assert lib.kvq_quant_append(ctypes.byref(ok), None, None, K.KVQ_BF16, 0, None, None, None, None, None,
+                                None) == K.KVQ_OK
+    assert lib.kvq_quant_append(ctypes.byref(ok), FAKE, FAKE, K.KVQ_BF16, 1, FAKE, None, None, FAKE, None,
+                                None) == K.KVQ_EINVAL  # rotation required for raw input
+    empty = K.make_cache(2, 0, None)
+    assert lib.kvq_quant_append(ctypes.byref(empty), FAKE, FAKE, K.KVQ_BF16, 1, FAKE, None, FAKE, FAKE, None,
+                                None) == K.KVQ_ENOSPACE
+    misaligned = K.make_cache(2, 4, FAKE + 4)
+    assert lib.kvq_quant_append(ctypes.byref(misaligned), FAKE, FAKE, K.KVQ_BF16, 1, FAKE, None, FAKE, FAKE, None,
+                                None) == K.KVQ_EINVAL
+
+
+def _decode(K, cache, batch=1, hq=4, max_pages=4, max_seq=64, sm_scale=0.0, q_dtype=None, out_dtype=None,
+            ws_bytes=1 << 20, num_splits=1, q=FAKE):
+    lib = K.load()
+    q_dtype = K.KVQ_BF16 if q_dtype is None else q_dtype
+    out_dtype = K.KVQ_F32 if out_dtype is None else out_dtype
+    return lib.kvq_decode_attn(ctypes.byref(cache) if cache is not None else None, q, q_dtype, batch, hq, FAKE,
+                               max_pages, FAKE, max_seq, FAKE, FAKE, sm_scale, FAKE, out_dtype, FAKE, ws_bytes,
+                               num_splits, None)
+
+
+def test_decode_argument_validation(K):
+    c = K.make_cache(1, 8, FAKE)
+    assert _decode(K, None) == K.KVQ_EINVAL
+    assert _decode(K, c, hq=3 * 1, batch=-1) == K.KVQ_EINVAL
+    assert _decode(K, K.make_cache(2, 8, FAKE), hq=3) == K.KVQ_EINVAL          # 3 q heads over 2 KV heads
+    assert _decode(K, c, hq=17) == K.KVQ_EUNSUPPORTED                           # g > 16
+    assert _decode(K, c, q_dtype=K.KVQ_F32_ROTATED) == K.KVQ_EUNSUPPORTED
+    assert _decode(K, c, out_dtype=5) == K.KVQ_EUNSUPPORTED
+    assert _decode(K, c, max_pages=3, max_seq=64) == K.KVQ_EINVAL               # 64 tokens need 4 pages
+    assert _decode(K, c, sm_scale=float("nan")) == K.KVQ_EINVAL
+    assert _decode(K, c, sm_scale=-1.0) == K.KVQ_EINVAL
+    assert _decode(K, c, num_splits=-2) == K.KVQ_EINVAL
+    assert _decode(K, c, q=None) == K.KVQ_EINVAL
+    need = K.kvq_decode_workspace_bytes(1, 4, 1, 64, 1)
+    assert _decode(K, c, ws_bytes=need - 1) == K.KVQ_ENOSPACE
+    assert "workspace" in K.kvq_last_error()
+    assert _decode(K, c, max_pages=512 * 2048 + 1, max_seq=512 * 2048 * 16 + 1) == K.KVQ_EUNSUPPORTED
+    assert _decode(K, K.make_cache(1, 0, None)) == K.KVQ_ENOSPACE
+    # an empty batch is a no-op
+    assert _decode(K, c, batch=0) == K.KVQ_OK
+
+
+def test_binding_raises_with_the_library_message(K):
+    c = K.make_cache(1, 8, FAKE, page_size=32)
+    with pytest.raises(K.KvqError) as e:
+        K.kvq_quant_append(c, FAKE, FAKE, K.KVQ_BF16, 1, FAKE, None, FAKE, FAKE, stream=0)
+    assert e.value.status == K.KVQ_EUNSUPPORTED and "page_size=32" in str(e.value)
+
+
+def test_binding_rejects_non_contiguous_arrays(K):
+    a = np.zeros((4, 4), dtype=np.int32)[:, ::2]
+    with pytest.raises(ValueError):
+        K._ptr(a)
