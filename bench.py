@@ -1,18 +1,18 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the rotated INT2 KV cache on one MI355X.
 
-One step = the whole hot path for one layer: quantize-append of the newest
-token of every sequence (position T-1 is re-appended so T stays fixed) and
-one fused decode-attention call over the packed cache.  Inputs are resident
+One step = the whole hot path for one layer in one kernel (kvq_decode_step):
+quantize-append of the newest token of every sequence (position T-1 is
+re-appended so T stays fixed) and decode attention over the packed cache.  Inputs are resident
 in HBM before timing starts.  Steps cycle over independent cache replicas
 ("layers") whose total size exceeds twice the 256 MB Infinity Cache, so the
 cache read comes from HBM, not from the MALL.
 
 Prints ONE JSON line:
   value      KV-tokens/s = sum_b T_b / step time (one GPU = whole job)
-  roofline   the decode-attention kernel: algorithmic bytes per launch / its
-             average duration from HIP events recorded around it on its own
-             stream inside the timed region, against 8 TB/s
+  roofline   the step kernel: algorithmic bytes per launch / its average
+             duration from HIP events stamped with the dispatch's own start and
+             end inside the timed region, against 8 TB/s
   cpu_baseline  the oracle (NumPy, fp64) timed on a bounded sample of the same step
 """
 
@@ -207,8 +207,7 @@ def main() -> int:
 
     # ---- per-step inputs: newest token of each sequence, queries, tables
     last = np.array([np.nonzero(case.tok_seq == b)[0][-1] for b in range(case.B)])
-    k_new, v_new = B16(case.k_bits[last]), B16(case.v_bits[last])
-    slots_new = T(case.slots[last])
+    k_new, v_new = B16(case.k_bits[last]), B16(case.v_bits[last])  # [B][H_kv][128]
     q = B16(case.q_bits)
     table = T(case.page_table)
     seq = T(case.seq_lens)
@@ -218,10 +217,10 @@ def main() -> int:
     outs = [torch.empty((case.B, case.Hq, 128), dtype=torch.bfloat16, device=dev) for _ in range(n_rep)]
 
     def step(r, ev_b=None, ev_e=None):
-        kvq.kvq_quant_append(caches[r], k_new, v_new, kvq.KVQ_BF16, case.B, slots_new, mus[r], rks[r], rvs[r], None)
-        kvq.kvq_decode_attn_traced(caches[r], q, kvq.KVQ_BF16, case.B, case.Hq, table, table.shape[1], seq, max_seq,
-                                   rks[r], rvs[r], 0.0, outs[r], kvq.KVQ_BF16, ws, ws_bytes, args.num_splits, None,
-                                   ev_b, ev_e)
+        # one kernel: quantize-append of the newest token (position T-1) of every sequence, then decode
+        kvq.kvq_decode_step(caches[r], k_new, v_new, kvq.KVQ_BF16, mus[r], q, kvq.KVQ_BF16, case.B, case.Hq, table,
+                            table.shape[1], seq, max_seq, rks[r], rvs[r], 0.0, outs[r], kvq.KVQ_BF16, ws, ws_bytes,
+                            args.num_splits, None, ev_b, ev_e)
 
     # eager reference output of every replica (also warms up the kernels)
     for r in range(n_rep):
@@ -273,7 +272,8 @@ def main() -> int:
 
     tokens = float(case.seq_lens.sum())
     n_pages = int(((case.seq_lens + PAGE - 1) // PAGE).sum())
-    alg_bytes = cache_bytes + 4 * n_pages  # packed cache + page-table entries read by the split kernel
+    # packed cache + page-table entries read, plus the newest token's bf16 k/v read and 96 B written per KV head
+    alg_bytes = cache_bytes + 4 * n_pages + case.B * case.Hkv * (512 + BYTES_PER_TOKEN_HEAD)
     achieved = alg_bytes / (split_avg_ms * 1e-3) / 1e9
     traffic = counters_for(kernel_source_sha(), args.workload)
 

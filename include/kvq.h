@@ -185,6 +185,38 @@ kvq_status kvq_decode_attn_traced(const kvq_cache* cache, const void* q, kvq_dty
                                   size_t workspace_bytes, int32_t num_splits, void* stream, void* ev_begin,
                                   void* ev_end);
 
+/*
+ * kvq_decode_step - one decode step in one kernel: quantize-append the newest
+ * token of every sequence, then decode attention over the whole context.
+ *
+ * OptR section 1 (key centering) and section 3.1, Eq. (4) for the append;
+ * section 3, Eq. (1)-(2) and section 3.2, Eq. (5) for the attention.  The
+ * results are those of kvq_quant_append of the tokens k_new[b], v_new[b] at
+ * position seq_lens[b] - 1 of each sequence b (slot page_table[b][t / 16] * 16
+ * + t % 16 with t = seq_lens[b] - 1), followed by kvq_decode_attn with the
+ * same arguments: the cache bytes written are identical to kvq_quant_append's,
+ * and the new token is attended from its packed INT2 levels.
+ *
+ * Arguments: those of kvq_decode_attn_traced, plus
+ *   k_new, v_new  device [batch][num_kv_heads][128], dtype kv_dtype (KVQ_BF16
+ *                 or KVQ_F32): the newest key and value of each sequence.
+ *   mu            device fp32 [num_kv_heads][128] key centre, or NULL (zero).
+ * seq_lens[b] counts the new token.  A sequence of length 0 appends nothing
+ * and outputs zeros.  If the page holding position seq_lens[b] - 1 is outside
+ * [0, num_pages), the token is neither written nor attended (as in
+ * kvq_quant_append and kvq_decode_attn).  The slot at that position is
+ * overwritten; its previous content is never read.  ev_begin / ev_end are
+ * optional timing events as in kvq_decode_attn_traced (NULL for none).
+ * Errors: those of kvq_decode_attn; KVQ_EINVAL if k_new or v_new is NULL;
+ * KVQ_EUNSUPPORTED for another kv_dtype.
+ */
+kvq_status kvq_decode_step(const kvq_cache* cache, const void* k_new, const void* v_new, kvq_dtype kv_dtype,
+                           const float* mu, const void* q, kvq_dtype q_dtype, int32_t batch, int32_t num_q_heads,
+                           const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
+                           int32_t max_seq_len, const float* r_k, const float* r_v, float sm_scale, void* out,
+                           kvq_dtype out_dtype, void* workspace, size_t workspace_bytes, int32_t num_splits,
+                           void* stream, void* ev_begin, void* ev_end);
+
 /* Page-table policies for kvq_page_table. */
 typedef enum {
   KVQ_PT_CONTIGUOUS = 0,  /* sequence b gets the next ceil(T_b/16) pages in order       */

@@ -30,6 +30,8 @@ the design notes of the repository):
 * R^T is applied to the query (as qR) and once to the attention output, which
   equals dequantize-then-rotate-back per token because R is orthogonal.
 * A sequence of length 0 attends to nothing and its output is zero.
+* A page-table entry outside [0, num_pages) marks an absent page: its
+  positions are neither written nor attended.
 
 Packed page layout.  The pages fix only that rotation keeps a regular paged
 layout; the byte layout below is this repository's format, stated here in
@@ -271,18 +273,27 @@ def check_orthogonal_all(r: np.ndarray, tol: float = 1e-6) -> None:
 
 
 # ----------------------------------------------------------- reading the cache
-def gather_sequence(pool, num_kv_heads, table_row, seq_len, h):
-    """Dequantized rotated keys x_hat and values w_hat [T, 128] of one sequence and KV head (fp64)."""
+def gather_sequence(pool, num_kv_heads, table_row, seq_len, h, num_pages=None):
+    """Dequantized rotated keys x_hat and values w_hat [T', 128] of one sequence and KV head (fp64).
+
+    A table entry outside [0, num_pages) marks an absent page: its positions
+    are left out, so T' = T minus the positions on absent pages.  ``num_pages``
+    defaults to the pool's size.
+    """
     T = int(seq_len)
     if T == 0:
         return np.zeros((0, HEAD_DIM)), np.zeros((0, HEAD_DIM))
     n_pages = (T + PAGE - 1) // PAGE
+    if num_pages is None:
+        num_pages = np.asarray(pool).size // (num_kv_heads * BLOCK_BYTES)
     pages = np.asarray(table_row[:n_pages], np.int64)
-    offs = (pages * num_kv_heads + int(h)) * BLOCK_BYTES
+    present = (pages >= 0) & (pages < num_pages)
+    offs = (np.where(present, pages, 0) * num_kv_heads + int(h)) * BLOCK_BYTES
     blocks = np.asarray(pool, np.uint8)[offs[:, None] + np.arange(BLOCK_BYTES)[None, :]]
     kc, ks, kz, vc, vs, vz = unpack_blocks(blocks)
-    x = int2_dequantize(kc, ks, kz).reshape(-1, HEAD_DIM)[:T]
-    w = int2_dequantize(vc, vs, vz).reshape(-1, HEAD_DIM)[:T]
+    keep = np.repeat(present, PAGE)[:T]
+    x = int2_dequantize(kc, ks, kz).reshape(-1, HEAD_DIM)[:T][keep]
+    w = int2_dequantize(vc, vs, vz).reshape(-1, HEAD_DIM)[:T][keep]
     return x, w
 
 
@@ -304,7 +315,7 @@ def softmax_attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray, scale
 
 
 def decode_attention(q, pool, num_kv_heads, page_table, seq_lens, r_k, r_v, sm_scale=None,
-                     heads=None, bypass=None) -> np.ndarray:
+                     heads=None, bypass=None, num_pages=None) -> np.ndarray:
     """Decode attention read from the packed cache (OptR §3.2 Eq. (5), §3.1 Eq. (4)).
 
     For query head j of sequence b, with h = j // g:
@@ -317,6 +328,8 @@ def decode_attention(q, pool, num_kv_heads, page_table, seq_lens, r_k, r_v, sm_s
     ``q`` is [B, H_q, 128]; returns fp64 [B, H_q, 128] (only ``heads`` = list
     of (b, j) pairs are filled when given; others stay zero).  ``bypass`` =
     (x, w, tok_seq) replaces the packed cache with unquantized rotated rows.
+    Pages whose table entry lies outside [0, num_pages) are absent: their
+    positions are not attended (a sequence with no present position outputs 0).
     """
     q = np.asarray(q, np.float64)
     B, Hq, d = q.shape
@@ -329,7 +342,7 @@ def decode_attention(q, pool, num_kv_heads, page_table, seq_lens, r_k, r_v, sm_s
         h = j // g
         if (b, h) not in cache:
             if bypass is None:
-                cache[(b, h)] = gather_sequence(pool, num_kv_heads, page_table[b], seq_lens[b], h)
+                cache[(b, h)] = gather_sequence(pool, num_kv_heads, page_table[b], seq_lens[b], h, num_pages)
             else:
                 x, w, tok_seq = bypass
                 sel = np.asarray(tok_seq) == b

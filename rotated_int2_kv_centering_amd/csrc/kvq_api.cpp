@@ -133,6 +133,86 @@ void shuffle(std::vector<int32_t>& v, SplitMix64& rng) {
   for (size_t i = v.size(); i > 1; --i) std::swap(v[i - 1], v[rng.below(i)]);
 }
 
+// Shared body of the decode entry points; k_new == nullptr is plain decode.
+kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* v_new, kvq_dtype kv_dtype,
+                         const float* mu, const void* q, kvq_dtype q_dtype, int32_t batch, int32_t num_q_heads,
+                         const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens, int32_t max_seq_len,
+                         const float* r_k, const float* r_v, float sm_scale, void* out, kvq_dtype out_dtype,
+                         void* workspace, size_t workspace_bytes_, int32_t num_splits, void* stream, void* ev_begin,
+                         void* ev_end) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (batch < 0) return fail(KVQ_EINVAL, "batch=%d must be >= 0", batch);
+  if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads != 0)
+    return fail(KVQ_EINVAL, "num_q_heads=%d must be a positive multiple of num_kv_heads=%d", num_q_heads,
+                cache->num_kv_heads);
+  const int g = num_q_heads / cache->num_kv_heads;
+  if (g > kMaxGroup) return fail(KVQ_EUNSUPPORTED, "query heads per KV head g=%d exceeds %d", g, kMaxGroup);
+  if (q_dtype != KVQ_BF16 && q_dtype != KVQ_F32) return fail(KVQ_EUNSUPPORTED, "q dtype must be bf16 or fp32");
+  if (out_dtype != KVQ_BF16 && out_dtype != KVQ_F32) return fail(KVQ_EUNSUPPORTED, "out dtype must be bf16 or fp32");
+  const bool stepping = k_new != nullptr || v_new != nullptr;
+  if (stepping && (k_new == nullptr || v_new == nullptr))
+    return fail(KVQ_EINVAL, "k_new and v_new must both be non-NULL");
+  if (stepping && kv_dtype != KVQ_BF16 && kv_dtype != KVQ_F32)
+    return fail(KVQ_EUNSUPPORTED, "new-token dtype must be bf16 or fp32");
+  if (max_seq_len < 0) return fail(KVQ_EINVAL, "max_seq_len=%d must be >= 0", max_seq_len);
+  if (num_splits < 0) return fail(KVQ_EINVAL, "num_splits=%d must be >= 0", num_splits);
+  if (max_pages < (max_seq_len + kPage - 1) / kPage)
+    return fail(KVQ_EINVAL, "max_pages=%d cannot hold max_seq_len=%d", max_pages, max_seq_len);
+  if (batch > 0 && max_seq_len > 0 && cache->num_pages == 0) return fail(KVQ_ENOSPACE, "cache has no pages");
+  if (std::isnan(sm_scale) || std::isinf(sm_scale) || sm_scale < 0.0f)
+    return fail(KVQ_EINVAL, "sm_scale must be finite and >= 0");
+  if (batch == 0) return KVQ_OK;
+  if (q == nullptr || page_table == nullptr || seq_lens == nullptr || r_k == nullptr || r_v == nullptr ||
+      out == nullptr || workspace == nullptr)
+    return fail(KVQ_EINVAL, "q, page_table, seq_lens, r_k, r_v, out and workspace must be non-NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return fail(KVQ_EINVAL, "workspace must be 16-byte aligned");
+  if (static_cast<long long>(batch) * num_q_heads > 0x7fffffffLL / kRowStride)
+    return fail(KVQ_EUNSUPPORTED, "batch * num_q_heads too large");
+
+  if (max_seq_len > kMaxContext)
+    return fail(KVQ_EUNSUPPORTED, "max_seq_len=%d exceeds the supported %lld", max_seq_len, kMaxContext);
+  kvq::DecodePlan plan;
+  if (!make_plan(batch, cache->num_kv_heads, g, max_seq_len, num_splits, &plan))
+    return fail(KVQ_EINVAL, "cannot plan the decode split");
+  const size_t need = workspace_bytes(batch, num_q_heads, cache->num_kv_heads, plan);
+  if (workspace_bytes_ < need)
+    return fail(KVQ_ENOSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes_, need);
+  if (static_cast<long long>(batch) * cache->num_kv_heads * plan.n_splits > 0x7fffffffLL)
+    return fail(KVQ_EUNSUPPORTED, "grid too large");
+
+  const float scale = sm_scale == 0.0f ? 1.0f / std::sqrt(static_cast<float>(kHeadDim)) : sm_scale;
+  kvq::DecodeParams a;
+  a.pool = static_cast<uint8_t*>(cache->pool);
+  a.num_kv_heads = cache->num_kv_heads;
+  a.num_pages = cache->num_pages;
+  a.q = q;
+  a.q_kind = q_dtype == KVQ_BF16 ? 0 : 1;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.g = g;
+  a.page_table = page_table;
+  a.max_pages = max_pages;
+  a.seq_lens = seq_lens;
+  a.r_k = r_k;
+  a.r_v = r_v;
+  a.logit_scale = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);  // log2(e)
+  a.out = out;
+  a.out_kind = out_dtype == KVQ_BF16 ? 0 : 1;
+  a.counters = static_cast<int32_t*>(workspace);
+  a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + counters_bytes(batch, cache->num_kv_heads));
+  a.pages_per_split = plan.pages_per_split;
+  a.n_splits = plan.n_splits;
+  a.k_new = stepping ? k_new : nullptr;
+  a.v_new = stepping ? v_new : nullptr;
+  a.kv_kind = kv_dtype == KVQ_BF16 ? 0 : 1;
+  a.mu = mu;
+  hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_begin),
+                                    static_cast<hipEvent_t>(ev_end));
+  if (e != hipSuccess) return hip_fail(e, stepping ? "decode step launch" : "decode launch");
+  return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -175,9 +255,9 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const void* q, kvq_dtype q_dt
                            const int32_t* seq_lens, int32_t max_seq_len, const float* r_k, const float* r_v,
                            float sm_scale, void* out, kvq_dtype out_dtype, void* workspace, size_t workspace_bytes_,
                            int32_t num_splits, void* stream) {
-  return kvq_decode_attn_traced(cache, q, q_dtype, batch, num_q_heads, page_table, max_pages, seq_lens, max_seq_len,
-                                r_k, r_v, sm_scale, out, out_dtype, workspace, workspace_bytes_, num_splits, stream,
-                                nullptr, nullptr);
+  return decode_common(cache, nullptr, nullptr, KVQ_BF16, nullptr, q, q_dtype, batch, num_q_heads, page_table,
+                       max_pages, seq_lens, max_seq_len, r_k, r_v, sm_scale, out, out_dtype, workspace,
+                       workspace_bytes_, num_splits, stream, nullptr, nullptr);
 }
 
 kvq_status kvq_decode_attn_traced(const kvq_cache* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
@@ -186,68 +266,21 @@ kvq_status kvq_decode_attn_traced(const kvq_cache* cache, const void* q, kvq_dty
                                   float sm_scale, void* out, kvq_dtype out_dtype, void* workspace,
                                   size_t workspace_bytes_, int32_t num_splits, void* stream, void* ev_begin,
                                   void* ev_end) {
-  kvq_status st = check_cache(cache);
-  if (st != KVQ_OK) return st;
-  if (batch < 0) return fail(KVQ_EINVAL, "batch=%d must be >= 0", batch);
-  if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads != 0)
-    return fail(KVQ_EINVAL, "num_q_heads=%d must be a positive multiple of num_kv_heads=%d", num_q_heads,
-                cache->num_kv_heads);
-  const int g = num_q_heads / cache->num_kv_heads;
-  if (g > kMaxGroup) return fail(KVQ_EUNSUPPORTED, "query heads per KV head g=%d exceeds %d", g, kMaxGroup);
-  if (q_dtype != KVQ_BF16 && q_dtype != KVQ_F32) return fail(KVQ_EUNSUPPORTED, "q dtype must be bf16 or fp32");
-  if (out_dtype != KVQ_BF16 && out_dtype != KVQ_F32) return fail(KVQ_EUNSUPPORTED, "out dtype must be bf16 or fp32");
-  if (max_seq_len < 0) return fail(KVQ_EINVAL, "max_seq_len=%d must be >= 0", max_seq_len);
-  if (num_splits < 0) return fail(KVQ_EINVAL, "num_splits=%d must be >= 0", num_splits);
-  if (max_pages < (max_seq_len + kPage - 1) / kPage)
-    return fail(KVQ_EINVAL, "max_pages=%d cannot hold max_seq_len=%d", max_pages, max_seq_len);
-  if (batch > 0 && max_seq_len > 0 && cache->num_pages == 0) return fail(KVQ_ENOSPACE, "cache has no pages");
-  if (std::isnan(sm_scale) || std::isinf(sm_scale) || sm_scale < 0.0f)
-    return fail(KVQ_EINVAL, "sm_scale must be finite and >= 0");
-  if (batch == 0) return KVQ_OK;
-  if (q == nullptr || page_table == nullptr || seq_lens == nullptr || r_k == nullptr || r_v == nullptr ||
-      out == nullptr || workspace == nullptr)
-    return fail(KVQ_EINVAL, "q, page_table, seq_lens, r_k, r_v, out and workspace must be non-NULL");
-  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return fail(KVQ_EINVAL, "workspace must be 16-byte aligned");
-  if (static_cast<long long>(batch) * num_q_heads > 0x7fffffffLL / kRowStride)
-    return fail(KVQ_EUNSUPPORTED, "batch * num_q_heads too large");
+  return decode_common(cache, nullptr, nullptr, KVQ_BF16, nullptr, q, q_dtype, batch, num_q_heads, page_table,
+                       max_pages, seq_lens, max_seq_len, r_k, r_v, sm_scale, out, out_dtype, workspace,
+                       workspace_bytes_, num_splits, stream, ev_begin, ev_end);
+}
 
-  if (max_seq_len > kMaxContext)
-    return fail(KVQ_EUNSUPPORTED, "max_seq_len=%d exceeds the supported %lld", max_seq_len, kMaxContext);
-  kvq::DecodePlan plan;
-  if (!make_plan(batch, cache->num_kv_heads, g, max_seq_len, num_splits, &plan))
-    return fail(KVQ_EINVAL, "cannot plan the decode split");
-  const size_t need = workspace_bytes(batch, num_q_heads, cache->num_kv_heads, plan);
-  if (workspace_bytes_ < need)
-    return fail(KVQ_ENOSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes_, need);
-  if (static_cast<long long>(batch) * cache->num_kv_heads * plan.n_splits > 0x7fffffffLL)
-    return fail(KVQ_EUNSUPPORTED, "grid too large");
-
-  const float scale = sm_scale == 0.0f ? 1.0f / std::sqrt(static_cast<float>(kHeadDim)) : sm_scale;
-  kvq::DecodeParams a;
-  a.pool = static_cast<const uint8_t*>(cache->pool);
-  a.num_kv_heads = cache->num_kv_heads;
-  a.num_pages = cache->num_pages;
-  a.q = q;
-  a.q_kind = q_dtype == KVQ_BF16 ? 0 : 1;
-  a.batch = batch;
-  a.num_q_heads = num_q_heads;
-  a.g = g;
-  a.page_table = page_table;
-  a.max_pages = max_pages;
-  a.seq_lens = seq_lens;
-  a.r_k = r_k;
-  a.r_v = r_v;
-  a.logit_scale = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);  // log2(e)
-  a.out = out;
-  a.out_kind = out_dtype == KVQ_BF16 ? 0 : 1;
-  a.counters = static_cast<int32_t*>(workspace);
-  a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + counters_bytes(batch, cache->num_kv_heads));
-  a.pages_per_split = plan.pages_per_split;
-  a.n_splits = plan.n_splits;
-  hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_begin),
-                                    static_cast<hipEvent_t>(ev_end));
-  if (e != hipSuccess) return hip_fail(e, "decode launch");
-  return KVQ_OK;
+kvq_status kvq_decode_step(const kvq_cache* cache, const void* k_new, const void* v_new, kvq_dtype kv_dtype,
+                           const float* mu, const void* q, kvq_dtype q_dtype, int32_t batch, int32_t num_q_heads,
+                           const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
+                           int32_t max_seq_len, const float* r_k, const float* r_v, float sm_scale, void* out,
+                           kvq_dtype out_dtype, void* workspace, size_t workspace_bytes_, int32_t num_splits,
+                           void* stream, void* ev_begin, void* ev_end) {
+  if (k_new == nullptr || v_new == nullptr) return fail(KVQ_EINVAL, "k_new and v_new must be non-NULL");
+  return decode_common(cache, k_new, v_new, kv_dtype, mu, q, q_dtype, batch, num_q_heads, page_table, max_pages,
+                       seq_lens, max_seq_len, r_k, r_v, sm_scale, out, out_dtype, workspace, workspace_bytes_,
+                       num_splits, stream, ev_begin, ev_end);
 }
 
 kvq_status kvq_page_table(int32_t policy, uint64_t seed, const int32_t* seq_lens, int32_t batch, int32_t page_size,

@@ -8,19 +8,15 @@
 //
 // Work decomposition: one workgroup of 256 threads per (tile of 16 tokens,
 // KV head, tensor K or V).  For the rotation, thread (j, half) sums rows
-// [64*half, 64*half + 64) of column j of R for all 16 tokens, with its 64 R
-// loads issued up front (column j is read coalesced across threads); the two
-// halves are added through LDS.  For quantization, each half takes 8 tokens
-// and thread j owns rotated channel j: groups of 32 channels are the two
-// 32-lane halves of each wave, so min/max are shuffle reductions in a wave.
-//
-// Stores: a token's K code words belong to that token alone (plain stores);
-// its metadata too.  A V code word holds 8 codes of each of two slots, so V
-// words are updated with 32-bit atomic and/or of the token's own bits, which
-// keeps concurrent appends to other slots of the same page correct.
+// [64*half, 64*half + 64) of column j of R for all 16 tokens as two fma chains
+// of 32 rows, with its 64 R loads issued up front (column j is read coalesced
+// across threads); the two halves are added through LDS, which is the shared
+// summation order of kvq_quant.h.  For quantization, each half takes 8 tokens
+// and thread j owns rotated channel j (kvq_quant.h: q2_pack_channel).
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_quant.h"
 
 namespace kvq {
 
@@ -66,11 +62,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     for (int ii = 0; ii < 64; ++ii) rv[ii] = R[ii * kHeadDim];  // all loads in flight at once
     float x[kAppendTile];
 #pragma unroll
-    for (int t = 0; t < kAppendTile; ++t) x[t] = 0.0f;
-#pragma unroll
-    for (int ii = 0; ii < 64; ++ii)
-#pragma unroll
-      for (int t = 0; t < kAppendTile; ++t) x[t] = fmaf(rows[t][64 * half + ii], rv[ii], x[t]);
+    for (int t = 0; t < kAppendTile; ++t) x[t] = rot_chains<64>(&rows[t][64 * half], rv);
 #pragma unroll
     for (int t = 0; t < kAppendTile; ++t) xpart[half][t][j] = x[t];
     __syncthreads();
@@ -80,9 +72,6 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
 
   // Quantize and pack: this half handles tokens 8*half .. 8*half + 7; within it,
   // wave w2 = (tid >> 6) & 1 holds channels 64*w2 .. 64*w2 + 63 (groups 2*w2, 2*w2 + 1).
-  const int lane = tid & 63;
-  const int w2 = (tid >> 6) & 1;
-  const int grp = j >> 5;
 #pragma unroll
   for (int tt = 0; tt < kAppendTile / 2; ++tt) {
     const int t = 8 * half + tt;
@@ -92,61 +81,9 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     const float xv = xpart[0][t][j];
     if (rot_out != nullptr) rot_out[((static_cast<size_t>(n) * num_kv_heads + h) * 2 + tensor) * kHeadDim + j] = xv;
 
-    // Q2 on the 32-channel group held by this 32-lane half-wave.
-    float mn = xv, mx = xv;
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) {
-      mn = fminf(mn, __shfl_xor(mn, off));
-      mx = fmaxf(mx, __shfl_xor(mx, off));
-    }
-    const float s32 = (mx - mn) / 3.0f;
-    const _Float16 s16 = static_cast<_Float16>(s32);
-    const _Float16 z16 = static_cast<_Float16>(mn);
-    const float sc = static_cast<float>(s16);
-    const float z = static_cast<float>(z16);
-    uint32_t code = 0;
-    if (sc != 0.0f) {
-      const float u = (xv - z) / sc;
-      code = static_cast<uint32_t>(fminf(fmaxf(rintf(u), 0.0f), 3.0f));
-    }
-
     const int page = slot >> 4;
-    const int off = slot & 15;
     uint8_t* block = pool + (static_cast<size_t>(page) * num_kv_heads + h) * kBlockBytes;
-
-    if (tensor == 0) {
-      // K: channel j -> kk = j/32, a = (j%32)/8, e = j%8; record 16a + off,
-      // word kk/2 (= w2), bit 2*(4*(kk%2) + e/2) + 16*(e%2).
-      const int kk = grp, a = (j & 31) >> 3, e = j & 7;
-      uint32_t w = code << (2 * (4 * (kk & 1) + (e >> 1)) + 16 * (e & 1));
-      w |= __shfl_xor(w, 1);
-      w |= __shfl_xor(w, 2);
-      w |= __shfl_xor(w, 4);
-      w |= __shfl_xor(w, 32);
-      if ((lane & 39) == 0) {  // e == 0 and kk%2 == 0: lanes 0, 8, 16, 24
-        *reinterpret_cast<uint32_t*>(block + 16 * (16 * a + off) + 4 * w2) = w;
-      }
-    } else {
-      // V: channel j -> t = j/16, b = j%16; slot -> a = off/4, i = off%4;
-      // record 16a + b, word V[i/2], bit 2t + 16*(i%2).
-      const int t16 = j >> 4, b = j & 15, a = off >> 2, i = off & 3;
-      const int shift = 16 * (i & 1);
-      uint32_t w = code << (2 * t16 + shift);
-      w |= __shfl_xor(w, 16);
-      w |= __shfl_xor(w, 32);
-      if (lane < 16) {
-        uint32_t* word = reinterpret_cast<uint32_t*>(block + 16 * (16 * a + b) + 8 + 4 * (i >> 1));
-        const uint32_t mask = 0xffu << (8 * w2 + shift);  // this wave's four tiles
-        atomicAnd(word, ~mask);
-        atomicOr(word, w);
-      }
-    }
-    if ((j & 31) == 0) {
-      const uint32_t pair = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, s16)) |
-                            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, z16)) << 16);
-      const int rec = 4 * grp + (off >> 2);
-      *reinterpret_cast<uint32_t*>(block + kCodeBytes + kMetaRecordBytes * rec + 16 * tensor + 4 * (off & 3)) = pair;
-    }
+    (void)q2_pack_channel(xv, j, tensor, block, slot & 15);
   }
 }
 

@@ -47,6 +47,7 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_quant.h"
 
 namespace kvq {
 
@@ -106,6 +107,12 @@ void decode_kernel(const DecodeParams p) {
   __shared__ float s_m[kW][kNH];
   __shared__ float s_l[kW][kNH];
   __shared__ int s_ticket;
+  // step form: the new token's centred key and value rows, rotation partials,
+  // rotated vectors, dequantized levels and per-head logits
+  __shared__ float s_nrow[2][kHeadDim];
+  __shared__ float s_npart[2][4][kHeadDim];
+  __shared__ float s_hat[2][kHeadDim];
+  __shared__ float s_nlog[kNH];
   // One LDS object per ring slot (distinct objects: loads into one slot never
   // alias reads of another): [wave][part][lane], part 0/1 = 64 x 16 B codes
   // of page 0/1, part 2 = 32 x 16 B metadata of page 0 then of page 1.
@@ -148,6 +155,12 @@ void decode_kernel(const DecodeParams p) {
   if (p0 >= n_pages) return;  // whole workgroup
   const int np = min(pps, n_pages - p0);
   const int npairs = (np + 1) >> 1;
+  // Step form: the last split appends the token at position T - 1 and attends
+  // it from its packed levels; the paged read masks that position, whose slot
+  // may still hold an older token (and is rewritten during this launch).
+  const bool stepping = p.k_new != nullptr;
+  const bool own = stepping && split == n_valid - 1;
+  const int T_read = stepping ? T - 1 : T;
 
   // ---- prologue loads, all issued before the first wait: this split's page
   // ids, the g query rows and R_K.  Indices are clamped in bounds and values
@@ -172,7 +185,7 @@ void decode_kernel(const DecodeParams p) {
   // [kRows * rpart, +kRows) of R_K; threads past the last part repeat it.
   constexpr int kParts = kThreads >= 4 * kHeadDim ? 4 : kThreads / kHeadDim;
   constexpr int kRows = kHeadDim / kParts;
-  static_assert(kParts >= 1 && kParts <= kW, "row parts fit in s_buf");
+  static_assert(kParts >= 2 && kParts <= kW, "row parts fit in s_buf");
   const int rc = tid & (kHeadDim - 1);
   const int rpart = min(tid / kHeadDim, kParts - 1);
   float rv[kRows];
@@ -180,6 +193,22 @@ void decode_kernel(const DecodeParams p) {
     const float* R = p.r_k + (static_cast<size_t>(h) * kHeadDim + kRows * rpart) * kHeadDim + rc;
 #pragma unroll
     for (int ii = 0; ii < kRows; ++ii) rv[ii] = R[ii * kHeadDim];
+  }
+  // step form, appending workgroup: the new key (centred, fp32) and value rows
+  // and the same rows of R_V
+  float nrow = 0.0f;
+  float rvv[kRows];
+  if (own) {
+    if (tid < 2 * kHeadDim) {
+      const int tensor = tid / kHeadDim;
+      const size_t ni = (static_cast<size_t>(b) * H + h) * kHeadDim + rc;
+      const void* src = tensor == 0 ? p.k_new : p.v_new;
+      nrow = p.kv_kind == 0 ? bf16_bits_to_f32(static_cast<const uint16_t*>(src)[ni]) : static_cast<const float*>(src)[ni];
+      if (tensor == 0 && p.mu != nullptr) nrow = nrow - p.mu[h * kHeadDim + rc];  // key centering (fp32)
+    }
+    const float* R = p.r_v + (static_cast<size_t>(h) * kHeadDim + kRows * rpart) * kHeadDim + rc;
+#pragma unroll
+    for (int ii = 0; ii < kRows; ++ii) rvv[ii] = R[ii * kHeadDim];
   }
 #pragma unroll
   for (int u = 0; u < kPidPerThread; ++u) {
@@ -191,7 +220,10 @@ void decode_kernel(const DecodeParams p) {
     const int idx = tid + u * kThreads;
     if (idx < kNH * kHeadDim) s_q[idx / kHeadDim][idx % kHeadDim] = qld[u];
   }
+  if (own && tid < 2 * kHeadDim) s_nrow[tid / kHeadDim][rc] = nrow;
   __syncthreads();
+  // the new token's slot: position T - 1 on the split's last page (masked page: no append)
+  const bool new_ok = own && s_pages[np - 1] >= 0;
 
   const int a = lane >> 4;    // row of 16 lanes: token quad (QK) / channel octet
   const int col = lane & 15;  // MFMA column: 4*grp + jj
@@ -237,6 +269,10 @@ void decode_kernel(const DecodeParams p) {
     }
 #pragma unroll
     for (int jh = 0; jh < kNH; ++jh) s_buf[rpart][jh][rc] = accq[jh];
+    if (new_ok) {  // rotation partials of the new key and value (shared summation order)
+      s_npart[0][rpart][rc] = rot_chains<kRows>(&s_nrow[0][kRows * rpart], rv);
+      s_npart[1][rpart][rc] = rot_chains<kRows>(&s_nrow[1][kRows * rpart], rvv);
+    }
   }
   __syncthreads();
   for (int idx = tid; idx < kNH * kHeadDim; idx += kThreads) {
@@ -247,7 +283,20 @@ void decode_kernel(const DecodeParams p) {
     for (int u = 0; u < kParts; ++u) sum += s_buf[u][jh][c];
     s_q[jh][c] = sum * p.logit_scale;
   }
+  if (new_ok && tid < 2 * kHeadDim) {
+    const int tensor = tid / kHeadDim;
+    const float x = kParts == 4 ? (s_npart[tensor][0][rc] + s_npart[tensor][1][rc]) +
+                                      (s_npart[tensor][2][rc] + s_npart[tensor][3][rc])
+                                : s_npart[tensor][0][rc] + s_npart[tensor][1][rc];
+    s_nrow[tensor][rc] = x;  // rotated
+  }
   __syncthreads();
+  if (new_ok && tid < 2 * kHeadDim) {  // quantize-append the new token (two waves per tensor)
+    const int tensor = tid / kHeadDim;
+    const int pos = T - 1;
+    uint8_t* blk = p.pool + (static_cast<size_t>(s_pages[np - 1]) * H + h) * kBlockBytes;
+    s_hat[tensor][rc] = q2_pack_channel(s_nrow[tensor][rc], rc, tensor, blk, pos & (kPage - 1));
+  }
   for (int jh = wave; jh < kNH; jh += kW) {
     float am = fmaxf(fabsf(s_q[jh][lane]), fabsf(s_q[jh][lane + 64]));
 #pragma unroll
@@ -259,6 +308,14 @@ void decode_kernel(const DecodeParams p) {
     }
   }
   __syncthreads();
+  if (new_ok) {  // logits (log2 units) of the new token: one wave per head
+    for (int jh = wave; jh < g; jh += kW) {
+      float d = fmaf(s_q[jh][lane], s_hat[0][lane], s_q[jh][lane + 64] * s_hat[0][lane + 64]);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+      if (lane == 0) s_nlog[jh] = d;
+    }
+  }
 
   // ---- block-diagonal query operands (fp16 hi/lo of q_hat * f)
   half8 qhi[kNQ][4], qlo[kNQ][4];
@@ -350,7 +407,7 @@ void decode_kernel(const DecodeParams p) {
         for (int i = 0; i < 4; ++i) {
           float s = fmaf(C[i], sk[i], zk[i] * qz[Q]);
           s = row_sum_stride4(s);
-          sp[Q][X][i] = (page_ok && pos0 + i < T) ? s : -INFINITY;
+          sp[Q][X][i] = (page_ok && pos0 + i < T_read) ? s : -INFINITY;
         }
       }
     }
@@ -459,12 +516,18 @@ void decode_kernel(const DecodeParams p) {
     float M = kNegBig;
 #pragma unroll
     for (int w = 0; w < kW; ++w) M = fmaxf(M, s_m[w][jh]);
+    if (new_ok) M = fmaxf(M, s_nlog[jh]);
     float av = 0.0f, lv = 0.0f;
 #pragma unroll
     for (int w = 0; w < kW; ++w) {
       const float wt = __builtin_amdgcn_exp2f(s_m[w][jh] - M);
       av = fmaf(wt, s_buf[w][jh][c], av);
       lv = fmaf(wt, s_l[w][jh], lv);
+    }
+    if (new_ok) {  // the new token, weight exp2(logit - M), level w_hat
+      const float wt = __builtin_amdgcn_exp2f(s_nlog[jh] - M);
+      av = fmaf(wt, s_hat[1][c], av);
+      lv += wt;
     }
     float* dst = p.part + ((head_base + split) * g + jh) * kPartStride;
     __hip_atomic_store(dst + c, av, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

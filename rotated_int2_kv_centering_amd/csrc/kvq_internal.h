@@ -18,7 +18,7 @@ struct DecodePlan {
 
 // Kernel arguments of the fused decode (passed by value).
 struct DecodeParams {
-  const uint8_t* pool;
+  uint8_t* pool;  // written only by the step form (the new token's slot)
   int num_kv_heads;
   int num_pages;
   const void* q;
@@ -38,6 +38,14 @@ struct DecodeParams {
   int32_t* counters;   // [batch][num_kv_heads], zero between calls
   int pages_per_split;
   int n_splits;
+  // Step form: when k_new is non-null, the token at position seq_lens[b] - 1 of
+  // every sequence is first quantize-appended from k_new/v_new [batch][H_kv][128]
+  // (kv_kind 0 bf16, 1 fp32; mu [H_kv][128] or null) by the workgroup whose
+  // split holds that position, and attended from its packed levels.
+  const void* k_new;
+  const void* v_new;
+  int kv_kind;
+  const float* mu;
 };
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end);

@@ -1,0 +1,100 @@
+// Rotation and Q2 quantize-pack of one token, shared by the append kernel and
+// the fused decode step so that both write identical bytes.
+//
+// OptR ("Output-Oriented Rotation for INT2 KV-Cache Quantization"), section 3.1,
+// Eq. (4): the cache stores Q2(zR).  Q2 here is asymmetric over groups of 32
+// consecutive rotated channels: s = fp16(fp32(max - min) / 3), z = fp16(min),
+// code = clamp(rint((x - z) / s), 0, 3) computed with the stored fp16 s and z
+// (all codes 0 when s is 0); the dequantized level is z + s * code.
+#pragma once
+
+#include "kvq_device.h"
+
+namespace kvq {
+
+// Rotation summation order.  Every rotated channel x[j] = sum_i a[i] R[i][j]
+// is formed as four fma chains over the row ranges [0,32), [32,64), [64,96),
+// [96,128) (each started from 0 and taken in row order), added as
+// (c0 + c1) + (c2 + c3).  Both kernels follow it, so a token's rotated fp32
+// value, and hence its codes, do not depend on which kernel appended it.
+template <int kRows>  // 32 or 64 consecutive rows of R held by this thread, starting at row 32*chain0
+__device__ __forceinline__ float rot_chains(const float* a, const float* r) {
+  static_assert(kRows == 32 || kRows == 64, "one or two chains");
+  float c0 = 0.0f;
+#pragma unroll
+  for (int ii = 0; ii < 32; ++ii) c0 = fmaf(a[ii], r[ii], c0);
+  if (kRows == 32) return c0;
+  float c1 = 0.0f;
+#pragma unroll
+  for (int ii = 32; ii < kRows; ++ii) c1 = fmaf(a[ii], r[ii], c1);
+  return c0 + c1;
+}
+
+// Quantizes channel j of one token's rotated vector and packs it into a block.
+// Called by the 128 threads j = 0..127 of one (token, KV head, tensor), laid
+// out as two whole waves (j = 64 * w2 + lane), so each 32-lane half-wave holds
+// one channel group.  `block` is the (page, KV head) block to write, or null to
+// only compute; `off` is the slot within the page (0..15); tensor 0 = K, 1 = V.
+// Returns the dequantized level of channel j.
+//
+// K code of slot s, channel c (kk = c/32, a = (c%32)/8, e = c%8): record
+// 16a + s, word K[kk/2], bit 2(4(kk%2) + e/2) + 16(e%2).  V code (t = c/16,
+// b = c%16, a = s/4, i = s%4): record 16a + b, word V[i/2], bit 2t + 16(i%2).
+// Metadata of slot s, group grp: record 4grp + s/4 at byte 1024 + 32*record,
+// K pair at +4(s%4), V pair at +16 + 4(s%4), each (fp16 scale, fp16 zero).
+// A K code word and a metadata pair belong to one slot (plain stores); a V
+// code word holds codes of two slots, so it is updated with atomic and/or of
+// this slot's bits only, which keeps concurrent writes to other slots intact.
+__device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, uint8_t* block, int off) {
+  const int lane = j & 63;
+  const int w2 = j >> 6;
+  const int grp = j >> 5;
+  float mn = xv, mx = xv;
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, o));
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+  }
+  const float s32 = (mx - mn) / 3.0f;
+  const _Float16 s16 = static_cast<_Float16>(s32);
+  const _Float16 z16 = static_cast<_Float16>(mn);
+  const float sc = static_cast<float>(s16);
+  const float z = static_cast<float>(z16);
+  uint32_t code = 0;
+  if (sc != 0.0f) {
+    const float u = (xv - z) / sc;
+    code = static_cast<uint32_t>(fminf(fmaxf(rintf(u), 0.0f), 3.0f));
+  }
+
+  if (tensor == 0) {
+    const int kk = grp, a = (j & 31) >> 3, e = j & 7;
+    uint32_t w = code << (2 * (4 * (kk & 1) + (e >> 1)) + 16 * (e & 1));
+    w |= __shfl_xor(w, 1);
+    w |= __shfl_xor(w, 2);
+    w |= __shfl_xor(w, 4);
+    w |= __shfl_xor(w, 32);
+    if (block != nullptr && (lane & 39) == 0)  // e == 0, kk even: lanes 0, 8, 16, 24 hold both groups' words
+      *reinterpret_cast<uint32_t*>(block + 16 * (16 * a + off) + 4 * w2) = w;
+  } else {
+    const int t16 = j >> 4, b = j & 15, a = off >> 2, i = off & 3;
+    const int shift = 16 * (i & 1);
+    uint32_t w = code << (2 * t16 + shift);
+    w |= __shfl_xor(w, 16);
+    w |= __shfl_xor(w, 32);
+    if (block != nullptr && lane < 16) {
+      uint32_t* word = reinterpret_cast<uint32_t*>(block + 16 * (16 * a + b) + 8 + 4 * (i >> 1));
+      const uint32_t mask = 0xffu << (8 * w2 + shift);  // this wave's four tiles of this slot
+      atomicAnd(word, ~mask);
+      atomicOr(word, w);
+    }
+  }
+  if (block != nullptr && (j & 31) == 0) {
+    const uint32_t pair = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, s16)) |
+                          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, z16)) << 16);
+    const int rec = 4 * grp + (off >> 2);
+    *reinterpret_cast<uint32_t*>(block + kCodeBytes + kMetaRecordBytes * rec + 16 * tensor + 4 * (off & 3)) = pair;
+  }
+  return fmaf(sc, static_cast<float>(code), z);
+}
+
+}  // namespace kvq

@@ -66,6 +66,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_decode_attn.restype = I32
     lib.kvq_decode_attn_traced.argtypes = [CP, P, I32, I32, I32, P, I32, P, I32, P, P, F, P, I32, P, SZ, I32, P, P, P]
     lib.kvq_decode_attn_traced.restype = I32
+    lib.kvq_decode_step.argtypes = [CP, P, P, I32, P, P, I32, I32, I32, P, I32, P, I32, P, P, F, P, I32, P, SZ, I32,
+                                    P, P, P]
+    lib.kvq_decode_step.restype = I32
     lib.kvq_page_table.argtypes = [I32, U64, P, I32, I32, I32, I32, P, P]
     lib.kvq_page_table.restype = I32
     lib.kvq_last_error.argtypes = []
@@ -149,6 +152,17 @@ def kvq_decode_attn_traced(cache: kvq_cache, q, q_dtype: int, batch: int, num_q_
                                          max_pages, _ptr(seq_lens), max_seq_len, _ptr(r_k), _ptr(r_v),
                                          float(sm_scale), _ptr(out), out_dtype, _ptr(workspace), int(workspace_bytes),
                                          num_splits, _stream(stream), ev_begin, ev_end))
+
+
+def kvq_decode_step(cache: kvq_cache, k_new, v_new, kv_dtype: int, mu, q, q_dtype: int, batch: int,
+                    num_q_heads: int, page_table, max_pages: int, seq_lens, max_seq_len: int, r_k, r_v,
+                    sm_scale: float, out, out_dtype: int, workspace, workspace_bytes: int, num_splits: int = 0,
+                    stream=None, ev_begin=None, ev_end=None) -> None:
+    """Append the newest token of every sequence (position seq_lens[b] - 1), then decode."""
+    _check(load().kvq_decode_step(ctypes.byref(cache), _ptr(k_new), _ptr(v_new), kv_dtype, _ptr(mu), _ptr(q), q_dtype,
+                                  batch, num_q_heads, _ptr(page_table), max_pages, _ptr(seq_lens), max_seq_len,
+                                  _ptr(r_k), _ptr(r_v), float(sm_scale), _ptr(out), out_dtype, _ptr(workspace),
+                                  int(workspace_bytes), num_splits, _stream(stream), ev_begin, ev_end))
 
 
 def kvq_page_table(policy: int, seed: int, seq_lens, page_size: int, num_pages: int, max_pages: int, table=None):

@@ -95,6 +95,28 @@ class DeviceCase:
             return out.cpu().numpy()
         return out.view(torch.int16).cpu().numpy().view(np.uint16)
 
+    def step(self, k_new, v_new, out_dtype="f32", num_splits=0, ws=None, mu="case"):
+        """kvq_decode_step with the case's queries, tables and lengths; k_new/v_new are
+        device tensors [B][H_kv][128] in the case's dtype."""
+        from rotated_int2_kv_centering_amd import kvq
+        c = self.c
+        max_seq = int(c.seq_lens.max(initial=0))
+        ws_bytes = kvq.kvq_decode_workspace_bytes(c.B, c.Hq, c.Hkv, max_seq, num_splits)
+        if ws is None:
+            ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=self.dev)
+        else:
+            ws_bytes = ws.numel()
+        tdt = torch.float32 if out_dtype == "f32" else torch.bfloat16
+        out = torch.full((c.B, c.Hq, 128), float("nan"), dtype=tdt, device=self.dev)
+        kvq.kvq_decode_step(self.cache, k_new, v_new, self.in_dtype, self.mu if mu == "case" else mu, self.q,
+                            self.in_dtype, c.B, c.Hq, self.table, int(self.table.shape[1]), self.seq_lens, max_seq,
+                            self.r_k, self.r_v, 0.0, out, kvq.KVQ_F32 if out_dtype == "f32" else kvq.KVQ_BF16, ws,
+                            ws_bytes, num_splits)
+        torch.cuda.synchronize()
+        if out_dtype == "f32":
+            return out.cpu().numpy()
+        return out.view(torch.int16).cpu().numpy().view(np.uint16)
+
     def pool_np(self) -> np.ndarray:
         return self.pool.cpu().numpy()
 

@@ -37,7 +37,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["kvq_pool_bytes", "kvq_quant_append", "kvq_decode_workspace_bytes", "kvq_decode_attn",
-                            "kvq_decode_attn_traced", "kvq_page_table", "kvq_last_error"]), names
+                            "kvq_decode_attn_traced", "kvq_decode_step", "kvq_page_table", "kvq_last_error"]), names
 
 
 def test_library_exports_exactly_the_declared_symbols(K):

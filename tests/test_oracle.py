@@ -377,6 +377,25 @@ def test_empty_sequence_gives_zero():
     assert not out[0].any() and np.abs(out[1]).max() > 0
 
 
+def test_absent_page_is_left_out():
+    """A page-table entry outside the pool marks an absent page: decode equals decode of the
+    same sequence with that page's tokens removed, laid out on fresh pages (brute-force layout)."""
+    c = _tiny(seq_lens=[64])  # 4 pages, contiguous 0..3
+    pool = np.zeros(O.pool_bytes(c.num_pages, 1), np.uint8)
+    O.append_tokens(pool, 1, c.slots, c.k, c.v, c.mu, c.r_k, c.r_v)
+    for bad in (c.num_pages, -1, 1 << 20):
+        table = c.page_table.copy()
+        table[0, 1] = bad  # positions 16..31 absent
+        got = O.decode_attention(c.q, pool, 1, table, c.seq_lens, c.r_k, c.r_v, num_pages=c.num_pages)
+        keep = np.r_[0:16, 32:64]
+        pool2 = np.zeros(O.pool_bytes(3, 1), np.uint8)
+        O.append_tokens(pool2, 1, np.arange(48), c.k[keep], c.v[keep], c.mu, c.r_k, c.r_v)
+        ref = O.decode_attention(c.q, pool2, 1, np.array([[0, 1, 2]]), np.array([48]), c.r_k, c.r_v)
+        np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+    table = np.full_like(c.page_table, -1)  # every page absent: nothing attended
+    assert not O.decode_attention(c.q, pool, 1, table, c.seq_lens, c.r_k, c.r_v).any()
+
+
 def test_output_error_decomposition_eq8():
     """OptR §3.2 Eq. (8): dy = dy_K + dy_V exactly (random W_O), Eq. (10) E_out = ||dy||^2."""
     rng = np.random.default_rng(18)
