@@ -53,20 +53,17 @@ namespace kvq {
 
 constexpr float kNegBig = -3.0e38f;  // finite "minus infinity" for running maxima
 constexpr float kTwo24 = 16777216.0f;
-#ifndef KVQ_RING_DEPTH
-#define KVQ_RING_DEPTH 3
-#endif
-// Page pairs per wave staged in LDS by direct global->LDS loads; kDepth - 1
-// pairs are in flight while one is computed.
-constexpr int kDepth = KVQ_RING_DEPTH;
+constexpr float kLazy = 8.0f;  // rescale threshold of the online softmax (log2 units)
 constexpr int kDmaPerPair = 4;  // K/V codes of page 0, of page 1; metadata of page 0, of page 1
-static_assert(kDepth >= 2 && kDepth <= 4, "ring depth 2..4");
 
-// Waves per workgroup and waves per SIMD the kernel is compiled for, by the
-// number of head quads: the g <= 4 kernel fits 3 waves per SIMD, so one
-// 12-wave workgroup fills a compute unit; the larger ones run 1 wave per SIMD.
-template <int kNQ> struct DecodeShape { static constexpr int waves = 4, waves_per_simd = 1; };
-template <> struct DecodeShape<1> { static constexpr int waves = 12, waves_per_simd = 3; };
+// Launch shape by the number of head quads: waves per workgroup, waves per
+// SIMD, and the per-wave ring depth (page pairs staged in LDS by direct
+// global->LDS loads; depth - 1 pairs are in flight while one is computed).
+// The g <= 4 kernel fits 3 waves per SIMD, so one 12-wave workgroup fills a
+// compute unit and its 4-slot rings use most of the LDS; the larger ones run
+// 1 wave per SIMD and keep more pairs in flight per wave instead.
+template <int kNQ> struct DecodeShape { static constexpr int waves = 4, waves_per_simd = 1, depth = 8; };
+template <> struct DecodeShape<1> { static constexpr int waves = 12, waves_per_simd = 3, depth = 3; };
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -95,31 +92,42 @@ __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int kNQ, int kW>  // quads of query heads (g <= 4 * kNQ), waves per workgroup
+template <int kNQ, int kW, int kDepth>  // quads of query heads (g <= 4 * kNQ), waves per workgroup, ring depth
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(DecodeShape<kNQ>::waves_per_simd)))
 void decode_kernel(const DecodeParams p) {
+  static_assert(kDepth >= 2 && kDmaPerPair * (kDepth - 1) <= 63, "ring depth within the vmcnt range");
   constexpr int kNH = 4 * kNQ;
   constexpr int kThreads = 64 * kW;
+  // q_hat and the new token's rotation: thread (column rc, part rpart) sums
+  // rows [kRows * rpart, +kRows) of R; threads past the last part repeat it.
+  constexpr int kParts = kThreads >= 4 * kHeadDim ? 4 : kThreads / kHeadDim;
+  constexpr int kRows = kHeadDim / kParts;
+  static_assert(kParts >= 2, "at least two row parts");
   __shared__ int s_pages[kMaxPagesPerSplit];
-  __shared__ float s_q[kNH][kHeadDim];        // q rows -> q_hat -> o_rot
-  __shared__ float s_buf[kW][kNH][kHeadDim];  // q_hat parts / per-wave partials / merge weights / R_V^T parts
+  __shared__ float s_q[kNH][kHeadDim];  // q rows -> q_hat -> o_rot
   __shared__ float s_f[kNH];
   __shared__ float s_m[kW][kNH];
   __shared__ float s_l[kW][kNH];
   __shared__ int s_ticket;
-  // step form: the new token's centred key and value rows, rotation partials,
-  // rotated vectors, dequantized levels and per-head logits
+  // step form: the new token's centred (then rotated) key and value rows,
+  // dequantized levels and per-head logits
   __shared__ float s_nrow[2][kHeadDim];
-  __shared__ float s_npart[2][4][kHeadDim];
   __shared__ float s_hat[2][kHeadDim];
   __shared__ float s_nlog[kNH];
-  // One LDS object per ring slot (distinct objects: loads into one slot never
-  // alias reads of another): [wave][part][lane], part 0/1 = 64 x 16 B codes
-  // of page 0/1, part 2 = 32 x 16 B metadata of page 0 then of page 1.
-  __shared__ uint4v s_ring0[kW][3][64];
-  __shared__ uint4v s_ring1[kW][3][64];
-  __shared__ uint4v s_ring2[kDepth > 2 ? kW : 1][3][64];
-  __shared__ uint4v s_ring3[kDepth > 3 ? kW : 1][3][64];
+  // Page-pair ring [slot][wave][part][lane]: part 0/1 = 64 x 16 B codes of
+  // page 0/1, part 2 = 32 x 16 B metadata of page 0 then of page 1.
+  __shared__ uint4v s_ring[kDepth][kW][3][64];
+  // Prologue scratch (q_hat partials [kParts][kNH][128], then the new token's
+  // partials [2][4][128]) lives in the last ring slot, which no load targets
+  // before the main loop, when it fits there.  After the main loop the whole
+  // ring holds the per-wave partials and then the R_V^T partial sums.
+  constexpr int kProFloats = (kParts * kNH + 2 * 4) * kHeadDim;
+  constexpr bool kProInRing = kProFloats * 4 <= kW * 3 * 64 * 16;
+  __shared__ float s_pro_sep[kProInRing ? 1 : kProFloats];
+  float* const s_pro = kProInRing ? reinterpret_cast<float*>(&s_ring[kDepth - 1][0][0][0]) : s_pro_sep;
+  float* const s_npart = s_pro + kParts * kNH * kHeadDim;
+  float* const s_post = reinterpret_cast<float*>(&s_ring[0][0][0][0]);
+  static_assert(sizeof(s_ring) >= sizeof(float) * kW * kNH * kHeadDim, "per-wave partials fit in the ring");
 
   const int H = p.num_kv_heads;
   const int g = p.g;
@@ -129,10 +137,8 @@ void decode_kernel(const DecodeParams p) {
   const int b = id / (H * p.n_splits);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  auto ring = [&](int slot) -> uint4v(*)[64] {
-    return slot == 0 ? s_ring0[wave] : slot == 1 ? s_ring1[wave] : slot == 2 ? s_ring2[wave] : s_ring3[wave];
-  };
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: ring addresses stay scalar
+  auto ring = [&](int slot) -> uint4v(*)[64] { return s_ring[slot][wave]; };
 
   // Pages past the table row are never read (a length beyond max_pages*16 is cut).
   const int T = min(p.seq_lens[b], p.max_pages * kPage);
@@ -170,22 +176,17 @@ void decode_kernel(const DecodeParams p) {
   int pid[kPidPerThread];
 #pragma unroll
   for (int u = 0; u < kPidPerThread; ++u) pid[u] = pt[min(tid + u * kThreads, np - 1)];
+  // q as raw dwords (the bf16 element's dword, or the fp32 element): one
+  // unconditional load each, converted after every prologue load is issued
   constexpr int kQPerThread = (kNH * kHeadDim + kThreads - 1) / kThreads;
-  float qld[kQPerThread];
+  uint32_t qraw[kQPerThread];
 #pragma unroll
   for (int u = 0; u < kQPerThread; ++u) {
     const int idx = min(tid + u * kThreads, kNH * kHeadDim - 1);
-    const int jh = idx / kHeadDim;
-    const size_t qi = (out_row0 + min(jh, g - 1)) * kHeadDim + idx % kHeadDim;
-    const float qraw = p.q_kind == 0 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[qi])
-                                     : static_cast<const float*>(p.q)[qi];
-    qld[u] = jh < g ? qraw : 0.0f;
+    const size_t qi = (out_row0 + min(idx / kHeadDim, g - 1)) * kHeadDim + idx % kHeadDim;
+    qraw[u] = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(p.q) +
+                                                 (p.q_kind == 0 ? (2 * qi) & ~static_cast<size_t>(3) : 4 * qi));
   }
-  // q_hat partial sums: thread (column rc, part rpart) takes rows
-  // [kRows * rpart, +kRows) of R_K; threads past the last part repeat it.
-  constexpr int kParts = kThreads >= 4 * kHeadDim ? 4 : kThreads / kHeadDim;
-  constexpr int kRows = kHeadDim / kParts;
-  static_assert(kParts >= 2 && kParts <= kW, "row parts fit in s_buf");
   const int rc = tid & (kHeadDim - 1);
   const int rpart = min(tid / kHeadDim, kParts - 1);
   float rv[kRows];
@@ -196,16 +197,13 @@ void decode_kernel(const DecodeParams p) {
   }
   // step form, appending workgroup: the new key (centred, fp32) and value rows
   // and the same rows of R_V
-  float nrow = 0.0f;
+  uint32_t nraw = 0, muraw = 0;
   float rvv[kRows];
+  const size_t ni = (static_cast<size_t>(b) * H + h) * kHeadDim + rc;
   if (own) {
-    if (tid < 2 * kHeadDim) {
-      const int tensor = tid / kHeadDim;
-      const size_t ni = (static_cast<size_t>(b) * H + h) * kHeadDim + rc;
-      const void* src = tensor == 0 ? p.k_new : p.v_new;
-      nrow = p.kv_kind == 0 ? bf16_bits_to_f32(static_cast<const uint16_t*>(src)[ni]) : static_cast<const float*>(src)[ni];
-      if (tensor == 0 && p.mu != nullptr) nrow = nrow - p.mu[h * kHeadDim + rc];  // key centering (fp32)
-    }
+    const uint8_t* src = static_cast<const uint8_t*>(tid < kHeadDim ? p.k_new : p.v_new);
+    nraw = *reinterpret_cast<const uint32_t*>(src + (p.kv_kind == 0 ? (2 * ni) & ~static_cast<size_t>(3) : 4 * ni));
+    muraw = *reinterpret_cast<const uint32_t*>(p.mu != nullptr ? p.mu + h * kHeadDim + rc : p.r_v);
     const float* R = p.r_v + (static_cast<size_t>(h) * kHeadDim + kRows * rpart) * kHeadDim + rc;
 #pragma unroll
     for (int ii = 0; ii < kRows; ++ii) rvv[ii] = R[ii * kHeadDim];
@@ -218,9 +216,25 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll
   for (int u = 0; u < kQPerThread; ++u) {
     const int idx = tid + u * kThreads;
-    if (idx < kNH * kHeadDim) s_q[idx / kHeadDim][idx % kHeadDim] = qld[u];
+    const size_t qi = (out_row0 + min(idx / kHeadDim, g - 1)) * kHeadDim + idx % kHeadDim;
+    const float qv = p.q_kind == 0 ? bf16_bits_to_f32(static_cast<uint16_t>(qraw[u] >> (16 * (qi & 1))))
+                                   : __uint_as_float(qraw[u]);
+    if (idx < kNH * kHeadDim) s_q[idx / kHeadDim][idx % kHeadDim] = idx / kHeadDim < g ? qv : 0.0f;
   }
-  if (own && tid < 2 * kHeadDim) s_nrow[tid / kHeadDim][rc] = nrow;
+  if (own && tid < 2 * kHeadDim) {
+    float nv = p.kv_kind == 0 ? bf16_bits_to_f32(static_cast<uint16_t>(nraw >> (16 * (ni & 1)))) : __uint_as_float(nraw);
+    if (tid < kHeadDim && p.mu != nullptr) nv = nv - __uint_as_float(muraw);  // key centering (fp32)
+    s_nrow[tid / kHeadDim][rc] = nv;
+  }
+  // Every prologue load must have landed before the first page-pair load is
+  // issued: the compiler's own waits know nothing of those (inline asm) loads,
+  // so a later wait for R would also wait for page data.
+#pragma unroll
+  for (int ii = 0; ii < kRows; ++ii) asm volatile("" ::"v"(rv[ii]));
+  if (own) {
+#pragma unroll
+    for (int ii = 0; ii < kRows; ++ii) asm volatile("" ::"v"(rvv[ii]));
+  }
   __syncthreads();
   // the new token's slot: position T - 1 on the split's last page (masked page: no append)
   const bool new_ok = own && s_pages[np - 1] >= 0;
@@ -268,10 +282,10 @@ void decode_kernel(const DecodeParams p) {
       for (int jh = 0; jh < kNH; ++jh) accq[jh] = fmaf(s_q[jh][kRows * rpart + ii], rv[ii], accq[jh]);
     }
 #pragma unroll
-    for (int jh = 0; jh < kNH; ++jh) s_buf[rpart][jh][rc] = accq[jh];
+    for (int jh = 0; jh < kNH; ++jh) s_pro[(rpart * kNH + jh) * kHeadDim + rc] = accq[jh];
     if (new_ok) {  // rotation partials of the new key and value (shared summation order)
-      s_npart[0][rpart][rc] = rot_chains<kRows>(&s_nrow[0][kRows * rpart], rv);
-      s_npart[1][rpart][rc] = rot_chains<kRows>(&s_nrow[1][kRows * rpart], rvv);
+      s_npart[(0 * 4 + rpart) * kHeadDim + rc] = rot_chains<kRows>(&s_nrow[0][kRows * rpart], rv);
+      s_npart[(1 * 4 + rpart) * kHeadDim + rc] = rot_chains<kRows>(&s_nrow[1][kRows * rpart], rvv);
     }
   }
   __syncthreads();
@@ -280,15 +294,14 @@ void decode_kernel(const DecodeParams p) {
     const int c = idx % kHeadDim;
     float sum = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kParts; ++u) sum += s_buf[u][jh][c];
+    for (int u = 0; u < kParts; ++u) sum += s_pro[(u * kNH + jh) * kHeadDim + c];
     s_q[jh][c] = sum * p.logit_scale;
   }
   if (new_ok && tid < 2 * kHeadDim) {
-    const int tensor = tid / kHeadDim;
-    const float x = kParts == 4 ? (s_npart[tensor][0][rc] + s_npart[tensor][1][rc]) +
-                                      (s_npart[tensor][2][rc] + s_npart[tensor][3][rc])
-                                : s_npart[tensor][0][rc] + s_npart[tensor][1][rc];
-    s_nrow[tensor][rc] = x;  // rotated
+    const float* np_ = s_npart + tid / kHeadDim * 4 * kHeadDim + rc;
+    const float x = kParts == 4 ? (np_[0] + np_[kHeadDim]) + (np_[2 * kHeadDim] + np_[3 * kHeadDim])
+                                : np_[0] + np_[kHeadDim];
+    s_nrow[tid / kHeadDim][rc] = x;  // rotated
   }
   __syncthreads();
   if (new_ok && tid < 2 * kHeadDim) {  // quantize-append the new token (two waves per tensor)
@@ -328,8 +341,9 @@ void decode_kernel(const DecodeParams p) {
     float qsum = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
+      // element e meets key register e/2, whose codes carry a factor 4^(e/2)
       const float qv = s_q[jl][32 * grp + 8 * a + e];
-      const float sc = qv * f;
+      const float sc = qv * f * (1.0f / static_cast<float>(1 << (2 * (e >> 1))));
       const _Float16 hh = static_cast<_Float16>(sc);
       hi[e] = hh;
       lo[e] = static_cast<_Float16>(sc - static_cast<float>(hh));
@@ -369,29 +383,30 @@ void decode_kernel(const DecodeParams p) {
     P.km1 = *reinterpret_cast<const uint4v*>(meta + 512 + meta_off);
     P.vm1 = *reinterpret_cast<const uint4v*>(meta + 512 + meta_off + 16);
     const int i0 = 2 * pair;
-    const bool ok0 = s_pages[i0] >= 0;
-    const bool has1 = i0 + 1 < np && s_pages[i0 + 1] >= 0;
+    // page ids and the pair's validity are wave-uniform (scalar registers)
+    const int ph0 = __builtin_amdgcn_readfirstlane(s_pages[i0]);
+    const int ph1 = __builtin_amdgcn_readfirstlane(i0 + 1 < np ? s_pages[i0 + 1] : -1);
+    const bool ok0 = ph0 >= 0;
+    const bool has1 = ph1 >= 0;
+    const bool full = ok0 && has1 && (p0 + i0 + 2) * kPage <= T_read;  // no position of the pair masked
     // logits (log2 units, divided by c1) for both pages
     float sp[kNQ][2][4];
 #pragma unroll
     for (int X = 0; X < 2; ++X) {
       const uint4v rec = X ? P.rec1 : P.rec0;
       const uint4v km = X ? P.km1 : P.km0;
+      // Key operands: a code at bits 2q (+16) of a word is the fp16 subnormal
+      // code * 4^q * 2^-24, so one AND per register; groups 1 and 3 sit in the
+      // upper byte of each half and are shifted down first.  The factor 4^q is
+      // divided out of the query operand.
+      const uint32_t kw[4] = {rec[0], rec[0] >> 8, rec[1], rec[1] >> 8};
       half8 kA[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const uint32_t w = kk < 2 ? rec[0] : rec[1];
-        const int sh = 8 * (kk & 1);
         uint4v rr;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) rr[q] = (w >> (sh + 2 * q)) & 0x00030003u;
+        for (int q = 0; q < 4; ++q) rr[q] = kw[kk] & (0x00030003u << (2 * q));
         kA[kk] = __builtin_bit_cast(half8, rr);
-      }
-      float sk[4], zk[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sk[i] = f16_lo(km[i]);
-        zk[i] = f16_hi(km[i]);
       }
       const int pos0 = (p0 + i0 + X) * kPage + 4 * a;
       const bool page_ok = X == 0 ? ok0 : has1;
@@ -405,31 +420,34 @@ void decode_kernel(const DecodeParams p) {
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float s = fmaf(C[i], sk[i], zk[i] * qz[Q]);
-          s = row_sum_stride4(s);
-          sp[Q][X][i] = (page_ok && pos0 + i < T_read) ? s : -INFINITY;
+          // s_grp * <codes, q_hat> + z_grp * sum(q_hat), scale/zero read as fp16 operands
+          float s = fmaf(C[i], f16_lo(km[i]), fmaf(f16_hi(km[i]), qz[Q], 0.0f));
+          sp[Q][X][i] = row_sum_stride4(s);
+        }
+        if (!full) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!(page_ok && pos0 + i < T_read)) sp[Q][X][i] = -INFINITY;
         }
       }
     }
 
-    // value operands: tile t holds channels 16t..16t+15
+    // Value operands: tile t holds channels 16t..16t+15.  Tiles 0-3 sit in the
+    // low byte of each half (bits 2t), tiles 4-7 in the high byte; a register
+    // of tile t holds the codes times 4^(t%4) (divided out of acc at the end).
+    const uint32_t vw[8] = {P.rec0[2], P.rec0[3], P.rec1[2], P.rec1[3],
+                            P.rec0[2] >> 8, P.rec0[3] >> 8, P.rec1[2] >> 8, P.rec1[3] >> 8};
     half8 vB[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
+      const uint32_t m = 0x00030003u << (2 * (t & 3));
+      const int hb = 4 * (t >> 2);
       uint4v rr;
-      rr[0] = (P.rec0[2] >> (2 * t)) & 0x00030003u;
-      rr[1] = (P.rec0[3] >> (2 * t)) & 0x00030003u;
-      rr[2] = (P.rec1[2] >> (2 * t)) & 0x00030003u;
-      rr[3] = (P.rec1[3] >> (2 * t)) & 0x00030003u;
+      rr[0] = vw[hb + 0] & m;
+      rr[1] = vw[hb + 1] & m;
+      rr[2] = vw[hb + 2] & m;
+      rr[3] = vw[hb + 3] & m;
       vB[t] = __builtin_bit_cast(half8, rr);
-    }
-    float sv[2][4], zv[2][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[0][i] = f16_lo(P.vm0[i]);
-      zv[0][i] = f16_hi(P.vm0[i]);
-      sv[1][i] = f16_lo(P.vm1[i]);
-      zv[1][i] = f16_hi(P.vm1[i]);
     }
 
     // online softmax and P.V per quad
@@ -441,8 +459,12 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, sp[Q][X][i]);
       mloc = rows_max(mloc);
-      const float m_new = fmaxf(m_run[Q], mloc * c1[Q]);
-      if (__ballot(m_new > m_run[Q]) != 0) {
+      // Lazy rescaling: the reference max moves only when some head's logits
+      // exceed it by more than kLazy (log2 units), so the weights
+      // exp2(logit - m_run) stay <= 2^kLazy and most pairs skip the rescale.
+      const float m_cand = mloc * c1[Q];
+      if (__ballot(m_cand > m_run[Q] + kLazy) != 0) {
+        const float m_new = fmaxf(m_run[Q], m_cand);
         const float alpha = __builtin_amdgcn_exp2f(m_run[Q] - m_new);
         const float al0 = dpp_f32<QuadBcast<0>::ctrl>(alpha);
         const float al1 = dpp_f32<QuadBcast<1>::ctrl>(alpha);
@@ -465,9 +487,10 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float pr = __builtin_amdgcn_exp2f(fmaf(sp[Q][X][i], c1[Q], -m_run[Q]));
+          const uint32_t vm = X ? P.vm1[i] : P.vm0[i];
           l_run[Q] += pr;
-          z_run[Q] = fmaf(pr, zv[X][i], z_run[Q]);
-          pA[4 * X + i] = static_cast<_Float16>(pr * sv[X][i]);
+          z_run[Q] = fmaf(f16_hi(vm), pr, z_run[Q]);
+          pA[4 * X + i] = static_cast<_Float16>(fmaf(f16_lo(vm), pr, 0.0f));
         }
 #pragma unroll
       for (int t = 0; t < 8; ++t) acc[Q][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pA, vB[t], acc[Q][t], 0, 0, 0);
@@ -485,6 +508,7 @@ void decode_kernel(const DecodeParams p) {
     }
   }
   wait_vmcnt<0>();  // no load into the ring outlives the loop
+  __syncthreads();   // every wave is done with the ring; its LDS is reused below
 
   // ---- per-wave results to LDS: lane (a, b) owns channels 32a + b and
   //      32a + 16 + b (tiles 2a, 2a+1) for the four heads of each quad.
@@ -497,7 +521,9 @@ void decode_kernel(const DecodeParams p) {
       const float zi = __shfl(zsum, 4 * a + i);  // zero part of head i, group a
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        if ((t >> 1) == a) s_buf[wave][4 * Q + i][16 * t + col] = acc[Q][t][i] * kTwo24 + zi;
+        if ((t >> 1) == a)  // undo the tile's code factor 4^(t%4) and the 2^-24 code scale
+          s_post[(wave * kNH + 4 * Q + i) * kHeadDim + 16 * t + col] =
+              acc[Q][t][i] * (kTwo24 / static_cast<float>(1 << (2 * (t & 3)))) + zi;
       }
     }
     if (lane < 4) {
@@ -508,9 +534,15 @@ void decode_kernel(const DecodeParams p) {
   __syncthreads();
 
   // ---- workgroup partial -> workspace (agent-scope stores: coherent across
-  //      XCDs without an L2 writeback)
+  //      XCDs without an L2 writeback).  Each thread keeps the elements it
+  //      stored, for the merge should this workgroup be the last.
+  constexpr int kIdx = (kNH * kHeadDim + kThreads - 1) / kThreads;  // output elements per thread
+  float own_m[kIdx], own_l[kIdx], own_a[kIdx];
   const size_t head_base = (static_cast<size_t>(b) * H + h) * p.n_splits;  // first partial of (b, h)
-  for (int idx = tid; idx < g * kHeadDim; idx += kThreads) {
+#pragma unroll
+  for (int k = 0; k < kIdx; ++k) {
+    const int idx = tid + k * kThreads;
+    if (idx >= g * kHeadDim) break;
     const int jh = idx / kHeadDim;
     const int c = idx % kHeadDim;
     float M = kNegBig;
@@ -521,7 +553,7 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll
     for (int w = 0; w < kW; ++w) {
       const float wt = __builtin_amdgcn_exp2f(s_m[w][jh] - M);
-      av = fmaf(wt, s_buf[w][jh][c], av);
+      av = fmaf(wt, s_post[(w * kNH + jh) * kHeadDim + c], av);
       lv = fmaf(wt, s_l[w][jh], lv);
     }
     if (new_ok) {  // the new token, weight exp2(logit - M), level w_hat
@@ -529,6 +561,9 @@ void decode_kernel(const DecodeParams p) {
       av = fmaf(wt, s_hat[1][c], av);
       lv += wt;
     }
+    own_m[k] = M;
+    own_l[k] = lv;
+    own_a[k] = av;
     float* dst = p.part + ((head_base + split) * g + jh) * kPartStride;
     __hip_atomic_store(dst + c, av, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (c == 0) {
@@ -547,8 +582,8 @@ void decode_kernel(const DecodeParams p) {
   __syncthreads();
   if (s_ticket != n_valid - 1) return;
 
-  // R_V rows for the output rotation, requested before the merge loads:
-  // thread (row oi, part oq) takes channels [kRows * oq, +kRows) of row oi
+  // R_V rows for the output rotation, requested before the partials: thread
+  // (row oi, part oq) takes channels [kRows * oq, +kRows) of row oi
   const int oi = tid & (kHeadDim - 1);
   const int oq = rpart;
   float4v rr[kRows / 4];
@@ -557,55 +592,59 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < kRows / 4; ++u) rr[u] = *reinterpret_cast<const float4v*>(Rrow + 4 * u);
   }
-  // log-sum-exp weights of every (split, head): wave w takes heads w, w+kW, ...,
-  // each lane up to kMaxSplits/64 splits, all loads in one round.
-  // s_w aliases s_buf: n_valid * g <= kMaxSplits * kNH <= 4 * kNH * kHeadDim.
-  static_assert(kMaxSplits <= 4 * kHeadDim, "merge weights fit in s_buf");
-  float* s_w = &s_buf[0][0][0];
+  // Merge, in one load round: every (split, head) max/sum pair is loaded by
+  // one thread and shared through LDS (the ring is free now), while thread
+  // (head jh, channel c) loads acc[c] of the first kAB splits; this
+  // workgroup's own split comes from registers.
+  constexpr int kAB = kNQ == 1 ? 32 : 8;  // splits per acc load round
+  static_assert(sizeof(s_ring) >= sizeof(float) * 2 * kMaxSplits * kNH, "max/sum pairs fit in the ring");
   const float* pb = p.part + head_base * g * kPartStride;
-  constexpr int kSplitsPerLane = kMaxSplits / 64;
-  for (int jh = wave; jh < g; jh += kW) {
-    float ms[kSplitsPerLane], ls[kSplitsPerLane];
+  float* s_ml = s_post;  // [split][head][2]: max, sum
+  const int n_ml = n_valid * g;
+  float av[kIdx][kAB];
+  auto load_acc = [&](int k, int s0) {
+    const int idx = min(tid + k * kThreads, g * kHeadDim - 1);
+    const int jh = idx / kHeadDim, c = idx % kHeadDim;
 #pragma unroll
-    for (int u = 0; u < kSplitsPerLane; ++u) {
-      const int sp_ = lane + 64 * u;
-      const float* ps = pb + (min(sp_, n_valid - 1) * g + jh) * kPartStride;
-      const float m_ld = ld_agent(ps + 128);
-      const float l_ld = ld_agent(ps + 129);
-      ms[u] = sp_ < n_valid ? m_ld : kNegBig;
-      ls[u] = sp_ < n_valid ? l_ld : 0.0f;
+    for (int u = 0; u < kAB; ++u) av[k][u] = ld_agent(pb + (min(s0 + u, n_valid - 1) * g + jh) * kPartStride + c);
+  };
+  float ml0 = 0.0f, ml1 = 0.0f;
+  if (tid < n_ml) {
+    ml0 = ld_agent(pb + static_cast<size_t>(tid) * kPartStride + 128);  // split tid / g, head tid % g
+    ml1 = ld_agent(pb + static_cast<size_t>(tid) * kPartStride + 129);
+  }
+#pragma unroll
+  for (int k = 0; k < kIdx; ++k) load_acc(k, 0);
+  for (int q = tid; q < n_ml; q += kThreads) {
+    if (q != tid) {  // beyond the first pair per thread
+      ml0 = ld_agent(pb + static_cast<size_t>(q) * kPartStride + 128);
+      ml1 = ld_agent(pb + static_cast<size_t>(q) * kPartStride + 129);
     }
-    float M = kNegBig;
-#pragma unroll
-    for (int u = 0; u < kSplitsPerLane; ++u) M = fmaxf(M, ms[u]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-    float lv = 0.0f;
-#pragma unroll
-    for (int u = 0; u < kSplitsPerLane; ++u) {
-      const int sp_ = lane + 64 * u;
-      const float wt = __builtin_amdgcn_exp2f(ms[u] - M);
-      if (sp_ < n_valid) s_w[sp_ * g + jh] = wt;
-      lv = fmaf(wt, ls[u], lv);
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) lv += __shfl_xor(lv, off);
-    if (lane == 0) s_f[jh] = lv > 0.0f ? 1.0f / lv : 0.0f;
+    s_ml[2 * q] = ml0;
+    s_ml[2 * q + 1] = ml1;
   }
   __syncthreads();
-  // weighted sums, 32 partial rows in flight per thread
-  for (int idx = tid; idx < g * kHeadDim; idx += kThreads) {
+#pragma unroll
+  for (int k = 0; k < kIdx; ++k) {
+    const int idx = tid + k * kThreads;
+    if (idx >= g * kHeadDim) break;
     const int jh = idx / kHeadDim;
     const int c = idx % kHeadDim;
-    float av = 0.0f;
-    for (int s0 = 0; s0 < n_valid; s0 += 32) {
-      float v[32];
+    float M = kNegBig, l = 0.0f;
+    for (int sp = 0; sp < n_valid; ++sp) M = fmaxf(M, s_ml[2 * (sp * g + jh)]);
+    for (int sp = 0; sp < n_valid; ++sp)
+      l = fmaf(__builtin_amdgcn_exp2f(s_ml[2 * (sp * g + jh)] - M), s_ml[2 * (sp * g + jh) + 1], l);
+    float o = 0.0f;
+    for (int s0 = 0; s0 < n_valid; s0 += kAB) {
+      if (s0 > 0) load_acc(k, s0);
 #pragma unroll
-      for (int u = 0; u < 32; ++u) v[u] = ld_agent(pb + (min(s0 + u, n_valid - 1) * g + jh) * kPartStride + c);
-#pragma unroll
-      for (int u = 0; u < 32; ++u) av = fmaf(s0 + u < n_valid ? s_w[min(s0 + u, n_valid - 1) * g + jh] : 0.0f, v[u], av);
+      for (int u = 0; u < kAB; ++u) {
+        const int sp = s0 + u;
+        if (sp < n_valid)
+          o = fmaf(__builtin_amdgcn_exp2f(s_ml[2 * (sp * g + jh)] - M), sp == split ? own_a[k] : av[k][u], o);
+      }
     }
-    s_q[jh][c] = av * s_f[jh];  // o_rot
+    s_q[jh][c] = l > 0.0f ? o / l : 0.0f;  // o_rot
   }
   __syncthreads();
 
@@ -621,7 +660,7 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll
         for (int jh = 0; jh < kNH; ++jh) o[jh] = fmaf(s_q[jh][kRows * oq + 4 * u + e], rr[u][e], o[jh]);
 #pragma unroll
-    for (int jh = 0; jh < kNH; ++jh) s_buf[oq][jh][oi] = o[jh];
+    for (int jh = 0; jh < kNH; ++jh) s_post[(oq * kNH + jh) * kHeadDim + oi] = o[jh];
   }
   __syncthreads();
   for (int idx = tid; idx < g * kHeadDim; idx += kThreads) {
@@ -629,7 +668,7 @@ void decode_kernel(const DecodeParams p) {
     const int i = idx % kHeadDim;
     float o = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kParts; ++u) o += s_buf[u][jh][i];
+    for (int u = 0; u < kParts; ++u) o += s_post[(u * kNH + jh) * kHeadDim + i];
     const size_t oidx = (out_row0 + jh) * kHeadDim + i;
     if (p.out_kind == 0)
       static_cast<uint16_t*>(p.out)[oidx] = f32_to_bf16_bits(o);
@@ -647,7 +686,7 @@ static hipError_t launch_one(const DecodeParams& prm, hipStream_t stream, hipEve
   constexpr int kW = DecodeShape<kNQ>::waves;
   DecodeParams arg = prm;
   void* args[] = {&arg};
-  return hipExtLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<kNQ, kW>),
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<kNQ, kW, DecodeShape<kNQ>::depth>),
                             dim3(prm.batch * prm.num_kv_heads * prm.n_splits), dim3(64 * kW), args, 0, stream,
                             ev_begin, ev_end, 0);
 }

@@ -17,7 +17,9 @@ constexpr int kMetaRecordBytes = 32;
 // Decode split limits and the partial-result row stride (floats).
 constexpr int kMaxPagesPerSplit = 2048;
 constexpr int kMaxSplits = 512;
-constexpr int kPartStride = 132;    // [0,128) unnormalised rotated output, [128] max (log2), [129] sum
+// Split partial row: [0,128) unnormalised rotated output, [128] max (log2
+// units), [129] sum of weights.
+constexpr int kPartStride = 132;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
