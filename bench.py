@@ -270,6 +270,18 @@ def main() -> int:
         f"(min {min(split_ms) * 1e3:.2f}, max {max(split_ms) * 1e3:.2f}); host enqueue {t_enqueue:.1f} ms "
         f"vs GPU {total_ms:.1f} ms")
 
+    # measured HBM read ceiling: a 1 GiB reduction (torch), best of 5, outside the timed region
+    big = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    ceil_gbps = 0.0
+    for _ in range(6):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        big.sum()
+        e1.record()
+        torch.cuda.synchronize()
+        ceil_gbps = max(ceil_gbps, big.numel() * 4 / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del big
+
     tokens = float(case.seq_lens.sum())
     n_pages = int(((case.seq_lens + PAGE - 1) // PAGE).sum())
     # packed cache + page-table entries read, plus the newest token's bf16 k/v read and 96 B written per KV head
@@ -307,6 +319,8 @@ def main() -> int:
         "decode_kernel_us": split_avg_ms * 1e3,
         "host_enqueue_ms": t_enqueue,
         "bulk_append_ms": bulk_ms,
+        "hbm_read_ceiling_gbps": ceil_gbps,
+        "frac_of_read_ceiling": achieved / ceil_gbps if ceil_gbps > 0 else None,
         "roofline": {
             "bound": "hbm",
             "achieved": achieved,
