@@ -14,14 +14,19 @@
 // summation order of kvq_quant.h.  For quantization, each half takes 8 tokens
 // and thread j owns rotated channel j (kvq_quant.h: q2_pack_channel).
 
+#include <algorithm>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 #include "kvq_quant.h"
+#include "kvq_rot.h"
 
 namespace kvq {
 
 constexpr int kAppendTile = 16;
 constexpr int kAppendThreads = 256;
+// Appends of at least this many raw tokens take the bulk (matrix-core) path.
+constexpr int kBulkMin = 64;
 
 template <int kIn>  // 0 = bf16 raw, 1 = fp32 raw, 2 = fp32 already centred and rotated
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(
@@ -87,12 +92,210 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Bulk path (n_tokens >= kBulkMin, raw bf16/fp32 input): workgroups of 8
+// waves, each bound to one (KV head, tensor) and striding over its tiles of
+// 512 tokens.  R is staged once in LDS
+// as split-fp16 MFMA operands (kvq_rot.h); each wave rotates 16 tokens at a
+// time on the matrix cores, passes the rotated rows through its own LDS rows,
+// and quantizes them with one lane per (token, 32-channel group)
+// (kvq_quant.h: q2_group32), packing the K and V words across lanes.
+constexpr int kBulkThreads = 512;
+constexpr int kBulkWaves = kBulkThreads / 64;
+constexpr int kBulkRounds = 4;                        // 16-token tiles per wave
+constexpr int kBulkTile = 16 * kBulkWaves * kBulkRounds;  // tokens per workgroup
+
+template <int kIn>  // 0 = bf16, 1 = fp32
+__global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
+    uint8_t* __restrict__ pool, int num_pages, int num_kv_heads, const void* __restrict__ k_in,
+    const void* __restrict__ v_in, int n_tokens, const int32_t* __restrict__ slots, const float* __restrict__ mu,
+    const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out) {
+  const int h = blockIdx.y;
+  const int tensor = blockIdx.z;  // 0: key, 1: value
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  __shared__ half8 s_op[32 * 2 * 64];                          // R operands, 64 KB
+  __shared__ float s_x[kBulkWaves][16][kHeadDim + 4];          // rotated rows of each wave's 16 tokens
+
+  stage_rotation((tensor == 0 ? r_k : r_v) + static_cast<size_t>(h) * kHeadDim * kHeadDim, s_op, wave, kBulkWaves,
+                 lane);
+  // this lane's A columns 32 kb + 8 kq + e; key centre (fp32) or 0
+  const int kq = lane >> 4, row = lane & 15;
+  float cen[4][8];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      cen[kb][e] = (tensor == 0 && mu != nullptr) ? mu[h * kHeadDim + 32 * kb + 8 * kq + e] : 0.0f;
+  __syncthreads();
+
+  const void* src = tensor == 0 ? k_in : v_in;
+  const int n_tiles = (n_tokens + kBulkTile - 1) / kBulkTile;
+  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
+    const int n0 = tile * kBulkTile;
+    // raw A rows of the wave's 16-token tile m, loaded one tile ahead: row `row`
+    // (clamped; rows past the end are never stored), columns 32 kb + 8 kq ..
+    constexpr int kRawWords = kIn == 0 ? 4 : 8;  // uint4v per lane: 4 kb x 8 bf16, or 4 kb x 8 fp32
+    auto load_raw = [&](int m, uint4v (&raw)[kRawWords]) {
+      const int r0 = n0 + 16 * (kBulkWaves * m + wave);
+      const size_t base = (static_cast<size_t>(min(r0 + row, n_tokens - 1)) * num_kv_heads + h) * kHeadDim;
+  #pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const size_t off = base + 32 * kb + 8 * kq;
+        if (kIn == 0) {
+          raw[kb] = *reinterpret_cast<const uint4v*>(static_cast<const uint16_t*>(src) + off);
+        } else {
+          raw[2 * kb] = *reinterpret_cast<const uint4v*>(static_cast<const float*>(src) + off);
+          raw[2 * kb + 1] = *reinterpret_cast<const uint4v*>(static_cast<const float*>(src) + off + 4);
+        }
+      }
+    };
+    uint4v raw[kRawWords], next[kRawWords];
+    load_raw(0, raw);
+    for (int m = 0; m < kBulkRounds; ++m) {
+      const int r0 = n0 + 16 * (kBulkWaves * m + wave);  // this wave's first token
+      if (m + 1 < kBulkRounds) load_raw(m + 1, next);
+      half8 a_hi[4], a_lo[4];
+  #pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        float a[8];
+        if (kIn == 0) {
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a[2 * e] = __uint_as_float(raw[kb][e] << 16);
+            a[2 * e + 1] = __uint_as_float(raw[kb][e] & 0xffff0000u);
+          }
+        } else {
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            a[e] = __uint_as_float(raw[2 * kb][e]);
+            a[4 + e] = __uint_as_float(raw[2 * kb + 1][e]);
+          }
+        }
+  #pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          _Float16 hh, ll;
+          split_f16(a[e] - cen[kb][e], hh, ll);  // key centering (fp32); values use centre 0
+          a_hi[kb][e] = hh;
+          a_lo[kb][e] = ll;
+        }
+      }
+      float4v C[8];
+      rotate16(a_hi, a_lo, s_op, lane, C);
+  #pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) s_x[wave][4 * (lane >> 4) + i][16 * nt + (lane & 15)] = C[nt][i];
+
+      // Quantize-pack this wave's 16 tokens: lane (token r, group g) holds the
+      // 32 channels of group g of token r.  The rows were written by this wave
+      // only; the barrier orders those LDS writes before the reads.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const int r = lane >> 2, g = lane & 3;
+      const int n = r0 + r;
+      float x[32];
+  #pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float4v q4 = *reinterpret_cast<const float4v*>(&s_x[wave][r][32 * g + 4 * u]);
+        x[4 * u] = q4[0];
+        x[4 * u + 1] = q4[1];
+        x[4 * u + 2] = q4[2];
+        x[4 * u + 3] = q4[3];
+      }
+      uint32_t pair, code[32];
+      q2_group32(x, pair, code);
+      const int slot = n < n_tokens ? slots[n] : -1;
+      const bool ok = slot >= 0 && slot < num_pages * kPage;  // same for the token's four lanes
+      if (rot_out != nullptr && n < n_tokens) {
+        float* dst = rot_out + ((static_cast<size_t>(n) * num_kv_heads + h) * 2 + tensor) * kHeadDim + 32 * g;
+  #pragma unroll
+        for (int u = 0; u < 8; ++u)
+          *reinterpret_cast<float4v*>(dst + 4 * u) = float4v{x[4 * u], x[4 * u + 1], x[4 * u + 2], x[4 * u + 3]};
+      }
+      // the 16 tokens fill one page in order: every word of the page is written whole
+      const int slot0 = __shfl(slot, 0);
+      const bool full = __builtin_amdgcn_ballot_w64(!(ok && slot == slot0 + r && (slot0 & 15) == 0)) == 0;
+      const int off = slot & 15;
+      uint8_t* block = pool + (static_cast<size_t>(ok ? slot >> 4 : 0) * num_kv_heads + h) * kBlockBytes;
+      if (ok) {  // metadata pair of (token, group): record 4g + off/4
+        *reinterpret_cast<uint32_t*>(block + kCodeBytes + kMetaRecordBytes * (4 * g + (off >> 2)) + 16 * tensor +
+                                     4 * (off & 3)) = pair;
+      }
+      if (tensor == 0) {
+        // K: channel 32g + 8ak + e -> record 16ak + off, word K[g/2], bit 2(4(g%2) + e/2) + 16(e%2)
+        uint32_t kw[4];
+  #pragma unroll
+        for (int ak = 0; ak < 4; ++ak) {
+          uint32_t w = 0;
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) w |= code[8 * ak + e] << (2 * (4 * (g & 1) + (e >> 1)) + 16 * (e & 1));
+          kw[ak] = w | __shfl_xor(w, 1);  // both groups of the word
+        }
+        if (ok && (g & 1) == 0) {
+  #pragma unroll
+          for (int ak = 0; ak < 4; ++ak) *reinterpret_cast<uint32_t*>(block + 16 * (16 * ak + off) + 4 * (g >> 1)) = kw[ak];
+        }
+      } else {
+        // V: channel 32g + 16tt + b -> record 16(off/4) + b, word V[(off%4)/2],
+        // bit 2(2g + tt) + 16(off%2); the token's bits of word b after the group OR
+        const int hs = 16 * (off & 1);
+        uint32_t vw[16];
+  #pragma unroll
+        for (int bb = 0; bb < 16; ++bb) {
+          uint32_t w = (code[bb] << (4 * g + hs)) | (code[16 + bb] << (4 * g + 2 + hs));
+          w |= __shfl_xor(w, 1);
+          w |= __shfl_xor(w, 2);
+          vw[bb] = w;
+        }
+        if (full) {  // pair the two slots of each word (tokens r and r ^ 1), plain stores
+  #pragma unroll
+          for (int bb = 0; bb < 16; ++bb) vw[bb] |= __shfl_xor(vw[bb], 4);
+          if ((r & 1) == 0) {
+  #pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int bb = 4 * g + u;
+              *reinterpret_cast<uint32_t*>(block + 16 * (16 * (off >> 2) + bb) + 8 + 4 * ((off & 3) >> 1)) = vw[bb];
+            }
+          }
+        } else if (ok) {  // other slots of the page may be written concurrently: only this slot's half
+          const uint32_t mask = 0xffffu << hs;
+  #pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int bb = 4 * g + u;
+            uint32_t* word = reinterpret_cast<uint32_t*>(block + 16 * (16 * (off >> 2) + bb) + 8 + 4 * ((off & 3) >> 1));
+            atomicAnd(word, ~mask);
+            atomicOr(word, vw[bb]);
+          }
+        }
+      }
+  #pragma unroll
+      for (int u = 0; u < kRawWords; ++u) raw[u] = next[u];
+    }
+  }  // tiles
+}
+
 hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const void* k, const void* v, int in_kind,
                          int n_tokens, const int32_t* slots, const float* mu, const float* r_k, const float* r_v,
                          float* rot_out, hipStream_t stream) {
+  (void)hipGetLastError();  // report only this call's launch errors, not stale ones
+  if (in_kind != 2 && n_tokens >= kBulkMin) {
+    // about one workgroup per compute unit in all, each staging its R once
+    const int n_tiles = (n_tokens + kBulkTile - 1) / kBulkTile;
+    const int per = std::max(1, std::min(n_tiles, (256 + 2 * num_kv_heads - 1) / (2 * num_kv_heads)));
+    const dim3 bgrid(per, num_kv_heads, 2);
+    if (in_kind == 0)
+      hipLaunchKernelGGL(append_bulk_kernel<0>, bgrid, dim3(kBulkThreads), 0, stream, pool, num_pages, num_kv_heads, k,
+                         v, n_tokens, slots, mu, r_k, r_v, rot_out);
+    else
+      hipLaunchKernelGGL(append_bulk_kernel<1>, bgrid, dim3(kBulkThreads), 0, stream, pool, num_pages, num_kv_heads, k,
+                         v, n_tokens, slots, mu, r_k, r_v, rot_out);
+    return hipGetLastError();
+  }
   const dim3 grid((n_tokens + kAppendTile - 1) / kAppendTile, num_kv_heads, 2);
   const dim3 block(kAppendThreads);
-  (void)hipGetLastError();  // report only this call's launch errors, not stale ones
   switch (in_kind) {
     case 0:
       hipLaunchKernelGGL(append_kernel<0>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,

@@ -97,4 +97,40 @@ __device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, ui
   return fmaf(sc, static_cast<float>(code), z);
 }
 
+// Q2 of one 32-channel group held by one lane (the bulk path): the same
+// result as q2_pack_channel's arithmetic.  The code of each element is
+// rint(fl(t / s)) clamped to 0..3 with t = fl(x - z); it is taken from
+// q = fl(t * fl(1 / s)), which lies within 3 * 2^-24 |q| of fl(t / s), unless
+// q is within 2^-19 of a half-integer, where the two could round apart: such a
+// lane recomputes its group with the IEEE division.
+__device__ __forceinline__ void q2_group32(const float (&x)[32], uint32_t& pair, uint32_t (&code)[32]) {
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int c = 1; c < 32; ++c) {
+    mn = fminf(mn, x[c]);
+    mx = fmaxf(mx, x[c]);
+  }
+  const float s32 = (mx - mn) / 3.0f;
+  const _Float16 s16 = static_cast<_Float16>(s32);
+  const _Float16 z16 = static_cast<_Float16>(mn);
+  const float sc = static_cast<float>(s16);
+  const float z = static_cast<float>(z16);
+  pair = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, s16)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, z16)) << 16);
+  bool near = false;
+  const float rcp = sc != 0.0f ? 1.0f / sc : 0.0f;
+#pragma unroll
+  for (int c = 0; c < 32; ++c) {
+    const float q = (x[c] - z) * rcp;
+    const float k = rintf(q);
+    near = near || fabsf(q - k) > 0.5f - 0x1p-19f;
+    code[c] = static_cast<uint32_t>(__builtin_amdgcn_fmed3f(k, 0.0f, 3.0f));
+  }
+  if (__builtin_amdgcn_ballot_w64(near) != 0 && near) {  // exact path, rarely taken
+#pragma unroll
+    for (int c = 0; c < 32; ++c)
+      code[c] = static_cast<uint32_t>(fminf(fmaxf(rintf((x[c] - z) / sc), 0.0f), 3.0f));
+  }
+}
+
 }  // namespace kvq

@@ -68,15 +68,18 @@ def test_prerotated_ties_ranges_and_degenerate_groups():
     np.testing.assert_array_equal(dc.pool_np(), _oracle_pool(case, dc.num_pages, case.slots, x, w))
 
 
+@pytest.mark.parametrize("path", ["fp32", "bulk"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_raw_path_rotation_and_codes(dtype):
-    """Raw path: the kernel's fp32 rotation is within the derived rounding bound of the
+def test_raw_path_rotation_and_codes(dtype, path):
+    """Raw path: the kernel's rotation is within the derived fp32 rounding bound of the
     oracle's fp64 rotation, and its codes/scales are bit-exact to the oracle's quantizer
-    run on the kernel's own rotated input (both decide codes in fp32)."""
+    run on the kernel's own rotated input (both decide codes in fp32).  Appends in
+    chunks of 16 take the fp32 rotation; one call of 115 tokens takes the bulk
+    (split-fp16 matrix-core) rotation, tail tile included."""
     dev = require_gpu()
     case = I.make_case("r", 41, B=2, Hq=16, Hkv=4, seq_lens=[70, 45], dtype=dtype, table_policy="interleaved")
     dc = DeviceCase(case, dev)
-    rot = dc.append(rot_out=True).cpu().numpy()
+    rot = dc.append(rot_out=True, chunk=16 if path == "fp32" else None).cpu().numpy()
     xg, wg = rot[:, :, 0, :], rot[:, :, 1, :]
     x64 = O.rotate(O.centre_keys(case.k, case.mu), case.r_k)
     w64 = O.rotate(case.v, case.r_v)
@@ -153,6 +156,8 @@ def test_full_size_append_sampled_tokens():
             np.testing.assert_array_equal(got[4][off].view(np.uint16), vs[n_i, h].view(np.uint16))
             np.testing.assert_array_equal(got[5][off].view(np.uint16), vz[n_i, h].view(np.uint16))
     x64 = O.rotate(O.centre_keys(case.k[idx], case.mu), case.r_k)
+    w64 = O.rotate(case.v[idx], case.r_v)
     for h in range(case.Hkv):
         a_k = O.centre_keys(case.k[idx], case.mu)[:, h]
         assert np.all(np.abs(rs[:, h, 0] - x64[:, h]) <= rotation_error_bound(a_k, case.r_k[h]) + 1e-30)
+        assert np.all(np.abs(rs[:, h, 1] - w64[:, h]) <= rotation_error_bound(case.v[idx][:, h], case.r_v[h]) + 1e-30)
