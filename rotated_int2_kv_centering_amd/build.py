@@ -1,7 +1,7 @@
-"""Build libkvq.so in-tree for gfx950 with hipcc.
+"""Build libkvq.so (and the libkvq_probe.so measurement aid) in-tree for gfx950 with hipcc.
 
 Run ``python -m rotated_int2_kv_centering_amd.build`` (or call ``build()``).
-The library is written next to this file; every call recompiles.
+The libraries are written next to this file; every call recompiles.
 """
 
 from __future__ import annotations
@@ -16,6 +16,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
 SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip"]
+# measurement aid (HBM read-rate probe), a library of its own outside the decode path
+PROBE_LIB = os.path.join(HERE, "libkvq_probe.so")
+PROBE_SOURCES = ["hbm_probe.hip"]
 ARCH = "gfx950"
 
 # hipcc flags: no fast-math (the quantizer needs IEEE fp32 division and
@@ -36,11 +39,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libkvq)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libkvq.so; returns its path."""
-    out_tmp = LIB + ".tmp"
+def _link(sources, lib: str, verbose: bool) -> str:
+    out_tmp = lib + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, "-shared", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", out_tmp]
+           *[os.path.join(CSRC, s) for s in sources], "-o", out_tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,8 +53,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(out_tmp, LIB)
-    return LIB
+    os.replace(out_tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source, link libkvq.so and libkvq_probe.so; returns libkvq.so's path."""
+    _link(PROBE_SOURCES, PROBE_LIB, verbose)
+    return _link(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

@@ -197,3 +197,29 @@ def test_binding_rejects_non_contiguous_arrays(K):
     a = np.zeros((4, 4), dtype=np.int32)[:, ::2]
     with pytest.raises(ValueError):
         K._ptr(a)
+
+
+def test_probe_library_exports_its_declared_symbol():
+    """The HBM read-rate probe (a measurement aid) is built beside libkvq and
+    exports exactly what include/kvq_probe.h declares; bad arguments are
+    rejected on the host, before any launch."""
+    from rotated_int2_kv_centering_amd import build
+
+    if not os.path.exists(build.PROBE_LIB):
+        build.build()
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "kvq_probe.h")).read(), flags=re.S)
+    declared = sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(kvq_\w+)\s*\(", text, flags=re.M)))
+    assert declared == ["kvq_probe_read_stream"]
+    out = subprocess.run(["nm", "-D", "--defined-only", build.PROBE_LIB], capture_output=True, text=True,
+                         check=True).stdout
+    exported = sorted({l.split()[-1] for l in out.splitlines() if l.split()[-2:-1] == ["T"] and "kvq_" in l.split()[-1]})
+    assert exported == declared
+    lib = ctypes.CDLL(build.PROBE_LIB)
+    f = lib.kvq_probe_read_stream
+    f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(None, 16, ctypes.c_void_p(256), 1, None) == 1          # null source
+    assert f(ctypes.c_void_p(256), 15, ctypes.c_void_p(256), 1, None) == 1  # not a multiple of 16
+    assert f(ctypes.c_void_p(264), 16, ctypes.c_void_p(256), 1, None) == 1  # misaligned
+    assert f(ctypes.c_void_p(256), 16, ctypes.c_void_p(256), 0, None) == 1  # no workgroups
+    assert f(ctypes.c_void_p(256), 0, ctypes.c_void_p(256), 1, None) == 0   # nothing to read: no launch
