@@ -83,7 +83,7 @@ int device_cu_count() {
 }
 
 // Decode workgroups per compute unit: each workgroup has as many waves as a
-// compute unit holds for its group size (12 for g <= 4, else 4).
+// compute unit holds for its group size (12 for g <= 4, 8 for g <= 8, else 4).
 int workgroups_per_cu(int) { return 1; }
 
 bool make_plan(int batch, int num_kv_heads, int g, int max_seq_len, int num_splits, kvq::DecodePlan* plan) {

@@ -60,10 +60,11 @@ constexpr int kDmaPerPair = 4;  // K/V codes of page 0, of page 1; metadata of p
 // SIMD, and the per-wave ring depth (page pairs staged in LDS by direct
 // global->LDS loads; depth - 1 pairs are in flight while one is computed).
 // The g <= 4 kernel fits 3 waves per SIMD, so one 12-wave workgroup fills a
-// compute unit and its 4-slot rings use most of the LDS; the larger ones run
-// 1 wave per SIMD and keep more pairs in flight per wave instead.
+// compute unit; g <= 8 fits 2 (256 registers); the largest runs 1 wave per
+// SIMD and keeps more pairs in flight per wave instead.
 template <int kNQ> struct DecodeShape { static constexpr int waves = 4, waves_per_simd = 1, depth = 8; };
 template <> struct DecodeShape<1> { static constexpr int waves = 12, waves_per_simd = 3, depth = 3; };
+template <> struct DecodeShape<2> { static constexpr int waves = 8, waves_per_simd = 2, depth = 4; };
 
 typedef __attribute__((address_space(3))) void lds_void;
 

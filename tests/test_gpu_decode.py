@@ -52,6 +52,7 @@ SHAPES = [
     (2, 4, 2, [129, 64], "interleaved"),        # g = 2
     (2, 32, 8, [1000, 257], "interleaved"),     # g = 4, Llama-3.1-8B heads
     (2, 64, 8, [513, 1024], "interleaved"),     # g = 8, 70B-class heads
+    (1, 6, 1, [150], "permuted"),               # g = 6 (second quad padded)
     (1, 12, 1, [200], "permuted"),              # g = 12 (padded quad)
     (1, 16, 1, [300], "permuted"),              # g = 16
 ]
