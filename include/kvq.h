@@ -142,7 +142,9 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
  *               be in [0, num_pages).  The kernel never reads outside the pool:
  *               a page id outside [0, num_pages) contributes no tokens, and a
  *               length beyond max_pages*16 is cut there.
- *   seq_lens    device int32 [batch], each in [0, max_seq_len].
+ *   seq_lens    device int32 [batch], each in [0, max_seq_len] (a longer one
+ *               is cut to max_seq_len; kvq_decode_step then appends nothing
+ *               for that sequence).
  *   max_seq_len host bound on seq_lens; must satisfy ceil(max_seq_len/16) <= max_pages.
  *   r_k, r_v    device fp32 [H_kv][128][128] as in kvq_quant_append.
  *   sm_scale    logit scale; 0 selects 1/sqrt(128).
@@ -151,13 +153,20 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
  *               nearest even.
  *   workspace   device, >= kvq_decode_workspace_bytes(...) bytes, 16-byte
  *               aligned, zero-filled before first use (see above).
- *   num_splits  0 = automatic; otherwise the requested number of sequence
- *               splits per (sequence, KV head).  The kernel caps a split at
- *               2048 pages and uses at most 512 splits, so the count used can
- *               differ; kvq_decode_workspace_bytes follows the same plan.
+ *   num_splits  0 = automatic: the kernel reads the batch's lengths and cuts
+ *               every sequence into splits of one common size, the smallest
+ *               (found in a few refinement rounds) for which all splits of all
+ *               (sequence, KV head) pairs fit in one workgroup per compute
+ *               unit, so short sequences take few workgroups and long ones
+ *               many.  Otherwise the requested number of splits per
+ *               (sequence, KV head), each sized for max_seq_len.  Either way
+ *               a split holds at most 2048 pages and a sequence at most 512
+ *               splits, so the count used can differ from the request;
+ *               kvq_decode_workspace_bytes follows the same plan.  Lengths
+ *               above max_seq_len are cut to max_seq_len.
  * Work decomposition: one kernel launch; one workgroup per compute unit
- * (12 waves for g <= 4, else 4) streams a split's pages, and the last
- * workgroup of each (sequence, KV head) merges the split partials
+ * (12 waves for g <= 4, 8 for g <= 8, else 4) streams a split's pages, and
+ * the last workgroup of each (sequence, KV head) merges the split partials
  * (log-sum-exp) and applies R_V^T.
  * Limits: max_seq_len <= 16777216 (512 splits x 2048 pages x 16 tokens).
  * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ENOSPACE (workspace too small),

@@ -90,21 +90,48 @@ bool make_plan(int batch, int num_kv_heads, int g, int max_seq_len, int num_spli
   if (batch < 0 || num_kv_heads < 1 || max_seq_len < 0 || num_splits < 0) return false;
   if (max_seq_len > kMaxContext) return false;
   const int n_pages = (max_seq_len + kPage - 1) / kPage;
+  const long long n1 = std::max(n_pages, 1);
   plan->n_pages_max = n_pages;
+  // no split of any plan holds more than kMaxSplits of one sequence's splits
+  const long long pps_floor = (n_pages + kMaxSplits - 1) / kMaxSplits;
+  const long long target = static_cast<long long>(workgroups_per_cu(g)) * device_cu_count();
+  plan->balanced = num_splits == 0 && static_cast<long long>(batch) * n1 <= 0x7fffffffLL;
+  if (plan->balanced) {
+    // The kernel picks pps in [pps_min, pps_max] from the batch's total pages P:
+    // pps >= H P / target, or pps = pps_max.  Sequence b takes max(1, ceil(p_b / pps))
+    // splits; that sum is below P / pps + B when some sequence is non-empty (and B
+    // otherwise), so at most max(ceil(target / H), ceil(B n / pps_max)) + B - 1 slots
+    // per KV head are used, and never more than B ceil(n / pps_min).
+    const long long pps_min = std::max<long long>(kMinPagesPerSplit, pps_floor);
+    const long long pps_max = kMaxPagesPerSplit;
+    const long long bound = std::max((target + num_kv_heads - 1) / num_kv_heads,
+                                     (static_cast<long long>(batch) * n1 + pps_max - 1) / pps_max) +
+                            std::max(batch, 1) - 1;
+    const long long per_seq = (n1 + pps_min - 1) / pps_min;
+    const long long slots = std::min(bound, static_cast<long long>(std::max(batch, 1)) * per_seq);
+    if (slots > 0x7fffffffLL) return false;
+    plan->pps_min = static_cast<int>(pps_min);
+    plan->pps_max = static_cast<int>(pps_max);
+    plan->target_wgs = static_cast<int>(target);
+    plan->pages_per_split = 0;
+    plan->n_splits = static_cast<int>(std::max<long long>(slots, 1));
+    return true;
+  }
   long long pps;
   if (num_splits > 0) {
-    pps = (std::max(n_pages, 1) + num_splits - 1) / num_splits;
+    pps = (n1 + num_splits - 1) / num_splits;
   } else {
-    // One resident wave of workgroups over all (sequence, KV head).
-    const long long target = static_cast<long long>(workgroups_per_cu(g)) * device_cu_count();
-    const long long work = static_cast<long long>(std::max(batch, 1)) * num_kv_heads * std::max(n_pages, 1);
+    // fixed plan sized for the longest sequence (only for batches whose page
+    // total overflows 32 bits)
+    const long long work = static_cast<long long>(std::max(batch, 1)) * num_kv_heads * n1;
     pps = std::max<long long>((work + target - 1) / target, kMinPagesPerSplit);
   }
-  pps = std::max<long long>(pps, (n_pages + kMaxSplits - 1) / kMaxSplits);
+  pps = std::max<long long>(pps, pps_floor);
   pps = std::min<long long>(pps, kMaxPagesPerSplit);
-  pps = std::max<long long>(1, std::min<long long>(pps, std::max(n_pages, 1)));
+  pps = std::max<long long>(1, std::min<long long>(pps, n1));
   plan->pages_per_split = static_cast<int>(pps);
   plan->n_splits = std::max(1, (n_pages + plan->pages_per_split - 1) / plan->pages_per_split);
+  plan->pps_min = plan->pps_max = plan->target_wgs = 0;
   return true;
 }
 
@@ -113,8 +140,8 @@ size_t counters_bytes(int batch, int num_kv_heads) {
 }
 
 size_t workspace_bytes(int batch, int num_q_heads, int num_kv_heads, const kvq::DecodePlan& plan) {
-  return counters_bytes(batch, num_kv_heads) +
-         sizeof(float) * static_cast<size_t>(batch) * num_q_heads * plan.n_splits * kRowStride;
+  const size_t rows = static_cast<size_t>(plan.balanced ? 1 : batch) * num_q_heads * plan.n_splits;
+  return counters_bytes(batch, num_kv_heads) + sizeof(float) * rows * kRowStride;
 }
 
 // splitmix64 (Steele, Lea, Flood 2014) as the page allocator's random stream.
@@ -178,7 +205,7 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
   const size_t need = workspace_bytes(batch, num_q_heads, cache->num_kv_heads, plan);
   if (workspace_bytes_ < need)
     return fail(KVQ_ENOSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes_, need);
-  if (static_cast<long long>(batch) * cache->num_kv_heads * plan.n_splits > 0x7fffffffLL)
+  if (static_cast<long long>(plan.balanced ? 1 : batch) * cache->num_kv_heads * plan.n_splits > 0x7fffffffLL)
     return fail(KVQ_EUNSUPPORTED, "grid too large");
 
   const float scale = sm_scale == 0.0f ? 1.0f / std::sqrt(static_cast<float>(kHeadDim)) : sm_scale;
@@ -201,8 +228,13 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
   a.out_kind = out_dtype == KVQ_BF16 ? 0 : 1;
   a.counters = static_cast<int32_t*>(workspace);
   a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + counters_bytes(batch, cache->num_kv_heads));
+  a.len_cap = static_cast<int>(std::min<long long>(max_seq_len, static_cast<long long>(max_pages) * kPage));
+  a.balanced = plan.balanced ? 1 : 0;
   a.pages_per_split = plan.pages_per_split;
   a.n_splits = plan.n_splits;
+  a.pps_min = plan.pps_min;
+  a.pps_max = plan.pps_max;
+  a.target_wgs = plan.target_wgs;
   a.k_new = stepping ? k_new : nullptr;
   a.v_new = stepping ? v_new : nullptr;
   a.kv_kind = kv_dtype == KVQ_BF16 ? 0 : 1;

@@ -88,6 +88,113 @@ struct PagePair {
   uint4v rec0, rec1, km0, vm0, km1, vm1;
 };
 
+// Sum of v over the workgroup, returned to every thread (s_red: kW ints).
+template <int kW>
+__device__ __forceinline__ int block_sum(int v, int lane, int wave, int* s_red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) t += s_red[w];
+  __syncthreads();  // s_red is free again
+  return t;
+}
+
+// Exclusive prefix sum of v in thread order; `total` receives the sum.
+template <int kW>
+__device__ __forceinline__ int block_excl_scan(int v, int lane, int wave, int* s_red, int& total) {
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) s_red[wave] = x;
+  __syncthreads();
+  int before = 0, t = 0;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    const int c = s_red[w];
+    before += w < wave ? c : 0;
+    t += c;
+  }
+  __syncthreads();
+  total = t;
+  return before + x - v;
+}
+
+__device__ __forceinline__ int seq_pages(const DecodeParams& p, int b) {
+  const int T = min(p.seq_lens[b], p.len_cap);
+  return T > 0 ? (T + kPage - 1) / kPage : 0;
+}
+
+// Balanced plan: the split of work slot w (of one KV head).  Every sequence b
+// takes max(1, ceil(pages_b / pps)) consecutive slots, in sequence order, with
+// pps sized from the batch's total pages; a slot past the last split gets b = -1.
+struct SplitLoc {
+  int b, split, pps, first;  // first = slot of split 0 of sequence b
+};
+template <int kW>
+__device__ SplitLoc locate_split(const DecodeParams& p, int w, int tid, int lane, int wave, int* s_red, int* s_loc) {
+  constexpr int kThreads = 64 * kW;
+  auto pps_for = [&](int total_pages) {
+    const long long want = (static_cast<long long>(p.num_kv_heads) * total_pages + p.target_wgs - 1) / p.target_wgs;
+    return static_cast<int>(min(max(want, static_cast<long long>(p.pps_min)), static_cast<long long>(p.pps_max)));
+  };
+  SplitLoc r;
+  if (p.batch == 1) {  // no scan needed
+    const int pages = seq_pages(p, 0);
+    r.pps = pps_for(pages);
+    const int n = max(1, (pages + r.pps - 1) / r.pps);
+    r.b = w < n ? 0 : -1;
+    r.split = w;
+    r.first = 0;
+    return r;
+  }
+  const int pages0 = tid < p.batch ? seq_pages(p, tid) : 0;  // first chunk, kept for the later passes
+  int tot = pages0;
+  for (int c = kThreads; c < p.batch; c += kThreads) tot += c + tid < p.batch ? seq_pages(p, c + tid) : 0;
+  r.pps = pps_for(block_sum<kW>(tot, lane, wave, s_red));
+  // Each sequence's last split is partial, so the split count can exceed the
+  // target; grow pps (proportionally, a few rounds) until every split of the
+  // batch has a workgroup slot in the first round of the grid.  The smallest
+  // such pps minimises the largest split.
+  auto n_splits_at = [&](int pps) {
+    int n = tid < p.batch ? max(1, (pages0 + pps - 1) / pps) : 0;
+    for (int c = kThreads; c < p.batch; c += kThreads)
+      n += c + tid < p.batch ? max(1, (seq_pages(p, c + tid) + pps - 1) / pps) : 0;
+    return block_sum<kW>(n, lane, wave, s_red);
+  };
+  for (int it = 0; it < 8 && r.pps < p.pps_max; ++it) {
+    const long long fill = static_cast<long long>(p.num_kv_heads) * n_splits_at(r.pps);
+    if (fill <= p.target_wgs) break;
+    const long long next = (static_cast<long long>(r.pps) * fill + p.target_wgs - 1) / p.target_wgs;
+    r.pps = static_cast<int>(min(max(next, static_cast<long long>(r.pps) + 1), static_cast<long long>(p.pps_max)));
+  }
+  if (tid == 0) s_loc[0] = -1;  // ordered before the publishing write by the scan's barriers
+  int run = 0;
+  for (int c = 0; c < p.batch; c += kThreads) {
+    const int i = c + tid;
+    const int pages = c == 0 ? pages0 : (i < p.batch ? seq_pages(p, i) : 0);
+    const int n = i < p.batch ? max(1, (pages + r.pps - 1) / r.pps) : 0;
+    int chunk_total;
+    const int excl = run + block_excl_scan<kW>(n, lane, wave, s_red, chunk_total);
+    if (w >= excl && w < excl + n) {  // exactly one thread of the batch
+      s_loc[0] = i;
+      s_loc[1] = w - excl;
+      s_loc[2] = excl;
+    }
+    run += chunk_total;
+  }
+  __syncthreads();
+  r.b = s_loc[0];
+  r.split = s_loc[1];
+  r.first = s_loc[2];
+  return r;
+}
+
 // Coherent (agent-scope) load of a value another workgroup stored with an agent-scope store.
 __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -134,15 +241,33 @@ void decode_kernel(const DecodeParams p) {
   const int g = p.g;
   const int id = blockIdx.x;
   const int h = id % H;
-  const int split = (id / H) % p.n_splits;
-  const int b = id / (H * p.n_splits);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: ring addresses stay scalar
   auto ring = [&](int slot) -> uint4v(*)[64] { return s_ring[slot][wave]; };
 
-  // Pages past the table row are never read (a length beyond max_pages*16 is cut).
-  const int T = min(p.seq_lens[b], p.max_pages * kPage);
+  // this workgroup's (sequence, split) and the partial row of the sequence's split 0
+  int b, split, pps;
+  size_t head_base;
+  if (p.balanced) {
+    __shared__ int s_red[kW], s_loc[3];
+    const SplitLoc loc = locate_split<kW>(p, id / H, tid, lane, wave, s_red, s_loc);
+    if (loc.b < 0) return;  // past the batch's last split (whole workgroup)
+    b = loc.b;
+    split = loc.split;
+    pps = loc.pps;
+    head_base = static_cast<size_t>(h) * p.n_splits + loc.first;
+  } else {
+    split = (id / H) % p.n_splits;
+    b = id / (H * p.n_splits);
+    pps = p.pages_per_split;
+    head_base = (static_cast<size_t>(b) * H + h) * p.n_splits;
+  }
+
+  // Pages past the table row are never read (a length beyond max_pages*16, or
+  // beyond the host's max_seq_len, is cut).
+  const int T_raw = p.seq_lens[b];
+  const int T = min(T_raw, p.len_cap);
   const int n_pages = T > 0 ? (T + kPage - 1) / kPage : 0;
   const size_t out_row0 = static_cast<size_t>(b) * p.num_q_heads + static_cast<size_t>(h) * g;
   if (n_pages == 0) {  // nothing to attend to: zero output, written once
@@ -156,7 +281,6 @@ void decode_kernel(const DecodeParams p) {
     }
     return;
   }
-  const int pps = p.pages_per_split;
   const int n_valid = (n_pages + pps - 1) / pps;
   const int p0 = split * pps;
   if (p0 >= n_pages) return;  // whole workgroup
@@ -237,8 +361,9 @@ void decode_kernel(const DecodeParams p) {
     for (int ii = 0; ii < kRows; ++ii) asm volatile("" ::"v"(rvv[ii]));
   }
   __syncthreads();
-  // the new token's slot: position T - 1 on the split's last page (masked page: no append)
-  const bool new_ok = own && s_pages[np - 1] >= 0;
+  // the new token's slot: position T - 1 on the split's last page (masked page,
+  // or a length that was cut: no append)
+  const bool new_ok = own && s_pages[np - 1] >= 0 && T_raw == T;
 
   const int a = lane >> 4;    // row of 16 lanes: token quad (QK) / channel octet
   const int col = lane & 15;  // MFMA column: 4*grp + jj
@@ -539,7 +664,6 @@ void decode_kernel(const DecodeParams p) {
   //      stored, for the merge should this workgroup be the last.
   constexpr int kIdx = (kNH * kHeadDim + kThreads - 1) / kThreads;  // output elements per thread
   float own_m[kIdx], own_l[kIdx], own_a[kIdx];
-  const size_t head_base = (static_cast<size_t>(b) * H + h) * p.n_splits;  // first partial of (b, h)
 #pragma unroll
   for (int k = 0; k < kIdx; ++k) {
     const int idx = tid + k * kThreads;
@@ -688,7 +812,8 @@ static hipError_t launch_one(const DecodeParams& prm, hipStream_t stream, hipEve
   DecodeParams arg = prm;
   void* args[] = {&arg};
   return hipExtLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<kNQ, kW, DecodeShape<kNQ>::depth>),
-                            dim3(prm.batch * prm.num_kv_heads * prm.n_splits), dim3(64 * kW), args, 0, stream,
+                            dim3((prm.balanced ? 1 : prm.batch) * prm.num_kv_heads * prm.n_splits), dim3(64 * kW),
+                            args, 0, stream,
                             ev_begin, ev_end, 0);
 }
 

@@ -10,10 +10,18 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
                          int n_tokens, const int32_t* slots, const float* mu, const float* r_k, const float* r_v,
                          float* rot_out, hipStream_t stream);
 
+// Split plan of one decode call.  Fixed plan (an explicit split count): every
+// sequence is cut into n_splits splits of pages_per_split pages.  Balanced
+// plan (automatic): the kernel sizes the splits from the batch's actual total
+// length (pages per split = clamp(ceil(H * total pages / target_wgs), pps_min,
+// pps_max)), so that short sequences take fewer workgroups; n_splits is then
+// the number of split slots per KV head, an upper bound on the batch's total.
 struct DecodePlan {
   int n_pages_max;      // ceil(max_seq_len / 16)
-  int pages_per_split;  // pages handled by one workgroup, <= kMaxPagesPerSplit
-  int n_splits;         // splits per (sequence, KV head), <= kMaxSplits
+  bool balanced;
+  int pages_per_split;  // fixed plan: pages handled by one workgroup, <= kMaxPagesPerSplit
+  int n_splits;         // fixed plan: splits per (sequence, KV head); balanced: slots per KV head
+  int pps_min, pps_max, target_wgs;  // balanced plan
 };
 
 // Kernel arguments of the fused decode (passed by value).
@@ -34,10 +42,16 @@ struct DecodeParams {
   float logit_scale;  // sm_scale * log2(e)
   void* out;
   int out_kind;        // 0 bf16, 1 fp32
-  float* part;         // [batch][num_kv_heads][n_splits][g][kPartStride]
+  // Split partials, rows of kPartStride floats: fixed plan
+  // [batch][num_kv_heads][n_splits][g]; balanced plan [num_kv_heads][n_splits][g],
+  // where the splits of sequence b take the slots after those of sequences < b.
+  float* part;
   int32_t* counters;   // [batch][num_kv_heads], zero between calls
+  int len_cap;         // lengths are cut at min(max_seq_len, max_pages * 16)
+  int balanced;        // DecodePlan fields
   int pages_per_split;
   int n_splits;
+  int pps_min, pps_max, target_wgs;
   // Step form: when k_new is non-null, the token at position seq_lens[b] - 1 of
   // every sequence is first quantize-appended from k_new/v_new [batch][H_kv][128]
   // (kv_kind 0 bf16, 1 fp32; mu [H_kv][128] or null) by the workgroup whose

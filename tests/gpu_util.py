@@ -74,10 +74,10 @@ class DeviceCase:
         torch.cuda.synchronize()
         return rot
 
-    def decode(self, out_dtype="f32", num_splits=0, q=None, table=None, ws=None):
+    def decode(self, out_dtype="f32", num_splits=0, q=None, table=None, ws=None, max_seq=None):
         from rotated_int2_kv_centering_amd import kvq
         c = self.c
-        max_seq = int(c.seq_lens.max(initial=0))
+        max_seq = int(c.seq_lens.max(initial=0)) if max_seq is None else int(max_seq)
         ws_bytes = kvq.kvq_decode_workspace_bytes(c.B, c.Hq, c.Hkv, max_seq, num_splits)
         if ws is None:
             ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=self.dev)

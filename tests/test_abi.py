@@ -72,6 +72,17 @@ def test_workspace_bytes_with_explicit_splits(K):
     assert K.kvq_decode_workspace_bytes(1, 4, 1, big, 600) == 256 + 4 * 4 * 300 * 132
 
 
+def test_workspace_bytes_automatic_plan(K):
+    # Automatic plan, 256 compute units: split slots per KV head
+    # S = min(B * ceil(pages / pps_min), max(ceil(256 / H_kv), ceil(B * pages / 2048)) + B - 1),
+    # pps_min = max(8, ceil(pages / 512)); partial rows = H_q * S.
+    assert K.kvq_decode_workspace_bytes(1, 32, 8, 131072, 0) == 256 + 4 * 32 * 32 * 132
+    assert K.kvq_decode_workspace_bytes(16, 32, 8, 65536, 0) == 512 + 4 * 32 * (32 + 15) * 132
+    assert K.kvq_decode_workspace_bytes(3, 8, 2, 100, 0) == 256 + 4 * 8 * 3 * 132  # one split per sequence
+    # B = 4, 8192 pages: max(32, ceil(4 * 8192 / 2048) = 16) + 3 = 35 slots
+    assert K.kvq_decode_workspace_bytes(4, 64, 8, 131072, 0) == 256 + 4 * 64 * 35 * 132
+
+
 def test_workspace_bytes_rejects_bad_shapes(K):
     assert K.kvq_decode_workspace_bytes(1, 6, 4, 100, 1) == 0   # Hq not a multiple of Hkv
     assert K.kvq_decode_workspace_bytes(-1, 4, 1, 100, 1) == 0

@@ -102,6 +102,57 @@ def test_page_permutation_gives_identical_output():
     np.testing.assert_array_equal(outs[0], outs[1])
 
 
+@pytest.mark.parametrize("Hq,B", [(4, 800), (8, 600)], ids=["g4_B800", "g8_B600"])
+def test_large_ragged_batch(Hq, B):
+    """The automatic plan sizes splits from the batch's total length inside the
+    kernel (a prefix scan over the sequence lengths, in chunks of one
+    workgroup's threads): a batch larger than a workgroup, lengths 0..60 with
+    empty sequences, every row against the oracle, under the automatic and a
+    fixed split plan."""
+    dev = require_gpu()
+    rng = np.random.default_rng(B)
+    lens = rng.integers(0, 61, size=B)
+    lens[::97] = 0
+    case = I.make_case("lb", 500 + B, B=B, Hq=Hq, Hkv=1, seq_lens=lens, table_policy="interleaved")
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False)
+    ref = _oracle_decode(case, dc.pool_np())
+    for ns in (0, 2):
+        got = dc.decode("f32", num_splits=ns)
+        assert np.isfinite(got).all()
+        assert not got[lens == 0].any()
+        assert max_abs_rel(got, ref) <= TOL, ns
+
+
+def test_ragged_batch_rows():
+    """Automatic plan on a ragged batch: the long sequences take many splits, the
+    short ones one, a one-token sequence a single page; every row matches the
+    oracle."""
+    dev = require_gpu()
+    lens = [4000, 70, 1, 2500]
+    case = I.make_case("rb", 77, B=4, Hq=32, Hkv=8, seq_lens=lens, table_policy="interleaved")
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False)
+    got = dc.decode("f32")
+    ref = _oracle_decode(case, dc.pool_np())
+    for b in range(4):
+        assert max_abs_rel(got[b], ref[b]) <= TOL, b
+
+
+def test_length_beyond_max_seq_len_is_cut():
+    """A sequence length above the host's max_seq_len is cut there: the row equals
+    attention over the first max_seq_len tokens (both split plans)."""
+    dev = require_gpu()
+    case = I.make_case("cut", 78, B=2, Hq=8, Hkv=2, seq_lens=[300, 120], table_policy="permuted")
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False)
+    cut = np.array([200, 120], dtype=np.int32)
+    ref = O.decode_attention(case.q, dc.pool_np(), case.Hkv, case.page_table, cut, case.r_k, case.r_v)
+    for ns in (0, 3):
+        got = dc.decode("f32", num_splits=ns, max_seq=200)
+        assert max_abs_rel(got, ref) <= TOL, ns
+
+
 def test_repeated_calls_are_deterministic():
     dev = require_gpu()
     case = I.make_case("r", 11, B=1, Hq=32, Hkv=8, seq_lens=[5000])
