@@ -32,6 +32,9 @@ the design notes of the repository):
 * A sequence of length 0 attends to nothing and its output is zero.
 * A page-table entry outside [0, num_pages) marks an absent page: its
   positions are neither written nor attended.
+* The BF16 window (optional): the first ``sinks`` and the last ``recent``
+  positions of a sequence are attended from their exact BF16 keys and values,
+  the rest from INT2; the page leaves its size open (``window_mask``).
 
 Packed page layout.  The pages fix only that rotation keeps a regular paged
 layout; the byte layout below is this repository's format, stated here in
@@ -352,6 +355,87 @@ def decode_attention(q, pool, num_kv_heads, page_table, seq_lens, r_k, r_v, sm_s
         q_hat = q[b, j] @ np.asarray(r_k[h], np.float64)
         o_rot = softmax_attention(q_hat, xh, wh, sm_scale)
         out[b, j] = o_rot @ np.asarray(r_v[h], np.float64).T
+    return out
+
+
+# --------------------------------------------------- exact (BF16) window
+def window_mask(seq_len: int, sinks: int, recent: int) -> np.ndarray:
+    """Positions of a sequence of length T kept exact next to the INT2 history.
+
+    OptR §3.1 (the text after Eq. (4)) stores the long history in INT2 and
+    keeps a small BF16 window, and attends the keys and values that remain
+    after the rotated INT2 quantization and the BF16 window restore; the page
+    does not size the window.  Reading: the first ``sinks`` positions and the
+    last ``recent`` positions (s >= T - recent) are exact, the rest INT2.
+    """
+    pos = np.arange(int(seq_len))
+    return (pos < sinks) | (pos >= int(seq_len) - recent)
+
+
+def window_slot(t: int, sinks: int, recent: int) -> int:
+    """Slot of position t in a sequence's window buffer: t for a sink, else
+    sinks + t mod recent (a ring over the recent positions)."""
+    return int(t) if t < sinks else sinks + int(t) % recent
+
+
+def effective_kv_window(pool, num_kv_heads, table_row, seq_len, h, mu_h, r_k_h, r_v_h, k_exact, v_exact,
+                        sinks, recent, num_pages=None):
+    """Keys and values attention uses for one sequence and KV head, in the original basis (fp64).
+
+    Window positions (``window_mask``) take k_exact[s], v_exact[s] (the BF16
+    window restore); every other position takes the INT2 cache's
+    D_R(k - mu) + mu = x_hat R_K^T + mu and D_R(v) = w_hat R_V^T (OptR §3.1
+    Eq. (4), with the §1 centering undone).  INT2 positions on absent pages
+    (table entry outside [0, num_pages)) are left out; window positions never
+    are.  k_exact, v_exact are [>= T, 128].
+    """
+    T = int(seq_len)
+    if T == 0:
+        return np.zeros((0, HEAD_DIM)), np.zeros((0, HEAD_DIM))
+    win = window_mask(T, sinks, recent)
+    n_pages = (T + PAGE - 1) // PAGE
+    if num_pages is None:
+        num_pages = np.asarray(pool).size // (num_kv_heads * BLOCK_BYTES)
+    pages = np.asarray(table_row[:n_pages], np.int64)
+    present = (pages >= 0) & (pages < num_pages)
+    offs = (np.where(present, pages, 0) * num_kv_heads + int(h)) * BLOCK_BYTES
+    blocks = np.asarray(pool, np.uint8)[offs[:, None] + np.arange(BLOCK_BYTES)[None, :]]
+    kc, ks, kz, vc, vs, vz = unpack_blocks(blocks)
+    x_hat = int2_dequantize(kc, ks, kz).reshape(-1, HEAD_DIM)[:T]
+    w_hat = int2_dequantize(vc, vs, vz).reshape(-1, HEAD_DIM)[:T]
+    k_int2 = x_hat @ np.asarray(r_k_h, np.float64).T + np.asarray(mu_h, np.float64)
+    v_int2 = w_hat @ np.asarray(r_v_h, np.float64).T
+    k_eff = np.where(win[:, None], np.asarray(k_exact, np.float64)[:T], k_int2)
+    v_eff = np.where(win[:, None], np.asarray(v_exact, np.float64)[:T], v_int2)
+    keep = win | np.repeat(present, PAGE)[:T]
+    return k_eff[keep], v_eff[keep]
+
+
+def decode_attention_window(q, pool, num_kv_heads, page_table, seq_lens, mu, r_k, r_v, k_seqs, v_seqs,
+                            sinks, recent, sm_scale=None, heads=None, num_pages=None) -> np.ndarray:
+    """OptR §3.2 Eq. (5) with the BF16 window: Eq. (1)-(2) attention of query
+    head j of sequence b over ``effective_kv_window`` of KV head h = j // g.
+
+    k_seqs[b], v_seqs[b] are the exact (BF16-valued) keys and values of
+    sequence b, [T_b, H_kv, 128], position-ordered; mu is [H_kv, 128] (None =
+    0).  Returns fp64 [B, H_q, 128] (only ``heads`` filled when given).
+    """
+    q = np.asarray(q, np.float64)
+    B, Hq, d = q.shape
+    g = Hq // num_kv_heads
+    sm_scale = 1.0 / np.sqrt(d) if sm_scale is None else float(sm_scale)
+    mu = np.zeros((num_kv_heads, d)) if mu is None else np.asarray(mu, np.float64)
+    out = np.zeros((B, Hq, d))
+    todo = [(b, j) for b in range(B) for j in range(Hq)] if heads is None else list(heads)
+    cache = {}
+    for b, j in todo:
+        h = j // g
+        if (b, h) not in cache:
+            cache[(b, h)] = effective_kv_window(pool, num_kv_heads, page_table[b], seq_lens[b], h, mu[h], r_k[h],
+                                                r_v[h], np.asarray(k_seqs[b])[:, h], np.asarray(v_seqs[b])[:, h],
+                                                sinks, recent, num_pages)
+        k_eff, v_eff = cache[(b, h)]
+        out[b, j] = softmax_attention(q[b, j], k_eff, v_eff, sm_scale)
     return out
 
 

@@ -426,3 +426,105 @@ def test_centering_reduces_int2_key_error_with_offsets():
         xq = O.int2_dequantize(*O.int2_quantize(x))
         errs.append(np.linalg.norm(x - xq))
     assert errs[1] < errs[0]
+
+
+# ------------------------------------------------------- exact (BF16) window
+def _seqs(c, a):
+    """Per-sequence, position-ordered copies [T_b, H_kv, 128] of a token array."""
+    out = []
+    for b in range(c.B):
+        sel = np.nonzero(c.tok_seq == b)[0]
+        out.append(np.asarray(a)[sel[np.argsort(c.tok_pos[sel])]])
+    return out
+
+
+def _window_case(**kw):
+    c = _tiny(B=2, Hq=8, Hkv=2, seq_lens=kw.pop("seq_lens", [50, 33]), table_policy="permuted", dtype="bf16", **kw)
+    pool = np.zeros(O.pool_bytes(c.num_pages, c.Hkv), np.uint8)
+    O.append_tokens(pool, c.Hkv, c.slots, c.k, c.v, c.mu, c.r_k, c.r_v)
+    return c, pool
+
+
+def test_window_covering_every_position_is_plain_attention():
+    """sinks + recent >= T: every key and value is restored exactly, so the output is
+    Eq. (1)-(2) attention on the raw (bf16) k and v, whatever the INT2 cache holds."""
+    c, pool = _window_case()
+    ks, vs = _seqs(c, c.k), _seqs(c, c.v)
+    for sinks, recent in ((0, 50), (4, 46), (50, 0), (8, 128)):
+        got = O.decode_attention_window(c.q, pool, c.Hkv, c.page_table, c.seq_lens, c.mu, c.r_k, c.r_v, ks, vs,
+                                        sinks, recent)
+        for b in range(c.B):
+            for j in range(c.Hq):
+                ref = _brute_attention(c.q[b, j], ks[b][:, j // 4], vs[b][:, j // 4], 1 / np.sqrt(128))
+                np.testing.assert_allclose(got[b, j], ref, rtol=0, atol=1e-12)
+
+
+def test_empty_window_equals_int2_decode():
+    """sinks = recent = 0: the original-basis effective-KV form equals the rotated-basis
+    decode (q R_K against x_hat, mu dropped, output mapped back by R_V^T)."""
+    c, pool = _window_case()
+    got = O.decode_attention_window(c.q, pool, c.Hkv, c.page_table, c.seq_lens, c.mu, c.r_k, c.r_v,
+                                    _seqs(c, c.k), _seqs(c, c.v), 0, 0)
+    ref = O.decode_attention(c.q, pool, c.Hkv, c.page_table, c.seq_lens, c.r_k, c.r_v)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
+
+
+def test_window_positions_brute_force():
+    """Which positions are exact, built independently with list slicing, then explicit
+    per-position effective keys/values and looped attention."""
+    c, pool = _window_case(seq_lens=[40, 9])
+    ks, vs = _seqs(c, c.k), _seqs(c, c.v)
+    x, w = O.rotated_inputs(c.k, c.v, c.mu, c.r_k, c.r_v)
+    kq = _seqs(c, O.int2_dequantize(*O.int2_quantize(x)))
+    vq = _seqs(c, O.int2_dequantize(*O.int2_quantize(w)))
+    for sinks, recent in ((3, 7), (0, 1), (5, 0), (6, 6), (12, 30)):
+        got = O.decode_attention_window(c.q, pool, c.Hkv, c.page_table, c.seq_lens, c.mu, c.r_k, c.r_v, ks, vs,
+                                        sinks, recent)
+        for b in range(c.B):
+            T = int(c.seq_lens[b])
+            positions = list(range(T))
+            exact = set(positions[:sinks]) | (set(positions[-recent:]) if recent else set())
+            for j in (0, 5):
+                h = j // 4
+                keys, vals = [], []
+                for s in positions:
+                    if s in exact:
+                        keys.append(ks[b][s, h])
+                        vals.append(vs[b][s, h])
+                    else:
+                        keys.append(kq[b][s, h] @ c.r_k[h].astype(np.float64).T + c.mu[h])
+                        vals.append(vq[b][s, h] @ c.r_v[h].astype(np.float64).T)
+                ref = _brute_attention(c.q[b, j], np.array(keys), np.array(vals), 1 / np.sqrt(128))
+                np.testing.assert_allclose(got[b, j], ref, rtol=0, atol=1e-11)
+    # one more exact position changes the output (the boundary is not off by one)
+    a = O.decode_attention_window(c.q, pool, c.Hkv, c.page_table, c.seq_lens, c.mu, c.r_k, c.r_v, ks, vs, 0, 7)
+    b_ = O.decode_attention_window(c.q, pool, c.Hkv, c.page_table, c.seq_lens, c.mu, c.r_k, c.r_v, ks, vs, 0, 8)
+    assert np.abs(a[0] - b_[0]).max() > 1e-6
+
+
+def test_window_slots_are_distinct():
+    """Within any length, the window positions map to distinct slots of the buffer."""
+    for sinks, recent in ((4, 128), (0, 5), (3, 1), (8, 0), (2, 16)):
+        for T in range(0, 300):
+            pos = np.nonzero(O.window_mask(T, sinks, recent))[0]
+            slots = [O.window_slot(t, sinks, recent) for t in pos]
+            assert len(set(slots)) == len(slots)
+            assert all(0 <= s < sinks + recent for s in slots)
+
+
+def test_window_positions_survive_absent_pages():
+    """An absent page drops its INT2 positions but not the window positions on it."""
+    c = _tiny(seq_lens=[64], dtype="bf16")
+    pool = np.zeros(O.pool_bytes(c.num_pages, 1), np.uint8)
+    O.append_tokens(pool, 1, c.slots, c.k, c.v, c.mu, c.r_k, c.r_v)
+    table = c.page_table.copy()
+    table[0, 0] = -1  # positions 0..15 absent from the INT2 cache; sinks 0..3 stay
+    ks, vs = _seqs(c, c.k), _seqs(c, c.v)
+    got = O.decode_attention_window(c.q, pool, 1, table, c.seq_lens, c.mu, c.r_k, c.r_v, ks, vs, 4, 10,
+                                    num_pages=c.num_pages)
+    k_eff, v_eff = O.effective_kv_window(pool, 1, c.page_table[0], 64, 0, c.mu[0], c.r_k[0], c.r_v[0], ks[0][:, 0],
+                                         vs[0][:, 0], 4, 10)
+    keep = np.r_[0:4, 16:64]
+    for j in range(c.Hq):
+        ref = _brute_attention(c.q[0, j], k_eff[keep], v_eff[keep], 1 / np.sqrt(128))
+        np.testing.assert_allclose(got[0, j], ref, rtol=0, atol=1e-11)
