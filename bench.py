@@ -176,6 +176,7 @@ def main() -> int:
                     help="length of the spin kernel that holds the stream while the timed steps are enqueued")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-kv-heads", type=int, default=8, help="KV heads in the oracle's timed sample (0 = skip)")
+    ap.add_argument("--window", default="", help="exact bf16 window 'sinks,recent' (e.g. 4,128); default none")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -253,11 +254,28 @@ def main() -> int:
     ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
     outs = [torch.empty((case.B, case.Hq, 128), dtype=torch.bfloat16, device=dev) for _ in range(n_rep)]
 
+    # optional exact window: one buffer per replica, filled with the window positions of the context
+    sinks, recent = (int(x) for x in args.window.split(",")) if args.window else (0, 0)
+    wins, win_bufs = [None] * n_rep, []
+    n_win_tok = 0
+    if sinks or recent:
+        keep = np.nonzero([(p < sinks) or (p >= case.seq_lens[b] - recent)
+                           for b, p in zip(case.tok_seq, case.tok_pos)])[0]
+        n_win_tok = len(keep)
+        kw, vw = B16(case.k_bits[keep]), B16(case.v_bits[keep])
+        for r in range(n_rep):
+            probe = kvq.make_window(sinks, recent, case.B)
+            win_bufs.append(torch.zeros(kvq.kvq_window_bytes(probe, case.Hkv), dtype=torch.uint8, device=dev))
+            wins[r] = kvq.make_window(sinks, recent, case.B, win_bufs[-1], mus[r])
+            kvq.kvq_window_fill(wins[r], case.Hkv, kw, vw, kvq.KVQ_BF16, n_win_tok, T(case.tok_seq[keep]),
+                                T(case.tok_pos[keep]), seq)
+        torch.cuda.synchronize()
+
     def step(r, ev_b=None, ev_e=None):
         # one kernel: quantize-append of the newest token (position T-1) of every sequence, then decode
         kvq.kvq_decode_step(caches[r], k_new, v_new, kvq.KVQ_BF16, mus[r], q, kvq.KVQ_BF16, case.B, case.Hq, table,
                             table.shape[1], seq, max_seq, rks[r], rvs[r], 0.0, outs[r], kvq.KVQ_BF16, ws, ws_bytes,
-                            args.num_splits, None, ev_b, ev_e)
+                            args.num_splits, window=wins[r], stream=None, ev_begin=ev_b, ev_end=ev_e)
 
     # eager reference output of every replica (also warms up the kernels)
     for r in range(n_rep):
@@ -325,6 +343,8 @@ def main() -> int:
     n_pages = int(((case.seq_lens + PAGE - 1) // PAGE).sum())
     # packed cache + page-table entries read, plus the newest token's bf16 k/v read and 96 B written per KV head
     alg_bytes = cache_bytes + 4 * n_pages + case.B * case.Hkv * (512 + BYTES_PER_TOKEN_HEAD)
+    # with an exact window: its bf16 key and value rows (512 B per position per KV head) are read too
+    alg_bytes += n_win_tok * case.Hkv * 512
     achieved = alg_bytes / (split_avg_ms * 1e-3) / 1e9
     traffic = counters_for(kernel_source_sha(), args.workload)
 
@@ -352,6 +372,7 @@ def main() -> int:
             "context_tokens": int(tokens), "group_size": 32, "page_size": PAGE,
             "page_table": "seeded permutation" if case.B == 1 else "seeded interleaved allocator",
             "cache_replicas": n_rep, "num_splits": args.num_splits or "auto",
+            "exact_window": {"sinks": sinks, "recent": recent} if (sinks or recent) else None,
         },
         "hbm_gbps_step": cache_bytes / (ms_per_step * 1e-3) / 1e9,
         "pct_peak_step": cache_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,

@@ -85,6 +85,37 @@ typedef struct {
   void* pool;           /* device, kvq_pool_bytes(cache) bytes, 16-byte aligned */
 } kvq_cache;
 
+/*
+ * Optional exact window next to the INT2 history (OptR section 3.1, the text
+ * after Eq. (4): the long history is stored in INT2 while a small BF16 window
+ * is kept, and attention uses the keys and values left after the rotated INT2
+ * quantization and the BF16 window restore; the page leaves the window's size
+ * open).  With a window, positions s < sinks and s >= T - recent of a sequence
+ * of length T are attended from their exact bf16 key and value kept in `buf`;
+ * every other position from the INT2 cache.  Every token is still quantized
+ * into the cache as usual (Q2 acts on each token alone, so the INT2 bytes are
+ * the same as if a token were quantized when it leaves the window).
+ * A window key's logit is <q, k - mu> * sm_scale: the same offset mu the keys
+ * were centred with at append, so that exact and INT2 logits share one
+ * constant shift.
+ *
+ *   sinks   0..8: leading positions kept exact.
+ *   recent  0..128: trailing positions kept exact.
+ *   batch   sequences the buffer holds (>= the batch of every call using it).
+ *   buf     device bf16 [batch][num_kv_heads][sinks + recent][2][128]: slot
+ *           t of a position t < sinks, else slot sinks + t % recent; in a slot
+ *           the key row, then the value row.  16-byte aligned.
+ *   mu      device fp32 [num_kv_heads][128] key offsets, or NULL (zero).
+ * A window with sinks == recent == 0 is the same as none.
+ */
+typedef struct {
+  int32_t sinks;
+  int32_t recent;
+  int32_t batch;
+  void* buf;
+  const float* mu;
+} kvq_window;
+
 /* Bytes of the pool: num_pages * num_kv_heads * 1536.  0 if `cache` is NULL
  * or has non-positive sizes. */
 size_t kvq_pool_bytes(const kvq_cache* cache);
@@ -164,10 +195,15 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
  *               splits, so the count used can differ from the request;
  *               kvq_decode_workspace_bytes follows the same plan.  Lengths
  *               above max_seq_len are cut to max_seq_len.
+ *   window      NULL, or an exact window (kvq_window): its positions are
+ *               attended from the window buffer (read only here), the others
+ *               from the cache.  The buffer's slots of every window position
+ *               must hold that position's key and value (kvq_window_fill,
+ *               kvq_decode_step).  Supported for g <= 8.
  * Work decomposition: one kernel launch; one workgroup per compute unit
  * (12 waves for g <= 4, 8 for g <= 8, else 4) streams a split's pages, and
  * the last workgroup of each (sequence, KV head) merges the split partials
- * (log-sum-exp) and applies R_V^T.
+ * (log-sum-exp), adds the window's part, and applies R_V^T.
  * Limits: max_seq_len <= 16777216 (512 splits x 2048 pages x 16 tokens).
  * Errors: KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ENOSPACE (workspace too small),
  * KVQ_EHIP.  batch == 0 is a no-op.
@@ -176,7 +212,7 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const void* q, kvq_dtype q_dt
                            int32_t num_q_heads, const int32_t* page_table, int32_t max_pages,
                            const int32_t* seq_lens, int32_t max_seq_len, const float* r_k, const float* r_v,
                            float sm_scale, void* out, kvq_dtype out_dtype, void* workspace,
-                           size_t workspace_bytes, int32_t num_splits, void* stream);
+                           size_t workspace_bytes, int32_t num_splits, const kvq_window* window, void* stream);
 
 /*
  * kvq_decode_attn_traced - kvq_decode_attn plus timing events for measurement.
@@ -191,8 +227,8 @@ kvq_status kvq_decode_attn_traced(const kvq_cache* cache, const void* q, kvq_dty
                                   int32_t num_q_heads, const int32_t* page_table, int32_t max_pages,
                                   const int32_t* seq_lens, int32_t max_seq_len, const float* r_k, const float* r_v,
                                   float sm_scale, void* out, kvq_dtype out_dtype, void* workspace,
-                                  size_t workspace_bytes, int32_t num_splits, void* stream, void* ev_begin,
-                                  void* ev_end);
+                                  size_t workspace_bytes, int32_t num_splits, const kvq_window* window,
+                                  void* stream, void* ev_begin, void* ev_end);
 
 /*
  * kvq_decode_step - one decode step in one kernel: quantize-append the newest
@@ -204,7 +240,10 @@ kvq_status kvq_decode_attn_traced(const kvq_cache* cache, const void* q, kvq_dty
  * position seq_lens[b] - 1 of each sequence b (slot page_table[b][t / 16] * 16
  * + t % 16 with t = seq_lens[b] - 1), followed by kvq_decode_attn with the
  * same arguments: the cache bytes written are identical to kvq_quant_append's,
- * and the new token is attended from its packed INT2 levels.
+ * and the new token is attended from its packed INT2 levels.  With a window
+ * whose positions include seq_lens[b] - 1, the new token is attended exactly
+ * instead and also stored into its window slot (bf16; fp32 input rounded to
+ * nearest even); it is still quantized into the cache.
  *
  * Arguments: those of kvq_decode_attn_traced, plus
  *   k_new, v_new  device [batch][num_kv_heads][128], dtype kv_dtype (KVQ_BF16
@@ -213,7 +252,8 @@ kvq_status kvq_decode_attn_traced(const kvq_cache* cache, const void* q, kvq_dty
  * seq_lens[b] counts the new token.  A sequence of length 0 appends nothing
  * and outputs zeros.  If the page holding position seq_lens[b] - 1 is outside
  * [0, num_pages), the token is neither written nor attended (as in
- * kvq_quant_append and kvq_decode_attn).  The slot at that position is
+ * kvq_quant_append and kvq_decode_attn), unless a window holds that position:
+ * then it is still stored into the window and attended from there.  The slot at that position is
  * overwritten; its previous content is never read.  ev_begin / ev_end are
  * optional timing events as in kvq_decode_attn_traced (NULL for none).
  * Errors: those of kvq_decode_attn; KVQ_EINVAL if k_new or v_new is NULL;
@@ -224,7 +264,33 @@ kvq_status kvq_decode_step(const kvq_cache* cache, const void* k_new, const void
                            const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
                            int32_t max_seq_len, const float* r_k, const float* r_v, float sm_scale, void* out,
                            kvq_dtype out_dtype, void* workspace, size_t workspace_bytes, int32_t num_splits,
-                           void* stream, void* ev_begin, void* ev_end);
+                           const kvq_window* window, void* stream, void* ev_begin, void* ev_end);
+
+/*
+ * kvq_window_bytes - bytes of the window buffer of `window` for num_kv_heads
+ * KV heads: batch * num_kv_heads * (sinks + recent) * 512.  0 on invalid input
+ * (NULL, sinks outside 0..8, recent outside 0..128, batch < 0, num_kv_heads < 1).
+ */
+size_t kvq_window_bytes(const kvq_window* window, int32_t num_kv_heads);
+
+/*
+ * kvq_window_fill - store the exact keys and values of window positions.
+ * The window of kvq_window (OptR section 3.1, the BF16 window kept next to
+ * the INT2 history).  Token i (sequence seq_ids[i], position positions[i])
+ * is stored iff its position is a window position of a sequence of length
+ * seq_lens[seq_ids[i]] (t < sinks, or T - recent <= t < T); other tokens are
+ * skipped.  Positions must be distinct within a sequence.
+ *   k, v        device [n_tokens][num_kv_heads][128], in_dtype KVQ_BF16 (copied
+ *               bit for bit) or KVQ_F32 (rounded to bf16, nearest even).
+ *   seq_ids, positions  device int32 [n_tokens]; a sequence id outside
+ *               [0, window->batch) or a negative position skips the token.
+ *   seq_lens    device int32 [window->batch]: the lengths the window is for.
+ * Errors: KVQ_EINVAL (NULL arguments, bad window), KVQ_EUNSUPPORTED (dtype),
+ * KVQ_EHIP.  n_tokens == 0 is a no-op.
+ */
+kvq_status kvq_window_fill(const kvq_window* window, int32_t num_kv_heads, const void* k, const void* v,
+                           kvq_dtype in_dtype, int32_t n_tokens, const int32_t* seq_ids, const int32_t* positions,
+                           const int32_t* seq_lens, void* stream);
 
 /* Page-table policies for kvq_page_table. */
 typedef enum {

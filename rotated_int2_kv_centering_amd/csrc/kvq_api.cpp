@@ -86,14 +86,20 @@ int device_cu_count() {
 // compute unit holds for its group size (12 for g <= 4, 8 for g <= 8, else 4).
 int workgroups_per_cu(int) { return 1; }
 
-bool make_plan(int batch, int num_kv_heads, int g, int max_seq_len, int num_splits, kvq::DecodePlan* plan) {
+// Splits of one (sequence, KV head) the merging workgroup can stage in LDS
+// next to an exact window (kvq_decode.hip lays the window out in the same
+// LDS; without a window the limit is kMaxSplits).
+int max_splits_with_window(int g) { return g <= 4 ? kMaxSplits : 128; }
+
+bool make_plan(int batch, int num_kv_heads, int g, int max_seq_len, int num_splits, kvq::DecodePlan* plan,
+               int max_splits = kMaxSplits) {
   if (batch < 0 || num_kv_heads < 1 || max_seq_len < 0 || num_splits < 0) return false;
   if (max_seq_len > kMaxContext) return false;
   const int n_pages = (max_seq_len + kPage - 1) / kPage;
   const long long n1 = std::max(n_pages, 1);
   plan->n_pages_max = n_pages;
-  // no split of any plan holds more than kMaxSplits of one sequence's splits
-  const long long pps_floor = (n_pages + kMaxSplits - 1) / kMaxSplits;
+  // no sequence is cut into more than max_splits splits
+  const long long pps_floor = (n_pages + max_splits - 1) / max_splits;
   const long long target = static_cast<long long>(workgroups_per_cu(g)) * device_cu_count();
   plan->balanced = num_splits == 0 && static_cast<long long>(batch) * n1 <= 0x7fffffffLL;
   if (plan->balanced) {
@@ -144,6 +150,23 @@ size_t workspace_bytes(int batch, int num_q_heads, int num_kv_heads, const kvq::
   return counters_bytes(batch, num_kv_heads) + sizeof(float) * rows * kRowStride;
 }
 
+constexpr int kMaxWindowSinks = 8;
+constexpr int kMaxWindowRecent = 128;
+
+// A window with no positions is the same as none.
+bool window_active(const kvq_window* w) { return w != nullptr && (w->sinks != 0 || w->recent != 0); }
+
+kvq_status check_window(const kvq_window* w) {
+  if (w->sinks < 0 || w->sinks > kMaxWindowSinks)
+    return fail(KVQ_EINVAL, "window sinks=%d must be in [0, %d]", w->sinks, kMaxWindowSinks);
+  if (w->recent < 0 || w->recent > kMaxWindowRecent)
+    return fail(KVQ_EINVAL, "window recent=%d must be in [0, %d]", w->recent, kMaxWindowRecent);
+  if (w->batch < 0) return fail(KVQ_EINVAL, "window batch=%d must be >= 0", w->batch);
+  if (w->buf == nullptr) return fail(KVQ_EINVAL, "window buffer is NULL");
+  if (reinterpret_cast<uintptr_t>(w->buf) % 16 != 0) return fail(KVQ_EINVAL, "window buffer must be 16-byte aligned");
+  return KVQ_OK;
+}
+
 // splitmix64 (Steele, Lea, Flood 2014) as the page allocator's random stream.
 struct SplitMix64 {
   uint64_t s;
@@ -165,8 +188,8 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
                          const float* mu, const void* q, kvq_dtype q_dtype, int32_t batch, int32_t num_q_heads,
                          const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens, int32_t max_seq_len,
                          const float* r_k, const float* r_v, float sm_scale, void* out, kvq_dtype out_dtype,
-                         void* workspace, size_t workspace_bytes_, int32_t num_splits, void* stream, void* ev_begin,
-                         void* ev_end) {
+                         void* workspace, size_t workspace_bytes_, int32_t num_splits, const kvq_window* window,
+                         void* stream, void* ev_begin, void* ev_end) {
   kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
   if (batch < 0) return fail(KVQ_EINVAL, "batch=%d must be >= 0", batch);
@@ -199,8 +222,17 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
 
   if (max_seq_len > kMaxContext)
     return fail(KVQ_EUNSUPPORTED, "max_seq_len=%d exceeds the supported %lld", max_seq_len, kMaxContext);
+  const bool win = window_active(window);
+  if (win) {
+    st = check_window(window);
+    if (st != KVQ_OK) return st;
+    if (window->batch < batch)
+      return fail(KVQ_EINVAL, "window holds %d sequences, the call has %d", window->batch, batch);
+    if (g > 8) return fail(KVQ_EUNSUPPORTED, "an exact window needs g <= 8 (g=%d)", g);
+  }
   kvq::DecodePlan plan;
-  if (!make_plan(batch, cache->num_kv_heads, g, max_seq_len, num_splits, &plan))
+  if (!make_plan(batch, cache->num_kv_heads, g, max_seq_len, num_splits, &plan,
+                 win ? max_splits_with_window(g) : kMaxSplits))
     return fail(KVQ_EINVAL, "cannot plan the decode split");
   const size_t need = workspace_bytes(batch, num_q_heads, cache->num_kv_heads, plan);
   if (workspace_bytes_ < need)
@@ -235,6 +267,10 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
   a.pps_min = plan.pps_min;
   a.pps_max = plan.pps_max;
   a.target_wgs = plan.target_wgs;
+  a.win = win ? static_cast<uint16_t*>(window->buf) : nullptr;
+  a.win_sinks = win ? window->sinks : 0;
+  a.win_recent = win ? window->recent : 0;
+  a.win_mu = win ? window->mu : nullptr;
   a.k_new = stepping ? k_new : nullptr;
   a.v_new = stepping ? v_new : nullptr;
   a.kv_kind = kv_dtype == KVQ_BF16 ? 0 : 1;
@@ -286,21 +322,21 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const void* q, kvq_dtype q_dt
                            int32_t num_q_heads, const int32_t* page_table, int32_t max_pages,
                            const int32_t* seq_lens, int32_t max_seq_len, const float* r_k, const float* r_v,
                            float sm_scale, void* out, kvq_dtype out_dtype, void* workspace, size_t workspace_bytes_,
-                           int32_t num_splits, void* stream) {
+                           int32_t num_splits, const kvq_window* window, void* stream) {
   return decode_common(cache, nullptr, nullptr, KVQ_BF16, nullptr, q, q_dtype, batch, num_q_heads, page_table,
                        max_pages, seq_lens, max_seq_len, r_k, r_v, sm_scale, out, out_dtype, workspace,
-                       workspace_bytes_, num_splits, stream, nullptr, nullptr);
+                       workspace_bytes_, num_splits, window, stream, nullptr, nullptr);
 }
 
 kvq_status kvq_decode_attn_traced(const kvq_cache* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
                                   int32_t num_q_heads, const int32_t* page_table, int32_t max_pages,
                                   const int32_t* seq_lens, int32_t max_seq_len, const float* r_k, const float* r_v,
                                   float sm_scale, void* out, kvq_dtype out_dtype, void* workspace,
-                                  size_t workspace_bytes_, int32_t num_splits, void* stream, void* ev_begin,
-                                  void* ev_end) {
+                                  size_t workspace_bytes_, int32_t num_splits, const kvq_window* window,
+                                  void* stream, void* ev_begin, void* ev_end) {
   return decode_common(cache, nullptr, nullptr, KVQ_BF16, nullptr, q, q_dtype, batch, num_q_heads, page_table,
                        max_pages, seq_lens, max_seq_len, r_k, r_v, sm_scale, out, out_dtype, workspace,
-                       workspace_bytes_, num_splits, stream, ev_begin, ev_end);
+                       workspace_bytes_, num_splits, window, stream, ev_begin, ev_end);
 }
 
 kvq_status kvq_decode_step(const kvq_cache* cache, const void* k_new, const void* v_new, kvq_dtype kv_dtype,
@@ -308,11 +344,40 @@ kvq_status kvq_decode_step(const kvq_cache* cache, const void* k_new, const void
                            const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
                            int32_t max_seq_len, const float* r_k, const float* r_v, float sm_scale, void* out,
                            kvq_dtype out_dtype, void* workspace, size_t workspace_bytes_, int32_t num_splits,
-                           void* stream, void* ev_begin, void* ev_end) {
+                           const kvq_window* window, void* stream, void* ev_begin, void* ev_end) {
   if (k_new == nullptr || v_new == nullptr) return fail(KVQ_EINVAL, "k_new and v_new must be non-NULL");
   return decode_common(cache, k_new, v_new, kv_dtype, mu, q, q_dtype, batch, num_q_heads, page_table, max_pages,
                        seq_lens, max_seq_len, r_k, r_v, sm_scale, out, out_dtype, workspace, workspace_bytes_,
-                       num_splits, stream, ev_begin, ev_end);
+                       num_splits, window, stream, ev_begin, ev_end);
+}
+
+size_t kvq_window_bytes(const kvq_window* window, int32_t num_kv_heads) {
+  if (window == nullptr || num_kv_heads < 1 || window->batch < 0 || window->sinks < 0 ||
+      window->sinks > kMaxWindowSinks || window->recent < 0 || window->recent > kMaxWindowRecent)
+    return 0;
+  return static_cast<size_t>(window->batch) * num_kv_heads * (window->sinks + window->recent) * 2 * kHeadDim *
+         sizeof(uint16_t);
+}
+
+kvq_status kvq_window_fill(const kvq_window* window, int32_t num_kv_heads, const void* k, const void* v,
+                           kvq_dtype in_dtype, int32_t n_tokens, const int32_t* seq_ids, const int32_t* positions,
+                           const int32_t* seq_lens, void* stream) {
+  if (window == nullptr) return fail(KVQ_EINVAL, "window is NULL");
+  if (num_kv_heads < 1) return fail(KVQ_EINVAL, "num_kv_heads=%d must be >= 1", num_kv_heads);
+  if (n_tokens < 0) return fail(KVQ_EINVAL, "n_tokens=%d must be >= 0", n_tokens);
+  if (in_dtype != KVQ_BF16 && in_dtype != KVQ_F32)
+    return fail(KVQ_EUNSUPPORTED, "window input dtype must be bf16 or fp32");
+  if (!window_active(window)) return KVQ_OK;  // no positions to keep
+  kvq_status st = check_window(window);
+  if (st != KVQ_OK) return st;
+  if (n_tokens == 0 || window->batch == 0) return KVQ_OK;
+  if (k == nullptr || v == nullptr || seq_ids == nullptr || positions == nullptr || seq_lens == nullptr)
+    return fail(KVQ_EINVAL, "k, v, seq_ids, positions and seq_lens must be non-NULL");
+  hipError_t e = kvq::launch_window_fill(static_cast<uint16_t*>(window->buf), window->batch, num_kv_heads,
+                                         window->sinks, window->recent, k, v, in_dtype == KVQ_BF16 ? 0 : 1, n_tokens,
+                                         seq_ids, positions, seq_lens, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "window_fill launch");
+  return KVQ_OK;
 }
 
 kvq_status kvq_page_table(int32_t policy, uint64_t seed, const int32_t* seq_lens, int32_t batch, int32_t page_size,

@@ -313,4 +313,56 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ exact window
+// The BF16 window kept next to the INT2 history (OptR section 3.1): one
+// workgroup per token copies its key and value rows of every KV head into the
+// window slot of its position, when that position is a window position of its
+// sequence (t < sinks, or T - recent <= t < T).  16 bytes (8 bf16) per thread
+// and step; fp32 input is rounded to bf16, nearest even.
+constexpr int kFillThreads = 128;
+
+__global__ __launch_bounds__(kFillThreads) void window_fill_kernel(uint16_t* __restrict__ buf, int batch, int H,
+                                                                   int sinks, int recent, const void* __restrict__ k,
+                                                                   const void* __restrict__ v, int in_kind,
+                                                                   const int32_t* __restrict__ seq_ids,
+                                                                   const int32_t* __restrict__ positions,
+                                                                   const int32_t* __restrict__ seq_lens) {
+  const int n = blockIdx.x;
+  const int b = seq_ids[n];
+  const int t = positions[n];
+  if (b < 0 || b >= batch || t < 0) return;
+  const int T = seq_lens[b];
+  if (t >= T || (t >= sinks && t < T - recent)) return;  // not a window position
+  const int slot = t < sinks ? t : sinks + t % recent;   // recent > 0 here
+  const int n_slots = sinks + recent;
+  for (int e = threadIdx.x; e < H * 2 * 16; e += kFillThreads) {
+    const int h = e >> 5, kv = (e >> 4) & 1, j = e & 15;
+    const size_t src = (static_cast<size_t>(n) * H + h) * kHeadDim + 8 * j;
+    uint4v w;
+    if (in_kind == 0) {
+      w = *reinterpret_cast<const uint4v*>(static_cast<const uint16_t*>(kv ? v : k) + src);
+    } else {
+      const float* f = static_cast<const float*>(kv ? v : k) + src;
+      const float4v lo = *reinterpret_cast<const float4v*>(f);
+      const float4v hi = *reinterpret_cast<const float4v*>(f + 4);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        w[i] = f32_to_bf16_bits(lo[2 * i]) | (static_cast<uint32_t>(f32_to_bf16_bits(lo[2 * i + 1])) << 16);
+        w[2 + i] = f32_to_bf16_bits(hi[2 * i]) | (static_cast<uint32_t>(f32_to_bf16_bits(hi[2 * i + 1])) << 16);
+      }
+    }
+    *reinterpret_cast<uint4v*>(buf + ((static_cast<size_t>(b) * H + h) * n_slots + slot) * 2 * kHeadDim +
+                               kv * kHeadDim + 8 * j) = w;
+  }
+}
+
+hipError_t launch_window_fill(uint16_t* buf, int batch, int num_kv_heads, int sinks, int recent, const void* k,
+                              const void* v, int in_kind, int n_tokens, const int32_t* seq_ids,
+                              const int32_t* positions, const int32_t* seq_lens, hipStream_t stream) {
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(window_fill_kernel, dim3(n_tokens), dim3(kFillThreads), 0, stream, buf, batch, num_kv_heads,
+                     sinks, recent, k, v, in_kind, seq_ids, positions, seq_lens);
+  return hipGetLastError();
+}
+
 }  // namespace kvq

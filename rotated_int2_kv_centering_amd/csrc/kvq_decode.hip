@@ -67,6 +67,7 @@ template <> struct DecodeShape<1> { static constexpr int waves = 12, waves_per_s
 template <> struct DecodeShape<2> { static constexpr int waves = 8, waves_per_simd = 2, depth = 4; };
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // 16 bytes per lane from global memory straight into LDS: lane l reads
 // base + voff (base wave-uniform, in SGPRs) and its bytes land at lds + 16*l
@@ -291,7 +292,15 @@ void decode_kernel(const DecodeParams p) {
   // may still hold an older token (and is rewritten during this launch).
   const bool stepping = p.k_new != nullptr;
   const bool own = stepping && split == n_valid - 1;
-  const int T_read = stepping ? T - 1 : T;
+  // INT2 positions attended from the paged cache: [int2_lo, int2_hi).  An exact
+  // window takes the first win_sinks and the last win_recent positions; in the
+  // step form the new token at T - 1 is attended from its packed levels
+  // instead (unless the window holds it).
+  const bool has_win = p.win != nullptr;
+  const bool new_in_win = stepping && has_win && (T - 1 < p.win_sinks || p.win_recent > 0);
+  const int int2_lo = has_win ? min(p.win_sinks, T) : 0;
+  int int2_hi = has_win ? max(int2_lo, T - p.win_recent) : T;
+  if (stepping && !new_in_win) int2_hi = min(int2_hi, T - 1);
 
   // ---- prologue loads, all issued before the first wait: this split's page
   // ids, the g query rows and R_K.  Indices are clamped in bounds and values
@@ -348,6 +357,12 @@ void decode_kernel(const DecodeParams p) {
   }
   if (own && tid < 2 * kHeadDim) {
     float nv = p.kv_kind == 0 ? bf16_bits_to_f32(static_cast<uint16_t>(nraw >> (16 * (ni & 1)))) : __uint_as_float(nraw);
+    if (new_in_win && T_raw == T) {  // the new token's exact row into its window slot (bf16, nearest even)
+      const int t = T - 1;
+      const int slot = t < p.win_sinks ? t : p.win_sinks + t % p.win_recent;
+      p.win[((static_cast<size_t>(b) * H + h) * (p.win_sinks + p.win_recent) + slot) * 2 * kHeadDim +
+            (tid / kHeadDim) * kHeadDim + rc] = f32_to_bf16_bits(nv);
+    }
     if (tid < kHeadDim && p.mu != nullptr) nv = nv - __uint_as_float(muraw);  // key centering (fp32)
     s_nrow[tid / kHeadDim][rc] = nv;
   }
@@ -364,6 +379,7 @@ void decode_kernel(const DecodeParams p) {
   // the new token's slot: position T - 1 on the split's last page (masked page,
   // or a length that was cut: no append)
   const bool new_ok = own && s_pages[np - 1] >= 0 && T_raw == T;
+  const bool new_att = new_ok && !new_in_win;  // attended from its packed levels here
 
   const int a = lane >> 4;    // row of 16 lanes: token quad (QK) / channel octet
   const int col = lane & 15;  // MFMA column: 4*grp + jj
@@ -447,7 +463,7 @@ void decode_kernel(const DecodeParams p) {
     }
   }
   __syncthreads();
-  if (new_ok) {  // logits (log2 units) of the new token: one wave per head
+  if (new_att) {  // logits (log2 units) of the new token: one wave per head
     for (int jh = wave; jh < g; jh += kW) {
       float d = fmaf(s_q[jh][lane], s_hat[0][lane], s_q[jh][lane + 64] * s_hat[0][lane + 64]);
 #pragma unroll
@@ -514,7 +530,8 @@ void decode_kernel(const DecodeParams p) {
     const int ph1 = __builtin_amdgcn_readfirstlane(i0 + 1 < np ? s_pages[i0 + 1] : -1);
     const bool ok0 = ph0 >= 0;
     const bool has1 = ph1 >= 0;
-    const bool full = ok0 && has1 && (p0 + i0 + 2) * kPage <= T_read;  // no position of the pair masked
+    // no position of the pair masked
+    const bool full = ok0 && has1 && (p0 + i0) * kPage >= int2_lo && (p0 + i0 + 2) * kPage <= int2_hi;
     // logits (log2 units, divided by c1) for both pages
     float sp[kNQ][2][4];
 #pragma unroll
@@ -553,7 +570,7 @@ void decode_kernel(const DecodeParams p) {
         if (!full) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            if (!(page_ok && pos0 + i < T_read)) sp[Q][X][i] = -INFINITY;
+            if (!(page_ok && pos0 + i >= int2_lo && pos0 + i < int2_hi)) sp[Q][X][i] = -INFINITY;
         }
       }
     }
@@ -673,7 +690,7 @@ void decode_kernel(const DecodeParams p) {
     float M = kNegBig;
 #pragma unroll
     for (int w = 0; w < kW; ++w) M = fmaxf(M, s_m[w][jh]);
-    if (new_ok) M = fmaxf(M, s_nlog[jh]);
+    if (new_att) M = fmaxf(M, s_nlog[jh]);
     float av = 0.0f, lv = 0.0f;
 #pragma unroll
     for (int w = 0; w < kW; ++w) {
@@ -681,7 +698,7 @@ void decode_kernel(const DecodeParams p) {
       av = fmaf(wt, s_post[(w * kNH + jh) * kHeadDim + c], av);
       lv = fmaf(wt, s_l[w][jh], lv);
     }
-    if (new_ok) {  // the new token, weight exp2(logit - M), level w_hat
+    if (new_att) {  // the new token, weight exp2(logit - M), level w_hat
       const float wt = __builtin_amdgcn_exp2f(s_nlog[jh] - M);
       av = fmaf(wt, s_hat[1][c], av);
       lv += wt;
@@ -740,6 +757,102 @@ void decode_kernel(const DecodeParams p) {
   }
 #pragma unroll
   for (int k = 0; k < kIdx; ++k) load_acc(k, 0);
+
+  // Exact window (g <= 8), on the matrix cores (v_mfma_f32_16x16x32_bf16; the
+  // window rows are exact bf16).  Rows: n_ws sinks, then positions w_r0 .. T-1,
+  // staged in the upper part of the ring (row-major, 512 B per row: the key,
+  // whose 16-byte chunks are XOR-swizzled by row % 16, then the value), above
+  // the merge's max/sum pairs (at most 2 * kNH * (max splits with a window)
+  // floats); the R_V^T partials later reuse the rows' space.
+  //   logits  C[head][row] = <q_head, k_row> over 16-row tiles: A = q split
+  //           into three bf16 parts (truncation; about 21 bits), B = key rows;
+  //           <q_head, mu> is taken off in fp32.
+  //   values  O[head][ch] = sum_row p[head][row] v_row[ch] over 16-channel tiles
+  //           and 32-row blocks: A = p in two bf16 parts, B = values.
+  // Both splits are made once into LDS in operand order.  Rows past n_w read
+  // row n_w - 1 (finite) and carry weight 0.
+  constexpr bool kWinOk = kNQ <= 2;
+  constexpr int kWinMax = 8 + 128;                    // window rows
+  constexpr int kWinLd = kWinOk ? (kWinMax * 32 + kThreads - 1) / kThreads : 1;  // 16-byte chunks per thread
+  constexpr int kWinRowsPad = 32 * ((kWinMax + 31) / 32);  // 32-row blocks of the value product
+  constexpr int kHeadRow = kWinRowsPad + 8;           // floats per head: logits, then p hi | p lo (bf16)
+  constexpr int kQpStride = kHeadDim + 8;             // bf16 per (part, head) row of the q parts
+  constexpr int kWinSplits = kNQ == 1 ? kMaxSplits : 128;  // splits per sequence allowed with a window
+  constexpr int kRingFloats = static_cast<int>(sizeof(s_ring) / sizeof(float));
+  constexpr int kOwOff = kRingFloats - kNH * kHeadDim;  // [kNH][128] window value sums
+  constexpr int kWmlOff = kOwOff - 2 * kNH;             // [kNH][2] window max, sum of weights
+  constexpr int kRowsOff = kWmlOff - kWinMax * kHeadDim;  // [kWinMax][2][128] bf16 rows
+  constexpr int kWpOff = kRowsOff - kNH * kHeadRow;     // [kNH][kHeadRow]
+  constexpr int kQpOff = kWpOff - 3 * kNH * kQpStride / 2;  // [3][kNH][kQpStride] bf16 q parts
+  constexpr int kWmuOff = kQpOff - kHeadDim - kNH;      // [128] mu, then [kNH] <q, mu>
+  static_assert(!kWinOk || (kRowsOff % 4 == 0 && kWpOff % 4 == 0 && kQpOff % 4 == 0 && kWmuOff >= 0 &&
+                            kWmuOff >= 2 * kNH * kWinSplits && kWmlOff >= kParts * kNH * kHeadDim),
+                "window staging fits above the merge scratch");
+  const bool win_here = kWinOk && has_win;
+  int n_ws = 0, w_r0 = 0, n_w = 0;
+  uint4v wraw[kWinLd];
+  uint32_t qwr[kQPerThread];
+  float wmu = 0.0f;
+  if (win_here) {
+    n_ws = min(p.win_sinks, T);
+    w_r0 = max(n_ws, T - p.win_recent);
+    n_w = n_ws + (T - w_r0);
+    const int n_slots = p.win_sinks + p.win_recent;
+    const uint16_t* wb = p.win + (static_cast<size_t>(b) * H + h) * n_slots * 2 * kHeadDim;
+    const size_t nrow = (static_cast<size_t>(b) * H + h) * kHeadDim;
+    // The step's new token (position T - 1, always the last window row when the
+    // window holds it) is read from k_new / v_new: its slot is written by the
+    // appending workgroup during this launch.  fp32 input: the row's 8 floats
+    // arrive as two 16-byte words (at most one chunk of it per thread) and are
+    // rounded to bf16 once all loads have landed.
+    const bool new_here = new_in_win && T_raw == T;
+    uint4v f32_hi = {0u, 0u, 0u, 0u};
+    int u_f32 = -1;
+#pragma unroll
+    for (int u = 0; u < kWinLd; ++u) {
+      const int idx = tid + u * kThreads;  // row wi, chunk j: 8 bf16 of the key (j < 16) or value row
+      const int wi = idx >> 5, j = idx & 31;
+      wraw[u] = uint4v{0u, 0u, 0u, 0u};
+      if (wi < n_w) {
+        if (new_here && wi == n_w - 1) {
+          const uint8_t* src = static_cast<const uint8_t*>(j < 16 ? p.k_new : p.v_new) +
+                               (nrow + 8 * (j & 15)) * (p.kv_kind == 0 ? 2 : 4);
+          wraw[u] = *reinterpret_cast<const uint4v*>(src);
+          if (p.kv_kind != 0) {
+            f32_hi = *reinterpret_cast<const uint4v*>(src + 16);
+            u_f32 = u;
+          }
+        } else {
+          const int t = wi < n_ws ? wi : w_r0 + (wi - n_ws);
+          const int slot = t < p.win_sinks ? t : p.win_sinks + t % p.win_recent;
+          wraw[u] = *reinterpret_cast<const uint4v*>(wb + static_cast<size_t>(slot) * 2 * kHeadDim + 8 * j);
+        }
+      }
+    }
+    if (u_f32 >= 0) {
+#pragma unroll
+      for (int u = 0; u < kWinLd; ++u) {
+        if (u == u_f32) {
+          const uint4v lo = wraw[u];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            wraw[u][i] = f32_to_bf16_bits(__uint_as_float(lo[2 * i])) |
+                         (static_cast<uint32_t>(f32_to_bf16_bits(__uint_as_float(lo[2 * i + 1]))) << 16);
+            wraw[u][2 + i] = f32_to_bf16_bits(__uint_as_float(f32_hi[2 * i])) |
+                             (static_cast<uint32_t>(f32_to_bf16_bits(__uint_as_float(f32_hi[2 * i + 1]))) << 16);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kQPerThread; ++u) {
+      const int idx = min(tid + u * kThreads, kNH * kHeadDim - 1);
+      const size_t qi = (out_row0 + min(idx / kHeadDim, g - 1)) * kHeadDim + idx % kHeadDim;
+      qwr[u] = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(p.q) +
+                                                  (p.q_kind == 0 ? (2 * qi) & ~static_cast<size_t>(3) : 4 * qi));
+    }
+    if (tid < kHeadDim && p.win_mu != nullptr) wmu = p.win_mu[h * kHeadDim + tid];
+  }
   for (int q = tid; q < n_ml; q += kThreads) {
     if (q != tid) {  // beyond the first pair per thread
       ml0 = ld_agent(pb + static_cast<size_t>(q) * kPartStride + 128);
@@ -748,7 +861,134 @@ void decode_kernel(const DecodeParams p) {
     s_ml[2 * q] = ml0;
     s_ml[2 * q + 1] = ml1;
   }
+  uint4v* const s_rows = reinterpret_cast<uint4v*>(s_post + kRowsOff);  // 32 chunks per row
+  float* const s_wp = s_post + kWpOff;
+  uint16_t* const s_qp = reinterpret_cast<uint16_t*>(s_post + kQpOff);
+  if (win_here) {
+#pragma unroll
+    for (int u = 0; u < kWinLd; ++u) {
+      const int idx = tid + u * kThreads;
+      const int wi = idx >> 5, j = idx & 31;
+      if (wi < n_w) s_rows[32 * wi + (j < 16 ? (j ^ (wi & 15)) : j)] = wraw[u];
+    }
+#pragma unroll
+    for (int u = 0; u < kQPerThread; ++u) {  // the query rows as given, and their three bf16 parts
+      const int idx = tid + u * kThreads;
+      const size_t qi = (out_row0 + min(idx / kHeadDim, g - 1)) * kHeadDim + idx % kHeadDim;
+      const float qv = p.q_kind == 0 ? bf16_bits_to_f32(static_cast<uint16_t>(qwr[u] >> (16 * (qi & 1))))
+                                     : __uint_as_float(qwr[u]);
+      if (idx < kNH * kHeadDim) {
+        const int jh = idx / kHeadDim, c = idx % kHeadDim;
+        float r = jh < g ? qv : 0.0f;
+        s_q[jh][c] = r;
+#pragma unroll
+        for (int sp = 0; sp < 3; ++sp) {
+          const uint32_t t = __float_as_uint(r) & 0xffff0000u;
+          s_qp[(sp * kNH + jh) * kQpStride + c] = static_cast<uint16_t>(t >> 16);
+          r -= __uint_as_float(t);
+        }
+      }
+    }
+    if (tid < kHeadDim) s_post[kWmuOff + tid] = wmu;
+  }
   __syncthreads();
+  if (win_here) {
+    const int hq = lane & 15, kq = lane >> 4;
+    // <q_head, mu>, one wave per head
+    for (int jh = wave; jh < g; jh += kW) {
+      float d = fmaf(s_q[jh][lane], s_post[kWmuOff + lane], s_q[jh][lane + 64] * s_post[kWmuOff + lane + 64]);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+      if (lane == 0) s_post[kWmuOff + kHeadDim + jh] = d;
+    }
+    // logits <q, k>, 16-row tiles: C lane (a, col) = heads 4a + i, window row 16 tile + col
+    for (int tile = wave; 16 * tile < n_w; tile += kW) {
+      const int wi = min(16 * tile + hq, n_w - 1);  // B column = window row
+      float4v C = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const bf16x8 kB = __builtin_bit_cast(bf16x8, s_rows[32 * wi + ((4 * kb + kq) ^ (wi & 15))]);
+#pragma unroll
+        for (int sp = 0; sp < 3; ++sp) {
+          const uint4v qa = hq < kNH ? *reinterpret_cast<const uint4v*>(s_qp + (sp * kNH + hq) * kQpStride + 32 * kb +
+                                                                        8 * kq)
+                                     : uint4v{0u, 0u, 0u, 0u};
+          C = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, qa), kB, C, 0, 0, 0);
+        }
+      }
+      const int col = 16 * tile + hq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int jh = 4 * kq + i;
+        if (jh < g && col < n_w) s_wp[jh * kHeadRow + col] = C[i];
+      }
+    }
+    __syncthreads();
+    // per head (one wave): logits (log2 units) = (<q, k> - <q, mu>) * scale, max, weights
+    // exp2(logit - max) split into bf16 hi | lo over the same row (all reads first), their sum
+    const int n_wpad = 32 * ((n_w + 31) / 32);
+    for (int jh = wave; jh < g; jh += kW) {
+      const float qmu = s_post[kWmuOff + kHeadDim + jh];
+      float lg[(kWinRowsPad + 63) / 64];
+      float m = kNegBig;
+#pragma unroll
+      for (int r = 0; r < (kWinRowsPad + 63) / 64; ++r) {
+        const int wi = lane + 64 * r;
+        lg[r] = wi < n_w ? (s_wp[jh * kHeadRow + wi] - qmu) * p.logit_scale : kNegBig;
+        m = fmaxf(m, lg[r]);
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      float l = 0.0f;
+      uint16_t* prow = reinterpret_cast<uint16_t*>(s_wp + jh * kHeadRow);
+#pragma unroll
+      for (int r = 0; r < (kWinRowsPad + 63) / 64; ++r) {
+        const int wi = lane + 64 * r;
+        const float e = wi < n_w ? __builtin_amdgcn_exp2f(lg[r] - m) : 0.0f;
+        l += e;
+        if (wi < n_wpad) {
+          const uint32_t t = __float_as_uint(e) & 0xffff0000u;
+          prow[wi] = static_cast<uint16_t>(t >> 16);
+          prow[kWinRowsPad + 8 + wi] = static_cast<uint16_t>((__float_as_uint(e - __uint_as_float(t))) >> 16);
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+      if (lane == 0) {
+        s_post[kWmlOff + 2 * jh] = m;
+        s_post[kWmlOff + 2 * jh + 1] = l;
+      }
+    }
+    __syncthreads();
+    // value sums: wave w < 8 takes channels 16 w .. +16; A = weights (hi, lo), B = values
+    if (wave < kHeadDim / 16) {
+      const uint16_t* vrows = reinterpret_cast<const uint16_t*>(s_rows) + kHeadDim + 16 * wave + hq;
+      const uint16_t* prow = reinterpret_cast<const uint16_t*>(s_wp + (hq < kNH ? hq : 0) * kHeadRow);
+      float4v C = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int kb = 0; kb < n_wpad / 32; ++kb) {
+        uint4v vv;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const int w0 = min(32 * kb + 8 * kq + 2 * e2, n_w - 1), w1 = min(32 * kb + 8 * kq + 2 * e2 + 1, n_w - 1);
+          vv[e2] = static_cast<uint32_t>(vrows[w0 * 2 * kHeadDim]) |
+                   (static_cast<uint32_t>(vrows[w1 * 2 * kHeadDim]) << 16);
+        }
+        const bool live = hq < g;
+        const uint4v ph = live ? *reinterpret_cast<const uint4v*>(prow + 32 * kb + 8 * kq) : uint4v{0u, 0u, 0u, 0u};
+        const uint4v pl = live ? *reinterpret_cast<const uint4v*>(prow + kWinRowsPad + 8 + 32 * kb + 8 * kq)
+                               : uint4v{0u, 0u, 0u, 0u};
+        const bf16x8 vB = __builtin_bit_cast(bf16x8, vv);
+        C = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ph), vB, C, 0, 0, 0);
+        C = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, pl), vB, C, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int jh = 4 * kq + i;
+        if (jh < g) s_post[kOwOff + jh * kHeadDim + 16 * wave + hq] = C[i];
+      }
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int k = 0; k < kIdx; ++k) {
     const int idx = tid + k * kThreads;
@@ -757,8 +997,12 @@ void decode_kernel(const DecodeParams p) {
     const int c = idx % kHeadDim;
     float M = kNegBig, l = 0.0f;
     for (int sp = 0; sp < n_valid; ++sp) M = fmaxf(M, s_ml[2 * (sp * g + jh)]);
+    const float wm = win_here ? s_post[kWmlOff + 2 * jh] : kNegBig;
+    M = fmaxf(M, wm);
     for (int sp = 0; sp < n_valid; ++sp)
       l = fmaf(__builtin_amdgcn_exp2f(s_ml[2 * (sp * g + jh)] - M), s_ml[2 * (sp * g + jh) + 1], l);
+    const float ww = __builtin_amdgcn_exp2f(wm - M);  // weight of the window's part
+    if (win_here) l = fmaf(ww, s_post[kWmlOff + 2 * jh + 1], l);
     float o = 0.0f;
     for (int s0 = 0; s0 < n_valid; s0 += kAB) {
       if (s0 > 0) load_acc(k, s0);
@@ -770,6 +1014,8 @@ void decode_kernel(const DecodeParams p) {
       }
     }
     s_q[jh][c] = l > 0.0f ? o / l : 0.0f;  // o_rot
+    if (win_here)  // the window's value sum (original basis), added after R_V^T
+      s_post[kOwOff + jh * kHeadDim + c] = l > 0.0f ? ww * s_post[kOwOff + jh * kHeadDim + c] / l : 0.0f;
   }
   __syncthreads();
 
@@ -794,6 +1040,7 @@ void decode_kernel(const DecodeParams p) {
     float o = 0.0f;
 #pragma unroll
     for (int u = 0; u < kParts; ++u) o += s_post[(u * kNH + jh) * kHeadDim + i];
+    if (win_here) o += s_post[kOwOff + jh * kHeadDim + i];
     const size_t oidx = (out_row0 + jh) * kHeadDim + i;
     if (p.out_kind == 0)
       static_cast<uint16_t*>(p.out)[oidx] = f32_to_bf16_bits(o);

@@ -16,6 +16,11 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
 // length (pages per split = clamp(ceil(H * total pages / target_wgs), pps_min,
 // pps_max)), so that short sequences take fewer workgroups; n_splits is then
 // the number of split slots per KV head, an upper bound on the batch's total.
+// Exact window fill: bf16 buf [batch][num_kv_heads][sinks + recent][2][128].
+hipError_t launch_window_fill(uint16_t* buf, int batch, int num_kv_heads, int sinks, int recent, const void* k,
+                              const void* v, int in_kind, int n_tokens, const int32_t* seq_ids,
+                              const int32_t* positions, const int32_t* seq_lens, hipStream_t stream);
+
 struct DecodePlan {
   int n_pages_max;      // ceil(max_seq_len / 16)
   bool balanced;
@@ -52,6 +57,13 @@ struct DecodeParams {
   int pages_per_split;
   int n_splits;
   int pps_min, pps_max, target_wgs;
+  // Exact window (win null = none): bf16 [batch'][num_kv_heads][win_sinks +
+  // win_recent][2][128]; positions t < win_sinks and t >= T - win_recent are
+  // attended from it (logit <q, k - win_mu>), the rest from the pool.  The
+  // step form also stores the new token into its slot.
+  uint16_t* win;
+  int win_sinks, win_recent;
+  const float* win_mu;
   // Step form: when k_new is non-null, the token at position seq_lens[b] - 1 of
   // every sequence is first quantize-appended from k_new/v_new [batch][H_kv][128]
   // (kv_kind 0 bf16, 1 fp32; mu [H_kv][128] or null) by the workgroup whose

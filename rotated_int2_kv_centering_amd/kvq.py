@@ -43,6 +43,11 @@ class kvq_cache(ctypes.Structure):
                 ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("pool", ctypes.c_void_p)]
 
 
+class kvq_window(ctypes.Structure):
+    _fields_ = [("sinks", ctypes.c_int32), ("recent", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("buf", ctypes.c_void_p), ("mu", ctypes.c_void_p)]
+
+
 _lib = None
 
 
@@ -56,19 +61,25 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     P, I32, U64, SZ, F = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t, ctypes.c_float
     CP = ctypes.POINTER(kvq_cache)
+    WP = ctypes.POINTER(kvq_window)
     lib.kvq_pool_bytes.argtypes = [CP]
     lib.kvq_pool_bytes.restype = SZ
     lib.kvq_quant_append.argtypes = [CP, P, P, I32, I32, P, P, P, P, P, P]
     lib.kvq_quant_append.restype = I32
     lib.kvq_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.kvq_decode_workspace_bytes.restype = SZ
-    lib.kvq_decode_attn.argtypes = [CP, P, I32, I32, I32, P, I32, P, I32, P, P, F, P, I32, P, SZ, I32, P]
+    lib.kvq_decode_attn.argtypes = [CP, P, I32, I32, I32, P, I32, P, I32, P, P, F, P, I32, P, SZ, I32, WP, P]
     lib.kvq_decode_attn.restype = I32
-    lib.kvq_decode_attn_traced.argtypes = [CP, P, I32, I32, I32, P, I32, P, I32, P, P, F, P, I32, P, SZ, I32, P, P, P]
+    lib.kvq_decode_attn_traced.argtypes = [CP, P, I32, I32, I32, P, I32, P, I32, P, P, F, P, I32, P, SZ, I32, WP, P,
+                                           P, P]
     lib.kvq_decode_attn_traced.restype = I32
     lib.kvq_decode_step.argtypes = [CP, P, P, I32, P, P, I32, I32, I32, P, I32, P, I32, P, P, F, P, I32, P, SZ, I32,
-                                    P, P, P]
+                                    WP, P, P, P]
     lib.kvq_decode_step.restype = I32
+    lib.kvq_window_bytes.argtypes = [WP, I32]
+    lib.kvq_window_bytes.restype = SZ
+    lib.kvq_window_fill.argtypes = [WP, I32, P, P, I32, I32, P, P, P, P]
+    lib.kvq_window_fill.restype = I32
     lib.kvq_page_table.argtypes = [I32, U64, P, I32, I32, I32, I32, P, P]
     lib.kvq_page_table.restype = I32
     lib.kvq_last_error.argtypes = []
@@ -118,6 +129,14 @@ def make_cache(num_kv_heads: int, num_pages: int, pool=None, head_dim: int = HEA
     return kvq_cache(num_kv_heads, head_dim, group_size, page_size, num_pages, _ptr(pool))
 
 
+def make_window(sinks: int, recent: int, batch: int, buf=None, mu=None) -> kvq_window:
+    return kvq_window(sinks, recent, batch, _ptr(buf), _ptr(mu))
+
+
+def _win(window):
+    return ctypes.byref(window) if window is not None else None
+
+
 # --------------------------------------------------------------- the calls
 def kvq_pool_bytes(cache: kvq_cache) -> int:
     return int(load().kvq_pool_bytes(ctypes.byref(cache)))
@@ -136,33 +155,43 @@ def kvq_decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, 
 
 def kvq_decode_attn(cache: kvq_cache, q, q_dtype: int, batch: int, num_q_heads: int, page_table, max_pages: int,
                     seq_lens, max_seq_len: int, r_k, r_v, sm_scale: float, out, out_dtype: int, workspace,
-                    workspace_bytes: int, num_splits: int = 0, stream=None) -> None:
+                    workspace_bytes: int, num_splits: int = 0, window=None, stream=None) -> None:
     _check(load().kvq_decode_attn(ctypes.byref(cache), _ptr(q), q_dtype, batch, num_q_heads, _ptr(page_table),
                                   max_pages, _ptr(seq_lens), max_seq_len, _ptr(r_k), _ptr(r_v), float(sm_scale),
                                   _ptr(out), out_dtype, _ptr(workspace), int(workspace_bytes), num_splits,
-                                  _stream(stream)))
+                                  _win(window), _stream(stream)))
 
 
 def kvq_decode_attn_traced(cache: kvq_cache, q, q_dtype: int, batch: int, num_q_heads: int, page_table,
                            max_pages: int, seq_lens, max_seq_len: int, r_k, r_v, sm_scale: float, out, out_dtype: int,
-                           workspace, workspace_bytes: int, num_splits: int = 0, stream=None, ev_begin=None,
-                           ev_end=None) -> None:
+                           workspace, workspace_bytes: int, num_splits: int = 0, window=None, stream=None,
+                           ev_begin=None, ev_end=None) -> None:
     """``ev_begin``/``ev_end`` are raw hipEvent_t addresses (or None)."""
     _check(load().kvq_decode_attn_traced(ctypes.byref(cache), _ptr(q), q_dtype, batch, num_q_heads, _ptr(page_table),
                                          max_pages, _ptr(seq_lens), max_seq_len, _ptr(r_k), _ptr(r_v),
                                          float(sm_scale), _ptr(out), out_dtype, _ptr(workspace), int(workspace_bytes),
-                                         num_splits, _stream(stream), ev_begin, ev_end))
+                                         num_splits, _win(window), _stream(stream), ev_begin, ev_end))
 
 
 def kvq_decode_step(cache: kvq_cache, k_new, v_new, kv_dtype: int, mu, q, q_dtype: int, batch: int,
                     num_q_heads: int, page_table, max_pages: int, seq_lens, max_seq_len: int, r_k, r_v,
                     sm_scale: float, out, out_dtype: int, workspace, workspace_bytes: int, num_splits: int = 0,
-                    stream=None, ev_begin=None, ev_end=None) -> None:
+                    window=None, stream=None, ev_begin=None, ev_end=None) -> None:
     """Append the newest token of every sequence (position seq_lens[b] - 1), then decode."""
     _check(load().kvq_decode_step(ctypes.byref(cache), _ptr(k_new), _ptr(v_new), kv_dtype, _ptr(mu), _ptr(q), q_dtype,
                                   batch, num_q_heads, _ptr(page_table), max_pages, _ptr(seq_lens), max_seq_len,
                                   _ptr(r_k), _ptr(r_v), float(sm_scale), _ptr(out), out_dtype, _ptr(workspace),
-                                  int(workspace_bytes), num_splits, _stream(stream), ev_begin, ev_end))
+                                  int(workspace_bytes), num_splits, _win(window), _stream(stream), ev_begin, ev_end))
+
+
+def kvq_window_bytes(window, num_kv_heads: int) -> int:
+    return int(load().kvq_window_bytes(_win(window), num_kv_heads))
+
+
+def kvq_window_fill(window, num_kv_heads: int, k, v, in_dtype: int, n_tokens: int, seq_ids, positions, seq_lens,
+                    stream=None) -> None:
+    _check(load().kvq_window_fill(_win(window), num_kv_heads, _ptr(k), _ptr(v), in_dtype, n_tokens, _ptr(seq_ids),
+                                  _ptr(positions), _ptr(seq_lens), _stream(stream)))
 
 
 def kvq_page_table(policy: int, seed: int, seq_lens, page_size: int, num_pages: int, max_pages: int, table=None):

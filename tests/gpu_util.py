@@ -74,7 +74,26 @@ class DeviceCase:
         torch.cuda.synchronize()
         return rot
 
-    def decode(self, out_dtype="f32", num_splits=0, q=None, table=None, ws=None, max_seq=None):
+    def window(self, sinks, recent, fill=True, tokens=None, mu="case"):
+        """A zeroed exact-window buffer for the case (kept alive on self), filled by
+        kvq_window_fill with every token (or the token indices ``tokens``)."""
+        from rotated_int2_kv_centering_amd import kvq
+        c = self.c
+        probe = kvq.make_window(sinks, recent, c.B)
+        nbytes = kvq.kvq_window_bytes(probe, c.Hkv)
+        self.win_buf = torch.zeros(max(nbytes, 16), dtype=torch.uint8, device=self.dev)
+        self.win = kvq.make_window(sinks, recent, c.B, self.win_buf, self.mu if mu == "case" else mu)
+        if fill:
+            sel = np.arange(c.n_tokens) if tokens is None else np.asarray(tokens, np.int64)
+            if len(sel):
+                idx = dev_tensor(sel, self.dev)
+                kvq.kvq_window_fill(self.win, c.Hkv, self.k[idx].contiguous(), self.v[idx].contiguous(), self.in_dtype,
+                                    len(sel), dev_tensor(c.tok_seq[sel].astype(np.int32), self.dev),
+                                    dev_tensor(c.tok_pos[sel].astype(np.int32), self.dev), self.seq_lens)
+            torch.cuda.synchronize()
+        return self.win
+
+    def decode(self, out_dtype="f32", num_splits=0, q=None, table=None, ws=None, max_seq=None, window=None):
         from rotated_int2_kv_centering_amd import kvq
         c = self.c
         max_seq = int(c.seq_lens.max(initial=0)) if max_seq is None else int(max_seq)
@@ -89,13 +108,14 @@ class DeviceCase:
         table = self.table if table is None else table
         kvq.kvq_decode_attn(self.cache, self.q if q is None else q, self.in_dtype, c.B, c.Hq, table,
                             int(table.shape[1]), self.seq_lens, max_seq, self.r_k, self.r_v, 0.0, out,
-                            kvq.KVQ_F32 if out_dtype == "f32" else kvq.KVQ_BF16, ws, ws_bytes, num_splits)
+                            kvq.KVQ_F32 if out_dtype == "f32" else kvq.KVQ_BF16, ws, ws_bytes, num_splits,
+                            window=window)
         torch.cuda.synchronize()
         if out_dtype == "f32":
             return out.cpu().numpy()
         return out.view(torch.int16).cpu().numpy().view(np.uint16)
 
-    def step(self, k_new, v_new, out_dtype="f32", num_splits=0, ws=None, mu="case"):
+    def step(self, k_new, v_new, out_dtype="f32", num_splits=0, ws=None, mu="case", window=None):
         """kvq_decode_step with the case's queries, tables and lengths; k_new/v_new are
         device tensors [B][H_kv][128] in the case's dtype."""
         from rotated_int2_kv_centering_amd import kvq
@@ -111,7 +131,7 @@ class DeviceCase:
         kvq.kvq_decode_step(self.cache, k_new, v_new, self.in_dtype, self.mu if mu == "case" else mu, self.q,
                             self.in_dtype, c.B, c.Hq, self.table, int(self.table.shape[1]), self.seq_lens, max_seq,
                             self.r_k, self.r_v, 0.0, out, kvq.KVQ_F32 if out_dtype == "f32" else kvq.KVQ_BF16, ws,
-                            ws_bytes, num_splits)
+                            ws_bytes, num_splits, window=window)
         torch.cuda.synchronize()
         if out_dtype == "f32":
             return out.cpu().numpy()

@@ -37,7 +37,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["kvq_pool_bytes", "kvq_quant_append", "kvq_decode_workspace_bytes", "kvq_decode_attn",
-                            "kvq_decode_attn_traced", "kvq_decode_step", "kvq_page_table", "kvq_last_error"]), names
+                            "kvq_decode_attn_traced", "kvq_decode_step", "kvq_window_bytes", "kvq_window_fill",
+                            "kvq_page_table", "kvq_last_error"]), names
 
 
 def test_library_exports_exactly_the_declared_symbols(K):
@@ -166,13 +167,13 @@ def test_append_argument_validation(K):
 
 
 def _decode(K, cache, batch=1, hq=4, max_pages=4, max_seq=64, sm_scale=0.0, q_dtype=None, out_dtype=None,
-            ws_bytes=1 << 20, num_splits=1, q=FAKE):
+            ws_bytes=1 << 20, num_splits=1, q=FAKE, window=None):
     lib = K.load()
     q_dtype = K.KVQ_BF16 if q_dtype is None else q_dtype
     out_dtype = K.KVQ_F32 if out_dtype is None else out_dtype
     return lib.kvq_decode_attn(ctypes.byref(cache) if cache is not None else None, q, q_dtype, batch, hq, FAKE,
                                max_pages, FAKE, max_seq, FAKE, FAKE, sm_scale, FAKE, out_dtype, FAKE, ws_bytes,
-                               num_splits, None)
+                               num_splits, ctypes.byref(window) if window is not None else None, None)
 
 
 def test_decode_argument_validation(K):
@@ -234,3 +235,34 @@ def test_probe_library_exports_its_declared_symbol():
     assert f(ctypes.c_void_p(264), 16, ctypes.c_void_p(256), 1, None) == 1  # misaligned
     assert f(ctypes.c_void_p(256), 16, ctypes.c_void_p(256), 0, None) == 1  # no workgroups
     assert f(ctypes.c_void_p(256), 0, ctypes.c_void_p(256), 1, None) == 0   # nothing to read: no launch
+
+
+def test_window_bytes_and_host_validation(K):
+    """The exact window: buffer size, and every bad window rejected on the host."""
+    W = K.make_window
+    assert K.kvq_window_bytes(W(4, 128, 2, FAKE), 8) == 2 * 8 * 132 * 512
+    assert K.kvq_window_bytes(W(0, 0, 2, FAKE), 8) == 0
+    assert K.kvq_window_bytes(W(9, 0, 1, FAKE), 1) == 0
+    assert K.kvq_window_bytes(W(0, 129, 1, FAKE), 1) == 0
+    assert K.kvq_window_bytes(W(1, 1, -1, FAKE), 1) == 0
+    assert K.kvq_window_bytes(None, 1) == 0
+    c = K.make_cache(1, 8, FAKE)
+    assert _decode(K, c, window=W(9, 4, 1, FAKE)) == K.KVQ_EINVAL          # too many sinks
+    assert _decode(K, c, window=W(4, 129, 1, FAKE)) == K.KVQ_EINVAL        # too many recent positions
+    assert _decode(K, c, window=W(4, 4, 1, None)) == K.KVQ_EINVAL          # no buffer
+    assert _decode(K, c, window=W(4, 4, 1, FAKE + 8)) == K.KVQ_EINVAL      # misaligned buffer
+    assert _decode(K, c, batch=2, window=W(4, 4, 1, FAKE)) == K.KVQ_EINVAL  # holds one sequence
+    assert _decode(K, c, hq=16, window=W(4, 4, 1, FAKE)) == K.KVQ_EUNSUPPORTED  # g = 16
+    lib = K.load()
+    w = W(4, 4, 2, FAKE)
+    fill = lib.kvq_window_fill
+    assert fill(None, 1, FAKE, FAKE, K.KVQ_BF16, 1, FAKE, FAKE, FAKE, None) == K.KVQ_EINVAL
+    assert fill(ctypes.byref(w), 0, FAKE, FAKE, K.KVQ_BF16, 1, FAKE, FAKE, FAKE, None) == K.KVQ_EINVAL
+    assert fill(ctypes.byref(w), 1, FAKE, FAKE, K.KVQ_BF16, -1, FAKE, FAKE, FAKE, None) == K.KVQ_EINVAL
+    assert fill(ctypes.byref(w), 1, FAKE, FAKE, K.KVQ_F32_ROTATED, 1, FAKE, FAKE, FAKE, None) == K.KVQ_EUNSUPPORTED
+    assert fill(ctypes.byref(w), 1, None, FAKE, K.KVQ_BF16, 1, FAKE, FAKE, FAKE, None) == K.KVQ_EINVAL
+    assert fill(ctypes.byref(w), 1, FAKE, FAKE, K.KVQ_BF16, 0, FAKE, FAKE, FAKE, None) == K.KVQ_OK  # no tokens
+    empty = W(0, 0, 2, None)
+    assert fill(ctypes.byref(empty), 1, FAKE, FAKE, K.KVQ_BF16, 5, FAKE, FAKE, FAKE, None) == K.KVQ_OK  # no window
+    bad = W(4, 4, 2, FAKE + 4)
+    assert fill(ctypes.byref(bad), 1, FAKE, FAKE, K.KVQ_BF16, 5, FAKE, FAKE, FAKE, None) == K.KVQ_EINVAL

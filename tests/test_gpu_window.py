@@ -1,0 +1,183 @@
+"""GPU parity of the exact (BF16) window through the C ABI.
+
+The window keeps the first `sinks` and the last `recent` positions of each
+sequence exact (OptR section 3.1: the INT2 history plus a small BF16 window).
+* kvq_window_fill writes exactly the window positions' bf16 rows into their
+  slots (bit for bit; fp32 input rounded to nearest even) and nothing else;
+* decode with a window is within 2e-3 max-abs-rel of the oracle's
+  decode_attention_window on the GPU's own pool and the exact bf16 k, v;
+* the step form stores the new token into its window slot, attends it exactly,
+  and still quantizes it into the cache byte for byte as kvq_quant_append.
+"""
+
+import numpy as np
+import pytest
+
+import kvq_inputs as I
+from oracle import kvq_oracle as O
+from tests.gpu_util import DeviceCase, bf16_tensor, dev_tensor, max_abs_rel, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+def _exact_bits(case, a_bits_or_f32):
+    return a_bits_or_f32 if case.dtype == "bf16" else I.bf16_bits(a_bits_or_f32)
+
+
+def _seqs(case, a):
+    out = []
+    for b in range(case.B):
+        sel = np.nonzero(case.tok_seq == b)[0]
+        out.append(np.asarray(a)[sel[np.argsort(case.tok_pos[sel])]])
+    return out
+
+
+def _exact_kv(case):
+    """Per-sequence exact (bf16-valued) keys and values, as the window holds them."""
+    kb = case.k_bits if case.dtype == "bf16" else I.bf16_bits(case.k)
+    vb = case.v_bits if case.dtype == "bf16" else I.bf16_bits(case.v)
+    return _seqs(case, I.bf16_to_f32(kb)), _seqs(case, I.bf16_to_f32(vb))
+
+
+def _oracle(case, pool, sinks, recent, heads=None):
+    ks, vs = _exact_kv(case)
+    return O.decode_attention_window(case.q, pool, case.Hkv, case.page_table, case.seq_lens, case.mu, case.r_k,
+                                     case.r_v, ks, vs, sinks, recent, heads=heads)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_window_fill_layout(dtype):
+    dev = require_gpu()
+    sinks, recent = 4, 16
+    case = I.make_case("wf", 61, B=3, Hq=8, Hkv=2, seq_lens=[50, 3, 20], dtype=dtype, table_policy="permuted")
+    dc = DeviceCase(case, dev)
+    dc.window(sinks, recent, fill=False)
+    dc.win_buf.fill_(0xAB)  # sentinel: slots nobody writes keep it
+    from rotated_int2_kv_centering_amd import kvq
+    kvq.kvq_window_fill(dc.win, case.Hkv, dc.k, dc.v, dc.in_dtype, case.n_tokens,
+                        dev_tensor(case.tok_seq.astype(np.int32), dev), dev_tensor(case.tok_pos.astype(np.int32), dev),
+                        dc.seq_lens)
+    import torch
+    torch.cuda.synchronize()
+    got = dc.win_buf.cpu().numpy().view(np.uint16).reshape(case.B, case.Hkv, sinks + recent, 2, 128)
+    expect = np.full_like(got, 0xABAB)
+    kb, vb = _exact_bits(case, case.k_bits if dtype == "bf16" else case.k), \
+        _exact_bits(case, case.v_bits if dtype == "bf16" else case.v)
+    for n in range(case.n_tokens):
+        b, t = int(case.tok_seq[n]), int(case.tok_pos[n])
+        if O.window_mask(case.seq_lens[b], sinks, recent)[t]:
+            slot = O.window_slot(t, sinks, recent)
+            expect[b, :, slot, 0] = kb[n]
+            expect[b, :, slot, 1] = vb[n]
+    np.testing.assert_array_equal(got, expect)
+
+
+WSHAPES = [
+    # (B, Hq, Hkv, seq_lens, sinks, recent)
+    (1, 4, 1, [1], 4, 128),          # one token, exact
+    (1, 4, 1, [100], 4, 128),        # window covers everything
+    (1, 4, 1, [300], 4, 128),        # window inside
+    (1, 4, 1, [300], 0, 16),         # recent only
+    (1, 4, 1, [300], 8, 0),          # sinks only
+    (2, 8, 2, [7, 140], 4, 3),       # a short sequence below the sink count
+    (3, 32, 8, [1000, 16, 257], 4, 128),
+    (2, 64, 8, [513, 1024], 4, 128),  # g = 8
+    (2, 2, 2, [77, 300], 2, 32),      # g = 1
+]
+
+
+@pytest.mark.parametrize("shape", WSHAPES,
+                         ids=lambda s: f"B{s[0]}_Hq{s[1]}_Hkv{s[2]}_T{'-'.join(map(str, s[3]))}_w{s[4]}+{s[5]}")
+def test_decode_window_parity(shape):
+    dev = require_gpu()
+    B, Hq, Hkv, lens, sinks, recent = shape
+    case = I.make_case("wd", 200 + sum(lens) + Hq, B=B, Hq=Hq, Hkv=Hkv, seq_lens=lens, table_policy="interleaved")
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False)
+    win = dc.window(sinks, recent)
+    ref = _oracle(case, dc.pool_np(), sinks, recent)
+    for ns in (0, 3):
+        got = dc.decode("f32", num_splits=ns, window=win)
+        assert np.isfinite(got).all()
+        assert max_abs_rel(got, ref) <= TOL, ns
+    # the bf16 output is the fp32 output rounded to nearest even
+    got16 = dc.decode("bf16", window=win)
+    np.testing.assert_array_equal(got16, I.bf16_bits(dc.decode("f32", window=win)))
+
+
+def test_window_changes_the_result_and_empty_window_is_none():
+    dev = require_gpu()
+    case = I.make_case("we", 71, B=1, Hq=32, Hkv=8, seq_lens=[2000])
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False)
+    plain = dc.decode("f32")
+    np.testing.assert_array_equal(dc.decode("f32", window=dc.window(0, 0)), plain)
+    with_win = dc.decode("f32", window=dc.window(4, 128))
+    assert np.abs(with_win - plain).max() > 1e-4  # exact keys differ from their INT2 levels
+
+
+def test_window_positions_on_an_absent_page_are_attended():
+    dev = require_gpu()
+    case = I.make_case("wa", 72, B=1, Hq=4, Hkv=1, seq_lens=[64], table_policy="contiguous")
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False)
+    table = case.page_table.copy()
+    table[0, 0] = -1  # positions 0..15 absent from the INT2 cache; the 4 sinks stay
+    win = dc.window(4, 10)
+    got = dc.decode("f32", table=dev_tensor(table.astype(np.int32), dev), window=win)
+    ks, vs = _exact_kv(case)
+    ref = O.decode_attention_window(case.q, dc.pool_np(), 1, table, case.seq_lens, case.mu, case.r_k, case.r_v, ks, vs,
+                                    4, 10, num_pages=case.num_pages)
+    assert max_abs_rel(got, ref) <= TOL
+
+
+def test_full_size_window_sampled_heads():
+    """The 8B shape at 128K with the 4 + 128 window, bulk-appended and window-filled."""
+    dev = require_gpu()
+    case = I.llama8b_case(131072)
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False, chunk=1 << 20)
+    T = int(case.seq_lens[0])
+    keep = np.nonzero(O.window_mask(T, 4, 128)[case.tok_pos])[0]
+    win = dc.window(4, 128, tokens=keep)
+    got = dc.decode("f32", window=win)
+    heads = [(0, 0), (0, 13), (0, 31)]
+    ref = _oracle(case, dc.pool_np(), 4, 128, heads=heads)
+    for b, j in heads:
+        assert max_abs_rel(got[b, j], ref[b, j]) <= TOL, j
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("sinks,recent", [(4, 16), (4, 0), (0, 1)])
+def test_step_with_window(dtype, sinks, recent):
+    """kvq_decode_step with a window: the cache bytes equal kvq_quant_append of the
+    new tokens, the new token's window slot holds its bf16 rows, and the output
+    matches the oracle with every window position exact."""
+    from rotated_int2_kv_centering_amd import kvq
+    import torch
+    dev = require_gpu()
+    case = I.make_case("ws", 80 + sinks + recent, B=3, Hq=8, Hkv=2, seq_lens=[40, 3, 17], dtype=dtype,
+                       table_policy="interleaved")
+    newest = np.array([np.nonzero(case.tok_seq == b)[0][-1] for b in range(case.B)])
+    old = np.setdiff1d(np.arange(case.n_tokens), newest)
+    # reference pool: every token appended by kvq_quant_append
+    ref_dc = DeviceCase(case, dev)
+    ref_dc.append(rot_out=False)
+    # step pool: all but the newest appended, window filled with all but the newest
+    dc = DeviceCase(case, dev)
+    sel = dev_tensor(old, dev)
+    kvq.kvq_quant_append(dc.cache, dc.k[sel].contiguous(), dc.v[sel].contiguous(), dc.in_dtype, len(old),
+                         dc.slots[sel].contiguous(), dc.mu, dc.r_k, dc.r_v)
+    win = dc.window(sinks, recent, tokens=old)
+    k_new, v_new = dc.k[dev_tensor(newest, dev)].contiguous(), dc.v[dev_tensor(newest, dev)].contiguous()
+    got = dc.step(k_new, v_new, window=win)
+    np.testing.assert_array_equal(dc.pool_np(), ref_dc.pool_np())
+    # the window now holds every window position, the new tokens included
+    full = DeviceCase(case, dev)
+    full.window(sinks, recent)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dc.win_buf.cpu().numpy(), full.win_buf.cpu().numpy())
+    ref = _oracle(case, dc.pool_np(), sinks, recent)
+    assert max_abs_rel(got, ref) <= TOL
