@@ -119,7 +119,10 @@ bool make_plan(int batch, int num_kv_heads, int g, int max_seq_len, int num_spli
     plan->pps_min = static_cast<int>(pps_min);
     plan->pps_max = static_cast<int>(pps_max);
     plan->target_wgs = static_cast<int>(target);
-    plan->pages_per_split = 0;
+    // the kernel's pps for one sequence of length max_seq_len: its guess of the
+    // split size under a batch of one, so page ids load before the length does
+    const long long want = (static_cast<long long>(num_kv_heads) * n_pages + target - 1) / target;
+    plan->pages_per_split = static_cast<int>(std::min(std::max(want, pps_min), pps_max));
     plan->n_splits = static_cast<int>(std::max<long long>(slots, 1));
     return true;
   }

@@ -12,10 +12,12 @@
 // contiguous range of the sequence's pages.  The workgroups of one KV head are
 // consecutive in the flattened grid with h fastest, so on an 8-XCD part the
 // workgroups of one KV head share an XCD's L2.
-//   prologue   load the split's page ids, the g query rows and R_K together;
-//              start streaming the first page pairs; compute
+//   prologue   load the split's page ids, the g query rows and R_K together
+//              (with the sequence length, from a guess of the split where one
+//              exists); start streaming the first page pair; compute
 //              q_hat = q R_K * sm_scale * log2(e) (fp32) and a per-head power
-//              of two f that brings max|q_hat*f| into [2^13, 2^14).
+//              of two f that brings max|q_hat*f| into [2^13, 2^14); request
+//              the next pairs.
 //   main loop  wave w takes page pairs w, w+kW, ...: each pair is copied by
 //              direct global->LDS loads into a ring of kDepth slots per wave
 //              (kDepth - 1 pairs in flight while one is computed); logits and
@@ -136,6 +138,7 @@ __device__ __forceinline__ int seq_pages(const DecodeParams& p, int b) {
 // pps sized from the batch's total pages; a slot past the last split gets b = -1.
 struct SplitLoc {
   int b, split, pps, first;  // first = slot of split 0 of sequence b
+  int len;                   // batch 1: seq_lens[0] as read (else unset)
 };
 template <int kW>
 __device__ SplitLoc locate_split(const DecodeParams& p, int w, int tid, int lane, int wave, int* s_red, int* s_loc) {
@@ -146,7 +149,9 @@ __device__ SplitLoc locate_split(const DecodeParams& p, int w, int tid, int lane
   };
   SplitLoc r;
   if (p.batch == 1) {  // no scan needed
-    const int pages = seq_pages(p, 0);
+    r.len = p.seq_lens[0];
+    const int T0 = min(r.len, p.len_cap);
+    const int pages = T0 > 0 ? (T0 + kPage - 1) / kPage : 0;
     r.pps = pps_for(pages);
     const int n = max(1, (pages + r.pps - 1) / r.pps);
     r.b = w < n ? 0 : -1;
@@ -247,9 +252,71 @@ void decode_kernel(const DecodeParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: ring addresses stay scalar
   auto ring = [&](int slot) -> uint4v(*)[64] { return s_ring[slot][wave]; };
 
+  // Loads that depend only on the (sequence, first page) are issued before the
+  // length is known, from a guess: exact under a fixed plan, the host's split
+  // size for a batch of one (right whenever the length is max_seq_len), none
+  // for a larger batch under the automatic plan.  A wrong guess reloads.
+  int b_g = -1, p0_g = 0;
+  if (!p.balanced) {
+    b_g = id / (H * p.n_splits);
+    p0_g = ((id / H) % p.n_splits) * p.pages_per_split;
+  } else if (p.batch == 1) {
+    b_g = 0;
+    p0_g = (id / H) * p.pages_per_split;
+  }
+  const bool stepping = p.k_new != nullptr;
+  constexpr int kPidPerThread = (kMaxPagesPerSplit + kThreads - 1) / kThreads;
+  constexpr int kQPerThread = (kNH * kHeadDim + kThreads - 1) / kThreads;
+  const int rc = tid & (kHeadDim - 1);
+  const int rpart = min(tid / kHeadDim, kParts - 1);
+  int pid[kPidPerThread];   // page ids of the split (index clamped into the table row)
+  uint32_t qraw[kQPerThread];  // q as raw dwords: the bf16 element's dword, or the fp32 element
+  uint32_t nraw = 0, muraw = 0;  // step form: the new key / value element, mu
+  float rv[kRows], rvv[kRows];   // rows [kRows * rpart, +kRows) of column rc of R_K, R_V
+  auto load_pages = [&](int bb, int pp0) {
+    const int32_t* pt = p.page_table + static_cast<size_t>(bb) * p.max_pages;
+#pragma unroll
+    for (int u = 0; u < kPidPerThread; ++u) pid[u] = pt[min(pp0 + tid + u * kThreads, p.max_pages - 1)];
+  };
+  auto load_seq = [&](int bb) {  // q rows and the new token of sequence bb
+    const size_t row0 = static_cast<size_t>(bb) * p.num_q_heads + static_cast<size_t>(h) * g;
+#pragma unroll
+    for (int u = 0; u < kQPerThread; ++u) {
+      const int idx = min(tid + u * kThreads, kNH * kHeadDim - 1);
+      const size_t qi = (row0 + min(idx / kHeadDim, g - 1)) * kHeadDim + idx % kHeadDim;
+      qraw[u] = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(p.q) +
+                                                   (p.q_kind == 0 ? (2 * qi) & ~static_cast<size_t>(3) : 4 * qi));
+    }
+    if (stepping) {
+      const size_t ni = (static_cast<size_t>(bb) * H + h) * kHeadDim + rc;
+      const uint8_t* src = static_cast<const uint8_t*>(tid < kHeadDim ? p.k_new : p.v_new);
+      nraw = *reinterpret_cast<const uint32_t*>(src + (p.kv_kind == 0 ? (2 * ni) & ~static_cast<size_t>(3) : 4 * ni));
+    }
+  };
+  if (b_g >= 0) {
+    load_pages(b_g, p0_g);
+    load_seq(b_g);
+  }
+  {
+    const float* R = p.r_k + (static_cast<size_t>(h) * kHeadDim + kRows * rpart) * kHeadDim + rc;
+#pragma unroll
+    for (int ii = 0; ii < kRows; ++ii) rv[ii] = R[ii * kHeadDim];
+  }
+  // the appending workgroup, guessed from max_seq_len (the last split of the guess)
+  const int pps_g = max(p.pages_per_split, 1);
+  const bool own_g = b_g >= 0 && (p0_g / pps_g) == ((p.len_cap + kPage - 1) / kPage + pps_g - 1) / pps_g - 1;
+  auto load_own = [&]() {
+    muraw = *reinterpret_cast<const uint32_t*>(p.mu != nullptr ? p.mu + h * kHeadDim + rc : p.r_v);
+    const float* R = p.r_v + (static_cast<size_t>(h) * kHeadDim + kRows * rpart) * kHeadDim + rc;
+#pragma unroll
+    for (int ii = 0; ii < kRows; ++ii) rvv[ii] = R[ii * kHeadDim];
+  };
+  if (stepping && own_g) load_own();
+
   // this workgroup's (sequence, split) and the partial row of the sequence's split 0
   int b, split, pps;
   size_t head_base;
+  int T_raw;
   if (p.balanced) {
     __shared__ int s_red[kW], s_loc[3];
     const SplitLoc loc = locate_split<kW>(p, id / H, tid, lane, wave, s_red, s_loc);
@@ -258,16 +325,17 @@ void decode_kernel(const DecodeParams p) {
     split = loc.split;
     pps = loc.pps;
     head_base = static_cast<size_t>(h) * p.n_splits + loc.first;
+    T_raw = p.batch == 1 ? loc.len : p.seq_lens[b];
   } else {
     split = (id / H) % p.n_splits;
     b = id / (H * p.n_splits);
     pps = p.pages_per_split;
     head_base = (static_cast<size_t>(b) * H + h) * p.n_splits;
+    T_raw = p.seq_lens[b];
   }
 
   // Pages past the table row are never read (a length beyond max_pages*16, or
   // beyond the host's max_seq_len, is cut).
-  const int T_raw = p.seq_lens[b];
   const int T = min(T_raw, p.len_cap);
   const int n_pages = T > 0 ? (T + kPage - 1) / kPage : 0;
   const size_t out_row0 = static_cast<size_t>(b) * p.num_q_heads + static_cast<size_t>(h) * g;
@@ -290,7 +358,6 @@ void decode_kernel(const DecodeParams p) {
   // Step form: the last split appends the token at position T - 1 and attends
   // it from its packed levels; the paged read masks that position, whose slot
   // may still hold an older token (and is rewritten during this launch).
-  const bool stepping = p.k_new != nullptr;
   const bool own = stepping && split == n_valid - 1;
   // INT2 positions attended from the paged cache: [int2_lo, int2_hi).  An exact
   // window takes the first win_sinks and the last win_recent positions; in the
@@ -302,46 +369,13 @@ void decode_kernel(const DecodeParams p) {
   int int2_hi = has_win ? max(int2_lo, T - p.win_recent) : T;
   if (stepping && !new_in_win) int2_hi = min(int2_hi, T - 1);
 
-  // ---- prologue loads, all issued before the first wait: this split's page
-  // ids, the g query rows and R_K.  Indices are clamped in bounds and values
-  // selected afterwards, so every load issues unconditionally.
-  constexpr int kPidPerThread = (kMaxPagesPerSplit + kThreads - 1) / kThreads;
-  const int32_t* pt = p.page_table + static_cast<size_t>(b) * p.max_pages + p0;
-  int pid[kPidPerThread];
-#pragma unroll
-  for (int u = 0; u < kPidPerThread; ++u) pid[u] = pt[min(tid + u * kThreads, np - 1)];
-  // q as raw dwords (the bf16 element's dword, or the fp32 element): one
-  // unconditional load each, converted after every prologue load is issued
-  constexpr int kQPerThread = (kNH * kHeadDim + kThreads - 1) / kThreads;
-  uint32_t qraw[kQPerThread];
-#pragma unroll
-  for (int u = 0; u < kQPerThread; ++u) {
-    const int idx = min(tid + u * kThreads, kNH * kHeadDim - 1);
-    const size_t qi = (out_row0 + min(idx / kHeadDim, g - 1)) * kHeadDim + idx % kHeadDim;
-    qraw[u] = *reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(p.q) +
-                                                 (p.q_kind == 0 ? (2 * qi) & ~static_cast<size_t>(3) : 4 * qi));
-  }
-  const int rc = tid & (kHeadDim - 1);
-  const int rpart = min(tid / kHeadDim, kParts - 1);
-  float rv[kRows];
-  {
-    const float* R = p.r_k + (static_cast<size_t>(h) * kHeadDim + kRows * rpart) * kHeadDim + rc;
-#pragma unroll
-    for (int ii = 0; ii < kRows; ++ii) rv[ii] = R[ii * kHeadDim];
-  }
-  // step form, appending workgroup: the new key (centred, fp32) and value rows
-  // and the same rows of R_V
-  uint32_t nraw = 0, muraw = 0;
-  float rvv[kRows];
+  // ---- prologue loads not yet issued (no guess, or a wrong one): this split's
+  // page ids, the g query rows and the new token.  Every prologue load lands
+  // before the first page-pair load is issued.
+  if (b != b_g || p0 != p0_g) load_pages(b, p0);
+  if (b != b_g) load_seq(b);
+  if (own && !own_g) load_own();
   const size_t ni = (static_cast<size_t>(b) * H + h) * kHeadDim + rc;
-  if (own) {
-    const uint8_t* src = static_cast<const uint8_t*>(tid < kHeadDim ? p.k_new : p.v_new);
-    nraw = *reinterpret_cast<const uint32_t*>(src + (p.kv_kind == 0 ? (2 * ni) & ~static_cast<size_t>(3) : 4 * ni));
-    muraw = *reinterpret_cast<const uint32_t*>(p.mu != nullptr ? p.mu + h * kHeadDim + rc : p.r_v);
-    const float* R = p.r_v + (static_cast<size_t>(h) * kHeadDim + kRows * rpart) * kHeadDim + rc;
-#pragma unroll
-    for (int ii = 0; ii < kRows; ++ii) rvv[ii] = R[ii * kHeadDim];
-  }
 #pragma unroll
   for (int u = 0; u < kPidPerThread; ++u) {
     const int i = tid + u * kThreads;
@@ -409,9 +443,10 @@ void decode_kernel(const DecodeParams p) {
 
   // Every wave keeps kDepth - 1 page pairs in flight ahead of the one it
   // computes (indices clamped to the last pair, so the wait counts are static;
-  // a wave near the end loads the last pair again and never uses it).
-#pragma unroll
-  for (int d = 0; d < kDepth - 1; ++d) issue(d, min(wave + kW * d, npairs - 1));
+  // a wave near the end loads the last pair again and never uses it).  The
+  // first pair is requested now; the others after q_hat, which would otherwise
+  // queue behind the whole grid's first requests.
+  issue(0, min(wave, npairs - 1));
 
   // ---- q_hat for the g query heads of this KV head
   if (tid < kParts * kHeadDim) {
@@ -471,6 +506,9 @@ void decode_kernel(const DecodeParams p) {
       if (lane == 0) s_nlog[jh] = d;
     }
   }
+
+#pragma unroll
+  for (int d = 1; d < kDepth - 1; ++d) issue(d, min(wave + kW * d, npairs - 1));
 
   // ---- block-diagonal query operands (fp16 hi/lo of q_hat * f)
   half8 qhi[kNQ][4], qlo[kNQ][4];
@@ -721,11 +759,9 @@ void decode_kernel(const DecodeParams p) {
   __syncthreads();
   if (tid == 0)
     s_ticket = __hip_atomic_fetch_add(p.counters + b * H + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (s_ticket != n_valid - 1) return;
-
-  // R_V rows for the output rotation, requested before the partials: thread
-  // (row oi, part oq) takes channels [kRows * oq, +kRows) of row oi
+  // R_V rows for the output rotation, requested by every workgroup right after
+  // its ticket (the merging one finds them in flight): thread (row oi, part oq)
+  // takes channels [kRows * oq, +kRows) of row oi
   const int oi = tid & (kHeadDim - 1);
   const int oq = rpart;
   float4v rr[kRows / 4];
@@ -734,6 +770,9 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < kRows / 4; ++u) rr[u] = *reinterpret_cast<const float4v*>(Rrow + 4 * u);
   }
+  __syncthreads();
+  if (s_ticket != n_valid - 1) return;
+
   // Merge, in one load round: every (split, head) max/sum pair is loaded by
   // one thread and shared through LDS (the ring is free now), while thread
   // (head jh, channel c) loads acc[c] of the first kAB splits; this

@@ -24,7 +24,8 @@ hipError_t launch_window_fill(uint16_t* buf, int batch, int num_kv_heads, int si
 struct DecodePlan {
   int n_pages_max;      // ceil(max_seq_len / 16)
   bool balanced;
-  int pages_per_split;  // fixed plan: pages handled by one workgroup, <= kMaxPagesPerSplit
+  int pages_per_split;  // fixed plan: pages handled by one workgroup, <= kMaxPagesPerSplit;
+                        // balanced: the split size for one sequence of max_seq_len (a guess)
   int n_splits;         // fixed plan: splits per (sequence, KV head); balanced: slots per KV head
   int pps_min, pps_max, target_wgs;  // balanced plan
 };
