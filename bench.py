@@ -101,8 +101,9 @@ def counters_for(kernel_src: str, workload: str):
 
 
 def kernel_source_sha() -> str:
+    """Hash of every source the decode kernel is compiled from (the counters file is keyed by it)."""
     h = hashlib.sha256()
-    for name in ("kvq_decode.hip", "kvq_device.h"):
+    for name in ("kvq_decode.hip", "kvq_device.h", "kvq_quant.h", "kvq_internal.h"):
         with open(os.path.join(ROOT, "rotated_int2_kv_centering_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()

@@ -22,9 +22,10 @@ Quantization* (arXiv 2608.02691):
 Readings where the page leaves a step open (each is listed with its reason in
 the design notes of the repository):
 
-* Q2 is asymmetric with clip ratio c = 1 and group size G = 32 consecutive
-  rotated channels of one token: scale s = (max - min)/3, zero z = min,
-  code = clamp(round_half_even((x - z)/s), 0, 3), level = z + s*code.
+* Q2 is asymmetric with group size G = 32 consecutive rotated channels of
+  one token and clip ratio c (default 1): with mn, mx = c*min, c*max,
+  scale s = (mx - mn)/3, zero z = mn, code = clamp(round_half_even((x - z)/s),
+  0, 3), level = z + s*code.
   The exact fp32/fp16 operation order is fixed in ``int2_quantize``.
 * mu is an input; it is subtracted from keys only and never added back.
 * R^T is applied to the query (as qR) and once to the attention output, which
@@ -107,29 +108,35 @@ def rotated_inputs(k, v, mu, r_k, r_v):
 
 
 # ---------------------------------------------------------- INT2 quantizer Q2
-def int2_quantize(x: np.ndarray):
-    """OptR §3.1: Q2(.; c=1, G=32), asymmetric, on fp32 rows of 128 channels.
+def int2_quantize(x: np.ndarray, clip: float = 1.0):
+    """OptR §3.1: Q2(.; c, G=32), asymmetric, on fp32 rows of 128 channels.
 
     ``x`` is float32 [..., 128].  Groups are 32 consecutive channels.  For each
     group, with every operation in IEEE fp32 (round to nearest even) unless
     stated:
 
-      mn, mx = min, max of the group
+      mn, mx = c * min, c * max of the group   (c = ``clip``, exact when c = 1)
       s32 = (mx - mn) / 3
       s16 = fp16(s32), z16 = fp16(mn)          (round to nearest even)
       s, z = float(s16), float(z16)
       if s == 0: every code is 0
       else code = clamp(round_half_even((x - z) / s), 0, 3)
 
+    The clip ratio c in (0, 1] narrows the range the four levels span (the page
+    names Q2(.; c, G) without defining c; reading: both ends of the group's
+    range are scaled by c, as the rotation baselines it builds on clip KV
+    groups); values past the narrowed range take the end codes.
     Returns (codes uint8 [..., 128], scale float16 [..., 4], zero float16 [..., 4]).
     Inputs must be finite with group ranges inside the fp16 range.
     """
     x = np.asarray(x)
     assert x.dtype == np.float32 and x.shape[-1] == HEAD_DIM
     assert np.isfinite(x).all(), "quantizer input must be finite"
+    c = np.float32(clip)
+    assert np.float32(0.0) < c <= np.float32(1.0), "clip ratio must be in (0, 1]"
     xg = x.reshape(x.shape[:-1] + (N_GROUPS, GROUP))
-    mn = xg.min(axis=-1)
-    mx = xg.max(axis=-1)
+    mn = (xg.min(axis=-1) * c).astype(np.float32)
+    mx = (xg.max(axis=-1) * c).astype(np.float32)
     rng = (mx - mn).astype(np.float32)
     s32 = (rng / np.float32(3.0)).astype(np.float32)
     s16 = s32.astype(np.float16)
@@ -243,14 +250,16 @@ def block_view(pool: np.ndarray, page: int, h: int, num_kv_heads: int) -> np.nda
 
 
 # ------------------------------------------------------------- quantize-append
-def quantize_append(pool: np.ndarray, num_kv_heads: int, slots, x: np.ndarray, w: np.ndarray) -> None:
+def quantize_append(pool: np.ndarray, num_kv_heads: int, slots, x: np.ndarray, w: np.ndarray,
+                    clip: float = 1.0) -> None:
     """Quantize rotated fp32 rows and store them at the given cache slots.
 
     ``x``/``w`` are float32 [n, H_kv, 128] (already centred and rotated);
-    ``slots[n]`` = page*16 + offset, all distinct.  Writes ``pool`` (uint8) in place.
+    ``slots[n]`` = page*16 + offset, all distinct; ``clip`` is Q2's clip ratio.
+    Writes ``pool`` (uint8) in place.
     """
-    kc, ks, kz = int2_quantize(x)
-    vc, vs, vz = int2_quantize(w)
+    kc, ks, kz = int2_quantize(x, clip)
+    vc, vs, vz = int2_quantize(w, clip)
     slots = np.asarray(slots, np.int64)
     assert len(np.unique(slots)) == len(slots), "slots must be distinct"
     pages = slots // PAGE
@@ -262,12 +271,12 @@ def quantize_append(pool: np.ndarray, num_kv_heads: int, slots, x: np.ndarray, w
                        block=block_view(pool, page, h, num_kv_heads), slots=offs)
 
 
-def append_tokens(pool, num_kv_heads, slots, k, v, mu, r_k, r_v) -> None:
+def append_tokens(pool, num_kv_heads, slots, k, v, mu, r_k, r_v, clip: float = 1.0) -> None:
     """Full write path: centre keys, rotate K and V, quantize, pack (OptR §1, §3.1 Eq. (4))."""
     check_orthogonal_all(r_k)
     check_orthogonal_all(r_v)
     x, w = rotated_inputs(k, v, mu, r_k, r_v)
-    quantize_append(pool, num_kv_heads, slots, x, w)
+    quantize_append(pool, num_kv_heads, slots, x, w, clip)
 
 
 def check_orthogonal_all(r: np.ndarray, tol: float = 1e-6) -> None:

@@ -528,3 +528,55 @@ def test_window_positions_survive_absent_pages():
     for j in range(c.Hq):
         ref = _brute_attention(c.q[0, j], k_eff[keep], v_eff[keep], 1 / np.sqrt(128))
         np.testing.assert_allclose(got[0, j], ref, rtol=0, atol=1e-11)
+
+
+# ------------------------------------------------------- Q2 clip ratio c < 1
+def test_quantizer_clip_golden_groups(golden_dir):
+    """OptR §3.1 Q2(.; c, G): hand-derived groups with c = 0.5 and c = 0.8 (both range ends
+    scale by c; values past the narrowed range take the end codes)."""
+    cases = {}
+    with open(os.path.join(golden_dir, "int2_clip_groups.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            name, field, *rest = line.split()
+            c = cases.setdefault(name, {})
+            if field == "values":
+                c[field] = np.array(_parse_runs(rest, float), dtype=np.float32)
+            elif field == "codes":
+                c[field] = np.array(_parse_runs(rest, int), dtype=np.uint8)
+            else:
+                c[field] = float(rest[0])
+    assert set(cases) == {"E", "F"}
+    for name, c in cases.items():
+        assert c["values"].shape == (32,) and c["codes"].shape == (32,)
+        row = np.tile(c["values"], 4)[None, :]
+        codes, s16, z16 = O.int2_quantize(row, clip=c["clip"])
+        for grp in range(4):
+            assert float(s16[0, grp]) == c["scale"], (name, grp)
+            assert float(z16[0, grp]) == c["zero"], (name, grp)
+            np.testing.assert_array_equal(codes[0, 32 * grp:32 * grp + 32], c["codes"], err_msg=name)
+
+
+def test_quantizer_clip_one_is_the_default_and_clipped_codes_are_nearest():
+    """c = 1 is the unclipped quantizer bit for bit; for c < 1 each code is the level of
+    z + s*{0..3} nearest to the value (ties aside), the ends absorbing values outside."""
+    rng = np.random.default_rng(31)
+    x = _random_rows(rng, 64, scale=3.0, offset=0.5)
+    np.testing.assert_array_equal(O.int2_quantize(x, clip=1.0)[0], O.int2_quantize(x)[0])
+    for c in (0.95, 0.8, 0.6):
+        codes, s16, z16 = O.int2_quantize(x, clip=c)
+        xg = x.reshape(64, 4, 32).astype(np.float64)
+        s = s16.astype(np.float64)[..., None]
+        z = z16.astype(np.float64)[..., None]
+        levels = z[..., None] + s[..., None] * np.arange(4)  # [64, 4, 1, 4]
+        dist = np.abs(xg[..., None] - levels)
+        got = np.take_along_axis(dist, codes.reshape(64, 4, 32)[..., None].astype(np.int64), -1)[..., 0]
+        best = dist.min(-1)
+        # the chosen level is nearest up to fp32 rounding of (x - z) / s
+        assert np.all(got <= best + 1e-5 * (np.abs(xg) + s[..., 0:1])), c
+        # a negative group minimum lies below the narrowed range (c * min > min): code 0
+        cg = codes.reshape(64, 4, 32)
+        at_min = (xg == xg.min(-1, keepdims=True)) & (xg < 0)
+        assert at_min.any() and np.all(cg[at_min] == 0), c
