@@ -14,11 +14,13 @@
  *     sum_s p_s (w_hat_s R^T) = (sum_s p_s w_hat_s) R^T, so the kernels rotate
  *     the query once, attend in the rotated basis straight from the packed
  *     codes, and rotate the output back once.
- * Q2 here is asymmetric with clip ratio 1 and G = 32 consecutive rotated
- * channels of one token: scale = (max - min)/3 and zero = min, both stored as
- * fp16 (round to nearest even); code = clamp(rint((x - zero)/scale), 0, 3)
- * computed in IEEE fp32 from the stored fp16 scale and zero; a group whose
- * stored scale is 0 gets all-zero codes.
+ * Q2 here is asymmetric over G = 32 consecutive rotated channels of one token,
+ * with the cache's clip ratio c (1 unless set): mn = c*min and mx = c*max in
+ * fp32, scale = (mx - mn)/3 and zero = mn, both stored as fp16 (round to
+ * nearest even); code = clamp(rint((x - zero)/scale), 0, 3) computed in IEEE
+ * fp32 from the stored fp16 scale and zero; a group whose stored scale is 0
+ * gets all-zero codes.  The page names Q2(.; c, G) without defining c; both
+ * range ends scaled by c is this library's reading.
  *
  * Geometry supported: head_dim 128, group 32, page 16 tokens, query heads per
  * KV head g = num_q_heads / num_kv_heads with 1 <= g <= 16.
@@ -83,6 +85,7 @@ typedef struct {
   int32_t page_size;    /* must be 16                                         */
   int32_t num_pages;    /* pages in the pool                                  */
   void* pool;           /* device, kvq_pool_bytes(cache) bytes, 16-byte aligned */
+  float clip_ratio;     /* Q2's clip ratio c in (0, 1]; 0 selects 1 (no clip)  */
 } kvq_cache;
 
 /*
@@ -138,7 +141,8 @@ size_t kvq_pool_bytes(const kvq_cache* cache);
  * Writes the K/V codes and fp16 scale/zero of every (token, KV head) into its
  * slot.  Other slots of the same page keep their contents.
  * Errors: KVQ_EINVAL (NULL cache/pool/k/v/slots, NULL r_k or r_v unless
- * pre-rotated, n_tokens < 0), KVQ_EUNSUPPORTED (geometry), KVQ_EHIP.
+ * pre-rotated, n_tokens < 0, clip_ratio outside [0, 1]), KVQ_EUNSUPPORTED
+ * (geometry), KVQ_EHIP.
  * n_tokens == 0 is a no-op.
  */
 kvq_status kvq_quant_append(const kvq_cache* cache, const void* k, const void* v, kvq_dtype in_dtype,

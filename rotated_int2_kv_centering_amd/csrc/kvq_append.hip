@@ -32,7 +32,7 @@ template <int kIn>  // 0 = bf16 raw, 1 = fp32 raw, 2 = fp32 already centred and 
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     uint8_t* __restrict__ pool, int num_pages, int num_kv_heads, const void* __restrict__ k_in,
     const void* __restrict__ v_in, int n_tokens, const int32_t* __restrict__ slots, const float* __restrict__ mu,
-    const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out) {
+    const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out, float clip) {
   const int tile = blockIdx.x;
   const int h = blockIdx.y;
   const int tensor = blockIdx.z;  // 0: key, 1: value
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
 
     const int page = slot >> 4;
     uint8_t* block = pool + (static_cast<size_t>(page) * num_kv_heads + h) * kBlockBytes;
-    (void)q2_pack_channel(xv, j, tensor, block, slot & 15);
+    (void)q2_pack_channel(xv, j, tensor, block, slot & 15, clip);
   }
 }
 
@@ -109,7 +109,7 @@ template <int kIn>  // 0 = bf16, 1 = fp32
 __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
     uint8_t* __restrict__ pool, int num_pages, int num_kv_heads, const void* __restrict__ k_in,
     const void* __restrict__ v_in, int n_tokens, const int32_t* __restrict__ slots, const float* __restrict__ mu,
-    const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out) {
+    const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out, float clip) {
   const int h = blockIdx.y;
   const int tensor = blockIdx.z;  // 0: key, 1: value
   const int tid = threadIdx.x;
@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
         x[4 * u + 3] = q4[3];
       }
       uint32_t pair, code[32];
-      q2_group32(x, pair, code);
+      q2_group32(x, clip, pair, code);
       const int slot = n < n_tokens ? slots[n] : -1;
       const bool ok = slot >= 0 && slot < num_pages * kPage;  // same for the token's four lanes
       if (rot_out != nullptr && n < n_tokens) {
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
 
 hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const void* k, const void* v, int in_kind,
                          int n_tokens, const int32_t* slots, const float* mu, const float* r_k, const float* r_v,
-                         float* rot_out, hipStream_t stream) {
+                         float* rot_out, float clip, hipStream_t stream) {
   (void)hipGetLastError();  // report only this call's launch errors, not stale ones
   if (in_kind != 2 && n_tokens >= kBulkMin) {
     // about one workgroup per compute unit in all, each staging its R once
@@ -288,10 +288,10 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
     const dim3 bgrid(per, num_kv_heads, 2);
     if (in_kind == 0)
       hipLaunchKernelGGL(append_bulk_kernel<0>, bgrid, dim3(kBulkThreads), 0, stream, pool, num_pages, num_kv_heads, k,
-                         v, n_tokens, slots, mu, r_k, r_v, rot_out);
+                         v, n_tokens, slots, mu, r_k, r_v, rot_out, clip);
     else
       hipLaunchKernelGGL(append_bulk_kernel<1>, bgrid, dim3(kBulkThreads), 0, stream, pool, num_pages, num_kv_heads, k,
-                         v, n_tokens, slots, mu, r_k, r_v, rot_out);
+                         v, n_tokens, slots, mu, r_k, r_v, rot_out, clip);
     return hipGetLastError();
   }
   const dim3 grid((n_tokens + kAppendTile - 1) / kAppendTile, num_kv_heads, 2);
@@ -299,15 +299,15 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
   switch (in_kind) {
     case 0:
       hipLaunchKernelGGL(append_kernel<0>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,
-                         slots, mu, r_k, r_v, rot_out);
+                         slots, mu, r_k, r_v, rot_out, clip);
       break;
     case 1:
       hipLaunchKernelGGL(append_kernel<1>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,
-                         slots, mu, r_k, r_v, rot_out);
+                         slots, mu, r_k, r_v, rot_out, clip);
       break;
     default:
       hipLaunchKernelGGL(append_kernel<2>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,
-                         slots, mu, r_k, r_v, rot_out);
+                         slots, mu, r_k, r_v, rot_out, clip);
       break;
   }
   return hipGetLastError();

@@ -485,7 +485,7 @@ void decode_kernel(const DecodeParams p) {
     const int tensor = tid / kHeadDim;
     const int pos = T - 1;
     uint8_t* blk = p.pool + (static_cast<size_t>(s_pages[np - 1]) * H + h) * kBlockBytes;
-    s_hat[tensor][rc] = q2_pack_channel(s_nrow[tensor][rc], rc, tensor, blk, pos & (kPage - 1));
+    s_hat[tensor][rc] = q2_pack_channel(s_nrow[tensor][rc], rc, tensor, blk, pos & (kPage - 1), p.clip);
   }
   for (int jh = wave; jh < kNH; jh += kW) {
     float am = fmaxf(fabsf(s_q[jh][lane]), fabsf(s_q[jh][lane + 64]));

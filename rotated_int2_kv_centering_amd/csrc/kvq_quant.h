@@ -5,7 +5,9 @@
 // Eq. (4): the cache stores Q2(zR).  Q2 here is asymmetric over groups of 32
 // consecutive rotated channels: s = fp16(fp32(max - min) / 3), z = fp16(min),
 // code = clamp(rint((x - z) / s), 0, 3) computed with the stored fp16 s and z
-// (all codes 0 when s is 0); the dequantized level is z + s * code.
+// (all codes 0 when s is 0); the dequantized level is z + s * code.  With a
+// clip ratio c < 1, min and max are first scaled by c (fp32), which narrows
+// the range the four levels span; values past it take the end codes.
 #pragma once
 
 #include "kvq_device.h"
@@ -45,7 +47,7 @@ __device__ __forceinline__ float rot_chains(const float* a, const float* r) {
 // A K code word and a metadata pair belong to one slot (plain stores); a V
 // code word holds codes of two slots, so it is updated with atomic and/or of
 // this slot's bits only, which keeps concurrent writes to other slots intact.
-__device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, uint8_t* block, int off) {
+__device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, uint8_t* block, int off, float clip) {
   const int lane = j & 63;
   const int w2 = j >> 6;
   const int grp = j >> 5;
@@ -55,6 +57,12 @@ __device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, ui
     mn = fminf(mn, __shfl_xor(mn, o));
     mx = fmaxf(mx, __shfl_xor(mx, o));
   }
+  mn *= clip;
+  mx *= clip;
+  // c*min and c*max are rounded to fp32 before anything else uses them (the
+  // fp16 zero included): without this the compiler may round c*min straight
+  // to fp16 in one mixed-precision multiply, which differs at fp16 ties.
+  asm volatile("" : "+v"(mn), "+v"(mx));
   const float s32 = (mx - mn) / 3.0f;
   const _Float16 s16 = static_cast<_Float16>(s32);
   const _Float16 z16 = static_cast<_Float16>(mn);
@@ -103,13 +111,19 @@ __device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, ui
 // q = fl(t * fl(1 / s)), which lies within 3 * 2^-24 |q| of fl(t / s), unless
 // q is within 2^-19 of a half-integer, where the two could round apart: such a
 // lane recomputes its group with the IEEE division.
-__device__ __forceinline__ void q2_group32(const float (&x)[32], uint32_t& pair, uint32_t (&code)[32]) {
+__device__ __forceinline__ void q2_group32(const float (&x)[32], float clip, uint32_t& pair, uint32_t (&code)[32]) {
   float mn = x[0], mx = x[0];
 #pragma unroll
   for (int c = 1; c < 32; ++c) {
     mn = fminf(mn, x[c]);
     mx = fmaxf(mx, x[c]);
   }
+  mn *= clip;
+  mx *= clip;
+  // c*min and c*max are rounded to fp32 before anything else uses them (the
+  // fp16 zero included): without this the compiler may round c*min straight
+  // to fp16 in one mixed-precision multiply, which differs at fp16 ties.
+  asm volatile("" : "+v"(mn), "+v"(mx));
   const float s32 = (mx - mn) / 3.0f;
   const _Float16 s16 = static_cast<_Float16>(s32);
   const _Float16 z16 = static_cast<_Float16>(mn);

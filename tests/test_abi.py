@@ -266,3 +266,16 @@ def test_window_bytes_and_host_validation(K):
     assert fill(ctypes.byref(empty), 1, FAKE, FAKE, K.KVQ_BF16, 5, FAKE, FAKE, FAKE, None) == K.KVQ_OK  # no window
     bad = W(4, 4, 2, FAKE + 4)
     assert fill(ctypes.byref(bad), 1, FAKE, FAKE, K.KVQ_BF16, 5, FAKE, FAKE, FAKE, None) == K.KVQ_EINVAL
+
+
+def test_cache_clip_ratio_layout_and_validation(K):
+    """kvq_cache.clip_ratio sits after the pool pointer; values outside [0, 1] (or NaN)
+    are rejected on the host before any launch."""
+    assert ctypes.sizeof(K.kvq_cache) == 40 and K.kvq_cache.clip_ratio.offset == 32
+    lib = K.load()
+    for bad in (1.5, -0.25, float("nan")):
+        c = K.make_cache(2, 4, FAKE, clip_ratio=bad)
+        assert lib.kvq_quant_append(ctypes.byref(c), FAKE, FAKE, K.KVQ_BF16, 1, FAKE, None, FAKE, FAKE, None,
+                                    None) == K.KVQ_EINVAL
+        assert "clip_ratio" in K.kvq_last_error()
+        assert _decode(K, K.make_cache(1, 8, FAKE, clip_ratio=bad)) == K.KVQ_EINVAL

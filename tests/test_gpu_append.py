@@ -20,9 +20,9 @@ def _prerotated_append(dc: DeviceCase, x: np.ndarray, w: np.ndarray, slots: np.n
     torch.cuda.synchronize()
 
 
-def _oracle_pool(case, num_pages, slots, x, w, base=None):
+def _oracle_pool(case, num_pages, slots, x, w, base=None, clip=1.0):
     pool = np.zeros(O.pool_bytes(num_pages, case.Hkv), np.uint8) if base is None else base.copy()
-    O.quantize_append(pool, case.Hkv, slots, x.astype(np.float32), w.astype(np.float32))
+    O.quantize_append(pool, case.Hkv, slots, x.astype(np.float32), w.astype(np.float32), clip)
     return pool
 
 
@@ -161,3 +161,43 @@ def test_full_size_append_sampled_tokens():
         a_k = O.centre_keys(case.k[idx], case.mu)[:, h]
         assert np.all(np.abs(rs[:, h, 0] - x64[:, h]) <= rotation_error_bound(a_k, case.r_k[h]) + 1e-30)
         assert np.all(np.abs(rs[:, h, 1] - w64[:, h]) <= rotation_error_bound(case.v[idx][:, h], case.r_v[h]) + 1e-30)
+
+
+# ------------------------------------------------------------ Q2 clip ratio
+@pytest.mark.parametrize("clip", [0.5, 0.7, 0.9])
+def test_prerotated_clipped_codes_bit_exact(clip):
+    """Q2(.; c, G) with c < 1 (the cache's clip_ratio): given the same rotated fp32
+    input, codes and fp16 scale/zero equal the oracle's quantizer bit for bit."""
+    dev = require_gpu()
+    case = I.make_case("c", 41, B=2, Hq=32, Hkv=8, seq_lens=[100, 37])
+    x, w = O.rotated_inputs(case.k, case.v, case.mu, case.r_k, case.r_v)
+    dc = DeviceCase(case, dev, clip_ratio=clip)
+    _prerotated_append(dc, x, w, case.slots)
+    np.testing.assert_array_equal(dc.pool_np(), _oracle_pool(case, dc.num_pages, case.slots, x, w, clip=clip))
+    unclipped = _oracle_pool(case, dc.num_pages, case.slots, x, w)
+    assert not np.array_equal(dc.pool_np(), unclipped)
+
+
+@pytest.mark.parametrize("path", ["fp32", "bulk"])
+def test_raw_path_clipped_codes(path):
+    """Raw bf16 input with c = 0.8, on both append kernels: codes and scale/zero are
+    bit-exact to the oracle's clipped quantizer run on the kernel's own rotated rows."""
+    dev = require_gpu()
+    case = I.make_case("rc", 42, B=2, Hq=16, Hkv=4, seq_lens=[70, 45], table_policy="interleaved")
+    dc = DeviceCase(case, dev, clip_ratio=0.8)
+    rot = dc.append(rot_out=True, chunk=16 if path == "fp32" else None).cpu().numpy()
+    expect = _oracle_pool(case, dc.num_pages, case.slots, rot[:, :, 0, :], rot[:, :, 1, :], clip=0.8)
+    np.testing.assert_array_equal(dc.pool_np(), expect)
+
+
+def test_decode_over_a_clipped_cache():
+    """Decode reads whatever levels the cache holds: on a clipped cache it matches the
+    oracle run on the same pool."""
+    from tests.gpu_util import max_abs_rel
+    dev = require_gpu()
+    case = I.make_case("dc", 43, B=2, Hq=32, Hkv=8, seq_lens=[900, 300], table_policy="interleaved")
+    dc = DeviceCase(case, dev, clip_ratio=0.85)
+    dc.append(rot_out=False)
+    got = dc.decode("f32")
+    ref = O.decode_attention(case.q, dc.pool_np(), case.Hkv, case.page_table, case.seq_lens, case.r_k, case.r_v)
+    assert max_abs_rel(got, ref) <= 2e-3

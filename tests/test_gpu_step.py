@@ -177,6 +177,28 @@ def test_step_without_mu_matches_zero_mu():
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
 
 
+def test_step_with_clip_ratio_writes_the_appended_bytes():
+    """The step quantizes the new token with the cache's clip ratio: its pool equals
+    kvq_quant_append's with the same c, and differs from the unclipped one."""
+    dev = require_gpu()
+    case = I.make_case("s5", 74, B=2, Hq=8, Hkv=2, seq_lens=[300, 41], table_policy="interleaved")
+    newest = _newest(case)
+    dc = DeviceCase(case, dev, clip_ratio=0.75)
+    _prefill(dc, case, newest)
+    k_new, v_new = _new_kv(case, dc, newest, dev)
+    got = dc.step(k_new, v_new, "f32")
+    ref_dc = DeviceCase(case, dev, clip_ratio=0.75)
+    ref_dc.pool.copy_(dc.pool)
+    _append_newest(ref_dc, newest)
+    assert np.array_equal(ref_dc.pool_np(), dc.pool_np())
+    plain = DeviceCase(case, dev)
+    plain.pool.copy_(dc.pool)
+    _append_newest(plain, newest)
+    assert not np.array_equal(plain.pool_np(), dc.pool_np())
+    ref = O.decode_attention(case.q, dc.pool_np(), case.Hkv, case.page_table, case.seq_lens, case.r_k, case.r_v)
+    assert max_abs_rel(got, ref) <= TOL
+
+
 @pytest.mark.parametrize("name", ["llama8b_t128k"])
 def test_full_size_step_sampled_heads(name):
     """The bench's workload and launch configuration: one step at 128K context."""
