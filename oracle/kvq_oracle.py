@@ -77,6 +77,26 @@ def check_orthogonal(r: np.ndarray, tol: float = 1e-6) -> None:
     assert err <= tol, f"rotation is not orthogonal (max |R^T R - I| = {err:.3g})"
 
 
+# -------------------------------------------------- structured rotation
+def hadamard_rotation(signs: np.ndarray) -> np.ndarray:
+    """Randomized Hadamard rotation per KV head, R = diag(s) H / sqrt(d) (fp64).
+
+    The rotation baseline the pages build OptR on (QuaRot) is a randomized
+    Hadamard transform; this is its plain matrix: H is Sylvester's Hadamard
+    matrix, H[i][j] = (-1)^popcount(i & j), and s a +-1 sign vector, so
+    (x R)_j = sum_i x_i s_i (-1)^popcount(i & j) / sqrt(d).  R is orthogonal
+    and enters every rotation function here like any other R.
+    ``signs`` is [H_kv, d] of +-1; returns [H_kv, d, d].
+    """
+    s = np.asarray(signs, np.float64)
+    assert np.all(np.abs(s) == 1.0), "signs must be +-1"
+    d = s.shape[-1]
+    idx = np.arange(d)
+    parity = np.vectorize(lambda v: bin(int(v)).count("1") & 1)(idx[:, None] & idx[None, :])
+    h = np.where(parity == 0, 1.0, -1.0)
+    return s[:, :, None] * h[None, :, :] / np.sqrt(d)
+
+
 # ---------------------------------------------- centering and rotation (fp64)
 def centre_keys(k: np.ndarray, mu: np.ndarray) -> np.ndarray:
     """OptR §1: attention-equivalent key reparameterisation, k - mu (fp64).

@@ -580,3 +580,39 @@ def test_quantizer_clip_one_is_the_default_and_clipped_codes_are_nearest():
         cg = codes.reshape(64, 4, 32)
         at_min = (xg == xg.min(-1, keepdims=True)) & (xg < 0)
         assert at_min.any() and np.all(cg[at_min] == 0), c
+
+
+# ------------------------------------------------ structured (Hadamard) rotation
+def _sylvester(d):
+    """Sylvester's construction by the Kronecker recursion H_2n = [[H, H], [H, -H]]."""
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def _fwht_recursive(x):
+    """Walsh-Hadamard transform of a vector by recursion on halves (unnormalised)."""
+    n = len(x)
+    if n == 1:
+        return x.copy()
+    a, b = _fwht_recursive(x[: n // 2]), _fwht_recursive(x[n // 2:])
+    return np.concatenate([a + b, a - b])
+
+
+def test_hadamard_rotation_matches_sylvester_and_fwht():
+    """hadamard_rotation(s) = diag(s) H / sqrt(128): H equals the Kronecker-recursive
+    Sylvester matrix, x R equals the recursive Walsh-Hadamard transform of x * s, R is
+    orthogonal, and with all signs +1 it is symmetric (its own inverse)."""
+    rng = np.random.default_rng(77)
+    signs = rng.choice([-1.0, 1.0], size=(2, 128))
+    r = O.hadamard_rotation(signs)
+    h = _sylvester(128)
+    for k in range(2):
+        np.testing.assert_array_equal(r[k] * np.sqrt(128), signs[k][:, None] * h)
+        assert np.abs(r[k].T @ r[k] - np.eye(128)).max() < 1e-14
+        x = rng.standard_normal(128)
+        np.testing.assert_allclose(x @ r[k], _fwht_recursive(x * signs[k]) / np.sqrt(128), rtol=0, atol=1e-13)
+    plain = O.hadamard_rotation(np.ones((1, 128)))[0]
+    np.testing.assert_allclose(plain @ plain, np.eye(128), atol=1e-14)
+    np.testing.assert_array_equal(plain, plain.T)
