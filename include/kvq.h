@@ -77,6 +77,18 @@ typedef enum {
                           run (mu, r_k, r_v are ignored and may be NULL)        */
 } kvq_dtype;
 
+/* How the rotations r_k, r_v passed to every call are given.
+ *   KVQ_ROT_DENSE     fp32 [H_kv][128][128], row-major, any orthogonal R.
+ *   KVQ_ROT_HADAMARD  fp32 [H_kv][128] signs s (each +1 or -1) of the
+ *                     randomized Hadamard rotation R = diag(s) H / sqrt(128),
+ *                     H[i][j] = (-1)^popcount(i & j) (Sylvester), the rotation
+ *                     family of QuaRot, one of the two base rotations
+ *                     OptR corrects (OptR section 1 and section 2).  The
+ *                     kernels apply it as a fast Walsh-Hadamard transform
+ *                     (x R = WHT(x * s) / sqrt(128)) instead of a 128 x 128
+ *                     product; the bulk matrix-core append is not used. */
+typedef enum { KVQ_ROT_DENSE = 0, KVQ_ROT_HADAMARD = 1 } kvq_rotation;
+
 /* Geometry of one layer's packed cache. */
 typedef struct {
   int32_t num_kv_heads; /* H_kv >= 1                                          */
@@ -86,6 +98,7 @@ typedef struct {
   int32_t num_pages;    /* pages in the pool                                  */
   void* pool;           /* device, kvq_pool_bytes(cache) bytes, 16-byte aligned */
   float clip_ratio;     /* Q2's clip ratio c in (0, 1]; 0 selects 1 (no clip)  */
+  int32_t rotation;     /* kvq_rotation: how r_k and r_v describe R           */
 } kvq_cache;
 
 /*
@@ -133,15 +146,16 @@ size_t kvq_pool_bytes(const kvq_cache* cache);
  *             distinct, each in [0, num_pages*16).  Out-of-range slots are
  *             skipped by the kernel (never written).
  *   mu        device fp32 [H_kv][128], the key centre; NULL means 0.
- *   r_k, r_v  device fp32 [H_kv][128][128], row-major, x_rot[j] = sum_i x[i] R[i][j].
- *             Must be orthogonal (not checked).
+ *   r_k, r_v  device fp32 [H_kv][128][128], row-major, x_rot[j] = sum_i x[i] R[i][j]
+ *             (must be orthogonal, not checked); under KVQ_ROT_HADAMARD the
+ *             signs [H_kv][128] instead (cache->rotation).
  *   rot_out   optional device fp32 [n_tokens][H_kv][2][128]: receives the
  *             fp32 quantizer inputs (index 0: centred rotated key, 1: rotated
  *             value) exactly as the kernel quantized them.  NULL = not written.
  * Writes the K/V codes and fp16 scale/zero of every (token, KV head) into its
  * slot.  Other slots of the same page keep their contents.
  * Errors: KVQ_EINVAL (NULL cache/pool/k/v/slots, NULL r_k or r_v unless
- * pre-rotated, n_tokens < 0, clip_ratio outside [0, 1]), KVQ_EUNSUPPORTED
+ * pre-rotated, n_tokens < 0, clip_ratio outside [0, 1], unknown rotation), KVQ_EUNSUPPORTED
  * (geometry), KVQ_EHIP.
  * n_tokens == 0 is a no-op.
  */
@@ -181,7 +195,7 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
  *               is cut to max_seq_len; kvq_decode_step then appends nothing
  *               for that sequence).
  *   max_seq_len host bound on seq_lens; must satisfy ceil(max_seq_len/16) <= max_pages.
- *   r_k, r_v    device fp32 [H_kv][128][128] as in kvq_quant_append.
+ *   r_k, r_v    device fp32, dense or Hadamard signs as in kvq_quant_append.
  *   sm_scale    logit scale; 0 selects 1/sqrt(128).
  *   out         device [batch][num_q_heads][128] of out_dtype (KVQ_BF16 or
  *               KVQ_F32).  The bf16 output is the fp32 result rounded to

@@ -153,6 +153,9 @@ class Case:
     k_bits: Optional[np.ndarray] = None
     v_bits: Optional[np.ndarray] = None
     outlier_channels: Optional[np.ndarray] = None
+    # "dense": r_k, r_v are [H_kv][128][128] orthogonal matrices; "hadamard": they
+    # are [H_kv][128] sign vectors (+-1) of a randomized Hadamard rotation
+    rotation: str = "dense"
 
     @property
     def g(self) -> int:
@@ -174,7 +177,7 @@ def _draw_keys(seed, n_tok, Hkv, outlier_ch, offsets, sub):
 def make_case(name: str, seed: int, B: int, Hq: int, Hkv: int, seq_lens, dtype: str = "bf16",
               n_outliers: int = 3, mu_tokens: int = 2048, table_policy: str = "permuted",
               shared_rotation: bool = False, num_pages: Optional[int] = None,
-              mu_zero: bool = False, identity_rotation: bool = False) -> Case:
+              mu_zero: bool = False, identity_rotation: bool = False, rotation: str = "dense") -> Case:
     seq_lens = np.asarray(seq_lens, dtype=np.int32)
     assert seq_lens.shape == (B,) and Hq % Hkv == 0
     out_rng = rng_for(seed, "outliers")
@@ -214,7 +217,15 @@ def make_case(name: str, seed: int, B: int, Hq: int, Hkv: int, seq_lens, dtype: 
     elif dtype != "f32":
         raise ValueError(dtype)
 
-    if identity_rotation:
+    if rotation == "hadamard":  # seeded +-1 signs per KV head
+        r_k = np.stack([rng_for(seed, "r_k", h).choice(np.array([-1.0, 1.0], np.float32), HEAD_DIM)
+                        for h in range(Hkv)]).astype(np.float32)
+        r_v = r_k.copy() if shared_rotation else np.stack(
+            [rng_for(seed, "r_v", h).choice(np.array([-1.0, 1.0], np.float32), HEAD_DIM)
+             for h in range(Hkv)]).astype(np.float32)
+    elif rotation != "dense":
+        raise ValueError(rotation)
+    elif identity_rotation:
         r_k = np.broadcast_to(np.eye(HEAD_DIM, dtype=np.float32), (Hkv, HEAD_DIM, HEAD_DIM)).copy()
         r_v = r_k.copy()
     else:
@@ -232,7 +243,7 @@ def make_case(name: str, seed: int, B: int, Hq: int, Hkv: int, seq_lens, dtype: 
     return Case(name=name, dtype=dtype, B=B, Hq=Hq, Hkv=Hkv, seq_lens=seq_lens, page_table=table,
                 num_pages=int(npages), q=q, k=k, v=v, tok_seq=tok_seq, tok_pos=tok_pos, slots=slots,
                 mu=mu, r_k=r_k, r_v=r_v, q_bits=q_bits, k_bits=k_bits, v_bits=v_bits,
-                outlier_channels=outlier_ch)
+                outlier_channels=outlier_ch, rotation=rotation)
 
 
 # Named workloads.  Sizes follow the tiny case and the Llama-3.1-8B-shaped and

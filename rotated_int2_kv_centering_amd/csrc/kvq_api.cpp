@@ -55,6 +55,8 @@ kvq_status check_cache(const kvq_cache* c) {
     return fail(KVQ_EUNSUPPORTED, "num_pages=%d exceeds the int32 slot range", c->num_pages);
   if (c->pool == nullptr && c->num_pages > 0) return fail(KVQ_EINVAL, "cache pool is NULL");
   if (reinterpret_cast<uintptr_t>(c->pool) % 16 != 0) return fail(KVQ_EINVAL, "cache pool must be 16-byte aligned");
+  if (c->rotation != KVQ_ROT_DENSE && c->rotation != KVQ_ROT_HADAMARD)
+    return fail(KVQ_EINVAL, "rotation=%d must be KVQ_ROT_DENSE or KVQ_ROT_HADAMARD", c->rotation);
   if (!(c->clip_ratio >= 0.0f && c->clip_ratio <= 1.0f))
     return fail(KVQ_EINVAL, "clip_ratio=%g must be in [0, 1] (0 selects 1)", static_cast<double>(c->clip_ratio));
   return KVQ_OK;
@@ -283,6 +285,7 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
   a.v_new = stepping ? v_new : nullptr;
   a.kv_kind = kv_dtype == KVQ_BF16 ? 0 : 1;
   a.clip = clip_of(cache);
+  a.rot_kind = cache->rotation;
   a.mu = mu;
   hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_begin),
                                     static_cast<hipEvent_t>(ev_end));
@@ -314,7 +317,7 @@ kvq_status kvq_quant_append(const kvq_cache* cache, const void* k, const void* v
     return fail(KVQ_EINVAL, "r_k and r_v must be non-NULL unless the input is pre-rotated");
   const int kind = in_dtype == KVQ_BF16 ? 0 : (in_dtype == KVQ_F32 ? 1 : 2);
   hipError_t e = kvq::launch_append(static_cast<uint8_t*>(cache->pool), cache->num_pages, cache->num_kv_heads, k, v,
-                                    kind, n_tokens, slots, mu, r_k, r_v, rot_out, clip_of(cache),
+                                    kind, n_tokens, slots, mu, r_k, r_v, rot_out, clip_of(cache), cache->rotation,
                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "quant_append launch");
   return KVQ_OK;

@@ -32,7 +32,8 @@ template <int kIn>  // 0 = bf16 raw, 1 = fp32 raw, 2 = fp32 already centred and 
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     uint8_t* __restrict__ pool, int num_pages, int num_kv_heads, const void* __restrict__ k_in,
     const void* __restrict__ v_in, int n_tokens, const int32_t* __restrict__ slots, const float* __restrict__ mu,
-    const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out, float clip) {
+    const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out, float clip,
+    int rot_kind) {
   const int tile = blockIdx.x;
   const int h = blockIdx.y;
   const int tensor = blockIdx.z;  // 0: key, 1: value
@@ -59,6 +60,15 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
 
   if (kIn == 2) {
     for (int t = half; t < kAppendTile; t += 2) xpart[0][t][j] = rows[t][j];
+  } else if (rot_kind == 1) {
+    // x = WHT(a * s) / sqrt(128): this half transforms tokens 8*half .. 8*half + 7
+    __shared__ float xch[2][kHeadDim];
+    const float sg = (tensor == 0 ? r_k : r_v)[h * kHeadDim + j];
+#pragma unroll 1
+    for (int tt = 0; tt < kAppendTile / 2; ++tt) {
+      const int t = (kAppendTile / 2) * half + tt;
+      xpart[0][t][j] = wht128(rows[t][j] * sg, j, xch[half]) * kInvSqrt128;
+    }
   } else {
     // x[t][j] = sum_i rows[t][i] R[i][j]: this thread sums i in [64*half, 64*half + 64)
     const float* R = (tensor == 0 ? r_k : r_v) + (static_cast<size_t>(h) * kHeadDim + 64 * half) * kHeadDim + j;
@@ -279,9 +289,9 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
 
 hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const void* k, const void* v, int in_kind,
                          int n_tokens, const int32_t* slots, const float* mu, const float* r_k, const float* r_v,
-                         float* rot_out, float clip, hipStream_t stream) {
+                         float* rot_out, float clip, int rot_kind, hipStream_t stream) {
   (void)hipGetLastError();  // report only this call's launch errors, not stale ones
-  if (in_kind != 2 && n_tokens >= kBulkMin) {
+  if (in_kind != 2 && n_tokens >= kBulkMin && rot_kind == 0) {  // the matrix-core path takes a dense R
     // about one workgroup per compute unit in all, each staging its R once
     const int n_tiles = (n_tokens + kBulkTile - 1) / kBulkTile;
     const int per = std::max(1, std::min(n_tiles, (256 + 2 * num_kv_heads - 1) / (2 * num_kv_heads)));
@@ -299,15 +309,15 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
   switch (in_kind) {
     case 0:
       hipLaunchKernelGGL(append_kernel<0>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,
-                         slots, mu, r_k, r_v, rot_out, clip);
+                         slots, mu, r_k, r_v, rot_out, clip, rot_kind);
       break;
     case 1:
       hipLaunchKernelGGL(append_kernel<1>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,
-                         slots, mu, r_k, r_v, rot_out, clip);
+                         slots, mu, r_k, r_v, rot_out, clip, rot_kind);
       break;
     default:
       hipLaunchKernelGGL(append_kernel<2>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,
-                         slots, mu, r_k, r_v, rot_out, clip);
+                         slots, mu, r_k, r_v, rot_out, clip, rot_kind);
       break;
   }
   return hipGetLastError();

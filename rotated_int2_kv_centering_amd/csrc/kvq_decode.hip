@@ -297,19 +297,30 @@ void decode_kernel(const DecodeParams p) {
     load_pages(b_g, p0_g);
     load_seq(b_g);
   }
-  {
+  const bool hadamard = p.rot_kind == 1;  // R = diag(s) H / sqrt(128): r_k, r_v hold the signs s
+  if (!hadamard) {
     const float* R = p.r_k + (static_cast<size_t>(h) * kHeadDim + kRows * rpart) * kHeadDim + rc;
 #pragma unroll
     for (int ii = 0; ii < kRows; ++ii) rv[ii] = R[ii * kHeadDim];
+  } else {
+#pragma unroll
+    for (int ii = 1; ii < kRows; ++ii) rv[ii] = 0.0f;
+    rv[0] = p.r_k[h * kHeadDim + rc];
   }
   // the appending workgroup, guessed from max_seq_len (the last split of the guess)
   const int pps_g = max(p.pages_per_split, 1);
   const bool own_g = b_g >= 0 && (p0_g / pps_g) == ((p.len_cap + kPage - 1) / kPage + pps_g - 1) / pps_g - 1;
   auto load_own = [&]() {
     muraw = *reinterpret_cast<const uint32_t*>(p.mu != nullptr ? p.mu + h * kHeadDim + rc : p.r_v);
-    const float* R = p.r_v + (static_cast<size_t>(h) * kHeadDim + kRows * rpart) * kHeadDim + rc;
+    if (!hadamard) {
+      const float* R = p.r_v + (static_cast<size_t>(h) * kHeadDim + kRows * rpart) * kHeadDim + rc;
 #pragma unroll
-    for (int ii = 0; ii < kRows; ++ii) rvv[ii] = R[ii * kHeadDim];
+      for (int ii = 0; ii < kRows; ++ii) rvv[ii] = R[ii * kHeadDim];
+    } else {
+#pragma unroll
+      for (int ii = 1; ii < kRows; ++ii) rvv[ii] = 0.0f;
+      rvv[0] = p.r_v[h * kHeadDim + rc];
+    }
   };
   if (stepping && own_g) load_own();
 
@@ -449,6 +460,26 @@ void decode_kernel(const DecodeParams p) {
   issue(0, min(wave, npairs - 1));
 
   // ---- q_hat for the g query heads of this KV head
+  constexpr int kVecPasses = (kNH * kHeadDim + kThreads - 1) / kThreads;  // 128-vectors per thread (Hadamard)
+  if (hadamard) {
+    // q_hat = WHT(q * s_K) / sqrt(128) * scale, and the new token's centred key and
+    // value rows by the transform the append kernel uses (kvq_quant.h: wht128)
+#pragma unroll 1
+    for (int pass = 0; pass < kVecPasses; ++pass) {
+      const int idx = tid + pass * kThreads;
+      const bool act = idx < kNH * kHeadDim;
+      const int jh = min(idx / kHeadDim, kNH - 1), c = idx & (kHeadDim - 1);
+      const float y = wht128(act ? s_q[jh][c] * rv[0] : 0.0f, c, act ? s_pro + jh * kHeadDim : nullptr);
+      if (act) s_q[jh][c] = y * kInvSqrt128 * p.logit_scale;
+    }
+    if (new_ok) {
+      const bool act = tid < 2 * kHeadDim;
+      const int tensor = min(tid / kHeadDim, 1);
+      const float x = act ? s_nrow[tensor][rc] * (tensor == 0 ? rv[0] : rvv[0]) : 0.0f;
+      const float y = wht128(x, rc, act ? s_npart + tensor * kHeadDim : nullptr);
+      if (act) s_nrow[tensor][rc] = y * kInvSqrt128;  // rotated
+    }
+  } else {
   if (tid < kParts * kHeadDim) {
     float accq[kNH];
 #pragma unroll
@@ -480,6 +511,7 @@ void decode_kernel(const DecodeParams p) {
                                 : np_[0] + np_[kHeadDim];
     s_nrow[tid / kHeadDim][rc] = x;  // rotated
   }
+  }  // dense R
   __syncthreads();
   if (new_ok && tid < 2 * kHeadDim) {  // quantize-append the new token (two waves per tensor)
     const int tensor = tid / kHeadDim;
@@ -765,10 +797,13 @@ void decode_kernel(const DecodeParams p) {
   const int oi = tid & (kHeadDim - 1);
   const int oq = rpart;
   float4v rr[kRows / 4];
-  {
+  float sgv = 0.0f;  // Hadamard: the sign of output channel oi
+  if (!hadamard) {
     const float* Rrow = p.r_v + (static_cast<size_t>(h) * kHeadDim + oi) * kHeadDim + kRows * oq;
 #pragma unroll
     for (int u = 0; u < kRows / 4; ++u) rr[u] = *reinterpret_cast<const float4v*>(Rrow + 4 * u);
+  } else {
+    sgv = p.r_v[h * kHeadDim + oi];
   }
   __syncthreads();
   if (s_ticket != n_valid - 1) return;
@@ -1058,6 +1093,25 @@ void decode_kernel(const DecodeParams p) {
   }
   __syncthreads();
 
+  auto store_out = [&](int jh, int i, float o) {
+    if (win_here) o += s_post[kOwOff + jh * kHeadDim + i];
+    const size_t oidx = (out_row0 + jh) * kHeadDim + i;
+    if (p.out_kind == 0)
+      static_cast<uint16_t*>(p.out)[oidx] = f32_to_bf16_bits(o);
+    else
+      static_cast<float*>(p.out)[oidx] = o;
+  };
+  if (hadamard) {
+    // o = o_rot R_V^T = s_V * WHT(o_rot) / sqrt(128), one vector per (2 waves, pass)
+#pragma unroll 1
+    for (int pass = 0; pass < kVecPasses; ++pass) {
+      const int idx = tid + pass * kThreads;
+      const bool act = idx < kNH * kHeadDim;
+      const int jh = min(idx / kHeadDim, kNH - 1), i = idx & (kHeadDim - 1);
+      const float y = wht128(act ? s_q[jh][i] : 0.0f, i, act ? s_post + jh * kHeadDim : nullptr);
+      if (act && jh < g) store_out(jh, i, y * kInvSqrt128 * sgv);
+    }
+  } else {
   // o = o_rot R_V^T: o[i] = sum_c o_rot[c] R_V[i][c]; thread (i, part) sums kRows channels
   if (tid < kParts * kHeadDim) {
     float o[kNH];
@@ -1079,13 +1133,9 @@ void decode_kernel(const DecodeParams p) {
     float o = 0.0f;
 #pragma unroll
     for (int u = 0; u < kParts; ++u) o += s_post[(u * kNH + jh) * kHeadDim + i];
-    if (win_here) o += s_post[kOwOff + jh * kHeadDim + i];
-    const size_t oidx = (out_row0 + jh) * kHeadDim + i;
-    if (p.out_kind == 0)
-      static_cast<uint16_t*>(p.out)[oidx] = f32_to_bf16_bits(o);
-    else
-      static_cast<float*>(p.out)[oidx] = o;
+    store_out(jh, i, o);
   }
+  }  // dense R
   if (tid == 0) __hip_atomic_store(p.counters + b * H + h, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

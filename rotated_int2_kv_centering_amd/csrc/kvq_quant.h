@@ -32,6 +32,31 @@ __device__ __forceinline__ float rot_chains(const float* a, const float* r) {
   return c0 + c1;
 }
 
+// Randomized Hadamard rotation R = diag(s) H / sqrt(128) (H Sylvester's
+// Hadamard matrix, H[i][j] = (-1)^popcount(i & j)): x R = WHT(x * s) / sqrt(128)
+// and y R^T = s * WHT(y) / sqrt(128).  wht128 is the unnormalised Walsh-Hadamard
+// transform of a 128-vector held one element per thread by two whole waves
+// (element c = 64 * wave-pair index + lane): stage k = 0..6 turns the pair
+// (c, c ^ 2^k) with bit k of c clear into (x_c + x_c', x_c - x_c'); stages 0..5
+// shuffle within the wave, stage 6 crosses the two waves through `xch` (128
+// floats per vector).  Every thread of the workgroup calls it (it holds two
+// barriers); threads without a vector pass xch = nullptr.  One fixed order, so
+// the append and the fused decode step round identically.
+constexpr float kInvSqrt128 = 0.0883883476483184405f;
+
+__device__ __forceinline__ float wht128(float x, int c, float* xch) {
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    const float p = __shfl_xor(x, 1 << k);
+    x = (c & (1 << k)) ? p - x : x + p;
+  }
+  if (xch != nullptr) xch[c] = x;
+  __syncthreads();
+  const float p = xch != nullptr ? xch[c ^ 64] : 0.0f;
+  __syncthreads();  // xch free again
+  return (c & 64) ? p - x : x + p;
+}
+
 // Quantizes channel j of one token's rotated vector and packs it into a block.
 // Called by the 128 threads j = 0..127 of one (token, KV head, tensor), laid
 // out as two whole waves (j = 64 * w2 + lane), so each 32-lane half-wave holds

@@ -25,6 +25,8 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 KVQ_OK, KVQ_EINVAL, KVQ_EUNSUPPORTED, KVQ_ENOSPACE, KVQ_EHIP = 0, 1, 2, 3, 4
 # kvq_dtype
 KVQ_BF16, KVQ_F32, KVQ_F32_ROTATED = 0, 1, 2
+# kvq_rotation
+KVQ_ROT_DENSE, KVQ_ROT_HADAMARD = 0, 1
 # kvq_pt_policy
 KVQ_PT_CONTIGUOUS, KVQ_PT_PERMUTED, KVQ_PT_INTERLEAVED, KVQ_PT_VALIDATE = 0, 1, 2, 3
 
@@ -41,7 +43,7 @@ class KvqError(RuntimeError):
 class kvq_cache(ctypes.Structure):
     _fields_ = [("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("pool", ctypes.c_void_p),
-                ("clip_ratio", ctypes.c_float)]
+                ("clip_ratio", ctypes.c_float), ("rotation", ctypes.c_int32)]
 
 
 class kvq_window(ctypes.Structure):
@@ -126,8 +128,8 @@ def _check(status: int) -> None:
 
 
 def make_cache(num_kv_heads: int, num_pages: int, pool=None, head_dim: int = HEAD_DIM, group_size: int = GROUP_SIZE,
-               page_size: int = PAGE_SIZE, clip_ratio: float = 0.0) -> kvq_cache:
-    return kvq_cache(num_kv_heads, head_dim, group_size, page_size, num_pages, _ptr(pool), clip_ratio)
+               page_size: int = PAGE_SIZE, clip_ratio: float = 0.0, rotation: int = 0) -> kvq_cache:
+    return kvq_cache(num_kv_heads, head_dim, group_size, page_size, num_pages, _ptr(pool), clip_ratio, rotation)
 
 
 def make_window(sinks: int, recent: int, batch: int, buf=None, mu=None) -> kvq_window:

@@ -43,7 +43,8 @@ class DeviceCase:
         self.dev = dev
         self.num_pages = int(num_pages or case.num_pages)
         self.pool = torch.zeros(O.pool_bytes(self.num_pages, case.Hkv), dtype=torch.uint8, device=dev)
-        self.cache = kvq.make_cache(case.Hkv, self.num_pages, self.pool, clip_ratio=clip_ratio)
+        self.cache = kvq.make_cache(case.Hkv, self.num_pages, self.pool, clip_ratio=clip_ratio,
+                                    rotation=kvq.KVQ_ROT_HADAMARD if case.rotation == "hadamard" else kvq.KVQ_ROT_DENSE)
         if case.dtype == "bf16":
             self.k = bf16_tensor(case.k_bits, dev)
             self.v = bf16_tensor(case.v_bits, dev)
@@ -139,6 +140,14 @@ class DeviceCase:
 
     def pool_np(self) -> np.ndarray:
         return self.pool.cpu().numpy()
+
+
+def dense_rotations(case):
+    """(R_K, R_V) as dense [H_kv][128][128] matrices for oracle calls: the case's own,
+    or the oracle's matrices of its Hadamard signs."""
+    if case.rotation == "hadamard":
+        return O.hadamard_rotation(case.r_k), O.hadamard_rotation(case.r_v)
+    return case.r_k, case.r_v
 
 
 def max_abs_rel(got: np.ndarray, ref: np.ndarray) -> float:

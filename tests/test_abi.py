@@ -272,6 +272,9 @@ def test_cache_clip_ratio_layout_and_validation(K):
     """kvq_cache.clip_ratio sits after the pool pointer; values outside [0, 1] (or NaN)
     are rejected on the host before any launch."""
     assert ctypes.sizeof(K.kvq_cache) == 40 and K.kvq_cache.clip_ratio.offset == 32
+    assert K.kvq_cache.rotation.offset == 36
+    assert _decode(K, K.make_cache(1, 8, FAKE, rotation=2)) == K.KVQ_EINVAL  # unknown rotation kind
+    assert "rotation" in K.kvq_last_error()
     lib = K.load()
     for bad in (1.5, -0.25, float("nan")):
         c = K.make_cache(2, 4, FAKE, clip_ratio=bad)

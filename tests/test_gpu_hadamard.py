@@ -1,0 +1,126 @@
+"""GPU parity with a structured (randomized Hadamard) rotation through the C ABI.
+
+Under KVQ_ROT_HADAMARD the caller passes sign vectors s and R = diag(s) H /
+sqrt(128); the kernels apply a fast Walsh-Hadamard transform instead of a dense
+product.  The oracle uses the dense matrix of the same signs
+(oracle.hadamard_rotation).  Same gates as the dense tests: the kernel's rotated
+rows within the fp32 rounding bound of the fp64 product, codes bit-exact to the
+oracle's quantizer on those rows, the step writing the append's bytes, decode
+within 2e-3.
+"""
+
+import numpy as np
+import pytest
+
+import kvq_inputs as I
+from oracle import kvq_oracle as O
+from tests.gpu_util import (DeviceCase, dense_rotations, dev_tensor, max_abs_rel, require_gpu,
+                            rotation_error_bound)
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.mark.parametrize("dtype,lens", [("bf16", [70, 45]), ("f32", [30, 2]), ("bf16", [300, 5])])
+def test_append_rotation_and_codes(dtype, lens):
+    dev = require_gpu()
+    case = I.make_case("h", 90 + sum(lens), B=2, Hq=16, Hkv=4, seq_lens=lens, dtype=dtype,
+                       table_policy="interleaved", rotation="hadamard")
+    r_k, r_v = dense_rotations(case)
+    dc = DeviceCase(case, dev)
+    rot = dc.append(rot_out=True).cpu().numpy()
+    xg, wg = rot[:, :, 0, :], rot[:, :, 1, :]
+    a = O.centre_keys(case.k, case.mu)
+    x64 = O.rotate(a, r_k)
+    w64 = O.rotate(case.v, r_v)
+    for h in range(case.Hkv):
+        assert np.all(np.abs(xg[:, h] - x64[:, h]) <= rotation_error_bound(a[:, h], r_k[h]) + 1e-30)
+        assert np.all(np.abs(wg[:, h] - w64[:, h]) <= rotation_error_bound(case.v[:, h], r_v[h]) + 1e-30)
+    expect = np.zeros_like(dc.pool_np())
+    O.quantize_append(expect, case.Hkv, case.slots, xg, wg)
+    np.testing.assert_array_equal(dc.pool_np(), expect)
+
+
+SHAPES = [
+    (1, 4, 1, [256]),
+    (2, 2, 2, [77, 300]),         # g = 1
+    (2, 32, 8, [1000, 257]),      # g = 4
+    (2, 64, 8, [513, 1024]),      # g = 8
+    (1, 16, 1, [300]),            # g = 16
+    (3, 8, 2, [0, 5, 100]),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"B{s[0]}_Hq{s[1]}_Hkv{s[2]}_T{'-'.join(map(str, s[3]))}")
+def test_decode_parity(shape):
+    dev = require_gpu()
+    B, Hq, Hkv, lens = shape
+    case = I.make_case("hd", 190 + sum(lens) + Hq, B=B, Hq=Hq, Hkv=Hkv, seq_lens=lens,
+                       table_policy="interleaved", rotation="hadamard")
+    r_k, r_v = dense_rotations(case)
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False)
+    ref = O.decode_attention(case.q, dc.pool_np(), case.Hkv, case.page_table, case.seq_lens, r_k, r_v)
+    for ns in (0, 3):
+        got = dc.decode("f32", num_splits=ns)
+        assert max_abs_rel(got, ref) <= TOL, ns
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_step_writes_the_appended_bytes(dtype):
+    """The fused step rotates the new token with the same transform as the append kernel."""
+    from rotated_int2_kv_centering_amd import kvq
+    import torch
+    dev = require_gpu()
+    case = I.make_case("hs", 95, B=3, Hq=8, Hkv=2, seq_lens=[40, 1, 17], dtype=dtype, table_policy="interleaved",
+                       rotation="hadamard")
+    r_k, r_v = dense_rotations(case)
+    newest = np.array([np.nonzero(case.tok_seq == b)[0][-1] for b in range(case.B)])
+    old = np.setdiff1d(np.arange(case.n_tokens), newest)
+    ref_dc = DeviceCase(case, dev)
+    ref_dc.append(rot_out=False)
+    dc = DeviceCase(case, dev)
+    sel = dev_tensor(old, dev)
+    kvq.kvq_quant_append(dc.cache, dc.k[sel].contiguous(), dc.v[sel].contiguous(), dc.in_dtype, len(old),
+                         dc.slots[sel].contiguous(), dc.mu, dc.r_k, dc.r_v)
+    torch.cuda.synchronize()
+    nsel = dev_tensor(newest, dev)
+    got = dc.step(dc.k[nsel].contiguous(), dc.v[nsel].contiguous(), "f32")
+    np.testing.assert_array_equal(dc.pool_np(), ref_dc.pool_np())
+    ref = O.decode_attention(case.q, dc.pool_np(), case.Hkv, case.page_table, case.seq_lens, r_k, r_v)
+    assert max_abs_rel(got, ref) <= TOL
+
+
+def test_window_with_hadamard_rotation():
+    dev = require_gpu()
+    case = I.make_case("hw", 96, B=2, Hq=32, Hkv=8, seq_lens=[700, 90], table_policy="interleaved",
+                       rotation="hadamard")
+    r_k, r_v = dense_rotations(case)
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False)
+    win = dc.window(4, 64)
+    got = dc.decode("f32", window=win)
+    ks, vs = [], []
+    for b in range(case.B):
+        sel = np.nonzero(case.tok_seq == b)[0]
+        ks.append(case.k[sel])
+        vs.append(case.v[sel])
+    ref = O.decode_attention_window(case.q, dc.pool_np(), case.Hkv, case.page_table, case.seq_lens, case.mu, r_k,
+                                    r_v, ks, vs, 4, 64)
+    assert max_abs_rel(got, ref) <= TOL
+
+
+def test_full_size_hadamard_sampled_heads():
+    """The 8B shape at 128K with a Hadamard rotation: bulk-size append (taking the
+    transform path) and one decode, sampled heads against the oracle."""
+    dev = require_gpu()
+    case = I.make_case("hf", 2, B=1, Hq=32, Hkv=8, seq_lens=[131072], table_policy="permuted", rotation="hadamard")
+    r_k, r_v = dense_rotations(case)
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False, chunk=1 << 20)
+    got = dc.decode("f32")
+    heads = [(0, 0), (0, 17), (0, 31)]
+    ref = O.decode_attention(case.q, dc.pool_np(), case.Hkv, case.page_table, case.seq_lens, r_k, r_v, heads=heads)
+    for b, j in heads:
+        assert max_abs_rel(got[b, j], ref[b, j]) <= TOL, j
