@@ -44,13 +44,13 @@ PAGE = 16
 
 WORKLOADS = {
     "llama8b_t128k": ("Llama-3.1-8B-shaped decode, batch 1, context 131072 (32 q / 8 kv heads, d=128)",
-                      lambda I: I.llama8b_case(131072)),
+                      lambda I, rot: I.llama8b_case(131072, rotation=rot)),
     "llama8b_t32k": ("Llama-3.1-8B-shaped decode, batch 1, context 32768 (32 q / 8 kv heads, d=128)",
-                     lambda I: I.llama8b_case(32768)),
+                     lambda I, rot: I.llama8b_case(32768, rotation=rot)),
     "llama8b_batch16": ("Llama-3.1-8B-shaped decode, batch 16, contexts uniform in [4K, 64K]",
-                        lambda I: I.batched_case()),
+                        lambda I, rot: I.batched_case(rotation=rot)),
     "gqa70b_b4_t128k": ("70B-class GQA decode (64 q / 8 kv heads), batch 4, context 131072 each",
-                        lambda I: I.seventy_b_case()),
+                        lambda I, rot: I.seventy_b_case(rotation=rot)),
 }
 
 
@@ -145,14 +145,17 @@ def cpu_baseline(case, pool_np, kv_heads_sample: int):
     from oracle import kvq_oracle as O
 
     hs = list(range(min(kv_heads_sample, case.Hkv)))
+    r_k, r_v = case.r_k, case.r_v
+    if case.rotation == "hadamard":
+        r_k, r_v = O.hadamard_rotation(r_k), O.hadamard_rotation(r_v)
     heads = [(b, j) for b in range(case.B) for j in range(case.Hq) if j // case.g in hs]
     last = np.array([np.nonzero(case.tok_seq == b)[0][-1] for b in range(case.B)])
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         pool = pool_np.copy()
-        x, w = O.rotated_inputs(case.k[last], case.v[last], case.mu, case.r_k, case.r_v)
+        x, w = O.rotated_inputs(case.k[last], case.v[last], case.mu, r_k, r_v)
         O.quantize_append(pool, case.Hkv, case.slots[last], x, w)
-        O.decode_attention(case.q, pool, case.Hkv, case.page_table, case.seq_lens, case.r_k, case.r_v, heads=heads)
+        O.decode_attention(case.q, pool, case.Hkv, case.page_table, case.seq_lens, r_k, r_v, heads=heads)
         dt = time.perf_counter() - t0
     step_est = dt * case.Hkv / len(hs)
     tokens = float(case.seq_lens.sum())
@@ -178,6 +181,8 @@ def main() -> int:
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-kv-heads", type=int, default=8, help="KV heads in the oracle's timed sample (0 = skip)")
     ap.add_argument("--window", default="", help="exact bf16 window 'sinks,recent' (e.g. 4,128); default none")
+    ap.add_argument("--rotation", default="dense", choices=["dense", "hadamard"],
+                    help="R as a dense random orthogonal matrix, or a randomized Hadamard rotation (sign vectors)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -201,7 +206,7 @@ def main() -> int:
     desc, make = WORKLOADS[args.workload]
 
     t_gen = time.perf_counter()
-    case = make(I)
+    case = make(I, args.rotation)
     log(f"[bench] generated {case.name}: B={case.B} Hq={case.Hq} Hkv={case.Hkv} sum(T)={int(case.seq_lens.sum())} "
         f"in {time.perf_counter() - t_gen:.1f}s")
 
@@ -218,10 +223,11 @@ def main() -> int:
     # ---- replica 0: bulk quantize-append of the whole context
     k_all, v_all = B16(case.k_bits), B16(case.v_bits)
     slots_all = T(case.slots)
+    rot_kind = kvq.KVQ_ROT_HADAMARD if args.rotation == "hadamard" else kvq.KVQ_ROT_DENSE
     pools, caches, rks, rvs, mus = [], [], [], [], []
     for r in range(n_rep):
         pools.append(torch.zeros(pool_bytes, dtype=torch.uint8, device=dev))
-        caches.append(kvq.make_cache(case.Hkv, case.num_pages, pools[-1]))
+        caches.append(kvq.make_cache(case.Hkv, case.num_pages, pools[-1], rotation=rot_kind))
         rks.append(T(case.r_k))
         rvs.append(T(case.r_v))
         mus.append(T(case.mu))
@@ -347,7 +353,7 @@ def main() -> int:
     # with an exact window: its bf16 key and value rows (512 B per position per KV head) are read too
     alg_bytes += n_win_tok * case.Hkv * 512
     achieved = alg_bytes / (split_avg_ms * 1e-3) / 1e9
-    traffic = counters_for(kernel_source_sha(), args.workload)
+    traffic = counters_for(kernel_source_sha(), args.workload + ("" if args.rotation == "dense" else "_" + args.rotation))
 
     cpu = None
     if args.cpu_kv_heads > 0:
@@ -366,7 +372,8 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "int2 cache, f16 MFMA operands, f32 accumulate",
-        "data": "synthetic (seeded bf16 q/k/v with outlier key channels and per-channel offsets, random orthogonal R)",
+        "data": "synthetic (seeded bf16 q/k/v with outlier key channels and per-channel offsets, "
+                + ("random orthogonal R)" if args.rotation == "dense" else "randomized Hadamard R)"),
         "config": {
             "workload": desc,
             "batch": case.B, "num_q_heads": case.Hq, "num_kv_heads": case.Hkv, "head_dim": 128,
@@ -374,6 +381,7 @@ def main() -> int:
             "page_table": "seeded permutation" if case.B == 1 else "seeded interleaved allocator",
             "cache_replicas": n_rep, "num_splits": args.num_splits or "auto",
             "exact_window": {"sinks": sinks, "recent": recent} if (sinks or recent) else None,
+            "rotation": args.rotation,
         },
         "hbm_gbps_step": cache_bytes / (ms_per_step * 1e-3) / 1e9,
         "pct_peak_step": cache_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,

@@ -254,27 +254,27 @@ def tiny_case(seed: int = 1) -> Case:
                      mu_tokens=256, table_policy="contiguous", shared_rotation=True)
 
 
-def llama8b_case(T: int, seed: int = 2, B: int = 1) -> Case:
+def llama8b_case(T: int, seed: int = 2, B: int = 1, rotation: str = "dense") -> Case:
     """32 query / 8 KV heads, bf16, permuted page table, mu from the first 2048 tokens."""
     return make_case(f"llama8b_b{B}_t{T}", seed, B=B, Hq=32, Hkv=8, seq_lens=[T] * B, dtype="bf16",
-                     n_outliers=3, mu_tokens=2048, table_policy="permuted")
+                     n_outliers=3, mu_tokens=2048, table_policy="permuted", rotation=rotation)
 
 
 def batched_lengths(B: int = 16, lo: int = 4096, hi: int = 65536, seed: int = 4) -> np.ndarray:
     return rng_for(seed, "lengths").integers(lo, hi + 1, size=B).astype(np.int32)
 
 
-def batched_case(seed: int = 4, B: int = 16, lo: int = 4096, hi: int = 65536) -> Case:
+def batched_case(seed: int = 4, B: int = 16, lo: int = 4096, hi: int = 65536, rotation: str = "dense") -> Case:
     """8B shape, batch 16, lengths uniform in [4K, 64K], interleaved page allocator."""
     lens = batched_lengths(B, lo, hi, seed)
     return make_case(f"llama8b_batch{B}", seed, B=B, Hq=32, Hkv=8, seq_lens=lens, dtype="bf16",
-                     n_outliers=3, mu_tokens=2048, table_policy="interleaved")
+                     n_outliers=3, mu_tokens=2048, table_policy="interleaved", rotation=rotation)
 
 
-def seventy_b_case(T: int = 131072, B: int = 4, seed: int = 5) -> Case:
+def seventy_b_case(T: int = 131072, B: int = 4, seed: int = 5, rotation: str = "dense") -> Case:
     """64 query / 8 KV heads (group 8), bf16, interleaved page allocator."""
     return make_case(f"gqa70b_b{B}_t{T}", seed, B=B, Hq=64, Hkv=8, seq_lens=[T] * B, dtype="bf16",
-                     n_outliers=3, mu_tokens=2048, table_policy="interleaved")
+                     n_outliers=3, mu_tokens=2048, table_policy="interleaved", rotation=rotation)
 
 
 def list_cases() -> List[str]:

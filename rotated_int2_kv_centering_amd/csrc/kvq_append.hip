@@ -105,17 +105,22 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
 // ---------------------------------------------------------------------------
 // Bulk path (n_tokens >= kBulkMin, raw bf16/fp32 input): workgroups of 8
 // waves, each bound to one (KV head, tensor) and striding over its tiles of
-// 512 tokens.  R is staged once in LDS
+// 512 tokens.  Dense R (kRot = 0) is staged once in LDS
 // as split-fp16 MFMA operands (kvq_rot.h); each wave rotates 16 tokens at a
-// time on the matrix cores, passes the rotated rows through its own LDS rows,
-// and quantizes them with one lane per (token, 32-channel group)
-// (kvq_quant.h: q2_group32), packing the K and V words across lanes.
+// time on the matrix cores.  A Hadamard R (kRot = 1) is applied in registers:
+// lane (row, kq) holds columns 32 kb + 8 kq + e of one token, so the seven
+// butterfly stages run on column bits 0-2 (e) and 5-6 (kb) inside the lane and
+// on bits 3-4 (kq) across lanes 16 and 32 apart, in the stage order of wht128,
+// which makes the result bitwise that of the tiled kernel.  Either way the
+// wave passes the rotated rows through its own LDS rows and quantizes them
+// with one lane per (token, 32-channel group) (kvq_quant.h: q2_group32),
+// packing the K and V words across lanes.
 constexpr int kBulkThreads = 512;
 constexpr int kBulkWaves = kBulkThreads / 64;
 constexpr int kBulkRounds = 4;                        // 16-token tiles per wave
 constexpr int kBulkTile = 16 * kBulkWaves * kBulkRounds;  // tokens per workgroup
 
-template <int kIn>  // 0 = bf16, 1 = fp32
+template <int kIn, int kRot>  // kIn: 0 = bf16, 1 = fp32; kRot: 0 = dense R, 1 = Hadamard signs
 __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
     uint8_t* __restrict__ pool, int num_pages, int num_kv_heads, const void* __restrict__ k_in,
     const void* __restrict__ v_in, int n_tokens, const int32_t* __restrict__ slots, const float* __restrict__ mu,
@@ -125,19 +130,22 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  __shared__ half8 s_op[32 * 2 * 64];                          // R operands, 64 KB
+  __shared__ half8 s_op[kRot == 0 ? 32 * 2 * 64 : 1];          // R operands, 64 KB (dense R only)
   __shared__ float s_x[kBulkWaves][16][kHeadDim + 4];          // rotated rows of each wave's 16 tokens
 
-  stage_rotation((tensor == 0 ? r_k : r_v) + static_cast<size_t>(h) * kHeadDim * kHeadDim, s_op, wave, kBulkWaves,
-                 lane);
-  // this lane's A columns 32 kb + 8 kq + e; key centre (fp32) or 0
+  if (kRot == 0)
+    stage_rotation((tensor == 0 ? r_k : r_v) + static_cast<size_t>(h) * kHeadDim * kHeadDim, s_op, wave, kBulkWaves,
+                   lane);
+  // this lane's A columns 32 kb + 8 kq + e; key centre (fp32) or 0, and the Hadamard signs
   const int kq = lane >> 4, row = lane & 15;
-  float cen[4][8];
+  float cen[4][8], sgn[4][8];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int e = 0; e < 8; ++e) {
       cen[kb][e] = (tensor == 0 && mu != nullptr) ? mu[h * kHeadDim + 32 * kb + 8 * kq + e] : 0.0f;
+      sgn[kb][e] = kRot == 1 ? (tensor == 0 ? r_k : r_v)[h * kHeadDim + 32 * kb + 8 * kq + e] : 0.0f;
+    }
   __syncthreads();
 
   const void* src = tensor == 0 ? k_in : v_in;
@@ -167,6 +175,7 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
       const int r0 = n0 + 16 * (kBulkWaves * m + wave);  // this wave's first token
       if (m + 1 < kBulkRounds) load_raw(m + 1, next);
       half8 a_hi[4], a_lo[4];
+      float ah[4][8];  // Hadamard: the centred, sign-flipped row values
   #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         float a[8];
@@ -185,18 +194,68 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
         }
   #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          _Float16 hh, ll;
-          split_f16(a[e] - cen[kb][e], hh, ll);  // key centering (fp32); values use centre 0
-          a_hi[kb][e] = hh;
-          a_lo[kb][e] = ll;
+          if (kRot == 0) {
+            _Float16 hh, ll;
+            split_f16(a[e] - cen[kb][e], hh, ll);  // key centering (fp32); values use centre 0
+            a_hi[kb][e] = hh;
+            a_lo[kb][e] = ll;
+          } else {
+            ah[kb][e] = (a[e] - cen[kb][e]) * sgn[kb][e];
+          }
         }
       }
-      float4v C[8];
-      rotate16(a_hi, a_lo, s_op, lane, C);
+      if (kRot == 0) {
+        float4v C[8];
+        rotate16(a_hi, a_lo, s_op, lane, C);
   #pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
+        for (int nt = 0; nt < 8; ++nt)
   #pragma unroll
-        for (int i = 0; i < 4; ++i) s_x[wave][4 * (lane >> 4) + i][16 * nt + (lane & 15)] = C[nt][i];
+          for (int i = 0; i < 4; ++i) s_x[wave][4 * (lane >> 4) + i][16 * nt + (lane & 15)] = C[nt][i];
+      } else {
+        // stage k pairs column c (bit k clear) with c + 2^k: (lo, hi) -> (lo + hi, lo - hi)
+  #pragma unroll
+        for (int k = 0; k < 3; ++k)  // column bits 0-2: e
+  #pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+  #pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if ((e & (1 << k)) == 0) {
+                const float lo = ah[kb][e], hi = ah[kb][e | (1 << k)];
+                ah[kb][e] = lo + hi;
+                ah[kb][e | (1 << k)] = lo - hi;
+              }
+  #pragma unroll
+        for (int k = 3; k < 5; ++k) {  // column bits 3-4: kq, lane bits 4-5
+          const int lb = 16 << (k - 3);
+  #pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+  #pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float pv = __shfl_xor(ah[kb][e], lb);
+              ah[kb][e] = (lane & lb) ? pv - ah[kb][e] : ah[kb][e] + pv;
+            }
+        }
+  #pragma unroll
+        for (int k = 5; k < 7; ++k)  // column bits 5-6: kb
+  #pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+            if ((kb & (1 << (k - 5))) == 0) {
+  #pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const float lo = ah[kb][e], hi = ah[kb | (1 << (k - 5))][e];
+                ah[kb][e] = lo + hi;
+                ah[kb | (1 << (k - 5))][e] = lo - hi;
+              }
+            }
+  #pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          float* dst = &s_x[wave][row][32 * kb + 8 * kq];
+          *reinterpret_cast<float4v*>(dst) = float4v{ah[kb][0] * kInvSqrt128, ah[kb][1] * kInvSqrt128,
+                                                     ah[kb][2] * kInvSqrt128, ah[kb][3] * kInvSqrt128};
+          *reinterpret_cast<float4v*>(dst + 4) = float4v{ah[kb][4] * kInvSqrt128, ah[kb][5] * kInvSqrt128,
+                                                         ah[kb][6] * kInvSqrt128, ah[kb][7] * kInvSqrt128};
+        }
+      }
 
       // Quantize-pack this wave's 16 tokens: lane (token r, group g) holds the
       // 32 channels of group g of token r.  The rows were written by this wave
@@ -291,17 +350,16 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
                          int n_tokens, const int32_t* slots, const float* mu, const float* r_k, const float* r_v,
                          float* rot_out, float clip, int rot_kind, hipStream_t stream) {
   (void)hipGetLastError();  // report only this call's launch errors, not stale ones
-  if (in_kind != 2 && n_tokens >= kBulkMin && rot_kind == 0) {  // the matrix-core path takes a dense R
-    // about one workgroup per compute unit in all, each staging its R once
+  if (in_kind != 2 && n_tokens >= kBulkMin) {
+    // about one workgroup per compute unit in all (each staging its dense R once;
+    // over 128 VGPRs per lane, one 8-wave workgroup fills a compute unit)
     const int n_tiles = (n_tokens + kBulkTile - 1) / kBulkTile;
     const int per = std::max(1, std::min(n_tiles, (256 + 2 * num_kv_heads - 1) / (2 * num_kv_heads)));
     const dim3 bgrid(per, num_kv_heads, 2);
-    if (in_kind == 0)
-      hipLaunchKernelGGL(append_bulk_kernel<0>, bgrid, dim3(kBulkThreads), 0, stream, pool, num_pages, num_kv_heads, k,
-                         v, n_tokens, slots, mu, r_k, r_v, rot_out, clip);
-    else
-      hipLaunchKernelGGL(append_bulk_kernel<1>, bgrid, dim3(kBulkThreads), 0, stream, pool, num_pages, num_kv_heads, k,
-                         v, n_tokens, slots, mu, r_k, r_v, rot_out, clip);
+    auto kern = in_kind == 0 ? (rot_kind == 0 ? append_bulk_kernel<0, 0> : append_bulk_kernel<0, 1>)
+                             : (rot_kind == 0 ? append_bulk_kernel<1, 0> : append_bulk_kernel<1, 1>);
+    hipLaunchKernelGGL(kern, bgrid, dim3(kBulkThreads), 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens, slots,
+                       mu, r_k, r_v, rot_out, clip);
     return hipGetLastError();
   }
   const dim3 grid((n_tokens + kAppendTile - 1) / kAppendTile, num_kv_heads, 2);

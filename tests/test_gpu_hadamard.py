@@ -124,3 +124,19 @@ def test_full_size_hadamard_sampled_heads():
     ref = O.decode_attention(case.q, dc.pool_np(), case.Hkv, case.page_table, case.seq_lens, r_k, r_v, heads=heads)
     for b, j in heads:
         assert max_abs_rel(got[b, j], ref[b, j]) <= TOL, j
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_bulk_append_equals_tiled_append(dtype):
+    """One call over >= 64 tokens takes the bulk kernel (transform in registers), calls
+    of 32 tokens the tiled one (transform through wht128): the same stage order gives
+    the same bytes, and rot_out matches row for row."""
+    dev = require_gpu()
+    case = I.make_case("hb", 97, B=3, Hq=8, Hkv=2, seq_lens=[700, 33, 290], dtype=dtype, table_policy="interleaved",
+                       rotation="hadamard")
+    bulk = DeviceCase(case, dev)
+    rot_b = bulk.append(rot_out=True).cpu().numpy()
+    tiled = DeviceCase(case, dev)
+    rot_t = tiled.append(rot_out=True, chunk=32).cpu().numpy()
+    np.testing.assert_array_equal(rot_b, rot_t)
+    np.testing.assert_array_equal(bulk.pool_np(), tiled.pool_np())
