@@ -22,8 +22,8 @@ Quantization* (arXiv 2608.02691):
 Readings where the page leaves a step open (each is listed with its reason in
 the design notes of the repository):
 
-* Q2 is asymmetric with group size G = 32 consecutive rotated channels of
-  one token and clip ratio c (default 1): with mn, mx = c*min, c*max,
+* Q2 is asymmetric with group size G (32 by default; 64 or 128) consecutive
+  rotated channels of one token and clip ratio c (default 1): with mn, mx = c*min, c*max,
   scale s = (mx - mn)/3, zero z = mn, code = clamp(round_half_even((x - z)/s),
   0, 3), level = z + s*code.
   The exact fp32/fp16 operation order is fixed in ``int2_quantize``.
@@ -128,10 +128,11 @@ def rotated_inputs(k, v, mu, r_k, r_v):
 
 
 # ---------------------------------------------------------- INT2 quantizer Q2
-def int2_quantize(x: np.ndarray, clip: float = 1.0):
-    """OptR §3.1: Q2(.; c, G=32), asymmetric, on fp32 rows of 128 channels.
+def int2_quantize(x: np.ndarray, clip: float = 1.0, group: int = GROUP):
+    """OptR §3.1: Q2(.; c, G), asymmetric, on fp32 rows of 128 channels.
 
-    ``x`` is float32 [..., 128].  Groups are 32 consecutive channels.  For each
+    ``x`` is float32 [..., 128].  Groups are G = ``group`` (32, 64 or 128)
+    consecutive channels.  For each
     group, with every operation in IEEE fp32 (round to nearest even) unless
     stated:
 
@@ -146,7 +147,7 @@ def int2_quantize(x: np.ndarray, clip: float = 1.0):
     names Q2(.; c, G) without defining c; reading: both ends of the group's
     range are scaled by c, as the rotation baselines it builds on clip KV
     groups); values past the narrowed range take the end codes.
-    Returns (codes uint8 [..., 128], scale float16 [..., 4], zero float16 [..., 4]).
+    Returns (codes uint8 [..., 128], scale float16 [..., 128/G], zero float16 [..., 128/G]).
     Inputs must be finite with group ranges inside the fp16 range.
     """
     x = np.asarray(x)
@@ -154,7 +155,8 @@ def int2_quantize(x: np.ndarray, clip: float = 1.0):
     assert np.isfinite(x).all(), "quantizer input must be finite"
     c = np.float32(clip)
     assert np.float32(0.0) < c <= np.float32(1.0), "clip ratio must be in (0, 1]"
-    xg = x.reshape(x.shape[:-1] + (N_GROUPS, GROUP))
+    assert group in (32, 64, 128), "group size must be 32, 64 or 128"
+    xg = x.reshape(x.shape[:-1] + (HEAD_DIM // group, group))
     mn = (xg.min(axis=-1) * c).astype(np.float32)
     mx = (xg.max(axis=-1) * c).astype(np.float32)
     rng = (mx - mn).astype(np.float32)
@@ -172,10 +174,20 @@ def int2_quantize(x: np.ndarray, clip: float = 1.0):
 
 
 def int2_dequantize(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
-    """Level of each code, z + s*code, exact in fp64 (OptR §3.1, four levels per group)."""
-    c = np.asarray(codes, np.float64).reshape(codes.shape[:-1] + (N_GROUPS, GROUP))
+    """Level of each code, z + s*code, exact in fp64 (OptR §3.1, four levels per group).
+    The group size is 128 / (number of scale entries per row)."""
+    n_g = np.asarray(s16).shape[-1]
+    c = np.asarray(codes, np.float64).reshape(codes.shape[:-1] + (n_g, HEAD_DIM // n_g))
     lv = np.asarray(z16, np.float64)[..., None] + np.asarray(s16, np.float64)[..., None] * c
     return lv.reshape(codes.shape)
+
+
+def meta_per_32(a: np.ndarray) -> np.ndarray:
+    """Per-group scales (or zeros) [..., 128/G] spread over the block's four
+    32-channel metadata entries [..., 4]: each entry holds the pair of the group
+    containing its channels (the block layout keeps four pairs for every G)."""
+    a = np.asarray(a)
+    return np.repeat(a, N_GROUPS // a.shape[-1], axis=-1)
 
 
 # ------------------------------------------------------------ pack / unpack
@@ -271,15 +283,16 @@ def block_view(pool: np.ndarray, page: int, h: int, num_kv_heads: int) -> np.nda
 
 # ------------------------------------------------------------- quantize-append
 def quantize_append(pool: np.ndarray, num_kv_heads: int, slots, x: np.ndarray, w: np.ndarray,
-                    clip: float = 1.0) -> None:
+                    clip: float = 1.0, group: int = GROUP) -> None:
     """Quantize rotated fp32 rows and store them at the given cache slots.
 
     ``x``/``w`` are float32 [n, H_kv, 128] (already centred and rotated);
-    ``slots[n]`` = page*16 + offset, all distinct; ``clip`` is Q2's clip ratio.
-    Writes ``pool`` (uint8) in place.
+    ``slots[n]`` = page*16 + offset, all distinct; ``clip`` and ``group`` are
+    Q2's clip ratio c and group size G.  Writes ``pool`` (uint8) in place.
     """
-    kc, ks, kz = int2_quantize(x, clip)
-    vc, vs, vz = int2_quantize(w, clip)
+    kc, ks, kz = int2_quantize(x, clip, group)
+    vc, vs, vz = int2_quantize(w, clip, group)
+    ks, kz, vs, vz = (meta_per_32(a) for a in (ks, kz, vs, vz))
     slots = np.asarray(slots, np.int64)
     assert len(np.unique(slots)) == len(slots), "slots must be distinct"
     pages = slots // PAGE
@@ -291,12 +304,12 @@ def quantize_append(pool: np.ndarray, num_kv_heads: int, slots, x: np.ndarray, w
                        block=block_view(pool, page, h, num_kv_heads), slots=offs)
 
 
-def append_tokens(pool, num_kv_heads, slots, k, v, mu, r_k, r_v, clip: float = 1.0) -> None:
+def append_tokens(pool, num_kv_heads, slots, k, v, mu, r_k, r_v, clip: float = 1.0, group: int = GROUP) -> None:
     """Full write path: centre keys, rotate K and V, quantize, pack (OptR §1, §3.1 Eq. (4))."""
     check_orthogonal_all(r_k)
     check_orthogonal_all(r_v)
     x, w = rotated_inputs(k, v, mu, r_k, r_v)
-    quantize_append(pool, num_kv_heads, slots, x, w, clip)
+    quantize_append(pool, num_kv_heads, slots, x, w, clip, group)
 
 
 def check_orthogonal_all(r: np.ndarray, tol: float = 1e-6) -> None:

@@ -616,3 +616,83 @@ def test_hadamard_rotation_matches_sylvester_and_fwht():
     plain = O.hadamard_rotation(np.ones((1, 128)))[0]
     np.testing.assert_allclose(plain @ plain, np.eye(128), atol=1e-14)
     np.testing.assert_array_equal(plain, plain.T)
+
+
+# ------------------------------------------------ Q2 group size G = 64, 128
+def _group_row():
+    """One row whose 32-channel halves have different ranges, so G = 32, 64 and 128
+    give different scales: channels 0-31 alternate 0, 3; 32-63 alternate -3, 0;
+    64-95 alternate 10, 10.75; 96-127 alternate 10.25, 10.5 (all exact in fp16)."""
+    alt = lambda a, b: np.where(np.arange(32) % 2 == 0, a, b)
+    return np.concatenate([alt(0.0, 3.0), alt(-3.0, 0.0), alt(10.0, 10.75), alt(10.25, 10.5)]).astype(np.float32)[None]
+
+
+def test_quantizer_group_sizes_hand_derived():
+    """Hand-derived codes of _group_row for each G (closed forms, no quantizer call):
+    G = 64: group 0 spans [-3, 3]: s = 2, z = -3, levels -3, -1, 1, 3, so 0 -> 1.5 -> 2
+            (half to even), 3 -> 3, -3 -> 0; group 1 spans [10, 10.75]: s = 0.25, z = 10,
+            so 10 -> 0, 10.75 -> 3, 10.25 -> 1, 10.5 -> 2.
+    G = 128: one group spanning [-3, 10.75]: s32 = 13.75 / 3 = 4.58333..., fp16 of it is
+            1173 * 2^-8 = 4.58203125, z = -3; (x + 3) / s = 0, 0.655, 1.309, 2.837, 2.892,
+            2.946, 3.0017 for x = -3, 0, 3, 10, 10.25, 10.5, 10.75: codes 0, 1, 1, 3, 3, 3, 3.
+    G = 32: channels 0-31 alone span [0, 3]: s = 1, z = 0, so 0 -> 0 (unlike G = 64)."""
+    x = _group_row()
+    alt = lambda a, b: np.where(np.arange(32) % 2 == 0, a, b)
+    c64, s64, z64 = O.int2_quantize(x, group=64)
+    np.testing.assert_array_equal(s64[0], np.array([2.0, 0.25], np.float16))
+    np.testing.assert_array_equal(z64[0], np.array([-3.0, 10.0], np.float16))
+    np.testing.assert_array_equal(c64[0], np.concatenate([alt(2, 3), alt(0, 2), alt(0, 3), alt(1, 2)]))
+    c128, s128, z128 = O.int2_quantize(x, group=128)
+    assert s128[0, 0] == np.float16(4.58203125) and z128[0, 0] == np.float16(-3.0)
+    np.testing.assert_array_equal(c128[0], np.concatenate([alt(1, 1), alt(0, 1), alt(3, 3), alt(3, 3)]))
+    c32, s32, _ = O.int2_quantize(x, group=32)
+    assert s32[0, 0] == np.float16(1.0) and c32[0, 0] == 0 and c32[0, 1] == 3
+
+
+def test_quantizer_group_sizes_nearest_level_and_shared_metadata():
+    """For G = 64 and 128: four levels per group, each code the nearest level (brute
+    force), G = 32 the default; a packed block repeats each group's pair over its
+    32-channel metadata entries, and unpacking gives back the same levels."""
+    rng = np.random.default_rng(41)
+    x = np.concatenate([_random_rows(rng, 40), _random_rows(rng, 24, 5.0, -1.0)])
+    np.testing.assert_array_equal(O.int2_quantize(x)[0], O.int2_quantize(x, group=32)[0])
+    for g in (64, 128):
+        codes, s16, z16 = O.int2_quantize(x, group=g)
+        assert s16.shape == (64, 128 // g)
+        xg = x.reshape(64, 128 // g, g).astype(np.float64)
+        levels = z16.astype(np.float64)[..., None, None] + s16.astype(np.float64)[..., None, None] * np.arange(4)
+        dist = np.abs(xg[..., None] - levels)
+        got = np.take_along_axis(dist, codes.reshape(64, 128 // g, g)[..., None].astype(np.int64), -1)[..., 0]
+        tol = 4 * np.spacing(np.maximum(s16.astype(np.float32), np.float32(1e-30))).astype(np.float64)[..., None]
+        assert np.all(got <= dist.min(-1) + tol + 1e-12), g
+        # pack 16 rows into one block and read it back
+        blk = O.pack_block(codes[:16], O.meta_per_32(s16[:16]), O.meta_per_32(z16[:16]),
+                           codes[16:32], O.meta_per_32(s16[16:32]), O.meta_per_32(z16[16:32]))
+        kc, ks, kz, vc, vs, vz = O.unpack_block(blk)
+        for grp in range(4):
+            np.testing.assert_array_equal(ks[:, grp], s16[:16, grp * 32 // g])
+            np.testing.assert_array_equal(vz[:, grp], z16[16:32, grp * 32 // g])
+        np.testing.assert_array_equal(O.int2_dequantize(kc, ks, kz), O.int2_dequantize(codes[:16], s16[:16], z16[:16]))
+        np.testing.assert_array_equal(O.int2_dequantize(vc, vs, vz),
+                                      O.int2_dequantize(codes[16:32], s16[16:32], z16[16:32]))
+
+
+def test_decode_with_group_size_equals_attention_on_effective_kv():
+    """Decode over a pool written with G = 64 or 128 equals attention on the effective
+    K/V of Q2(.; 1, G), as for G = 32 (OptR §3.2, Eq. (5))."""
+    c = _tiny(B=2, Hq=8, Hkv=2, seq_lens=[50, 33], table_policy="permuted")
+    x, w = O.rotated_inputs(c.k, c.v, c.mu, c.r_k, c.r_v)
+    for g in (64, 128):
+        pool = np.zeros(O.pool_bytes(c.num_pages, c.Hkv), np.uint8)
+        O.append_tokens(pool, c.Hkv, c.slots, c.k, c.v, c.mu, c.r_k, c.r_v, group=g)
+        got = O.decode_attention(c.q, pool, c.Hkv, c.page_table, c.seq_lens, c.r_k, c.r_v)
+        kq = O.int2_dequantize(*O.int2_quantize(x, group=g))
+        vq = O.int2_dequantize(*O.int2_quantize(w, group=g))
+        for b in range(c.B):
+            sel = c.tok_seq == b
+            for j in range(c.Hq):
+                h = j // 4
+                k_eff = kq[sel, h] @ c.r_k[h].astype(np.float64).T + c.mu[h]
+                v_eff = vq[sel, h] @ c.r_v[h].astype(np.float64).T
+                ref = O.softmax_attention(c.q[b, j], k_eff, v_eff, 1 / np.sqrt(128))
+                np.testing.assert_allclose(got[b, j], ref, rtol=0, atol=1e-11)
