@@ -64,7 +64,7 @@ extern "C" {
 typedef enum {
   KVQ_OK = 0,
   KVQ_EINVAL = 1,       /* null pointer, negative size, inconsistent sizes    */
-  KVQ_EUNSUPPORTED = 2, /* geometry other than d=128, G=32, page 16, g<=16    */
+  KVQ_EUNSUPPORTED = 2, /* geometry other than d=128, G in {32,64,128}, page 16, g<=16 */
   KVQ_ENOSPACE = 3,     /* page pool too small / workspace too small          */
   KVQ_EHIP = 4          /* a HIP runtime call or kernel launch failed         */
 } kvq_status;
@@ -93,7 +93,10 @@ typedef enum { KVQ_ROT_DENSE = 0, KVQ_ROT_HADAMARD = 1 } kvq_rotation;
 typedef struct {
   int32_t num_kv_heads; /* H_kv >= 1                                          */
   int32_t head_dim;     /* must be 128                                        */
-  int32_t group_size;   /* must be 32                                         */
+  int32_t group_size;   /* Q2's group size G: 32, 64 or 128 consecutive rotated
+                           channels.  The block layout is the same for every G:
+                           it keeps one (scale, zero) pair per 32 channels, each
+                           holding the pair of the group containing them       */
   int32_t page_size;    /* must be 16                                         */
   int32_t num_pages;    /* pages in the pool                                  */
   void* pool;           /* device, kvq_pool_bytes(cache) bytes, 16-byte aligned */

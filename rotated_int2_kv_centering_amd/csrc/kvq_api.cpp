@@ -34,7 +34,7 @@ kvq_status hip_fail(hipError_t e, const char* what) {
 }
 
 constexpr int kHeadDim = 128;
-constexpr int kGroup = 32;
+constexpr int kGroupMetadata = 32;  // the block keeps one (scale, zero) pair per 32 channels
 constexpr int kPage = 16;
 constexpr size_t kBlockBytes = 1536;
 constexpr int kRowStride = 132;  // floats per split partial (acc[128], max, sum, pad)
@@ -46,9 +46,11 @@ constexpr long long kMaxContext = static_cast<long long>(kMaxPagesPerSplit) * kM
 
 kvq_status check_cache(const kvq_cache* c) {
   if (c == nullptr) return fail(KVQ_EINVAL, "cache is NULL");
-  if (c->head_dim != kHeadDim || c->group_size != kGroup || c->page_size != kPage)
-    return fail(KVQ_EUNSUPPORTED, "unsupported geometry head_dim=%d group_size=%d page_size=%d (need 128/32/16)",
-                c->head_dim, c->group_size, c->page_size);
+  if (c->head_dim != kHeadDim || c->page_size != kPage ||
+      (c->group_size != kGroupMetadata && c->group_size != 2 * kGroupMetadata && c->group_size != kHeadDim))
+    return fail(KVQ_EUNSUPPORTED,
+                "unsupported geometry head_dim=%d group_size=%d page_size=%d (need 128, 32/64/128, 16)", c->head_dim,
+                c->group_size, c->page_size);
   if (c->num_kv_heads < 1) return fail(KVQ_EINVAL, "num_kv_heads=%d must be >= 1", c->num_kv_heads);
   if (c->num_pages < 0) return fail(KVQ_EINVAL, "num_pages=%d must be >= 0", c->num_pages);
   if (static_cast<long long>(c->num_pages) * kPage > 0x7fffffffLL)
@@ -285,6 +287,7 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
   a.v_new = stepping ? v_new : nullptr;
   a.kv_kind = kv_dtype == KVQ_BF16 ? 0 : 1;
   a.clip = clip_of(cache);
+  a.gsize = cache->group_size;
   a.rot_kind = cache->rotation;
   a.mu = mu;
   hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_begin),
@@ -318,7 +321,7 @@ kvq_status kvq_quant_append(const kvq_cache* cache, const void* k, const void* v
   const int kind = in_dtype == KVQ_BF16 ? 0 : (in_dtype == KVQ_F32 ? 1 : 2);
   hipError_t e = kvq::launch_append(static_cast<uint8_t*>(cache->pool), cache->num_pages, cache->num_kv_heads, k, v,
                                     kind, n_tokens, slots, mu, r_k, r_v, rot_out, clip_of(cache), cache->rotation,
-                                    static_cast<hipStream_t>(stream));
+                                    cache->group_size, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "quant_append launch");
   return KVQ_OK;
 }

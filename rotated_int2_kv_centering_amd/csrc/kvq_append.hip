@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     uint8_t* __restrict__ pool, int num_pages, int num_kv_heads, const void* __restrict__ k_in,
     const void* __restrict__ v_in, int n_tokens, const int32_t* __restrict__ slots, const float* __restrict__ mu,
     const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out, float clip,
-    int rot_kind) {
+    int rot_kind, int gsize) {
   const int tile = blockIdx.x;
   const int h = blockIdx.y;
   const int tensor = blockIdx.z;  // 0: key, 1: value
@@ -85,11 +85,22 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
   }
   __syncthreads();
 
+  // G = 128: a group spans both waves of a half; each wave's range of each token first
+  __shared__ float2 s_rng[kAppendTile][2];
+  if (gsize == 128) {
+    for (int tt = 0; tt < kAppendTile / 2; ++tt) {
+      const int t = (kAppendTile / 2) * half + tt;
+      const float2 r = q2_wave_range(xpart[0][t][j], 64);
+      if ((j & 63) == 0) s_rng[t][j >> 6] = r;
+    }
+    __syncthreads();
+  }
+
   // Quantize and pack: this half handles tokens 8*half .. 8*half + 7; within it,
   // wave w2 = (tid >> 6) & 1 holds channels 64*w2 .. 64*w2 + 63 (groups 2*w2, 2*w2 + 1).
 #pragma unroll
   for (int tt = 0; tt < kAppendTile / 2; ++tt) {
-    const int t = 8 * half + tt;
+    const int t = (kAppendTile / 2) * half + tt;
     const int n = n0 + t;
     const int slot = t < nt ? slots[n] : -1;
     if (slot < 0 || slot >= num_pages * kPage) continue;  // uniform over the half; bad slots are skipped
@@ -98,7 +109,14 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
 
     const int page = slot >> 4;
     uint8_t* block = pool + (static_cast<size_t>(page) * num_kv_heads + h) * kBlockBytes;
-    (void)q2_pack_channel(xv, j, tensor, block, slot & 15, clip);
+    float2 r;
+    if (gsize == 128) {
+      const float2 a = s_rng[t][0], b = s_rng[t][1];
+      r = float2{fminf(a.x, b.x), fmaxf(a.y, b.y)};
+    } else {
+      r = q2_wave_range(xv, gsize);
+    }
+    (void)q2_pack_channel(xv, j, tensor, block, slot & 15, clip, r.x, r.y);
   }
 }
 
@@ -124,7 +142,7 @@ template <int kIn, int kRot>  // kIn: 0 = bf16, 1 = fp32; kRot: 0 = dense R, 1 =
 __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
     uint8_t* __restrict__ pool, int num_pages, int num_kv_heads, const void* __restrict__ k_in,
     const void* __restrict__ v_in, int n_tokens, const int32_t* __restrict__ slots, const float* __restrict__ mu,
-    const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out, float clip) {
+    const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out, float clip, int gsize) {
   const int h = blockIdx.y;
   const int tensor = blockIdx.z;  // 0: key, 1: value
   const int tid = threadIdx.x;
@@ -275,7 +293,7 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
         x[4 * u + 3] = q4[3];
       }
       uint32_t pair, code[32];
-      q2_group32(x, clip, pair, code);
+      q2_group32(x, clip, gsize, pair, code);
       const int slot = n < n_tokens ? slots[n] : -1;
       const bool ok = slot >= 0 && slot < num_pages * kPage;  // same for the token's four lanes
       if (rot_out != nullptr && n < n_tokens) {
@@ -348,7 +366,7 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
 
 hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const void* k, const void* v, int in_kind,
                          int n_tokens, const int32_t* slots, const float* mu, const float* r_k, const float* r_v,
-                         float* rot_out, float clip, int rot_kind, hipStream_t stream) {
+                         float* rot_out, float clip, int rot_kind, int gsize, hipStream_t stream) {
   (void)hipGetLastError();  // report only this call's launch errors, not stale ones
   if (in_kind != 2 && n_tokens >= kBulkMin) {
     // about one workgroup per compute unit in all (each staging its dense R once;
@@ -359,7 +377,7 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
     auto kern = in_kind == 0 ? (rot_kind == 0 ? append_bulk_kernel<0, 0> : append_bulk_kernel<0, 1>)
                              : (rot_kind == 0 ? append_bulk_kernel<1, 0> : append_bulk_kernel<1, 1>);
     hipLaunchKernelGGL(kern, bgrid, dim3(kBulkThreads), 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens, slots,
-                       mu, r_k, r_v, rot_out, clip);
+                       mu, r_k, r_v, rot_out, clip, gsize);
     return hipGetLastError();
   }
   const dim3 grid((n_tokens + kAppendTile - 1) / kAppendTile, num_kv_heads, 2);
@@ -367,15 +385,15 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
   switch (in_kind) {
     case 0:
       hipLaunchKernelGGL(append_kernel<0>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,
-                         slots, mu, r_k, r_v, rot_out, clip, rot_kind);
+                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize);
       break;
     case 1:
       hipLaunchKernelGGL(append_kernel<1>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,
-                         slots, mu, r_k, r_v, rot_out, clip, rot_kind);
+                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize);
       break;
     default:
       hipLaunchKernelGGL(append_kernel<2>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,
-                         slots, mu, r_k, r_v, rot_out, clip, rot_kind);
+                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize);
       break;
   }
   return hipGetLastError();

@@ -227,6 +227,7 @@ void decode_kernel(const DecodeParams p) {
   // dequantized levels and per-head logits
   __shared__ float s_nrow[2][kHeadDim];
   __shared__ float s_hat[2][kHeadDim];
+  __shared__ float2 s_nrng[4];  // G = 128: the new token's range per wave
   __shared__ float s_nlog[kNH];
   // Page-pair ring [slot][wave][part][lane]: part 0/1 = 64 x 16 B codes of
   // page 0/1, part 2 = 32 x 16 B metadata of page 0 then of page 1.
@@ -513,11 +514,23 @@ void decode_kernel(const DecodeParams p) {
   }
   }  // dense R
   __syncthreads();
-  if (new_ok && tid < 2 * kHeadDim) {  // quantize-append the new token (two waves per tensor)
-    const int tensor = tid / kHeadDim;
-    const int pos = T - 1;
-    uint8_t* blk = p.pool + (static_cast<size_t>(s_pages[np - 1]) * H + h) * kBlockBytes;
-    s_hat[tensor][rc] = q2_pack_channel(s_nrow[tensor][rc], rc, tensor, blk, pos & (kPage - 1), p.clip);
+  if (new_ok) {  // quantize-append the new token (two waves per tensor); new_ok is uniform here
+    float2 rg = float2{0.0f, 0.0f};
+    if (tid < 2 * kHeadDim) rg = q2_wave_range(s_nrow[tid / kHeadDim][rc], p.gsize);
+    if (p.gsize == 128) {  // a group spans the tensor's two waves
+      if (tid < 2 * kHeadDim && lane == 0) s_nrng[wave] = rg;
+      __syncthreads();
+      if (tid < 2 * kHeadDim) {
+        const float2 a = s_nrng[wave & ~1], b = s_nrng[wave | 1];
+        rg = float2{fminf(a.x, b.x), fmaxf(a.y, b.y)};
+      }
+    }
+    if (tid < 2 * kHeadDim) {
+      const int tensor = tid / kHeadDim;
+      const int pos = T - 1;
+      uint8_t* blk = p.pool + (static_cast<size_t>(s_pages[np - 1]) * H + h) * kBlockBytes;
+      s_hat[tensor][rc] = q2_pack_channel(s_nrow[tensor][rc], rc, tensor, blk, pos & (kPage - 1), p.clip, rg.x, rg.y);
+    }
   }
   for (int jh = wave; jh < kNH; jh += kW) {
     float am = fmaxf(fabsf(s_q[jh][lane]), fabsf(s_q[jh][lane + 64]));

@@ -57,12 +57,32 @@ __device__ __forceinline__ float wht128(float x, int c, float* xch) {
   return (c & 64) ? p - x : x + p;
 }
 
+// Range (min, max) of the Q2 group of channel j over the lanes of the calling
+// wave, for one token's rotated vector held as in q2_pack_channel: G = 32 is a
+// half-wave, G = 64 the whole wave; a G = 128 group spans both waves, whose
+// ranges the caller combines (min and max are exact in any order).
+__device__ __forceinline__ float2 q2_wave_range(float xv, int gsize) {
+  float mn = xv, mx = xv;
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, o));
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+  }
+  if (gsize > 32) {
+    mn = fminf(mn, __shfl_xor(mn, 32));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+  }
+  return float2{mn, mx};
+}
+
 // Quantizes channel j of one token's rotated vector and packs it into a block.
 // Called by the 128 threads j = 0..127 of one (token, KV head, tensor), laid
-// out as two whole waves (j = 64 * w2 + lane), so each 32-lane half-wave holds
-// one channel group.  `block` is the (page, KV head) block to write, or null to
-// only compute; `off` is the slot within the page (0..15); tensor 0 = K, 1 = V.
-// Returns the dequantized level of channel j.
+// out as two whole waves (j = 64 * w2 + lane), with (mn, mx) the unclipped
+// range of channel j's group (q2_wave_range).  `block` is the (page, KV head)
+// block to write, or null to only compute; `off` is the slot within the page
+// (0..15); tensor 0 = K, 1 = V.  The block keeps one metadata pair per 32
+// channels: for G > 32 each holds its group's pair.  Returns the dequantized
+// level of channel j.
 //
 // K code of slot s, channel c (kk = c/32, a = (c%32)/8, e = c%8): record
 // 16a + s, word K[kk/2], bit 2(4(kk%2) + e/2) + 16(e%2).  V code (t = c/16,
@@ -72,16 +92,11 @@ __device__ __forceinline__ float wht128(float x, int c, float* xch) {
 // A K code word and a metadata pair belong to one slot (plain stores); a V
 // code word holds codes of two slots, so it is updated with atomic and/or of
 // this slot's bits only, which keeps concurrent writes to other slots intact.
-__device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, uint8_t* block, int off, float clip) {
+__device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, uint8_t* block, int off, float clip,
+                                                float mn, float mx) {
   const int lane = j & 63;
   const int w2 = j >> 6;
   const int grp = j >> 5;
-  float mn = xv, mx = xv;
-#pragma unroll
-  for (int o = 16; o >= 1; o >>= 1) {
-    mn = fminf(mn, __shfl_xor(mn, o));
-    mx = fmaxf(mx, __shfl_xor(mx, o));
-  }
   mn *= clip;
   mx *= clip;
   // c*min and c*max are rounded to fp32 before anything else uses them (the
@@ -130,18 +145,29 @@ __device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, ui
   return fmaf(sc, static_cast<float>(code), z);
 }
 
-// Q2 of one 32-channel group held by one lane (the bulk path): the same
-// result as q2_pack_channel's arithmetic.  The code of each element is
+// Q2 of the 32 channels [32 g, 32 g + 32) of one token held by one lane (the
+// bulk path), lane 4 r + g for token r: the same result as q2_pack_channel's
+// arithmetic.  For G = 64 and 128 the range is combined over lanes g ^ 1 and
+// g ^ 2 (all lanes of the wave call it).  The code of each element is
 // rint(fl(t / s)) clamped to 0..3 with t = fl(x - z); it is taken from
 // q = fl(t * fl(1 / s)), which lies within 3 * 2^-24 |q| of fl(t / s), unless
 // q is within 2^-19 of a half-integer, where the two could round apart: such a
 // lane recomputes its group with the IEEE division.
-__device__ __forceinline__ void q2_group32(const float (&x)[32], float clip, uint32_t& pair, uint32_t (&code)[32]) {
+__device__ __forceinline__ void q2_group32(const float (&x)[32], float clip, int gsize, uint32_t& pair,
+                                           uint32_t (&code)[32]) {
   float mn = x[0], mx = x[0];
 #pragma unroll
   for (int c = 1; c < 32; ++c) {
     mn = fminf(mn, x[c]);
     mx = fmaxf(mx, x[c]);
+  }
+  if (gsize > 32) {
+    mn = fminf(mn, __shfl_xor(mn, 1));
+    mx = fmaxf(mx, __shfl_xor(mx, 1));
+  }
+  if (gsize > 64) {
+    mn = fminf(mn, __shfl_xor(mn, 2));
+    mx = fmaxf(mx, __shfl_xor(mx, 2));
   }
   mn *= clip;
   mx *= clip;

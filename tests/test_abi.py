@@ -149,6 +149,11 @@ def test_append_argument_validation(K):
     assert lib.kvq_quant_append(ctypes.byref(bad_geom), FAKE, FAKE, K.KVQ_BF16, 1, FAKE, None, FAKE, FAKE, None,
                                 None) == K.KVQ_EUNSUPPORTED
     assert "head_dim=64" in K.kvq_last_error()
+    for g in (16, 48, 256):  # Q2 group sizes other than 32, 64, 128
+        assert lib.kvq_quant_append(ctypes.byref(K.make_cache(2, 4, FAKE, group_size=g)), FAKE, FAKE, K.KVQ_BF16, 1,
+                                    FAKE, None, FAKE, FAKE, None, None) == K.KVQ_EUNSUPPORTED
+        assert f"group_size={g}" in K.kvq_last_error()
+        assert _decode(K, K.make_cache(1, 8, FAKE, group_size=g)) == K.KVQ_EUNSUPPORTED
     assert lib.kvq_quant_append(ctypes.byref(ok), FAKE, FAKE, 7, 1, FAKE, None, FAKE, FAKE, None,
                                 None) == K.KVQ_EUNSUPPORTED
     assert lib.kvq_quant_append(ctypes.byref(ok), FAKE, FAKE, K.KVQ_BF16, -1, FAKE, None, FAKE, FAKE, None,
