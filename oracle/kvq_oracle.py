@@ -540,3 +540,55 @@ def output_error_terms(q, keys, values, keys_q, values_q, w_o, scale=None):
     dy_v = (pt @ (np.asarray(values_q, np.float64) - values)) @ w_o.T
     e_rec = float(((keys - keys_q) ** 2).sum() + ((values - values_q) ** 2).sum())
     return yt - y, dy_k, dy_v, e_rec, float(((yt - y) ** 2).sum())
+
+
+def present_positions(table_row, seq_len: int, num_pages: int) -> np.ndarray:
+    """Mask [T] of the positions whose page is present (table entry in [0, num_pages))."""
+    T = int(seq_len)
+    n_pages = (T + PAGE - 1) // PAGE
+    pages = np.asarray(table_row[:n_pages], np.int64)
+    return np.repeat((pages >= 0) & (pages < num_pages), PAGE)[:T]
+
+
+def output_error(q, pool, num_kv_heads, page_table, seq_lens, k_seqs, v_seqs, mu, r_k, r_v, w_o,
+                 sm_scale=None, num_pages=None):
+    """OptR §3.2 Eq. (6)-(10) at the decode position of every sequence, from the packed cache (fp64).
+
+    Query head j of sequence b (KV head h = j // g) attends positions 0..T_b-1.
+    Exact keys/values are k_seqs[b][:, h], v_seqs[b][:, h]; the effective ones
+    (§3.1) are k~ = x_hat R_K^T + mu and v~ = w_hat R_V^T from the pool.
+    Positions on absent pages are left out of both, as in decode.  W_O,j is
+    columns [j d, (j + 1) d) of ``w_o`` [d_model, H_q d] (a model's output
+    projection, row-major).  Per (b, j) this is ``output_error_terms``.
+    Returns dy_k, dy_v [B, H_q, d_model], e_out [B, H_q] (Eq. (10)) and
+    e_rec [B, H_kv] (Eq. (9), the cache of sequence b and KV head h).
+    """
+    q = np.asarray(q, np.float64)
+    B, Hq, d = q.shape
+    g = Hq // num_kv_heads
+    sm_scale = 1.0 / np.sqrt(d) if sm_scale is None else float(sm_scale)
+    w_o = np.asarray(w_o, np.float64)
+    d_model = w_o.shape[0]
+    if num_pages is None:
+        num_pages = np.asarray(pool).size // (num_kv_heads * BLOCK_BYTES)
+    dy_k = np.zeros((B, Hq, d_model))
+    dy_v = np.zeros((B, Hq, d_model))
+    e_out = np.zeros((B, Hq))
+    e_rec = np.zeros((B, num_kv_heads))
+    for b in range(B):
+        T = int(seq_lens[b])
+        keep = present_positions(page_table[b], T, num_pages)
+        for h in range(num_kv_heads):
+            x_hat, w_hat = gather_sequence(pool, num_kv_heads, page_table[b], T, h, num_pages)
+            k_eff = x_hat @ np.asarray(r_k[h], np.float64).T + np.asarray(mu[h], np.float64)
+            v_eff = w_hat @ np.asarray(r_v[h], np.float64).T
+            k_ex = np.asarray(k_seqs[b], np.float64)[:T, h][keep]
+            v_ex = np.asarray(v_seqs[b], np.float64)[:T, h][keep]
+            if k_ex.shape[0] == 0:
+                continue
+            for j in range(h * g, (h + 1) * g):
+                w_oj = w_o[:, j * d:(j + 1) * d]
+                _, dk, dv, er, eo = output_error_terms(q[b, j], k_ex, v_ex, k_eff, v_eff, w_oj, sm_scale)
+                dy_k[b, j], dy_v[b, j], e_out[b, j] = dk, dv, eo
+                e_rec[b, h] = er
+    return dy_k, dy_v, e_out, e_rec

@@ -696,3 +696,96 @@ def test_decode_with_group_size_equals_attention_on_effective_kv():
                 v_eff = vq[sel, h] @ c.r_v[h].astype(np.float64).T
                 ref = O.softmax_attention(c.q[b, j], k_eff, v_eff, 1 / np.sqrt(128))
                 np.testing.assert_allclose(got[b, j], ref, rtol=0, atol=1e-11)
+
+
+# ----------------------------------------------- output-error evaluator (Eq. 6-10)
+def _eval_case(lens=(50, 0, 33), Hq=8, Hkv=2, d_model=96, seed=81):
+    c = _tiny(B=len(lens), Hq=Hq, Hkv=Hkv, seq_lens=list(lens), table_policy="permuted")
+    pool = np.zeros(O.pool_bytes(c.num_pages, c.Hkv), np.uint8)
+    O.append_tokens(pool, c.Hkv, c.slots, c.k, c.v, c.mu, c.r_k, c.r_v)
+    ks = [c.k[c.tok_seq == b] for b in range(c.B)]
+    vs = [c.v[c.tok_seq == b] for b in range(c.B)]
+    w_o = np.random.default_rng(seed).standard_normal((d_model, Hq * 128)) / np.sqrt(128)
+    return c, pool, ks, vs, w_o
+
+
+def test_output_error_matches_decode_and_plain_attention():
+    """dy_K + dy_V equals (decode read from the pool - exact attention) W_O,j^T: the
+    decode oracle works in the rotated basis (q R_K against x_hat), this one on the
+    effective keys in the original basis.  dy_K alone equals the exact values read
+    with the INT2-key probabilities minus exact attention; e_out = ||dy||^2; an empty
+    sequence gives zeros."""
+    c, pool, ks, vs, w_o = _eval_case()
+    dy_k, dy_v, e_out, e_rec = O.output_error(c.q, pool, c.Hkv, c.page_table, c.seq_lens, ks, vs, c.mu, c.r_k,
+                                              c.r_v, w_o)
+    o_q = O.decode_attention(c.q, pool, c.Hkv, c.page_table, c.seq_lens, c.r_k, c.r_v)
+    s = 1 / np.sqrt(128)
+    g = c.Hq // c.Hkv
+    for b in range(c.B):
+        for j in range(c.Hq):
+            h = j // g
+            w_oj = w_o[:, j * 128:(j + 1) * 128]
+            if c.seq_lens[b] == 0:
+                assert not dy_k[b, j].any() and not dy_v[b, j].any() and e_out[b, j] == 0 and e_rec[b, h] == 0
+                continue
+            o = O.softmax_attention(c.q[b, j], ks[b][:, h], vs[b][:, h], s)
+            np.testing.assert_allclose(dy_k[b, j] + dy_v[b, j], (o_q[b, j] - o) @ w_oj.T, rtol=0, atol=1e-10)
+            x_hat, _ = O.gather_sequence(pool, c.Hkv, c.page_table[b], c.seq_lens[b], h)
+            k_eff = x_hat @ c.r_k[h].astype(np.float64).T + c.mu[h]
+            o_kq = O.softmax_attention(c.q[b, j], k_eff, vs[b][:, h], s)
+            np.testing.assert_allclose(dy_k[b, j], (o_kq - o) @ w_oj.T, rtol=0, atol=1e-10)
+            dy = dy_k[b, j] + dy_v[b, j]
+            assert abs(e_out[b, j] - dy @ dy) <= 1e-9 * max(e_out[b, j], 1e-30)
+
+
+def test_output_error_reconstruction_term_per_token():
+    """e_rec (Eq. (9)) summed token by token: each slot unpacked alone, its levels
+    rotated back, mu added to the key; the squared distances to the exact rows."""
+    c, pool, ks, vs, w_o = _eval_case(lens=(37, 16))
+    *_, e_rec = O.output_error(c.q, pool, c.Hkv, c.page_table, c.seq_lens, ks, vs, c.mu, c.r_k, c.r_v, w_o)
+    for b in range(c.B):
+        for h in range(c.Hkv):
+            tot = 0.0
+            for t in range(int(c.seq_lens[b])):
+                page = int(c.page_table[b, t // 16])
+                kc, ksc, kz, vc, vsc, vz = O.unpack_block(O.block_view(pool, page, h, c.Hkv))
+                xk = O.int2_dequantize(kc[t % 16][None], ksc[t % 16][None], kz[t % 16][None])[0]
+                xv = O.int2_dequantize(vc[t % 16][None], vsc[t % 16][None], vz[t % 16][None])[0]
+                kt = xk @ c.r_k[h].astype(np.float64).T + c.mu[h]
+                vt = xv @ c.r_v[h].astype(np.float64).T
+                tot += ((ks[b][t, h] - kt) ** 2).sum() + ((vs[b][t, h] - vt) ** 2).sum()
+            assert abs(e_rec[b, h] - tot) <= 1e-10 * tot
+
+
+def test_output_error_leaves_out_absent_pages_and_exact_cache_gives_zero():
+    """An absent page's positions drop out of the exact and the INT2 readouts alike
+    (so e_rec shrinks by their terms); with the effective K/V passed as the exact
+    ones every term is zero."""
+    c, pool, ks, vs, w_o = _eval_case(lens=(40,))
+    table = c.page_table.copy()
+    table[0, 1] = c.num_pages + 7
+    full = O.output_error(c.q, pool, c.Hkv, c.page_table, c.seq_lens, ks, vs, c.mu, c.r_k, c.r_v, w_o)
+    cut = O.output_error(c.q, pool, c.Hkv, table, c.seq_lens, ks, vs, c.mu, c.r_k, c.r_v, w_o)
+    keep = np.r_[0:16, 32:40]
+    ks2 = [ks[0][keep]]
+    vs2 = [vs[0][keep]]
+    # the same as a sequence made of the present positions only (exact rows and cache rows)
+    for h in range(c.Hkv):
+        x_hat, w_hat = O.gather_sequence(pool, c.Hkv, table[0], 40, h)
+        assert x_hat.shape[0] == 24
+    assert cut[3][0].sum() < full[3][0].sum()
+    o_q = O.decode_attention(c.q, pool, c.Hkv, table, c.seq_lens, c.r_k, c.r_v)
+    for j in range(c.Hq):
+        h = j // (c.Hq // c.Hkv)
+        o = O.softmax_attention(c.q[0, j], ks2[0][:, h], vs2[0][:, h], 1 / np.sqrt(128))
+        np.testing.assert_allclose(cut[0][0, j] + cut[1][0, j], (o_q[0, j] - o) @ w_o[:, j * 128:(j + 1) * 128].T,
+                                   rtol=0, atol=1e-10)
+    # exact rows equal to the effective ones: no error at all
+    eff_k, eff_v = [], []
+    for h in range(c.Hkv):
+        x_hat, w_hat = O.gather_sequence(pool, c.Hkv, c.page_table[0], 40, h)
+        eff_k.append(x_hat @ c.r_k[h].astype(np.float64).T + c.mu[h])
+        eff_v.append(w_hat @ c.r_v[h].astype(np.float64).T)
+    z = O.output_error(c.q, pool, c.Hkv, c.page_table, c.seq_lens, [np.stack(eff_k, 1)], [np.stack(eff_v, 1)],
+                       c.mu, c.r_k, c.r_v, w_o)
+    assert max(np.abs(z[0]).max(), np.abs(z[1]).max(), z[2].max(), z[3].max()) < 1e-20
