@@ -167,6 +167,24 @@ kvq_status kvq_quant_append(const kvq_cache* cache, const void* k, const void* v
                             const float* r_v, float* rot_out, void* stream);
 
 /*
+ * kvq_quant_append_err - kvq_quant_append that also reports each token's
+ * squared quantization error, the per-token terms of E_rec (OptR section 3.2,
+ * Eq. (9)).
+ *
+ *   sq_err    device fp32 [n_tokens][H_kv][2][2], 16-byte aligned, or NULL:
+ *             entry [n][h][t][i] = sum over channels c in [64 i, 64 i + 64) of
+ *             (x_c - level_c)^2, the rotated quantizer input of tensor t (0 key,
+ *             1 value) minus its INT2 level.  R is orthogonal, so the two halves
+ *             add up to ||k - k~||^2 (or ||v - v~||^2) of the effective rows.
+ *             Tokens whose slot is skipped are not written.
+ * Every other argument, the bytes written to the cache and the errors are those
+ * of kvq_quant_append.
+ */
+kvq_status kvq_quant_append_err(const kvq_cache* cache, const void* k, const void* v, kvq_dtype in_dtype,
+                                int32_t n_tokens, const int32_t* slots, const float* mu, const float* r_k,
+                                const float* r_v, float* rot_out, float* sq_err, void* stream);
+
+/*
  * kvq_decode_workspace_bytes - device workspace needed by kvq_decode_attn for
  * the same (batch, num_q_heads, num_kv_heads, max_seq_len, num_splits).
  * num_splits 0 selects the automatic split plan.  Returns 0 on invalid input.
@@ -286,6 +304,57 @@ kvq_status kvq_decode_step(const kvq_cache* cache, const void* k_new, const void
                            int32_t max_seq_len, const float* r_k, const float* r_v, float sm_scale, void* out,
                            kvq_dtype out_dtype, void* workspace, size_t workspace_bytes, int32_t num_splits,
                            const kvq_window* window, void* stream, void* ev_begin, void* ev_end);
+
+/*
+ * kvq_output_error_workspace_bytes - device workspace needed by
+ * kvq_output_error for the same (batch, num_q_heads, num_kv_heads,
+ * max_seq_len, d_model); 0 on invalid input (batch above 64 included).  It
+ * holds ticket counters, split partials and the readout differences; zero-fill
+ * it before its first use (completed calls leave the counters at zero).
+ */
+size_t kvq_output_error_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t max_seq_len, int32_t d_model);
+
+/*
+ * kvq_output_error - OptR section 3.2, Eq. (6)-(10): the output-space error the
+ * INT2 cache causes at the decode position of each sequence, split into its
+ * key-induced and value-induced terms (Eq. (8)).  For query head j of sequence
+ * b (KV head h = j / g), over the positions s < T_b on present pages:
+ *   p  = softmax_s(sm_scale <q_j, k_s>)            (exact keys, Eq. (1))
+ *   p~ = softmax_s(sm_scale <q_j, k~_s>)           (effective keys, Eq. (5))
+ *   dy_k[b][j] = (sum_s (p~_s - p_s) v_s) W_O,j^T   (key-induced)
+ *   dy_v[b][j] = (sum_s p~_s (v~_s - v_s)) W_O,j^T  (value-induced)
+ *   e_out[b][j] = ||dy_k + dy_v||^2                 (Eq. (10))
+ *   e_rec[b][h] = sum_s (||k_s - k~_s||^2 + ||v_s - v~_s||^2)  (Eq. (9))
+ * with k~ = x_hat R_K^T + mu and v~ = w_hat R_V^T read from the cache.
+ *
+ *   cache, q, q_dtype, batch (<= 64), num_q_heads, page_table, max_pages,
+ *   seq_lens, max_seq_len, r_k, r_v, sm_scale: as in kvq_decode_attn.
+ *   k, v         device [rows][H_kv][128] of kv_dtype (bf16 or fp32), 16-byte
+ *                aligned: the exact keys and values; position s of sequence b
+ *                is row row_offsets[b] + s.
+ *   row_offsets  device int64 [batch].
+ *   sq_err       device fp32 [rows][H_kv][2][2] from kvq_quant_append_err
+ *                (same row order), or NULL: e_rec is then written as 0.
+ *   w_o          device [d_model][H_q * 128] of w_dtype (bf16 or fp32), 16-byte
+ *                aligned: the layer's output projection, W_O,j = columns
+ *                [128 j, 128 j + 128).
+ *   dy_k, dy_v   device fp32 [batch][H_q][d_model].
+ *   e_out        device fp32 [batch][H_q].   e_rec  device fp32 [batch][H_kv].
+ *   workspace    device, kvq_output_error_workspace_bytes(...) bytes, 16-byte
+ *                aligned, zero before first use.
+ * Two kernels on `stream`, no allocation, no synchronization.  mu is not
+ * needed: <q_j, mu> shifts all effective logits of head j equally.
+ * Errors: KVQ_EINVAL (NULL arguments, misalignment, bad shapes), KVQ_EUNSUPPORTED
+ * (dtype, g > 16, batch > 64), KVQ_ENOSPACE (workspace too small), KVQ_EHIP.
+ */
+kvq_status kvq_output_error(const kvq_cache* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
+                            int32_t num_q_heads, const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
+                            int32_t max_seq_len, const void* k, const void* v, kvq_dtype kv_dtype,
+                            const int64_t* row_offsets, const float* sq_err, const float* r_k, const float* r_v,
+                            float sm_scale, const void* w_o, kvq_dtype w_dtype, int32_t d_model, float* dy_k,
+                            float* dy_v, float* e_out, float* e_rec, void* workspace, size_t workspace_bytes,
+                            void* stream);
 
 /*
  * kvq_window_bytes - bytes of the window buffer of `window` for num_kv_heads

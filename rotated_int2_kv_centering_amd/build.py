@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_eval.hip"]
 # measurement aid (HBM read-rate probe), a library of its own outside the decode path
 PROBE_LIB = os.path.join(HERE, "libkvq_probe.so")
 PROBE_SOURCES = ["hbm_probe.hip"]

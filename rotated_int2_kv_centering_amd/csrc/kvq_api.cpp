@@ -296,6 +296,37 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
   return KVQ_OK;
 }
 
+// Output-error evaluator: split plan and workspace layout.
+struct EvalPlan {
+  int n_splits, pages_per_split, n_hc, n_chunks;
+  size_t counters_off, proj_counters_off, part_off, dobuf_off, echunk_off, total;
+};
+
+bool make_eval_plan(int batch, int num_q_heads, int num_kv_heads, int max_seq_len, int d_model, EvalPlan* e) {
+  if (batch < 0 || batch > kvq::kMaxEvalBatch || num_q_heads < 1 || num_kv_heads < 1 ||
+      num_q_heads % num_kv_heads != 0 || max_seq_len < 0 || d_model < 1)
+    return false;
+  const int g = num_q_heads / num_kv_heads;
+  if (g > kMaxGroup) return false;
+  const int n_pages = (max_seq_len + kPage - 1) / kPage;
+  // about one workgroup per compute unit in all
+  const int want = std::max(1, (256 + batch * num_kv_heads - 1) / std::max(1, batch * num_kv_heads));
+  int n_splits = std::max(1, std::min({want, std::max(n_pages, 1), kvq::kMaxEvalSplits}));
+  e->pages_per_split = std::max(1, (n_pages + n_splits - 1) / n_splits);
+  e->n_splits = std::max(1, (n_pages + e->pages_per_split - 1) / e->pages_per_split);
+  e->n_hc = (g + kvq::kEvHeads - 1) / kvq::kEvHeads;
+  e->n_chunks = (d_model + kvq::kProjRows - 1) / kvq::kProjRows;
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  const size_t slots = static_cast<size_t>(batch) * num_kv_heads * e->n_hc;
+  e->counters_off = 0;
+  e->proj_counters_off = up(slots * 4);
+  e->part_off = e->proj_counters_off + up(static_cast<size_t>(num_q_heads) * 4);
+  e->dobuf_off = e->part_off + up(slots * e->n_splits * kvq::kEvHeads * kvq::kEvPartStride * 4);
+  e->echunk_off = e->dobuf_off + up(static_cast<size_t>(batch) * num_q_heads * 2 * kHeadDim * 4);
+  e->total = e->echunk_off + up(static_cast<size_t>(num_q_heads) * e->n_chunks * kvq::kMaxEvalBatch * 4);
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -308,6 +339,12 @@ size_t kvq_pool_bytes(const kvq_cache* cache) {
 kvq_status kvq_quant_append(const kvq_cache* cache, const void* k, const void* v, kvq_dtype in_dtype,
                             int32_t n_tokens, const int32_t* slots, const float* mu, const float* r_k,
                             const float* r_v, float* rot_out, void* stream) {
+  return kvq_quant_append_err(cache, k, v, in_dtype, n_tokens, slots, mu, r_k, r_v, rot_out, nullptr, stream);
+}
+
+kvq_status kvq_quant_append_err(const kvq_cache* cache, const void* k, const void* v, kvq_dtype in_dtype,
+                                int32_t n_tokens, const int32_t* slots, const float* mu, const float* r_k,
+                                const float* r_v, float* rot_out, float* sq_err, void* stream) {
   kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
   if (n_tokens < 0) return fail(KVQ_EINVAL, "n_tokens=%d must be >= 0", n_tokens);
@@ -321,7 +358,7 @@ kvq_status kvq_quant_append(const kvq_cache* cache, const void* k, const void* v
   const int kind = in_dtype == KVQ_BF16 ? 0 : (in_dtype == KVQ_F32 ? 1 : 2);
   hipError_t e = kvq::launch_append(static_cast<uint8_t*>(cache->pool), cache->num_pages, cache->num_kv_heads, k, v,
                                     kind, n_tokens, slots, mu, r_k, r_v, rot_out, clip_of(cache), cache->rotation,
-                                    cache->group_size, static_cast<hipStream_t>(stream));
+                                    cache->group_size, sq_err, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "quant_append launch");
   return KVQ_OK;
 }
@@ -365,6 +402,100 @@ kvq_status kvq_decode_step(const kvq_cache* cache, const void* k_new, const void
   return decode_common(cache, k_new, v_new, kv_dtype, mu, q, q_dtype, batch, num_q_heads, page_table, max_pages,
                        seq_lens, max_seq_len, r_k, r_v, sm_scale, out, out_dtype, workspace, workspace_bytes_,
                        num_splits, window, stream, ev_begin, ev_end);
+}
+
+size_t kvq_output_error_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t max_seq_len, int32_t d_model) {
+  EvalPlan e;
+  if (!make_eval_plan(batch, num_q_heads, num_kv_heads, max_seq_len, d_model, &e)) return 0;
+  return e.total;
+}
+
+kvq_status kvq_output_error(const kvq_cache* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
+                            int32_t num_q_heads, const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens,
+                            int32_t max_seq_len, const void* k, const void* v, kvq_dtype kv_dtype,
+                            const int64_t* row_offsets, const float* sq_err, const float* r_k, const float* r_v,
+                            float sm_scale, const void* w_o, kvq_dtype w_dtype, int32_t d_model, float* dy_k,
+                            float* dy_v, float* e_out, float* e_rec, void* workspace, size_t workspace_bytes_,
+                            void* stream) {
+  kvq_status st = check_cache(cache);
+  if (st != KVQ_OK) return st;
+  if (batch < 0) return fail(KVQ_EINVAL, "batch=%d must be >= 0", batch);
+  if (batch > kvq::kMaxEvalBatch)
+    return fail(KVQ_EUNSUPPORTED, "batch=%d exceeds the evaluator's %d", batch, kvq::kMaxEvalBatch);
+  if (num_q_heads < 1 || num_q_heads % cache->num_kv_heads != 0)
+    return fail(KVQ_EINVAL, "num_q_heads=%d must be a positive multiple of num_kv_heads=%d", num_q_heads,
+                cache->num_kv_heads);
+  const int g = num_q_heads / cache->num_kv_heads;
+  if (g > kMaxGroup) return fail(KVQ_EUNSUPPORTED, "query heads per KV head g=%d exceeds %d", g, kMaxGroup);
+  if (q_dtype != KVQ_BF16 && q_dtype != KVQ_F32) return fail(KVQ_EUNSUPPORTED, "q dtype must be bf16 or fp32");
+  if (kv_dtype != KVQ_BF16 && kv_dtype != KVQ_F32) return fail(KVQ_EUNSUPPORTED, "k/v dtype must be bf16 or fp32");
+  if (w_dtype != KVQ_BF16 && w_dtype != KVQ_F32) return fail(KVQ_EUNSUPPORTED, "w_o dtype must be bf16 or fp32");
+  if (d_model < 1) return fail(KVQ_EINVAL, "d_model=%d must be >= 1", d_model);
+  if (max_seq_len < 0) return fail(KVQ_EINVAL, "max_seq_len=%d must be >= 0", max_seq_len);
+  if (max_seq_len > kMaxContext)
+    return fail(KVQ_EUNSUPPORTED, "max_seq_len=%d exceeds the supported %lld", max_seq_len, kMaxContext);
+  if (max_pages < (max_seq_len + kPage - 1) / kPage)
+    return fail(KVQ_EINVAL, "max_pages=%d cannot hold max_seq_len=%d", max_pages, max_seq_len);
+  if (std::isnan(sm_scale) || std::isinf(sm_scale) || sm_scale < 0.0f)
+    return fail(KVQ_EINVAL, "sm_scale must be finite and >= 0");
+  if (batch == 0) return KVQ_OK;
+  if (batch > 0 && max_seq_len > 0 && cache->num_pages == 0) return fail(KVQ_ENOSPACE, "cache has no pages");
+  if (q == nullptr || page_table == nullptr || seq_lens == nullptr || k == nullptr || v == nullptr ||
+      row_offsets == nullptr || r_k == nullptr || r_v == nullptr || w_o == nullptr || dy_k == nullptr ||
+      dy_v == nullptr || e_out == nullptr || e_rec == nullptr || workspace == nullptr)
+    return fail(KVQ_EINVAL, "q, page_table, seq_lens, k, v, row_offsets, r_k, r_v, w_o, dy_k, dy_v, e_out, e_rec "
+                            "and workspace must be non-NULL (only sq_err may be NULL)");
+  for (const void* a : {static_cast<const void*>(k), static_cast<const void*>(v), static_cast<const void*>(sq_err),
+                        static_cast<const void*>(w_o), static_cast<const void*>(workspace)})
+    if (reinterpret_cast<uintptr_t>(a) % 16 != 0)
+      return fail(KVQ_EINVAL, "k, v, sq_err, w_o and workspace must be 16-byte aligned");
+  EvalPlan plan;
+  if (!make_eval_plan(batch, num_q_heads, cache->num_kv_heads, max_seq_len, d_model, &plan))
+    return fail(KVQ_EUNSUPPORTED, "unsupported evaluator shape");
+  if (workspace_bytes_ < plan.total)
+    return fail(KVQ_ENOSPACE, "workspace of %zu bytes is below the %zu needed", workspace_bytes_, plan.total);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  kvq::EvalParams a{};
+  a.pool = static_cast<const uint8_t*>(cache->pool);
+  a.num_kv_heads = cache->num_kv_heads;
+  a.num_pages = cache->num_pages;
+  a.q = q;
+  a.q_kind = q_dtype == KVQ_BF16 ? 0 : 1;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.g = g;
+  a.page_table = page_table;
+  a.max_pages = max_pages;
+  a.seq_lens = seq_lens;
+  a.len_cap = std::min<long long>(max_seq_len, static_cast<long long>(max_pages) * kPage);
+  a.k = k;
+  a.v = v;
+  a.kv_kind = kv_dtype == KVQ_BF16 ? 0 : 1;
+  a.row0 = row_offsets;
+  a.sq_err = sq_err;
+  a.r_k = r_k;
+  a.r_v = r_v;
+  a.rot_kind = cache->rotation;
+  a.sm_scale = sm_scale == 0.0f ? 1.0f / std::sqrt(static_cast<float>(kHeadDim)) : sm_scale;
+  a.n_splits = plan.n_splits;
+  a.pages_per_split = plan.pages_per_split;
+  a.part = reinterpret_cast<float*>(ws + plan.part_off);
+  a.counters = reinterpret_cast<int32_t*>(ws + plan.counters_off);
+  a.dobuf = reinterpret_cast<float*>(ws + plan.dobuf_off);
+  a.e_rec = e_rec;
+  a.w_o = w_o;
+  a.w_kind = w_dtype == KVQ_BF16 ? 0 : 1;
+  a.d_model = d_model;
+  a.n_chunks = plan.n_chunks;
+  a.dy_k = dy_k;
+  a.dy_v = dy_v;
+  a.e_out = e_out;
+  a.e_chunk = reinterpret_cast<float*>(ws + plan.echunk_off);
+  a.proj_counters = reinterpret_cast<int32_t*>(ws + plan.proj_counters_off);
+  hipError_t e = kvq::launch_eval(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "output_error launch");
+  return KVQ_OK;
 }
 
 size_t kvq_window_bytes(const kvq_window* window, int32_t num_kv_heads) {

@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     uint8_t* __restrict__ pool, int num_pages, int num_kv_heads, const void* __restrict__ k_in,
     const void* __restrict__ v_in, int n_tokens, const int32_t* __restrict__ slots, const float* __restrict__ mu,
     const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out, float clip,
-    int rot_kind, int gsize) {
+    int rot_kind, int gsize, float* __restrict__ sq_err) {
   const int tile = blockIdx.x;
   const int h = blockIdx.y;
   const int tensor = blockIdx.z;  // 0: key, 1: value
@@ -116,7 +116,13 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     } else {
       r = q2_wave_range(xv, gsize);
     }
-    (void)q2_pack_channel(xv, j, tensor, block, slot & 15, clip, r.x, r.y);
+    const float lvl = q2_pack_channel(xv, j, tensor, block, slot & 15, clip, r.x, r.y);
+    if (sq_err != nullptr) {  // squared error over this wave's 64 channels
+      float e = (xv - lvl) * (xv - lvl);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) e += __shfl_xor(e, o);
+      if ((j & 63) == 0) sq_err[((static_cast<size_t>(n) * num_kv_heads + h) * 2 + tensor) * 2 + (j >> 6)] = e;
+    }
   }
 }
 
@@ -142,7 +148,8 @@ template <int kIn, int kRot>  // kIn: 0 = bf16, 1 = fp32; kRot: 0 = dense R, 1 =
 __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
     uint8_t* __restrict__ pool, int num_pages, int num_kv_heads, const void* __restrict__ k_in,
     const void* __restrict__ v_in, int n_tokens, const int32_t* __restrict__ slots, const float* __restrict__ mu,
-    const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out, float clip, int gsize) {
+    const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out, float clip, int gsize,
+    float* __restrict__ sq_err) {
   const int h = blockIdx.y;
   const int tensor = blockIdx.z;  // 0: key, 1: value
   const int tid = threadIdx.x;
@@ -296,6 +303,18 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
       q2_group32(x, clip, gsize, pair, code);
       const int slot = n < n_tokens ? slots[n] : -1;
       const bool ok = slot >= 0 && slot < num_pages * kPage;  // same for the token's four lanes
+      if (sq_err != nullptr) {  // squared error of groups g and g ^ 1: channels [64 (g / 2), +64)
+        const float sc = __builtin_bit_cast(_Float16, static_cast<uint16_t>(pair & 0xffffu));
+        const float zr = __builtin_bit_cast(_Float16, static_cast<uint16_t>(pair >> 16));
+        float e = 0.0f;
+  #pragma unroll
+        for (int c = 0; c < 32; ++c) {
+          const float d = x[c] - fmaf(sc, static_cast<float>(code[c]), zr);
+          e = fmaf(d, d, e);
+        }
+        e += __shfl_xor(e, 1);
+        if (ok && (g & 1) == 0) sq_err[((static_cast<size_t>(n) * num_kv_heads + h) * 2 + tensor) * 2 + (g >> 1)] = e;
+      }
       if (rot_out != nullptr && n < n_tokens) {
         float* dst = rot_out + ((static_cast<size_t>(n) * num_kv_heads + h) * 2 + tensor) * kHeadDim + 32 * g;
   #pragma unroll
@@ -366,7 +385,7 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
 
 hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const void* k, const void* v, int in_kind,
                          int n_tokens, const int32_t* slots, const float* mu, const float* r_k, const float* r_v,
-                         float* rot_out, float clip, int rot_kind, int gsize, hipStream_t stream) {
+                         float* rot_out, float clip, int rot_kind, int gsize, float* sq_err, hipStream_t stream) {
   (void)hipGetLastError();  // report only this call's launch errors, not stale ones
   if (in_kind != 2 && n_tokens >= kBulkMin) {
     // about one workgroup per compute unit in all (each staging its dense R once;
@@ -377,7 +396,7 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
     auto kern = in_kind == 0 ? (rot_kind == 0 ? append_bulk_kernel<0, 0> : append_bulk_kernel<0, 1>)
                              : (rot_kind == 0 ? append_bulk_kernel<1, 0> : append_bulk_kernel<1, 1>);
     hipLaunchKernelGGL(kern, bgrid, dim3(kBulkThreads), 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens, slots,
-                       mu, r_k, r_v, rot_out, clip, gsize);
+                       mu, r_k, r_v, rot_out, clip, gsize, sq_err);
     return hipGetLastError();
   }
   const dim3 grid((n_tokens + kAppendTile - 1) / kAppendTile, num_kv_heads, 2);
@@ -385,15 +404,15 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
   switch (in_kind) {
     case 0:
       hipLaunchKernelGGL(append_kernel<0>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,
-                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize);
+                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize, sq_err);
       break;
     case 1:
       hipLaunchKernelGGL(append_kernel<1>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,
-                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize);
+                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize, sq_err);
       break;
     default:
       hipLaunchKernelGGL(append_kernel<2>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,
-                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize);
+                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize, sq_err);
       break;
   }
   return hipGetLastError();

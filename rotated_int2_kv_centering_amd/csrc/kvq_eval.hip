@@ -1,0 +1,600 @@
+// Output-error evaluator (OptR section 3.2, Eq. (6)-(10)) at the decode position
+// of each sequence, read from the packed cache.
+//
+// For query head j of sequence b (KV head h = j / g) over the positions s < T_b
+// on present pages, with c = sm_scale * log2(e):
+//   exact      a_s  = c <q_j, k_s>                 p  = softmax(a)
+//   INT2 keys  a~_s = c <q_j R_K, x_hat_s>          p~ = softmax(a~)
+// (the effective key is x_hat R_K^T + mu; <q_j, mu> shifts every a~_s equally
+// and drops out of p~).  Three readouts:
+//   A = sum p v,   B = sum p~ v,   C = (sum p~ w_hat) R_V^T
+// so that dO_K = B - A (key-induced, Eq. (8) before W_O) and dO_V = C - B
+// (value-induced).  eval_attn_kernel computes them with one workgroup per
+// (split of pages, KV head, sequence) and a last-workgroup merge;
+// eval_project_kernel then applies W_O,j (dy = dO W_O,j^T) and forms
+// E_out = ||dy_K + dy_V||^2 (Eq. (10)).  E_rec (Eq. (9)) sums the per-token
+// squared quantization errors the append wrote (rotated basis, which R
+// preserves).
+//
+// This is a calibration-time diagnostic, written for clarity on the vector
+// ALUs: per page a wave stages the 16 tokens' exact rows and the packed block in
+// LDS; lane (token, head quad) forms both logits of its heads, then lane
+// (channel pair) accumulates the three readouts.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kEvWaves = 4;
+constexpr int kEvThreads = 64 * kEvWaves;
+constexpr int kRowPad = kHeadDim + 4;  // LDS row stride (floats) of staged exact rows: conflict-free row reads
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kInvSqrt128f = 0.0883883476483184405f;
+
+__device__ __forceinline__ float ld_ag(const float* a) {
+  return __hip_atomic_load(a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_ag(float* a, float v) {
+  __hip_atomic_store(a, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// R[i][c] of KV head h: a dense row-major matrix, or diag(s) H / sqrt(128) from the signs s.
+__device__ __forceinline__ float rot_elem(const float* r, int rot_kind, int h, int i, int c) {
+  if (rot_kind == 0) return r[(static_cast<size_t>(h) * kHeadDim + i) * kHeadDim + c];
+  const float s = r[h * kHeadDim + i];
+  return (__popc(i & c) & 1) ? -s * kInvSqrt128f : s * kInvSqrt128f;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One page's global data held in registers while the previous page is computed.
+template <bool kF32>
+struct PageRegs {
+  static constexpr int kRowWords = kF32 ? 8 : 4;  // uint4 per lane for 16 rows of k (or v)
+  uint4v k[kRowWords], v[kRowWords], blk[2];
+  float err;  // this lane's token's squared error (lanes 0..15)
+};
+
+template <int kNH, bool kF32>
+__global__ __launch_bounds__(kEvThreads) void eval_attn_kernel(const EvalParams p) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int H = p.num_kv_heads;
+  const int b = blockIdx.y;
+  const int h = blockIdx.x % H;
+  const int split = blockIdx.x / H;
+  const int hc = blockIdx.z;                           // chunk of at most kEvHeads query heads of KV head h
+  const int n_hc = gridDim.z;
+  const int g = min(kEvHeads, p.g - kEvHeads * hc);    // query heads of this workgroup
+  const int T = min(max(p.seq_lens[b], 0), p.len_cap);
+  const int n_pages = (T + kPage - 1) / kPage;
+  const int n_valid = (n_pages + p.pages_per_split - 1) / p.pages_per_split;
+  const size_t row_j0 =  // output row of (b, j = h g_kv + kEvHeads hc)
+      static_cast<size_t>(b) * p.num_q_heads + static_cast<size_t>(h) * p.g + kEvHeads * hc;
+  const size_t slot = (static_cast<size_t>(b) * H + h) * n_hc + hc;  // counter and partial block
+  if (n_valid == 0) {  // nothing attended: no differences and no reconstruction error
+    if (split == 0) {
+      for (int idx = tid; idx < g * 2 * kHeadDim; idx += kEvThreads) p.dobuf[row_j0 * 2 * kHeadDim + idx] = 0.0f;
+      if (tid == 0 && hc == 0) p.e_rec[b * H + h] = 0.0f;
+    }
+    return;
+  }
+  if (split >= n_valid) return;
+
+  __shared__ float s_q[kNH][kHeadDim];   // q * c
+  __shared__ float s_qh[kNH][kHeadDim];  // q R_K * c
+  __shared__ float s_qs[kNH][4];         // per-32-channel sums of s_qh
+  // per-wave page staging, reused by the merges
+  constexpr int kStage = 2 * kPage * kRowPad + kBlockBytes / 4 + 2 * kNH * kPage + 2 * kNH;
+  constexpr int kMergeW = kEvWaves * kNH * (3 * kHeadDim + 4) + kEvWaves;
+  constexpr int kBuf = kEvWaves * kStage > kMergeW ? kEvWaves * kStage : kMergeW;
+  __shared__ float s_buf[kBuf];
+  __shared__ int s_ticket;
+
+  // ---- queries, scaled by c, and their rotation q R_K
+  const float c_log2 = p.sm_scale * kLog2e;
+  for (int idx = tid; idx < kNH * kHeadDim; idx += kEvThreads) {
+    const int jj = idx / kHeadDim, c = idx % kHeadDim;
+    float qv = 0.0f;
+    if (jj < g) {
+      const size_t qi = (row_j0 + jj) * kHeadDim + c;
+      qv = p.q_kind == 0 ? bf16_bits_to_f32(static_cast<const uint16_t*>(p.q)[qi]) : static_cast<const float*>(p.q)[qi];
+    }
+    s_q[jj][c] = qv * c_log2;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < kNH * kHeadDim; idx += kEvThreads) {
+    const int jj = idx / kHeadDim, c = idx % kHeadDim;
+    float acc = 0.0f;
+    for (int i = 0; i < kHeadDim; ++i) acc = fmaf(s_q[jj][i], rot_elem(p.r_k, p.rot_kind, h, i, c), acc);
+    s_qh[jj][c] = acc;
+  }
+  __syncthreads();
+  if (tid < kNH * 4) {
+    const int jj = tid / 4, grp = tid % 4;
+    float s = 0.0f;
+    for (int c = 0; c < 32; ++c) s += s_qh[jj][32 * grp + c];
+    s_qs[jj][grp] = s;
+  }
+  __syncthreads();
+
+  // ---- this wave's pages: first + wave, + kEvWaves, ...
+  float* const st = s_buf + wave * kStage;
+  float* const s_k = st;                                   // [16][kRowPad]
+  float* const s_v = st + kPage * kRowPad;                 // [16][kRowPad]
+  uint32_t* const s_blk = reinterpret_cast<uint32_t*>(st + 2 * kPage * kRowPad);  // 384 words
+  float* const s_p = st + 2 * kPage * kRowPad + kBlockBytes / 4;  // [2][kNH][16]
+  float* const s_al = s_p + 2 * kNH * kPage;                      // [2][kNH]
+
+  const int p_first = split * p.pages_per_split;
+  const int p_end = min(p_first + p.pages_per_split, n_pages);
+  const int64_t row0 = p.row0[b];
+  constexpr int kHQ = kNH / 4;  // heads per lane in the logit phase: j = jq + 4 u
+  const int t_l = lane & 15, jq = lane >> 4;
+  float m_a[kHQ], l_a[kHQ], m_q[kHQ], l_q[kHQ];
+#pragma unroll
+  for (int u = 0; u < kHQ; ++u) {
+    m_a[u] = -INFINITY;
+    m_q[u] = -INFINITY;
+    l_a[u] = 0.0f;
+    l_q[u] = 0.0f;
+  }
+  float accA[kNH][2], accB[kNH][2], accC[kNH][2];
+#pragma unroll
+  for (int jj = 0; jj < kNH; ++jj)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) accA[jj][e] = accB[jj][e] = accC[jj][e] = 0.0f;
+  float e_acc = 0.0f;
+
+  auto page_of = [&](int pg) -> int {
+    const int id = p.page_table[static_cast<size_t>(b) * p.max_pages + pg];
+    return (id >= 0 && id < p.num_pages) ? id : -1;
+  };
+  auto load_page = [&](int pg, int id, PageRegs<kF32>& r) {
+    const int nt = min(kPage, T - kPage * pg);
+    const uint8_t* blk = p.pool + (static_cast<size_t>(id) * H + h) * kBlockBytes;
+    r.blk[0] = *reinterpret_cast<const uint4v*>(blk + 16 * lane);
+    r.blk[1] = lane < 32 ? *reinterpret_cast<const uint4v*>(blk + 16 * (64 + lane)) : uint4v{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < PageRegs<kF32>::kRowWords; ++u) {
+      const int idx = u * 64 + lane;
+      const int t = kF32 ? idx >> 5 : idx >> 4;
+      const int part = kF32 ? idx & 31 : idx & 15;
+      if (t < nt) {
+        const size_t e0 = (static_cast<size_t>(row0 + kPage * pg + t) * H + h) * kHeadDim + (kF32 ? 4 : 8) * part;
+        if (kF32) {
+          r.k[u] = *reinterpret_cast<const uint4v*>(static_cast<const float*>(p.k) + e0);
+          r.v[u] = *reinterpret_cast<const uint4v*>(static_cast<const float*>(p.v) + e0);
+        } else {
+          r.k[u] = *reinterpret_cast<const uint4v*>(static_cast<const uint16_t*>(p.k) + e0);
+          r.v[u] = *reinterpret_cast<const uint4v*>(static_cast<const uint16_t*>(p.v) + e0);
+        }
+      } else {
+        r.k[u] = uint4v{0u, 0u, 0u, 0u};
+        r.v[u] = uint4v{0u, 0u, 0u, 0u};
+      }
+    }
+    r.err = 0.0f;
+    if (p.sq_err != nullptr && lane < nt) {
+      const float4v e4 =
+          *reinterpret_cast<const float4v*>(p.sq_err + (static_cast<size_t>(row0 + kPage * pg + lane) * H + h) * 4);
+      r.err = (e4[0] + e4[1]) + (e4[2] + e4[3]);
+    }
+  };
+  auto stage_page = [&](const PageRegs<kF32>& r) {
+    reinterpret_cast<uint4v*>(s_blk)[lane] = r.blk[0];
+    if (lane < 32) reinterpret_cast<uint4v*>(s_blk)[64 + lane] = r.blk[1];
+#pragma unroll
+    for (int u = 0; u < PageRegs<kF32>::kRowWords; ++u) {
+      const int idx = u * 64 + lane;
+      const int t = kF32 ? idx >> 5 : idx >> 4;
+      const int part = kF32 ? idx & 31 : idx & 15;
+      if (kF32) {
+        *reinterpret_cast<uint4v*>(s_k + t * kRowPad + 4 * part) = r.k[u];
+        *reinterpret_cast<uint4v*>(s_v + t * kRowPad + 4 * part) = r.v[u];
+      } else {
+        const uint4v kw = r.k[u], vw = r.v[u];
+        float* kd = s_k + t * kRowPad + 8 * part;
+        float* vd = s_v + t * kRowPad + 8 * part;
+        *reinterpret_cast<float4v*>(kd) = float4v{__uint_as_float(kw[0] << 16), __uint_as_float(kw[0] & 0xffff0000u),
+                                                  __uint_as_float(kw[1] << 16), __uint_as_float(kw[1] & 0xffff0000u)};
+        *reinterpret_cast<float4v*>(kd + 4) = float4v{__uint_as_float(kw[2] << 16), __uint_as_float(kw[2] & 0xffff0000u),
+                                                      __uint_as_float(kw[3] << 16), __uint_as_float(kw[3] & 0xffff0000u)};
+        *reinterpret_cast<float4v*>(vd) = float4v{__uint_as_float(vw[0] << 16), __uint_as_float(vw[0] & 0xffff0000u),
+                                                  __uint_as_float(vw[1] << 16), __uint_as_float(vw[1] & 0xffff0000u)};
+        *reinterpret_cast<float4v*>(vd + 4) = float4v{__uint_as_float(vw[2] << 16), __uint_as_float(vw[2] & 0xffff0000u),
+                                                      __uint_as_float(vw[3] << 16), __uint_as_float(vw[3] & 0xffff0000u)};
+      }
+    }
+  };
+
+  // pages of this wave, skipping absent ones; the next present page is loaded ahead
+  auto next_present = [&](int pg) {
+    while (pg < p_end && page_of(pg) < 0) pg += kEvWaves;
+    return pg;
+  };
+  int pg = next_present(p_first + wave);
+  PageRegs<kF32> cur;
+  if (pg < p_end) load_page(pg, page_of(pg), cur);
+  while (pg < p_end) {
+    const int nt = min(kPage, T - kPage * pg);
+    const int pg_next = next_present(pg + kEvWaves);
+    stage_page(cur);
+    e_acc += cur.err;
+    PageRegs<kF32> nxt;
+    if (pg_next < p_end) load_page(pg_next, page_of(pg_next), nxt);
+    wave_sync();
+
+    // ---- logits: lane (token t_l, head quad jq) forms a and a~ of heads jq + 4 u
+    float ea[kHQ], eq[kHQ];
+    {
+      float dq[kHQ][4];
+#pragma unroll
+      for (int u = 0; u < kHQ; ++u) {
+        ea[u] = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) dq[u][kk] = 0.0f;
+      }
+      const float* krow = s_k + t_l * kRowPad;
+#pragma unroll 4
+      for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
+        const float4v kv = *reinterpret_cast<const float4v*>(krow + 4 * c4);
+#pragma unroll
+        for (int u = 0; u < kHQ; ++u) {
+          const float4v qv = *reinterpret_cast<const float4v*>(&s_q[jq + 4 * u][4 * c4]);
+          ea[u] = fmaf(qv[0], kv[0], fmaf(qv[1], kv[1], fmaf(qv[2], kv[2], fmaf(qv[3], kv[3], ea[u]))));
+        }
+      }
+      // K codes of slot t_l: record 16 a + t_l holds words K0 (groups 0, 1) and K1 (groups 2, 3);
+      // channel 32 kk + 8 a + e sits at bit 2 (4 (kk % 2) + e / 2) + 16 (e % 2)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const uint32_t w01[2] = {s_blk[4 * (16 * a + t_l)], s_blk[4 * (16 * a + t_l) + 1]};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint32_t w = w01[kk >> 1];
+          float cf[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            cf[e] = static_cast<float>((w >> (2 * (4 * (kk & 1) + (e >> 1)) + 16 * (e & 1))) & 3u);
+#pragma unroll
+          for (int u = 0; u < kHQ; ++u) {
+            const float4v q0 = *reinterpret_cast<const float4v*>(&s_qh[jq + 4 * u][32 * kk + 8 * a]);
+            const float4v q1 = *reinterpret_cast<const float4v*>(&s_qh[jq + 4 * u][32 * kk + 8 * a + 4]);
+            dq[u][kk] = fmaf(q0[0], cf[0], fmaf(q0[1], cf[1], fmaf(q0[2], cf[2], fmaf(q0[3], cf[3], dq[u][kk]))));
+            dq[u][kk] = fmaf(q1[0], cf[4], fmaf(q1[1], cf[5], fmaf(q1[2], cf[6], fmaf(q1[3], cf[7], dq[u][kk]))));
+          }
+        }
+      }
+      // a~ = sum over groups of s * <q_hat, codes> + z * sum(q_hat): K (scale, zero) of (group kk, slot t_l)
+#pragma unroll
+      for (int u = 0; u < kHQ; ++u) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const uint32_t pr = s_blk[(kCodeBytes + kMetaRecordBytes * (4 * kk + (t_l >> 2))) / 4 + (t_l & 3)];
+          acc = fmaf(f16_lo(pr), dq[u][kk], fmaf(f16_hi(pr), s_qs[jq + 4 * u][kk], acc));
+        }
+        eq[u] = acc;
+        if (t_l >= nt) {
+          ea[u] = -INFINITY;
+          eq[u] = -INFINITY;
+        }
+      }
+    }
+
+    // ---- online softmax per head over this page's 16 tokens (lanes sharing jq)
+#pragma unroll
+    for (int u = 0; u < kHQ; ++u) {
+      const int jj = jq + 4 * u;
+      float ma = ea[u], mq = eq[u];
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) {
+        ma = fmaxf(ma, __shfl_xor(ma, o));
+        mq = fmaxf(mq, __shfl_xor(mq, o));
+      }
+      const float na = fmaxf(m_a[u], ma), nq = fmaxf(m_q[u], mq);
+      const float ala = __builtin_amdgcn_exp2f(m_a[u] - na), alq = __builtin_amdgcn_exp2f(m_q[u] - nq);
+      const float pa = __builtin_amdgcn_exp2f(ea[u] - na), pq = __builtin_amdgcn_exp2f(eq[u] - nq);
+      float sa = pa, sq = pq;
+#pragma unroll
+      for (int o = 8; o >= 1; o >>= 1) {
+        sa += __shfl_xor(sa, o);
+        sq += __shfl_xor(sq, o);
+      }
+      l_a[u] = fmaf(l_a[u], ala, sa);
+      l_q[u] = fmaf(l_q[u], alq, sq);
+      m_a[u] = na;
+      m_q[u] = nq;
+      if (jj < g) {
+        s_p[jj * kPage + t_l] = pa;
+        s_p[(kNH + jj) * kPage + t_l] = pq;
+        if (t_l == 0) {
+          s_al[jj] = ala;
+          s_al[kNH + jj] = alq;
+        }
+      }
+    }
+    wave_sync();
+
+    // ---- readouts: lane (channels c0, c0 + 1)
+    {
+      const int c0 = 2 * lane;
+#pragma unroll
+      for (int jj = 0; jj < kNH; ++jj) {
+        if (jj < g) {
+          const float ala = s_al[jj], alq = s_al[kNH + jj];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            accA[jj][e] *= ala;
+            accB[jj][e] *= alq;
+            accC[jj][e] *= alq;
+          }
+        }
+      }
+      // V code of slot t, channel c: record 16 (t / 4) + c % 16, word V[(t % 4) / 2], bit 2 (c / 16) + 16 (t % 2);
+      // V (scale, zero) of (group c / 32, slot t): record 4 (c / 32) + t / 4, at +16 + 4 (t % 4)
+      const int tile = c0 >> 4, b0 = c0 & 15, grp = c0 >> 5;
+      for (int t = 0; t < nt; ++t) {
+        const int wsel = 2 + ((t & 3) >> 1);
+        const int sh = 2 * tile + 16 * (t & 1);
+        const uint32_t w0 = s_blk[4 * (16 * (t >> 2) + b0) + wsel];
+        const uint32_t w1 = s_blk[4 * (16 * (t >> 2) + b0 + 1) + wsel];
+        const uint32_t pr = s_blk[(kCodeBytes + kMetaRecordBytes * (4 * grp + (t >> 2)) + 16) / 4 + (t & 3)];
+        const float sv = f16_lo(pr), zv = f16_hi(pr);
+        const float wh0 = fmaf(sv, static_cast<float>((w0 >> sh) & 3u), zv);
+        const float wh1 = fmaf(sv, static_cast<float>((w1 >> sh) & 3u), zv);
+        const float v0 = s_v[t * kRowPad + c0], v1 = s_v[t * kRowPad + c0 + 1];
+#pragma unroll
+        for (int jj = 0; jj < kNH; ++jj) {
+          if (jj < g) {
+            const float pa = s_p[jj * kPage + t], pq = s_p[(kNH + jj) * kPage + t];
+            accA[jj][0] = fmaf(pa, v0, accA[jj][0]);
+            accA[jj][1] = fmaf(pa, v1, accA[jj][1]);
+            accB[jj][0] = fmaf(pq, v0, accB[jj][0]);
+            accB[jj][1] = fmaf(pq, v1, accB[jj][1]);
+            accC[jj][0] = fmaf(pq, wh0, accC[jj][0]);
+            accC[jj][1] = fmaf(pq, wh1, accC[jj][1]);
+          }
+        }
+      }
+    }
+    wave_sync();  // staging free for the next page
+    pg = pg_next;
+    cur = nxt;
+  }
+
+  // ---- merge the waves: [wave][head][A | B | C (128 each) | m_a l_a m_q l_q], then [wave] errors
+  __syncthreads();
+  constexpr int kWRow = 3 * kHeadDim + 4;
+  float* const s_mw = s_buf;
+  float* const s_merr = s_buf + kEvWaves * kNH * kWRow;
+#pragma unroll
+  for (int jj = 0; jj < kNH; ++jj) {
+    if (jj < g) {
+      float* row = s_mw + (wave * kNH + jj) * kWRow;
+      row[2 * lane] = accA[jj][0];
+      row[2 * lane + 1] = accA[jj][1];
+      row[kHeadDim + 2 * lane] = accB[jj][0];
+      row[kHeadDim + 2 * lane + 1] = accB[jj][1];
+      row[2 * kHeadDim + 2 * lane] = accC[jj][0];
+      row[2 * kHeadDim + 2 * lane + 1] = accC[jj][1];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kHQ; ++u) {
+    const int jj = jq + 4 * u;
+    if (jj < g && t_l == 0) {
+      float* row = s_mw + (wave * kNH + jj) * kWRow + 3 * kHeadDim;
+      row[0] = m_a[u];
+      row[1] = l_a[u];
+      row[2] = m_q[u];
+      row[3] = l_q[u];
+    }
+  }
+  const float e_w = wave_sum(lane < kPage ? e_acc : 0.0f);
+  if (lane == 0) s_merr[wave] = e_w;
+  __syncthreads();
+
+  float* const part_base = p.part + slot * p.n_splits * kEvHeads * kEvPartStride;
+  for (int idx = tid; idx < g * kHeadDim; idx += kEvThreads) {
+    const int jj = idx / kHeadDim, c = idx % kHeadDim;
+    float Ma = -INFINITY, Mq = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kEvWaves; ++w) {
+      const float* st4 = s_mw + (w * kNH + jj) * kWRow + 3 * kHeadDim;
+      Ma = fmaxf(Ma, st4[0]);
+      Mq = fmaxf(Mq, st4[2]);
+    }
+    float A = 0.0f, B = 0.0f, C = 0.0f, La = 0.0f, Lq = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kEvWaves; ++w) {
+      const float* row = s_mw + (w * kNH + jj) * kWRow;
+      const float fa = Ma == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(row[3 * kHeadDim] - Ma);
+      const float fq = Mq == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(row[3 * kHeadDim + 2] - Mq);
+      A = fmaf(fa, row[c], A);
+      B = fmaf(fq, row[kHeadDim + c], B);
+      C = fmaf(fq, row[2 * kHeadDim + c], C);
+      La = fmaf(fa, row[3 * kHeadDim + 1], La);
+      Lq = fmaf(fq, row[3 * kHeadDim + 3], Lq);
+    }
+    float* dst = part_base + (static_cast<size_t>(split) * g + jj) * kEvPartStride;
+    st_ag(dst + c, A);
+    st_ag(dst + kHeadDim + c, B);
+    st_ag(dst + 2 * kHeadDim + c, C);
+    if (c == 0) {
+      st_ag(dst + 3 * kHeadDim, Ma);
+      st_ag(dst + 3 * kHeadDim + 1, La);
+      st_ag(dst + 3 * kHeadDim + 2, Mq);
+      st_ag(dst + 3 * kHeadDim + 3, Lq);
+      if (jj == 0) st_ag(dst + 3 * kHeadDim + 4, (s_merr[0] + s_merr[1]) + (s_merr[2] + s_merr[3]));
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0)
+    s_ticket = __hip_atomic_fetch_add(p.counters + slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (s_ticket != n_valid - 1) return;
+
+  // ---- the last workgroup of (b, h) merges the splits
+  float* const s_st = s_buf;                              // [split][head][4]
+  float* const s_se = s_buf + n_valid * g * 4;             // [split]
+  float* const s_crot = s_se + n_valid;                    // [head][128] C in the rotated basis
+  float* const s_oa = s_crot + g * kHeadDim;               // [head][128] A
+  float* const s_ob = s_oa + g * kHeadDim;                 // [head][128] B
+  static_assert(kMaxEvalSplits * kNH * 4 + kMaxEvalSplits + 3 * kNH * kHeadDim <= kBuf, "split merge fits the buffer");
+  for (int idx = tid; idx < n_valid * g; idx += kEvThreads) {
+    const float* src = part_base + static_cast<size_t>(idx) * kEvPartStride + 3 * kHeadDim;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_st[4 * idx + e] = ld_ag(src + e);
+    if (idx % g == 0) s_se[idx / g] = ld_ag(src + 4);
+  }
+  __syncthreads();
+  for (int idx = tid; idx < g * kHeadDim; idx += kEvThreads) {
+    const int jj = idx / kHeadDim, c = idx % kHeadDim;
+    float Ma = -INFINITY, Mq = -INFINITY;
+    for (int s = 0; s < n_valid; ++s) {
+      Ma = fmaxf(Ma, s_st[4 * (s * g + jj)]);
+      Mq = fmaxf(Mq, s_st[4 * (s * g + jj) + 2]);
+    }
+    float A = 0.0f, B = 0.0f, C = 0.0f, La = 0.0f, Lq = 0.0f;
+    for (int s = 0; s < n_valid; ++s) {
+      const float* st4 = s_st + 4 * (s * g + jj);
+      const float fa = Ma == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(st4[0] - Ma);
+      const float fq = Mq == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(st4[2] - Mq);
+      const float* row = part_base + (static_cast<size_t>(s) * g + jj) * kEvPartStride;
+      A = fmaf(fa, ld_ag(row + c), A);
+      B = fmaf(fq, ld_ag(row + kHeadDim + c), B);
+      C = fmaf(fq, ld_ag(row + 2 * kHeadDim + c), C);
+      La = fmaf(fa, st4[1], La);
+      Lq = fmaf(fq, st4[3], Lq);
+    }
+    s_oa[idx] = La > 0.0f ? A / La : 0.0f;
+    s_ob[idx] = Lq > 0.0f ? B / Lq : 0.0f;
+    s_crot[idx] = Lq > 0.0f ? C / Lq : 0.0f;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < g * kHeadDim; idx += kEvThreads) {
+    const int jj = idx / kHeadDim, i = idx % kHeadDim;
+    float C = 0.0f;  // (C_rot R_V^T)_i = sum_c C_rot[c] R_V[i][c]
+    for (int c = 0; c < kHeadDim; ++c) C = fmaf(s_crot[jj * kHeadDim + c], rot_elem(p.r_v, p.rot_kind, h, i, c), C);
+    float* d = p.dobuf + (row_j0 + jj) * 2 * kHeadDim;
+    d[i] = s_ob[idx] - s_oa[idx];     // key-induced: B - A
+    d[kHeadDim + i] = C - s_ob[idx];  // value-induced: C - B
+  }
+  if (tid == 0) {
+    float e = 0.0f;
+    for (int s = 0; s < n_valid; ++s) e += s_se[s];
+    if (hc == 0) p.e_rec[b * H + h] = p.sq_err != nullptr ? e : 0.0f;
+    __hip_atomic_store(p.counters + slot, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// dy = dO W_O,j^T for every sequence: workgroup (head j, chunk of kProjRows rows of
+// W_O); wave w takes rows w, w + 4, ...; lane (channel pair) and a wave sum per
+// (row, sequence).  E_out = ||dy_K + dy_V||^2: per-chunk sums, added in chunk
+// order by the last workgroup of head j.
+template <bool kWF32>
+__global__ __launch_bounds__(kEvThreads) void eval_project_kernel(const EvalParams p) {
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int j = blockIdx.x;
+  const int chunk = blockIdx.y;
+  const int Hq = p.num_q_heads;
+  const int B = p.batch;
+  __shared__ float s_do[kMaxEvalBatch][2 * kHeadDim];
+  __shared__ float s_e[kEvWaves][kMaxEvalBatch];
+  __shared__ int s_ticket;
+  for (int idx = tid; idx < B * 2 * kHeadDim; idx += kEvThreads) {
+    const int bb = idx / (2 * kHeadDim), c = idx % (2 * kHeadDim);
+    s_do[bb][c] = p.dobuf[(static_cast<size_t>(bb) * Hq + j) * 2 * kHeadDim + c];
+  }
+  for (int idx = tid; idx < kEvWaves * kMaxEvalBatch; idx += kEvThreads) s_e[idx / kMaxEvalBatch][idx % kMaxEvalBatch] = 0.0f;
+  __syncthreads();
+  const int r0 = chunk * kProjRows;
+  const int r1 = min(r0 + kProjRows, p.d_model);
+  const size_t ld = static_cast<size_t>(Hq) * kHeadDim;
+  for (int r = r0 + wave; r < r1; r += kEvWaves) {
+    float w0, w1;
+    const size_t wi = r * ld + static_cast<size_t>(j) * kHeadDim + 2 * lane;
+    if (kWF32) {
+      const float* w = static_cast<const float*>(p.w_o) + wi;
+      w0 = w[0];
+      w1 = w[1];
+    } else {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.w_o) + wi);
+      w0 = __uint_as_float(w << 16);
+      w1 = __uint_as_float(w & 0xffff0000u);
+    }
+    for (int bb = 0; bb < B; ++bb) {
+      const float pk = wave_sum(fmaf(s_do[bb][2 * lane], w0, s_do[bb][2 * lane + 1] * w1));
+      const float pv = wave_sum(fmaf(s_do[bb][kHeadDim + 2 * lane], w0, s_do[bb][kHeadDim + 2 * lane + 1] * w1));
+      if (lane == 0) {
+        const size_t oi = (static_cast<size_t>(bb) * Hq + j) * p.d_model + r;
+        p.dy_k[oi] = pk;
+        p.dy_v[oi] = pv;
+        const float dy = pk + pv;
+        s_e[wave][bb] = fmaf(dy, dy, s_e[wave][bb]);
+      }
+    }
+  }
+  __syncthreads();
+  float* const e_chunk = p.e_chunk + static_cast<size_t>(j) * p.n_chunks * kMaxEvalBatch;
+  if (tid < B) st_ag(e_chunk + static_cast<size_t>(chunk) * kMaxEvalBatch + tid,
+                     (s_e[0][tid] + s_e[1][tid]) + (s_e[2][tid] + s_e[3][tid]));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0)
+    s_ticket = __hip_atomic_fetch_add(p.proj_counters + j, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (s_ticket != p.n_chunks - 1) return;
+  if (tid < B) {
+    float e = 0.0f;
+    for (int ch = 0; ch < p.n_chunks; ++ch) e += ld_ag(e_chunk + static_cast<size_t>(ch) * kMaxEvalBatch + tid);
+    p.e_out[static_cast<size_t>(tid) * Hq + j] = e;
+  }
+  if (tid == 0) __hip_atomic_store(p.proj_counters + j, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int kNH>
+hipError_t launch_attn(const EvalParams& p, hipStream_t stream) {
+  const dim3 grid(p.num_kv_heads * p.n_splits, p.batch, (p.g + kEvHeads - 1) / kEvHeads);
+  if (p.kv_kind == 1)
+    hipLaunchKernelGGL((eval_attn_kernel<kNH, true>), grid, dim3(kEvThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((eval_attn_kernel<kNH, false>), grid, dim3(kEvThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_eval(const EvalParams& p, hipStream_t stream) {
+  (void)hipGetLastError();  // report only this call's launch errors
+  hipError_t e = p.g <= 4 ? launch_attn<4>(p, stream) : launch_attn<kEvHeads>(p, stream);
+  if (e != hipSuccess) return e;
+  const dim3 pgrid(p.num_q_heads, p.n_chunks);
+  if (p.w_kind == 1)
+    hipLaunchKernelGGL(eval_project_kernel<true>, pgrid, dim3(kEvThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL(eval_project_kernel<false>, pgrid, dim3(kEvThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -8,7 +8,7 @@ namespace kvq {
 
 hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const void* k, const void* v, int in_kind,
                          int n_tokens, const int32_t* slots, const float* mu, const float* r_k, const float* r_v,
-                         float* rot_out, float clip, int rot_kind, int gsize, hipStream_t stream);
+                         float* rot_out, float clip, int rot_kind, int gsize, float* sq_err, hipStream_t stream);
 
 // Split plan of one decode call.  Fixed plan (an explicit split count): every
 // sequence is cut into n_splits splits of pages_per_split pages.  Balanced
@@ -79,5 +79,48 @@ struct DecodeParams {
 };
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end);
+
+// Output-error evaluator (OptR section 3.2, Eq. (6)-(10)).
+constexpr int kEvPartStride = 392;   // split partial row: A, B, C [128 each], m_a, l_a, m_q, l_q, e_rec (head 0)
+constexpr int kMaxEvalBatch = 64;
+constexpr int kMaxEvalSplits = 256;
+constexpr int kProjRows = 128;       // rows of W_O per projection workgroup
+constexpr int kEvHeads = 8;          // query heads per evaluator workgroup (g = 16 takes two chunks)
+
+struct EvalParams {
+  const uint8_t* pool;
+  int num_kv_heads, num_pages;
+  const void* q;
+  int q_kind;  // 0 bf16, 1 fp32
+  int batch, num_q_heads, g;
+  const int32_t* page_table;
+  int max_pages;
+  const int32_t* seq_lens;
+  int len_cap;
+  const void* k;  // exact rows [row][H_kv][128]; sequence b's position s is row row0[b] + s
+  const void* v;
+  int kv_kind;    // 0 bf16, 1 fp32
+  const int64_t* row0;
+  const float* sq_err;  // [row][H_kv][2][2] from the append, or null (e_rec = 0)
+  const float* r_k;
+  const float* r_v;
+  int rot_kind;   // 0 dense [H][128][128], 1 Hadamard signs [H][128]
+  float sm_scale;
+  int n_splits, pages_per_split;
+  float* part;             // [B][H_kv][head chunk][n_splits][kEvHeads][kEvPartStride]
+  int32_t* counters;       // [B][H_kv][head chunk], zero between calls
+  float* dobuf;            // [B][H_q][2][128]: dO_K, dO_V
+  float* e_rec;            // [B][H_kv]
+  const void* w_o;         // [d_model][H_q * 128]
+  int w_kind;              // 0 bf16, 1 fp32
+  int d_model, n_chunks;
+  float* dy_k;             // [B][H_q][d_model]
+  float* dy_v;
+  float* e_out;            // [B][H_q]
+  float* e_chunk;          // [H_q][n_chunks][kMaxEvalBatch]
+  int32_t* proj_counters;  // [H_q], zero between calls
+};
+
+hipError_t launch_eval(const EvalParams& p, hipStream_t stream);
 
 }  // namespace kvq

@@ -69,6 +69,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_pool_bytes.restype = SZ
     lib.kvq_quant_append.argtypes = [CP, P, P, I32, I32, P, P, P, P, P, P]
     lib.kvq_quant_append.restype = I32
+    lib.kvq_quant_append_err.argtypes = [CP, P, P, I32, I32, P, P, P, P, P, P, P]
+    lib.kvq_quant_append_err.restype = I32
+    lib.kvq_output_error_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
+    lib.kvq_output_error_workspace_bytes.restype = SZ
+    lib.kvq_output_error.argtypes = [CP, P, I32, I32, I32, P, I32, P, I32, P, P, I32, P, P, P, P, F, P, I32, I32, P, P,
+                                     P, P, P, SZ, P]
+    lib.kvq_output_error.restype = I32
     lib.kvq_decode_workspace_bytes.argtypes = [I32, I32, I32, I32, I32]
     lib.kvq_decode_workspace_bytes.restype = SZ
     lib.kvq_decode_attn.argtypes = [CP, P, I32, I32, I32, P, I32, P, I32, P, P, F, P, I32, P, SZ, I32, WP, P]
@@ -149,6 +156,28 @@ def kvq_quant_append(cache: kvq_cache, k, v, in_dtype: int, n_tokens: int, slots
                      stream=None) -> None:
     _check(load().kvq_quant_append(ctypes.byref(cache), _ptr(k), _ptr(v), in_dtype, n_tokens, _ptr(slots), _ptr(mu),
                                    _ptr(r_k), _ptr(r_v), _ptr(rot_out), _stream(stream)))
+
+
+def kvq_quant_append_err(cache: kvq_cache, k, v, in_dtype: int, n_tokens: int, slots, mu, r_k, r_v, rot_out=None,
+                         sq_err=None, stream=None) -> None:
+    _check(load().kvq_quant_append_err(ctypes.byref(cache), _ptr(k), _ptr(v), in_dtype, n_tokens, _ptr(slots),
+                                       _ptr(mu), _ptr(r_k), _ptr(r_v), _ptr(rot_out), _ptr(sq_err), _stream(stream)))
+
+
+def kvq_output_error_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int,
+                                     d_model: int) -> int:
+    return int(load().kvq_output_error_workspace_bytes(batch, num_q_heads, num_kv_heads, max_seq_len, d_model))
+
+
+def kvq_output_error(cache: kvq_cache, q, q_dtype: int, batch: int, num_q_heads: int, page_table, max_pages: int,
+                     seq_lens, max_seq_len: int, k, v, kv_dtype: int, row_offsets, sq_err, r_k, r_v, sm_scale: float,
+                     w_o, w_dtype: int, d_model: int, dy_k, dy_v, e_out, e_rec, workspace, workspace_bytes: int,
+                     stream=None) -> None:
+    _check(load().kvq_output_error(ctypes.byref(cache), _ptr(q), q_dtype, batch, num_q_heads, _ptr(page_table),
+                                   max_pages, _ptr(seq_lens), max_seq_len, _ptr(k), _ptr(v), kv_dtype,
+                                   _ptr(row_offsets), _ptr(sq_err), _ptr(r_k), _ptr(r_v), float(sm_scale), _ptr(w_o),
+                                   w_dtype, d_model, _ptr(dy_k), _ptr(dy_v), _ptr(e_out), _ptr(e_rec),
+                                   _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
 def kvq_decode_workspace_bytes(batch: int, num_q_heads: int, num_kv_heads: int, max_seq_len: int,

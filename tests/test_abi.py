@@ -36,8 +36,9 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    assert names == sorted(["kvq_pool_bytes", "kvq_quant_append", "kvq_decode_workspace_bytes", "kvq_decode_attn",
-                            "kvq_decode_attn_traced", "kvq_decode_step", "kvq_window_bytes", "kvq_window_fill",
+    assert names == sorted(["kvq_pool_bytes", "kvq_quant_append", "kvq_quant_append_err", "kvq_decode_workspace_bytes",
+                            "kvq_decode_attn", "kvq_decode_attn_traced", "kvq_decode_step", "kvq_window_bytes",
+                            "kvq_window_fill", "kvq_output_error_workspace_bytes", "kvq_output_error",
                             "kvq_page_table", "kvq_last_error"]), names
 
 
@@ -287,3 +288,47 @@ def test_cache_clip_ratio_layout_and_validation(K):
                                     None) == K.KVQ_EINVAL
         assert "clip_ratio" in K.kvq_last_error()
         assert _decode(K, K.make_cache(1, 8, FAKE, clip_ratio=bad)) == K.KVQ_EINVAL
+
+
+def _eval(K, cache, batch=1, hq=4, max_pages=4, max_seq=64, d_model=96, ws_bytes=1 << 22, sq_err=FAKE, k=FAKE,
+          w_o=FAKE, kv_dtype=None, w_dtype=None, row_offsets=FAKE):
+    lib = K.load()
+    kv_dtype = K.KVQ_BF16 if kv_dtype is None else kv_dtype
+    w_dtype = K.KVQ_BF16 if w_dtype is None else w_dtype
+    return lib.kvq_output_error(ctypes.byref(cache) if cache is not None else None, FAKE, K.KVQ_BF16, batch, hq, FAKE,
+                                max_pages, FAKE, max_seq, k, FAKE, kv_dtype, row_offsets, sq_err, FAKE, FAKE, 0.0,
+                                w_o, w_dtype, d_model, FAKE, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+
+
+def test_output_error_workspace_and_validation(K):
+    """The evaluator's host checks (no launch is reached): sizes, shapes, dtypes,
+    alignment, the batch cap, and the append-with-errors entry point's checks."""
+    ws = K.kvq_output_error_workspace_bytes
+    assert ws(1, 32, 8, 131072, 4096) > 0 and ws(1, 32, 8, 131072, 4096) % 256 == 0
+    assert ws(64, 32, 8, 1024, 4096) > ws(1, 32, 8, 1024, 4096)
+    assert ws(65, 32, 8, 1024, 4096) == 0          # batch above 64
+    assert ws(1, 34, 2, 1024, 4096) == 0           # g = 17
+    assert ws(1, 3, 2, 1024, 4096) == 0            # 3 q heads over 2 KV heads
+    assert ws(1, 4, 1, 1024, 0) == 0               # d_model < 1
+    c = K.make_cache(1, 8, FAKE)
+    assert _eval(K, None) == K.KVQ_EINVAL
+    assert _eval(K, c, batch=65) == K.KVQ_EUNSUPPORTED
+    assert "64" in K.kvq_last_error()
+    assert _eval(K, c, hq=17) == K.KVQ_EUNSUPPORTED
+    assert _eval(K, c, kv_dtype=K.KVQ_F32_ROTATED) == K.KVQ_EUNSUPPORTED
+    assert _eval(K, c, w_dtype=9) == K.KVQ_EUNSUPPORTED
+    assert _eval(K, c, d_model=0) == K.KVQ_EINVAL
+    assert _eval(K, c, max_pages=3) == K.KVQ_EINVAL
+    assert _eval(K, c, k=None) == K.KVQ_EINVAL
+    assert _eval(K, c, row_offsets=None) == K.KVQ_EINVAL
+    assert _eval(K, c, w_o=FAKE + 4) == K.KVQ_EINVAL and "aligned" in K.kvq_last_error()
+    assert _eval(K, c, sq_err=FAKE + 8) == K.KVQ_EINVAL
+    need = K.kvq_output_error_workspace_bytes(1, 4, 1, 64, 96)
+    assert _eval(K, c, ws_bytes=need - 1) == K.KVQ_ENOSPACE
+    assert _eval(K, c, batch=0) == K.KVQ_OK        # an empty batch is a no-op
+    assert _eval(K, K.make_cache(1, 8, FAKE, rotation=3)) == K.KVQ_EINVAL
+    lib = K.load()
+    assert lib.kvq_quant_append_err(ctypes.byref(c), None, None, K.KVQ_BF16, 0, None, None, None, None, None, None,
+                                    None) == K.KVQ_OK
+    assert lib.kvq_quant_append_err(ctypes.byref(c), FAKE, FAKE, K.KVQ_BF16, -1, FAKE, None, FAKE, FAKE, None, FAKE,
+                                    None) == K.KVQ_EINVAL
