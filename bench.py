@@ -169,6 +169,76 @@ def cpu_baseline(case, pool_np, kv_heads_sample: int):
     }
 
 
+def bench_evaluator(args, torch, I, kvq, dev, desc, case) -> int:
+    """Time kvq_output_error (the output-error evaluator, one call per step) on the
+    workload's cache, written by kvq_quant_append_err, with a bf16 W_O of d_model
+    4096 x (H_q 128), and print one JSON line for it."""
+    import numpy as np
+
+    def T(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    def B16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    rot_kind = kvq.KVQ_ROT_HADAMARD if args.rotation == "hadamard" else kvq.KVQ_ROT_DENSE
+    pool = torch.zeros(case.num_pages * case.Hkv * 1536, dtype=torch.uint8, device=dev)
+    cache = kvq.make_cache(case.Hkv, case.num_pages, pool, rotation=rot_kind)
+    k, v = B16(case.k_bits), B16(case.v_bits)
+    r_k, r_v, mu = T(case.r_k), T(case.r_v), T(case.mu)
+    sq_err = torch.zeros((case.n_tokens, case.Hkv, 2, 2), dtype=torch.float32, device=dev)
+    kvq.kvq_quant_append_err(cache, k, v, kvq.KVQ_BF16, case.n_tokens, T(case.slots), mu, r_k, r_v, None, sq_err)
+    d_model = 4096
+    w_bits = I.bf16_bits((np.random.default_rng(9).standard_normal((d_model, case.Hq * 128)) / np.sqrt(128))
+                         .astype(np.float32))
+    w_o = B16(w_bits)
+    max_seq = int(case.seq_lens.max())
+    ws_bytes = kvq.kvq_output_error_workspace_bytes(case.B, case.Hq, case.Hkv, max_seq, d_model)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
+    row_off = T(np.concatenate([[0], np.cumsum(case.seq_lens)[:-1]]).astype(np.int64))
+    table, seq, q = T(case.page_table), T(case.seq_lens), B16(case.q_bits)
+    dy_k = torch.empty((case.B, case.Hq, d_model), dtype=torch.float32, device=dev)
+    dy_v, e_out = torch.empty_like(dy_k), torch.empty((case.B, case.Hq), dtype=torch.float32, device=dev)
+    e_rec = torch.empty((case.B, case.Hkv), dtype=torch.float32, device=dev)
+
+    def call():
+        kvq.kvq_output_error(cache, q, kvq.KVQ_BF16, case.B, case.Hq, table, int(case.page_table.shape[1]), seq,
+                             max_seq, k, v, kvq.KVQ_BF16, row_off, sq_err, r_k, r_v, 0.0, w_o, kvq.KVQ_BF16, d_model,
+                             dy_k, dy_v, e_out, e_rec, ws, ws_bytes)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in evs:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    tokens = float(case.seq_lens.sum())
+    n_pages = int(((case.seq_lens + PAGE - 1) // PAGE).sum())
+    n_hc = -(-case.g // 8)
+    # per (token, KV head, head chunk): bf16 k and v (512 B), the packed bytes (96 B), the squared errors (16 B);
+    # page-table entries; W_O once (bf16); q, outputs and split partials are not counted
+    alg = tokens * case.Hkv * n_hc * (512 + BYTES_PER_TOKEN_HEAD + 16) + 4 * n_pages + d_model * case.Hq * 128 * 2
+    achieved = alg / (ms * 1e-3) / 1e9
+    log(f"[bench] output-error evaluator: {ms * 1e3:.1f} us per call ({args.steps} calls), {achieved:.0f} GB/s "
+        f"algorithmic")
+    res = {
+        "metric": "INT2 output-error evaluator (Eq. 6-10) KV-tokens/s",
+        "value": tokens / (ms * 1e-3), "unit": "KV-tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32 (bf16 exact k/v/W_O, int2 cache)", "data": "synthetic",
+        "config": {"workload": desc, "d_model": d_model, "rotation": args.rotation},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": None},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -181,6 +251,8 @@ def main() -> int:
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-kv-heads", type=int, default=8, help="KV heads in the oracle's timed sample (0 = skip)")
     ap.add_argument("--window", default="", help="exact bf16 window 'sinks,recent' (e.g. 4,128); default none")
+    ap.add_argument("--evaluator", action="store_true",
+                    help="time the output-error evaluator (kvq_output_error) instead of the decode step")
     ap.add_argument("--rotation", default="dense", choices=["dense", "hadamard"],
                     help="R as a dense random orthogonal matrix, or a randomized Hadamard rotation (sign vectors)")
     args = ap.parse_args()
@@ -209,6 +281,8 @@ def main() -> int:
     case = make(I, args.rotation)
     log(f"[bench] generated {case.name}: B={case.B} Hq={case.Hq} Hkv={case.Hkv} sum(T)={int(case.seq_lens.sum())} "
         f"in {time.perf_counter() - t_gen:.1f}s")
+    if args.evaluator:
+        return bench_evaluator(args, torch, I, kvq, dev, desc, case)
 
     def T(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)

@@ -309,8 +309,8 @@ bool make_eval_plan(int batch, int num_q_heads, int num_kv_heads, int max_seq_le
   const int g = num_q_heads / num_kv_heads;
   if (g > kMaxGroup) return false;
   const int n_pages = (max_seq_len + kPage - 1) / kPage;
-  // about one workgroup per compute unit in all
-  const int want = std::max(1, (256 + batch * num_kv_heads - 1) / std::max(1, batch * num_kv_heads));
+  // about two workgroups per compute unit in all (two fit one CU's LDS for g <= 4)
+  const int want = std::max(1, (512 + batch * num_kv_heads - 1) / std::max(1, batch * num_kv_heads));
   int n_splits = std::max(1, std::min({want, std::max(n_pages, 1), kvq::kMaxEvalSplits}));
   e->pages_per_split = std::max(1, (n_pages + n_splits - 1) / n_splits);
   e->n_splits = std::max(1, (n_pages + e->pages_per_split - 1) / e->pages_per_split);

@@ -70,7 +70,8 @@ struct PageRegs {
 };
 
 template <int kNH, bool kF32>
-__global__ __launch_bounds__(kEvThreads) void eval_attn_kernel(const EvalParams p) {
+__global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2))) void eval_attn_kernel(
+    const EvalParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -251,15 +252,20 @@ __global__ __launch_bounds__(kEvThreads) void eval_attn_kernel(const EvalParams 
         for (int kk = 0; kk < 4; ++kk) dq[u][kk] = 0.0f;
       }
       const float* krow = s_k + t_l * kRowPad;
+      float ea2[kHQ][2];  // two interleaved sums: shorter dependency chains
+#pragma unroll
+      for (int u = 0; u < kHQ; ++u) ea2[u][0] = ea2[u][1] = 0.0f;
 #pragma unroll 4
       for (int c4 = 0; c4 < kHeadDim / 4; ++c4) {
         const float4v kv = *reinterpret_cast<const float4v*>(krow + 4 * c4);
 #pragma unroll
         for (int u = 0; u < kHQ; ++u) {
           const float4v qv = *reinterpret_cast<const float4v*>(&s_q[jq + 4 * u][4 * c4]);
-          ea[u] = fmaf(qv[0], kv[0], fmaf(qv[1], kv[1], fmaf(qv[2], kv[2], fmaf(qv[3], kv[3], ea[u]))));
+          ea2[u][c4 & 1] = fmaf(qv[0], kv[0], fmaf(qv[1], kv[1], fmaf(qv[2], kv[2], fmaf(qv[3], kv[3], ea2[u][c4 & 1]))));
         }
       }
+#pragma unroll
+      for (int u = 0; u < kHQ; ++u) ea[u] = ea2[u][0] + ea2[u][1];
       // K codes of slot t_l: record 16 a + t_l holds words K0 (groups 0, 1) and K1 (groups 2, 3);
       // channel 32 kk + 8 a + e sits at bit 2 (4 (kk % 2) + e / 2) + 16 (e % 2)
 #pragma unroll
@@ -506,12 +512,15 @@ __global__ __launch_bounds__(kEvThreads) void eval_attn_kernel(const EvalParams 
   }
 }
 
-// dy = dO W_O,j^T for every sequence: workgroup (head j, chunk of kProjRows rows of
-// W_O); wave w takes rows w, w + 4, ...; lane (channel pair) and a wave sum per
-// (row, sequence).  E_out = ||dy_K + dy_V||^2: per-chunk sums, added in chunk
-// order by the last workgroup of head j.
+// dy = dO W_O,j^T for every sequence: workgroup (head j, chunk of kProjRows rows
+// of W_O), one thread per row r reading its 128 weights (a 256 or 512 B
+// contiguous run; a wave's 64 runs stay in L1 while it walks them) against dO
+// rows broadcast from LDS, so no cross-lane sums are needed and dy stores are
+// coalesced.  E_out = ||dy_K + dy_V||^2: per-chunk sums, added in chunk order by
+// the last workgroup of head j.
 template <bool kWF32>
 __global__ __launch_bounds__(kEvThreads) void eval_project_kernel(const EvalParams p) {
+  static_assert(kProjRows == kEvThreads, "one row per thread");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -526,32 +535,53 @@ __global__ __launch_bounds__(kEvThreads) void eval_project_kernel(const EvalPara
     const int bb = idx / (2 * kHeadDim), c = idx % (2 * kHeadDim);
     s_do[bb][c] = p.dobuf[(static_cast<size_t>(bb) * Hq + j) * 2 * kHeadDim + c];
   }
-  for (int idx = tid; idx < kEvWaves * kMaxEvalBatch; idx += kEvThreads) s_e[idx / kMaxEvalBatch][idx % kMaxEvalBatch] = 0.0f;
   __syncthreads();
-  const int r0 = chunk * kProjRows;
-  const int r1 = min(r0 + kProjRows, p.d_model);
-  const size_t ld = static_cast<size_t>(Hq) * kHeadDim;
-  for (int r = r0 + wave; r < r1; r += kEvWaves) {
-    float w0, w1;
-    const size_t wi = r * ld + static_cast<size_t>(j) * kHeadDim + 2 * lane;
-    if (kWF32) {
-      const float* w = static_cast<const float*>(p.w_o) + wi;
-      w0 = w[0];
-      w1 = w[1];
-    } else {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.w_o) + wi);
-      w0 = __uint_as_float(w << 16);
-      w1 = __uint_as_float(w & 0xffff0000u);
+  const int r = chunk * kProjRows + tid;
+  const bool live = r < p.d_model;
+  const size_t w0i = static_cast<size_t>(live ? r : 0) * Hq * kHeadDim + static_cast<size_t>(j) * kHeadDim;
+  for (int bb0 = 0; bb0 < B; bb0 += 4) {  // four sequences per pass over the row
+    float ak[4] = {0.0f, 0.0f, 0.0f, 0.0f}, av[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int c8 = 0; c8 < kHeadDim / 8; ++c8) {
+      float w[8];
+      if (kWF32) {
+        const float4v a = *reinterpret_cast<const float4v*>(static_cast<const float*>(p.w_o) + w0i + 8 * c8);
+        const float4v b = *reinterpret_cast<const float4v*>(static_cast<const float*>(p.w_o) + w0i + 8 * c8 + 4);
+        for (int e = 0; e < 4; ++e) {
+          w[e] = a[e];
+          w[4 + e] = b[e];
+        }
+      } else {
+        const uint4v a = *reinterpret_cast<const uint4v*>(static_cast<const uint16_t*>(p.w_o) + w0i + 8 * c8);
+        for (int e = 0; e < 4; ++e) {
+          w[2 * e] = __uint_as_float(a[e] << 16);
+          w[2 * e + 1] = __uint_as_float(a[e] & 0xffff0000u);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (bb0 + u < B) {
+          const float* dk = s_do[bb0 + u] + 8 * c8;
+          const float* dv = s_do[bb0 + u] + kHeadDim + 8 * c8;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            ak[u] = fmaf(dk[e], w[e], ak[u]);
+            av[u] = fmaf(dv[e], w[e], av[u]);
+          }
+        }
+      }
     }
-    for (int bb = 0; bb < B; ++bb) {
-      const float pk = wave_sum(fmaf(s_do[bb][2 * lane], w0, s_do[bb][2 * lane + 1] * w1));
-      const float pv = wave_sum(fmaf(s_do[bb][kHeadDim + 2 * lane], w0, s_do[bb][kHeadDim + 2 * lane + 1] * w1));
-      if (lane == 0) {
-        const size_t oi = (static_cast<size_t>(bb) * Hq + j) * p.d_model + r;
-        p.dy_k[oi] = pk;
-        p.dy_v[oi] = pv;
-        const float dy = pk + pv;
-        s_e[wave][bb] = fmaf(dy, dy, s_e[wave][bb]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int bb = bb0 + u;
+      if (bb < B) {
+        if (live) {
+          const size_t oi = (static_cast<size_t>(bb) * Hq + j) * p.d_model + r;
+          p.dy_k[oi] = ak[u];
+          p.dy_v[oi] = av[u];
+        }
+        const float dy = ak[u] + av[u];
+        const float e = wave_sum(live ? dy * dy : 0.0f);
+        if (lane == 0) s_e[wave][bb] = e;
       }
     }
   }

@@ -84,7 +84,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t e
 constexpr int kEvPartStride = 392;   // split partial row: A, B, C [128 each], m_a, l_a, m_q, l_q, e_rec (head 0)
 constexpr int kMaxEvalBatch = 64;
 constexpr int kMaxEvalSplits = 256;
-constexpr int kProjRows = 128;       // rows of W_O per projection workgroup
+constexpr int kProjRows = 256;       // rows of W_O per projection workgroup (one per thread)
 constexpr int kEvHeads = 8;          // query heads per evaluator workgroup (g = 16 takes two chunks)
 
 struct EvalParams {
