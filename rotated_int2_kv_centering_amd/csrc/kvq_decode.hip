@@ -82,6 +82,15 @@ __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, void* 
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_addr)
                : "memory", "m0");
 }
+
+// dma16 with the cache policy of an agent-scope load (sc1): reads what other
+// workgroups stored with agent-scope stores, as ld_agent does.
+__device__ __forceinline__ void dma16_agent(const uint8_t* base, uint32_t voff, void* lds) {
+  const uint32_t lds_addr =
+      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(lds))));
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 sc1" ::"v"(voff), "s"(base), "s"(lds_addr)
+               : "memory", "m0");
+}
 template <int kN>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kN) : "memory");
@@ -821,15 +830,19 @@ void decode_kernel(const DecodeParams p) {
   __syncthreads();
   if (s_ticket != n_valid - 1) return;
 
-  // Merge, in one load round: every (split, head) max/sum pair is loaded by
-  // one thread and shared through LDS (the ring is free now), while thread
-  // (head jh, channel c) loads acc[c] of the first kAB splits; this
-  // workgroup's own split comes from registers.
+  // Merge, in one load round.  Without a window, when they fit, the split
+  // partial rows (contiguous in the workspace) are copied whole into the ring,
+  // which is free now, by 16-byte coherent DMA (1 KB per wave instruction).
+  // Otherwise every (split, head) max/sum pair is loaded by one thread and
+  // shared through LDS, while thread (head jh, channel c) loads acc[c] of the
+  // first kAB splits; this workgroup's own split comes from registers.
   constexpr int kAB = kNQ == 1 ? 32 : 8;  // splits per acc load round
   static_assert(sizeof(s_ring) >= sizeof(float) * 2 * kMaxSplits * kNH, "max/sum pairs fit in the ring");
   const float* pb = p.part + head_base * g * kPartStride;
   float* s_ml = s_post;  // [split][head][2]: max, sum
   const int n_ml = n_valid * g;
+  const int n_img = n_ml * kPartStride;  // floats of the partial rows
+  const bool img = !has_win && n_img + 64 * 4 <= static_cast<int>(sizeof(s_ring) / sizeof(float));
   float av[kIdx][kAB];
   auto load_acc = [&](int k, int s0) {
     const int idx = min(tid + k * kThreads, g * kHeadDim - 1);
@@ -838,12 +851,21 @@ void decode_kernel(const DecodeParams p) {
     for (int u = 0; u < kAB; ++u) av[k][u] = ld_agent(pb + (min(s0 + u, n_valid - 1) * g + jh) * kPartStride + c);
   };
   float ml0 = 0.0f, ml1 = 0.0f;
-  if (tid < n_ml) {
-    ml0 = ld_agent(pb + static_cast<size_t>(tid) * kPartStride + 128);  // split tid / g, head tid % g
-    ml1 = ld_agent(pb + static_cast<size_t>(tid) * kPartStride + 129);
-  }
+  if (img) {
+    // chunk ch of 16 B lands at s_post + 4 ch; the last instruction's spare
+    // lanes repeat the last chunk into the 1 KB of slack after the rows
+    static_assert(kPartStride % 4 == 0, "partial rows are whole 16-byte chunks");
+    const int n_ch = n_img / 4;
+    for (int c0 = 64 * wave; c0 < n_ch; c0 += 64 * kW)
+      dma16_agent(reinterpret_cast<const uint8_t*>(pb), 16 * min(c0 + lane, n_ch - 1), s_post + 4 * c0);
+  } else {
+    if (tid < n_ml) {
+      ml0 = ld_agent(pb + static_cast<size_t>(tid) * kPartStride + 128);  // split tid / g, head tid % g
+      ml1 = ld_agent(pb + static_cast<size_t>(tid) * kPartStride + 129);
+    }
 #pragma unroll
-  for (int k = 0; k < kIdx; ++k) load_acc(k, 0);
+    for (int k = 0; k < kIdx; ++k) load_acc(k, 0);
+  }
 
   // Exact window (g <= 8), on the matrix cores (v_mfma_f32_16x16x32_bf16; the
   // window rows are exact bf16).  Rows: n_ws sinks, then positions w_r0 .. T-1,
@@ -940,7 +962,7 @@ void decode_kernel(const DecodeParams p) {
     }
     if (tid < kHeadDim && p.win_mu != nullptr) wmu = p.win_mu[h * kHeadDim + tid];
   }
-  for (int q = tid; q < n_ml; q += kThreads) {
+  for (int q = tid; q < (img ? 0 : n_ml); q += kThreads) {
     if (q != tid) {  // beyond the first pair per thread
       ml0 = ld_agent(pb + static_cast<size_t>(q) * kPartStride + 128);
       ml1 = ld_agent(pb + static_cast<size_t>(q) * kPartStride + 129);
@@ -978,6 +1000,7 @@ void decode_kernel(const DecodeParams p) {
     }
     if (tid < kHeadDim) s_post[kWmuOff + tid] = wmu;
   }
+  if (img) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial-row copies have landed
   __syncthreads();
   if (win_here) {
     const int hq = lane & 15, kq = lane >> 4;
@@ -1083,6 +1106,19 @@ void decode_kernel(const DecodeParams p) {
     const int jh = idx / kHeadDim;
     const int c = idx % kHeadDim;
     float M = kNegBig, l = 0.0f;
+    if (img) {  // the whole rows are in the ring: [split][head][acc 128 | max | sum | pad]
+      const float* row = s_post + jh * kPartStride;
+      for (int sp = 0; sp < n_valid; ++sp) M = fmaxf(M, row[sp * g * kPartStride + 128]);
+      float o = 0.0f;
+      for (int sp = 0; sp < n_valid; ++sp) {
+        const float* r = row + sp * g * kPartStride;
+        const float w = __builtin_amdgcn_exp2f(r[128] - M);
+        l = fmaf(w, r[129], l);
+        o = fmaf(w, r[c], o);
+      }
+      s_q[jh][c] = l > 0.0f ? o / l : 0.0f;  // o_rot
+      continue;
+    }
     for (int sp = 0; sp < n_valid; ++sp) M = fmaxf(M, s_ml[2 * (sp * g + jh)]);
     const float wm = win_here ? s_post[kWmlOff + 2 * jh] : kNegBig;
     M = fmaxf(M, wm);
