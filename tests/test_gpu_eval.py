@@ -180,3 +180,12 @@ def test_full_size_llama8b_t32k():
     case = I.llama8b_case(32768)
     ev = Evaluated(case, dev, d_model=4096)
     _check(ev.run(), ev.oracle())
+
+
+def test_full_size_llama8b_t128k():
+    """The evaluator's benchmark configuration: the 8B shape at 128K with a 4096-wide
+    bf16 W_O, every head against the oracle."""
+    dev = require_gpu()
+    case = I.llama8b_case(131072)
+    ev = Evaluated(case, dev, d_model=4096)
+    _check(ev.run(), ev.oracle())
