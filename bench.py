@@ -136,10 +136,11 @@ def read_ceiling_gbps(torch, dev, n_bytes: int = 2 << 30) -> float:
     return best
 
 
-def cpu_baseline(case, pool_np, kv_heads_sample: int):
+def cpu_baseline(case, pool_np, kv_heads_sample: int, window=None):
     """Time the oracle (as it stands) on KV heads [0, kv_heads_sample) of the step:
-    the append of the newest token and the decode of their query heads, then scale
-    to the whole step.  BLAS is held to one thread, so cores = 1."""
+    the append of the newest token and the decode of their query heads (with the
+    exact window (sinks, recent) when given), then scale to the whole step.  BLAS
+    is held to one thread, so cores = 1."""
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle import kvq_oracle as O
@@ -155,7 +156,13 @@ def cpu_baseline(case, pool_np, kv_heads_sample: int):
         pool = pool_np.copy()
         x, w = O.rotated_inputs(case.k[last], case.v[last], case.mu, r_k, r_v)
         O.quantize_append(pool, case.Hkv, case.slots[last], x, w)
-        O.decode_attention(case.q, pool, case.Hkv, case.page_table, case.seq_lens, r_k, r_v, heads=heads)
+        if window:
+            k_seqs = [case.k[case.tok_seq == b] for b in range(case.B)]
+            v_seqs = [case.v[case.tok_seq == b] for b in range(case.B)]
+            O.decode_attention_window(case.q, pool, case.Hkv, case.page_table, case.seq_lens, case.mu, r_k, r_v,
+                                      k_seqs, v_seqs, window[0], window[1], heads=heads)
+        else:
+            O.decode_attention(case.q, pool, case.Hkv, case.page_table, case.seq_lens, r_k, r_v, heads=heads)
         dt = time.perf_counter() - t0
     step_est = dt * case.Hkv / len(hs)
     tokens = float(case.seq_lens.sum())
@@ -225,6 +232,26 @@ def bench_evaluator(args, torch, I, kvq, dev, desc, case) -> int:
     achieved = alg / (ms * 1e-3) / 1e9
     log(f"[bench] output-error evaluator: {ms * 1e3:.1f} us per call ({args.steps} calls), {achieved:.0f} GB/s "
         f"algorithmic")
+    cpu = None
+    if args.cpu_kv_heads > 0:  # the oracle's output_error on KV heads [0, n), scaled to all heads
+        from threadpoolctl import threadpool_limits
+        from oracle import kvq_oracle as O
+        log("[bench] timing the oracle on the CPU ...")
+        hs = list(range(min(args.cpu_kv_heads, case.Hkv, 1)))
+        rk, rv = case.r_k, case.r_v
+        if case.rotation == "hadamard":
+            rk, rv = O.hadamard_rotation(rk), O.hadamard_rotation(rv)
+        pool_np = pool.cpu().numpy()
+        k_seqs = [case.k[case.tok_seq == b] for b in range(case.B)]
+        v_seqs = [case.v[case.tok_seq == b] for b in range(case.B)]
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            O.output_error(case.q, pool_np, case.Hkv, case.page_table, case.seq_lens, k_seqs, v_seqs, case.mu, rk, rv,
+                           I.bf16_to_f32(w_bits), kv_heads=hs)
+            dt = time.perf_counter() - t0
+        cpu = {"value": tokens / (dt * case.Hkv / len(hs)), "unit": "KV-tokens/s", "cores": 1, "kind": "oracle",
+               "sample": f"oracle (NumPy fp64) output_error on KV head 0 of {case.Hkv} ({dt:.1f} s), scaled by "
+                         f"{case.Hkv}"}
     res = {
         "metric": "INT2 output-error evaluator (Eq. 6-10) KV-tokens/s",
         "value": tokens / (ms * 1e-3), "unit": "KV-tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -233,7 +260,7 @@ def bench_evaluator(args, torch, I, kvq, dev, desc, case) -> int:
         "config": {"workload": desc, "d_model": d_model, "rotation": args.rotation},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": None},
-        "cpu_baseline": None,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
     return 0
@@ -427,12 +454,15 @@ def main() -> int:
     # with an exact window: its bf16 key and value rows (512 B per position per KV head) are read too
     alg_bytes += n_win_tok * case.Hkv * 512
     achieved = alg_bytes / (split_avg_ms * 1e-3) / 1e9
-    traffic = counters_for(kernel_source_sha(), args.workload + ("" if args.rotation == "dense" else "_" + args.rotation))
+    # the committed counter summaries are per workload, without a window and with a dense R
+    variant = ("" if args.rotation == "dense" else "_" + args.rotation) + (f"_window{sinks}_{recent}" if n_win_tok else "")
+    traffic = counters_for(kernel_source_sha(), args.workload + variant)
 
     cpu = None
     if args.cpu_kv_heads > 0:
         log("[bench] timing the oracle on the CPU ...")
-        cpu = cpu_baseline(case, pools[0].cpu().numpy(), args.cpu_kv_heads)
+        cpu = cpu_baseline(case, pools[0].cpu().numpy(), args.cpu_kv_heads,
+                           window=(sinks, recent) if (sinks or recent) else None)
 
     res = {
         "metric": "INT2 decode attention KV-tokens/s + HBM GB/s (% peak), 8B GQA shape @128K",

@@ -551,7 +551,7 @@ def present_positions(table_row, seq_len: int, num_pages: int) -> np.ndarray:
 
 
 def output_error(q, pool, num_kv_heads, page_table, seq_lens, k_seqs, v_seqs, mu, r_k, r_v, w_o,
-                 sm_scale=None, num_pages=None):
+                 sm_scale=None, num_pages=None, kv_heads=None):
     """OptR §3.2 Eq. (6)-(10) at the decode position of every sequence, from the packed cache (fp64).
 
     Query head j of sequence b (KV head h = j // g) attends positions 0..T_b-1.
@@ -562,6 +562,8 @@ def output_error(q, pool, num_kv_heads, page_table, seq_lens, k_seqs, v_seqs, mu
     projection, row-major).  Per (b, j) this is ``output_error_terms``.
     Returns dy_k, dy_v [B, H_q, d_model], e_out [B, H_q] (Eq. (10)) and
     e_rec [B, H_kv] (Eq. (9), the cache of sequence b and KV head h).
+    ``kv_heads`` (default all) limits the work to those KV heads and their query
+    heads; the other entries stay zero.
     """
     q = np.asarray(q, np.float64)
     B, Hq, d = q.shape
@@ -578,7 +580,7 @@ def output_error(q, pool, num_kv_heads, page_table, seq_lens, k_seqs, v_seqs, mu
     for b in range(B):
         T = int(seq_lens[b])
         keep = present_positions(page_table[b], T, num_pages)
-        for h in range(num_kv_heads):
+        for h in (range(num_kv_heads) if kv_heads is None else kv_heads):
             x_hat, w_hat = gather_sequence(pool, num_kv_heads, page_table[b], T, h, num_pages)
             k_eff = x_hat @ np.asarray(r_k[h], np.float64).T + np.asarray(mu[h], np.float64)
             v_eff = w_hat @ np.asarray(r_v[h], np.float64).T
