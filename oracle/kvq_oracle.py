@@ -55,6 +55,13 @@ token slots of one (page p, KV head h) and starts at byte (p*H_kv + h)*1536:
   (channels 32*grp .. 32*grp+31): at byte 1024 + 32*m + 4*i the K pair and at
   byte 1024 + 32*m + 16 + 4*i the V pair, each pair being the fp16 scale
   (low two bytes) then the fp16 zero, little-endian.
+
+With 4-bit keys (key_bits = 4: the asymmetric K4V2 budget) a block is 2048
+bytes.  The 1536 bytes above keep their layout, the K words holding the low
+two bits of each key code (code & 3); bytes [1536, 2048) are 64 records of 8
+bytes, record r = 16*a + s holding words H0, H1 at byte 1536 + 8*r: the high
+two bits (code >> 2) of the key code of slot s, channel c sit in record
+16*a + s, word H[kk // 2], at the same bit as its low bits in K[kk // 2].
 """
 
 from __future__ import annotations
@@ -67,6 +74,13 @@ N_GROUPS = HEAD_DIM // GROUP
 PAGE = 16
 BLOCK_BYTES = 1536
 CODE_BYTES = 1024
+HI_PLANE = 1536  # byte offset of the 4-bit keys' high-bit plane
+
+
+def block_bytes(key_bits: int = 2) -> int:
+    """Bytes of one (page, KV head) block: 1536 for 2-bit keys, 2048 for 4-bit keys."""
+    assert key_bits in (2, 4), "key codes are 2 or 4 bits"
+    return BLOCK_BYTES if key_bits == 2 else BLOCK_BYTES + 512
 
 
 # --------------------------------------------------------------------- checks
@@ -128,8 +142,10 @@ def rotated_inputs(k, v, mu, r_k, r_v):
 
 
 # ---------------------------------------------------------- INT2 quantizer Q2
-def int2_quantize(x: np.ndarray, clip: float = 1.0, group: int = GROUP):
-    """OptR §3.1: Q2(.; c, G), asymmetric, on fp32 rows of 128 channels.
+def int2_quantize(x: np.ndarray, clip: float = 1.0, group: int = GROUP, bits: int = 2):
+    """OptR §3.1: Q2(.; c, G), asymmetric, on fp32 rows of 128 channels;
+    ``bits`` = 4 gives the same quantizer with 16 levels (the 4-bit keys of a
+    K4V2 budget): the divisor 3 below becomes 15 and codes run 0..15.
 
     ``x`` is float32 [..., 128].  Groups are G = ``group`` (32, 64 or 128)
     consecutive channels.  For each
@@ -156,11 +172,13 @@ def int2_quantize(x: np.ndarray, clip: float = 1.0, group: int = GROUP):
     c = np.float32(clip)
     assert np.float32(0.0) < c <= np.float32(1.0), "clip ratio must be in (0, 1]"
     assert group in (32, 64, 128), "group size must be 32, 64 or 128"
+    assert bits in (2, 4), "2 or 4 bits"
+    n_lv = np.float32((1 << bits) - 1)
     xg = x.reshape(x.shape[:-1] + (HEAD_DIM // group, group))
     mn = (xg.min(axis=-1) * c).astype(np.float32)
     mx = (xg.max(axis=-1) * c).astype(np.float32)
     rng = (mx - mn).astype(np.float32)
-    s32 = (rng / np.float32(3.0)).astype(np.float32)
+    s32 = (rng / n_lv).astype(np.float32)
     s16 = s32.astype(np.float16)
     z16 = mn.astype(np.float16)
     assert np.isfinite(s16).all() and np.isfinite(z16).all(), "group range exceeds fp16"
@@ -169,7 +187,7 @@ def int2_quantize(x: np.ndarray, clip: float = 1.0, group: int = GROUP):
     t = (xg - z).astype(np.float32)
     with np.errstate(divide="ignore", invalid="ignore"):
         u = np.where(s > 0, t / np.where(s > 0, s, np.float32(1.0)), np.float32(0.0)).astype(np.float32)
-    codes = np.clip(np.rint(u), 0, 3).astype(np.uint8)
+    codes = np.clip(np.rint(u), 0, int(n_lv)).astype(np.uint8)
     return codes.reshape(x.shape), s16, z16
 
 
@@ -214,27 +232,38 @@ _V_POS = np.array([[_v_position(s, c) for c in range(HEAD_DIM)] for s in range(P
 
 
 def pack_block(k_codes, k_s16, k_z16, v_codes, v_s16, v_z16, block: np.ndarray | None = None,
-               slots=None) -> np.ndarray:
+               slots=None, key_bits: int = 2) -> np.ndarray:
     """Write token slots of one (page, KV head) block in the layout above.
 
     ``k_codes``/``v_codes`` are uint8 [n, 128]; scales/zeros float16 [n, 4];
     ``slots`` (default 0..n-1, distinct) are the slot indices inside the page.
     Bits of slots not written are left as they were in ``block``.
     """
-    blk = np.zeros(BLOCK_BYTES, np.uint8) if block is None else block
-    assert blk.shape == (BLOCK_BYTES,) and blk.dtype == np.uint8
+    nb = block_bytes(key_bits)
+    blk = np.zeros(nb, np.uint8) if block is None else block
+    assert blk.shape == (nb,) and blk.dtype == np.uint8
     n = np.asarray(k_codes).shape[0]
     slots = np.arange(n) if slots is None else np.asarray(slots, np.int64)
     assert len(np.unique(slots)) == len(slots)
     words = blk[:CODE_BYTES].view("<u4").reshape(-1)           # 64 records x 4 words
-    for codes, table in ((k_codes, _K_POS), (v_codes, _V_POS)):
+    k_codes = np.asarray(k_codes, np.uint32)
+    assert key_bits == 4 or k_codes.max(initial=0) <= 3
+    for codes, table in ((k_codes & 3, _K_POS), (v_codes, _V_POS)):
         pos = table[slots]                                      # [n, 128, (record, word, bit)]
         idx = (pos[..., 0] * 4 + pos[..., 1]).reshape(-1)
         bit = pos[..., 2].reshape(-1).astype(np.uint32)
         val = np.asarray(codes, np.uint32).reshape(-1)
         np.bitwise_and.at(words, idx, ~(np.uint32(3) << bit))
         np.bitwise_or.at(words, idx, (val & np.uint32(3)) << bit)
-    meta = blk[CODE_BYTES:].view("<u2").reshape(16, 2, 4, 2)   # [record m][K/V][i][scale/zero]
+    if key_bits == 4:  # high bits of the key codes: record r at 1536 + 8 r, word H[kk // 2], same bit
+        hi = blk[HI_PLANE:].view("<u4").reshape(-1)              # 64 records x 2 words
+        pos = _K_POS[slots]
+        idx = (pos[..., 0] * 2 + pos[..., 1]).reshape(-1)
+        bit = pos[..., 2].reshape(-1).astype(np.uint32)
+        val = (k_codes >> np.uint32(2)).reshape(-1)
+        np.bitwise_and.at(hi, idx, ~(np.uint32(3) << bit))
+        np.bitwise_or.at(hi, idx, (val & np.uint32(3)) << bit)
+    meta = blk[CODE_BYTES:BLOCK_BYTES].view("<u2").reshape(16, 2, 4, 2)   # [record m][K/V][i][scale/zero]
     for idx, s in enumerate(slots):
         a, i = int(s) // 4, int(s) % 4
         for grp in range(N_GROUPS):
@@ -246,15 +275,15 @@ def pack_block(k_codes, k_s16, k_z16, v_codes, v_s16, v_z16, block: np.ndarray |
     return blk
 
 
-def unpack_blocks(blocks: np.ndarray):
+def unpack_blocks(blocks: np.ndarray, key_bits: int = 2):
     """Inverse of ``pack_block`` for a stack of blocks [n, 1536] (all 16 slots each).
 
     Returns (k_codes, k_s16, k_z16, v_codes, v_s16, v_z16) with codes uint8
     [n, 16, 128] and scales/zeros float16 [n, 16, 4].
     """
-    blk = np.ascontiguousarray(blocks, np.uint8).reshape(-1, BLOCK_BYTES)
+    blk = np.ascontiguousarray(blocks, np.uint8).reshape(-1, block_bytes(key_bits))
     words = blk[:, :CODE_BYTES].view("<u4").reshape(-1, 64, 4).astype(np.int64)
-    meta = blk[:, CODE_BYTES:].view("<f2").reshape(-1, 16, 2, 4, 2)   # [n][record m][K/V][i][scale/zero]
+    meta = blk[:, CODE_BYTES:BLOCK_BYTES].view("<f2").reshape(-1, 16, 2, 4, 2)   # [n][record m][K/V][i][scale/zero]
 
     def gather(pos):
         rec, word, bit = pos[..., 0], pos[..., 1], pos[..., 2]      # [16, 128] each
@@ -263,34 +292,40 @@ def unpack_blocks(blocks: np.ndarray):
     slots = np.arange(PAGE)
     rec = 4 * np.arange(N_GROUPS)[None, :] + (slots // 4)[:, None]     # [slot, grp] -> record m
     i = np.broadcast_to((slots % 4)[:, None], rec.shape)
-    return (gather(_K_POS), meta[:, rec, 0, i, 0], meta[:, rec, 0, i, 1],
+    k = gather(_K_POS)
+    if key_bits == 4:
+        hi = blk[:, HI_PLANE:].view("<u4").reshape(-1, 64, 2).astype(np.int64)
+        r_, w_, b_ = _K_POS[..., 0], _K_POS[..., 1], _K_POS[..., 2]
+        k = k + (((hi[:, r_, w_] >> b_[None]) & 3) << 2).astype(np.uint8)
+    return (k, meta[:, rec, 0, i, 0], meta[:, rec, 0, i, 1],
             gather(_V_POS), meta[:, rec, 1, i, 0], meta[:, rec, 1, i, 1])
 
 
-def unpack_block(block: np.ndarray):
+def unpack_block(block: np.ndarray, key_bits: int = 2):
     """``unpack_blocks`` for a single block: codes [16, 128], scales/zeros [16, 4]."""
-    return tuple(x[0] for x in unpack_blocks(np.asarray(block, np.uint8)[None]))
+    return tuple(x[0] for x in unpack_blocks(np.asarray(block, np.uint8)[None], key_bits))
 
 
-def pool_bytes(num_pages: int, num_kv_heads: int) -> int:
-    return int(num_pages) * int(num_kv_heads) * BLOCK_BYTES
+def pool_bytes(num_pages: int, num_kv_heads: int, key_bits: int = 2) -> int:
+    return int(num_pages) * int(num_kv_heads) * block_bytes(key_bits)
 
 
-def block_view(pool: np.ndarray, page: int, h: int, num_kv_heads: int) -> np.ndarray:
-    off = (int(page) * num_kv_heads + int(h)) * BLOCK_BYTES
-    return pool[off:off + BLOCK_BYTES]
+def block_view(pool: np.ndarray, page: int, h: int, num_kv_heads: int, key_bits: int = 2) -> np.ndarray:
+    nb = block_bytes(key_bits)
+    off = (int(page) * num_kv_heads + int(h)) * nb
+    return pool[off:off + nb]
 
 
 # ------------------------------------------------------------- quantize-append
 def quantize_append(pool: np.ndarray, num_kv_heads: int, slots, x: np.ndarray, w: np.ndarray,
-                    clip: float = 1.0, group: int = GROUP) -> None:
+                    clip: float = 1.0, group: int = GROUP, key_bits: int = 2) -> None:
     """Quantize rotated fp32 rows and store them at the given cache slots.
 
     ``x``/``w`` are float32 [n, H_kv, 128] (already centred and rotated);
     ``slots[n]`` = page*16 + offset, all distinct; ``clip`` and ``group`` are
     Q2's clip ratio c and group size G.  Writes ``pool`` (uint8) in place.
     """
-    kc, ks, kz = int2_quantize(x, clip, group)
+    kc, ks, kz = int2_quantize(x, clip, group, key_bits)
     vc, vs, vz = int2_quantize(w, clip, group)
     ks, kz, vs, vz = (meta_per_32(a) for a in (ks, kz, vs, vz))
     slots = np.asarray(slots, np.int64)
@@ -301,15 +336,16 @@ def quantize_append(pool: np.ndarray, num_kv_heads: int, slots, x: np.ndarray, w
         offs = slots[sel] % PAGE
         for h in range(num_kv_heads):
             pack_block(kc[sel, h], ks[sel, h], kz[sel, h], vc[sel, h], vs[sel, h], vz[sel, h],
-                       block=block_view(pool, page, h, num_kv_heads), slots=offs)
+                       block=block_view(pool, page, h, num_kv_heads, key_bits), slots=offs, key_bits=key_bits)
 
 
-def append_tokens(pool, num_kv_heads, slots, k, v, mu, r_k, r_v, clip: float = 1.0, group: int = GROUP) -> None:
+def append_tokens(pool, num_kv_heads, slots, k, v, mu, r_k, r_v, clip: float = 1.0, group: int = GROUP,
+                  key_bits: int = 2) -> None:
     """Full write path: centre keys, rotate K and V, quantize, pack (OptR §1, §3.1 Eq. (4))."""
     check_orthogonal_all(r_k)
     check_orthogonal_all(r_v)
     x, w = rotated_inputs(k, v, mu, r_k, r_v)
-    quantize_append(pool, num_kv_heads, slots, x, w, clip, group)
+    quantize_append(pool, num_kv_heads, slots, x, w, clip, group, key_bits)
 
 
 def check_orthogonal_all(r: np.ndarray, tol: float = 1e-6) -> None:
@@ -318,7 +354,7 @@ def check_orthogonal_all(r: np.ndarray, tol: float = 1e-6) -> None:
 
 
 # ----------------------------------------------------------- reading the cache
-def gather_sequence(pool, num_kv_heads, table_row, seq_len, h, num_pages=None):
+def gather_sequence(pool, num_kv_heads, table_row, seq_len, h, num_pages=None, key_bits: int = 2):
     """Dequantized rotated keys x_hat and values w_hat [T', 128] of one sequence and KV head (fp64).
 
     A table entry outside [0, num_pages) marks an absent page: its positions
@@ -330,12 +366,12 @@ def gather_sequence(pool, num_kv_heads, table_row, seq_len, h, num_pages=None):
         return np.zeros((0, HEAD_DIM)), np.zeros((0, HEAD_DIM))
     n_pages = (T + PAGE - 1) // PAGE
     if num_pages is None:
-        num_pages = np.asarray(pool).size // (num_kv_heads * BLOCK_BYTES)
+        num_pages = np.asarray(pool).size // (num_kv_heads * block_bytes(key_bits))
     pages = np.asarray(table_row[:n_pages], np.int64)
     present = (pages >= 0) & (pages < num_pages)
-    offs = (np.where(present, pages, 0) * num_kv_heads + int(h)) * BLOCK_BYTES
-    blocks = np.asarray(pool, np.uint8)[offs[:, None] + np.arange(BLOCK_BYTES)[None, :]]
-    kc, ks, kz, vc, vs, vz = unpack_blocks(blocks)
+    offs = (np.where(present, pages, 0) * num_kv_heads + int(h)) * block_bytes(key_bits)
+    blocks = np.asarray(pool, np.uint8)[offs[:, None] + np.arange(block_bytes(key_bits))[None, :]]
+    kc, ks, kz, vc, vs, vz = unpack_blocks(blocks, key_bits)
     keep = np.repeat(present, PAGE)[:T]
     x = int2_dequantize(kc, ks, kz).reshape(-1, HEAD_DIM)[:T][keep]
     w = int2_dequantize(vc, vs, vz).reshape(-1, HEAD_DIM)[:T][keep]
@@ -360,7 +396,7 @@ def softmax_attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray, scale
 
 
 def decode_attention(q, pool, num_kv_heads, page_table, seq_lens, r_k, r_v, sm_scale=None,
-                     heads=None, bypass=None, num_pages=None) -> np.ndarray:
+                     heads=None, bypass=None, num_pages=None, key_bits: int = 2) -> np.ndarray:
     """Decode attention read from the packed cache (OptR §3.2 Eq. (5), §3.1 Eq. (4)).
 
     For query head j of sequence b, with h = j // g:
@@ -387,7 +423,8 @@ def decode_attention(q, pool, num_kv_heads, page_table, seq_lens, r_k, r_v, sm_s
         h = j // g
         if (b, h) not in cache:
             if bypass is None:
-                cache[(b, h)] = gather_sequence(pool, num_kv_heads, page_table[b], seq_lens[b], h, num_pages)
+                cache[(b, h)] = gather_sequence(pool, num_kv_heads, page_table[b], seq_lens[b], h, num_pages,
+                                                key_bits)
             else:
                 x, w, tok_seq = bypass
                 sel = np.asarray(tok_seq) == b
@@ -421,7 +458,7 @@ def window_slot(t: int, sinks: int, recent: int) -> int:
 
 
 def effective_kv_window(pool, num_kv_heads, table_row, seq_len, h, mu_h, r_k_h, r_v_h, k_exact, v_exact,
-                        sinks, recent, num_pages=None):
+                        sinks, recent, num_pages=None, key_bits: int = 2):
     """Keys and values attention uses for one sequence and KV head, in the original basis (fp64).
 
     Window positions (``window_mask``) take k_exact[s], v_exact[s] (the BF16
@@ -437,12 +474,12 @@ def effective_kv_window(pool, num_kv_heads, table_row, seq_len, h, mu_h, r_k_h, 
     win = window_mask(T, sinks, recent)
     n_pages = (T + PAGE - 1) // PAGE
     if num_pages is None:
-        num_pages = np.asarray(pool).size // (num_kv_heads * BLOCK_BYTES)
+        num_pages = np.asarray(pool).size // (num_kv_heads * block_bytes(key_bits))
     pages = np.asarray(table_row[:n_pages], np.int64)
     present = (pages >= 0) & (pages < num_pages)
-    offs = (np.where(present, pages, 0) * num_kv_heads + int(h)) * BLOCK_BYTES
-    blocks = np.asarray(pool, np.uint8)[offs[:, None] + np.arange(BLOCK_BYTES)[None, :]]
-    kc, ks, kz, vc, vs, vz = unpack_blocks(blocks)
+    offs = (np.where(present, pages, 0) * num_kv_heads + int(h)) * block_bytes(key_bits)
+    blocks = np.asarray(pool, np.uint8)[offs[:, None] + np.arange(block_bytes(key_bits))[None, :]]
+    kc, ks, kz, vc, vs, vz = unpack_blocks(blocks, key_bits)
     x_hat = int2_dequantize(kc, ks, kz).reshape(-1, HEAD_DIM)[:T]
     w_hat = int2_dequantize(vc, vs, vz).reshape(-1, HEAD_DIM)[:T]
     k_int2 = x_hat @ np.asarray(r_k_h, np.float64).T + np.asarray(mu_h, np.float64)
@@ -454,7 +491,7 @@ def effective_kv_window(pool, num_kv_heads, table_row, seq_len, h, mu_h, r_k_h, 
 
 
 def decode_attention_window(q, pool, num_kv_heads, page_table, seq_lens, mu, r_k, r_v, k_seqs, v_seqs,
-                            sinks, recent, sm_scale=None, heads=None, num_pages=None) -> np.ndarray:
+                            sinks, recent, sm_scale=None, heads=None, num_pages=None, key_bits: int = 2) -> np.ndarray:
     """OptR §3.2 Eq. (5) with the BF16 window: Eq. (1)-(2) attention of query
     head j of sequence b over ``effective_kv_window`` of KV head h = j // g.
 
@@ -475,7 +512,7 @@ def decode_attention_window(q, pool, num_kv_heads, page_table, seq_lens, mu, r_k
         if (b, h) not in cache:
             cache[(b, h)] = effective_kv_window(pool, num_kv_heads, page_table[b], seq_lens[b], h, mu[h], r_k[h],
                                                 r_v[h], np.asarray(k_seqs[b])[:, h], np.asarray(v_seqs[b])[:, h],
-                                                sinks, recent, num_pages)
+                                                sinks, recent, num_pages, key_bits)
         k_eff, v_eff = cache[(b, h)]
         out[b, j] = softmax_attention(q[b, j], k_eff, v_eff, sm_scale)
     return out
@@ -551,7 +588,7 @@ def present_positions(table_row, seq_len: int, num_pages: int) -> np.ndarray:
 
 
 def output_error(q, pool, num_kv_heads, page_table, seq_lens, k_seqs, v_seqs, mu, r_k, r_v, w_o,
-                 sm_scale=None, num_pages=None, kv_heads=None):
+                 sm_scale=None, num_pages=None, kv_heads=None, key_bits: int = 2):
     """OptR §3.2 Eq. (6)-(10) at the decode position of every sequence, from the packed cache (fp64).
 
     Query head j of sequence b (KV head h = j // g) attends positions 0..T_b-1.
@@ -572,7 +609,7 @@ def output_error(q, pool, num_kv_heads, page_table, seq_lens, k_seqs, v_seqs, mu
     w_o = np.asarray(w_o, np.float64)
     d_model = w_o.shape[0]
     if num_pages is None:
-        num_pages = np.asarray(pool).size // (num_kv_heads * BLOCK_BYTES)
+        num_pages = np.asarray(pool).size // (num_kv_heads * block_bytes(key_bits))
     dy_k = np.zeros((B, Hq, d_model))
     dy_v = np.zeros((B, Hq, d_model))
     e_out = np.zeros((B, Hq))
@@ -581,7 +618,7 @@ def output_error(q, pool, num_kv_heads, page_table, seq_lens, k_seqs, v_seqs, mu
         T = int(seq_lens[b])
         keep = present_positions(page_table[b], T, num_pages)
         for h in (range(num_kv_heads) if kv_heads is None else kv_heads):
-            x_hat, w_hat = gather_sequence(pool, num_kv_heads, page_table[b], T, h, num_pages)
+            x_hat, w_hat = gather_sequence(pool, num_kv_heads, page_table[b], T, h, num_pages, key_bits)
             k_eff = x_hat @ np.asarray(r_k[h], np.float64).T + np.asarray(mu[h], np.float64)
             v_eff = w_hat @ np.asarray(r_v[h], np.float64).T
             k_ex = np.asarray(k_seqs[b], np.float64)[:T, h][keep]

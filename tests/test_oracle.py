@@ -789,3 +789,103 @@ def test_output_error_leaves_out_absent_pages_and_exact_cache_gives_zero():
     z = O.output_error(c.q, pool, c.Hkv, c.page_table, c.seq_lens, [np.stack(eff_k, 1)], [np.stack(eff_v, 1)],
                        c.mu, c.r_k, c.r_v, w_o)
     assert max(np.abs(z[0]).max(), np.abs(z[1]).max(), z[2].max(), z[3].max()) < 1e-20
+
+
+# ------------------------------------------------- 4-bit keys (K4V2 budget)
+def test_k4_block_layout_golden(golden_dir):
+    """Hand-derived byte positions of 4-bit key codes (low bits in place, high
+    bits in the plane at byte 1536); values and metadata are unaffected."""
+    with open(os.path.join(golden_dir, "block_layout_k4.txt")) as f:
+        lines = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    z = np.zeros((1, 128), np.uint8)
+    zf = np.zeros((1, 4), np.float16)
+    for parts in lines:
+        slot, ch, code, *pairs = map(int, parts[1:])
+        kc = z.copy()
+        kc[0, ch] = code
+        blk = O.pack_block(kc, zf, zf, z, zf, zf, slots=[slot], key_bits=4)
+        assert blk.size == 2048
+        want = dict(zip(pairs[0::2], pairs[1::2]))
+        nz = np.nonzero(blk)[0]
+        assert set(nz) == set(want) and all(blk[b] == v for b, v in want.items()), parts
+        back = O.unpack_block(blk, key_bits=4)[0]
+        assert back[slot, ch] == code and np.count_nonzero(back) == 1
+    assert len(lines) == 4
+
+
+def test_quantizer_four_bits_hand_derived_and_nearest():
+    """bits = 4: a group holding 0..15 twice is exact (s = 1, z = 0); 7.5 ties to 8;
+    a group spanning [-1, 2] has s = fp16(0.2) = 0.199951171875, so 0 -> 5.  Every
+    code is the nearest of 16 levels (brute force); 2-bit and 4-bit agree on
+    the range (z and the span of the levels)."""
+    row = np.zeros(128, np.float32)
+    row[:32] = np.tile(np.arange(16, dtype=np.float32), 2)
+    row[32:64] = np.float32(0.0)
+    row[32], row[33], row[34] = 0.0, 7.5, 15.0
+    row[64:96] = np.float32(0.0)
+    row[64], row[65] = -1.0, 2.0
+    row[96:] = np.float32(3.0)
+    codes, s16, z16 = O.int2_quantize(row[None], bits=4)
+    np.testing.assert_array_equal(codes[0, :32], np.tile(np.arange(16), 2))
+    assert s16[0, 0] == np.float16(1.0) and z16[0, 0] == np.float16(0.0)
+    assert codes[0, 33] == 8 and codes[0, 34] == 15 and codes[0, 32] == 0
+    assert s16[0, 2] == np.float16(0.199951171875) and z16[0, 2] == np.float16(-1.0)
+    assert codes[0, 66] == 5 and codes[0, 64] == 0 and codes[0, 65] == 15
+    assert s16[0, 3] == 0 and np.all(codes[0, 96:] == 0)  # constant group
+    rng = np.random.default_rng(43)
+    x = _random_rows(rng, 64, 3.0, 0.5)
+    codes, s16, z16 = O.int2_quantize(x, bits=4)
+    assert codes.max() <= 15
+    xg = x.reshape(64, 4, 32).astype(np.float64)
+    levels = z16.astype(np.float64)[..., None, None] + s16.astype(np.float64)[..., None, None] * np.arange(16)
+    dist = np.abs(xg[..., None] - levels)
+    got = np.take_along_axis(dist, codes.reshape(64, 4, 32)[..., None].astype(np.int64), -1)[..., 0]
+    tol = 4 * np.spacing(np.maximum(s16.astype(np.float32), np.float32(1e-30))).astype(np.float64)[..., None]
+    assert np.all(got <= dist.min(-1) + tol + 1e-12)
+    c2, s2, z2 = O.int2_quantize(x)
+    np.testing.assert_array_equal(z2, z16)
+    np.testing.assert_allclose(3 * s2.astype(np.float64), 15 * s16.astype(np.float64), rtol=2e-3)
+
+
+def test_k4_pack_unpack_roundtrip_and_partial_writes():
+    rng = np.random.default_rng(44)
+    kc = rng.integers(0, 16, (16, 128)).astype(np.uint8)
+    vc = rng.integers(0, 4, (16, 128)).astype(np.uint8)
+    ks, kz, vs, vz = (rng.standard_normal((16, 4)).astype(np.float16) for _ in range(4))
+    blk = O.pack_block(kc, ks, kz, vc, vs, vz, key_bits=4)
+    out = O.unpack_block(blk, key_bits=4)
+    for got, want in zip(out, (kc, ks, kz, vc, vs, vz)):
+        np.testing.assert_array_equal(got, want)
+    # the 2-bit reading of the first 1536 bytes sees the low bits
+    np.testing.assert_array_equal(O.unpack_block(blk[:1536])[0], kc & 3)
+    # rewriting slots 3 and 9 leaves the other slots intact
+    kc2 = rng.integers(0, 16, (2, 128)).astype(np.uint8)
+    O.pack_block(kc2, ks[:2], kz[:2], vc[:2], vs[:2], vz[:2], block=blk, slots=[3, 9], key_bits=4)
+    back = O.unpack_block(blk, key_bits=4)[0]
+    np.testing.assert_array_equal(back[[3, 9]], kc2)
+    keep = np.setdiff1d(np.arange(16), [3, 9])
+    np.testing.assert_array_equal(back[keep], kc[keep])
+
+
+def test_k4_decode_equals_attention_on_effective_kv_and_is_closer():
+    """Decode over a 4-bit-key pool equals Eq. (1)-(2) attention on k~ = Q4((k - mu) R_K)
+    R_K^T + mu and v~ = Q2(v R_V) R_V^T (OptR §3.2, Eq. (5)); its key error is below
+    the 2-bit one."""
+    c = _tiny(B=2, Hq=8, Hkv=2, seq_lens=[50, 33], table_policy="permuted")
+    pool = np.zeros(O.pool_bytes(c.num_pages, c.Hkv, key_bits=4), np.uint8)
+    O.append_tokens(pool, c.Hkv, c.slots, c.k, c.v, c.mu, c.r_k, c.r_v, key_bits=4)
+    got = O.decode_attention(c.q, pool, c.Hkv, c.page_table, c.seq_lens, c.r_k, c.r_v, key_bits=4)
+    x, w = O.rotated_inputs(c.k, c.v, c.mu, c.r_k, c.r_v)
+    kq = O.int2_dequantize(*O.int2_quantize(x, bits=4))
+    vq = O.int2_dequantize(*O.int2_quantize(w))
+    for b in range(c.B):
+        sel = c.tok_seq == b
+        for j in range(c.Hq):
+            h = j // 4
+            k_eff = kq[sel, h] @ c.r_k[h].astype(np.float64).T + c.mu[h]
+            v_eff = vq[sel, h] @ c.r_v[h].astype(np.float64).T
+            ref = O.softmax_attention(c.q[b, j], k_eff, v_eff, 1 / np.sqrt(128))
+            np.testing.assert_allclose(got[b, j], ref, rtol=0, atol=1e-11)
+    e4 = np.abs(kq - x).mean()
+    e2 = np.abs(O.int2_dequantize(*O.int2_quantize(x)) - x).mean()
+    assert e4 < 0.3 * e2
