@@ -136,7 +136,7 @@ def read_ceiling_gbps(torch, dev, n_bytes: int = 2 << 30) -> float:
     return best
 
 
-def cpu_baseline(case, pool_np, kv_heads_sample: int, window=None):
+def cpu_baseline(case, pool_np, kv_heads_sample: int, window=None, key_bits: int = 2):
     """Time the oracle (as it stands) on KV heads [0, kv_heads_sample) of the step:
     the append of the newest token and the decode of their query heads (with the
     exact window (sinks, recent) when given), then scale to the whole step.  BLAS
@@ -155,14 +155,15 @@ def cpu_baseline(case, pool_np, kv_heads_sample: int, window=None):
         t0 = time.perf_counter()
         pool = pool_np.copy()
         x, w = O.rotated_inputs(case.k[last], case.v[last], case.mu, r_k, r_v)
-        O.quantize_append(pool, case.Hkv, case.slots[last], x, w)
+        O.quantize_append(pool, case.Hkv, case.slots[last], x, w, key_bits=key_bits)
         if window:
             k_seqs = [case.k[case.tok_seq == b] for b in range(case.B)]
             v_seqs = [case.v[case.tok_seq == b] for b in range(case.B)]
             O.decode_attention_window(case.q, pool, case.Hkv, case.page_table, case.seq_lens, case.mu, r_k, r_v,
-                                      k_seqs, v_seqs, window[0], window[1], heads=heads)
+                                      k_seqs, v_seqs, window[0], window[1], heads=heads, key_bits=key_bits)
         else:
-            O.decode_attention(case.q, pool, case.Hkv, case.page_table, case.seq_lens, r_k, r_v, heads=heads)
+            O.decode_attention(case.q, pool, case.Hkv, case.page_table, case.seq_lens, r_k, r_v, heads=heads,
+                               key_bits=key_bits)
         dt = time.perf_counter() - t0
     step_est = dt * case.Hkv / len(hs)
     tokens = float(case.seq_lens.sum())
@@ -278,6 +279,8 @@ def main() -> int:
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-kv-heads", type=int, default=8, help="KV heads in the oracle's timed sample (0 = skip)")
     ap.add_argument("--window", default="", help="exact bf16 window 'sinks,recent' (e.g. 4,128); default none")
+    ap.add_argument("--key-bits", type=int, default=2, choices=[2, 4],
+                    help="bits per key code: 2, or 4 (the K4V2 budget: 2048-byte blocks); values keep 2")
     ap.add_argument("--evaluator", action="store_true",
                     help="time the output-error evaluator (kvq_output_error) instead of the decode step")
     ap.add_argument("--rotation", default="dense", choices=["dense", "hadamard"],
@@ -317,8 +320,10 @@ def main() -> int:
     def B16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
-    cache_bytes = int(case.seq_lens.sum()) * case.Hkv * BYTES_PER_TOKEN_HEAD
-    pool_bytes = case.num_pages * case.Hkv * 1536
+    # per token and KV head: K and V codes, K and V (scale, zero); 4-bit keys add 32 B of key bits
+    bpt = BYTES_PER_TOKEN_HEAD + (32 if args.key_bits == 4 else 0)
+    cache_bytes = int(case.seq_lens.sum()) * case.Hkv * bpt
+    pool_bytes = case.num_pages * case.Hkv * (2048 if args.key_bits == 4 else 1536)
     n_rep = args.replicas or max(2, -(-2 * MALL_BYTES // pool_bytes) + 1)
 
     # ---- replica 0: bulk quantize-append of the whole context
@@ -328,7 +333,7 @@ def main() -> int:
     pools, caches, rks, rvs, mus = [], [], [], [], []
     for r in range(n_rep):
         pools.append(torch.zeros(pool_bytes, dtype=torch.uint8, device=dev))
-        caches.append(kvq.make_cache(case.Hkv, case.num_pages, pools[-1], rotation=rot_kind))
+        caches.append(kvq.make_cache(case.Hkv, case.num_pages, pools[-1], rotation=rot_kind, key_bits=args.key_bits))
         rks.append(T(case.r_k))
         rvs.append(T(case.r_v))
         mus.append(T(case.mu))
@@ -343,7 +348,7 @@ def main() -> int:
         e1.record()
         torch.cuda.synchronize()
     bulk_ms = e0.elapsed_time(e1)
-    bulk_alg = case.n_tokens * case.Hkv * (512 + BYTES_PER_TOKEN_HEAD)
+    bulk_alg = case.n_tokens * case.Hkv * (512 + bpt)
     for r in range(1, n_rep):
         pools[r].copy_(pools[0])
     del k_all, v_all, slots_all
@@ -450,19 +455,20 @@ def main() -> int:
     tokens = float(case.seq_lens.sum())
     n_pages = int(((case.seq_lens + PAGE - 1) // PAGE).sum())
     # packed cache + page-table entries read, plus the newest token's bf16 k/v read and 96 B written per KV head
-    alg_bytes = cache_bytes + 4 * n_pages + case.B * case.Hkv * (512 + BYTES_PER_TOKEN_HEAD)
+    alg_bytes = cache_bytes + 4 * n_pages + case.B * case.Hkv * (512 + bpt)
     # with an exact window: its bf16 key and value rows (512 B per position per KV head) are read too
     alg_bytes += n_win_tok * case.Hkv * 512
     achieved = alg_bytes / (split_avg_ms * 1e-3) / 1e9
     # the committed counter summaries are per workload, without a window and with a dense R
-    variant = ("" if args.rotation == "dense" else "_" + args.rotation) + (f"_window{sinks}_{recent}" if n_win_tok else "")
+    variant = (("" if args.rotation == "dense" else "_" + args.rotation) + (f"_window{sinks}_{recent}" if n_win_tok else "")
+               + ("_k4" if args.key_bits == 4 else ""))
     traffic = counters_for(kernel_source_sha(), args.workload + variant)
 
     cpu = None
     if args.cpu_kv_heads > 0:
         log("[bench] timing the oracle on the CPU ...")
         cpu = cpu_baseline(case, pools[0].cpu().numpy(), args.cpu_kv_heads,
-                           window=(sinks, recent) if (sinks or recent) else None)
+                           window=(sinks, recent) if (sinks or recent) else None, key_bits=args.key_bits)
 
     res = {
         "metric": "INT2 decode attention KV-tokens/s + HBM GB/s (% peak), 8B GQA shape @128K",
@@ -486,6 +492,7 @@ def main() -> int:
             "cache_replicas": n_rep, "num_splits": args.num_splits or "auto",
             "exact_window": {"sinks": sinks, "recent": recent} if (sinks or recent) else None,
             "rotation": args.rotation,
+            "key_bits": args.key_bits,
         },
         "hbm_gbps_step": cache_bytes / (ms_per_step * 1e-3) / 1e9,
         "pct_peak_step": cache_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,

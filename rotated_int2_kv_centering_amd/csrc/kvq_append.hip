@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     uint8_t* __restrict__ pool, int num_pages, int num_kv_heads, const void* __restrict__ k_in,
     const void* __restrict__ v_in, int n_tokens, const int32_t* __restrict__ slots, const float* __restrict__ mu,
     const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out, float clip,
-    int rot_kind, int gsize, float* __restrict__ sq_err) {
+    int rot_kind, int gsize, float* __restrict__ sq_err, int kbits) {
   const int tile = blockIdx.x;
   const int h = blockIdx.y;
   const int tensor = blockIdx.z;  // 0: key, 1: value
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     if (rot_out != nullptr) rot_out[((static_cast<size_t>(n) * num_kv_heads + h) * 2 + tensor) * kHeadDim + j] = xv;
 
     const int page = slot >> 4;
-    uint8_t* block = pool + (static_cast<size_t>(page) * num_kv_heads + h) * kBlockBytes;
+    uint8_t* block = pool + (static_cast<size_t>(page) * num_kv_heads + h) * (kbits == 4 ? kBlockBytesK4 : kBlockBytes);
     float2 r;
     if (gsize == 128) {
       const float2 a = s_rng[t][0], b = s_rng[t][1];
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     } else {
       r = q2_wave_range(xv, gsize);
     }
-    const float lvl = q2_pack_channel(xv, j, tensor, block, slot & 15, clip, r.x, r.y);
+    const float lvl = q2_pack_channel(xv, j, tensor, block, slot & 15, clip, r.x, r.y, kbits);
     if (sq_err != nullptr) {  // squared error over this wave's 64 channels
       float e = (xv - lvl) * (xv - lvl);
 #pragma unroll
@@ -149,8 +149,9 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
     uint8_t* __restrict__ pool, int num_pages, int num_kv_heads, const void* __restrict__ k_in,
     const void* __restrict__ v_in, int n_tokens, const int32_t* __restrict__ slots, const float* __restrict__ mu,
     const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out, float clip, int gsize,
-    float* __restrict__ sq_err) {
+    float* __restrict__ sq_err, int kbits) {
   const int h = blockIdx.y;
+  const bool k4 = blockIdx.z == 0 && kbits == 4;  // this workgroup packs 4-bit keys
   const int tensor = blockIdx.z;  // 0: key, 1: value
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
         x[4 * u + 3] = q4[3];
       }
       uint32_t pair, code[32];
-      q2_group32(x, clip, gsize, pair, code);
+      q2_group32(x, clip, gsize, pair, code, k4 ? 15.0f : 3.0f);
       const int slot = n < n_tokens ? slots[n] : -1;
       const bool ok = slot >= 0 && slot < num_pages * kPage;  // same for the token's four lanes
       if (sq_err != nullptr) {  // squared error of groups g and g ^ 1: channels [64 (g / 2), +64)
@@ -325,7 +326,8 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
       const int slot0 = __shfl(slot, 0);
       const bool full = __builtin_amdgcn_ballot_w64(!(ok && slot == slot0 + r && (slot0 & 15) == 0)) == 0;
       const int off = slot & 15;
-      uint8_t* block = pool + (static_cast<size_t>(ok ? slot >> 4 : 0) * num_kv_heads + h) * kBlockBytes;
+      uint8_t* block =  // the block stride follows the cache format (key bits), for the value tensor too
+          pool + (static_cast<size_t>(ok ? slot >> 4 : 0) * num_kv_heads + h) * (kbits == 4 ? kBlockBytesK4 : kBlockBytes);
       if (ok) {  // metadata pair of (token, group): record 4g + off/4
         *reinterpret_cast<uint32_t*>(block + kCodeBytes + kMetaRecordBytes * (4 * g + (off >> 2)) + 16 * tensor +
                                      4 * (off & 3)) = pair;
@@ -333,16 +335,25 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
       if (tensor == 0) {
         // K: channel 32g + 8ak + e -> record 16ak + off, word K[g/2], bit 2(4(g%2) + e/2) + 16(e%2)
         uint32_t kw[4];
+        uint32_t khw[4];  // 4-bit keys: the high bits, same positions, in the plane at kKHiPlane
   #pragma unroll
         for (int ak = 0; ak < 4; ++ak) {
-          uint32_t w = 0;
+          uint32_t w = 0, wh = 0;
   #pragma unroll
-          for (int e = 0; e < 8; ++e) w |= code[8 * ak + e] << (2 * (4 * (g & 1) + (e >> 1)) + 16 * (e & 1));
+          for (int e = 0; e < 8; ++e) {
+            const int sh = 2 * (4 * (g & 1) + (e >> 1)) + 16 * (e & 1);
+            w |= (code[8 * ak + e] & 3u) << sh;
+            wh |= (code[8 * ak + e] >> 2) << sh;
+          }
           kw[ak] = w | __shfl_xor(w, 1);  // both groups of the word
+          khw[ak] = wh | __shfl_xor(wh, 1);
         }
         if (ok && (g & 1) == 0) {
   #pragma unroll
-          for (int ak = 0; ak < 4; ++ak) *reinterpret_cast<uint32_t*>(block + 16 * (16 * ak + off) + 4 * (g >> 1)) = kw[ak];
+          for (int ak = 0; ak < 4; ++ak) {
+            *reinterpret_cast<uint32_t*>(block + 16 * (16 * ak + off) + 4 * (g >> 1)) = kw[ak];
+            if (k4) *reinterpret_cast<uint32_t*>(block + kKHiPlane + 8 * (16 * ak + off) + 4 * (g >> 1)) = khw[ak];
+          }
         }
       } else {
         // V: channel 32g + 16tt + b -> record 16(off/4) + b, word V[(off%4)/2],
@@ -385,7 +396,8 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
 
 hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const void* k, const void* v, int in_kind,
                          int n_tokens, const int32_t* slots, const float* mu, const float* r_k, const float* r_v,
-                         float* rot_out, float clip, int rot_kind, int gsize, float* sq_err, hipStream_t stream) {
+                         float* rot_out, float clip, int rot_kind, int gsize, float* sq_err, int kbits,
+                         hipStream_t stream) {
   (void)hipGetLastError();  // report only this call's launch errors, not stale ones
   if (in_kind != 2 && n_tokens >= kBulkMin) {
     // about one workgroup per compute unit in all (each staging its dense R once;
@@ -396,7 +408,7 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
     auto kern = in_kind == 0 ? (rot_kind == 0 ? append_bulk_kernel<0, 0> : append_bulk_kernel<0, 1>)
                              : (rot_kind == 0 ? append_bulk_kernel<1, 0> : append_bulk_kernel<1, 1>);
     hipLaunchKernelGGL(kern, bgrid, dim3(kBulkThreads), 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens, slots,
-                       mu, r_k, r_v, rot_out, clip, gsize, sq_err);
+                       mu, r_k, r_v, rot_out, clip, gsize, sq_err, kbits);
     return hipGetLastError();
   }
   const dim3 grid((n_tokens + kAppendTile - 1) / kAppendTile, num_kv_heads, 2);
@@ -404,15 +416,15 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
   switch (in_kind) {
     case 0:
       hipLaunchKernelGGL(append_kernel<0>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,
-                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize, sq_err);
+                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize, sq_err, kbits);
       break;
     case 1:
       hipLaunchKernelGGL(append_kernel<1>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,
-                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize, sq_err);
+                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize, sq_err, kbits);
       break;
     default:
       hipLaunchKernelGGL(append_kernel<2>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,
-                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize, sq_err);
+                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize, sq_err, kbits);
       break;
   }
   return hipGetLastError();

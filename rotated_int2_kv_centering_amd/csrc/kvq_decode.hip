@@ -56,7 +56,9 @@ namespace kvq {
 constexpr float kNegBig = -3.0e38f;  // finite "minus infinity" for running maxima
 constexpr float kTwo24 = 16777216.0f;
 constexpr float kLazy = 8.0f;  // rescale threshold of the online softmax (log2 units)
-constexpr int kDmaPerPair = 4;  // K/V codes of page 0, of page 1; metadata of page 0, of page 1
+// DMA instructions per page pair: K/V codes of page 0, of page 1; metadata of
+// page 0, of page 1; with 4-bit keys also the high-bit planes of pages 0 and 1.
+template <bool kK4> struct PairDma { static constexpr int n = kK4 ? 6 : 4; };
 
 // Launch shape by the number of head quads: waves per workgroup, waves per
 // SIMD, and the per-wave ring depth (page pairs staged in LDS by direct
@@ -64,9 +66,9 @@ constexpr int kDmaPerPair = 4;  // K/V codes of page 0, of page 1; metadata of p
 // The g <= 4 kernel fits 3 waves per SIMD, so one 12-wave workgroup fills a
 // compute unit; g <= 8 fits 2 (256 registers); the largest runs 1 wave per
 // SIMD and keeps more pairs in flight per wave instead.
-template <int kNQ> struct DecodeShape { static constexpr int waves = 4, waves_per_simd = 1, depth = 8; };
-template <> struct DecodeShape<1> { static constexpr int waves = 12, waves_per_simd = 3, depth = 3; };
-template <> struct DecodeShape<2> { static constexpr int waves = 8, waves_per_simd = 2, depth = 4; };
+template <int kNQ> struct DecodeShape { static constexpr int waves = 4, waves_per_simd = 1, depth = 8, depth_k4 = 6; };
+template <> struct DecodeShape<1> { static constexpr int waves = 12, waves_per_simd = 3, depth = 3, depth_k4 = 3; };
+template <> struct DecodeShape<2> { static constexpr int waves = 8, waves_per_simd = 2, depth = 4, depth_k4 = 4; };
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -215,9 +217,13 @@ __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int kNQ, int kW, int kDepth>  // quads of query heads (g <= 4 * kNQ), waves per workgroup, ring depth
+// quads of query heads (g <= 4 * kNQ), waves per workgroup, ring depth, 4-bit keys
+template <int kNQ, int kW, int kDepth, bool kK4>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(DecodeShape<kNQ>::waves_per_simd)))
 void decode_kernel(const DecodeParams p) {
+  constexpr int kDmaPerPair = PairDma<kK4>::n;
+  constexpr int kRingParts = kK4 ? 4 : 3;  // codes of page 0, of page 1, metadata, (4-bit keys) high planes
+  constexpr int kBlk = kK4 ? kBlockBytesK4 : kBlockBytes;
   static_assert(kDepth >= 2 && kDmaPerPair * (kDepth - 1) <= 63, "ring depth within the vmcnt range");
   constexpr int kNH = 4 * kNQ;
   constexpr int kThreads = 64 * kW;
@@ -240,13 +246,13 @@ void decode_kernel(const DecodeParams p) {
   __shared__ float s_nlog[kNH];
   // Page-pair ring [slot][wave][part][lane]: part 0/1 = 64 x 16 B codes of
   // page 0/1, part 2 = 32 x 16 B metadata of page 0 then of page 1.
-  __shared__ uint4v s_ring[kDepth][kW][3][64];
+  __shared__ uint4v s_ring[kDepth][kW][kRingParts][64];
   // Prologue scratch (q_hat partials [kParts][kNH][128], then the new token's
   // partials [2][4][128]) lives in the last ring slot, which no load targets
   // before the main loop, when it fits there.  After the main loop the whole
   // ring holds the per-wave partials and then the R_V^T partial sums.
   constexpr int kProFloats = (kParts * kNH + 2 * 4) * kHeadDim;
-  constexpr bool kProInRing = kProFloats * 4 <= kW * 3 * 64 * 16;
+  constexpr bool kProInRing = kProFloats * 4 <= kW * kRingParts * 64 * 16;
   __shared__ float s_pro_sep[kProInRing ? 1 : kProFloats];
   float* const s_pro = kProInRing ? reinterpret_cast<float*>(&s_ring[kDepth - 1][0][0][0]) : s_pro_sep;
   float* const s_npart = s_pro + kParts * kNH * kHeadDim;
@@ -441,8 +447,8 @@ void decode_kernel(const DecodeParams p) {
   const int grp = col >> 2;
   const int jj = col & 3;
   const int meta_off = kMetaRecordBytes * (4 * grp + a);  // within a page's metadata
-  const uint8_t* pool_h = p.pool + static_cast<size_t>(h) * kBlockBytes;
-  const size_t page_stride = static_cast<size_t>(H) * kBlockBytes;
+  const uint8_t* pool_h = p.pool + static_cast<size_t>(h) * kBlk;
+  const size_t page_stride = static_cast<size_t>(H) * kBlk;
 
   auto issue = [&](int slot, int pair) {
     const int i0 = 2 * pair;
@@ -460,6 +466,12 @@ void decode_kernel(const DecodeParams p) {
       dma16(blk0, kCodeBytes + 16 * lane, &r[2][0]);
     else
       dma16(blk1, kCodeBytes - 512 + 16 * lane, &r[2][0]);
+    if (kK4) {  // the keys' high-bit planes, page 0 then page 1 (512 B each)
+      if (lane < 32)
+        dma16(blk0, kKHiPlane + 16 * lane, &r[kRingParts - 1][0]);
+      else
+        dma16(blk1, kKHiPlane - 512 + 16 * lane, &r[kRingParts - 1][0]);
+    }
   };
 
   // Every wave keeps kDepth - 1 page pairs in flight ahead of the one it
@@ -537,8 +549,9 @@ void decode_kernel(const DecodeParams p) {
     if (tid < 2 * kHeadDim) {
       const int tensor = tid / kHeadDim;
       const int pos = T - 1;
-      uint8_t* blk = p.pool + (static_cast<size_t>(s_pages[np - 1]) * H + h) * kBlockBytes;
-      s_hat[tensor][rc] = q2_pack_channel(s_nrow[tensor][rc], rc, tensor, blk, pos & (kPage - 1), p.clip, rg.x, rg.y);
+      uint8_t* blk = p.pool + (static_cast<size_t>(s_pages[np - 1]) * H + h) * kBlk;
+      s_hat[tensor][rc] =
+          q2_pack_channel(s_nrow[tensor][rc], rc, tensor, blk, pos & (kPage - 1), p.clip, rg.x, rg.y, kK4 ? 4 : 2);
     }
   }
   for (int jh = wave; jh < kNH; jh += kW) {
@@ -616,6 +629,14 @@ void decode_kernel(const DecodeParams p) {
     P.vm0 = *reinterpret_cast<const uint4v*>(meta + meta_off + 16);
     P.km1 = *reinterpret_cast<const uint4v*>(meta + 512 + meta_off);
     P.vm1 = *reinterpret_cast<const uint4v*>(meta + 512 + meta_off + 16);
+    uint32_t kh[2][2] = {{0u, 0u}, {0u, 0u}};  // 4-bit keys: high-plane words H0, H1 of record `lane`, per page
+    if (kK4) {
+      const uint32_t* hp = reinterpret_cast<const uint32_t*>(&r[kRingParts - 1][0]);
+      kh[0][0] = hp[2 * lane];
+      kh[0][1] = hp[2 * lane + 1];
+      kh[1][0] = hp[128 + 2 * lane];
+      kh[1][1] = hp[128 + 2 * lane + 1];
+    }
     const int i0 = 2 * pair;
     // page ids and the pair's validity are wave-uniform (scalar registers)
     const int ph0 = __builtin_amdgcn_readfirstlane(s_pages[i0]);
@@ -643,6 +664,18 @@ void decode_kernel(const DecodeParams p) {
         for (int q = 0; q < 4; ++q) rr[q] = kw[kk] & (0x00030003u << (2 * q));
         kA[kk] = __builtin_bit_cast(half8, rr);
       }
+      // 4-bit keys: the high two bits, same extraction; code = low + 4 high
+      half8 kAh[4];
+      if (kK4) {
+        const uint32_t hw[4] = {kh[X][0], kh[X][0] >> 8, kh[X][1], kh[X][1] >> 8};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          uint4v rr;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) rr[q] = hw[kk] & (0x00030003u << (2 * q));
+          kAh[kk] = __builtin_bit_cast(half8, rr);
+        }
+      }
       const int pos0 = (p0 + i0 + X) * kPage + 4 * a;
       const bool page_ok = X == 0 ? ok0 : has1;
 #pragma unroll
@@ -652,6 +685,16 @@ void decode_kernel(const DecodeParams p) {
         for (int kk = 0; kk < 4; ++kk) {
           C = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[kk], qhi[Q][kk], C, 0, 0, 0);
           C = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[kk], qlo[Q][kk], C, 0, 0, 0);
+        }
+        if (kK4) {
+          float4v Ch = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            Ch = __builtin_amdgcn_mfma_f32_16x16x32_f16(kAh[kk], qhi[Q][kk], Ch, 0, 0, 0);
+            Ch = __builtin_amdgcn_mfma_f32_16x16x32_f16(kAh[kk], qlo[Q][kk], Ch, 0, 0, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) C[i] = fmaf(4.0f, Ch[i], C[i]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1191,12 +1234,13 @@ void decode_kernel(const DecodeParams p) {
 // ----------------------------------------------------------------- launcher
 // hipExtLaunchKernel stamps the events with the dispatch's own start and end
 // times, so an event pair measures the kernel alone.
-template <int kNQ>
+template <int kNQ, bool kK4>
 static hipError_t launch_one(const DecodeParams& prm, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
   constexpr int kW = DecodeShape<kNQ>::waves;
+  constexpr int kD = kK4 ? DecodeShape<kNQ>::depth_k4 : DecodeShape<kNQ>::depth;
   DecodeParams arg = prm;
   void* args[] = {&arg};
-  return hipExtLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<kNQ, kW, DecodeShape<kNQ>::depth>),
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<kNQ, kW, kD, kK4>),
                             dim3((prm.balanced ? 1 : prm.batch) * prm.num_kv_heads * prm.n_splits), dim3(64 * kW),
                             args, 0, stream,
                             ev_begin, ev_end, 0);
@@ -1205,12 +1249,13 @@ static hipError_t launch_one(const DecodeParams& prm, hipStream_t stream, hipEve
 hipError_t launch_decode(const DecodeParams& prm, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
   (void)hipGetLastError();  // report only this call's launch errors, not stale ones
   hipError_t err;
+  const bool k4 = prm.kbits == 4;
   if (prm.g <= 4)
-    err = launch_one<1>(prm, stream, ev_begin, ev_end);
+    err = k4 ? launch_one<1, true>(prm, stream, ev_begin, ev_end) : launch_one<1, false>(prm, stream, ev_begin, ev_end);
   else if (prm.g <= 8)
-    err = launch_one<2>(prm, stream, ev_begin, ev_end);
+    err = k4 ? launch_one<2, true>(prm, stream, ev_begin, ev_end) : launch_one<2, false>(prm, stream, ev_begin, ev_end);
   else
-    err = launch_one<4>(prm, stream, ev_begin, ev_end);
+    err = k4 ? launch_one<4, true>(prm, stream, ev_begin, ev_end) : launch_one<4, false>(prm, stream, ev_begin, ev_end);
   if (err != hipSuccess) return err;
   return hipGetLastError();
 }

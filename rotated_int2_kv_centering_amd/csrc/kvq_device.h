@@ -11,6 +11,7 @@ constexpr int kHeadDim = 128;
 constexpr int kGroup = 32;
 constexpr int kPage = 16;
 constexpr int kBlockBytes = 1536;   // one (page, KV head) block
+constexpr int kBlockBytesK4 = 2048;  // the same with 4-bit keys (high-bit plane at byte 1536)
 constexpr int kCodeBytes = 1024;    // 64 records x 16 B of K/V code words
 constexpr int kMetaRecordBytes = 32;
 

@@ -8,7 +8,8 @@ namespace kvq {
 
 hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const void* k, const void* v, int in_kind,
                          int n_tokens, const int32_t* slots, const float* mu, const float* r_k, const float* r_v,
-                         float* rot_out, float clip, int rot_kind, int gsize, float* sq_err, hipStream_t stream);
+                         float* rot_out, float clip, int rot_kind, int gsize, float* sq_err, int kbits,
+                         hipStream_t stream);
 
 // Split plan of one decode call.  Fixed plan (an explicit split count): every
 // sequence is cut into n_splits splits of pages_per_split pages.  Balanced
@@ -75,6 +76,7 @@ struct DecodeParams {
   const float* mu;
   float clip;  // Q2's clip ratio for the appended token
   int gsize;   // Q2's group size G (32, 64 or 128) for the appended token
+  int kbits;   // bits per key code: 2, or 4 (2048-byte blocks with a high-bit plane)
   int rot_kind;  // 0: r_k, r_v are dense [H][128][128]; 1: Hadamard, r_k, r_v are signs [H][128]
 };
 

@@ -81,8 +81,10 @@ __device__ __forceinline__ float2 q2_wave_range(float xv, int gsize) {
 // range of channel j's group (q2_wave_range).  `block` is the (page, KV head)
 // block to write, or null to only compute; `off` is the slot within the page
 // (0..15); tensor 0 = K, 1 = V.  The block keeps one metadata pair per 32
-// channels: for G > 32 each holds its group's pair.  Returns the dequantized
-// level of channel j.
+// channels: for G > 32 each holds its group's pair.  kbits = 4 quantizes the
+// key to 16 levels: its low two bits go where a 2-bit code would, its high two
+// bits to the plane at byte kKHiPlane (record r at 8 r, same word and bit).
+// Returns the dequantized level of channel j.
 //
 // K code of slot s, channel c (kk = c/32, a = (c%32)/8, e = c%8): record
 // 16a + s, word K[kk/2], bit 2(4(kk%2) + e/2) + 16(e%2).  V code (t = c/16,
@@ -92,8 +94,12 @@ __device__ __forceinline__ float2 q2_wave_range(float xv, int gsize) {
 // A K code word and a metadata pair belong to one slot (plain stores); a V
 // code word holds codes of two slots, so it is updated with atomic and/or of
 // this slot's bits only, which keeps concurrent writes to other slots intact.
+constexpr int kKHiPlane = 1536;  // byte offset of the 4-bit keys' high-bit plane in a 2048-byte block
+
 __device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, uint8_t* block, int off, float clip,
-                                                float mn, float mx) {
+                                                float mn, float mx, int kbits = 2) {
+  const bool k4 = tensor == 0 && kbits == 4;
+  const float n_lv = k4 ? 15.0f : 3.0f;
   const int lane = j & 63;
   const int w2 = j >> 6;
   const int grp = j >> 5;
@@ -103,7 +109,7 @@ __device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, ui
   // fp16 zero included): without this the compiler may round c*min straight
   // to fp16 in one mixed-precision multiply, which differs at fp16 ties.
   asm volatile("" : "+v"(mn), "+v"(mx));
-  const float s32 = (mx - mn) / 3.0f;
+  const float s32 = (mx - mn) / n_lv;
   const _Float16 s16 = static_cast<_Float16>(s32);
   const _Float16 z16 = static_cast<_Float16>(mn);
   const float sc = static_cast<float>(s16);
@@ -111,18 +117,28 @@ __device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, ui
   uint32_t code = 0;
   if (sc != 0.0f) {
     const float u = (xv - z) / sc;
-    code = static_cast<uint32_t>(fminf(fmaxf(rintf(u), 0.0f), 3.0f));
+    code = static_cast<uint32_t>(fminf(fmaxf(rintf(u), 0.0f), n_lv));
   }
 
   if (tensor == 0) {
     const int kk = grp, a = (j & 31) >> 3, e = j & 7;
-    uint32_t w = code << (2 * (4 * (kk & 1) + (e >> 1)) + 16 * (e & 1));
+    const int sh = 2 * (4 * (kk & 1) + (e >> 1)) + 16 * (e & 1);
+    uint32_t w = (code & 3u) << sh;
+    uint32_t wh = (code >> 2) << sh;  // 4-bit keys: the high bits (0 otherwise)
     w |= __shfl_xor(w, 1);
     w |= __shfl_xor(w, 2);
     w |= __shfl_xor(w, 4);
     w |= __shfl_xor(w, 32);
-    if (block != nullptr && (lane & 39) == 0)  // e == 0, kk even: lanes 0, 8, 16, 24 hold both groups' words
+    if (k4) {
+      wh |= __shfl_xor(wh, 1);
+      wh |= __shfl_xor(wh, 2);
+      wh |= __shfl_xor(wh, 4);
+      wh |= __shfl_xor(wh, 32);
+    }
+    if (block != nullptr && (lane & 39) == 0) {  // e == 0, kk even: lanes 0, 8, 16, 24 hold both groups' words
       *reinterpret_cast<uint32_t*>(block + 16 * (16 * a + off) + 4 * w2) = w;
+      if (k4) *reinterpret_cast<uint32_t*>(block + kKHiPlane + 8 * (16 * a + off) + 4 * w2) = wh;
+    }
   } else {
     const int t16 = j >> 4, b = j & 15, a = off >> 2, i = off & 3;
     const int shift = 16 * (i & 1);
@@ -154,7 +170,7 @@ __device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, ui
 // q is within 2^-19 of a half-integer, where the two could round apart: such a
 // lane recomputes its group with the IEEE division.
 __device__ __forceinline__ void q2_group32(const float (&x)[32], float clip, int gsize, uint32_t& pair,
-                                           uint32_t (&code)[32]) {
+                                           uint32_t (&code)[32], float n_lv = 3.0f) {
   float mn = x[0], mx = x[0];
 #pragma unroll
   for (int c = 1; c < 32; ++c) {
@@ -175,7 +191,7 @@ __device__ __forceinline__ void q2_group32(const float (&x)[32], float clip, int
   // fp16 zero included): without this the compiler may round c*min straight
   // to fp16 in one mixed-precision multiply, which differs at fp16 ties.
   asm volatile("" : "+v"(mn), "+v"(mx));
-  const float s32 = (mx - mn) / 3.0f;
+  const float s32 = (mx - mn) / n_lv;  // n_lv = 3, or 15 for 4-bit keys
   const _Float16 s16 = static_cast<_Float16>(s32);
   const _Float16 z16 = static_cast<_Float16>(mn);
   const float sc = static_cast<float>(s16);
@@ -189,12 +205,12 @@ __device__ __forceinline__ void q2_group32(const float (&x)[32], float clip, int
     const float q = (x[c] - z) * rcp;
     const float k = rintf(q);
     near = near || fabsf(q - k) > 0.5f - 0x1p-19f;
-    code[c] = static_cast<uint32_t>(__builtin_amdgcn_fmed3f(k, 0.0f, 3.0f));
+    code[c] = static_cast<uint32_t>(__builtin_amdgcn_fmed3f(k, 0.0f, n_lv));
   }
   if (__builtin_amdgcn_ballot_w64(near) != 0 && near) {  // exact path, rarely taken
 #pragma unroll
     for (int c = 0; c < 32; ++c)
-      code[c] = static_cast<uint32_t>(fminf(fmaxf(rintf((x[c] - z) / sc), 0.0f), 3.0f));
+      code[c] = static_cast<uint32_t>(fminf(fmaxf(rintf((x[c] - z) / sc), 0.0f), n_lv));
   }
 }
 

@@ -277,8 +277,11 @@ def test_window_bytes_and_host_validation(K):
 def test_cache_clip_ratio_layout_and_validation(K):
     """kvq_cache.clip_ratio sits after the pool pointer; values outside [0, 1] (or NaN)
     are rejected on the host before any launch."""
-    assert ctypes.sizeof(K.kvq_cache) == 40 and K.kvq_cache.clip_ratio.offset == 32
-    assert K.kvq_cache.rotation.offset == 36
+    assert ctypes.sizeof(K.kvq_cache) == 48 and K.kvq_cache.clip_ratio.offset == 32
+    assert K.kvq_cache.rotation.offset == 36 and K.kvq_cache.key_bits.offset == 40
+    assert K.kvq_pool_bytes(K.make_cache(2, 8, FAKE, key_bits=4)) == 2 * 8 * 2048
+    assert K.kvq_pool_bytes(K.make_cache(2, 8, FAKE, key_bits=0)) == 2 * 8 * 1536
+    assert _decode(K, K.make_cache(1, 8, FAKE, key_bits=3)) == K.KVQ_EUNSUPPORTED and "key_bits" in K.kvq_last_error()
     assert _decode(K, K.make_cache(1, 8, FAKE, rotation=2)) == K.KVQ_EINVAL  # unknown rotation kind
     assert "rotation" in K.kvq_last_error()
     lib = K.load()
