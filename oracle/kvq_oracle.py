@@ -56,8 +56,9 @@ token slots of one (page p, KV head h) and starts at byte (p*H_kv + h)*1536:
   byte 1024 + 32*m + 16 + 4*i the V pair, each pair being the fp16 scale
   (low two bytes) then the fp16 zero, little-endian.
 
-With 4-bit keys (key_bits = 4: the asymmetric K4V2 budget) a block is 2048
-bytes.  The 1536 bytes above keep their layout, the K words holding the low
+With 4-bit keys (key_bits = 4, a K4V2 budget) a block is 2048 bytes; 3-bit
+keys (key_bits = 3, the page's K3V2 budget) use the same block, their high
+part being a single bit.  The 1536 bytes above keep their layout, the K words holding the low
 two bits of each key code (code & 3); bytes [1536, 2048) are 64 records of 8
 bytes, record r = 16*a + s holding words H0, H1 at byte 1536 + 8*r: the high
 two bits (code >> 2) of the key code of slot s, channel c sit in record
@@ -78,8 +79,8 @@ HI_PLANE = 1536  # byte offset of the 4-bit keys' high-bit plane
 
 
 def block_bytes(key_bits: int = 2) -> int:
-    """Bytes of one (page, KV head) block: 1536 for 2-bit keys, 2048 for 4-bit keys."""
-    assert key_bits in (2, 4), "key codes are 2 or 4 bits"
+    """Bytes of one (page, KV head) block: 1536 for 2-bit keys, 2048 for 3- and 4-bit keys."""
+    assert key_bits in (2, 3, 4), "key codes are 2, 3 or 4 bits"
     return BLOCK_BYTES if key_bits == 2 else BLOCK_BYTES + 512
 
 
@@ -144,8 +145,9 @@ def rotated_inputs(k, v, mu, r_k, r_v):
 # ---------------------------------------------------------- INT2 quantizer Q2
 def int2_quantize(x: np.ndarray, clip: float = 1.0, group: int = GROUP, bits: int = 2):
     """OptR §3.1: Q2(.; c, G), asymmetric, on fp32 rows of 128 channels;
-    ``bits`` = 4 gives the same quantizer with 16 levels (the 4-bit keys of a
-    K4V2 budget): the divisor 3 below becomes 15 and codes run 0..15.
+    ``bits`` = 3 or 4 gives the same quantizer with 8 or 16 levels (3- and 4-bit
+    keys of K3V2 / K4V2 budgets): the divisor 3 below becomes 2^bits - 1 and
+    codes run 0..2^bits - 1.
 
     ``x`` is float32 [..., 128].  Groups are G = ``group`` (32, 64 or 128)
     consecutive channels.  For each
@@ -172,7 +174,7 @@ def int2_quantize(x: np.ndarray, clip: float = 1.0, group: int = GROUP, bits: in
     c = np.float32(clip)
     assert np.float32(0.0) < c <= np.float32(1.0), "clip ratio must be in (0, 1]"
     assert group in (32, 64, 128), "group size must be 32, 64 or 128"
-    assert bits in (2, 4), "2 or 4 bits"
+    assert bits in (2, 3, 4), "2, 3 or 4 bits"
     n_lv = np.float32((1 << bits) - 1)
     xg = x.reshape(x.shape[:-1] + (HEAD_DIM // group, group))
     mn = (xg.min(axis=-1) * c).astype(np.float32)
@@ -247,7 +249,7 @@ def pack_block(k_codes, k_s16, k_z16, v_codes, v_s16, v_z16, block: np.ndarray |
     assert len(np.unique(slots)) == len(slots)
     words = blk[:CODE_BYTES].view("<u4").reshape(-1)           # 64 records x 4 words
     k_codes = np.asarray(k_codes, np.uint32)
-    assert key_bits == 4 or k_codes.max(initial=0) <= 3
+    assert k_codes.max(initial=0) < (1 << key_bits)
     for codes, table in ((k_codes & 3, _K_POS), (v_codes, _V_POS)):
         pos = table[slots]                                      # [n, 128, (record, word, bit)]
         idx = (pos[..., 0] * 4 + pos[..., 1]).reshape(-1)
@@ -255,7 +257,7 @@ def pack_block(k_codes, k_s16, k_z16, v_codes, v_s16, v_z16, block: np.ndarray |
         val = np.asarray(codes, np.uint32).reshape(-1)
         np.bitwise_and.at(words, idx, ~(np.uint32(3) << bit))
         np.bitwise_or.at(words, idx, (val & np.uint32(3)) << bit)
-    if key_bits == 4:  # high bits of the key codes: record r at 1536 + 8 r, word H[kk // 2], same bit
+    if key_bits > 2:  # high bits of the key codes: record r at 1536 + 8 r, word H[kk // 2], same bit
         hi = blk[HI_PLANE:].view("<u4").reshape(-1)              # 64 records x 2 words
         pos = _K_POS[slots]
         idx = (pos[..., 0] * 2 + pos[..., 1]).reshape(-1)
@@ -293,7 +295,7 @@ def unpack_blocks(blocks: np.ndarray, key_bits: int = 2):
     rec = 4 * np.arange(N_GROUPS)[None, :] + (slots // 4)[:, None]     # [slot, grp] -> record m
     i = np.broadcast_to((slots % 4)[:, None], rec.shape)
     k = gather(_K_POS)
-    if key_bits == 4:
+    if key_bits > 2:
         hi = blk[:, HI_PLANE:].view("<u4").reshape(-1, 64, 2).astype(np.int64)
         r_, w_, b_ = _K_POS[..., 0], _K_POS[..., 1], _K_POS[..., 2]
         k = k + (((hi[:, r_, w_] >> b_[None]) & 3) << 2).astype(np.uint8)

@@ -889,3 +889,37 @@ def test_k4_decode_equals_attention_on_effective_kv_and_is_closer():
     e4 = np.abs(kq - x).mean()
     e2 = np.abs(O.int2_dequantize(*O.int2_quantize(x)) - x).mean()
     assert e4 < 0.3 * e2
+
+
+def test_quantizer_three_bits_hand_derived_and_nearest():
+    """bits = 3 (K3V2 keys): a group holding 0..7 four times is exact (s = 1, z = 0);
+    3.5 ties to 4; codes stay in 0..7, each the nearest of 8 levels (brute force);
+    a 3-bit pool decodes like attention on its effective keys."""
+    row = np.zeros(128, np.float32)
+    row[:32] = np.tile(np.arange(8, dtype=np.float32), 4)
+    row[32:64] = 0.0
+    row[32], row[33], row[34] = 0.0, 3.5, 7.0
+    codes, s16, z16 = O.int2_quantize(row[None], bits=3)
+    np.testing.assert_array_equal(codes[0, :32], np.tile(np.arange(8), 4))
+    assert s16[0, 0] == np.float16(1.0) and codes[0, 33] == 4 and codes[0, 34] == 7
+    rng = np.random.default_rng(45)
+    x = _random_rows(rng, 64, 2.0, -0.5)
+    codes, s16, z16 = O.int2_quantize(x, bits=3)
+    assert codes.max() <= 7
+    xg = x.reshape(64, 4, 32).astype(np.float64)
+    levels = z16.astype(np.float64)[..., None, None] + s16.astype(np.float64)[..., None, None] * np.arange(8)
+    dist = np.abs(xg[..., None] - levels)
+    got = np.take_along_axis(dist, codes.reshape(64, 4, 32)[..., None].astype(np.int64), -1)[..., 0]
+    tol = 4 * np.spacing(np.maximum(s16.astype(np.float32), np.float32(1e-30))).astype(np.float64)[..., None]
+    assert np.all(got <= dist.min(-1) + tol + 1e-12)
+    c = _tiny(B=1, Hq=4, Hkv=1, seq_lens=[40], table_policy="permuted")
+    pool = np.zeros(O.pool_bytes(c.num_pages, c.Hkv, key_bits=3), np.uint8)
+    O.append_tokens(pool, c.Hkv, c.slots, c.k, c.v, c.mu, c.r_k, c.r_v, key_bits=3)
+    got = O.decode_attention(c.q, pool, c.Hkv, c.page_table, c.seq_lens, c.r_k, c.r_v, key_bits=3)
+    xr, wr = O.rotated_inputs(c.k, c.v, c.mu, c.r_k, c.r_v)
+    kq = O.int2_dequantize(*O.int2_quantize(xr, bits=3))
+    vq = O.int2_dequantize(*O.int2_quantize(wr))
+    for j in range(c.Hq):
+        ref = O.softmax_attention(c.q[0, j], kq[:, 0] @ c.r_k[0].astype(np.float64).T + c.mu[0],
+                                  vq[:, 0] @ c.r_v[0].astype(np.float64).T, 1 / np.sqrt(128))
+        np.testing.assert_allclose(got[0, j], ref, rtol=0, atol=1e-11)
