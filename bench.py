@@ -279,8 +279,8 @@ def main() -> int:
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-kv-heads", type=int, default=8, help="KV heads in the oracle's timed sample (0 = skip)")
     ap.add_argument("--window", default="", help="exact bf16 window 'sinks,recent' (e.g. 4,128); default none")
-    ap.add_argument("--key-bits", type=int, default=2, choices=[2, 4],
-                    help="bits per key code: 2, or 4 (the K4V2 budget: 2048-byte blocks); values keep 2")
+    ap.add_argument("--key-bits", type=int, default=2, choices=[2, 3, 4],
+                    help="bits per key code: 2, or 3 / 4 (K3V2 / K4V2: 2048-byte blocks); values keep 2")
     ap.add_argument("--evaluator", action="store_true",
                     help="time the output-error evaluator (kvq_output_error) instead of the decode step")
     ap.add_argument("--rotation", default="dense", choices=["dense", "hadamard"],
@@ -321,9 +321,9 @@ def main() -> int:
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
     # per token and KV head: K and V codes, K and V (scale, zero); 4-bit keys add 32 B of key bits
-    bpt = BYTES_PER_TOKEN_HEAD + (32 if args.key_bits == 4 else 0)
+    bpt = BYTES_PER_TOKEN_HEAD + (32 if args.key_bits > 2 else 0)
     cache_bytes = int(case.seq_lens.sum()) * case.Hkv * bpt
-    pool_bytes = case.num_pages * case.Hkv * (2048 if args.key_bits == 4 else 1536)
+    pool_bytes = case.num_pages * case.Hkv * (2048 if args.key_bits > 2 else 1536)
     n_rep = args.replicas or max(2, -(-2 * MALL_BYTES // pool_bytes) + 1)
 
     # ---- replica 0: bulk quantize-append of the whole context
@@ -461,7 +461,7 @@ def main() -> int:
     achieved = alg_bytes / (split_avg_ms * 1e-3) / 1e9
     # the committed counter summaries are per workload, without a window and with a dense R
     variant = (("" if args.rotation == "dense" else "_" + args.rotation) + (f"_window{sinks}_{recent}" if n_win_tok else "")
-               + ("_k4" if args.key_bits == 4 else ""))
+               + (f"_k{args.key_bits}" if args.key_bits > 2 else ""))
     traffic = counters_for(kernel_source_sha(), args.workload + variant)
 
     cpu = None

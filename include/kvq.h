@@ -102,12 +102,13 @@ typedef struct {
   void* pool;           /* device, kvq_pool_bytes(cache) bytes, 16-byte aligned */
   float clip_ratio;     /* Q2's clip ratio c in (0, 1]; 0 selects 1 (no clip)  */
   int32_t rotation;     /* kvq_rotation: how r_k and r_v describe R           */
-  int32_t key_bits;     /* bits per key code: 2 (or 0, the default) or 4, the
-                           K4V2 budget (values keep 2 bits).  With 4 a block is
-                           2048 bytes: the 1536-byte layout holds each key
-                           code's low two bits and bytes [1536, 2048) its high
-                           two bits (record r = 16 a + s at 1536 + 8 r, words
-                           H0, H1 at the bits of K0, K1)                      */
+  int32_t key_bits;     /* bits per key code: 2 (or 0, the default), 3 (K3V2)
+                           or 4 (K4V2); values keep 2 bits.  With 3 or 4 a block
+                           is 2048 bytes: the 1536-byte layout holds each key
+                           code's low two bits and bytes [1536, 2048) the rest
+                           (record r = 16 a + s at 1536 + 8 r, words H0, H1 at
+                           the bits of K0, K1; one bit used for 3-bit keys).
+                           kvq_output_error takes 2-bit keys only            */
 } kvq_cache;
 
 /*

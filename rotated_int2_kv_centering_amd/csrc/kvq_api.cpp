@@ -58,8 +58,8 @@ kvq_status check_cache(const kvq_cache* c) {
     return fail(KVQ_EUNSUPPORTED, "num_pages=%d exceeds the int32 slot range", c->num_pages);
   if (c->pool == nullptr && c->num_pages > 0) return fail(KVQ_EINVAL, "cache pool is NULL");
   if (reinterpret_cast<uintptr_t>(c->pool) % 16 != 0) return fail(KVQ_EINVAL, "cache pool must be 16-byte aligned");
-  if (c->key_bits != 0 && c->key_bits != 2 && c->key_bits != 4)
-    return fail(KVQ_EUNSUPPORTED, "key_bits=%d must be 2 or 4 (0 selects 2)", c->key_bits);
+  if (c->key_bits != 0 && c->key_bits != 2 && c->key_bits != 3 && c->key_bits != 4)
+    return fail(KVQ_EUNSUPPORTED, "key_bits=%d must be 2, 3 or 4 (0 selects 2)", c->key_bits);
   if (c->rotation != KVQ_ROT_DENSE && c->rotation != KVQ_ROT_HADAMARD)
     return fail(KVQ_EINVAL, "rotation=%d must be KVQ_ROT_DENSE or KVQ_ROT_HADAMARD", c->rotation);
   if (!(c->clip_ratio >= 0.0f && c->clip_ratio <= 1.0f))
@@ -291,7 +291,7 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
   a.kv_kind = kv_dtype == KVQ_BF16 ? 0 : 1;
   a.clip = clip_of(cache);
   a.gsize = cache->group_size;
-  a.kbits = cache->key_bits == 4 ? 4 : 2;
+  a.kbits = cache->key_bits > 2 ? cache->key_bits : 2;
   a.rot_kind = cache->rotation;
   a.mu = mu;
   hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_begin),
@@ -338,7 +338,7 @@ extern "C" {
 size_t kvq_pool_bytes(const kvq_cache* cache) {
   if (cache == nullptr || cache->num_kv_heads <= 0 || cache->num_pages <= 0) return 0;
   return static_cast<size_t>(cache->num_pages) * static_cast<size_t>(cache->num_kv_heads) *
-         (cache->key_bits == 4 ? kBlockBytesK4 : kBlockBytes);
+         (cache->key_bits > 2 ? kBlockBytesK4 : kBlockBytes);
 }
 
 kvq_status kvq_quant_append(const kvq_cache* cache, const void* k, const void* v, kvq_dtype in_dtype,
@@ -363,7 +363,7 @@ kvq_status kvq_quant_append_err(const kvq_cache* cache, const void* k, const voi
   const int kind = in_dtype == KVQ_BF16 ? 0 : (in_dtype == KVQ_F32 ? 1 : 2);
   hipError_t e = kvq::launch_append(static_cast<uint8_t*>(cache->pool), cache->num_pages, cache->num_kv_heads, k, v,
                                     kind, n_tokens, slots, mu, r_k, r_v, rot_out, clip_of(cache), cache->rotation,
-                                    cache->group_size, sq_err, cache->key_bits == 4 ? 4 : 2,
+                                    cache->group_size, sq_err, cache->key_bits > 2 ? cache->key_bits : 2,
                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "quant_append launch");
   return KVQ_OK;
@@ -426,7 +426,7 @@ kvq_status kvq_output_error(const kvq_cache* cache, const void* q, kvq_dtype q_d
                             void* stream) {
   kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
-  if (cache->key_bits == 4) return fail(KVQ_EUNSUPPORTED, "4-bit keys are not read by this call yet");
+  if (cache->key_bits > 2) return fail(KVQ_EUNSUPPORTED, "keys wider than 2 bits are not read by this call yet");
   if (batch < 0) return fail(KVQ_EINVAL, "batch=%d must be >= 0", batch);
   if (batch > kvq::kMaxEvalBatch)
     return fail(KVQ_EUNSUPPORTED, "batch=%d exceeds the evaluator's %d", batch, kvq::kMaxEvalBatch);

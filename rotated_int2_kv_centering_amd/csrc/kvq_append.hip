@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     if (rot_out != nullptr) rot_out[((static_cast<size_t>(n) * num_kv_heads + h) * 2 + tensor) * kHeadDim + j] = xv;
 
     const int page = slot >> 4;
-    uint8_t* block = pool + (static_cast<size_t>(page) * num_kv_heads + h) * (kbits == 4 ? kBlockBytesK4 : kBlockBytes);
+    uint8_t* block = pool + (static_cast<size_t>(page) * num_kv_heads + h) * (kbits > 2 ? kBlockBytesK4 : kBlockBytes);
     float2 r;
     if (gsize == 128) {
       const float2 a = s_rng[t][0], b = s_rng[t][1];
@@ -151,7 +151,7 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
     const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out, float clip, int gsize,
     float* __restrict__ sq_err, int kbits) {
   const int h = blockIdx.y;
-  const bool k4 = blockIdx.z == 0 && kbits == 4;  // this workgroup packs 4-bit keys
+  const bool k4 = blockIdx.z == 0 && kbits > 2;  // this workgroup packs 3- or 4-bit keys
   const int tensor = blockIdx.z;  // 0: key, 1: value
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -301,7 +301,7 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
         x[4 * u + 3] = q4[3];
       }
       uint32_t pair, code[32];
-      q2_group32(x, clip, gsize, pair, code, k4 ? 15.0f : 3.0f);
+      q2_group32(x, clip, gsize, pair, code, k4 ? static_cast<float>((1 << kbits) - 1) : 3.0f);
       const int slot = n < n_tokens ? slots[n] : -1;
       const bool ok = slot >= 0 && slot < num_pages * kPage;  // same for the token's four lanes
       if (sq_err != nullptr) {  // squared error of groups g and g ^ 1: channels [64 (g / 2), +64)
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
       const bool full = __builtin_amdgcn_ballot_w64(!(ok && slot == slot0 + r && (slot0 & 15) == 0)) == 0;
       const int off = slot & 15;
       uint8_t* block =  // the block stride follows the cache format (key bits), for the value tensor too
-          pool + (static_cast<size_t>(ok ? slot >> 4 : 0) * num_kv_heads + h) * (kbits == 4 ? kBlockBytesK4 : kBlockBytes);
+          pool + (static_cast<size_t>(ok ? slot >> 4 : 0) * num_kv_heads + h) * (kbits > 2 ? kBlockBytesK4 : kBlockBytes);
       if (ok) {  // metadata pair of (token, group): record 4g + off/4
         *reinterpret_cast<uint32_t*>(block + kCodeBytes + kMetaRecordBytes * (4 * g + (off >> 2)) + 16 * tensor +
                                      4 * (off & 3)) = pair;

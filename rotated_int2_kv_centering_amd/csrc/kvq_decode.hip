@@ -551,7 +551,7 @@ void decode_kernel(const DecodeParams p) {
       const int pos = T - 1;
       uint8_t* blk = p.pool + (static_cast<size_t>(s_pages[np - 1]) * H + h) * kBlk;
       s_hat[tensor][rc] =
-          q2_pack_channel(s_nrow[tensor][rc], rc, tensor, blk, pos & (kPage - 1), p.clip, rg.x, rg.y, kK4 ? 4 : 2);
+          q2_pack_channel(s_nrow[tensor][rc], rc, tensor, blk, pos & (kPage - 1), p.clip, rg.x, rg.y, p.kbits);
     }
   }
   for (int jh = wave; jh < kNH; jh += kW) {
@@ -1249,7 +1249,7 @@ static hipError_t launch_one(const DecodeParams& prm, hipStream_t stream, hipEve
 hipError_t launch_decode(const DecodeParams& prm, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
   (void)hipGetLastError();  // report only this call's launch errors, not stale ones
   hipError_t err;
-  const bool k4 = prm.kbits == 4;
+  const bool k4 = prm.kbits > 2;  // 3- and 4-bit keys share the wide-key block and kernel
   if (prm.g <= 4)
     err = k4 ? launch_one<1, true>(prm, stream, ev_begin, ev_end) : launch_one<1, false>(prm, stream, ev_begin, ev_end);
   else if (prm.g <= 8)

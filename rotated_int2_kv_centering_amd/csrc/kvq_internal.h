@@ -76,7 +76,7 @@ struct DecodeParams {
   const float* mu;
   float clip;  // Q2's clip ratio for the appended token
   int gsize;   // Q2's group size G (32, 64 or 128) for the appended token
-  int kbits;   // bits per key code: 2, or 4 (2048-byte blocks with a high-bit plane)
+  int kbits;   // bits per key code: 2, or 3 / 4 (2048-byte blocks with a high-bit plane)
   int rot_kind;  // 0: r_k, r_v are dense [H][128][128]; 1: Hadamard, r_k, r_v are signs [H][128]
 };
 

@@ -81,9 +81,9 @@ __device__ __forceinline__ float2 q2_wave_range(float xv, int gsize) {
 // range of channel j's group (q2_wave_range).  `block` is the (page, KV head)
 // block to write, or null to only compute; `off` is the slot within the page
 // (0..15); tensor 0 = K, 1 = V.  The block keeps one metadata pair per 32
-// channels: for G > 32 each holds its group's pair.  kbits = 4 quantizes the
-// key to 16 levels: its low two bits go where a 2-bit code would, its high two
-// bits to the plane at byte kKHiPlane (record r at 8 r, same word and bit).
+// channels: for G > 32 each holds its group's pair.  kbits = 3 or 4 quantizes
+// the key to 8 or 16 levels: its low two bits go where a 2-bit code would, the
+// rest to the plane at byte kKHiPlane (record r at 8 r, same word and bit).
 // Returns the dequantized level of channel j.
 //
 // K code of slot s, channel c (kk = c/32, a = (c%32)/8, e = c%8): record
@@ -98,8 +98,8 @@ constexpr int kKHiPlane = 1536;  // byte offset of the 4-bit keys' high-bit plan
 
 __device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, uint8_t* block, int off, float clip,
                                                 float mn, float mx, int kbits = 2) {
-  const bool k4 = tensor == 0 && kbits == 4;
-  const float n_lv = k4 ? 15.0f : 3.0f;
+  const bool k4 = tensor == 0 && kbits > 2;  // a wide key: high part in the plane
+  const float n_lv = tensor == 0 ? static_cast<float>((1 << kbits) - 1) : 3.0f;
   const int lane = j & 63;
   const int w2 = j >> 6;
   const int grp = j >> 5;
@@ -191,7 +191,7 @@ __device__ __forceinline__ void q2_group32(const float (&x)[32], float clip, int
   // fp16 zero included): without this the compiler may round c*min straight
   // to fp16 in one mixed-precision multiply, which differs at fp16 ties.
   asm volatile("" : "+v"(mn), "+v"(mx));
-  const float s32 = (mx - mn) / n_lv;  // n_lv = 3, or 15 for 4-bit keys
+  const float s32 = (mx - mn) / n_lv;  // n_lv = 3, or 7 / 15 for 3- / 4-bit keys
   const _Float16 s16 = static_cast<_Float16>(s32);
   const _Float16 z16 = static_cast<_Float16>(mn);
   const float sc = static_cast<float>(s16);

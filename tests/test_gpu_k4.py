@@ -1,7 +1,7 @@
-"""GPU parity of 4-bit keys (the K4V2 budget) through the C ABI.
+"""GPU parity of 3- and 4-bit keys (K3V2, K4V2 budgets) through the C ABI.
 
-A cache with key_bits = 4 holds 2048-byte blocks: the 2-bit layout with each
-key code's low two bits, plus a high-bit plane.  Gates as for 2-bit keys: the
+A cache with key_bits = 3 or 4 holds 2048-byte blocks: the 2-bit layout with
+each key code's low two bits, plus a plane with the rest.  Gates as for 2-bit keys: the
 kernel's rotated rows within the fp32 bound of the fp64 rotation and the bytes
 bit-exact to the oracle's 16-level quantizer and packing on those rows (both
 append kernels); the fused step writing the append's bytes; decode within 2e-3
@@ -22,19 +22,21 @@ TOL = 2e-3
 K4 = 4
 
 
-@pytest.mark.parametrize("dtype,lens,rotation,group", [
-    ("bf16", [40, 9], "dense", 32),       # the tiled kernel
-    ("f32", [30, 2], "hadamard", 32),
-    ("bf16", [300, 77], "dense", 32),     # the bulk kernel
-    ("f32", [129, 64], "hadamard", 128),
-    ("bf16", [200, 50], "dense", 64),
+@pytest.mark.parametrize("dtype,lens,rotation,group,bits", [
+    ("bf16", [40, 9], "dense", 32, 4),       # the tiled kernel
+    ("f32", [30, 2], "hadamard", 32, 4),
+    ("bf16", [300, 77], "dense", 32, 4),     # the bulk kernel
+    ("f32", [129, 64], "hadamard", 128, 4),
+    ("bf16", [200, 50], "dense", 64, 4),
+    ("bf16", [40, 9], "dense", 32, 3),
+    ("f32", [300, 77], "dense", 32, 3),
 ])
-def test_append_bytes_match_the_oracle(dtype, lens, rotation, group):
+def test_append_bytes_match_the_oracle(dtype, lens, rotation, group, bits):
     dev = require_gpu()
     case = I.make_case("k4", 300 + sum(lens), B=2, Hq=8, Hkv=4, seq_lens=lens, dtype=dtype,
                        table_policy="interleaved", rotation=rotation)
     r_k, r_v = dense_rotations(case)
-    dc = DeviceCase(case, dev, group_size=group, key_bits=K4)
+    dc = DeviceCase(case, dev, group_size=group, key_bits=bits)
     rot = dc.append(rot_out=True).cpu().numpy()
     xg, wg = rot[:, :, 0, :], rot[:, :, 1, :]
     a = O.centre_keys(case.k, case.mu)
@@ -43,7 +45,7 @@ def test_append_bytes_match_the_oracle(dtype, lens, rotation, group):
         assert np.all(np.abs(xg[:, h] - x64[:, h]) <= rotation_error_bound(a[:, h], r_k[h]) + 1e-30)
         assert np.all(np.abs(wg[:, h] - w64[:, h]) <= rotation_error_bound(case.v[:, h], r_v[h]) + 1e-30)
     expect = np.zeros_like(dc.pool_np())
-    O.quantize_append(expect, case.Hkv, case.slots, xg, wg, group=group, key_bits=K4)
+    O.quantize_append(expect, case.Hkv, case.slots, xg, wg, group=group, key_bits=bits)
     np.testing.assert_array_equal(dc.pool_np(), expect)
 
 
@@ -57,15 +59,16 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("bits", [3, 4])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"B{s[0]}_Hq{s[1]}_Hkv{s[2]}_T{'-'.join(map(str, s[3]))}")
-def test_decode_parity(shape):
+def test_decode_parity(shape, bits):
     dev = require_gpu()
     B, Hq, Hkv, lens = shape
     case = I.make_case("k4d", 310 + sum(lens) + Hq, B=B, Hq=Hq, Hkv=Hkv, seq_lens=lens, table_policy="interleaved")
-    dc = DeviceCase(case, dev, key_bits=K4)
+    dc = DeviceCase(case, dev, key_bits=bits)
     dc.append(rot_out=False)
     ref = O.decode_attention(case.q, dc.pool_np(), case.Hkv, case.page_table, case.seq_lens, case.r_k, case.r_v,
-                             key_bits=K4)
+                             key_bits=bits)
     for ns in (0, 1, 3):
         got = dc.decode("f32", num_splits=ns)
         assert max_abs_rel(got, ref) <= TOL, ns
@@ -76,22 +79,23 @@ def test_decode_parity(shape):
 @pytest.mark.parametrize("shape", [(2, 32, 8, [1000, 17], "bf16"), (2, 64, 8, [513, 16], "f32"),
                                    (1, 16, 1, [300], "bf16"), (3, 8, 2, [0, 5, 100], "bf16")],
                          ids=lambda s: f"Hq{s[1]}_Hkv{s[2]}_{s[4]}")
-def test_step_writes_the_appended_bytes(shape):
+@pytest.mark.parametrize("bits", [3, 4])
+def test_step_writes_the_appended_bytes(shape, bits):
     dev = require_gpu()
     B, Hq, Hkv, lens, dtype = shape
     case = I.make_case("k4s", 320 + sum(lens) + Hq, B=B, Hq=Hq, Hkv=Hkv, seq_lens=lens, dtype=dtype,
                        table_policy="interleaved")
     newest = _newest(case)
-    a = DeviceCase(case, dev, key_bits=K4)
+    a = DeviceCase(case, dev, key_bits=bits)
     _prefill(a, case, newest)
-    b = DeviceCase(case, dev, key_bits=K4)
+    b = DeviceCase(case, dev, key_bits=bits)
     b.pool.copy_(a.pool)
     _append_newest(a, newest)
     k_new, v_new = _new_kv(case, b, newest, dev)
     got = b.step(k_new, v_new, "f32")
     np.testing.assert_array_equal(b.pool_np(), a.pool_np())
     ref = O.decode_attention(case.q, b.pool_np(), Hkv, case.page_table, case.seq_lens, case.r_k, case.r_v,
-                             key_bits=K4)
+                             key_bits=bits)
     assert max_abs_rel(got, ref) <= TOL
 
 
