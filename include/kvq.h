@@ -107,8 +107,7 @@ typedef struct {
                            is 2048 bytes: the 1536-byte layout holds each key
                            code's low two bits and bytes [1536, 2048) the rest
                            (record r = 16 a + s at 1536 + 8 r, words H0, H1 at
-                           the bits of K0, K1; one bit used for 3-bit keys).
-                           kvq_output_error takes 2-bit keys only            */
+                           the bits of K0, K1; one bit used for 3-bit keys)   */
 } kvq_cache;
 
 /*

@@ -426,7 +426,6 @@ kvq_status kvq_output_error(const kvq_cache* cache, const void* q, kvq_dtype q_d
                             void* stream) {
   kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
-  if (cache->key_bits > 2) return fail(KVQ_EUNSUPPORTED, "keys wider than 2 bits are not read by this call yet");
   if (batch < 0) return fail(KVQ_EINVAL, "batch=%d must be >= 0", batch);
   if (batch > kvq::kMaxEvalBatch)
     return fail(KVQ_EUNSUPPORTED, "batch=%d exceeds the evaluator's %d", batch, kvq::kMaxEvalBatch);
@@ -484,6 +483,7 @@ kvq_status kvq_output_error(const kvq_cache* cache, const void* q, kvq_dtype q_d
   a.r_k = r_k;
   a.r_v = r_v;
   a.rot_kind = cache->rotation;
+  a.kbits = cache->key_bits > 2 ? cache->key_bits : 2;
   a.sm_scale = sm_scale == 0.0f ? 1.0f / std::sqrt(static_cast<float>(kHeadDim)) : sm_scale;
   a.n_splits = plan.n_splits;
   a.pages_per_split = plan.pages_per_split;

@@ -69,7 +69,7 @@ struct PageRegs {
   float err;  // this lane's token's squared error (lanes 0..15)
 };
 
-template <int kNH, bool kF32>
+template <int kNH, bool kF32, bool kWide>  // kWide: 3- or 4-bit keys (2048-byte blocks)
 __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2))) void eval_attn_kernel(
     const EvalParams p) {
   const int tid = threadIdx.x;
@@ -101,7 +101,9 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   __shared__ float s_qh[kNH][kHeadDim];  // q R_K * c
   __shared__ float s_qs[kNH][4];         // per-32-channel sums of s_qh
   // per-wave page staging, reused by the merges
-  constexpr int kStage = 2 * kPage * kRowPad + kBlockBytes / 4 + 2 * kNH * kPage + 2 * kNH;
+  constexpr int kBlkWords = (kWide ? kBlockBytesK4 : kBlockBytes) / 4;
+  constexpr int kStage = 2 * kPage * kRowPad + kBlkWords + 2 * kNH * kPage + 2 * kNH;
+  constexpr bool wide = kWide;  // the high-bit plane at byte 1536
   constexpr int kMergeW = kEvWaves * kNH * (3 * kHeadDim + 4) + kEvWaves;
   constexpr int kBuf = kEvWaves * kStage > kMergeW ? kEvWaves * kStage : kMergeW;
   __shared__ float s_buf[kBuf];
@@ -138,8 +140,8 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   float* const st = s_buf + wave * kStage;
   float* const s_k = st;                                   // [16][kRowPad]
   float* const s_v = st + kPage * kRowPad;                 // [16][kRowPad]
-  uint32_t* const s_blk = reinterpret_cast<uint32_t*>(st + 2 * kPage * kRowPad);  // 384 words
-  float* const s_p = st + 2 * kPage * kRowPad + kBlockBytes / 4;  // [2][kNH][16]
+  uint32_t* const s_blk = reinterpret_cast<uint32_t*>(st + 2 * kPage * kRowPad);  // 384 (512 with wide keys) words
+  float* const s_p = st + 2 * kPage * kRowPad + kBlkWords;  // [2][kNH][16]
   float* const s_al = s_p + 2 * kNH * kPage;                      // [2][kNH]
 
   const int p_first = split * p.pages_per_split;
@@ -168,9 +170,9 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   };
   auto load_page = [&](int pg, int id, PageRegs<kF32>& r) {
     const int nt = min(kPage, T - kPage * pg);
-    const uint8_t* blk = p.pool + (static_cast<size_t>(id) * H + h) * kBlockBytes;
+    const uint8_t* blk = p.pool + (static_cast<size_t>(id) * H + h) * (wide ? kBlockBytesK4 : kBlockBytes);
     r.blk[0] = *reinterpret_cast<const uint4v*>(blk + 16 * lane);
-    r.blk[1] = lane < 32 ? *reinterpret_cast<const uint4v*>(blk + 16 * (64 + lane)) : uint4v{0u, 0u, 0u, 0u};
+    r.blk[1] = (lane < 32 || wide) ? *reinterpret_cast<const uint4v*>(blk + 16 * (64 + lane)) : uint4v{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < PageRegs<kF32>::kRowWords; ++u) {
       const int idx = u * 64 + lane;
@@ -199,7 +201,7 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   };
   auto stage_page = [&](const PageRegs<kF32>& r) {
     reinterpret_cast<uint4v*>(s_blk)[lane] = r.blk[0];
-    if (lane < 32) reinterpret_cast<uint4v*>(s_blk)[64 + lane] = r.blk[1];
+    if (lane < 32 || wide) reinterpret_cast<uint4v*>(s_blk)[64 + lane] = r.blk[1];
 #pragma unroll
     for (int u = 0; u < PageRegs<kF32>::kRowWords; ++u) {
       const int idx = u * 64 + lane;
@@ -271,13 +273,18 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const uint32_t w01[2] = {s_blk[4 * (16 * a + t_l)], s_blk[4 * (16 * a + t_l) + 1]};
+        // wide keys: the high bits, record 16 a + t_l of the plane at word 384, words H0, H1
+        const uint32_t h01[2] = {wide ? s_blk[384 + 2 * (16 * a + t_l)] : 0u,
+                                 wide ? s_blk[384 + 2 * (16 * a + t_l) + 1] : 0u};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const uint32_t w = w01[kk >> 1];
+          const uint32_t w = w01[kk >> 1], wh = h01[kk >> 1];
           float cf[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            cf[e] = static_cast<float>((w >> (2 * (4 * (kk & 1) + (e >> 1)) + 16 * (e & 1))) & 3u);
+          for (int e = 0; e < 8; ++e) {
+            const int sh = 2 * (4 * (kk & 1) + (e >> 1)) + 16 * (e & 1);
+            cf[e] = static_cast<float>(((w >> sh) & 3u) | (((wh >> sh) & 3u) << 2));
+          }
 #pragma unroll
           for (int u = 0; u < kHQ; ++u) {
             const float4v q0 = *reinterpret_cast<const float4v*>(&s_qh[jq + 4 * u][32 * kk + 8 * a]);
@@ -603,21 +610,26 @@ __global__ __launch_bounds__(kEvThreads) void eval_project_kernel(const EvalPara
   if (tid == 0) __hip_atomic_store(p.proj_counters + j, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int kNH>
+template <int kNH, bool kWide>
 hipError_t launch_attn(const EvalParams& p, hipStream_t stream) {
   const dim3 grid(p.num_kv_heads * p.n_splits, p.batch, (p.g + kEvHeads - 1) / kEvHeads);
   if (p.kv_kind == 1)
-    hipLaunchKernelGGL((eval_attn_kernel<kNH, true>), grid, dim3(kEvThreads), 0, stream, p);
+    hipLaunchKernelGGL((eval_attn_kernel<kNH, true, kWide>), grid, dim3(kEvThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((eval_attn_kernel<kNH, false>), grid, dim3(kEvThreads), 0, stream, p);
+    hipLaunchKernelGGL((eval_attn_kernel<kNH, false, kWide>), grid, dim3(kEvThreads), 0, stream, p);
   return hipGetLastError();
+}
+
+template <bool kWide>
+hipError_t launch_attn_g(const EvalParams& p, hipStream_t stream) {
+  return p.g <= 4 ? launch_attn<4, kWide>(p, stream) : launch_attn<kEvHeads, kWide>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_eval(const EvalParams& p, hipStream_t stream) {
   (void)hipGetLastError();  // report only this call's launch errors
-  hipError_t e = p.g <= 4 ? launch_attn<4>(p, stream) : launch_attn<kEvHeads>(p, stream);
+  hipError_t e = p.kbits > 2 ? launch_attn_g<true>(p, stream) : launch_attn_g<false>(p, stream);
   if (e != hipSuccess) return e;
   const dim3 pgrid(p.num_q_heads, p.n_chunks);
   if (p.w_kind == 1)

@@ -107,6 +107,7 @@ struct EvalParams {
   const float* r_k;
   const float* r_v;
   int rot_kind;   // 0 dense [H][128][128], 1 Hadamard signs [H][128]
+  int kbits;      // bits per key code (3 and 4: 2048-byte blocks)
   float sm_scale;
   int n_splits, pages_per_split;
   float* part;             // [B][H_kv][head chunk][n_splits][kEvHeads][kEvPartStride]

@@ -125,13 +125,3 @@ def test_full_size_four_bit_keys_sampled_heads():
                              heads=heads, key_bits=K4)
     for b, j in heads:
         assert max_abs_rel(got[b, j], ref[b, j]) <= TOL, j
-
-
-def test_evaluator_rejects_four_bit_keys():
-    from rotated_int2_kv_centering_amd import kvq
-    require_gpu()
-    c = kvq.make_cache(1, 8, 1 << 20, key_bits=K4)
-    assert kvq.load().kvq_output_error(
-        __import__("ctypes").byref(c), 1 << 20, kvq.KVQ_BF16, 1, 4, 1 << 20, 4, 1 << 20, 64, 1 << 20, 1 << 20,
-        kvq.KVQ_BF16, 1 << 20, None, 1 << 20, 1 << 20, 0.0, 1 << 20, kvq.KVQ_BF16, 96, 1 << 20, 1 << 20, 1 << 20,
-        1 << 20, 1 << 20, 1 << 24, None) == kvq.KVQ_EUNSUPPORTED
