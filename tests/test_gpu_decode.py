@@ -231,3 +231,19 @@ def test_full_size_sampled_heads(name):
     for b, j in heads:
         err = max_abs_rel(got[b, j], ref[b, j])
         assert err <= TOL, (b, j, err)
+
+
+@pytest.mark.parametrize("num_splits", [64, 100])
+def test_many_splits_take_the_register_merge(num_splits):
+    """With more (split, head) partial rows than the ring holds (64 splits x 4 heads x
+    132 floats > the g <= 4 ring), the merging workgroup loads them per thread instead
+    of staging them by DMA; both merges must agree with the oracle."""
+    dev = require_gpu()
+    case = I.make_case("ms", 91 + num_splits, B=2, Hq=8, Hkv=2, seq_lens=[4096, 3000], table_policy="interleaved")
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False, chunk=1 << 20)
+    ref = O.decode_attention(case.q, dc.pool_np(), case.Hkv, case.page_table, case.seq_lens, case.r_k, case.r_v)
+    got = dc.decode("f32", num_splits=num_splits)
+    assert max_abs_rel(got, ref) <= TOL
+    auto = dc.decode("f32")  # the automatic plan stages the rows
+    assert max_abs_rel(auto, ref) <= TOL
