@@ -63,6 +63,13 @@ two bits of each key code (code & 3); bytes [1536, 2048) are 64 records of 8
 bytes, record r = 16*a + s holding words H0, H1 at byte 1536 + 8*r: the high
 two bits (code >> 2) of the key code of slot s, channel c sit in record
 16*a + s, word H[kk // 2], at the same bit as its low bits in K[kk // 2].
+
+Values of 3 or 4 bits (val_bits; K3V3 is the page's symmetric budget) add
+another 512-byte plane after the keys' plane, at P = 1536 (2-bit keys) or
+P = 2048 (wider keys), so a K3V3 block is 2560 bytes.  Its 64 records of 8
+bytes hold words VH0, VH1 at byte P + 8*r: the high bits of the V code of slot
+s, channel c sit in record 16*a + b, word VH[i // 2], at the same bit as its
+low bits in V[i // 2].
 """
 
 from __future__ import annotations
@@ -78,10 +85,16 @@ CODE_BYTES = 1024
 HI_PLANE = 1536  # byte offset of the 4-bit keys' high-bit plane
 
 
-def block_bytes(key_bits: int = 2) -> int:
-    """Bytes of one (page, KV head) block: 1536 for 2-bit keys, 2048 for 3- and 4-bit keys."""
-    assert key_bits in (2, 3, 4), "key codes are 2, 3 or 4 bits"
-    return BLOCK_BYTES if key_bits == 2 else BLOCK_BYTES + 512
+def block_bytes(key_bits: int = 2, val_bits: int = 2) -> int:
+    """Bytes of one (page, KV head) block: 1536, plus 512 for 3- or 4-bit keys and
+    512 for 3- or 4-bit values."""
+    assert key_bits in (2, 3, 4) and val_bits in (2, 3, 4), "codes are 2, 3 or 4 bits"
+    return BLOCK_BYTES + 512 * (key_bits > 2) + 512 * (val_bits > 2)
+
+
+def value_plane(key_bits: int = 2) -> int:
+    """Byte offset of the wide values' high-bit plane: after the keys' plane, if any."""
+    return HI_PLANE + 512 * (key_bits > 2)
 
 
 # --------------------------------------------------------------------- checks
@@ -234,14 +247,14 @@ _V_POS = np.array([[_v_position(s, c) for c in range(HEAD_DIM)] for s in range(P
 
 
 def pack_block(k_codes, k_s16, k_z16, v_codes, v_s16, v_z16, block: np.ndarray | None = None,
-               slots=None, key_bits: int = 2) -> np.ndarray:
+               slots=None, key_bits: int = 2, val_bits: int = 2) -> np.ndarray:
     """Write token slots of one (page, KV head) block in the layout above.
 
     ``k_codes``/``v_codes`` are uint8 [n, 128]; scales/zeros float16 [n, 4];
     ``slots`` (default 0..n-1, distinct) are the slot indices inside the page.
     Bits of slots not written are left as they were in ``block``.
     """
-    nb = block_bytes(key_bits)
+    nb = block_bytes(key_bits, val_bits)
     blk = np.zeros(nb, np.uint8) if block is None else block
     assert blk.shape == (nb,) and blk.dtype == np.uint8
     n = np.asarray(k_codes).shape[0]
@@ -249,8 +262,9 @@ def pack_block(k_codes, k_s16, k_z16, v_codes, v_s16, v_z16, block: np.ndarray |
     assert len(np.unique(slots)) == len(slots)
     words = blk[:CODE_BYTES].view("<u4").reshape(-1)           # 64 records x 4 words
     k_codes = np.asarray(k_codes, np.uint32)
-    assert k_codes.max(initial=0) < (1 << key_bits)
-    for codes, table in ((k_codes & 3, _K_POS), (v_codes, _V_POS)):
+    v_codes = np.asarray(v_codes, np.uint32)
+    assert k_codes.max(initial=0) < (1 << key_bits) and v_codes.max(initial=0) < (1 << val_bits)
+    for codes, table in ((k_codes & 3, _K_POS), (v_codes & 3, _V_POS)):
         pos = table[slots]                                      # [n, 128, (record, word, bit)]
         idx = (pos[..., 0] * 4 + pos[..., 1]).reshape(-1)
         bit = pos[..., 2].reshape(-1).astype(np.uint32)
@@ -258,11 +272,20 @@ def pack_block(k_codes, k_s16, k_z16, v_codes, v_s16, v_z16, block: np.ndarray |
         np.bitwise_and.at(words, idx, ~(np.uint32(3) << bit))
         np.bitwise_or.at(words, idx, (val & np.uint32(3)) << bit)
     if key_bits > 2:  # high bits of the key codes: record r at 1536 + 8 r, word H[kk // 2], same bit
-        hi = blk[HI_PLANE:].view("<u4").reshape(-1)              # 64 records x 2 words
+        hi = blk[HI_PLANE:HI_PLANE + 512].view("<u4").reshape(-1)  # 64 records x 2 words
         pos = _K_POS[slots]
         idx = (pos[..., 0] * 2 + pos[..., 1]).reshape(-1)
         bit = pos[..., 2].reshape(-1).astype(np.uint32)
         val = (k_codes >> np.uint32(2)).reshape(-1)
+        np.bitwise_and.at(hi, idx, ~(np.uint32(3) << bit))
+        np.bitwise_or.at(hi, idx, (val & np.uint32(3)) << bit)
+    if val_bits > 2:  # high bits of the value codes: record r at value_plane + 8 r, word VH[i // 2], same bit
+        vp = value_plane(key_bits)
+        hi = blk[vp:vp + 512].view("<u4").reshape(-1)
+        pos = _V_POS[slots]
+        idx = (pos[..., 0] * 2 + pos[..., 1] - 2).reshape(-1)
+        bit = pos[..., 2].reshape(-1).astype(np.uint32)
+        val = (v_codes >> np.uint32(2)).reshape(-1)
         np.bitwise_and.at(hi, idx, ~(np.uint32(3) << bit))
         np.bitwise_or.at(hi, idx, (val & np.uint32(3)) << bit)
     meta = blk[CODE_BYTES:BLOCK_BYTES].view("<u2").reshape(16, 2, 4, 2)   # [record m][K/V][i][scale/zero]
@@ -277,13 +300,13 @@ def pack_block(k_codes, k_s16, k_z16, v_codes, v_s16, v_z16, block: np.ndarray |
     return blk
 
 
-def unpack_blocks(blocks: np.ndarray, key_bits: int = 2):
+def unpack_blocks(blocks: np.ndarray, key_bits: int = 2, val_bits: int = 2):
     """Inverse of ``pack_block`` for a stack of blocks [n, 1536] (all 16 slots each).
 
     Returns (k_codes, k_s16, k_z16, v_codes, v_s16, v_z16) with codes uint8
     [n, 16, 128] and scales/zeros float16 [n, 16, 4].
     """
-    blk = np.ascontiguousarray(blocks, np.uint8).reshape(-1, block_bytes(key_bits))
+    blk = np.ascontiguousarray(blocks, np.uint8).reshape(-1, block_bytes(key_bits, val_bits))
     words = blk[:, :CODE_BYTES].view("<u4").reshape(-1, 64, 4).astype(np.int64)
     meta = blk[:, CODE_BYTES:BLOCK_BYTES].view("<f2").reshape(-1, 16, 2, 4, 2)   # [n][record m][K/V][i][scale/zero]
 
@@ -296,31 +319,37 @@ def unpack_blocks(blocks: np.ndarray, key_bits: int = 2):
     i = np.broadcast_to((slots % 4)[:, None], rec.shape)
     k = gather(_K_POS)
     if key_bits > 2:
-        hi = blk[:, HI_PLANE:].view("<u4").reshape(-1, 64, 2).astype(np.int64)
+        hi = blk[:, HI_PLANE:HI_PLANE + 512].view("<u4").reshape(-1, 64, 2).astype(np.int64)
         r_, w_, b_ = _K_POS[..., 0], _K_POS[..., 1], _K_POS[..., 2]
         k = k + (((hi[:, r_, w_] >> b_[None]) & 3) << 2).astype(np.uint8)
+    v = gather(_V_POS)
+    if val_bits > 2:
+        vp = value_plane(key_bits)
+        hi = blk[:, vp:vp + 512].view("<u4").reshape(-1, 64, 2).astype(np.int64)
+        r_, w_, b_ = _V_POS[..., 0], _V_POS[..., 1] - 2, _V_POS[..., 2]
+        v = v + (((hi[:, r_, w_] >> b_[None]) & 3) << 2).astype(np.uint8)
     return (k, meta[:, rec, 0, i, 0], meta[:, rec, 0, i, 1],
-            gather(_V_POS), meta[:, rec, 1, i, 0], meta[:, rec, 1, i, 1])
+            v, meta[:, rec, 1, i, 0], meta[:, rec, 1, i, 1])
 
 
-def unpack_block(block: np.ndarray, key_bits: int = 2):
+def unpack_block(block: np.ndarray, key_bits: int = 2, val_bits: int = 2):
     """``unpack_blocks`` for a single block: codes [16, 128], scales/zeros [16, 4]."""
-    return tuple(x[0] for x in unpack_blocks(np.asarray(block, np.uint8)[None], key_bits))
+    return tuple(x[0] for x in unpack_blocks(np.asarray(block, np.uint8)[None], key_bits, val_bits))
 
 
-def pool_bytes(num_pages: int, num_kv_heads: int, key_bits: int = 2) -> int:
-    return int(num_pages) * int(num_kv_heads) * block_bytes(key_bits)
+def pool_bytes(num_pages: int, num_kv_heads: int, key_bits: int = 2, val_bits: int = 2) -> int:
+    return int(num_pages) * int(num_kv_heads) * block_bytes(key_bits, val_bits)
 
 
-def block_view(pool: np.ndarray, page: int, h: int, num_kv_heads: int, key_bits: int = 2) -> np.ndarray:
-    nb = block_bytes(key_bits)
+def block_view(pool: np.ndarray, page: int, h: int, num_kv_heads: int, key_bits: int = 2, val_bits: int = 2) -> np.ndarray:
+    nb = block_bytes(key_bits, val_bits)
     off = (int(page) * num_kv_heads + int(h)) * nb
     return pool[off:off + nb]
 
 
 # ------------------------------------------------------------- quantize-append
 def quantize_append(pool: np.ndarray, num_kv_heads: int, slots, x: np.ndarray, w: np.ndarray,
-                    clip: float = 1.0, group: int = GROUP, key_bits: int = 2) -> None:
+                    clip: float = 1.0, group: int = GROUP, key_bits: int = 2, val_bits: int = 2) -> None:
     """Quantize rotated fp32 rows and store them at the given cache slots.
 
     ``x``/``w`` are float32 [n, H_kv, 128] (already centred and rotated);
@@ -328,7 +357,7 @@ def quantize_append(pool: np.ndarray, num_kv_heads: int, slots, x: np.ndarray, w
     Q2's clip ratio c and group size G.  Writes ``pool`` (uint8) in place.
     """
     kc, ks, kz = int2_quantize(x, clip, group, key_bits)
-    vc, vs, vz = int2_quantize(w, clip, group)
+    vc, vs, vz = int2_quantize(w, clip, group, val_bits)
     ks, kz, vs, vz = (meta_per_32(a) for a in (ks, kz, vs, vz))
     slots = np.asarray(slots, np.int64)
     assert len(np.unique(slots)) == len(slots), "slots must be distinct"
@@ -338,16 +367,17 @@ def quantize_append(pool: np.ndarray, num_kv_heads: int, slots, x: np.ndarray, w
         offs = slots[sel] % PAGE
         for h in range(num_kv_heads):
             pack_block(kc[sel, h], ks[sel, h], kz[sel, h], vc[sel, h], vs[sel, h], vz[sel, h],
-                       block=block_view(pool, page, h, num_kv_heads, key_bits), slots=offs, key_bits=key_bits)
+                       block=block_view(pool, page, h, num_kv_heads, key_bits, val_bits), slots=offs, key_bits=key_bits,
+                       val_bits=val_bits)
 
 
 def append_tokens(pool, num_kv_heads, slots, k, v, mu, r_k, r_v, clip: float = 1.0, group: int = GROUP,
-                  key_bits: int = 2) -> None:
+                  key_bits: int = 2, val_bits: int = 2) -> None:
     """Full write path: centre keys, rotate K and V, quantize, pack (OptR §1, §3.1 Eq. (4))."""
     check_orthogonal_all(r_k)
     check_orthogonal_all(r_v)
     x, w = rotated_inputs(k, v, mu, r_k, r_v)
-    quantize_append(pool, num_kv_heads, slots, x, w, clip, group, key_bits)
+    quantize_append(pool, num_kv_heads, slots, x, w, clip, group, key_bits, val_bits)
 
 
 def check_orthogonal_all(r: np.ndarray, tol: float = 1e-6) -> None:
@@ -356,7 +386,7 @@ def check_orthogonal_all(r: np.ndarray, tol: float = 1e-6) -> None:
 
 
 # ----------------------------------------------------------- reading the cache
-def gather_sequence(pool, num_kv_heads, table_row, seq_len, h, num_pages=None, key_bits: int = 2):
+def gather_sequence(pool, num_kv_heads, table_row, seq_len, h, num_pages=None, key_bits: int = 2, val_bits: int = 2):
     """Dequantized rotated keys x_hat and values w_hat [T', 128] of one sequence and KV head (fp64).
 
     A table entry outside [0, num_pages) marks an absent page: its positions
@@ -368,12 +398,12 @@ def gather_sequence(pool, num_kv_heads, table_row, seq_len, h, num_pages=None, k
         return np.zeros((0, HEAD_DIM)), np.zeros((0, HEAD_DIM))
     n_pages = (T + PAGE - 1) // PAGE
     if num_pages is None:
-        num_pages = np.asarray(pool).size // (num_kv_heads * block_bytes(key_bits))
+        num_pages = np.asarray(pool).size // (num_kv_heads * block_bytes(key_bits, val_bits))
     pages = np.asarray(table_row[:n_pages], np.int64)
     present = (pages >= 0) & (pages < num_pages)
-    offs = (np.where(present, pages, 0) * num_kv_heads + int(h)) * block_bytes(key_bits)
-    blocks = np.asarray(pool, np.uint8)[offs[:, None] + np.arange(block_bytes(key_bits))[None, :]]
-    kc, ks, kz, vc, vs, vz = unpack_blocks(blocks, key_bits)
+    offs = (np.where(present, pages, 0) * num_kv_heads + int(h)) * block_bytes(key_bits, val_bits)
+    blocks = np.asarray(pool, np.uint8)[offs[:, None] + np.arange(block_bytes(key_bits, val_bits))[None, :]]
+    kc, ks, kz, vc, vs, vz = unpack_blocks(blocks, key_bits, val_bits)
     keep = np.repeat(present, PAGE)[:T]
     x = int2_dequantize(kc, ks, kz).reshape(-1, HEAD_DIM)[:T][keep]
     w = int2_dequantize(vc, vs, vz).reshape(-1, HEAD_DIM)[:T][keep]
@@ -398,7 +428,7 @@ def softmax_attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray, scale
 
 
 def decode_attention(q, pool, num_kv_heads, page_table, seq_lens, r_k, r_v, sm_scale=None,
-                     heads=None, bypass=None, num_pages=None, key_bits: int = 2) -> np.ndarray:
+                     heads=None, bypass=None, num_pages=None, key_bits: int = 2, val_bits: int = 2) -> np.ndarray:
     """Decode attention read from the packed cache (OptR §3.2 Eq. (5), §3.1 Eq. (4)).
 
     For query head j of sequence b, with h = j // g:
@@ -426,7 +456,7 @@ def decode_attention(q, pool, num_kv_heads, page_table, seq_lens, r_k, r_v, sm_s
         if (b, h) not in cache:
             if bypass is None:
                 cache[(b, h)] = gather_sequence(pool, num_kv_heads, page_table[b], seq_lens[b], h, num_pages,
-                                                key_bits)
+                                                key_bits, val_bits)
             else:
                 x, w, tok_seq = bypass
                 sel = np.asarray(tok_seq) == b
@@ -460,7 +490,7 @@ def window_slot(t: int, sinks: int, recent: int) -> int:
 
 
 def effective_kv_window(pool, num_kv_heads, table_row, seq_len, h, mu_h, r_k_h, r_v_h, k_exact, v_exact,
-                        sinks, recent, num_pages=None, key_bits: int = 2):
+                        sinks, recent, num_pages=None, key_bits: int = 2, val_bits: int = 2):
     """Keys and values attention uses for one sequence and KV head, in the original basis (fp64).
 
     Window positions (``window_mask``) take k_exact[s], v_exact[s] (the BF16
@@ -476,12 +506,12 @@ def effective_kv_window(pool, num_kv_heads, table_row, seq_len, h, mu_h, r_k_h, 
     win = window_mask(T, sinks, recent)
     n_pages = (T + PAGE - 1) // PAGE
     if num_pages is None:
-        num_pages = np.asarray(pool).size // (num_kv_heads * block_bytes(key_bits))
+        num_pages = np.asarray(pool).size // (num_kv_heads * block_bytes(key_bits, val_bits))
     pages = np.asarray(table_row[:n_pages], np.int64)
     present = (pages >= 0) & (pages < num_pages)
-    offs = (np.where(present, pages, 0) * num_kv_heads + int(h)) * block_bytes(key_bits)
-    blocks = np.asarray(pool, np.uint8)[offs[:, None] + np.arange(block_bytes(key_bits))[None, :]]
-    kc, ks, kz, vc, vs, vz = unpack_blocks(blocks, key_bits)
+    offs = (np.where(present, pages, 0) * num_kv_heads + int(h)) * block_bytes(key_bits, val_bits)
+    blocks = np.asarray(pool, np.uint8)[offs[:, None] + np.arange(block_bytes(key_bits, val_bits))[None, :]]
+    kc, ks, kz, vc, vs, vz = unpack_blocks(blocks, key_bits, val_bits)
     x_hat = int2_dequantize(kc, ks, kz).reshape(-1, HEAD_DIM)[:T]
     w_hat = int2_dequantize(vc, vs, vz).reshape(-1, HEAD_DIM)[:T]
     k_int2 = x_hat @ np.asarray(r_k_h, np.float64).T + np.asarray(mu_h, np.float64)
@@ -493,7 +523,7 @@ def effective_kv_window(pool, num_kv_heads, table_row, seq_len, h, mu_h, r_k_h, 
 
 
 def decode_attention_window(q, pool, num_kv_heads, page_table, seq_lens, mu, r_k, r_v, k_seqs, v_seqs,
-                            sinks, recent, sm_scale=None, heads=None, num_pages=None, key_bits: int = 2) -> np.ndarray:
+                            sinks, recent, sm_scale=None, heads=None, num_pages=None, key_bits: int = 2, val_bits: int = 2) -> np.ndarray:
     """OptR §3.2 Eq. (5) with the BF16 window: Eq. (1)-(2) attention of query
     head j of sequence b over ``effective_kv_window`` of KV head h = j // g.
 
@@ -514,7 +544,7 @@ def decode_attention_window(q, pool, num_kv_heads, page_table, seq_lens, mu, r_k
         if (b, h) not in cache:
             cache[(b, h)] = effective_kv_window(pool, num_kv_heads, page_table[b], seq_lens[b], h, mu[h], r_k[h],
                                                 r_v[h], np.asarray(k_seqs[b])[:, h], np.asarray(v_seqs[b])[:, h],
-                                                sinks, recent, num_pages, key_bits)
+                                                sinks, recent, num_pages, key_bits, val_bits)
         k_eff, v_eff = cache[(b, h)]
         out[b, j] = softmax_attention(q[b, j], k_eff, v_eff, sm_scale)
     return out
@@ -590,7 +620,7 @@ def present_positions(table_row, seq_len: int, num_pages: int) -> np.ndarray:
 
 
 def output_error(q, pool, num_kv_heads, page_table, seq_lens, k_seqs, v_seqs, mu, r_k, r_v, w_o,
-                 sm_scale=None, num_pages=None, kv_heads=None, key_bits: int = 2):
+                 sm_scale=None, num_pages=None, kv_heads=None, key_bits: int = 2, val_bits: int = 2):
     """OptR §3.2 Eq. (6)-(10) at the decode position of every sequence, from the packed cache (fp64).
 
     Query head j of sequence b (KV head h = j // g) attends positions 0..T_b-1.
@@ -611,7 +641,7 @@ def output_error(q, pool, num_kv_heads, page_table, seq_lens, k_seqs, v_seqs, mu
     w_o = np.asarray(w_o, np.float64)
     d_model = w_o.shape[0]
     if num_pages is None:
-        num_pages = np.asarray(pool).size // (num_kv_heads * block_bytes(key_bits))
+        num_pages = np.asarray(pool).size // (num_kv_heads * block_bytes(key_bits, val_bits))
     dy_k = np.zeros((B, Hq, d_model))
     dy_v = np.zeros((B, Hq, d_model))
     e_out = np.zeros((B, Hq))
@@ -620,7 +650,8 @@ def output_error(q, pool, num_kv_heads, page_table, seq_lens, k_seqs, v_seqs, mu
         T = int(seq_lens[b])
         keep = present_positions(page_table[b], T, num_pages)
         for h in (range(num_kv_heads) if kv_heads is None else kv_heads):
-            x_hat, w_hat = gather_sequence(pool, num_kv_heads, page_table[b], T, h, num_pages, key_bits)
+            x_hat, w_hat = gather_sequence(pool, num_kv_heads, page_table[b], T, h, num_pages, key_bits,
+                                           val_bits)
             k_eff = x_hat @ np.asarray(r_k[h], np.float64).T + np.asarray(mu[h], np.float64)
             v_eff = w_hat @ np.asarray(r_v[h], np.float64).T
             k_ex = np.asarray(k_seqs[b], np.float64)[:T, h][keep]

@@ -923,3 +923,82 @@ def test_quantizer_three_bits_hand_derived_and_nearest():
         ref = O.softmax_attention(c.q[0, j], kq[:, 0] @ c.r_k[0].astype(np.float64).T + c.mu[0],
                                   vq[:, 0] @ c.r_v[0].astype(np.float64).T, 1 / np.sqrt(128))
         np.testing.assert_allclose(got[0, j], ref, rtol=0, atol=1e-11)
+
+
+# ------------------------------------------- 3- and 4-bit values (K3V3 budget)
+def test_wide_value_block_layout_golden(golden_dir):
+    """Hand-derived byte positions of wide value codes (low bits in place, high
+    bits in the value plane after the keys' plane); keys and metadata are
+    unaffected and the block grows by 512 bytes."""
+    with open(os.path.join(golden_dir, "block_layout_wide_v.txt")) as f:
+        lines = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    z = np.zeros((1, 128), np.uint8)
+    zf = np.zeros((1, 4), np.float16)
+    for parts in lines:
+        kb, vb, slot, ch, code, *pairs = map(int, parts[1:])
+        vc = z.copy()
+        vc[0, ch] = code
+        blk = O.pack_block(z, zf, zf, vc, zf, zf, slots=[slot], key_bits=kb, val_bits=vb)
+        assert blk.size == 1536 + 512 * (kb > 2) + 512 * (vb > 2)
+        want = dict(zip(pairs[0::2], pairs[1::2]))
+        nz = np.nonzero(blk)[0]
+        assert set(nz) == set(want) and all(blk[b] == v for b, v in want.items()), parts
+        back = O.unpack_block(blk, key_bits=kb, val_bits=vb)[3]
+        assert back[slot, ch] == code and np.count_nonzero(back) == 1
+    assert len(lines) == 4
+
+
+def test_wide_value_pack_unpack_roundtrip_and_planes_independent():
+    """K3V3 and K4V4 blocks round-trip; the key plane and the value plane do not
+    overlap (rewriting values leaves every key bit as it was and vice versa)."""
+    rng = np.random.default_rng(46)
+    for kb, vb in ((3, 3), (4, 4), (2, 4)):
+        kc = rng.integers(0, 1 << kb, (16, 128)).astype(np.uint8)
+        vc = rng.integers(0, 1 << vb, (16, 128)).astype(np.uint8)
+        ks, kz, vs, vz = (rng.standard_normal((16, 4)).astype(np.float16) for _ in range(4))
+        blk = O.pack_block(kc, ks, kz, vc, vs, vz, key_bits=kb, val_bits=vb)
+        for got, want in zip(O.unpack_block(blk, key_bits=kb, val_bits=vb), (kc, ks, kz, vc, vs, vz)):
+            np.testing.assert_array_equal(got, want)
+        # the 2-bit reading of the first 1536 bytes sees the low bits of both
+        lo = O.unpack_block(blk[:1536])
+        np.testing.assert_array_equal(lo[0], kc & 3)
+        np.testing.assert_array_equal(lo[3], vc & 3)
+        vc2 = rng.integers(0, 1 << vb, (16, 128)).astype(np.uint8)
+        O.pack_block(kc, ks, kz, vc2, vs, vz, block=blk, key_bits=kb, val_bits=vb)
+        back = O.unpack_block(blk, key_bits=kb, val_bits=vb)
+        np.testing.assert_array_equal(back[0], kc)
+        np.testing.assert_array_equal(back[3], vc2)
+
+
+def test_wide_value_decode_equals_attention_on_effective_kv_and_is_closer():
+    """Decode over a K3V3 pool equals Eq. (1)-(2) attention on k~ = Q3((k - mu) R_K)
+    R_K^T + mu and v~ = Q3(v R_V) R_V^T (OptR §3.2, Eq. (5)); its value
+    reconstruction error is below the 2-bit one, and so is the value part of
+    the output error (Eq. (8))."""
+    c = _tiny(B=2, Hq=8, Hkv=2, seq_lens=[50, 33], table_policy="permuted")
+    pools = {}
+    for vb in (2, 3):
+        pool = np.zeros(O.pool_bytes(c.num_pages, c.Hkv, key_bits=3, val_bits=vb), np.uint8)
+        O.append_tokens(pool, c.Hkv, c.slots, c.k, c.v, c.mu, c.r_k, c.r_v, key_bits=3, val_bits=vb)
+        pools[vb] = pool
+    got = O.decode_attention(c.q, pools[3], c.Hkv, c.page_table, c.seq_lens, c.r_k, c.r_v, key_bits=3,
+                             val_bits=3)
+    x, w = O.rotated_inputs(c.k, c.v, c.mu, c.r_k, c.r_v)
+    kq = O.int2_dequantize(*O.int2_quantize(x, bits=3))
+    vq = O.int2_dequantize(*O.int2_quantize(w, bits=3))
+    for b in range(c.B):
+        sel = c.tok_seq == b
+        for j in range(c.Hq):
+            h = j // 4
+            k_eff = kq[sel, h] @ c.r_k[h].astype(np.float64).T + c.mu[h]
+            v_eff = vq[sel, h] @ c.r_v[h].astype(np.float64).T
+            ref = O.softmax_attention(c.q[b, j], k_eff, v_eff, 1 / np.sqrt(128))
+            np.testing.assert_allclose(got[b, j], ref, rtol=0, atol=1e-11)
+    assert np.abs(vq - w).mean() < 0.6 * np.abs(O.int2_dequantize(*O.int2_quantize(w)) - w).mean()
+    rng = np.random.default_rng(47)
+    w_o = rng.standard_normal((64, c.Hq * 128)) / np.sqrt(c.Hq * 128)
+    k_seqs = [c.k[c.tok_seq == b] for b in range(c.B)]
+    v_seqs = [c.v[c.tok_seq == b] for b in range(c.B)]
+    dv = {vb: O.output_error(c.q, pools[vb], c.Hkv, c.page_table, c.seq_lens, k_seqs, v_seqs, c.mu, c.r_k,
+                             c.r_v, w_o, key_bits=3, val_bits=vb)[1] for vb in (2, 3)}
+    assert np.linalg.norm(dv[3]) < 0.6 * np.linalg.norm(dv[2])
