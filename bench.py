@@ -136,7 +136,7 @@ def read_ceiling_gbps(torch, dev, n_bytes: int = 2 << 30) -> float:
     return best
 
 
-def cpu_baseline(case, pool_np, kv_heads_sample: int, window=None, key_bits: int = 2):
+def cpu_baseline(case, pool_np, kv_heads_sample: int, window=None, key_bits: int = 2, val_bits: int = 2):
     """Time the oracle (as it stands) on KV heads [0, kv_heads_sample) of the step:
     the append of the newest token and the decode of their query heads (with the
     exact window (sinks, recent) when given), then scale to the whole step.  BLAS
@@ -155,15 +155,16 @@ def cpu_baseline(case, pool_np, kv_heads_sample: int, window=None, key_bits: int
         t0 = time.perf_counter()
         pool = pool_np.copy()
         x, w = O.rotated_inputs(case.k[last], case.v[last], case.mu, r_k, r_v)
-        O.quantize_append(pool, case.Hkv, case.slots[last], x, w, key_bits=key_bits)
+        O.quantize_append(pool, case.Hkv, case.slots[last], x, w, key_bits=key_bits, val_bits=val_bits)
         if window:
             k_seqs = [case.k[case.tok_seq == b] for b in range(case.B)]
             v_seqs = [case.v[case.tok_seq == b] for b in range(case.B)]
             O.decode_attention_window(case.q, pool, case.Hkv, case.page_table, case.seq_lens, case.mu, r_k, r_v,
-                                      k_seqs, v_seqs, window[0], window[1], heads=heads, key_bits=key_bits)
+                                      k_seqs, v_seqs, window[0], window[1], heads=heads, key_bits=key_bits,
+                                      val_bits=val_bits)
         else:
             O.decode_attention(case.q, pool, case.Hkv, case.page_table, case.seq_lens, r_k, r_v, heads=heads,
-                               key_bits=key_bits)
+                               key_bits=key_bits, val_bits=val_bits)
         dt = time.perf_counter() - t0
     step_est = dt * case.Hkv / len(hs)
     tokens = float(case.seq_lens.sum())
@@ -280,7 +281,9 @@ def main() -> int:
     ap.add_argument("--cpu-kv-heads", type=int, default=8, help="KV heads in the oracle's timed sample (0 = skip)")
     ap.add_argument("--window", default="", help="exact bf16 window 'sinks,recent' (e.g. 4,128); default none")
     ap.add_argument("--key-bits", type=int, default=2, choices=[2, 3, 4],
-                    help="bits per key code: 2, or 3 / 4 (K3V2 / K4V2: 2048-byte blocks); values keep 2")
+                    help="bits per key code: 2, or 3 / 4 (K3V2 / K4V2: a 512-byte high-bit plane per block)")
+    ap.add_argument("--val-bits", type=int, default=2, choices=[2, 3, 4],
+                    help="bits per value code: 2, or 3 / 4 (with 3-bit keys, K3V3: another 512-byte plane)")
     ap.add_argument("--evaluator", action="store_true",
                     help="time the output-error evaluator (kvq_output_error) instead of the decode step")
     ap.add_argument("--rotation", default="dense", choices=["dense", "hadamard"],
@@ -320,10 +323,11 @@ def main() -> int:
     def B16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
-    # per token and KV head: K and V codes, K and V (scale, zero); 4-bit keys add 32 B of key bits
-    bpt = BYTES_PER_TOKEN_HEAD + (32 if args.key_bits > 2 else 0)
+    # per token and KV head: K and V codes, K and V (scale, zero); each 3- or 4-bit tensor adds
+    # the 32 B of its high-bit plane
+    bpt = BYTES_PER_TOKEN_HEAD + (32 if args.key_bits > 2 else 0) + (32 if args.val_bits > 2 else 0)
     cache_bytes = int(case.seq_lens.sum()) * case.Hkv * bpt
-    pool_bytes = case.num_pages * case.Hkv * (2048 if args.key_bits > 2 else 1536)
+    pool_bytes = case.num_pages * case.Hkv * PAGE * bpt
     n_rep = args.replicas or max(2, -(-2 * MALL_BYTES // pool_bytes) + 1)
 
     # ---- replica 0: bulk quantize-append of the whole context
@@ -333,7 +337,8 @@ def main() -> int:
     pools, caches, rks, rvs, mus = [], [], [], [], []
     for r in range(n_rep):
         pools.append(torch.zeros(pool_bytes, dtype=torch.uint8, device=dev))
-        caches.append(kvq.make_cache(case.Hkv, case.num_pages, pools[-1], rotation=rot_kind, key_bits=args.key_bits))
+        caches.append(kvq.make_cache(case.Hkv, case.num_pages, pools[-1], rotation=rot_kind, key_bits=args.key_bits,
+                                     val_bits=args.val_bits))
         rks.append(T(case.r_k))
         rvs.append(T(case.r_v))
         mus.append(T(case.mu))
@@ -461,14 +466,15 @@ def main() -> int:
     achieved = alg_bytes / (split_avg_ms * 1e-3) / 1e9
     # the committed counter summaries are per workload, without a window and with a dense R
     variant = (("" if args.rotation == "dense" else "_" + args.rotation) + (f"_window{sinks}_{recent}" if n_win_tok else "")
-               + (f"_k{args.key_bits}" if args.key_bits > 2 else ""))
+               + (f"_k{args.key_bits}" if args.key_bits > 2 else "") + (f"_v{args.val_bits}" if args.val_bits > 2 else ""))
     traffic = counters_for(kernel_source_sha(), args.workload + variant)
 
     cpu = None
     if args.cpu_kv_heads > 0:
         log("[bench] timing the oracle on the CPU ...")
         cpu = cpu_baseline(case, pools[0].cpu().numpy(), args.cpu_kv_heads,
-                           window=(sinks, recent) if (sinks or recent) else None, key_bits=args.key_bits)
+                           window=(sinks, recent) if (sinks or recent) else None, key_bits=args.key_bits,
+                           val_bits=args.val_bits)
 
     res = {
         "metric": "INT2 decode attention KV-tokens/s + HBM GB/s (% peak), 8B GQA shape @128K",
@@ -493,6 +499,7 @@ def main() -> int:
             "exact_window": {"sinks": sinks, "recent": recent} if (sinks or recent) else None,
             "rotation": args.rotation,
             "key_bits": args.key_bits,
+            "val_bits": args.val_bits,
         },
         "hbm_gbps_step": cache_bytes / (ms_per_step * 1e-3) / 1e9,
         "pct_peak_step": cache_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,

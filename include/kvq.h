@@ -38,6 +38,10 @@
  *                s = 4a + i, at +4i the K (fp16 scale, fp16 zero) pair of
  *                channel group grp, at +16+4i the V pair.
  * A slot index is page*16 + offset.  96 bytes per token per KV head.
+ * Caches with 3- or 4-bit keys or values (kvq_cache.key_bits, val_bits)
+ * append a 512-byte high-bit plane per widened tensor to every block, so the
+ * block is 1536, 2048 or 2560 bytes and block (p, h) starts at
+ * (p*num_kv_heads + h) * block bytes.
  *
  * Conventions for every call.
  *   - Pointers marked "device" are HIP device (or managed) memory; "host" are
@@ -103,11 +107,19 @@ typedef struct {
   float clip_ratio;     /* Q2's clip ratio c in (0, 1]; 0 selects 1 (no clip)  */
   int32_t rotation;     /* kvq_rotation: how r_k and r_v describe R           */
   int32_t key_bits;     /* bits per key code: 2 (or 0, the default), 3 (K3V2)
-                           or 4 (K4V2); values keep 2 bits.  With 3 or 4 a block
-                           is 2048 bytes: the 1536-byte layout holds each key
-                           code's low two bits and bytes [1536, 2048) the rest
-                           (record r = 16 a + s at 1536 + 8 r, words H0, H1 at
-                           the bits of K0, K1; one bit used for 3-bit keys)   */
+                           or 4 (K4V2).  With 3 or 4 the 1536-byte layout holds
+                           each key code's low two bits and a 512-byte plane
+                           at byte 1536 the rest (record r = 16 a + s at
+                           1536 + 8 r, words H0, H1 at the bits of K0, K1; one
+                           bit used for 3-bit keys)                           */
+  int32_t val_bits;     /* bits per value code: 2 (or 0, the default), 3 (K3V3
+                           with 3-bit keys) or 4.  With 3 or 4 another 512-byte
+                           plane follows (at byte 1536, or 2048 after a key
+                           plane): record r = 16 a + b at P + 8 r, words VH0,
+                           VH1 at the bits of V0, V1 hold each value code's
+                           high bits.  A block is 1536 bytes plus 512 per
+                           plane: 1536 (K2V2), 2048 (K3V2, K4V2, K2V4) or
+                           2560 (K3V3, K4V4)                                 */
 } kvq_cache;
 
 /*
@@ -141,7 +153,8 @@ typedef struct {
   const float* mu;
 } kvq_window;
 
-/* Bytes of the pool: num_pages * num_kv_heads * 1536.  0 if `cache` is NULL
+/* Bytes of the pool: num_pages * num_kv_heads * block bytes (1536, plus 512
+ * for 3- or 4-bit keys and 512 for 3- or 4-bit values).  0 if `cache` is NULL
  * or has non-positive sizes. */
 size_t kvq_pool_bytes(const kvq_cache* cache);
 

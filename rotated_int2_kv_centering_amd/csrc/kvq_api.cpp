@@ -37,7 +37,7 @@ constexpr int kHeadDim = 128;
 constexpr int kGroupMetadata = 32;  // the block keeps one (scale, zero) pair per 32 channels
 constexpr int kPage = 16;
 constexpr size_t kBlockBytes = 1536;
-constexpr size_t kBlockBytesK4 = 2048;  // 4-bit keys
+constexpr size_t kPlaneBytes = 512;  // high-bit plane of 3- or 4-bit key or value codes
 constexpr int kRowStride = 132;  // floats per split partial (acc[128], max, sum, pad)
 constexpr int kMaxGroup = 16;
 constexpr int kMinPagesPerSplit = 8;
@@ -60,6 +60,8 @@ kvq_status check_cache(const kvq_cache* c) {
   if (reinterpret_cast<uintptr_t>(c->pool) % 16 != 0) return fail(KVQ_EINVAL, "cache pool must be 16-byte aligned");
   if (c->key_bits != 0 && c->key_bits != 2 && c->key_bits != 3 && c->key_bits != 4)
     return fail(KVQ_EUNSUPPORTED, "key_bits=%d must be 2, 3 or 4 (0 selects 2)", c->key_bits);
+  if (c->val_bits != 0 && c->val_bits != 2 && c->val_bits != 3 && c->val_bits != 4)
+    return fail(KVQ_EUNSUPPORTED, "val_bits=%d must be 2, 3 or 4 (0 selects 2)", c->val_bits);
   if (c->rotation != KVQ_ROT_DENSE && c->rotation != KVQ_ROT_HADAMARD)
     return fail(KVQ_EINVAL, "rotation=%d must be KVQ_ROT_DENSE or KVQ_ROT_HADAMARD", c->rotation);
   if (!(c->clip_ratio >= 0.0f && c->clip_ratio <= 1.0f))
@@ -69,6 +71,13 @@ kvq_status check_cache(const kvq_cache* c) {
 
 // Q2's clip ratio of a cache (0 selects 1).
 float clip_of(const kvq_cache* c) { return c->clip_ratio == 0.0f ? 1.0f : c->clip_ratio; }
+// Bits per key and per value code (0 selects 2).
+int kbits_of(const kvq_cache* c) { return c->key_bits > 2 ? c->key_bits : 2; }
+int vbits_of(const kvq_cache* c) { return c->val_bits > 2 ? c->val_bits : 2; }
+// Bytes of one (page, KV head) block: one high-bit plane per tensor wider than 2 bits.
+size_t block_bytes_of(const kvq_cache* c) {
+  return kBlockBytes + (kbits_of(c) > 2 ? kPlaneBytes : 0) + (vbits_of(c) > 2 ? kPlaneBytes : 0);
+}
 
 // Compute units of the current device, cached per device id (256 when no
 // device can be queried, e.g. on a host without a GPU).
@@ -291,7 +300,8 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
   a.kv_kind = kv_dtype == KVQ_BF16 ? 0 : 1;
   a.clip = clip_of(cache);
   a.gsize = cache->group_size;
-  a.kbits = cache->key_bits > 2 ? cache->key_bits : 2;
+  a.kbits = kbits_of(cache);
+  a.vbits = vbits_of(cache);
   a.rot_kind = cache->rotation;
   a.mu = mu;
   hipError_t e = kvq::launch_decode(a, static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_begin),
@@ -337,8 +347,7 @@ extern "C" {
 
 size_t kvq_pool_bytes(const kvq_cache* cache) {
   if (cache == nullptr || cache->num_kv_heads <= 0 || cache->num_pages <= 0) return 0;
-  return static_cast<size_t>(cache->num_pages) * static_cast<size_t>(cache->num_kv_heads) *
-         (cache->key_bits > 2 ? kBlockBytesK4 : kBlockBytes);
+  return static_cast<size_t>(cache->num_pages) * static_cast<size_t>(cache->num_kv_heads) * block_bytes_of(cache);
 }
 
 kvq_status kvq_quant_append(const kvq_cache* cache, const void* k, const void* v, kvq_dtype in_dtype,
@@ -363,7 +372,7 @@ kvq_status kvq_quant_append_err(const kvq_cache* cache, const void* k, const voi
   const int kind = in_dtype == KVQ_BF16 ? 0 : (in_dtype == KVQ_F32 ? 1 : 2);
   hipError_t e = kvq::launch_append(static_cast<uint8_t*>(cache->pool), cache->num_pages, cache->num_kv_heads, k, v,
                                     kind, n_tokens, slots, mu, r_k, r_v, rot_out, clip_of(cache), cache->rotation,
-                                    cache->group_size, sq_err, cache->key_bits > 2 ? cache->key_bits : 2,
+                                    cache->group_size, sq_err, kbits_of(cache), vbits_of(cache),
                                     static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "quant_append launch");
   return KVQ_OK;
@@ -483,7 +492,8 @@ kvq_status kvq_output_error(const kvq_cache* cache, const void* q, kvq_dtype q_d
   a.r_k = r_k;
   a.r_v = r_v;
   a.rot_kind = cache->rotation;
-  a.kbits = cache->key_bits > 2 ? cache->key_bits : 2;
+  a.kbits = kbits_of(cache);
+  a.vbits = vbits_of(cache);
   a.sm_scale = sm_scale == 0.0f ? 1.0f / std::sqrt(static_cast<float>(kHeadDim)) : sm_scale;
   a.n_splits = plan.n_splits;
   a.pages_per_split = plan.pages_per_split;

@@ -33,7 +33,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     uint8_t* __restrict__ pool, int num_pages, int num_kv_heads, const void* __restrict__ k_in,
     const void* __restrict__ v_in, int n_tokens, const int32_t* __restrict__ slots, const float* __restrict__ mu,
     const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out, float clip,
-    int rot_kind, int gsize, float* __restrict__ sq_err, int kbits) {
+    int rot_kind, int gsize, float* __restrict__ sq_err, int kbits, int vbits) {
   const int tile = blockIdx.x;
   const int h = blockIdx.y;
   const int tensor = blockIdx.z;  // 0: key, 1: value
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     if (rot_out != nullptr) rot_out[((static_cast<size_t>(n) * num_kv_heads + h) * 2 + tensor) * kHeadDim + j] = xv;
 
     const int page = slot >> 4;
-    uint8_t* block = pool + (static_cast<size_t>(page) * num_kv_heads + h) * (kbits > 2 ? kBlockBytesK4 : kBlockBytes);
+    uint8_t* block = pool + (static_cast<size_t>(page) * num_kv_heads + h) * block_bytes(kbits, vbits);
     float2 r;
     if (gsize == 128) {
       const float2 a = s_rng[t][0], b = s_rng[t][1];
@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     } else {
       r = q2_wave_range(xv, gsize);
     }
-    const float lvl = q2_pack_channel(xv, j, tensor, block, slot & 15, clip, r.x, r.y, kbits);
+    const float lvl = q2_pack_channel(xv, j, tensor, block, slot & 15, clip, r.x, r.y, kbits, vbits);
     if (sq_err != nullptr) {  // squared error over this wave's 64 channels
       float e = (xv - lvl) * (xv - lvl);
 #pragma unroll
@@ -149,10 +149,11 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
     uint8_t* __restrict__ pool, int num_pages, int num_kv_heads, const void* __restrict__ k_in,
     const void* __restrict__ v_in, int n_tokens, const int32_t* __restrict__ slots, const float* __restrict__ mu,
     const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out, float clip, int gsize,
-    float* __restrict__ sq_err, int kbits) {
+    float* __restrict__ sq_err, int kbits, int vbits) {
   const int h = blockIdx.y;
-  const bool k4 = blockIdx.z == 0 && kbits > 2;  // this workgroup packs 3- or 4-bit keys
   const int tensor = blockIdx.z;  // 0: key, 1: value
+  const int bits = tensor == 0 ? kbits : vbits;
+  const bool wide = bits > 2;  // this workgroup packs 3- or 4-bit codes (high bits in the tensor's plane)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -301,7 +302,7 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
         x[4 * u + 3] = q4[3];
       }
       uint32_t pair, code[32];
-      q2_group32(x, clip, gsize, pair, code, k4 ? static_cast<float>((1 << kbits) - 1) : 3.0f);
+      q2_group32(x, clip, gsize, pair, code, static_cast<float>((1 << bits) - 1));
       const int slot = n < n_tokens ? slots[n] : -1;
       const bool ok = slot >= 0 && slot < num_pages * kPage;  // same for the token's four lanes
       if (sq_err != nullptr) {  // squared error of groups g and g ^ 1: channels [64 (g / 2), +64)
@@ -326,8 +327,8 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
       const int slot0 = __shfl(slot, 0);
       const bool full = __builtin_amdgcn_ballot_w64(!(ok && slot == slot0 + r && (slot0 & 15) == 0)) == 0;
       const int off = slot & 15;
-      uint8_t* block =  // the block stride follows the cache format (key bits), for the value tensor too
-          pool + (static_cast<size_t>(ok ? slot >> 4 : 0) * num_kv_heads + h) * (kbits > 2 ? kBlockBytesK4 : kBlockBytes);
+      uint8_t* block =  // the block stride follows the cache format (key and value bits)
+          pool + (static_cast<size_t>(ok ? slot >> 4 : 0) * num_kv_heads + h) * block_bytes(kbits, vbits);
       if (ok) {  // metadata pair of (token, group): record 4g + off/4
         *reinterpret_cast<uint32_t*>(block + kCodeBytes + kMetaRecordBytes * (4 * g + (off >> 2)) + 16 * tensor +
                                      4 * (off & 3)) = pair;
@@ -352,39 +353,46 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
   #pragma unroll
           for (int ak = 0; ak < 4; ++ak) {
             *reinterpret_cast<uint32_t*>(block + 16 * (16 * ak + off) + 4 * (g >> 1)) = kw[ak];
-            if (k4) *reinterpret_cast<uint32_t*>(block + kKHiPlane + 8 * (16 * ak + off) + 4 * (g >> 1)) = khw[ak];
+            if (wide) *reinterpret_cast<uint32_t*>(block + kKHiPlane + 8 * (16 * ak + off) + 4 * (g >> 1)) = khw[ak];
           }
         }
       } else {
         // V: channel 32g + 16tt + b -> record 16(off/4) + b, word V[(off%4)/2],
         // bit 2(2g + tt) + 16(off%2); the token's bits of word b after the group OR
+        // The high bits of wide values go to the same positions of the values'
+        // plane: record 16(off/4) + b at v_hi_plane + 8 record, word VH[(off%4)/2].
         const int hs = 16 * (off & 1);
-        uint32_t vw[16];
+  #pragma unroll 1
+        for (int part = 0; part < (wide ? 2 : 1); ++part) {
+          const int dn = 2 * part;  // part 0: bits 0-1 of each code, part 1: bits 2-3
+          uint32_t vw[16];
   #pragma unroll
-        for (int bb = 0; bb < 16; ++bb) {
-          uint32_t w = (code[bb] << (4 * g + hs)) | (code[16 + bb] << (4 * g + 2 + hs));
-          w |= __shfl_xor(w, 1);
-          w |= __shfl_xor(w, 2);
-          vw[bb] = w;
-        }
-        if (full) {  // pair the two slots of each word (tokens r and r ^ 1), plain stores
+          for (int bb = 0; bb < 16; ++bb) {
+            uint32_t w = (((code[bb] >> dn) & 3u) << (4 * g + hs)) | (((code[16 + bb] >> dn) & 3u) << (4 * g + 2 + hs));
+            w |= __shfl_xor(w, 1);
+            w |= __shfl_xor(w, 2);
+            vw[bb] = w;
+          }
+          auto word_at = [&](int bb) {
+            const int rec = 16 * (off >> 2) + bb;
+            return reinterpret_cast<uint32_t*>(block + (part == 0 ? 16 * rec + 8 : v_hi_plane(kbits) + 8 * rec) +
+                                               4 * ((off & 3) >> 1));
+          };
+          if (full) {  // pair the two slots of each word (tokens r and r ^ 1), plain stores
   #pragma unroll
-          for (int bb = 0; bb < 16; ++bb) vw[bb] |= __shfl_xor(vw[bb], 4);
-          if ((r & 1) == 0) {
+            for (int bb = 0; bb < 16; ++bb) vw[bb] |= __shfl_xor(vw[bb], 4);
+            if ((r & 1) == 0) {
+  #pragma unroll
+              for (int u = 0; u < 4; ++u) *word_at(4 * g + u) = vw[4 * g + u];
+            }
+          } else if (ok) {  // other slots of the page may be written concurrently: only this slot's half
+            const uint32_t mask = 0xffffu << hs;
   #pragma unroll
             for (int u = 0; u < 4; ++u) {
-              const int bb = 4 * g + u;
-              *reinterpret_cast<uint32_t*>(block + 16 * (16 * (off >> 2) + bb) + 8 + 4 * ((off & 3) >> 1)) = vw[bb];
+              uint32_t* word = word_at(4 * g + u);
+              atomicAnd(word, ~mask);
+              atomicOr(word, vw[4 * g + u]);
             }
-          }
-        } else if (ok) {  // other slots of the page may be written concurrently: only this slot's half
-          const uint32_t mask = 0xffffu << hs;
-  #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int bb = 4 * g + u;
-            uint32_t* word = reinterpret_cast<uint32_t*>(block + 16 * (16 * (off >> 2) + bb) + 8 + 4 * ((off & 3) >> 1));
-            atomicAnd(word, ~mask);
-            atomicOr(word, vw[bb]);
           }
         }
       }
@@ -396,7 +404,7 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
 
 hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const void* k, const void* v, int in_kind,
                          int n_tokens, const int32_t* slots, const float* mu, const float* r_k, const float* r_v,
-                         float* rot_out, float clip, int rot_kind, int gsize, float* sq_err, int kbits,
+                         float* rot_out, float clip, int rot_kind, int gsize, float* sq_err, int kbits, int vbits,
                          hipStream_t stream) {
   (void)hipGetLastError();  // report only this call's launch errors, not stale ones
   if (in_kind != 2 && n_tokens >= kBulkMin) {
@@ -408,7 +416,7 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
     auto kern = in_kind == 0 ? (rot_kind == 0 ? append_bulk_kernel<0, 0> : append_bulk_kernel<0, 1>)
                              : (rot_kind == 0 ? append_bulk_kernel<1, 0> : append_bulk_kernel<1, 1>);
     hipLaunchKernelGGL(kern, bgrid, dim3(kBulkThreads), 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens, slots,
-                       mu, r_k, r_v, rot_out, clip, gsize, sq_err, kbits);
+                       mu, r_k, r_v, rot_out, clip, gsize, sq_err, kbits, vbits);
     return hipGetLastError();
   }
   const dim3 grid((n_tokens + kAppendTile - 1) / kAppendTile, num_kv_heads, 2);
@@ -416,15 +424,15 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
   switch (in_kind) {
     case 0:
       hipLaunchKernelGGL(append_kernel<0>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,
-                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize, sq_err, kbits);
+                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize, sq_err, kbits, vbits);
       break;
     case 1:
       hipLaunchKernelGGL(append_kernel<1>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,
-                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize, sq_err, kbits);
+                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize, sq_err, kbits, vbits);
       break;
     default:
       hipLaunchKernelGGL(append_kernel<2>, grid, block, 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens,
-                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize, sq_err, kbits);
+                         slots, mu, r_k, r_v, rot_out, clip, rot_kind, gsize, sq_err, kbits, vbits);
       break;
   }
   return hipGetLastError();

@@ -57,18 +57,21 @@ constexpr float kNegBig = -3.0e38f;  // finite "minus infinity" for running maxi
 constexpr float kTwo24 = 16777216.0f;
 constexpr float kLazy = 8.0f;  // rescale threshold of the online softmax (log2 units)
 // DMA instructions per page pair: K/V codes of page 0, of page 1; metadata of
-// page 0, of page 1; with 4-bit keys also the high-bit planes of pages 0 and 1.
-template <bool kK4> struct PairDma { static constexpr int n = kK4 ? 6 : 4; };
+// page 0, of page 1; with 3- or 4-bit keys (values) also the keys' (values')
+// high-bit planes of pages 0 and 1.
+template <bool kKW, bool kVW> struct PairDma { static constexpr int n = 4 + 2 * kKW + 2 * kVW; };
 
-// Launch shape by the number of head quads: waves per workgroup, waves per
-// SIMD, and the per-wave ring depth (page pairs staged in LDS by direct
-// global->LDS loads; depth - 1 pairs are in flight while one is computed).
-// The g <= 4 kernel fits 3 waves per SIMD, so one 12-wave workgroup fills a
-// compute unit; g <= 8 fits 2 (256 registers); the largest runs 1 wave per
-// SIMD and keeps more pairs in flight per wave instead.
-template <int kNQ> struct DecodeShape { static constexpr int waves = 4, waves_per_simd = 1, depth = 8, depth_k4 = 6; };
-template <> struct DecodeShape<1> { static constexpr int waves = 12, waves_per_simd = 3, depth = 3, depth_k4 = 3; };
-template <> struct DecodeShape<2> { static constexpr int waves = 8, waves_per_simd = 2, depth = 4, depth_k4 = 4; };
+// Launch shape by the number of head quads and of ring parts per page pair (3
+// for 2-bit codes, one more per high-bit plane): waves per workgroup (a
+// quarter of them per SIMD) and the per-wave ring depth (page pairs staged in
+// LDS by direct global->LDS loads; depth - 1 pairs are in flight while one is
+// computed).  The g <= 4 kernel fits 3 waves per SIMD, so one 12-wave
+// workgroup fills a compute unit, while its ring fits the LDS (up to one
+// plane); g <= 8 fits 2 (256 registers); the largest runs 1 wave per SIMD and
+// keeps more pairs in flight per wave instead.
+template <int kNQ, int kParts> struct DecodeShape { static constexpr int waves = 4, depth = kParts == 3 ? 8 : 6; };
+template <int kParts> struct DecodeShape<1, kParts> { static constexpr int waves = kParts <= 4 ? 12 : 8, depth = 3; };
+template <int kParts> struct DecodeShape<2, kParts> { static constexpr int waves = 8, depth = kParts <= 4 ? 4 : 3; };
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -217,13 +220,17 @@ __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// quads of query heads (g <= 4 * kNQ), waves per workgroup, ring depth, 4-bit keys
-template <int kNQ, int kW, int kDepth, bool kK4>
-__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(DecodeShape<kNQ>::waves_per_simd)))
+// quads of query heads (g <= 4 * kNQ), waves per workgroup, ring depth, 3- or
+// 4-bit keys, 3- or 4-bit values
+template <int kNQ, int kW, int kDepth, bool kKW, bool kVW>
+__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kW / 4)))
 void decode_kernel(const DecodeParams p) {
-  constexpr int kDmaPerPair = PairDma<kK4>::n;
-  constexpr int kRingParts = kK4 ? 4 : 3;  // codes of page 0, of page 1, metadata, (4-bit keys) high planes
-  constexpr int kBlk = kK4 ? kBlockBytesK4 : kBlockBytes;
+  constexpr int kDmaPerPair = PairDma<kKW, kVW>::n;
+  // ring parts: codes of page 0, of page 1, metadata, then the keys' and the values' high-bit planes
+  constexpr int kRingParts = 3 + kKW + kVW;
+  constexpr int kKPart = 3, kVPart = 3 + kKW;
+  constexpr int kBlk = block_bytes(kKW ? 4 : 2, kVW ? 4 : 2);
+  constexpr int kVPlane = v_hi_plane(kKW ? 4 : 2);
   static_assert(kDepth >= 2 && kDmaPerPair * (kDepth - 1) <= 63, "ring depth within the vmcnt range");
   constexpr int kNH = 4 * kNQ;
   constexpr int kThreads = 64 * kW;
@@ -245,7 +252,8 @@ void decode_kernel(const DecodeParams p) {
   __shared__ float2 s_nrng[4];  // G = 128: the new token's range per wave
   __shared__ float s_nlog[kNH];
   // Page-pair ring [slot][wave][part][lane]: part 0/1 = 64 x 16 B codes of
-  // page 0/1, part 2 = 32 x 16 B metadata of page 0 then of page 1.
+  // page 0/1, part 2 = 32 x 16 B metadata of page 0 then of page 1; parts 3
+  // and on: the high-bit planes of page 0 then of page 1 (keys', values').
   __shared__ uint4v s_ring[kDepth][kW][kRingParts][64];
   // Prologue scratch (q_hat partials [kParts][kNH][128], then the new token's
   // partials [2][4][128]) lives in the last ring slot, which no load targets
@@ -466,11 +474,17 @@ void decode_kernel(const DecodeParams p) {
       dma16(blk0, kCodeBytes + 16 * lane, &r[2][0]);
     else
       dma16(blk1, kCodeBytes - 512 + 16 * lane, &r[2][0]);
-    if (kK4) {  // the keys' high-bit planes, page 0 then page 1 (512 B each)
+    if (kKW) {  // the keys' high-bit planes, page 0 then page 1 (512 B each)
       if (lane < 32)
-        dma16(blk0, kKHiPlane + 16 * lane, &r[kRingParts - 1][0]);
+        dma16(blk0, kKHiPlane + 16 * lane, &r[kKPart][0]);
       else
-        dma16(blk1, kKHiPlane - 512 + 16 * lane, &r[kRingParts - 1][0]);
+        dma16(blk1, kKHiPlane - 512 + 16 * lane, &r[kKPart][0]);
+    }
+    if (kVW) {  // the values' high-bit planes
+      if (lane < 32)
+        dma16(blk0, kVPlane + 16 * lane, &r[kVPart][0]);
+      else
+        dma16(blk1, kVPlane - 512 + 16 * lane, &r[kVPart][0]);
     }
   };
 
@@ -551,7 +565,7 @@ void decode_kernel(const DecodeParams p) {
       const int pos = T - 1;
       uint8_t* blk = p.pool + (static_cast<size_t>(s_pages[np - 1]) * H + h) * kBlk;
       s_hat[tensor][rc] =
-          q2_pack_channel(s_nrow[tensor][rc], rc, tensor, blk, pos & (kPage - 1), p.clip, rg.x, rg.y, p.kbits);
+          q2_pack_channel(s_nrow[tensor][rc], rc, tensor, blk, pos & (kPage - 1), p.clip, rg.x, rg.y, p.kbits, p.vbits);
     }
   }
   for (int jh = wave; jh < kNH; jh += kW) {
@@ -629,13 +643,21 @@ void decode_kernel(const DecodeParams p) {
     P.vm0 = *reinterpret_cast<const uint4v*>(meta + meta_off + 16);
     P.km1 = *reinterpret_cast<const uint4v*>(meta + 512 + meta_off);
     P.vm1 = *reinterpret_cast<const uint4v*>(meta + 512 + meta_off + 16);
-    uint32_t kh[2][2] = {{0u, 0u}, {0u, 0u}};  // 4-bit keys: high-plane words H0, H1 of record `lane`, per page
-    if (kK4) {
-      const uint32_t* hp = reinterpret_cast<const uint32_t*>(&r[kRingParts - 1][0]);
+    // wide codes: the plane words (H0, H1 or VH0, VH1) of record `lane`, per page
+    uint32_t kh[2][2] = {{0u, 0u}, {0u, 0u}}, vh[2][2] = {{0u, 0u}, {0u, 0u}};
+    if (kKW) {
+      const uint32_t* hp = reinterpret_cast<const uint32_t*>(&r[kKPart][0]);
       kh[0][0] = hp[2 * lane];
       kh[0][1] = hp[2 * lane + 1];
       kh[1][0] = hp[128 + 2 * lane];
       kh[1][1] = hp[128 + 2 * lane + 1];
+    }
+    if (kVW) {
+      const uint32_t* hp = reinterpret_cast<const uint32_t*>(&r[kVPart][0]);
+      vh[0][0] = hp[2 * lane];
+      vh[0][1] = hp[2 * lane + 1];
+      vh[1][0] = hp[128 + 2 * lane];
+      vh[1][1] = hp[128 + 2 * lane + 1];
     }
     const int i0 = 2 * pair;
     // page ids and the pair's validity are wave-uniform (scalar registers)
@@ -654,27 +676,21 @@ void decode_kernel(const DecodeParams p) {
       // Key operands: a code at bits 2q (+16) of a word is the fp16 subnormal
       // code * 4^q * 2^-24, so one AND per register; groups 1 and 3 sit in the
       // upper byte of each half and are shifted down first.  The factor 4^q is
-      // divided out of the query operand.
+      // divided out of the query operand.  A wide key's high bits, moved two
+      // bits up, fill bits 2q + 2 and 2q + 3: low | high is the whole code times
+      // 4^q (at most 15 * 64 < 2^10, still a subnormal), one AND-OR more.
       const uint32_t kw[4] = {rec[0], rec[0] >> 8, rec[1], rec[1] >> 8};
+      const uint32_t kw2[4] = {kh[X][0] << 2, (kh[X][0] >> 8) << 2, kh[X][1] << 2, (kh[X][1] >> 8) << 2};
       half8 kA[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         uint4v rr;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) rr[q] = kw[kk] & (0x00030003u << (2 * q));
-        kA[kk] = __builtin_bit_cast(half8, rr);
-      }
-      // 4-bit keys: the high two bits, same extraction; code = low + 4 high
-      half8 kAh[4];
-      if (kK4) {
-        const uint32_t hw[4] = {kh[X][0], kh[X][0] >> 8, kh[X][1], kh[X][1] >> 8};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          uint4v rr;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) rr[q] = hw[kk] & (0x00030003u << (2 * q));
-          kAh[kk] = __builtin_bit_cast(half8, rr);
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t m = 0x00030003u << (2 * q);
+          rr[q] = kKW ? ((kw[kk] & m) | (kw2[kk] & (m << 2))) : (kw[kk] & m);
         }
+        kA[kk] = __builtin_bit_cast(half8, rr);
       }
       const int pos0 = (p0 + i0 + X) * kPage + 4 * a;
       const bool page_ok = X == 0 ? ok0 : has1;
@@ -685,16 +701,6 @@ void decode_kernel(const DecodeParams p) {
         for (int kk = 0; kk < 4; ++kk) {
           C = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[kk], qhi[Q][kk], C, 0, 0, 0);
           C = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[kk], qlo[Q][kk], C, 0, 0, 0);
-        }
-        if (kK4) {
-          float4v Ch = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            Ch = __builtin_amdgcn_mfma_f32_16x16x32_f16(kAh[kk], qhi[Q][kk], Ch, 0, 0, 0);
-            Ch = __builtin_amdgcn_mfma_f32_16x16x32_f16(kAh[kk], qlo[Q][kk], Ch, 0, 0, 0);
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) C[i] = fmaf(4.0f, Ch[i], C[i]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -713,18 +719,19 @@ void decode_kernel(const DecodeParams p) {
     // Value operands: tile t holds channels 16t..16t+15.  Tiles 0-3 sit in the
     // low byte of each half (bits 2t), tiles 4-7 in the high byte; a register
     // of tile t holds the codes times 4^(t%4) (divided out of acc at the end).
+    // Wide values: the plane's bits two up, OR-ed in as for the keys.
     const uint32_t vw[8] = {P.rec0[2], P.rec0[3], P.rec1[2], P.rec1[3],
                             P.rec0[2] >> 8, P.rec0[3] >> 8, P.rec1[2] >> 8, P.rec1[3] >> 8};
+    const uint32_t vw2[8] = {vh[0][0] << 2, vh[0][1] << 2, vh[1][0] << 2, vh[1][1] << 2,
+                             (vh[0][0] >> 8) << 2, (vh[0][1] >> 8) << 2, (vh[1][0] >> 8) << 2, (vh[1][1] >> 8) << 2};
     half8 vB[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const uint32_t m = 0x00030003u << (2 * (t & 3));
       const int hb = 4 * (t >> 2);
       uint4v rr;
-      rr[0] = vw[hb + 0] & m;
-      rr[1] = vw[hb + 1] & m;
-      rr[2] = vw[hb + 2] & m;
-      rr[3] = vw[hb + 3] & m;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rr[i] = kVW ? ((vw[hb + i] & m) | (vw2[hb + i] & (m << 2))) : (vw[hb + i] & m);
       vB[t] = __builtin_bit_cast(half8, rr);
     }
 
@@ -1234,28 +1241,38 @@ void decode_kernel(const DecodeParams p) {
 // ----------------------------------------------------------------- launcher
 // hipExtLaunchKernel stamps the events with the dispatch's own start and end
 // times, so an event pair measures the kernel alone.
-template <int kNQ, bool kK4>
+template <int kNQ, bool kKW, bool kVW>
 static hipError_t launch_one(const DecodeParams& prm, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
-  constexpr int kW = DecodeShape<kNQ>::waves;
-  constexpr int kD = kK4 ? DecodeShape<kNQ>::depth_k4 : DecodeShape<kNQ>::depth;
+  constexpr int kW = DecodeShape<kNQ, 3 + kKW + kVW>::waves;
+  constexpr int kD = DecodeShape<kNQ, 3 + kKW + kVW>::depth;
   DecodeParams arg = prm;
   void* args[] = {&arg};
-  return hipExtLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<kNQ, kW, kD, kK4>),
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<kNQ, kW, kD, kKW, kVW>),
                             dim3((prm.balanced ? 1 : prm.batch) * prm.num_kv_heads * prm.n_splits), dim3(64 * kW),
                             args, 0, stream,
                             ev_begin, ev_end, 0);
 }
 
+// 3- and 4-bit codes of a tensor share one kernel (the plane's unused bit is 0)
+template <int kNQ>
+static hipError_t launch_bits(const DecodeParams& prm, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
+  const bool kw = prm.kbits > 2, vw = prm.vbits > 2;
+  if (kw)
+    return vw ? launch_one<kNQ, true, true>(prm, stream, ev_begin, ev_end)
+              : launch_one<kNQ, true, false>(prm, stream, ev_begin, ev_end);
+  return vw ? launch_one<kNQ, false, true>(prm, stream, ev_begin, ev_end)
+            : launch_one<kNQ, false, false>(prm, stream, ev_begin, ev_end);
+}
+
 hipError_t launch_decode(const DecodeParams& prm, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
   (void)hipGetLastError();  // report only this call's launch errors, not stale ones
   hipError_t err;
-  const bool k4 = prm.kbits > 2;  // 3- and 4-bit keys share the wide-key block and kernel
   if (prm.g <= 4)
-    err = k4 ? launch_one<1, true>(prm, stream, ev_begin, ev_end) : launch_one<1, false>(prm, stream, ev_begin, ev_end);
+    err = launch_bits<1>(prm, stream, ev_begin, ev_end);
   else if (prm.g <= 8)
-    err = k4 ? launch_one<2, true>(prm, stream, ev_begin, ev_end) : launch_one<2, false>(prm, stream, ev_begin, ev_end);
+    err = launch_bits<2>(prm, stream, ev_begin, ev_end);
   else
-    err = k4 ? launch_one<4, true>(prm, stream, ev_begin, ev_end) : launch_one<4, false>(prm, stream, ev_begin, ev_end);
+    err = launch_bits<4>(prm, stream, ev_begin, ev_end);
   if (err != hipSuccess) return err;
   return hipGetLastError();
 }

@@ -65,11 +65,11 @@ __device__ __forceinline__ void wave_sync() {
 template <bool kF32>
 struct PageRegs {
   static constexpr int kRowWords = kF32 ? 8 : 4;  // uint4 per lane for 16 rows of k (or v)
-  uint4v k[kRowWords], v[kRowWords], blk[2];
+  uint4v k[kRowWords], v[kRowWords], blk[3];  // the block as 16-byte chunks lane, 64 + lane, 128 + lane
   float err;  // this lane's token's squared error (lanes 0..15)
 };
 
-template <int kNH, bool kF32, bool kWide>  // kWide: 3- or 4-bit keys (2048-byte blocks)
+template <int kNH, bool kF32, int kPlanes>  // kPlanes: high-bit planes per block (3- or 4-bit keys, values)
 __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2))) void eval_attn_kernel(
     const EvalParams p) {
   const int tid = threadIdx.x;
@@ -101,9 +101,13 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   __shared__ float s_qh[kNH][kHeadDim];  // q R_K * c
   __shared__ float s_qs[kNH][4];         // per-32-channel sums of s_qh
   // per-wave page staging, reused by the merges
-  constexpr int kBlkWords = (kWide ? kBlockBytesK4 : kBlockBytes) / 4;
+  constexpr int kBlk = kBlockBytes + kPlaneBytes * kPlanes;
+  constexpr int kBlkWords = kBlk / 4;
+  constexpr int kBlkChunks = kBlk / 16;
   constexpr int kStage = 2 * kPage * kRowPad + kBlkWords + 2 * kNH * kPage + 2 * kNH;
-  constexpr bool wide = kWide;  // the high-bit plane at byte 1536
+  const bool kwide = kPlanes > 0 && p.kbits > 2;     // the keys' high-bit plane at byte 1536
+  const bool vwide = kPlanes > 0 && p.vbits > 2;     // the values' plane after it
+  const int vpw = v_hi_plane(p.kbits) / 4;           // word index of the values' plane
   constexpr int kMergeW = kEvWaves * kNH * (3 * kHeadDim + 4) + kEvWaves;
   constexpr int kBuf = kEvWaves * kStage > kMergeW ? kEvWaves * kStage : kMergeW;
   __shared__ float s_buf[kBuf];
@@ -140,7 +144,7 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   float* const st = s_buf + wave * kStage;
   float* const s_k = st;                                   // [16][kRowPad]
   float* const s_v = st + kPage * kRowPad;                 // [16][kRowPad]
-  uint32_t* const s_blk = reinterpret_cast<uint32_t*>(st + 2 * kPage * kRowPad);  // 384 (512 with wide keys) words
+  uint32_t* const s_blk = reinterpret_cast<uint32_t*>(st + 2 * kPage * kRowPad);  // the block: 384, 512 or 640 words
   float* const s_p = st + 2 * kPage * kRowPad + kBlkWords;  // [2][kNH][16]
   float* const s_al = s_p + 2 * kNH * kPage;                      // [2][kNH]
 
@@ -170,9 +174,11 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   };
   auto load_page = [&](int pg, int id, PageRegs<kF32>& r) {
     const int nt = min(kPage, T - kPage * pg);
-    const uint8_t* blk = p.pool + (static_cast<size_t>(id) * H + h) * (wide ? kBlockBytesK4 : kBlockBytes);
-    r.blk[0] = *reinterpret_cast<const uint4v*>(blk + 16 * lane);
-    r.blk[1] = (lane < 32 || wide) ? *reinterpret_cast<const uint4v*>(blk + 16 * (64 + lane)) : uint4v{0u, 0u, 0u, 0u};
+    const uint8_t* blk = p.pool + (static_cast<size_t>(id) * H + h) * kBlk;
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+      r.blk[u] = 64 * u + lane < kBlkChunks ? *reinterpret_cast<const uint4v*>(blk + 16 * (64 * u + lane))
+                                            : uint4v{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < PageRegs<kF32>::kRowWords; ++u) {
       const int idx = u * 64 + lane;
@@ -200,8 +206,9 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
     }
   };
   auto stage_page = [&](const PageRegs<kF32>& r) {
-    reinterpret_cast<uint4v*>(s_blk)[lane] = r.blk[0];
-    if (lane < 32 || wide) reinterpret_cast<uint4v*>(s_blk)[64 + lane] = r.blk[1];
+#pragma unroll
+    for (int u = 0; u < 3; ++u)
+      if (64 * u + lane < kBlkChunks) reinterpret_cast<uint4v*>(s_blk)[64 * u + lane] = r.blk[u];
 #pragma unroll
     for (int u = 0; u < PageRegs<kF32>::kRowWords; ++u) {
       const int idx = u * 64 + lane;
@@ -274,8 +281,8 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
       for (int a = 0; a < 4; ++a) {
         const uint32_t w01[2] = {s_blk[4 * (16 * a + t_l)], s_blk[4 * (16 * a + t_l) + 1]};
         // wide keys: the high bits, record 16 a + t_l of the plane at word 384, words H0, H1
-        const uint32_t h01[2] = {wide ? s_blk[384 + 2 * (16 * a + t_l)] : 0u,
-                                 wide ? s_blk[384 + 2 * (16 * a + t_l) + 1] : 0u};
+        const uint32_t h01[2] = {kwide ? s_blk[384 + 2 * (16 * a + t_l)] : 0u,
+                                 kwide ? s_blk[384 + 2 * (16 * a + t_l) + 1] : 0u};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const uint32_t w = w01[kk >> 1], wh = h01[kk >> 1];
@@ -368,10 +375,16 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
         const int sh = 2 * tile + 16 * (t & 1);
         const uint32_t w0 = s_blk[4 * (16 * (t >> 2) + b0) + wsel];
         const uint32_t w1 = s_blk[4 * (16 * (t >> 2) + b0 + 1) + wsel];
+        uint32_t cv0 = (w0 >> sh) & 3u, cv1 = (w1 >> sh) & 3u;
+        if (vwide) {  // high bits: the same record and bit of the values' plane, word VH[(t % 4) / 2]
+          const int hsel = (t & 3) >> 1;
+          cv0 |= ((s_blk[vpw + 2 * (16 * (t >> 2) + b0) + hsel] >> sh) & 3u) << 2;
+          cv1 |= ((s_blk[vpw + 2 * (16 * (t >> 2) + b0 + 1) + hsel] >> sh) & 3u) << 2;
+        }
         const uint32_t pr = s_blk[(kCodeBytes + kMetaRecordBytes * (4 * grp + (t >> 2)) + 16) / 4 + (t & 3)];
         const float sv = f16_lo(pr), zv = f16_hi(pr);
-        const float wh0 = fmaf(sv, static_cast<float>((w0 >> sh) & 3u), zv);
-        const float wh1 = fmaf(sv, static_cast<float>((w1 >> sh) & 3u), zv);
+        const float wh0 = fmaf(sv, static_cast<float>(cv0), zv);
+        const float wh1 = fmaf(sv, static_cast<float>(cv1), zv);
         const float v0 = s_v[t * kRowPad + c0], v1 = s_v[t * kRowPad + c0 + 1];
 #pragma unroll
         for (int jj = 0; jj < kNH; ++jj) {
@@ -610,26 +623,28 @@ __global__ __launch_bounds__(kEvThreads) void eval_project_kernel(const EvalPara
   if (tid == 0) __hip_atomic_store(p.proj_counters + j, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int kNH, bool kWide>
+template <int kNH, int kPlanes>
 hipError_t launch_attn(const EvalParams& p, hipStream_t stream) {
   const dim3 grid(p.num_kv_heads * p.n_splits, p.batch, (p.g + kEvHeads - 1) / kEvHeads);
   if (p.kv_kind == 1)
-    hipLaunchKernelGGL((eval_attn_kernel<kNH, true, kWide>), grid, dim3(kEvThreads), 0, stream, p);
+    hipLaunchKernelGGL((eval_attn_kernel<kNH, true, kPlanes>), grid, dim3(kEvThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((eval_attn_kernel<kNH, false, kWide>), grid, dim3(kEvThreads), 0, stream, p);
+    hipLaunchKernelGGL((eval_attn_kernel<kNH, false, kPlanes>), grid, dim3(kEvThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-template <bool kWide>
+template <int kPlanes>
 hipError_t launch_attn_g(const EvalParams& p, hipStream_t stream) {
-  return p.g <= 4 ? launch_attn<4, kWide>(p, stream) : launch_attn<kEvHeads, kWide>(p, stream);
+  return p.g <= 4 ? launch_attn<4, kPlanes>(p, stream) : launch_attn<kEvHeads, kPlanes>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_eval(const EvalParams& p, hipStream_t stream) {
   (void)hipGetLastError();  // report only this call's launch errors
-  hipError_t e = p.kbits > 2 ? launch_attn_g<true>(p, stream) : launch_attn_g<false>(p, stream);
+  const int planes = (p.kbits > 2) + (p.vbits > 2);  // 3- and 4-bit codes of a tensor share one block layout
+  hipError_t e = planes == 0 ? launch_attn_g<0>(p, stream)
+                             : (planes == 1 ? launch_attn_g<1>(p, stream) : launch_attn_g<2>(p, stream));
   if (e != hipSuccess) return e;
   const dim3 pgrid(p.num_q_heads, p.n_chunks);
   if (p.w_kind == 1)

@@ -8,7 +8,7 @@ namespace kvq {
 
 hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const void* k, const void* v, int in_kind,
                          int n_tokens, const int32_t* slots, const float* mu, const float* r_k, const float* r_v,
-                         float* rot_out, float clip, int rot_kind, int gsize, float* sq_err, int kbits,
+                         float* rot_out, float clip, int rot_kind, int gsize, float* sq_err, int kbits, int vbits,
                          hipStream_t stream);
 
 // Split plan of one decode call.  Fixed plan (an explicit split count): every
@@ -76,7 +76,8 @@ struct DecodeParams {
   const float* mu;
   float clip;  // Q2's clip ratio for the appended token
   int gsize;   // Q2's group size G (32, 64 or 128) for the appended token
-  int kbits;   // bits per key code: 2, or 3 / 4 (2048-byte blocks with a high-bit plane)
+  int kbits;   // bits per key code: 2, or 3 / 4 (a high-bit plane at byte 1536)
+  int vbits;   // bits per value code: 2, or 3 / 4 (a high-bit plane after the keys' one, if any)
   int rot_kind;  // 0: r_k, r_v are dense [H][128][128]; 1: Hadamard, r_k, r_v are signs [H][128]
 };
 
@@ -107,7 +108,8 @@ struct EvalParams {
   const float* r_k;
   const float* r_v;
   int rot_kind;   // 0 dense [H][128][128], 1 Hadamard signs [H][128]
-  int kbits;      // bits per key code (3 and 4: 2048-byte blocks)
+  int kbits;      // bits per key code (3 and 4: a high-bit plane at byte 1536)
+  int vbits;      // bits per value code (3 and 4: a high-bit plane after the keys' one, if any)
   float sm_scale;
   int n_splits, pages_per_split;
   float* part;             // [B][H_kv][head chunk][n_splits][kEvHeads][kEvPartStride]

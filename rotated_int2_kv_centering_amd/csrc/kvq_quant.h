@@ -81,10 +81,10 @@ __device__ __forceinline__ float2 q2_wave_range(float xv, int gsize) {
 // range of channel j's group (q2_wave_range).  `block` is the (page, KV head)
 // block to write, or null to only compute; `off` is the slot within the page
 // (0..15); tensor 0 = K, 1 = V.  The block keeps one metadata pair per 32
-// channels: for G > 32 each holds its group's pair.  kbits = 3 or 4 quantizes
-// the key to 8 or 16 levels: its low two bits go where a 2-bit code would, the
-// rest to the plane at byte kKHiPlane (record r at 8 r, same word and bit).
-// Returns the dequantized level of channel j.
+// channels: for G > 32 each holds its group's pair.  kbits (vbits) = 3 or 4
+// quantizes the key (value) to 8 or 16 levels: its low two bits go where a
+// 2-bit code would, the rest to the tensor's plane (kvq_device.h: record r at
+// 8 r, the same word and bit).  Returns the dequantized level of channel j.
 //
 // K code of slot s, channel c (kk = c/32, a = (c%32)/8, e = c%8): record
 // 16a + s, word K[kk/2], bit 2(4(kk%2) + e/2) + 16(e%2).  V code (t = c/16,
@@ -94,12 +94,11 @@ __device__ __forceinline__ float2 q2_wave_range(float xv, int gsize) {
 // A K code word and a metadata pair belong to one slot (plain stores); a V
 // code word holds codes of two slots, so it is updated with atomic and/or of
 // this slot's bits only, which keeps concurrent writes to other slots intact.
-constexpr int kKHiPlane = 1536;  // byte offset of the 4-bit keys' high-bit plane in a 2048-byte block
-
 __device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, uint8_t* block, int off, float clip,
-                                                float mn, float mx, int kbits = 2) {
+                                                float mn, float mx, int kbits = 2, int vbits = 2) {
   const bool k4 = tensor == 0 && kbits > 2;  // a wide key: high part in the plane
-  const float n_lv = tensor == 0 ? static_cast<float>((1 << kbits) - 1) : 3.0f;
+  const bool v4 = tensor == 1 && vbits > 2;  // a wide value: high part in the values' plane
+  const float n_lv = static_cast<float>((1 << (tensor == 0 ? kbits : vbits)) - 1);
   const int lane = j & 63;
   const int w2 = j >> 6;
   const int grp = j >> 5;
@@ -142,14 +141,24 @@ __device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, ui
   } else {
     const int t16 = j >> 4, b = j & 15, a = off >> 2, i = off & 3;
     const int shift = 16 * (i & 1);
-    uint32_t w = code << (2 * t16 + shift);
+    uint32_t w = (code & 3u) << (2 * t16 + shift);
+    uint32_t wh = (code >> 2) << (2 * t16 + shift);  // wide values: the high bits (0 otherwise)
     w |= __shfl_xor(w, 16);
     w |= __shfl_xor(w, 32);
+    if (v4) {
+      wh |= __shfl_xor(wh, 16);
+      wh |= __shfl_xor(wh, 32);
+    }
     if (block != nullptr && lane < 16) {
       uint32_t* word = reinterpret_cast<uint32_t*>(block + 16 * (16 * a + b) + 8 + 4 * (i >> 1));
       const uint32_t mask = 0xffu << (8 * w2 + shift);  // this wave's four tiles of this slot
       atomicAnd(word, ~mask);
       atomicOr(word, w);
+      if (v4) {  // the plane's words are shared by slots as the V words are
+        uint32_t* hword = reinterpret_cast<uint32_t*>(block + v_hi_plane(kbits) + 8 * (16 * a + b) + 4 * (i >> 1));
+        atomicAnd(hword, ~mask);
+        atomicOr(hword, wh);
+      }
     }
   }
   if (block != nullptr && (j & 31) == 0) {
@@ -191,7 +200,7 @@ __device__ __forceinline__ void q2_group32(const float (&x)[32], float clip, int
   // fp16 zero included): without this the compiler may round c*min straight
   // to fp16 in one mixed-precision multiply, which differs at fp16 ties.
   asm volatile("" : "+v"(mn), "+v"(mx));
-  const float s32 = (mx - mn) / n_lv;  // n_lv = 3, or 7 / 15 for 3- / 4-bit keys
+  const float s32 = (mx - mn) / n_lv;  // n_lv = 3, or 7 / 15 for 3- / 4-bit codes
   const _Float16 s16 = static_cast<_Float16>(s32);
   const _Float16 z16 = static_cast<_Float16>(mn);
   const float sc = static_cast<float>(s16);

@@ -43,7 +43,8 @@ class KvqError(RuntimeError):
 class kvq_cache(ctypes.Structure):
     _fields_ = [("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("num_pages", ctypes.c_int32), ("pool", ctypes.c_void_p),
-                ("clip_ratio", ctypes.c_float), ("rotation", ctypes.c_int32), ("key_bits", ctypes.c_int32)]
+                ("clip_ratio", ctypes.c_float), ("rotation", ctypes.c_int32), ("key_bits", ctypes.c_int32),
+                ("val_bits", ctypes.c_int32)]
 
 
 class kvq_window(ctypes.Structure):
@@ -135,9 +136,10 @@ def _check(status: int) -> None:
 
 
 def make_cache(num_kv_heads: int, num_pages: int, pool=None, head_dim: int = HEAD_DIM, group_size: int = GROUP_SIZE,
-               page_size: int = PAGE_SIZE, clip_ratio: float = 0.0, rotation: int = 0, key_bits: int = 2) -> kvq_cache:
+               page_size: int = PAGE_SIZE, clip_ratio: float = 0.0, rotation: int = 0, key_bits: int = 2,
+               val_bits: int = 2) -> kvq_cache:
     return kvq_cache(num_kv_heads, head_dim, group_size, page_size, num_pages, _ptr(pool), clip_ratio, rotation,
-                     key_bits)
+                     key_bits, val_bits)
 
 
 def make_window(sinks: int, recent: int, batch: int, buf=None, mu=None) -> kvq_window:

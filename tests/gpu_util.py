@@ -37,16 +37,18 @@ def bf16_tensor(bits: np.ndarray, dev):
 class DeviceCase:
     """Device copies of a case's inputs and one zeroed pool."""
 
-    def __init__(self, case: I.Case, dev, num_pages=None, clip_ratio=0.0, group_size=32, key_bits=2):
+    def __init__(self, case: I.Case, dev, num_pages=None, clip_ratio=0.0, group_size=32, key_bits=2, val_bits=2):
         from rotated_int2_kv_centering_amd import kvq
         self.c = case
         self.dev = dev
         self.num_pages = int(num_pages or case.num_pages)
         self.key_bits = key_bits
-        self.pool = torch.zeros(O.pool_bytes(self.num_pages, case.Hkv, key_bits), dtype=torch.uint8, device=dev)
+        self.val_bits = val_bits
+        self.pool = torch.zeros(O.pool_bytes(self.num_pages, case.Hkv, key_bits, val_bits), dtype=torch.uint8,
+                                device=dev)
         self.group_size = group_size
         self.cache = kvq.make_cache(case.Hkv, self.num_pages, self.pool, clip_ratio=clip_ratio, group_size=group_size,
-                                    key_bits=key_bits,
+                                    key_bits=key_bits, val_bits=val_bits,
                                     rotation=kvq.KVQ_ROT_HADAMARD if case.rotation == "hadamard" else kvq.KVQ_ROT_DENSE)
         if case.dtype == "bf16":
             self.k = bf16_tensor(case.k_bits, dev)

@@ -283,6 +283,12 @@ def test_cache_clip_ratio_layout_and_validation(K):
     assert K.kvq_pool_bytes(K.make_cache(2, 8, FAKE, key_bits=0)) == 2 * 8 * 1536
     assert _decode(K, K.make_cache(1, 8, FAKE, key_bits=5)) == K.KVQ_EUNSUPPORTED and "key_bits" in K.kvq_last_error()
     assert K.kvq_pool_bytes(K.make_cache(2, 8, FAKE, key_bits=3)) == 2 * 8 * 2048
+    # 3- and 4-bit values add the values' plane: 2048 alone, 2560 with a keys' plane
+    assert K.kvq_cache.val_bits.offset == 44
+    assert K.kvq_pool_bytes(K.make_cache(2, 8, FAKE, val_bits=4)) == 2 * 8 * 2048
+    assert K.kvq_pool_bytes(K.make_cache(2, 8, FAKE, key_bits=3, val_bits=3)) == 2 * 8 * 2560
+    assert K.kvq_pool_bytes(K.make_cache(2, 8, FAKE, key_bits=4, val_bits=2)) == 2 * 8 * 2048
+    assert _decode(K, K.make_cache(1, 8, FAKE, val_bits=1)) == K.KVQ_EUNSUPPORTED and "val_bits" in K.kvq_last_error()
     assert _decode(K, K.make_cache(1, 8, FAKE, rotation=2)) == K.KVQ_EINVAL  # unknown rotation kind
     assert "rotation" in K.kvq_last_error()
     lib = K.load()

@@ -47,12 +47,14 @@ def _rows_max_rel(got, ref):
 class Evaluated:
     """Append with squared errors, then kvq_output_error; results on the host."""
 
-    def __init__(self, case, dev, d_model=96, w_dtype="bf16", table=None, with_err=True, seed=7, key_bits=2):
+    def __init__(self, case, dev, d_model=96, w_dtype="bf16", table=None, with_err=True, seed=7, key_bits=2,
+                 val_bits=2):
         import torch
         from rotated_int2_kv_centering_amd import kvq
         self.c = c = case
         self.key_bits = key_bits
-        self.dc = dc = DeviceCase(case, dev, key_bits=key_bits)
+        self.val_bits = val_bits
+        self.dc = dc = DeviceCase(case, dev, key_bits=key_bits, val_bits=val_bits)
         n = c.n_tokens
         self.sq_err = torch.zeros((max(n, 1), c.Hkv, 2, 2), dtype=torch.float32, device=dev)
         kvq.kvq_quant_append_err(dc.cache, dc.k, dc.v, dc.in_dtype, n, dc.slots, dc.mu, dc.r_k, dc.r_v, None,
@@ -94,7 +96,8 @@ class Evaluated:
         ks = [c.k[c.tok_seq == b] for b in range(c.B)]
         vs = [c.v[c.tok_seq == b] for b in range(c.B)]
         dy_k, dy_v, e_out, e_rec = O.output_error(c.q, self.dc.pool_np(), c.Hkv, self.table, c.seq_lens, ks, vs, c.mu,
-                                                  r_k, r_v, self.w_o, num_pages=c.num_pages, key_bits=self.key_bits)
+                                                  r_k, r_v, self.w_o, num_pages=c.num_pages, key_bits=self.key_bits,
+                                                  val_bits=self.val_bits)
         return dict(dy_k=dy_k, dy_v=dy_v, e_out=e_out, e_rec=e_rec)
 
 
