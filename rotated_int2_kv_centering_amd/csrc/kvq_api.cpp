@@ -113,7 +113,7 @@ int workgroups_per_cu(int) { return 1; }
 int max_splits_with_window(int g) { return g <= 4 ? kMaxSplits : 128; }
 
 bool make_plan(int batch, int num_kv_heads, int g, int max_seq_len, int num_splits, kvq::DecodePlan* plan,
-               int max_splits = kMaxSplits) {
+               int max_splits = kMaxSplits, bool stepping = false) {
   if (batch < 0 || num_kv_heads < 1 || max_seq_len < 0 || num_splits < 0) return false;
   if (max_seq_len > kMaxContext) return false;
   const int n_pages = (max_seq_len + kPage - 1) / kPage;
@@ -144,6 +144,9 @@ bool make_plan(int batch, int num_kv_heads, int g, int max_seq_len, int num_spli
     // split size under a batch of one, so page ids load before the length does
     const long long want = (static_cast<long long>(num_kv_heads) * n_pages + target - 1) / target;
     plan->pages_per_split = static_cast<int>(std::min(std::max(want, pps_min), pps_max));
+    if (batch == 1)  // the kernel's split size for the step form (a shorter appending split)
+      plan->pages_per_split =
+          kvq::step_pages_per_split(n_pages, plan->pages_per_split, static_cast<int>(pps_max), stepping);
     plan->n_splits = static_cast<int>(std::max<long long>(slots, 1));
     return true;
   }
@@ -256,7 +259,7 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
   }
   kvq::DecodePlan plan;
   if (!make_plan(batch, cache->num_kv_heads, g, max_seq_len, num_splits, &plan,
-                 win ? max_splits_with_window(g) : kMaxSplits))
+                 win ? max_splits_with_window(g) : kMaxSplits, stepping))
     return fail(KVQ_EINVAL, "cannot plan the decode split");
   const size_t need = workspace_bytes(batch, num_q_heads, cache->num_kv_heads, plan);
   if (workspace_bytes_ < need)

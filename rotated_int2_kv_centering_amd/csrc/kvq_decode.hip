@@ -166,7 +166,7 @@ __device__ SplitLoc locate_split(const DecodeParams& p, int w, int tid, int lane
     r.len = p.seq_lens[0];
     const int T0 = min(r.len, p.len_cap);
     const int pages = T0 > 0 ? (T0 + kPage - 1) / kPage : 0;
-    r.pps = pps_for(pages);
+    r.pps = step_pages_per_split(pages, pps_for(pages), p.pps_max, p.k_new != nullptr);
     const int n = max(1, (pages + r.pps - 1) / r.pps);
     r.b = w < n ? 0 : -1;
     r.split = w;
@@ -255,6 +255,11 @@ void decode_kernel(const DecodeParams p) {
   // page 0/1, part 2 = 32 x 16 B metadata of page 0 then of page 1; parts 3
   // and on: the high-bit planes of page 0 then of page 1 (keys', values').
   __shared__ uint4v s_ring[kDepth][kW][kRingParts][64];
+  // merge of split partial rows staged whole in the ring: the weight of every
+  // (split, head) row and each head's sum of weights
+  constexpr int kMaxImgRows = static_cast<int>(sizeof(s_ring) / sizeof(float)) / kPartStride;
+  __shared__ float s_wgt[kMaxImgRows];
+  __shared__ float s_wsum[kNH];
   // Prologue scratch (q_hat partials [kParts][kNH][128], then the new token's
   // partials [2][4][128]) lives in the last ring slot, which no load targets
   // before the main loop, when it fits there.  After the main loop the whole
@@ -1149,6 +1154,29 @@ void decode_kernel(const DecodeParams p) {
     }
     __syncthreads();
   }
+  // Whole rows in the ring ([split][head][acc 128 | max | sum | pad]): wave jh
+  // takes head jh's rows, lane l the splits l, l + 64, ...: the head's max M,
+  // the weights exp2(max_split - M) into s_wgt and their sum; the output sums
+  // below then read weights and rows with no chain of dependent reads.
+  if (img) {
+    for (int jh = wave; jh < g; jh += kW) {
+      float m = kNegBig;
+      for (int sp = lane; sp < n_valid; sp += 64) m = fmaxf(m, s_post[(sp * g + jh) * kPartStride + 128]);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      float l = 0.0f;
+      for (int sp = lane; sp < n_valid; sp += 64) {
+        const float* r = s_post + (sp * g + jh) * kPartStride;
+        const float w = __builtin_amdgcn_exp2f(r[128] - m);
+        s_wgt[sp * g + jh] = w;
+        l = fmaf(w, r[129], l);
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
+      if (lane == 0) s_wsum[jh] = l;
+    }
+    __syncthreads();
+  }
 #pragma unroll
   for (int k = 0; k < kIdx; ++k) {
     const int idx = tid + k * kThreads;
@@ -1156,16 +1184,13 @@ void decode_kernel(const DecodeParams p) {
     const int jh = idx / kHeadDim;
     const int c = idx % kHeadDim;
     float M = kNegBig, l = 0.0f;
-    if (img) {  // the whole rows are in the ring: [split][head][acc 128 | max | sum | pad]
-      const float* row = s_post + jh * kPartStride;
-      for (int sp = 0; sp < n_valid; ++sp) M = fmaxf(M, row[sp * g * kPartStride + 128]);
+    if (img) {
+      const float* col = s_post + jh * kPartStride + c;
+      const float* wv = s_wgt + jh;
       float o = 0.0f;
-      for (int sp = 0; sp < n_valid; ++sp) {
-        const float* r = row + sp * g * kPartStride;
-        const float w = __builtin_amdgcn_exp2f(r[128] - M);
-        l = fmaf(w, r[129], l);
-        o = fmaf(w, r[c], o);
-      }
+#pragma unroll 8
+      for (int sp = 0; sp < n_valid; ++sp) o = fmaf(wv[sp * g], col[sp * g * kPartStride], o);
+      l = s_wsum[jh];
       s_q[jh][c] = l > 0.0f ? o / l : 0.0f;  // o_rot
       continue;
     }

@@ -22,6 +22,25 @@ hipError_t launch_window_fill(uint16_t* buf, int batch, int num_kv_heads, int si
                               const void* v, int in_kind, int n_tokens, const int32_t* seq_ids,
                               const int32_t* positions, const int32_t* seq_lens, hipStream_t stream);
 
+// Step form, batch of one: the split holding the new token (the last) also
+// rotates, quantizes and packs it before its page loop, about as long as this
+// many pages of the loop take, so it is planned up to this many pages (at most
+// half a split) shorter than the others.
+constexpr int kStepSplitDeficit = 48;
+
+// Pages per split of a batch of one under the automatic plan, from the pages
+// p of the sequence and the split size pps0 the balanced plan gives: the same
+// split count, with the last split up to kStepSplitDeficit pages shorter when
+// the call appends.  Host and kernel both use it (the host to guess the page
+// ids of a split before the length is read).
+__host__ __device__ inline int step_pages_per_split(int pages, int pps0, int pps_max, bool stepping) {
+  const int n = pages > 0 ? (pages + pps0 - 1) / pps0 : 1;
+  if (!stepping || n < 2) return pps0;
+  const int d = pps0 / 2 < kStepSplitDeficit ? pps0 / 2 : kStepSplitDeficit;
+  const int pps = (pages + d + n - 1) / n;  // n * pps >= pages + d, and still n splits
+  return pps <= pps_max ? pps : pps0;
+}
+
 struct DecodePlan {
   int n_pages_max;      // ceil(max_seq_len / 16)
   bool balanced;
