@@ -207,8 +207,9 @@ kvq_status kvq_quant_append_err(const kvq_cache* cache, const void* k, const voi
  * kvq_decode_workspace_bytes - device workspace needed by kvq_decode_attn for
  * the same (batch, num_q_heads, num_kv_heads, max_seq_len, num_splits).
  * num_splits 0 selects the automatic split plan.  Returns 0 on invalid input.
- * The workspace holds per-(sequence, KV head) ticket counters and the split
- * partials.  It must be zero-filled before its first use; every completed
+ * The workspace holds per-(sequence, KV head) ticket counters, the split
+ * partials and one row per output row for an exact window's part (used when a
+ * window is given).  It must be zero-filled before its first use; every completed
  * call leaves the counters at zero again, so a workspace is then reusable
  * without clearing.  Calls that share one workspace must not overlap in time
  * (same stream, or ordered by events).

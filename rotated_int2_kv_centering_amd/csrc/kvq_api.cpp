@@ -113,7 +113,7 @@ int workgroups_per_cu(int) { return 1; }
 int max_splits_with_window(int g) { return g <= 4 ? kMaxSplits : 128; }
 
 bool make_plan(int batch, int num_kv_heads, int g, int max_seq_len, int num_splits, kvq::DecodePlan* plan,
-               int max_splits = kMaxSplits, bool stepping = false) {
+               int max_splits = kMaxSplits, int extra = 0) {
   if (batch < 0 || num_kv_heads < 1 || max_seq_len < 0 || num_splits < 0) return false;
   if (max_seq_len > kMaxContext) return false;
   const int n_pages = (max_seq_len + kPage - 1) / kPage;
@@ -144,9 +144,9 @@ bool make_plan(int batch, int num_kv_heads, int g, int max_seq_len, int num_spli
     // split size under a batch of one, so page ids load before the length does
     const long long want = (static_cast<long long>(num_kv_heads) * n_pages + target - 1) / target;
     plan->pages_per_split = static_cast<int>(std::min(std::max(want, pps_min), pps_max));
-    if (batch == 1)  // the kernel's split size for the step form (a shorter appending split)
+    if (batch == 1)  // the kernel's split size with an append or a window (a shorter last split)
       plan->pages_per_split =
-          kvq::step_pages_per_split(n_pages, plan->pages_per_split, static_cast<int>(pps_max), stepping);
+          kvq::step_pages_per_split(n_pages, plan->pages_per_split, static_cast<int>(pps_max), extra);
     plan->n_splits = static_cast<int>(std::max<long long>(slots, 1));
     return true;
   }
@@ -172,9 +172,15 @@ size_t counters_bytes(int batch, int num_kv_heads) {
   return (static_cast<size_t>(batch) * num_kv_heads * sizeof(int32_t) + 255) / 256 * 256;
 }
 
+// Workspace: merge counters, split partial rows, then one window row per output
+// row (used when a window is given).
+size_t split_rows_bytes(int batch, int num_q_heads, const kvq::DecodePlan& plan) {
+  return sizeof(float) * static_cast<size_t>(plan.balanced ? 1 : batch) * num_q_heads * plan.n_splits * kRowStride;
+}
+
 size_t workspace_bytes(int batch, int num_q_heads, int num_kv_heads, const kvq::DecodePlan& plan) {
-  const size_t rows = static_cast<size_t>(plan.balanced ? 1 : batch) * num_q_heads * plan.n_splits;
-  return counters_bytes(batch, num_kv_heads) + sizeof(float) * rows * kRowStride;
+  return counters_bytes(batch, num_kv_heads) + split_rows_bytes(batch, num_q_heads, plan) +
+         sizeof(float) * static_cast<size_t>(batch) * num_q_heads * kRowStride;
 }
 
 constexpr int kMaxWindowSinks = 8;
@@ -259,7 +265,7 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
   }
   kvq::DecodePlan plan;
   if (!make_plan(batch, cache->num_kv_heads, g, max_seq_len, num_splits, &plan,
-                 win ? max_splits_with_window(g) : kMaxSplits, stepping))
+                 win ? max_splits_with_window(g) : kMaxSplits, static_cast<int>(stepping) + static_cast<int>(win)))
     return fail(KVQ_EINVAL, "cannot plan the decode split");
   const size_t need = workspace_bytes(batch, num_q_heads, cache->num_kv_heads, plan);
   if (workspace_bytes_ < need)
@@ -298,6 +304,8 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
   a.win_sinks = win ? window->sinks : 0;
   a.win_recent = win ? window->recent : 0;
   a.win_mu = win ? window->mu : nullptr;
+  a.win_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + counters_bytes(batch, cache->num_kv_heads) +
+                                        split_rows_bytes(batch, num_q_heads, plan));
   a.k_new = stepping ? k_new : nullptr;
   a.v_new = stepping ? v_new : nullptr;
   a.kv_kind = kv_dtype == KVQ_BF16 ? 0 : 1;

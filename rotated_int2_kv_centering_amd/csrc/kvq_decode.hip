@@ -166,7 +166,7 @@ __device__ SplitLoc locate_split(const DecodeParams& p, int w, int tid, int lane
     r.len = p.seq_lens[0];
     const int T0 = min(r.len, p.len_cap);
     const int pages = T0 > 0 ? (T0 + kPage - 1) / kPage : 0;
-    r.pps = step_pages_per_split(pages, pps_for(pages), p.pps_max, p.k_new != nullptr);
+    r.pps = step_pages_per_split(pages, pps_for(pages), p.pps_max, (p.k_new != nullptr) + (p.win != nullptr));
     const int n = max(1, (pages + r.pps - 1) / r.pps);
     r.b = w < n ? 0 : -1;
     r.split = w;
@@ -259,7 +259,7 @@ void decode_kernel(const DecodeParams p) {
   // (split, head) row and each head's sum of weights
   constexpr int kMaxImgRows = static_cast<int>(sizeof(s_ring) / sizeof(float)) / kPartStride;
   __shared__ float s_wgt[kMaxImgRows];
-  __shared__ float s_wsum[kNH];
+  __shared__ float s_wsum[kNH], s_wmax[kNH];
   // Prologue scratch (q_hat partials [kParts][kNH][128], then the new token's
   // partials [2][4][128]) lives in the last ring slot, which no load targets
   // before the main loop, when it fits there.  After the main loop the whole
@@ -861,69 +861,12 @@ void decode_kernel(const DecodeParams p) {
     }
   }
 
-  // ---- the last workgroup of (b, h) merges the splits.  The partial stores
-  // complete (vmcnt 0) before the ticket is taken; the merging workgroup reads
-  // them with agent-scope loads after seeing the last ticket.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tid == 0)
-    s_ticket = __hip_atomic_fetch_add(p.counters + b * H + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // R_V rows for the output rotation, requested by every workgroup right after
-  // its ticket (the merging one finds them in flight): thread (row oi, part oq)
-  // takes channels [kRows * oq, +kRows) of row oi
-  const int oi = tid & (kHeadDim - 1);
-  const int oq = rpart;
-  float4v rr[kRows / 4];
-  float sgv = 0.0f;  // Hadamard: the sign of output channel oi
-  if (!hadamard) {
-    const float* Rrow = p.r_v + (static_cast<size_t>(h) * kHeadDim + oi) * kHeadDim + kRows * oq;
-#pragma unroll
-    for (int u = 0; u < kRows / 4; ++u) rr[u] = *reinterpret_cast<const float4v*>(Rrow + 4 * u);
-  } else {
-    sgv = p.r_v[h * kHeadDim + oi];
-  }
-  __syncthreads();
-  if (s_ticket != n_valid - 1) return;
-
-  // Merge, in one load round.  Without a window, when they fit, the split
-  // partial rows (contiguous in the workspace) are copied whole into the ring,
-  // which is free now, by 16-byte coherent DMA (1 KB per wave instruction).
-  // Otherwise every (split, head) max/sum pair is loaded by one thread and
-  // shared through LDS, while thread (head jh, channel c) loads acc[c] of the
-  // first kAB splits; this workgroup's own split comes from registers.
-  constexpr int kAB = kNQ == 1 ? 32 : 8;  // splits per acc load round
-  static_assert(sizeof(s_ring) >= sizeof(float) * 2 * kMaxSplits * kNH, "max/sum pairs fit in the ring");
-  const float* pb = p.part + head_base * g * kPartStride;
-  float* s_ml = s_post;  // [split][head][2]: max, sum
-  const int n_ml = n_valid * g;
-  const int n_img = n_ml * kPartStride;  // floats of the partial rows
-  const bool img = !has_win && n_img + 64 * 4 <= static_cast<int>(sizeof(s_ring) / sizeof(float));
-  float av[kIdx][kAB];
-  auto load_acc = [&](int k, int s0) {
-    const int idx = min(tid + k * kThreads, g * kHeadDim - 1);
-    const int jh = idx / kHeadDim, c = idx % kHeadDim;
-#pragma unroll
-    for (int u = 0; u < kAB; ++u) av[k][u] = ld_agent(pb + (min(s0 + u, n_valid - 1) * g + jh) * kPartStride + c);
-  };
-  float ml0 = 0.0f, ml1 = 0.0f;
-  if (img) {
-    // chunk ch of 16 B lands at s_post + 4 ch; the last instruction's spare
-    // lanes repeat the last chunk into the 1 KB of slack after the rows
-    static_assert(kPartStride % 4 == 0, "partial rows are whole 16-byte chunks");
-    const int n_ch = n_img / 4;
-    for (int c0 = 64 * wave; c0 < n_ch; c0 += 64 * kW)
-      dma16_agent(reinterpret_cast<const uint8_t*>(pb), 16 * min(c0 + lane, n_ch - 1), s_post + 4 * c0);
-  } else {
-    if (tid < n_ml) {
-      ml0 = ld_agent(pb + static_cast<size_t>(tid) * kPartStride + 128);  // split tid / g, head tid % g
-      ml1 = ld_agent(pb + static_cast<size_t>(tid) * kPartStride + 129);
-    }
-#pragma unroll
-    for (int k = 0; k < kIdx; ++k) load_acc(k, 0);
-  }
-
   // Exact window (g <= 8), on the matrix cores (v_mfma_f32_16x16x32_bf16; the
-  // window rows are exact bf16).  Rows: n_ws sinks, then positions w_r0 .. T-1,
+  // window rows are exact bf16), computed by the workgroup of the sequence's
+  // last split after its page loop and stored to the workspace before its
+  // ticket (the window row of each query head: acc 128 | max | sum, acc
+  // unnormalised and in the original basis); the merging workgroup loads it
+  // with the split rows.  Rows: n_ws sinks, then positions w_r0 .. T-1,
   // staged in the upper part of the ring (row-major, 512 B per row: the key,
   // whose 16-byte chunks are XOR-swizzled by row % 16, then the value), above
   // the merge's max/sum pairs (at most 2 * kNH * (max splits with a window)
@@ -953,11 +896,12 @@ void decode_kernel(const DecodeParams p) {
                             kWmuOff >= 2 * kNH * kWinSplits && kWmlOff >= kParts * kNH * kHeadDim),
                 "window staging fits above the merge scratch");
   const bool win_here = kWinOk && has_win;
+  const bool win_wg = win_here && split == n_valid - 1;  // computes the window part
   int n_ws = 0, w_r0 = 0, n_w = 0;
   uint4v wraw[kWinLd];
   uint32_t qwr[kQPerThread];
   float wmu = 0.0f;
-  if (win_here) {
+  if (win_wg) {
     n_ws = min(p.win_sinks, T);
     w_r0 = max(n_ws, T - p.win_recent);
     n_w = n_ws + (T - w_r0);
@@ -1017,18 +961,11 @@ void decode_kernel(const DecodeParams p) {
     }
     if (tid < kHeadDim && p.win_mu != nullptr) wmu = p.win_mu[h * kHeadDim + tid];
   }
-  for (int q = tid; q < (img ? 0 : n_ml); q += kThreads) {
-    if (q != tid) {  // beyond the first pair per thread
-      ml0 = ld_agent(pb + static_cast<size_t>(q) * kPartStride + 128);
-      ml1 = ld_agent(pb + static_cast<size_t>(q) * kPartStride + 129);
-    }
-    s_ml[2 * q] = ml0;
-    s_ml[2 * q + 1] = ml1;
-  }
+  if (win_wg) __syncthreads();  // the per-wave partials were read; the ring takes the window rows
   uint4v* const s_rows = reinterpret_cast<uint4v*>(s_post + kRowsOff);  // 32 chunks per row
   float* const s_wp = s_post + kWpOff;
   uint16_t* const s_qp = reinterpret_cast<uint16_t*>(s_post + kQpOff);
-  if (win_here) {
+  if (win_wg) {
 #pragma unroll
     for (int u = 0; u < kWinLd; ++u) {
       const int idx = tid + u * kThreads;
@@ -1055,9 +992,8 @@ void decode_kernel(const DecodeParams p) {
     }
     if (tid < kHeadDim) s_post[kWmuOff + tid] = wmu;
   }
-  if (img) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial-row copies have landed
-  __syncthreads();
-  if (win_here) {
+  if (win_wg) __syncthreads();
+  if (win_wg) {
     const int hq = lane & 15, kq = lane >> 4;
     // <q_head, mu>, one wave per head
     for (int jh = wave; jh < g; jh += kW) {
@@ -1153,7 +1089,103 @@ void decode_kernel(const DecodeParams p) {
       }
     }
     __syncthreads();
+    // the window rows to the workspace (agent scope, like the split partials)
+    for (int idx = tid; idx < g * kHeadDim; idx += kThreads) {
+      const int jh = idx / kHeadDim, c = idx % kHeadDim;
+      float* dst = p.win_part + (out_row0 + jh) * kPartStride;
+      __hip_atomic_store(dst + c, s_post[kOwOff + jh * kHeadDim + c], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (c == 0) {
+        __hip_atomic_store(dst + 128, s_post[kWmlOff + 2 * jh], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(dst + 129, s_post[kWmlOff + 2 * jh + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
   }
+
+  // ---- the last workgroup of (b, h) merges the splits.  The partial stores
+  // complete (vmcnt 0) before the ticket is taken; the merging workgroup reads
+  // them with agent-scope loads after seeing the last ticket.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0)
+    s_ticket = __hip_atomic_fetch_add(p.counters + b * H + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // R_V rows for the output rotation, requested by every workgroup right after
+  // its ticket (the merging one finds them in flight): thread (row oi, part oq)
+  // takes channels [kRows * oq, +kRows) of row oi
+  const int oi = tid & (kHeadDim - 1);
+  const int oq = rpart;
+  float4v rr[kRows / 4];
+  float sgv = 0.0f;  // Hadamard: the sign of output channel oi
+  if (!hadamard) {
+    const float* Rrow = p.r_v + (static_cast<size_t>(h) * kHeadDim + oi) * kHeadDim + kRows * oq;
+#pragma unroll
+    for (int u = 0; u < kRows / 4; ++u) rr[u] = *reinterpret_cast<const float4v*>(Rrow + 4 * u);
+  } else {
+    sgv = p.r_v[h * kHeadDim + oi];
+  }
+  __syncthreads();
+  if (s_ticket != n_valid - 1) return;
+
+  // Merge, in one load round.  When they fit, the split partial rows
+  // (contiguous in the workspace) are copied whole into the ring, which is free
+  // now, by 16-byte coherent DMA (1 KB per wave instruction).  Otherwise every
+  // (split, head) max/sum pair is loaded by one thread and shared through LDS,
+  // while thread (head jh, channel c) loads acc[c] of the first kAB splits;
+  // this workgroup's own split comes from registers.  With a window, each
+  // thread also loads its channel of the head's window row.
+  constexpr int kAB = kNQ == 1 ? 32 : 8;  // splits per acc load round
+  static_assert(sizeof(s_ring) >= sizeof(float) * 2 * kMaxSplits * kNH, "max/sum pairs fit in the ring");
+  const float* pb = p.part + head_base * g * kPartStride;
+  float* s_ml = s_post;  // [split][head][2]: max, sum
+  const int n_ml = n_valid * g;
+  const int n_img = n_ml * kPartStride;  // floats of the partial rows
+  // staged rows stay below the window's value sums (kOwOff) when there is a window
+  const bool img = n_img + 64 * 4 <= (win_here ? kOwOff : kRingFloats);
+  float av[kIdx][kAB];
+  auto load_acc = [&](int k, int s0) {
+    const int idx = min(tid + k * kThreads, g * kHeadDim - 1);
+    const int jh = idx / kHeadDim, c = idx % kHeadDim;
+#pragma unroll
+    for (int u = 0; u < kAB; ++u) av[k][u] = ld_agent(pb + (min(s0 + u, n_valid - 1) * g + jh) * kPartStride + c);
+  };
+  float ml0 = 0.0f, ml1 = 0.0f;
+  if (img) {
+    // chunk ch of 16 B lands at s_post + 4 ch; the last instruction's spare
+    // lanes repeat the last chunk into the 1 KB of slack after the rows
+    static_assert(kPartStride % 4 == 0, "partial rows are whole 16-byte chunks");
+    const int n_ch = n_img / 4;
+    for (int c0 = 64 * wave; c0 < n_ch; c0 += 64 * kW)
+      dma16_agent(reinterpret_cast<const uint8_t*>(pb), 16 * min(c0 + lane, n_ch - 1), s_post + 4 * c0);
+  } else {
+    if (tid < n_ml) {
+      ml0 = ld_agent(pb + static_cast<size_t>(tid) * kPartStride + 128);  // split tid / g, head tid % g
+      ml1 = ld_agent(pb + static_cast<size_t>(tid) * kPartStride + 129);
+    }
+#pragma unroll
+    for (int k = 0; k < kIdx; ++k) load_acc(k, 0);
+  }
+  // the window row of thread (head, channel): acc, max, sum
+  float w_acc[kIdx], w_m[kIdx], w_l[kIdx];
+  if (win_here) {
+#pragma unroll
+    for (int k = 0; k < kIdx; ++k) {
+      const int idx = min(tid + k * kThreads, g * kHeadDim - 1);
+      const float* wr = p.win_part + (out_row0 + idx / kHeadDim) * kPartStride;
+      w_acc[k] = ld_agent(wr + idx % kHeadDim);
+      w_m[k] = ld_agent(wr + 128);
+      w_l[k] = ld_agent(wr + 129);
+    }
+  }
+
+  for (int q = tid; q < (img ? 0 : n_ml); q += kThreads) {
+    if (q != tid) {  // beyond the first pair per thread
+      ml0 = ld_agent(pb + static_cast<size_t>(q) * kPartStride + 128);
+      ml1 = ld_agent(pb + static_cast<size_t>(q) * kPartStride + 129);
+    }
+    s_ml[2 * q] = ml0;
+    s_ml[2 * q + 1] = ml1;
+  }
+  if (img) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial-row copies have landed
+  __syncthreads();
   // Whole rows in the ring ([split][head][acc 128 | max | sum | pad]): wave jh
   // takes head jh's rows, lane l the splits l, l + 64, ...: the head's max M,
   // the weights exp2(max_split - M) into s_wgt and their sum; the output sums
@@ -1173,7 +1205,10 @@ void decode_kernel(const DecodeParams p) {
       }
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
-      if (lane == 0) s_wsum[jh] = l;
+      if (lane == 0) {
+        s_wsum[jh] = l;
+        s_wmax[jh] = m;
+      }
     }
     __syncthreads();
   }
@@ -1191,16 +1226,23 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll 8
       for (int sp = 0; sp < n_valid; ++sp) o = fmaf(wv[sp * g], col[sp * g * kPartStride], o);
       l = s_wsum[jh];
+      if (win_here) {  // the window's part: its weight against the splits' max, value sum added after R_V^T
+        const float m = s_wmax[jh], mx = fmaxf(m, w_m[k]);
+        const float a = __builtin_amdgcn_exp2f(m - mx), ww = __builtin_amdgcn_exp2f(w_m[k] - mx);
+        l = fmaf(a, l, ww * w_l[k]);
+        o *= a;
+        s_post[kOwOff + jh * kHeadDim + c] = l > 0.0f ? ww * w_acc[k] / l : 0.0f;
+      }
       s_q[jh][c] = l > 0.0f ? o / l : 0.0f;  // o_rot
       continue;
     }
     for (int sp = 0; sp < n_valid; ++sp) M = fmaxf(M, s_ml[2 * (sp * g + jh)]);
-    const float wm = win_here ? s_post[kWmlOff + 2 * jh] : kNegBig;
+    const float wm = win_here ? w_m[k] : kNegBig;
     M = fmaxf(M, wm);
     for (int sp = 0; sp < n_valid; ++sp)
       l = fmaf(__builtin_amdgcn_exp2f(s_ml[2 * (sp * g + jh)] - M), s_ml[2 * (sp * g + jh) + 1], l);
     const float ww = __builtin_amdgcn_exp2f(wm - M);  // weight of the window's part
-    if (win_here) l = fmaf(ww, s_post[kWmlOff + 2 * jh + 1], l);
+    if (win_here) l = fmaf(ww, w_l[k], l);
     float o = 0.0f;
     for (int s0 = 0; s0 < n_valid; s0 += kAB) {
       if (s0 > 0) load_acc(k, s0);
@@ -1213,7 +1255,7 @@ void decode_kernel(const DecodeParams p) {
     }
     s_q[jh][c] = l > 0.0f ? o / l : 0.0f;  // o_rot
     if (win_here)  // the window's value sum (original basis), added after R_V^T
-      s_post[kOwOff + jh * kHeadDim + c] = l > 0.0f ? ww * s_post[kOwOff + jh * kHeadDim + c] / l : 0.0f;
+      s_post[kOwOff + jh * kHeadDim + c] = l > 0.0f ? ww * w_acc[k] / l : 0.0f;
   }
   __syncthreads();
 

@@ -22,21 +22,23 @@ hipError_t launch_window_fill(uint16_t* buf, int batch, int num_kv_heads, int si
                               const void* v, int in_kind, int n_tokens, const int32_t* seq_ids,
                               const int32_t* positions, const int32_t* seq_lens, hipStream_t stream);
 
-// Step form, batch of one: the split holding the new token (the last) also
-// rotates, quantizes and packs it before its page loop, about as long as this
-// many pages of the loop take, so it is planned up to this many pages (at most
-// half a split) shorter than the others.
+// Batch of one: the workgroup of the last split also does the step's append
+// (rotating, quantizing and packing the new token before its page loop) and
+// the exact window's part (after it), each about as long as this many pages of
+// the loop take, so that split is planned up to this many pages per extra task
+// (at most half a split) shorter than the others.
 constexpr int kStepSplitDeficit = 48;
 
 // Pages per split of a batch of one under the automatic plan, from the pages
 // p of the sequence and the split size pps0 the balanced plan gives: the same
-// split count, with the last split up to kStepSplitDeficit pages shorter when
-// the call appends.  Host and kernel both use it (the host to guess the page
-// ids of a split before the length is read).
-__host__ __device__ inline int step_pages_per_split(int pages, int pps0, int pps_max, bool stepping) {
+// split count, with the last split up to extra * kStepSplitDeficit pages
+// shorter (extra: 1 for an append, 1 for a window).  Host and kernel both use
+// it (the host to guess the page ids of a split before the length is read).
+__host__ __device__ inline int step_pages_per_split(int pages, int pps0, int pps_max, int extra) {
   const int n = pages > 0 ? (pages + pps0 - 1) / pps0 : 1;
-  if (!stepping || n < 2) return pps0;
-  const int d = pps0 / 2 < kStepSplitDeficit ? pps0 / 2 : kStepSplitDeficit;
+  if (extra <= 0 || n < 2) return pps0;
+  const int want = extra * kStepSplitDeficit;
+  const int d = pps0 / 2 < want ? pps0 / 2 : want;
   const int pps = (pages + d + n - 1) / n;  // n * pps >= pages + d, and still n splits
   return pps <= pps_max ? pps : pps0;
 }
@@ -85,6 +87,7 @@ struct DecodeParams {
   uint16_t* win;
   int win_sinks, win_recent;
   const float* win_mu;
+  float* win_part;  // the window's part per output row [batch * num_q_heads][kPartStride]: acc 128, max, sum
   // Step form: when k_new is non-null, the token at position seq_lens[b] - 1 of
   // every sequence is first quantize-appended from k_new/v_new [batch][H_kv][128]
   // (kv_kind 0 bf16, 1 fp32; mu [H_kv][128] or null) by the workgroup whose

@@ -64,25 +64,26 @@ def test_pool_bytes(K):
 
 
 def test_workspace_bytes_with_explicit_splits(K):
-    # counters (B*Hkv int32, padded to 256 B) + B*Hq*n_splits partial rows of 132 floats;
-    # 1000 tokens = 63 pages: 7 splits of 9 pages
-    assert K.kvq_decode_workspace_bytes(2, 8, 2, 1000, 7) == 256 + 4 * 2 * 8 * 7 * 132
+    # counters (B*Hkv int32, padded to 256 B) + B*Hq*n_splits partial rows of 132 floats
+    # + B*Hq window rows of 132 floats; 1000 tokens = 63 pages: 7 splits of 9 pages
+    assert K.kvq_decode_workspace_bytes(2, 8, 2, 1000, 7) == 256 + 4 * 2 * 8 * 7 * 132 + 4 * 2 * 8 * 132
     # a request of more splits than pages gives one page per split
-    assert K.kvq_decode_workspace_bytes(1, 4, 1, 40, 16) == 256 + 4 * 1 * 4 * 3 * 132
+    assert K.kvq_decode_workspace_bytes(1, 4, 1, 40, 16) == 256 + 4 * 1 * 4 * 3 * 132 + 4 * 4 * 132
     # at most 512 splits: pages per split grow instead
     big = 600 * 16
-    assert K.kvq_decode_workspace_bytes(1, 4, 1, big, 600) == 256 + 4 * 4 * 300 * 132
+    assert K.kvq_decode_workspace_bytes(1, 4, 1, big, 600) == 256 + 4 * 4 * 300 * 132 + 4 * 4 * 132
 
 
 def test_workspace_bytes_automatic_plan(K):
     # Automatic plan, 256 compute units: split slots per KV head
     # S = min(B * ceil(pages / pps_min), max(ceil(256 / H_kv), ceil(B * pages / 2048)) + B - 1),
-    # pps_min = max(8, ceil(pages / 512)); partial rows = H_q * S.
-    assert K.kvq_decode_workspace_bytes(1, 32, 8, 131072, 0) == 256 + 4 * 32 * 32 * 132
-    assert K.kvq_decode_workspace_bytes(16, 32, 8, 65536, 0) == 512 + 4 * 32 * (32 + 15) * 132
-    assert K.kvq_decode_workspace_bytes(3, 8, 2, 100, 0) == 256 + 4 * 8 * 3 * 132  # one split per sequence
+    # pps_min = max(8, ceil(pages / 512)); partial rows = H_q * S; window rows = B * H_q.
+    assert K.kvq_decode_workspace_bytes(1, 32, 8, 131072, 0) == 256 + 4 * 32 * 32 * 132 + 4 * 32 * 132
+    assert K.kvq_decode_workspace_bytes(16, 32, 8, 65536, 0) == 512 + 4 * 32 * (32 + 15) * 132 + 4 * 16 * 32 * 132
+    # one split per sequence
+    assert K.kvq_decode_workspace_bytes(3, 8, 2, 100, 0) == 256 + 4 * 8 * 3 * 132 + 4 * 3 * 8 * 132
     # B = 4, 8192 pages: max(32, ceil(4 * 8192 / 2048) = 16) + 3 = 35 slots
-    assert K.kvq_decode_workspace_bytes(4, 64, 8, 131072, 0) == 256 + 4 * 64 * 35 * 132
+    assert K.kvq_decode_workspace_bytes(4, 64, 8, 131072, 0) == 256 + 4 * 64 * 35 * 132 + 4 * 4 * 64 * 132
 
 
 def test_workspace_bytes_rejects_bad_shapes(K):
