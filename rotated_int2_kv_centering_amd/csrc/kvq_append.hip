@@ -323,9 +323,13 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
         for (int u = 0; u < 8; ++u)
           *reinterpret_cast<float4v*>(dst + 4 * u) = float4v{x[4 * u], x[4 * u + 1], x[4 * u + 2], x[4 * u + 3]};
       }
-      // the 16 tokens fill one page in order: every word of the page is written whole
-      const int slot0 = __shfl(slot, 0);
-      const bool full = __builtin_amdgcn_ballot_w64(!(ok && slot == slot0 + r && (slot0 & 15) == 0)) == 0;
+      // Slots 2k and 2k + 1 of a page share their V words.  The partner of this
+      // token's slot is held by token r - 1 or r + 1 of the tile when this call
+      // writes it there (lane 4 pr + g, the same group).
+      const int pr = (slot & 1) ? r - 1 : r + 1;
+      const int plane = 4 * (pr & 15) + g;
+      const int pslot = __shfl(slot, plane);
+      const bool paired = ok && pr >= 0 && pr < 16 && pslot == (slot ^ 1);
       const int off = slot & 15;
       uint8_t* block =  // the block stride follows the cache format (key and value bits)
           pool + (static_cast<size_t>(ok ? slot >> 4 : 0) * num_kv_heads + h) * block_bytes(kbits, vbits);
@@ -378,20 +382,21 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
             return reinterpret_cast<uint32_t*>(block + (part == 0 ? 16 * rec + 8 : v_hi_plane(kbits) + 8 * rec) +
                                                4 * ((off & 3) >> 1));
           };
-          if (full) {  // pair the two slots of each word (tokens r and r ^ 1), plain stores
+          // Both slots of a word written by this tile: the even slot's lane stores
+          // the combined word whole.  Otherwise the partner slot may be written
+          // concurrently by another tile (or keeps an older token): only this
+          // slot's half, with atomic and/or.
+          const uint32_t mask = 0xffffu << hs;
   #pragma unroll
-            for (int bb = 0; bb < 16; ++bb) vw[bb] |= __shfl_xor(vw[bb], 4);
-            if ((r & 1) == 0) {
-  #pragma unroll
-              for (int u = 0; u < 4; ++u) *word_at(4 * g + u) = vw[4 * g + u];
-            }
-          } else if (ok) {  // other slots of the page may be written concurrently: only this slot's half
-            const uint32_t mask = 0xffffu << hs;
-  #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+          for (int u = 0; u < 4; ++u) {
+            const uint32_t mine = vw[4 * g + u];
+            const uint32_t other = __shfl(mine, plane);
+            if (paired) {
+              if ((slot & 1) == 0) *word_at(4 * g + u) = mine | other;
+            } else if (ok) {
               uint32_t* word = word_at(4 * g + u);
               atomicAnd(word, ~mask);
-              atomicOr(word, vw[4 * g + u]);
+              atomicOr(word, mine);
             }
           }
         }

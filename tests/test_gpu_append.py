@@ -109,6 +109,38 @@ def test_same_page_tokens_in_one_call_any_order():
     np.testing.assert_array_equal(dc.pool_np(), expect)
 
 
+@pytest.mark.parametrize("order,vb", [("misaligned", 2), ("scrambled", 2), ("misaligned", 4)])
+def test_bulk_append_shared_value_words(order, vb):
+    """The bulk kernel over a dirty pool: sequences whose tokens start off the
+    16-token tile grid (value words shared by slot pairs split across tiles),
+    tokens in a scrambled order, and dropped slots whose partner is written
+    alone.  Bytes equal the oracle's quantizer and packing on the kernel's own
+    rotated rows; slots not written keep their dirty bits."""
+    from rotated_int2_kv_centering_amd import kvq
+    import torch
+    dev = require_gpu()
+    case = I.make_case("bs", 71 + vb, B=3, Hq=8, Hkv=2, seq_lens=[300, 77, 130], dtype="bf16",
+                       table_policy="interleaved")
+    dc = DeviceCase(case, dev, val_bits=vb)
+    dc.pool.copy_(dev_tensor(np.random.default_rng(7).integers(0, 256, dc.pool.numel()).astype(np.uint8), dev))
+    dirty = dc.pool_np()
+    n = case.n_tokens
+    perm = np.arange(n) if order == "misaligned" else np.random.default_rng(8).permutation(n)
+    slots = case.slots[perm].astype(np.int32).copy()
+    drop = np.random.default_rng(9).choice(n, 9, replace=False)
+    slots[drop] = -1
+    idx = dev_tensor(perm.astype(np.int64), dev)
+    rot = torch.empty((n, case.Hkv, 2, 128), dtype=torch.float32, device=dev)
+    kvq.kvq_quant_append(dc.cache, dc.k[idx].contiguous(), dc.v[idx].contiguous(), dc.in_dtype, n,
+                         dev_tensor(slots, dev), dc.mu, dc.r_k, dc.r_v, rot)
+    torch.cuda.synchronize()
+    r = rot.cpu().numpy()
+    keep = slots >= 0
+    expect = dirty.copy()
+    O.quantize_append(expect, case.Hkv, slots[keep], r[keep, :, 0], r[keep, :, 1], val_bits=vb)
+    np.testing.assert_array_equal(dc.pool_np(), expect)
+
+
 def test_invalid_slots_are_skipped_and_other_slots_kept():
     dev = require_gpu()
     case = I.make_case("i", 61, B=1, Hq=4, Hkv=1, seq_lens=[20], dtype="f32", table_policy="contiguous")
