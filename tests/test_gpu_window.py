@@ -181,3 +181,46 @@ def test_step_with_window(dtype, sinks, recent):
     np.testing.assert_array_equal(dc.win_buf.cpu().numpy(), full.win_buf.cpu().numpy())
     ref = _oracle(case, dc.pool_np(), sinks, recent)
     assert max_abs_rel(got, ref) <= TOL
+
+
+@pytest.mark.parametrize("shape", [(1, 4, 1, [2000], 64), (1, 64, 8, [3000], 40), (2, 32, 8, [900, 1500], 24)],
+                         ids=lambda s: f"Hq{s[1]}_Hkv{s[2]}_T{'-'.join(map(str, s[3]))}_ns{s[4]}")
+def test_decode_window_many_splits(shape):
+    """Enough splits that the merging workgroup cannot stage the partial rows and
+    loads them per thread; the window rows come from the workspace either way."""
+    dev = require_gpu()
+    B, Hq, Hkv, lens, ns = shape
+    case = I.make_case("wm", 230 + sum(lens) + Hq, B=B, Hq=Hq, Hkv=Hkv, seq_lens=lens, table_policy="interleaved")
+    dc = DeviceCase(case, dev)
+    dc.append(rot_out=False)
+    win = dc.window(4, 128)
+    ref = _oracle(case, dc.pool_np(), 4, 128)
+    for n in (ns, 0):
+        got = dc.decode("f32", num_splits=n, window=win)
+        assert max_abs_rel(got, ref) <= TOL, n
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_step_with_window_batch_one(dtype):
+    """A batch of one at a length that the automatic plan cuts into many splits:
+    the last split appends the new token and computes the window's part (and is
+    planned shorter for both); bytes equal the append's, output the oracle's."""
+    from rotated_int2_kv_centering_amd import kvq
+    import torch
+    dev = require_gpu()
+    case = I.make_case("wb", 91, B=1, Hq=32, Hkv=8, seq_lens=[5000], dtype=dtype, table_policy="permuted")
+    newest = np.array([case.n_tokens - 1])
+    old = np.arange(case.n_tokens - 1)
+    ref_dc = DeviceCase(case, dev)
+    ref_dc.append(rot_out=False)
+    dc = DeviceCase(case, dev)
+    sel = dev_tensor(old, dev)
+    kvq.kvq_quant_append(dc.cache, dc.k[sel].contiguous(), dc.v[sel].contiguous(), dc.in_dtype, len(old),
+                         dc.slots[sel].contiguous(), dc.mu, dc.r_k, dc.r_v)
+    win = dc.window(4, 128, tokens=old)
+    k_new, v_new = dc.k[dev_tensor(newest, dev)].contiguous(), dc.v[dev_tensor(newest, dev)].contiguous()
+    got = dc.step(k_new, v_new, window=win)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dc.pool_np(), ref_dc.pool_np())
+    ref = _oracle(case, dc.pool_np(), 4, 128)
+    assert max_abs_rel(got, ref) <= TOL
