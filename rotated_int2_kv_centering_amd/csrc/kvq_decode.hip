@@ -221,8 +221,8 @@ __device__ __forceinline__ float ld_agent(const float* p) {
 }
 
 // quads of query heads (g <= 4 * kNQ), waves per workgroup, ring depth, 3- or
-// 4-bit keys, 3- or 4-bit values
-template <int kNQ, int kW, int kDepth, bool kKW, bool kVW>
+// 4-bit keys, 3- or 4-bit values, Hadamard rotation
+template <int kNQ, int kW, int kDepth, bool kKW, bool kVW, bool kHad>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kW / 4)))
 void decode_kernel(const DecodeParams p) {
   constexpr int kDmaPerPair = PairDma<kKW, kVW>::n;
@@ -327,6 +327,7 @@ void decode_kernel(const DecodeParams p) {
     load_seq(b_g);
   }
   const bool hadamard = p.rot_kind == 1;  // R = diag(s) H / sqrt(128): r_k, r_v hold the signs s
+  const float vmid = 0.5f * static_cast<float>((1 << p.vbits) - 1);  // middle value code
   if (!hadamard) {
     const float* R = p.r_k + (static_cast<size_t>(h) * kHeadDim + kRows * rpart) * kHeadDim + rc;
 #pragma unroll
@@ -771,6 +772,15 @@ void decode_kernel(const DecodeParams p) {
         z_run[Q] *= alpha;
         m_run[Q] = m_new;
       }
+      // A = p * s_v as fp16.  Its rounding error times the codes would, in the
+      // sum over tokens, leave an error common to the 32 channels of a group
+      // (the code part of the value sum largely cancels against the zero-point
+      // part, z_v being about the group's minimum); a Hadamard R_V^T gathers
+      // such an error into single output channels, where it came within a few
+      // percent of the 2e-3 gate.  With a Hadamard R the rounding error times
+      // the middle code goes into the zero-point sum instead, so what is left
+      // multiplies (code - middle), which has no common part.  A dense R
+      // spreads the error over all channels and needs no correction.
       half8 pA;
 #pragma unroll
       for (int X = 0; X < 2; ++X)
@@ -780,7 +790,14 @@ void decode_kernel(const DecodeParams p) {
           const uint32_t vm = X ? P.vm1[i] : P.vm0[i];
           l_run[Q] += pr;
           z_run[Q] = fmaf(f16_hi(vm), pr, z_run[Q]);
-          pA[4 * X + i] = static_cast<_Float16>(fmaf(f16_lo(vm), pr, 0.0f));
+          if (kHad) {
+            const float ps = f16_lo(vm) * pr;
+            const _Float16 hi = static_cast<_Float16>(ps);
+            pA[4 * X + i] = hi;
+            z_run[Q] = fmaf(vmid, ps - static_cast<float>(hi), z_run[Q]);
+          } else {
+            pA[4 * X + i] = static_cast<_Float16>(fmaf(f16_lo(vm), pr, 0.0f));
+          }
         }
 #pragma unroll
       for (int t = 0; t < 8; ++t) acc[Q][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pA, vB[t], acc[Q][t], 0, 0, 0);
@@ -1314,7 +1331,9 @@ static hipError_t launch_one(const DecodeParams& prm, hipStream_t stream, hipEve
   constexpr int kD = DecodeShape<kNQ, 3 + kKW + kVW>::depth;
   DecodeParams arg = prm;
   void* args[] = {&arg};
-  return hipExtLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<kNQ, kW, kD, kKW, kVW>),
+  const void* kern = prm.rot_kind == 1 ? reinterpret_cast<const void*>(&decode_kernel<kNQ, kW, kD, kKW, kVW, true>)
+                                       : reinterpret_cast<const void*>(&decode_kernel<kNQ, kW, kD, kKW, kVW, false>);
+  return hipExtLaunchKernel(kern,
                             dim3((prm.balanced ? 1 : prm.batch) * prm.num_kv_heads * prm.n_splits), dim3(64 * kW),
                             args, 0, stream,
                             ev_begin, ev_end, 0);

@@ -62,7 +62,8 @@ def test_decode_parity(shape):
     dc = DeviceCase(case, dev)
     dc.append(rot_out=False)
     ref = O.decode_attention(case.q, dc.pool_np(), case.Hkv, case.page_table, case.seq_lens, r_k, r_v)
-    for ns in (0, 3):
+    # one split (the longest per-wave sums) is where fp16 P.V operands alone came closest to the gate
+    for ns in (0, 1, 3, 7):
         got = dc.decode("f32", num_splits=ns)
         assert max_abs_rel(got, ref) <= TOL, ns
 
