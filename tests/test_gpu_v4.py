@@ -80,6 +80,26 @@ def test_decode_parity(shape, kb, vb):
     assert np.array_equal(got16, I.bf16_bits(dc.decode("f32").astype(np.float32)))
 
 
+@pytest.mark.parametrize("kb,vb", [(2, 3), (4, 4)], ids=lambda b: str(b))
+@pytest.mark.parametrize("shape", [(2, 32, 8, [1000, 257]), (2, 64, 8, [513, 1024]), (1, 16, 1, [300])],
+                         ids=lambda s: f"B{s[0]}_Hq{s[1]}_Hkv{s[2]}_T{'-'.join(map(str, s[3]))}")
+def test_hadamard_decode_parity(shape, kb, vb):
+    """A Hadamard R_V with wide values: the kernel's correction for the fp16 rounding of p * s_v is taken about
+    the tensor's own middle code (3.5 or 7.5), and one split per sequence gives the longest sums."""
+    dev = require_gpu()
+    B, Hq, Hkv, lens = shape
+    case = I.make_case("v4h", 430 + sum(lens) + Hq + kb, B=B, Hq=Hq, Hkv=Hkv, seq_lens=lens,
+                       table_policy="interleaved", rotation="hadamard")
+    r_k, r_v = dense_rotations(case)
+    dc = DeviceCase(case, dev, key_bits=kb, val_bits=vb)
+    dc.append(rot_out=False)
+    ref = O.decode_attention(case.q, dc.pool_np(), case.Hkv, case.page_table, case.seq_lens, r_k, r_v,
+                             key_bits=kb, val_bits=vb)
+    for ns in (0, 1, 3):
+        got = dc.decode("f32", num_splits=ns)
+        assert max_abs_rel(got, ref) <= TOL, ns
+
+
 @pytest.mark.parametrize("shape", [(2, 32, 8, [1000, 17], "bf16"), (2, 64, 8, [513, 16], "f32"),
                                    (1, 16, 1, [300], "bf16"), (3, 8, 2, [0, 5, 100], "bf16")],
                          ids=lambda s: f"Hq{s[1]}_Hkv{s[2]}_{s[4]}")
