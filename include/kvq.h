@@ -176,6 +176,14 @@ size_t kvq_pool_bytes(const kvq_cache* cache);
  *             value) exactly as the kernel quantized them.  NULL = not written.
  * Writes the K/V codes and fp16 scale/zero of every (token, KV head) into its
  * slot.  Other slots of the same page keep their contents.
+ * Input range: every rotated value (k - mu) R_K and v R_V must be finite with
+ * |x| <= 65504, and every Q2 group's (max - min) / 3 (times c) at most 65504,
+ * so that the fp16 scale and zero are finite; outside that the stored bytes
+ * are unspecified.  Inside it every path takes any finite input: fewer than 64
+ * raw tokens are rotated with fp32 fused multiply-adds, 64 or more on the
+ * matrix cores, each row scaled by its own power of two before it is split
+ * into fp16 parts (so no magnitude overflows the split, and the rotation stays
+ * within the fp32 rounding bound of a 128-term dot product).
  * Errors: KVQ_EINVAL (NULL cache/pool/k/v/slots, NULL r_k or r_v unless
  * pre-rotated, n_tokens < 0, clip_ratio outside [0, 1], unknown rotation), KVQ_EUNSUPPORTED
  * (geometry), KVQ_EHIP.
@@ -259,6 +267,17 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
  *               from the cache.  The buffer's slots of every window position
  *               must hold that position's key and value (kvq_window_fill,
  *               kvq_decode_step).  Supported for g <= 8.
+ * Value range: every scale and zero the cache format stores (any finite fp16).
+ * The P.V product runs on the matrix cores with the fp16 operand p * s_v (p a
+ * softmax weight, s_v a value group's scale); the kernel keeps that operand in
+ * a power-of-two unit per value group, chosen from the largest scale of each
+ * run of 32 positions, so it never overflows and, for the positions with that
+ * scale, stays normal.  Precision limit: when, within 32 consecutive positions
+ * (one page pair) of one value group, the scales span more than about 2^20
+ * and the positions with the largest scales weigh less than about 2^-20 of
+ * the others, those others' share of the value sum loses precision (an fp16
+ * subnormal operand).  Stale slots past a sequence's end and absent pages may
+ * hold any bytes: they weigh nothing.
  * Work decomposition: one kernel launch; one workgroup per compute unit
  * (12 waves for g <= 4, 8 for g <= 8, else 4) streams a split's pages, and
  * the last workgroup of each (sequence, KV head) merges the split partials

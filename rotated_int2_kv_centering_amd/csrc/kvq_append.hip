@@ -202,7 +202,7 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
       const int r0 = n0 + 16 * (kBulkWaves * m + wave);  // this wave's first token
       if (m + 1 < kBulkRounds) load_raw(m + 1, next);
       half8 a_hi[4], a_lo[4];
-      float ah[4][8];  // Hadamard: the centred, sign-flipped row values
+      float ah[4][8];  // the centred row values (Hadamard: also sign-flipped)
   #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         float a[8];
@@ -220,20 +220,38 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
           }
         }
   #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          if (kRot == 0) {
-            _Float16 hh, ll;
-            split_f16(a[e] - cen[kb][e], hh, ll);  // key centering (fp32); values use centre 0
-            a_hi[kb][e] = hh;
-            a_lo[kb][e] = ll;
-          } else {
-            ah[kb][e] = (a[e] - cen[kb][e]) * sgn[kb][e];
-          }
-        }
+        for (int e = 0; e < 8; ++e)  // key centering (fp32); values use centre 0
+          ah[kb][e] = kRot == 0 ? a[e] - cen[kb][e] : (a[e] - cen[kb][e]) * sgn[kb][e];
       }
       if (kRot == 0) {
+        // the row's split scale from its largest magnitude (its 128 values over
+        // the four lanes 16 kq + row), and the unscale of output rows 4 (lane/16) + i
+        float amax = 0.0f;
+  #pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(ah[kb][e]));
+        float u0, u1;
+        swap16(amax, u0, u1);
+        amax = fmaxf(u0, u1);
+        swap32(amax, u0, u1);
+        amax = fmaxf(u0, u1);
+        const float rs = row_split_scale(amax);
+  #pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+  #pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            _Float16 hh, ll;
+            split_f16(ah[kb][e], rs, hh, ll);
+            a_hi[kb][e] = hh;
+            a_lo[kb][e] = ll;
+          }
+        const float inv = 1.0f / (rs * kRotScale);  // a power of two: exact
+        float unscale[4];
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) unscale[i] = __shfl(inv, 4 * (lane >> 4) + i);  // lane r holds row r
         float4v C[8];
-        rotate16(a_hi, a_lo, s_op, lane, C);
+        rotate16(a_hi, a_lo, s_op, lane, unscale, C);
   #pragma unroll
         for (int nt = 0; nt < 8; ++nt)
   #pragma unroll

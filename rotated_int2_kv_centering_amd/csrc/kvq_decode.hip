@@ -627,13 +627,28 @@ void decode_kernel(const DecodeParams p) {
     }
   }
 
-  float m_run[kNQ], l_run[kNQ], z_run[kNQ];
+  // Online-softmax state per quad.  m_run: the reference max of the lane's head
+  // (log2 units); thr = (m_run + kLazy) / c1, the logit (in MFMA units) above
+  // which the reference must move.  The P.V operand p * s_v is kept in units
+  // of 2^e_u, e_u per value group (the lane's group grp, shared by the quads):
+  // weights are formed as exp2(logit - m_run - e_u), so l_run, z_run and acc
+  // hold 2^-e_u times their value.  e_u keeps the page pair's largest value
+  // scale s_v of the group within [2^(e_u-3), 2^(e_u+7)); moving it (rarely)
+  // rescales the sums.  With weights <= 2^kLazy the fp16 operand then stays
+  // below 2^15, for every scale the cache format stores, and the group's
+  // largest scale gives operands of at least p * 2^-3 (normal down to
+  // p = 2^-11).  m_adj = m_run + e_u is the exp2 argument's offset.
+  float m_run[kNQ], l_run[kNQ], z_run[kNQ], m_adj[kNQ], thr[kNQ];
+  float e_u = 0.0f;
+  _Float16 u_hi = static_cast<_Float16>(128.0f), u_lo = static_cast<_Float16>(0.125f);  // 2^(e_u+7), 2^(e_u-3)
   float4v acc[kNQ][8];
 #pragma unroll
   for (int Q = 0; Q < kNQ; ++Q) {
     m_run[Q] = kNegBig;
     l_run[Q] = 0.0f;
     z_run[Q] = 0.0f;
+    m_adj[Q] = kNegBig;
+    thr[Q] = -INFINITY;  // the first pair with a live position sets the reference
 #pragma unroll
     for (int t = 0; t < 8; ++t) acc[Q][t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
   }
@@ -720,6 +735,19 @@ void decode_kernel(const DecodeParams p) {
             if (!(page_ok && pos0 + i >= int2_lo && pos0 + i < int2_hi)) sp[Q][X][i] = -INFINITY;
         }
       }
+      // A masked position (stale slot, absent page, window position) weighs 0;
+      // its value metadata may hold any bits, so it is cleared (0 * inf would
+      // be NaN in the P.V operand and the zero-point sum).
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (!(page_ok && pos0 + i >= int2_lo && pos0 + i < int2_hi)) {
+            if (X)
+              P.vm1[i] = 0u;
+            else
+              P.vm0[i] = 0u;
+          }
+      }
     }
 
     // Value operands: tile t holds channels 16t..16t+15.  Tiles 0-3 sit in the
@@ -741,21 +769,70 @@ void decode_kernel(const DecodeParams p) {
       vB[t] = __builtin_bit_cast(half8, rr);
     }
 
+    // The P.V operand's unit per value group, from the pair's value scales
+    // (lane: its group's scales of 8 positions; masked ones are 0): any scale
+    // at or above 2^(e_u+7), or a group whose scales are all below 2^(e_u-3)
+    // but not all zero, moves that group's unit so that its largest scale
+    // lies in [2^6, 2^7) units, and rescales the sums kept in the old unit.
+    {
+      auto s16 = [](uint32_t w) { return __builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)); };
+      _Float16 smx = s16(P.vm0[0]);
+#pragma unroll
+      for (int i = 1; i < 4; ++i) smx = __builtin_fmaxf16(smx, s16(P.vm0[i]));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) smx = __builtin_fmaxf16(smx, s16(P.vm1[i]));
+      const uint64_t b_hi = __ballot(smx >= u_hi);
+      const uint64_t b_lo = __ballot(smx >= u_lo);
+      const uint64_t b_nz = __ballot(smx > static_cast<_Float16>(0.0f));
+      // bit 4 grp of fold(b): some lane of group grp (lanes 16 a + 4 grp + jj) is set
+      auto fold = [](uint64_t b) {
+        b |= b >> 32;
+        b |= b >> 16;
+        b |= b >> 1;
+        b |= b >> 2;
+        return b & 0x1111ull;
+      };
+      if ((b_hi | (fold(b_nz) & ~fold(b_lo))) != 0) {  // rare
+        float gs = static_cast<float>(smx);           // the group's largest scale
+        gs = fmaxf(gs, dpp_f32<QuadXor1::ctrl>(gs));
+        gs = fmaxf(gs, dpp_f32<QuadXor2::ctrl>(gs));
+        gs = rows_max(gs);
+        int ex = 0;
+        frexpf(gs, &ex);  // gs in [2^(ex-1), 2^ex)
+        const bool move = gs >= static_cast<float>(u_hi) || (gs < static_cast<float>(u_lo) && gs > 0.0f);
+        const float e_new = move ? static_cast<float>(ex - 7) : e_u;
+        const float fl = ldexpf(1.0f, static_cast<int>(e_u - e_new));  // old unit / new unit, this lane's group
+        const float fa = __shfl(fl, 4 * a);                              // the same for acc rows of group a
+#pragma unroll
+        for (int Q = 0; Q < kNQ; ++Q) {
+#pragma unroll
+          for (int t = 0; t < 8; ++t) acc[Q][t] *= fa;
+          l_run[Q] *= fl;
+          z_run[Q] *= fl;
+          m_adj[Q] = m_run[Q] + e_new;
+        }
+        e_u = e_new;
+        u_hi = static_cast<_Float16>(ldexpf(1.0f, static_cast<int>(e_u) + 7));  // inf past fp16: never reached
+        u_lo = static_cast<_Float16>(ldexpf(1.0f, static_cast<int>(e_u) - 3));  // 0 below fp16: no lower unit
+      }
+    }
+
     // online softmax and P.V per quad
 #pragma unroll
     for (int Q = 0; Q < kNQ; ++Q) {
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int X = 0; X < 2; ++X)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mloc = fmaxf(mloc, sp[Q][X][i]);
-      mloc = rows_max(mloc);
       // Lazy rescaling: the reference max moves only when some head's logits
       // exceed it by more than kLazy (log2 units), so the weights
       // exp2(logit - m_run) stay <= 2^kLazy and most pairs skip the rescale.
-      const float m_cand = mloc * c1[Q];
-      if (__ballot(m_cand > m_run[Q] + kLazy) != 0) {
-        const float m_new = fmaxf(m_run[Q], m_cand);
+      // The test is lane-local against thr (c1 is a power of two, so
+      // logit * c1 > m_run + kLazy exactly when logit > thr); only a pair that
+      // moves the reference reduces its maximum across the rows.
+      float smax = sp[Q][0][0];
+#pragma unroll
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) smax = fmaxf(smax, sp[Q][X][i]);
+      if (__ballot(smax > thr[Q]) != 0) {
+        const float m_new = fmaxf(m_run[Q], rows_max(smax) * c1[Q]);
         const float alpha = __builtin_amdgcn_exp2f(m_run[Q] - m_new);
         const float al0 = dpp_f32<QuadBcast<0>::ctrl>(alpha);
         const float al1 = dpp_f32<QuadBcast<1>::ctrl>(alpha);
@@ -771,22 +848,25 @@ void decode_kernel(const DecodeParams p) {
         l_run[Q] *= alpha;
         z_run[Q] *= alpha;
         m_run[Q] = m_new;
+        m_adj[Q] = m_new + e_u;
+        thr[Q] = (m_new + kLazy) * (1.0f / c1[Q]);
       }
-      // A = p * s_v as fp16.  Its rounding error times the codes would, in the
-      // sum over tokens, leave an error common to the 32 channels of a group
-      // (the code part of the value sum largely cancels against the zero-point
-      // part, z_v being about the group's minimum); a Hadamard R_V^T gathers
-      // such an error into single output channels, where it came within a few
-      // percent of the 2e-3 gate.  With a Hadamard R the rounding error times
-      // the middle code goes into the zero-point sum instead, so what is left
-      // multiplies (code - middle), which has no common part.  A dense R
-      // spreads the error over all channels and needs no correction.
+      // A = p * s_v as fp16, in units of 2^e_u.  Its rounding error times the
+      // codes would, in the sum over tokens, leave an error common to the 32
+      // channels of a group (the code part of the value sum largely cancels
+      // against the zero-point part, z_v being about the group's minimum); a
+      // Hadamard R_V^T gathers such an error into single output channels, where
+      // it came within a few percent of the 2e-3 gate.  With a Hadamard R the
+      // rounding error times the middle code goes into the zero-point sum
+      // instead, so what is left multiplies (code - middle), which has no
+      // common part.  A dense R spreads the error over all channels and needs
+      // no correction.
       half8 pA;
 #pragma unroll
       for (int X = 0; X < 2; ++X)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float pr = __builtin_amdgcn_exp2f(fmaf(sp[Q][X][i], c1[Q], -m_run[Q]));
+          const float pr = __builtin_amdgcn_exp2f(fmaf(sp[Q][X][i], c1[Q], -m_adj[Q]));
           const uint32_t vm = X ? P.vm1[i] : P.vm0[i];
           l_run[Q] += pr;
           z_run[Q] = fmaf(f16_hi(vm), pr, z_run[Q]);
@@ -821,16 +901,20 @@ void decode_kernel(const DecodeParams p) {
   //      32a + 16 + b (tiles 2a, 2a+1) for the four heads of each quad.
 #pragma unroll
   for (int Q = 0; Q < kNQ; ++Q) {
-    const float lsum = rows_sum(l_run[Q]);
-    const float zsum = rows_sum(z_run[Q]);  // lane (., grp, jj): sum_s p z_v for (jj, grp)
+    // the sums were kept in units of 2^e_u of the lane's value group: lanes
+    // 0..3 (group 0) carry the weight sums, acc rows of group a take group a's unit
+    const float unit = ldexpf(1.0f, static_cast<int>(e_u));
+    const float unit_a = __shfl(unit, 4 * a);
+    const float lsum = rows_sum(l_run[Q]) * unit;
+    const float zsum = rows_sum(z_run[Q]) * unit;  // lane (., grp, jj): sum_s p z_v for (jj, grp)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float zi = __shfl(zsum, 4 * a + i);  // zero part of head i, group a
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        if ((t >> 1) == a)  // undo the tile's code factor 4^(t%4) and the 2^-24 code scale
+        if ((t >> 1) == a)  // undo the tile's code factor 4^(t%4), the 2^-24 code scale and the unit
           s_post[(wave * kNH + 4 * Q + i) * kHeadDim + 16 * t + col] =
-              acc[Q][t][i] * (kTwo24 / static_cast<float>(1 << (2 * (t & 3)))) + zi;
+              acc[Q][t][i] * ((kTwo24 / static_cast<float>(1 << (2 * (t & 3)))) * unit_a) + zi;
       }
     }
     if (lane < 4) {

@@ -63,6 +63,9 @@ constexpr int kDppRowRor4 = 0x124;
 constexpr int kDppRowRor8 = 0x128;
 template <int kLane>
 struct QuadBcast { static constexpr int ctrl = kLane | (kLane << 2) | (kLane << 4) | (kLane << 6); };
+// quad_perm [1,0,3,2] and [2,3,0,1]: the lane paired by bit 0, by bit 1
+struct QuadXor1 { static constexpr int ctrl = 1 | (0 << 2) | (3 << 4) | (2 << 6); };
+struct QuadXor2 { static constexpr int ctrl = 2 | (3 << 2) | (0 << 4) | (1 << 6); };
 
 // Sum over the lanes {n, n^4, n^8, n^12} of each 16-lane row (lane bits 2..3).
 __device__ __forceinline__ float row_sum_stride4(float x) {

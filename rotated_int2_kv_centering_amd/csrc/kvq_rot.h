@@ -2,9 +2,14 @@
 // quantize-append (OptR, section 3.1, Eq. (4): the cache stores Q2(zR)).
 //
 // Precision.  Both operands are split into fp16 pairs, a = a_hi + a_lo and
-// R = R_hi + R_lo (each part rounded to nearest), after scaling a and R by
-// 2^4 (exact) so that the low parts of small values stay normal.  The product
-// is a_hi R_hi + a_hi R_lo + a_lo R_hi accumulated in fp32 by
+// R = R_hi + R_lo (each part rounded to nearest).  R (entries at most 1 in
+// magnitude) is scaled by 2^10, so that the low parts of its entries stay
+// normal down to 2^-13; each row a is scaled by its own power of two 2^k,
+// chosen so that the row's largest magnitude lands in [2^9, 2^10): any finite
+// fp32 row then splits without overflow, and the low parts of the values that
+// matter stay normal.  Both scalings are exact and are undone on the product
+// (products stay below 2^20, sums of 128 below 2^27).  The product is
+// a_hi R_hi + a_hi R_lo + a_lo R_hi accumulated in fp32 by
 // v_mfma_f32_16x16x32_f16; the dropped a_lo R_lo and the rounding of the
 // parts are about 2^-21 of sum |a| |R|, far inside the fp32 error bound of a
 // sequential dot product (about 2^-16 of that sum for 128 terms).
@@ -20,14 +25,21 @@
 
 namespace kvq {
 
-constexpr float kRotScale = 16.0f;          // applied to a and to R before the split
-constexpr float kRotUnscale = 1.0f / 256.0f;
+constexpr float kRotScale = 1024.0f;  // applied to R before the split
 
-// The fp16 pair of v * 2^4.
-__device__ __forceinline__ void split_f16(float v, _Float16& hi, _Float16& lo) {
-  const float s = v * kRotScale;
+// The fp16 pair of v * scale (scale a power of two).
+__device__ __forceinline__ void split_f16(float v, float scale, _Float16& hi, _Float16& lo) {
+  const float s = v * scale;
   hi = static_cast<_Float16>(s);
   lo = static_cast<_Float16>(s - static_cast<float>(hi));
+}
+
+// The power of two that brings a row whose largest magnitude is amax into
+// [2^9, 2^10) (1 for an all-zero row).
+__device__ __forceinline__ float row_split_scale(float amax) {
+  int ex = 0;
+  frexpf(amax, &ex);  // amax in [2^(ex-1), 2^ex)
+  return amax > 0.0f ? ldexpf(1.0f, 10 - ex) : 1.0f;
 }
 
 // R operands in LDS: op[((kb * 8 + nt) * 2 + part) * 64 + lane], part 0 = hi,
@@ -46,7 +58,7 @@ __device__ __forceinline__ void stage_rotation(const float* __restrict__ R, half
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       _Float16 h, l;
-      split_f16(v[e], h, l);
+      split_f16(v[e], kRotScale, h, l);
       hi[e] = h;
       lo[e] = l;
     }
@@ -56,11 +68,12 @@ __device__ __forceinline__ void stage_rotation(const float* __restrict__ R, half
 }
 
 // x = a R for the 16 rows held in A-operand layout (a_hi/a_lo[kb] per lane);
-// C[nt] receives output tile nt, already unscaled.  Every tile accumulates
+// C[nt] receives output tile nt, multiplied by unscale[i] in row 4 (lane/16) + i
+// (the inverse of that row's split scale times 2^-10).  Every tile accumulates
 // hi*hi, hi*lo, lo*hi for kb = 0, 1, 2, 3 in that order; the tiles are
 // interleaved so that consecutive MFMAs never depend on each other.
 __device__ __forceinline__ void rotate16(const half8 (&a_hi)[4], const half8 (&a_lo)[4], const half8* op, int lane,
-                                         float4v (&C)[8]) {
+                                         const float (&unscale)[4], float4v (&C)[8]) {
   float4v acc[8];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) acc[nt] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
@@ -85,7 +98,7 @@ __device__ __forceinline__ void rotate16(const half8 (&a_hi)[4], const half8 (&a
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) C[nt][i] = acc[nt][i] * kRotUnscale;
+    for (int i = 0; i < 4; ++i) C[nt][i] = acc[nt][i] * unscale[i];
 }
 
 }  // namespace kvq

@@ -502,6 +502,28 @@ def test_window_positions_brute_force():
     assert np.abs(a[0] - b_[0]).max() > 1e-6
 
 
+def test_window_slots_golden(golden_dir):
+    """window_slot and window_mask against hand-derived slots and positions
+    (tests/golden/window_slots.txt).  A ring over the recent positions started at
+    the first recent position (sinks + (t - sinks) mod recent) would differ."""
+    n_slot = n_mask = 0
+    with open(os.path.join(golden_dir, "window_slots.txt")) as f:
+        for line in f:
+            f_ = line.split()
+            if not f_ or f_[0].startswith("#"):
+                continue
+            if f_[0] == "slot":
+                sinks, recent, t, slot = map(int, f_[1:])
+                assert O.window_slot(t, sinks, recent) == slot, line
+                n_slot += 1
+            else:
+                sinks, recent, T = map(int, f_[1:4])
+                want = [int(x) for x in f_[4:]]
+                assert list(np.nonzero(O.window_mask(T, sinks, recent))[0]) == want, line
+                n_mask += 1
+    assert n_slot >= 20 and n_mask >= 6
+
+
 def test_window_slots_are_distinct():
     """Within any length, the window positions map to distinct slots of the buffer."""
     for sinks, recent in ((4, 128), (0, 5), (3, 1), (8, 0), (2, 16)):
