@@ -218,9 +218,13 @@ kvq_status kvq_quant_append_err(const kvq_cache* cache, const void* k, const voi
  * The workspace holds per-(sequence, KV head) ticket counters, the split
  * partials and one row per output row for an exact window's part (used when a
  * window is given).  It must be zero-filled before its first use; every completed
- * call leaves the counters at zero again, so a workspace is then reusable
- * without clearing.  Calls that share one workspace must not overlap in time
- * (same stream, or ordered by events).
+ * call leaves the counters at zero again.  The counters take a fixed prefix of
+ * 16 KiB for any call with batch * num_kv_heads <= 4096, so a workspace is
+ * reusable without clearing by every such call, whatever its shape; a call
+ * with more (sequence, KV head) pairs uses a longer prefix, and a workspace
+ * whose calls change that length must be zero-filled again in between.  Calls
+ * that share one workspace must not overlap in time (same stream, or ordered
+ * by events).
  */
 size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t max_seq_len, int32_t num_splits);
@@ -349,7 +353,9 @@ kvq_status kvq_decode_step(const kvq_cache* cache, const void* k_new, const void
  * kvq_output_error for the same (batch, num_q_heads, num_kv_heads,
  * max_seq_len, d_model); 0 on invalid input (batch above 64 included).  It
  * holds ticket counters, split partials and the readout differences; zero-fill
- * it before its first use (completed calls leave the counters at zero).
+ * it before its first use (completed calls leave the counters at zero, in
+ * fixed prefixes for up to 4096 workgroup tickets (batch * num_kv_heads *
+ * ceil(g / 8)) and 1024 query heads, so such calls of any shape can reuse it).
  */
 size_t kvq_output_error_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t max_seq_len, int32_t d_model);

@@ -6,6 +6,7 @@ The libraries are written next to this file; every call recompiles.
 
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -15,7 +16,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_eval.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_decode_g8.hip", "kvq_decode_g16.hip",
+           "kvq_eval.hip"]
 # measurement aid (HBM read-rate probe), a library of its own outside the decode path
 PROBE_LIB = os.path.join(HERE, "libkvq_probe.so")
 PROBE_SOURCES = ["hbm_probe.hip"]
@@ -39,10 +41,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libkvq)")
 
 
-def _link(sources, lib: str, verbose: bool) -> str:
-    out_tmp = lib + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, "-shared", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in sources], "-o", out_tmp]
+def _run(cmd, verbose: bool):
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,6 +52,20 @@ def _link(sources, lib: str, verbose: bool) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
+
+
+def _link(sources, lib: str, verbose: bool) -> str:
+    """Compile every source to an object (in parallel), then link the shared library."""
+    obj_dir = os.path.join(HERE, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    objs = [os.path.join(obj_dir, os.path.splitext(s)[0] + ".o") for s in sources]
+    jobs = [[hipcc(), *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(sources, objs)]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1, 8)) as ex:
+        for f in [ex.submit(_run, j, verbose) for j in jobs]:
+            f.result()
+    out_tmp = lib + ".tmp"
+    _run([hipcc(), *HIP_FLAGS, "-shared", *objs, "-o", out_tmp], verbose)
     os.replace(out_tmp, lib)
     return lib
 

@@ -168,8 +168,15 @@ bool make_plan(int batch, int num_kv_heads, int g, int max_seq_len, int num_spli
   return true;
 }
 
+// The merge tickets take a fixed prefix of the workspace, sized for up to
+// kCounterSlots (sequence, KV head) pairs whatever the call's batch, so a
+// workspace reused for another shape finds them where every completed call
+// leaves them: at zero (a layout that moved with the batch would put one
+// call's split partials where a later call reads its tickets).
+constexpr size_t kCounterSlots = 4096;
 size_t counters_bytes(int batch, int num_kv_heads) {
-  return (static_cast<size_t>(batch) * num_kv_heads * sizeof(int32_t) + 255) / 256 * 256;
+  const size_t n = std::max(static_cast<size_t>(batch) * num_kv_heads, kCounterSlots);
+  return (n * sizeof(int32_t) + 255) / 256 * 256;
 }
 
 // Workspace: merge counters, split partial rows, then one window row per output
@@ -222,7 +229,7 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
                          const int32_t* page_table, int32_t max_pages, const int32_t* seq_lens, int32_t max_seq_len,
                          const float* r_k, const float* r_v, float sm_scale, void* out, kvq_dtype out_dtype,
                          void* workspace, size_t workspace_bytes_, int32_t num_splits, const kvq_window* window,
-                         void* stream, void* ev_begin, void* ev_end) {
+                         void* stream, void* ev_begin, void* ev_end, size_t ticket_bytes = 0) {
   kvq_status st = check_cache(cache);
   if (st != KVQ_OK) return st;
   if (batch < 0) return fail(KVQ_EINVAL, "batch=%d must be >= 0", batch);
@@ -267,7 +274,13 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
   if (!make_plan(batch, cache->num_kv_heads, g, max_seq_len, num_splits, &plan,
                  win ? max_splits_with_window(g) : kMaxSplits, static_cast<int>(stepping) + static_cast<int>(win)))
     return fail(KVQ_EINVAL, "cannot plan the decode split");
-  const size_t need = workspace_bytes(batch, num_q_heads, cache->num_kv_heads, plan);
+  // the tickets' prefix: the caller workspace's, or a fixed one (static workspace)
+  const size_t tickets = ticket_bytes != 0 ? ticket_bytes : counters_bytes(batch, cache->num_kv_heads);
+  if (static_cast<size_t>(batch) * cache->num_kv_heads * sizeof(int32_t) > tickets)
+    return fail(KVQ_ENOSPACE, "batch * num_kv_heads = %lld exceeds the %zu tickets of the workspace",
+                static_cast<long long>(batch) * cache->num_kv_heads, tickets / sizeof(int32_t));
+  const size_t need = workspace_bytes(batch, num_q_heads, cache->num_kv_heads, plan) -
+                      counters_bytes(batch, cache->num_kv_heads) + tickets;
   if (workspace_bytes_ < need)
     return fail(KVQ_ENOSPACE, "workspace of %zu bytes is smaller than the %zu bytes needed", workspace_bytes_, need);
   if (static_cast<long long>(plan.balanced ? 1 : batch) * cache->num_kv_heads * plan.n_splits > 0x7fffffffLL)
@@ -292,7 +305,7 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
   a.out = out;
   a.out_kind = out_dtype == KVQ_BF16 ? 0 : 1;
   a.counters = static_cast<int32_t*>(workspace);
-  a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + counters_bytes(batch, cache->num_kv_heads));
+  a.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + tickets);
   a.len_cap = static_cast<int>(std::min<long long>(max_seq_len, static_cast<long long>(max_pages) * kPage));
   a.balanced = plan.balanced ? 1 : 0;
   a.pages_per_split = plan.pages_per_split;
@@ -304,7 +317,7 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
   a.win_sinks = win ? window->sinks : 0;
   a.win_recent = win ? window->recent : 0;
   a.win_mu = win ? window->mu : nullptr;
-  a.win_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + counters_bytes(batch, cache->num_kv_heads) +
+  a.win_part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + tickets +
                                         split_rows_bytes(batch, num_q_heads, plan));
   a.k_new = stepping ? k_new : nullptr;
   a.v_new = stepping ? v_new : nullptr;
@@ -343,9 +356,11 @@ bool make_eval_plan(int batch, int num_q_heads, int num_kv_heads, int max_seq_le
   e->n_chunks = (d_model + kvq::kProjRows - 1) / kvq::kProjRows;
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   const size_t slots = static_cast<size_t>(batch) * num_kv_heads * e->n_hc;
+  // both ticket arrays in fixed prefixes (as for decode): up to 4096 workgroup
+  // tickets and 1024 projection tickets keep one layout across shapes
   e->counters_off = 0;
-  e->proj_counters_off = up(slots * 4);
-  e->part_off = e->proj_counters_off + up(static_cast<size_t>(num_q_heads) * 4);
+  e->proj_counters_off = up(std::max<size_t>(slots, 4096) * 4);
+  e->part_off = e->proj_counters_off + up(std::max<size_t>(num_q_heads, 1024) * 4);
   e->dobuf_off = e->part_off + up(slots * e->n_splits * kvq::kEvHeads * kvq::kEvPartStride * 4);
   e->echunk_off = e->dobuf_off + up(static_cast<size_t>(batch) * num_q_heads * 2 * kHeadDim * 4);
   e->total = e->echunk_off + up(static_cast<size_t>(num_q_heads) * e->n_chunks * kvq::kMaxEvalBatch * 4);

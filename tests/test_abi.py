@@ -37,7 +37,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["kvq_pool_bytes", "kvq_quant_append", "kvq_quant_append_err", "kvq_decode_workspace_bytes",
-                            "kvq_decode_attn", "kvq_decode_attn_traced", "kvq_decode_step", "kvq_window_bytes",
+                            "kvq_decode_attn", "kvq_decode_attn_traced", "kvq_decode_step",
+                            "kvq_window_bytes",
                             "kvq_window_fill", "kvq_output_error_workspace_bytes", "kvq_output_error",
                             "kvq_page_table", "kvq_last_error"]), names
 
@@ -63,27 +64,37 @@ def test_pool_bytes(K):
     assert K.kvq_pool_bytes(K.make_cache(8, 0)) == 0
 
 
+CTR = 4096 * 4  # the fixed ticket prefix
+
+
 def test_workspace_bytes_with_explicit_splits(K):
-    # counters (B*Hkv int32, padded to 256 B) + B*Hq*n_splits partial rows of 132 floats
-    # + B*Hq window rows of 132 floats; 1000 tokens = 63 pages: 7 splits of 9 pages
-    assert K.kvq_decode_workspace_bytes(2, 8, 2, 1000, 7) == 256 + 4 * 2 * 8 * 7 * 132 + 4 * 2 * 8 * 132
+    # counters (a fixed 16 KiB prefix: up to 4096 (sequence, KV head) int32 tickets)
+    # + B*Hq*n_splits partial rows of 132 floats + B*Hq window rows of 132 floats;
+    # 1000 tokens = 63 pages: 7 splits of 9 pages
+    assert K.kvq_decode_workspace_bytes(2, 8, 2, 1000, 7) == CTR + 4 * 2 * 8 * 7 * 132 + 4 * 2 * 8 * 132
     # a request of more splits than pages gives one page per split
-    assert K.kvq_decode_workspace_bytes(1, 4, 1, 40, 16) == 256 + 4 * 1 * 4 * 3 * 132 + 4 * 4 * 132
+    assert K.kvq_decode_workspace_bytes(1, 4, 1, 40, 16) == CTR + 4 * 1 * 4 * 3 * 132 + 4 * 4 * 132
     # at most 512 splits: pages per split grow instead
     big = 600 * 16
-    assert K.kvq_decode_workspace_bytes(1, 4, 1, big, 600) == 256 + 4 * 4 * 300 * 132 + 4 * 4 * 132
+    assert K.kvq_decode_workspace_bytes(1, 4, 1, big, 600) == CTR + 4 * 4 * 300 * 132 + 4 * 4 * 132
 
 
 def test_workspace_bytes_automatic_plan(K):
     # Automatic plan, 256 compute units: split slots per KV head
     # S = min(B * ceil(pages / pps_min), max(ceil(256 / H_kv), ceil(B * pages / 2048)) + B - 1),
     # pps_min = max(8, ceil(pages / 512)); partial rows = H_q * S; window rows = B * H_q.
-    assert K.kvq_decode_workspace_bytes(1, 32, 8, 131072, 0) == 256 + 4 * 32 * 32 * 132 + 4 * 32 * 132
-    assert K.kvq_decode_workspace_bytes(16, 32, 8, 65536, 0) == 512 + 4 * 32 * (32 + 15) * 132 + 4 * 16 * 32 * 132
+    assert K.kvq_decode_workspace_bytes(1, 32, 8, 131072, 0) == CTR + 4 * 32 * 32 * 132 + 4 * 32 * 132
+    assert K.kvq_decode_workspace_bytes(16, 32, 8, 65536, 0) == CTR + 4 * 32 * (32 + 15) * 132 + 4 * 16 * 32 * 132
     # one split per sequence
-    assert K.kvq_decode_workspace_bytes(3, 8, 2, 100, 0) == 256 + 4 * 8 * 3 * 132 + 4 * 3 * 8 * 132
+    assert K.kvq_decode_workspace_bytes(3, 8, 2, 100, 0) == CTR + 4 * 8 * 3 * 132 + 4 * 3 * 8 * 132
     # B = 4, 8192 pages: max(32, ceil(4 * 8192 / 2048) = 16) + 3 = 35 slots
-    assert K.kvq_decode_workspace_bytes(4, 64, 8, 131072, 0) == 256 + 4 * 64 * 35 * 132 + 4 * 4 * 64 * 132
+    assert K.kvq_decode_workspace_bytes(4, 64, 8, 131072, 0) == CTR + 4 * 64 * 35 * 132 + 4 * 4 * 64 * 132
+
+
+def test_workspace_ticket_prefix_grows_past_4096_pairs(K):
+    # batch 600 x 8 KV heads = 4800 tickets: 19200 bytes (a multiple of 256)
+    n = K.kvq_decode_workspace_bytes(600, 32, 8, 160, 1)
+    assert n == 19200 + 4 * 600 * 32 * 1 * 132 + 4 * 600 * 32 * 132
 
 
 def test_workspace_bytes_rejects_bad_shapes(K):

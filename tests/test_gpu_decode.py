@@ -178,6 +178,22 @@ def test_one_workspace_reused_across_calls_and_shapes():
         np.testing.assert_array_equal(dc.decode("f32", num_splits=ns, ws=ws), fresh[(id(dc), ns)])
 
 
+def test_workspace_reused_across_batches_beyond_one_counter_block():
+    """Shapes with more than 64 (sequence, KV head) pairs, which would spill past a
+    256-byte ticket block: a batch of 20 x 8 KV heads, a batch of one, and the
+    batch of 20 again, all through one workspace, each equal to a fresh run."""
+    import torch
+    dev = require_gpu()
+    a = DeviceCase(I.make_case("wc", 17, B=20, Hq=32, Hkv=8, seq_lens=list(range(40, 840, 40))), dev)
+    b = DeviceCase(I.make_case("wd", 18, B=1, Hq=32, Hkv=8, seq_lens=[5000]), dev)
+    for dc in (a, b):
+        dc.append(rot_out=False)
+    fresh = {id(dc): dc.decode("f32") for dc in (a, b)}
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device=dev)
+    for dc in (a, b, a, b, a):
+        np.testing.assert_array_equal(dc.decode("f32", ws=ws), fresh[id(dc)])
+
+
 def test_centering_is_invisible_to_attention_on_exact_cache():
     """OptR section 1: centering shifts every logit of a query by <q, mu>, so softmax is
     unchanged.  Keys k = mu + 0.5 * levels and values 0.25 * levels (R = I) quantize
