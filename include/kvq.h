@@ -297,6 +297,29 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const void* q, kvq_dtype q_dt
                            size_t workspace_bytes, int32_t num_splits, const kvq_window* window, void* stream);
 
 /*
+ * kvq_decode_attn_noalloc - kvq_decode_attn without a workspace argument, for
+ * callers that cannot allocate device memory (code under stream capture,
+ * serving loops or harnesses that forbid allocation).  It allocates nothing:
+ * its workspace is a static device array of 8 MiB per GPU, held by the library
+ * until the process ends, whose first 64 KiB hold the merge tickets.  The
+ * first call on a device sets the array up (its device address, and the
+ * tickets cleared by a kernel on `stream`); every completed call leaves the
+ * tickets at zero.  Every call on one GPU shares that array, so calls that
+ * overlap in time on one GPU (different streams, or threads) race; keep them
+ * ordered.
+ * Arguments, results and the other errors are those of kvq_decode_attn (same
+ * kernels, same split plan, bit-identical outputs).  KVQ_ENOSPACE when the
+ * call needs more than the array holds: batch * num_kv_heads above 16384, or
+ * split and window rows above 8 MiB - 64 KiB (for example, 32 query heads of
+ * a 128K sequence need about 0.55 MiB).
+ */
+kvq_status kvq_decode_attn_noalloc(const kvq_cache* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
+                                   int32_t num_q_heads, const int32_t* page_table, int32_t max_pages,
+                                   const int32_t* seq_lens, int32_t max_seq_len, const float* r_k, const float* r_v,
+                                   float sm_scale, void* out, kvq_dtype out_dtype, int32_t num_splits,
+                                   const kvq_window* window, void* stream);
+
+/*
  * kvq_decode_attn_traced - kvq_decode_attn plus timing events for measurement.
  * Identical arguments, results and errors; in addition, when non-NULL,
  * `ev_begin` and `ev_end` (hipEvent_t created by the caller, with timing)

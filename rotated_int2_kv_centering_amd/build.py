@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
 SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_decode.hip", "kvq_decode_g8.hip", "kvq_decode_g16.hip",
-           "kvq_eval.hip"]
+           "kvq_eval.hip", "kvq_noalloc.hip"]
 # measurement aid (HBM read-rate probe), a library of its own outside the decode path
 PROBE_LIB = os.path.join(HERE, "libkvq_probe.so")
 PROBE_SOURCES = ["hbm_probe.hip"]

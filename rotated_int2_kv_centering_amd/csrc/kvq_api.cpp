@@ -422,6 +422,39 @@ kvq_status kvq_decode_attn(const kvq_cache* cache, const void* q, kvq_dtype q_dt
                        workspace_bytes_, num_splits, window, stream, nullptr, nullptr);
 }
 
+kvq_status kvq_decode_attn_noalloc(const kvq_cache* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
+                                   int32_t num_q_heads, const int32_t* page_table, int32_t max_pages,
+                                   const int32_t* seq_lens, int32_t max_seq_len, const float* r_k, const float* r_v,
+                                   float sm_scale, void* out, kvq_dtype out_dtype, int32_t num_splits,
+                                   const kvq_window* window, void* stream) {
+  // the shape is checked against the static workspace before the device is touched
+  if (cache != nullptr && batch > 0 && cache->num_kv_heads > 0 && num_q_heads > 0 &&
+      num_q_heads % cache->num_kv_heads == 0) {
+    kvq::DecodePlan plan;
+    const int g = num_q_heads / cache->num_kv_heads;
+    if (make_plan(batch, cache->num_kv_heads, g, max_seq_len, num_splits, &plan,
+                  window_active(window) ? max_splits_with_window(g) : kMaxSplits, window_active(window) ? 1 : 0)) {
+      const size_t need = kvq::kStaticTicketBytes + split_rows_bytes(batch, num_q_heads, plan) +
+                          sizeof(float) * static_cast<size_t>(batch) * num_q_heads * kRowStride;
+      if (need > kvq::kStaticScratchBytes)
+        return fail(KVQ_ENOSPACE, "the call needs %zu bytes of workspace, above the static workspace's %zu", need,
+                    kvq::kStaticScratchBytes);
+      if (static_cast<size_t>(batch) * cache->num_kv_heads * sizeof(int32_t) > kvq::kStaticTicketBytes)
+        return fail(KVQ_ENOSPACE, "batch * num_kv_heads = %lld exceeds the static workspace's %zu tickets",
+                    static_cast<long long>(batch) * cache->num_kv_heads, kvq::kStaticTicketBytes / sizeof(int32_t));
+    }
+  }
+  void* ws = nullptr;
+  if (batch > 0) {
+    const hipError_t e = kvq::static_scratch(&ws, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "static workspace set-up");
+  }
+  return decode_common(cache, nullptr, nullptr, KVQ_BF16, nullptr, q, q_dtype, batch, num_q_heads, page_table,
+                       max_pages, seq_lens, max_seq_len, r_k, r_v, sm_scale, out, out_dtype, ws,
+                       kvq::kStaticScratchBytes, num_splits, window, stream, nullptr, nullptr,
+                       kvq::kStaticTicketBytes);
+}
+
 kvq_status kvq_decode_attn_traced(const kvq_cache* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
                                   int32_t num_q_heads, const int32_t* page_table, int32_t max_pages,
                                   const int32_t* seq_lens, int32_t max_seq_len, const float* r_k, const float* r_v,

@@ -105,6 +105,14 @@ struct DecodeParams {
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end);
 
+// The static decode workspace of kvq_decode_attn_noalloc (kvq_noalloc.hip):
+// kStaticScratchBytes per GPU, the merge tickets in its first
+// kStaticTicketBytes.  static_scratch returns the current device's copy,
+// setting it up (address lookup, tickets cleared on `stream`) on first use.
+constexpr size_t kStaticScratchBytes = static_cast<size_t>(8) << 20;
+constexpr size_t kStaticTicketBytes = static_cast<size_t>(64) << 10;
+hipError_t static_scratch(void** out, hipStream_t stream);
+
 // Output-error evaluator (OptR section 3.2, Eq. (6)-(10)).
 constexpr int kEvPartStride = 392;   // split partial row: A, B, C [128 each], m_a, l_a, m_q, l_q, e_rec (head 0)
 constexpr int kMaxEvalBatch = 64;

@@ -81,6 +81,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kvq_decode_workspace_bytes.restype = SZ
     lib.kvq_decode_attn.argtypes = [CP, P, I32, I32, I32, P, I32, P, I32, P, P, F, P, I32, P, SZ, I32, WP, P]
     lib.kvq_decode_attn.restype = I32
+    lib.kvq_decode_attn_noalloc.argtypes = [CP, P, I32, I32, I32, P, I32, P, I32, P, P, F, P, I32, I32, WP, P]
+    lib.kvq_decode_attn_noalloc.restype = I32
     lib.kvq_decode_attn_traced.argtypes = [CP, P, I32, I32, I32, P, I32, P, I32, P, P, F, P, I32, P, SZ, I32, WP, P,
                                            P, P]
     lib.kvq_decode_attn_traced.restype = I32
@@ -195,6 +197,15 @@ def kvq_decode_attn(cache: kvq_cache, q, q_dtype: int, batch: int, num_q_heads: 
                                   max_pages, _ptr(seq_lens), max_seq_len, _ptr(r_k), _ptr(r_v), float(sm_scale),
                                   _ptr(out), out_dtype, _ptr(workspace), int(workspace_bytes), num_splits,
                                   _win(window), _stream(stream)))
+
+
+def kvq_decode_attn_noalloc(cache: kvq_cache, q, q_dtype: int, batch: int, num_q_heads: int, page_table,
+                            max_pages: int, seq_lens, max_seq_len: int, r_k, r_v, sm_scale: float, out,
+                            out_dtype: int, num_splits: int = 0, window=None, stream=None) -> None:
+    _check(load().kvq_decode_attn_noalloc(ctypes.byref(cache), _ptr(q), q_dtype, batch, num_q_heads,
+                                          _ptr(page_table), max_pages, _ptr(seq_lens), max_seq_len, _ptr(r_k),
+                                          _ptr(r_v), float(sm_scale), _ptr(out), out_dtype, num_splits, _win(window),
+                                          _stream(stream)))
 
 
 def kvq_decode_attn_traced(cache: kvq_cache, q, q_dtype: int, batch: int, num_q_heads: int, page_table,

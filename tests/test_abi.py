@@ -37,7 +37,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["kvq_pool_bytes", "kvq_quant_append", "kvq_quant_append_err", "kvq_decode_workspace_bytes",
-                            "kvq_decode_attn", "kvq_decode_attn_traced", "kvq_decode_step",
+                            "kvq_decode_attn", "kvq_decode_attn_noalloc", "kvq_decode_attn_traced", "kvq_decode_step",
                             "kvq_window_bytes",
                             "kvq_window_fill", "kvq_output_error_workspace_bytes", "kvq_output_error",
                             "kvq_page_table", "kvq_last_error"]), names
