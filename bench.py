@@ -8,18 +8,21 @@ in HBM before timing starts.  Steps cycle over independent cache replicas
 ("layers") whose total size exceeds twice the 256 MB Infinity Cache, so the
 cache read comes from HBM, not from the MALL.
 
-Two timed regions run the same steps: the first plain (it gives the step
-time), the second with a HIP event pair on every dispatch (it gives the step
-kernel's own duration; recording the events adds a few microseconds of
-command-processor work between dispatches, so that region's step time is not
-used for `value`).
+Timed regions run exactly --steps steps after exactly --warmup steps: one
+plain (it gives the step time and `value`), one with a HIP event pair on every
+dispatch (it gives the step kernel's own duration: mean, median, p10, p90;
+recording the events adds a few microseconds of command-processor work between
+dispatches, so that region's step time is not used for `value`), and the same
+two on a single replica (`hot_single_replica`: its cache stays resident in the
+MALL, so it is labelled and never `value`).
 
 Prints ONE JSON line:
   value      KV-tokens/s = sum_b T_b / step time (one GPU = whole job)
   roofline   the step kernel: algorithmic bytes per launch / its average
              duration from HIP events stamped with the dispatch's own start and
              end inside the second timed region, against 8 TB/s
-  cpu_baseline  the oracle (NumPy, fp64) timed on a bounded sample of the same step
+  cpu_baseline  the oracle (NumPy, fp64) timed on the same step on all the host's
+             cores (at most 16), and on one core for a sample of its KV heads
 """
 
 from __future__ import annotations
@@ -103,7 +106,7 @@ def counters_for(kernel_src: str, workload: str):
 def kernel_source_sha() -> str:
     """Hash of every source the decode kernel is compiled from (the counters file is keyed by it)."""
     h = hashlib.sha256()
-    for name in ("kvq_decode.hip", "kvq_device.h", "kvq_quant.h", "kvq_internal.h"):
+    for name in ("kvq_decode_kernel.h", "kvq_decode.hip", "kvq_device.h", "kvq_quant.h", "kvq_internal.h"):
         with open(os.path.join(ROOT, "rotated_int2_kv_centering_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -136,45 +139,86 @@ def read_ceiling_gbps(torch, dev, n_bytes: int = 2 << 30) -> float:
     return best
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_workers() -> int:
+    """Host threads for the oracle: the box's share of cores (at most 16 per GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
 def cpu_baseline(case, pool_np, kv_heads_sample: int, window=None, key_bits: int = 2, val_bits: int = 2):
-    """Time the oracle (as it stands) on KV heads [0, kv_heads_sample) of the step:
-    the append of the newest token and the decode of their query heads (with the
-    exact window (sinks, recent) when given), then scale to the whole step.  BLAS
-    is held to one thread, so cores = 1."""
+    """Time the oracle (as it stands) on the step: the append of the newest token,
+    then the decode of the query heads (with the exact window (sinks, recent) when
+    given), one KV head per task.  Two runs: KV heads [0, kv_heads_sample) on one
+    core (BLAS held to one thread), scaled to the whole step; and every KV head of
+    the step on a thread pool of all the host's cores (each task's BLAS on one
+    thread).  The all-core figure is the baseline reported."""
+    import concurrent.futures
     import numpy as np
     from threadpoolctl import threadpool_limits
     from oracle import kvq_oracle as O
 
-    hs = list(range(min(kv_heads_sample, case.Hkv)))
     r_k, r_v = case.r_k, case.r_v
     if case.rotation == "hadamard":
         r_k, r_v = O.hadamard_rotation(r_k), O.hadamard_rotation(r_v)
-    heads = [(b, j) for b in range(case.B) for j in range(case.Hq) if j // case.g in hs]
     last = np.array([np.nonzero(case.tok_seq == b)[0][-1] for b in range(case.B)])
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
+    k_seqs = [case.k[case.tok_seq == b] for b in range(case.B)] if window else None
+    v_seqs = [case.v[case.tok_seq == b] for b in range(case.B)] if window else None
+
+    def append():
         pool = pool_np.copy()
         x, w = O.rotated_inputs(case.k[last], case.v[last], case.mu, r_k, r_v)
         O.quantize_append(pool, case.Hkv, case.slots[last], x, w, key_bits=key_bits, val_bits=val_bits)
+        return pool
+
+    def decode(pool, h):
+        heads = [(b, j) for b in range(case.B) for j in range(case.Hq) if j // case.g == h]
         if window:
-            k_seqs = [case.k[case.tok_seq == b] for b in range(case.B)]
-            v_seqs = [case.v[case.tok_seq == b] for b in range(case.B)]
             O.decode_attention_window(case.q, pool, case.Hkv, case.page_table, case.seq_lens, case.mu, r_k, r_v,
                                       k_seqs, v_seqs, window[0], window[1], heads=heads, key_bits=key_bits,
                                       val_bits=val_bits)
         else:
             O.decode_attention(case.q, pool, case.Hkv, case.page_table, case.seq_lens, r_k, r_v, heads=heads,
                                key_bits=key_bits, val_bits=val_bits)
-        dt = time.perf_counter() - t0
-    step_est = dt * case.Hkv / len(hs)
+
+    hs = list(range(min(kv_heads_sample, case.Hkv)))
     tokens = float(case.seq_lens.sum())
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        pool = append()
+        for h in hs:
+            decode(pool, h)
+        dt1 = time.perf_counter() - t0
+        workers = cpu_workers()
+        t0 = time.perf_counter()
+        pool = append()
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(lambda h: decode(pool, h), range(case.Hkv)))
+        dtn = time.perf_counter() - t0
+    one = tokens / (dt1 * case.Hkv / len(hs))
     return {
-        "value": tokens / step_est,
+        "value": tokens / dtn,
         "unit": "KV-tokens/s",
-        "cores": 1,
+        "cores": workers,
         "kind": "oracle",
-        "sample": (f"oracle (NumPy fp64) append of the newest token + decode of the {len(heads)} query heads on KV heads "
-                   f"{hs[0]}..{hs[-1]} of the same step ({dt:.1f} s), scaled by {case.Hkv}/{len(hs)} KV heads"),
+        "cpu_model": cpu_model(),
+        "sample": (f"oracle (NumPy fp64) append of the newest token + decode of all {case.B * case.Hq} query heads of "
+                   f"the same step, one KV head per task on {workers} threads ({dtn:.1f} s)"),
+        "value_one_core": one,
+        "sample_one_core": (f"the same on one core for KV heads {hs[0]}..{hs[-1]} ({dt1:.1f} s), scaled by "
+                            f"{case.Hkv}/{len(hs)} KV heads"),
     }
 
 
@@ -278,7 +322,8 @@ def main() -> int:
     ap.add_argument("--hold-ms", type=float, default=60.0,
                     help="length of the spin kernel that holds the stream while the timed steps are enqueued")
     ap.add_argument("--num-splits", type=int, default=0)
-    ap.add_argument("--cpu-kv-heads", type=int, default=8, help="KV heads in the oracle's timed sample (0 = skip)")
+    ap.add_argument("--cpu-kv-heads", type=int, default=1,
+                    help="KV heads in the oracle's one-core sample (0 = skip the CPU baseline)")
     ap.add_argument("--window", default="", help="exact bf16 window 'sinks,recent' (e.g. 4,128); default none")
     ap.add_argument("--key-bits", type=int, default=2, choices=[2, 3, 4],
                     help="bits per key code: 2, or 3 / 4 (K3V2 / K4V2: a 512-byte high-bit plane per block)")
@@ -401,28 +446,28 @@ def main() -> int:
     torch.cuda.synchronize()
     eager_out = [o.clone() for o in outs]
 
-    n_cycles = max(1, -(-args.steps // n_rep))
-    steps = n_cycles * n_rep
+    steps = args.steps
     ev_b = [hip.event() for _ in range(steps)]
     ev_e = [hip.event() for _ in range(steps)]
 
-    def run_all(with_events):
-        for i in range(steps):
+    def run_all(n, with_events, replicas):
+        """n steps cycling over the given replicas."""
+        for i in range(n):
+            r = replicas[i % len(replicas)]
             if with_events:
-                step(i % n_rep, ev_b[i], ev_e[i])
+                step(r, ev_b[i], ev_e[i])
             else:
-                step(i % n_rep)
+                step(r)
 
-    # warm-up: at least `warmup` steps (whole passes of the step sequence)
-    warm_passes = max(1, -(-args.warmup // steps))
-    for _ in range(warm_passes):
-        run_all(True)
+    all_reps = list(range(n_rep))
+    # warm-up: exactly `warmup` steps over the replicas
+    run_all(args.warmup, False, all_reps)
     torch.cuda.synchronize()
     for r in range(n_rep):
         if not torch.equal(outs[r], eager_out[r]):
             raise RuntimeError(f"warm-up output differs from the first output on replica {r}")
 
-    def timed(with_events):
+    def timed(with_events, replicas):
         """`steps` whole steps, no host synchronisation inside.  A bounded spin
         kernel queued first holds the stream while the host enqueues every step,
         so the GPU then runs them back to back (no host launch gaps); the start
@@ -432,7 +477,7 @@ def main() -> int:
         torch.cuda._sleep(int(args.hold_ms * 1e-3 * 2.4e9))
         start.record()
         t_wall = time.perf_counter()
-        run_all(with_events)
+        run_all(steps, with_events, replicas)
         t_enq = (time.perf_counter() - t_wall) * 1e3
         stop.record()
         torch.cuda.synchronize()
@@ -441,17 +486,30 @@ def main() -> int:
                 raise RuntimeError(f"timed output differs from the first output on replica {r}")
         return start.elapsed_time(stop), t_enq
 
-    # ---- timed region 1: the step time
-    total_ms, t_enqueue = timed(False)
+    def pct(xs):
+        a = np.asarray(xs, np.float64)
+        return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)), "p90": float(np.percentile(a, 90)),
+                "mean": float(a.mean()), "min": float(a.min()), "max": float(a.max())}
+
+    # ---- timed region 1: the step time (replicas cycled, cold MALL)
+    total_ms, t_enqueue = timed(False, all_reps)
     ms_per_step = total_ms / steps
     # ---- timed region 2: the same steps, each dispatch bracketed by its own events
-    total_ev_ms, _ = timed(True)
+    total_ev_ms, _ = timed(True, all_reps)
     split_ms = [hip.elapsed_ms(ev_b[i], ev_e[i]) for i in range(steps)]
-    split_avg_ms = float(np.mean(split_ms))
+    period_ms = [hip.elapsed_ms(ev_b[i], ev_b[i + 1]) for i in range(steps - 1)] or [total_ev_ms]
+    kern = pct(np.asarray(split_ms) * 1e3)
+    split_avg_ms = kern["mean"] * 1e-3
     log(f"[bench] {steps} steps: {ms_per_step * 1e3:.2f} us/step; with per-dispatch events "
-        f"{total_ev_ms / steps * 1e3:.2f} us/step, decode kernel {split_avg_ms * 1e3:.2f} us "
-        f"(min {min(split_ms) * 1e3:.2f}, max {max(split_ms) * 1e3:.2f}); host enqueue {t_enqueue:.1f} ms "
-        f"vs GPU {total_ms:.1f} ms")
+        f"{total_ev_ms / steps * 1e3:.2f} us/step, decode kernel mean {kern['mean']:.2f} us (median "
+        f"{kern['median']:.2f}, p10 {kern['p10']:.2f}, p90 {kern['p90']:.2f}); host enqueue {t_enqueue:.1f} ms vs "
+        f"GPU {total_ms:.1f} ms")
+    # ---- hot: one replica only, so its cache stays resident in the 256 MB MALL
+    hot_ms, _ = timed(False, [0])
+    timed(True, [0])
+    hot_kern = pct([hip.elapsed_ms(ev_b[i], ev_e[i]) * 1e3 for i in range(steps)])
+    log(f"[bench] hot (one replica, MALL-resident): {hot_ms / steps * 1e3:.2f} us/step, kernel median "
+        f"{hot_kern['median']:.2f} us")
 
     # measured HBM read ceiling: a 2 GiB buffer streamed once by the probe kernel
     # (16-byte loads), best launch shape and best of 3, outside the timed regions
@@ -482,7 +540,7 @@ def main() -> int:
         "unit": "KV-tokens/s",
         "n_gpus": 1,
         "steps": steps,
-        "warmup": warm_passes * steps,
+        "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -504,7 +562,12 @@ def main() -> int:
         "hbm_gbps_step": cache_bytes / (ms_per_step * 1e-3) / 1e9,
         "pct_peak_step": cache_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
         "decode_kernel_us": split_avg_ms * 1e3,
+        "decode_kernel_us_dist": kern,
         "ms_per_step_with_dispatch_events": total_ev_ms / steps,
+        "step_period_us_with_events_dist": pct(np.asarray(period_ms) * 1e3),
+        "hot_single_replica": {"note": "one replica only: its cache stays resident in the 256 MB MALL (not HBM-bound)",
+                               "ms_per_step": hot_ms / steps, "decode_kernel_us_dist": hot_kern,
+                               "kv_tokens_per_s": tokens / (hot_ms / steps * 1e-3)},
         "host_enqueue_ms": t_enqueue,
         "bulk_append_us": bulk_ms * 1e3,
         "bulk_append_alg_gbps": bulk_alg / (bulk_ms * 1e-3) / 1e9,
