@@ -106,7 +106,15 @@ def counters_for(kernel_src: str, workload: str):
 def kernel_source_sha() -> str:
     """Hash of every source the decode kernel is compiled from (the counters file is keyed by it)."""
     h = hashlib.sha256()
-    for name in ("kvq_decode_kernel.h", "kvq_decode.hip", "kvq_device.h", "kvq_quant.h", "kvq_internal.h"):
+    for name in (
+        "kvq_decode_kernel.h",
+        "kvq_decode.hip",
+        "kvq_decode_g8.hip",
+        "kvq_decode_g16.hip",
+        "kvq_device.h",
+        "kvq_quant.h",
+        "kvq_internal.h",
+    ):
         with open(os.path.join(ROOT, "rotated_int2_kv_centering_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
