@@ -173,7 +173,8 @@ size_t kvq_pool_bytes(const kvq_cache* cache);
  *             signs [H_kv][128] instead (cache->rotation).
  *   rot_out   optional device fp32 [n_tokens][H_kv][2][128]: receives the
  *             fp32 quantizer inputs (index 0: centred rotated key, 1: rotated
- *             value) exactly as the kernel quantized them.  NULL = not written.
+ *             value) exactly as the kernel quantized them.  NULL = not written;
+ *             rows of tokens whose slot is skipped are not written either.
  * Writes the K/V codes and fp16 scale/zero of every (token, KV head) into its
  * slot.  Other slots of the same page keep their contents.
  * Input range: every rotated value (k - mu) R_K and v R_V must be finite with

@@ -15,6 +15,7 @@
 // and thread j owns rotated channel j (kvq_quant.h: q2_pack_channel).
 
 #include <algorithm>
+#include <type_traits>
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
@@ -127,22 +128,395 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Bulk path (n_tokens >= kBulkMin, raw bf16/fp32 input): workgroups of 8
-// waves, each bound to one (KV head, tensor) and striding over its tiles of
-// 512 tokens.  Dense R (kRot = 0) is staged once in LDS
-// as split-fp16 MFMA operands (kvq_rot.h); each wave rotates 16 tokens at a
-// time on the matrix cores.  A Hadamard R (kRot = 1) is applied in registers:
-// lane (row, kq) holds columns 32 kb + 8 kq + e of one token, so the seven
-// butterfly stages run on column bits 0-2 (e) and 5-6 (kb) inside the lane and
-// on bits 3-4 (kq) across lanes 16 and 32 apart, in the stage order of wht128,
-// which makes the result bitwise that of the tiled kernel.  Either way the
-// wave passes the rotated rows through its own LDS rows and quantizes them
-// with one lane per (token, 32-channel group) (kvq_quant.h: q2_group32),
-// packing the K and V words across lanes.
+// Bulk path (n_tokens >= kBulkMin, raw bf16/fp32 input).
+//
+// Workgroups of 8 waves, each bound to one KV head, with R_K and R_V staged
+// once in LDS as split-fp16 MFMA operands (kvq_rot.h; a Hadamard R needs
+// none).  A wave takes 32 tokens at a time and runs their keys, then their
+// values:
+//   1. lane l = 32 h + n loads channels [64 h, 64 h + 64) of token n (one
+//      contiguous piece of its row) and centres keys (fp32);
+//   2. the wave rotates the 32 rows on the matrix cores (kvq_rot.h), or, for
+//      a Hadamard R, runs the seven butterfly stages of wht128 in the same
+//      order: stages 0-5 inside the lane, stage 6 across the lane halves.
+//      Either way lane (h, n) ends up with channels [64 h, 64 h + 64) of the
+//      rotated token n, which are its Q2 groups 2h and 2h + 1 (G = 32);
+//   3. the lane quantizes them in registers (bulk_params, bulk_codes) and
+//      packs the codes straight into the block's words: a slot's K words are
+//      whole in one lane; its V half-words take one exchange across the lane
+//      halves, and the two slots of a V word one between neighbouring lanes;
+//   4. plain stores: the wave writes the K and the V words of its tile's
+//      records within microseconds of each other, so the lines of a block are
+//      whole in L2 before they leave.  A V word whose other slot is not the
+//      neighbouring token of the same tile is written as this slot's 16-bit
+//      half only.
+// ---------------------------------------------------------------------------
 constexpr int kBulkThreads = 512;
 constexpr int kBulkWaves = kBulkThreads / 64;
-constexpr int kBulkRounds = 4;                        // 16-token tiles per wave
-constexpr int kBulkTile = 16 * kBulkWaves * kBulkRounds;  // tokens per workgroup
+constexpr int kBulkTok = 32;                  // tokens per wave tile
+constexpr float kMagic = 12582912.0f;         // 1.5 * 2^23
+constexpr uint32_t kMagicBits = 0x4b400000u;  // its bits: fl(q + kMagic) keeps rint(q) in the low bits
+// sum of kMagicBits << p over the sixteen 2-bit fields p = 0, 2, .., 30 of a word
+constexpr uint32_t magic_fields() {
+  uint32_t s = 0;
+  for (int p = 0; p < 32; p += 2) s += kMagicBits << p;
+  return s;
+}
+constexpr uint32_t kMagicFields = magic_fields();
+
+__device__ __forceinline__ uint32_t dpp_xor1_u32(uint32_t x) {
+  return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), QuadXor1::ctrl, 0xf, 0xf, false));
+}
+
+// Q2 of one token's channels [64 h, 64 h + 64), held by one lane as c[v]
+// (v = channel - 64 h) in units of 1/u (u a power of two: x = c u exactly);
+// groups g = 0, 1 are v in [32 g, 32 g + 32).  The arithmetic is that of
+// q2_pack_channel (kvq_quant.h): s = fp16(fp32(max - min) / n_lv) and
+// z = fp16(min) after the clip, code = clamp(rint(fl(fl(x - z) / s)), 0, n_lv),
+// all codes 0 where s is 0.
+struct BulkGroups {
+  float sc[2], z[2];  // fp16 scale and zero of groups 0, 1 (as fp32)
+  float zn[2], top[2], r_lo[2], r_hi[2];
+  uint32_t pair[2];  // metadata words: fp16 scale | fp16 zero << 16
+};
+
+__device__ __forceinline__ BulkGroups bulk_params(const float (&c)[64], float u, float clip, int gsize, float n_lv) {
+  float mn[2], mx[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    mn[g] = c[32 * g];
+    mx[g] = c[32 * g];
+#pragma unroll
+    for (int v = 32 * g + 1; v < 32 * g + 32; ++v) {
+      mn[g] = fminf(mn[g], c[v]);
+      mx[g] = fmaxf(mx[g], c[v]);
+    }
+  }
+  if (gsize > 32) {  // G = 64: both groups of the lane
+    mn[0] = mn[1] = fminf(mn[0], mn[1]);
+    mx[0] = mx[1] = fmaxf(mx[0], mx[1]);
+  }
+  if (gsize > 64) {  // G = 128: and the other lane half
+    float p, q;
+    swap32(mn[0], p, q);
+    mn[0] = mn[1] = fminf(p, q);
+    swap32(mx[0], p, q);
+    mx[0] = mx[1] = fmaxf(p, q);
+  }
+  BulkGroups G;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    float lo = mn[g] * u, hi = mx[g] * u;  // exact: u is a power of two
+    lo *= clip;
+    hi *= clip;
+    // c*min and c*max are rounded to fp32 before anything else uses them
+    asm volatile("" : "+v"(lo), "+v"(hi));
+    const float s32 = (hi - lo) / n_lv;
+    const _Float16 s16 = static_cast<_Float16>(s32);
+    const _Float16 z16 = static_cast<_Float16>(lo);
+    G.sc[g] = static_cast<float>(s16);
+    G.z[g] = static_cast<float>(z16);
+    G.pair[g] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, s16)) |
+                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, z16)) << 16);
+    G.zn[g] = -G.z[g];
+    G.top[g] = G.sc[g] * n_lv;  // exact: an 11-bit by 4-bit product
+    const float rcp = G.sc[g] != 0.0f ? __builtin_amdgcn_rcpf(G.sc[g]) : 0.0f;
+    G.r_lo[g] = rcp * (1.0f - 0x1p-20f);
+    G.r_hi[g] = rcp * (1.0f + 0x1p-20f);
+  }
+  return G;
+}
+
+// The codes of the 64 values as y = kMagicBits + code, passed to pack(v, y);
+// with kErr, err(v, x, level) also sees each value and its dequantized level.
+//
+// The fast path (kExact false) divides nothing.  With t = fl(x - z) clamped
+// to [0, n_lv s] (n_lv s is exact, and clamping t clamps the code),
+// q1 = t r_lo and q2 = t r_hi bracket fl(t / s): r_lo and r_hi are 1/s moved
+// 2^-20 down and up, more than the reciprocal's error plus that of the rounded
+// quotient.  rint is monotone, so where rint(q1) = rint(q2) that is the code.
+// Each rint is taken inside the fused multiply-add that forms q, by adding
+// 1.5 * 2^23: the sum keeps the integer in its low bits.  The return value is
+// nonzero where some q1 and q2 round apart (fl(t / s) within about 2^-20 of a
+// half-integer, ties included); the caller then takes this lane's codes again
+// with kExact, the IEEE division.
+template <bool kExact, bool kErr, typename Pack, typename Err>
+__device__ __forceinline__ uint32_t bulk_codes(const float (&c)[64], float u, float n_lv, const BulkGroups& G,
+                                               Pack&& pack, Err&& err) {
+  uint32_t apart = 0;
+#pragma unroll
+  for (int v = 0; v < 64; ++v) {
+    const int g = v >> 5;
+    const float t = fmaf(c[v], u, G.zn[g]);
+    uint32_t y;
+    if (kExact) {
+      const float q = G.sc[g] != 0.0f ? fminf(fmaxf(rintf(t / G.sc[g]), 0.0f), n_lv) : 0.0f;
+      y = kMagicBits + static_cast<uint32_t>(q);
+    } else {
+      const float tc = __builtin_amdgcn_fmed3f(t, 0.0f, G.top[g]);
+      const float y1 = fmaf(tc, G.r_lo[g], kMagic);
+      const float y2 = fmaf(tc, G.r_hi[g], kMagic);
+      apart += __float_as_uint(y1) ^ __float_as_uint(y2);
+      y = __float_as_uint(y1);
+    }
+    pack(v, y);
+    if (kErr) err(v, c[v] * u, fmaf(G.sc[g], static_cast<float>(y - kMagicBits), G.z[g]));
+  }
+  return apart;
+}
+
+// K code word a (record 16 a + slot, word h) gets value v = 16 mt + 4 j + i of
+// the lane when a = 2 (mt & 1) + j / 2, at bit 2 (4 (mt / 2) + 2 (j & 1) +
+// i / 2) + 16 (i & 1): channel 64 h + v is c = 32 kk + 8 a + e with kk = 2 h +
+// mt / 2 and e = 4 (j & 1) + i (kvq_quant.h).  The lane's byte h of V
+// half-word b = 4 j + i (t = c / 16 = 4 h + mt) is byte i of word j, at bit
+// 8 i + 2 mt.
+__device__ __forceinline__ int kword_of(int v) { return 2 * ((v >> 4) & 1) + ((v >> 3) & 1); }
+__device__ __forceinline__ int kbit_of(int v) {
+  return 2 * (4 * (v >> 5) + 2 * ((v >> 2) & 1) + ((v & 3) >> 1)) + 16 * (v & 1);
+}
+__device__ __forceinline__ int vword_of(int v) { return (v >> 2) & 3; }
+__device__ __forceinline__ int vbit_of(int v) { return 8 * (v & 3) + 2 * (v >> 4); }
+
+// The 16-bit V half-words of this lane's token for b = 8 h + 2 q, 8 h + 2 q + 1
+// (word q, low and high half) from the byte words D[j] of both lane halves:
+// v_permlane32_swap exchanges lanes 32..63 of its first operand with lanes
+// 0..31 of its second, so each lane receives, in this order, the h = 0 and the
+// h = 1 byte words of the j it keeps (lower half: j = 0, 1; upper: 2, 3).
+__device__ __forceinline__ void v_halfwords(const uint32_t (&D)[4], uint32_t (&E)[4]) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const auto r = __builtin_amdgcn_permlane32_swap(D[p], D[p + 2], false, false);
+    E[2 * p] = __builtin_amdgcn_perm(r[1], r[0], 0x05010400u);      // bytes P0 Q0 P1 Q1
+    E[2 * p + 1] = __builtin_amdgcn_perm(r[1], r[0], 0x07030602u);  // bytes P2 Q2 P3 Q3
+  }
+}
+
+// Stores the V half-words E of this lane's token (slot `slot`, pslot that of
+// the neighbouring token of the tile, lane ^ 1) at byte offset `plane` and
+// word stride `rec_stride` of the block: both slots of a word in one 32-bit
+// store where the neighbour holds the other slot of the word (the odd token
+// of the pair stores b = 8 h + 4 .. + 7, the even one b = 8 h .. + 3), else
+// this slot's halves only.
+__device__ __forceinline__ void v_store(uint8_t* block, bool ok, int slot, int pslot, bool tok_odd, int h,
+                                        const uint32_t (&E)[4], int plane, int rec_stride, int word_off) {
+  const uint32_t send0 = tok_odd ? E[0] : E[2], send1 = tok_odd ? E[1] : E[3];
+  const uint32_t own0 = tok_odd ? E[2] : E[0], own1 = tok_odd ? E[3] : E[1];
+  const uint32_t recv0 = dpp_xor1_u32(send0), recv1 = dpp_xor1_u32(send1);
+  if (!ok) return;
+  const int off = slot & 15;
+  uint8_t* base = block + plane + rec_stride * 16 * (off >> 2) + word_off * ((off & 3) >> 1);
+  if (pslot == (slot ^ 1)) {  // both slots of the words: the low half is the even slot's
+    const uint32_t s_lo = (slot & 1) ? 0x01000504u : 0x05040100u;
+    const uint32_t s_hi = (slot & 1) ? 0x03020706u : 0x07060302u;
+    const int b0 = 8 * h + (tok_odd ? 4 : 0);
+    *reinterpret_cast<uint32_t*>(base + rec_stride * (b0 + 0)) = __builtin_amdgcn_perm(recv0, own0, s_lo);
+    *reinterpret_cast<uint32_t*>(base + rec_stride * (b0 + 1)) = __builtin_amdgcn_perm(recv0, own0, s_hi);
+    *reinterpret_cast<uint32_t*>(base + rec_stride * (b0 + 2)) = __builtin_amdgcn_perm(recv1, own1, s_lo);
+    *reinterpret_cast<uint32_t*>(base + rec_stride * (b0 + 3)) = __builtin_amdgcn_perm(recv1, own1, s_hi);
+  } else {
+    uint8_t* half = base + 2 * (off & 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      *reinterpret_cast<uint16_t*>(half + rec_stride * (8 * h + 2 * q)) = static_cast<uint16_t>(E[q] & 0xffffu);
+      *reinterpret_cast<uint16_t*>(half + rec_stride * (8 * h + 2 * q + 1)) = static_cast<uint16_t>(E[q] >> 16);
+    }
+  }
+}
+
+// Quantize-pack-store one tensor of a 32-token tile from the lane's 64 values
+// c (in units of 1/u).  kT = 0: keys, 1: values.
+template <int kT, bool kWide>
+__device__ __forceinline__ void bulk_store(const float (&c)[64], float u, uint8_t* __restrict__ pool, int num_pages,
+                                           int num_kv_heads, int hd, int n, int n_tokens,
+                                           const int32_t* __restrict__ slots, float* __restrict__ rot_out, float clip,
+                                           int gsize, float* __restrict__ sq_err, int kbits, int vbits, int lane) {
+  const int h = lane >> 5;
+  const float n_lv = static_cast<float>((1 << (kT == 0 ? kbits : vbits)) - 1);
+  const BulkGroups G = bulk_params(c, u, clip, gsize, n_lv);
+  // words: K code words a = 0..3 (kWide: + their high bits), or V byte words j = 0..3
+  uint32_t w[4], wh[4];
+  float e_sum = 0.0f;
+  auto reset = [&]() {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w[q] = kWide ? 0u : 0u - kMagicFields;  // 2-bit: the magic's bits cancel once all 16 fields are in
+      wh[q] = 0u;
+    }
+    e_sum = 0.0f;
+  };
+  auto pack = [&](int v, uint32_t y) {
+    const int q = kT == 0 ? kword_of(v) : vword_of(v);
+    const int b = kT == 0 ? kbit_of(v) : vbit_of(v);
+    if (kWide) {
+      w[q] |= (y & 3u) << b;
+      wh[q] |= ((y >> 2) & 3u) << b;
+    } else {
+      w[q] += y << b;
+    }
+  };
+  auto err = [&](int, float x, float lvl) {
+    const float d = x - lvl;
+    e_sum = fmaf(d, d, e_sum);
+  };
+  auto run = [&](auto exact_tag) {
+    constexpr bool kExact = decltype(exact_tag)::value;
+    return sq_err != nullptr ? bulk_codes<kExact, true>(c, u, n_lv, G, pack, err)
+                             : bulk_codes<kExact, false>(c, u, n_lv, G, pack, err);
+  };
+  reset();
+  if (run(std::false_type{}) != 0) {  // this lane: recompute with the division
+    reset();
+    run(std::true_type{});
+  }
+
+  const int token = n < n_tokens ? n : -1;
+  const int slot = token >= 0 ? slots[token] : -1;
+  const bool ok = slot >= 0 && slot < num_pages * kPage;
+  const int pslot = static_cast<int>(dpp_xor1_u32(static_cast<uint32_t>(slot)));
+  uint8_t* block =
+      pool + (static_cast<size_t>(ok ? slot >> 4 : 0) * num_kv_heads + hd) * block_bytes(kbits, vbits);
+  const int off = slot & 15;
+  if (kT == 1) {
+    uint32_t E[4];
+    v_halfwords(w, E);
+    v_store(block, ok, slot, pslot, (lane & 1) != 0, h, E, 8, 16, 4);
+    if (kWide) {
+      uint32_t EH[4];
+      v_halfwords(wh, EH);
+      v_store(block, ok, slot, pslot, (lane & 1) != 0, h, EH, v_hi_plane(kbits), 8, 4);
+    }
+  }
+  if (!ok) return;
+  if (kT == 0) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      *reinterpret_cast<uint32_t*>(block + 16 * (16 * a + off) + 4 * h) = w[a];
+      if (kWide) *reinterpret_cast<uint32_t*>(block + kKHiPlane + 8 * (16 * a + off) + 4 * h) = wh[a];
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < 2; ++g)  // metadata of group 2 h + g: record 4 (2 h + g) + off / 4
+    *reinterpret_cast<uint32_t*>(block + kCodeBytes + kMetaRecordBytes * (4 * (2 * h + g) + (off >> 2)) + 16 * kT +
+                                 4 * (off & 3)) = G.pair[g];
+  const size_t row = (static_cast<size_t>(token) * num_kv_heads + hd) * 2 + kT;
+  if (sq_err != nullptr) sq_err[row * 2 + h] = e_sum;  // channels [64 h, 64 h + 64)
+  if (rot_out != nullptr) {
+    float* dst = rot_out + row * kHeadDim + 64 * h;
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      *reinterpret_cast<float4v*>(dst + 4 * q) =
+          float4v{c[4 * q] * u, c[4 * q + 1] * u, c[4 * q + 2] * u, c[4 * q + 3] * u};
+  }
+}
+
+template <int kIn>
+struct BulkRaw {
+  uint4v w[kIn == 0 ? 8 : 16];  // channels [64 h, 64 h + 64) of the lane's token: bf16 or fp32
+};
+
+template <int kIn>
+__device__ __forceinline__ void bulk_load(BulkRaw<kIn>& r, const void* __restrict__ src, int n, int n_tokens,
+                                          int num_kv_heads, int hd, int h) {
+  const size_t base = (static_cast<size_t>(min(n, n_tokens - 1)) * num_kv_heads + hd) * kHeadDim + 64 * h;
+#pragma unroll
+  for (int q = 0; q < (kIn == 0 ? 8 : 16); ++q)
+    r.w[q] = kIn == 0 ? *reinterpret_cast<const uint4v*>(static_cast<const uint16_t*>(src) + base + 8 * q)
+                      : *reinterpret_cast<const uint4v*>(static_cast<const float*>(src) + base + 4 * q);
+}
+
+// Rotates (and quantizes, packs, stores) one tensor of the lane's token.
+template <int kIn, int kRot, int kT>
+__device__ __forceinline__ void bulk_tensor(const BulkRaw<kIn>& raw, const half8* op, const float* centre,
+                                            const float* sgn, uint8_t* __restrict__ pool, int num_pages,
+                                            int num_kv_heads, int hd, int n, int n_tokens,
+                                            const int32_t* __restrict__ slots, float* __restrict__ rot_out,
+                                            float clip, int gsize, float* __restrict__ sq_err, int kbits, int vbits,
+                                            int lane) {
+  const int h = lane >> 5;
+  float a[64];  // channel 64 h + v of the token, centred for keys
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int v = 8 * q + e;
+      if (kIn == 0) {
+        const uint32_t word = raw.w[q][e >> 1];
+        a[v] = __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16));
+      } else {
+        a[v] = __uint_as_float(raw.w[2 * q + (e >> 2)][e & 3]);
+      }
+    }
+  if (kT == 0) {  // key centering (fp32)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const float4v m4 = *reinterpret_cast<const float4v*>(centre + 64 * h + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a[4 * q + e] = a[4 * q + e] - m4[e];
+    }
+  }
+  float c[64];
+  float u = 1.0f;
+  if (kRot == 0) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 64; ++v) amax = fmaxf(amax, fabsf(a[v]));
+    float p, q;
+    swap32(amax, p, q);
+    const float rs = row_split_scale(fmaxf(p, q));
+    u = 1.0f / (rs * kRotScale);  // a power of two: exact
+    constexpr bool kLo = !(kIn == 0 && kT == 1);  // bf16 values scale exactly into fp16
+    half8 b_hi[8], b_lo[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (kLo) {
+          _Float16 hh, ll;
+          split_scaled(a[8 * ks + e], rs, hh, ll);
+          b_hi[ks][e] = hh;
+          b_lo[ks][e] = ll;
+        } else {
+          b_hi[ks][e] = static_cast<_Float16>(a[8 * ks + e] * rs);
+          b_lo[ks][e] = 0;
+        }
+      }
+    float16v acc[4];
+    rotate32<kLo>(b_hi, b_lo, op, lane, acc);
+#pragma unroll
+    for (int v = 0; v < 64; ++v) c[v] = acc[v >> 4][v & 15];
+  } else {
+    // x = WHT(a * s) / sqrt(128), the stages of wht128 in its order
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const float4v s4 = *reinterpret_cast<const float4v*>(sgn + 64 * h + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) c[4 * q + e] = a[4 * q + e] * s4[e];
+    }
+#pragma unroll
+    for (int k = 0; k < 6; ++k)  // channel bits 0-5: inside the lane
+#pragma unroll
+      for (int v = 0; v < 64; ++v)
+        if ((v & (1 << k)) == 0) {
+          const float lo = c[v], hi = c[v | (1 << k)];
+          c[v] = lo + hi;
+          c[v | (1 << k)] = lo - hi;
+        }
+    const float sg = h ? -1.0f : 1.0f;  // channel bit 6: the lane halves
+#pragma unroll
+    for (int v = 0; v < 64; ++v) {
+      float lo, hi;  // the h = 0 and the h = 1 element of the pair
+      swap32(c[v], lo, hi);
+      c[v] = fmaf(hi, sg, lo) * kInvSqrt128;
+    }
+  }
+  if ((kT == 0 ? kbits : vbits) > 2)
+    bulk_store<kT, true>(c, u, pool, num_pages, num_kv_heads, hd, n, n_tokens, slots, rot_out, clip, gsize, sq_err,
+                         kbits, vbits, lane);
+  else
+    bulk_store<kT, false>(c, u, pool, num_pages, num_kv_heads, hd, n, n_tokens, slots, rot_out, clip, gsize, sq_err,
+                          kbits, vbits, lane);
+}
 
 template <int kIn, int kRot>  // kIn: 0 = bf16, 1 = fp32; kRot: 0 = dense R, 1 = Hadamard signs
 __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
@@ -150,279 +524,51 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
     const void* __restrict__ v_in, int n_tokens, const int32_t* __restrict__ slots, const float* __restrict__ mu,
     const float* __restrict__ r_k, const float* __restrict__ r_v, float* __restrict__ rot_out, float clip, int gsize,
     float* __restrict__ sq_err, int kbits, int vbits) {
-  const int h = blockIdx.y;
-  const int tensor = blockIdx.z;  // 0: key, 1: value
-  const int bits = tensor == 0 ? kbits : vbits;
-  const bool wide = bits > 2;  // this workgroup packs 3- or 4-bit codes (high bits in the tensor's plane)
+  const int hd = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  __shared__ half8 s_op[kRot == 0 ? 32 * 2 * 64 : 1];          // R operands, 64 KB (dense R only)
-  __shared__ float s_x[kBulkWaves][16][kHeadDim + 4];          // rotated rows of each wave's 16 tokens
+  const int h = lane >> 5;
+  constexpr int kOps = 32 * 2 * 64;  // half8 operands of one R
+  __shared__ half8 s_op[kRot == 0 ? 2 * kOps : 1];  // R_K then R_V, 128 KB (dense R only)
+  __shared__ float s_vec[3][kHeadDim];              // key centre; Hadamard signs of K and V
 
-  if (kRot == 0)
-    stage_rotation((tensor == 0 ? r_k : r_v) + static_cast<size_t>(h) * kHeadDim * kHeadDim, s_op, wave, kBulkWaves,
-                   lane);
-  // this lane's A columns 32 kb + 8 kq + e; key centre (fp32) or 0, and the Hadamard signs
-  const int kq = lane >> 4, row = lane & 15;
-  float cen[4][8], sgn[4][8];
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      cen[kb][e] = (tensor == 0 && mu != nullptr) ? mu[h * kHeadDim + 32 * kb + 8 * kq + e] : 0.0f;
-      sgn[kb][e] = kRot == 1 ? (tensor == 0 ? r_k : r_v)[h * kHeadDim + 32 * kb + 8 * kq + e] : 0.0f;
-    }
+  if (kRot == 0) {
+    stage_rotation_t(r_k + static_cast<size_t>(hd) * kHeadDim * kHeadDim, s_op, wave, kBulkWaves, lane);
+    stage_rotation_t(r_v + static_cast<size_t>(hd) * kHeadDim * kHeadDim, s_op + kOps, wave, kBulkWaves, lane);
+  }
+  for (int i = tid; i < 3 * kHeadDim; i += kBulkThreads) {
+    const int which = i / kHeadDim, j = i % kHeadDim;
+    float val = 0.0f;
+    if (which == 0)
+      val = mu != nullptr ? mu[hd * kHeadDim + j] : 0.0f;
+    else if (kRot == 1)
+      val = (which == 1 ? r_k : r_v)[hd * kHeadDim + j];
+    s_vec[which][j] = val;
+  }
   __syncthreads();
 
-  const void* src = tensor == 0 ? k_in : v_in;
-  const int n_tiles = (n_tokens + kBulkTile - 1) / kBulkTile;
-  for (int tile = blockIdx.x; tile < n_tiles; tile += gridDim.x) {
-    const int n0 = tile * kBulkTile;
-    // raw A rows of the wave's 16-token tile m, loaded one tile ahead: row `row`
-    // (clamped; rows past the end are never stored), columns 32 kb + 8 kq ..
-    constexpr int kRawWords = kIn == 0 ? 4 : 8;  // uint4v per lane: 4 kb x 8 bf16, or 4 kb x 8 fp32
-    auto load_raw = [&](int m, uint4v (&raw)[kRawWords]) {
-      const int r0 = n0 + 16 * (kBulkWaves * m + wave);
-      const size_t base = (static_cast<size_t>(min(r0 + row, n_tokens - 1)) * num_kv_heads + h) * kHeadDim;
-  #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const size_t off = base + 32 * kb + 8 * kq;
-        if (kIn == 0) {
-          raw[kb] = *reinterpret_cast<const uint4v*>(static_cast<const uint16_t*>(src) + off);
-        } else {
-          raw[2 * kb] = *reinterpret_cast<const uint4v*>(static_cast<const float*>(src) + off);
-          raw[2 * kb + 1] = *reinterpret_cast<const uint4v*>(static_cast<const float*>(src) + off + 4);
-        }
-      }
-    };
-    uint4v raw[kRawWords], next[kRawWords];
-    load_raw(0, raw);
-    for (int m = 0; m < kBulkRounds; ++m) {
-      const int r0 = n0 + 16 * (kBulkWaves * m + wave);  // this wave's first token
-      if (m + 1 < kBulkRounds) load_raw(m + 1, next);
-      half8 a_hi[4], a_lo[4];
-      float ah[4][8];  // the centred row values (Hadamard: also sign-flipped)
-  #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        float a[8];
-        if (kIn == 0) {
-  #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            a[2 * e] = __uint_as_float(raw[kb][e] << 16);
-            a[2 * e + 1] = __uint_as_float(raw[kb][e] & 0xffff0000u);
-          }
-        } else {
-  #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            a[e] = __uint_as_float(raw[2 * kb][e]);
-            a[4 + e] = __uint_as_float(raw[2 * kb + 1][e]);
-          }
-        }
-  #pragma unroll
-        for (int e = 0; e < 8; ++e)  // key centering (fp32); values use centre 0
-          ah[kb][e] = kRot == 0 ? a[e] - cen[kb][e] : (a[e] - cen[kb][e]) * sgn[kb][e];
-      }
-      if (kRot == 0) {
-        // the row's split scale from its largest magnitude (its 128 values over
-        // the four lanes 16 kq + row), and the unscale of output rows 4 (lane/16) + i
-        float amax = 0.0f;
-  #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-  #pragma unroll
-          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(ah[kb][e]));
-        float u0, u1;
-        swap16(amax, u0, u1);
-        amax = fmaxf(u0, u1);
-        swap32(amax, u0, u1);
-        amax = fmaxf(u0, u1);
-        const float rs = row_split_scale(amax);
-  #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-  #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            _Float16 hh, ll;
-            split_f16(ah[kb][e], rs, hh, ll);
-            a_hi[kb][e] = hh;
-            a_lo[kb][e] = ll;
-          }
-        const float inv = 1.0f / (rs * kRotScale);  // a power of two: exact
-        float unscale[4];
-  #pragma unroll
-        for (int i = 0; i < 4; ++i) unscale[i] = __shfl(inv, 4 * (lane >> 4) + i);  // lane r holds row r
-        float4v C[8];
-        rotate16(a_hi, a_lo, s_op, lane, unscale, C);
-  #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-  #pragma unroll
-          for (int i = 0; i < 4; ++i) s_x[wave][4 * (lane >> 4) + i][16 * nt + (lane & 15)] = C[nt][i];
-      } else {
-        // stage k pairs column c (bit k clear) with c + 2^k: (lo, hi) -> (lo + hi, lo - hi)
-  #pragma unroll
-        for (int k = 0; k < 3; ++k)  // column bits 0-2: e
-  #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-  #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if ((e & (1 << k)) == 0) {
-                const float lo = ah[kb][e], hi = ah[kb][e | (1 << k)];
-                ah[kb][e] = lo + hi;
-                ah[kb][e | (1 << k)] = lo - hi;
-              }
-  #pragma unroll
-        for (int k = 3; k < 5; ++k) {  // column bits 3-4: kq, lane bits 4-5
-          const int lb = 16 << (k - 3);
-  #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-  #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float pv = __shfl_xor(ah[kb][e], lb);
-              ah[kb][e] = (lane & lb) ? pv - ah[kb][e] : ah[kb][e] + pv;
-            }
-        }
-  #pragma unroll
-        for (int k = 5; k < 7; ++k)  // column bits 5-6: kb
-  #pragma unroll
-          for (int kb = 0; kb < 4; ++kb)
-            if ((kb & (1 << (k - 5))) == 0) {
-  #pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const float lo = ah[kb][e], hi = ah[kb | (1 << (k - 5))][e];
-                ah[kb][e] = lo + hi;
-                ah[kb | (1 << (k - 5))][e] = lo - hi;
-              }
-            }
-  #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          float* dst = &s_x[wave][row][32 * kb + 8 * kq];
-          *reinterpret_cast<float4v*>(dst) = float4v{ah[kb][0] * kInvSqrt128, ah[kb][1] * kInvSqrt128,
-                                                     ah[kb][2] * kInvSqrt128, ah[kb][3] * kInvSqrt128};
-          *reinterpret_cast<float4v*>(dst + 4) = float4v{ah[kb][4] * kInvSqrt128, ah[kb][5] * kInvSqrt128,
-                                                         ah[kb][6] * kInvSqrt128, ah[kb][7] * kInvSqrt128};
-        }
-      }
-
-      // Quantize-pack this wave's 16 tokens: lane (token r, group g) holds the
-      // 32 channels of group g of token r.  The rows were written by this wave
-      // only; the barrier orders those LDS writes before the reads.
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      const int r = lane >> 2, g = lane & 3;
-      const int n = r0 + r;
-      float x[32];
-  #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float4v q4 = *reinterpret_cast<const float4v*>(&s_x[wave][r][32 * g + 4 * u]);
-        x[4 * u] = q4[0];
-        x[4 * u + 1] = q4[1];
-        x[4 * u + 2] = q4[2];
-        x[4 * u + 3] = q4[3];
-      }
-      uint32_t pair, code[32];
-      q2_group32(x, clip, gsize, pair, code, static_cast<float>((1 << bits) - 1));
-      const int slot = n < n_tokens ? slots[n] : -1;
-      const bool ok = slot >= 0 && slot < num_pages * kPage;  // same for the token's four lanes
-      if (sq_err != nullptr) {  // squared error of groups g and g ^ 1: channels [64 (g / 2), +64)
-        const float sc = __builtin_bit_cast(_Float16, static_cast<uint16_t>(pair & 0xffffu));
-        const float zr = __builtin_bit_cast(_Float16, static_cast<uint16_t>(pair >> 16));
-        float e = 0.0f;
-  #pragma unroll
-        for (int c = 0; c < 32; ++c) {
-          const float d = x[c] - fmaf(sc, static_cast<float>(code[c]), zr);
-          e = fmaf(d, d, e);
-        }
-        e += __shfl_xor(e, 1);
-        if (ok && (g & 1) == 0) sq_err[((static_cast<size_t>(n) * num_kv_heads + h) * 2 + tensor) * 2 + (g >> 1)] = e;
-      }
-      if (rot_out != nullptr && n < n_tokens) {
-        float* dst = rot_out + ((static_cast<size_t>(n) * num_kv_heads + h) * 2 + tensor) * kHeadDim + 32 * g;
-  #pragma unroll
-        for (int u = 0; u < 8; ++u)
-          *reinterpret_cast<float4v*>(dst + 4 * u) = float4v{x[4 * u], x[4 * u + 1], x[4 * u + 2], x[4 * u + 3]};
-      }
-      // Slots 2k and 2k + 1 of a page share their V words.  The partner of this
-      // token's slot is held by token r - 1 or r + 1 of the tile when this call
-      // writes it there (lane 4 pr + g, the same group).
-      const int pr = (slot & 1) ? r - 1 : r + 1;
-      const int plane = 4 * (pr & 15) + g;
-      const int pslot = __shfl(slot, plane);
-      const bool paired = ok && pr >= 0 && pr < 16 && pslot == (slot ^ 1);
-      const int off = slot & 15;
-      uint8_t* block =  // the block stride follows the cache format (key and value bits)
-          pool + (static_cast<size_t>(ok ? slot >> 4 : 0) * num_kv_heads + h) * block_bytes(kbits, vbits);
-      if (ok) {  // metadata pair of (token, group): record 4g + off/4
-        *reinterpret_cast<uint32_t*>(block + kCodeBytes + kMetaRecordBytes * (4 * g + (off >> 2)) + 16 * tensor +
-                                     4 * (off & 3)) = pair;
-      }
-      if (tensor == 0) {
-        // K: channel 32g + 8ak + e -> record 16ak + off, word K[g/2], bit 2(4(g%2) + e/2) + 16(e%2)
-        uint32_t kw[4];
-        uint32_t khw[4];  // 4-bit keys: the high bits, same positions, in the plane at kKHiPlane
-  #pragma unroll
-        for (int ak = 0; ak < 4; ++ak) {
-          uint32_t w = 0, wh = 0;
-  #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int sh = 2 * (4 * (g & 1) + (e >> 1)) + 16 * (e & 1);
-            w |= (code[8 * ak + e] & 3u) << sh;
-            wh |= (code[8 * ak + e] >> 2) << sh;
-          }
-          kw[ak] = w | __shfl_xor(w, 1);  // both groups of the word
-          khw[ak] = wh | __shfl_xor(wh, 1);
-        }
-        if (ok && (g & 1) == 0) {
-  #pragma unroll
-          for (int ak = 0; ak < 4; ++ak) {
-            *reinterpret_cast<uint32_t*>(block + 16 * (16 * ak + off) + 4 * (g >> 1)) = kw[ak];
-            if (wide) *reinterpret_cast<uint32_t*>(block + kKHiPlane + 8 * (16 * ak + off) + 4 * (g >> 1)) = khw[ak];
-          }
-        }
-      } else {
-        // V: channel 32g + 16tt + b -> record 16(off/4) + b, word V[(off%4)/2],
-        // bit 2(2g + tt) + 16(off%2); the token's bits of word b after the group OR
-        // The high bits of wide values go to the same positions of the values'
-        // plane: record 16(off/4) + b at v_hi_plane + 8 record, word VH[(off%4)/2].
-        const int hs = 16 * (off & 1);
-  #pragma unroll 1
-        for (int part = 0; part < (wide ? 2 : 1); ++part) {
-          const int dn = 2 * part;  // part 0: bits 0-1 of each code, part 1: bits 2-3
-          uint32_t vw[16];
-  #pragma unroll
-          for (int bb = 0; bb < 16; ++bb) {
-            uint32_t w = (((code[bb] >> dn) & 3u) << (4 * g + hs)) | (((code[16 + bb] >> dn) & 3u) << (4 * g + 2 + hs));
-            w |= __shfl_xor(w, 1);
-            w |= __shfl_xor(w, 2);
-            vw[bb] = w;
-          }
-          auto word_at = [&](int bb) {
-            const int rec = 16 * (off >> 2) + bb;
-            return reinterpret_cast<uint32_t*>(block + (part == 0 ? 16 * rec + 8 : v_hi_plane(kbits) + 8 * rec) +
-                                               4 * ((off & 3) >> 1));
-          };
-          // Both slots of a word written by this tile: the even slot's lane stores
-          // the combined word whole.  Otherwise the partner slot may be written
-          // concurrently by another tile (or keeps an older token): only this
-          // slot's half, with atomic and/or.
-          const uint32_t mask = 0xffffu << hs;
-  #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const uint32_t mine = vw[4 * g + u];
-            const uint32_t other = __shfl(mine, plane);
-            if (paired) {
-              if ((slot & 1) == 0) *word_at(4 * g + u) = mine | other;
-            } else if (ok) {
-              uint32_t* word = word_at(4 * g + u);
-              atomicAnd(word, ~mask);
-              atomicOr(word, mine);
-            }
-          }
-        }
-      }
-  #pragma unroll
-      for (int u = 0; u < kRawWords; ++u) raw[u] = next[u];
-    }
-  }  // tiles
+  const int n_tiles = (n_tokens + kBulkTok - 1) / kBulkTok;
+  const int stride = gridDim.x * kBulkWaves;
+  int tile = blockIdx.x * kBulkWaves + wave;
+  if (tile >= n_tiles) return;  // no barrier follows
+  const int nl = lane & 31;
+  constexpr bool kPrefetch = kIn == 0;  // fp32 rows are loaded where they are used (registers)
+  BulkRaw<kIn> rk, rv;
+  bulk_load<kIn>(rk, k_in, kBulkTok * tile + nl, n_tokens, num_kv_heads, hd, h);
+  for (; tile < n_tiles; tile += stride) {
+    const int n = kBulkTok * tile + nl;
+    if (kPrefetch) bulk_load<kIn>(rv, v_in, n, n_tokens, num_kv_heads, hd, h);
+    bulk_tensor<kIn, kRot, 0>(rk, s_op, s_vec[0], s_vec[1], pool, num_pages, num_kv_heads, hd, n, n_tokens, slots,
+                              rot_out, clip, gsize, sq_err, kbits, vbits, lane);
+    if (!kPrefetch) bulk_load<kIn>(rv, v_in, n, n_tokens, num_kv_heads, hd, h);
+    if (tile + stride < n_tiles && kPrefetch)
+      bulk_load<kIn>(rk, k_in, kBulkTok * (tile + stride) + nl, n_tokens, num_kv_heads, hd, h);
+    bulk_tensor<kIn, kRot, 1>(rv, s_op + kOps, s_vec[0], s_vec[2], pool, num_pages, num_kv_heads, hd, n, n_tokens,
+                              slots, rot_out, clip, gsize, sq_err, kbits, vbits, lane);
+    if (!kPrefetch && tile + stride < n_tiles)
+      bulk_load<kIn>(rk, k_in, kBulkTok * (tile + stride) + nl, n_tokens, num_kv_heads, hd, h);
+  }
 }
 
 hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const void* k, const void* v, int in_kind,
@@ -431,11 +577,13 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
                          hipStream_t stream) {
   (void)hipGetLastError();  // report only this call's launch errors, not stale ones
   if (in_kind != 2 && n_tokens >= kBulkMin) {
-    // about one workgroup per compute unit in all (each staging its dense R once;
-    // over 128 VGPRs per lane, one 8-wave workgroup fills a compute unit)
-    const int n_tiles = (n_tokens + kBulkTile - 1) / kBulkTile;
-    const int per = std::max(1, std::min(n_tiles, (256 + 2 * num_kv_heads - 1) / (2 * num_kv_heads)));
-    const dim3 bgrid(per, num_kv_heads, 2);
+    // about one workgroup per compute unit in all (each stages R_K and R_V of its
+    // head once, 128 KB of LDS: one 8-wave workgroup fills a compute unit), and
+    // no more workgroups per head than it has 32-token tiles for their waves
+    const int n_tiles = (n_tokens + kBulkTok - 1) / kBulkTok;
+    const int per = std::max(1, std::min((n_tiles + kBulkWaves - 1) / kBulkWaves,
+                                         (256 + num_kv_heads - 1) / num_kv_heads));
+    const dim3 bgrid(per, num_kv_heads);
     auto kern = in_kind == 0 ? (rot_kind == 0 ? append_bulk_kernel<0, 0> : append_bulk_kernel<0, 1>)
                              : (rot_kind == 0 ? append_bulk_kernel<1, 0> : append_bulk_kernel<1, 1>);
     hipLaunchKernelGGL(kern, bgrid, dim3(kBulkThreads), 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens, slots,
