@@ -180,7 +180,19 @@ struct BulkGroups {
   uint32_t pair[2];  // metadata words: fp16 scale | fp16 zero << 16
 };
 
+// d / b rounded to nearest, for b = 3, 7 or 15 and y = 1/b rounded to nearest:
+// Markstein's correction q1 = q0 + (d - q0 b) y of q0 = d y, whose residual
+// d - q0 b the fused multiply-add forms exactly, is the correctly rounded
+// quotient (for d normal or zero; a subnormal d gives a quotient that fp16
+// flushes to 0 either way).
+__device__ __forceinline__ float div_exact(float d, float b, float y) {
+  const float q0 = d * y;
+  const float r = fmaf(-q0, b, d);
+  return fmaf(r, y, q0);
+}
+
 __device__ __forceinline__ BulkGroups bulk_params(const float (&c)[64], float u, float clip, int gsize, float n_lv) {
+  const float inv_lv = n_lv == 3.0f ? 1.0f / 3.0f : (n_lv == 7.0f ? 1.0f / 7.0f : 1.0f / 15.0f);
   float mn[2], mx[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
@@ -211,7 +223,7 @@ __device__ __forceinline__ BulkGroups bulk_params(const float (&c)[64], float u,
     hi *= clip;
     // c*min and c*max are rounded to fp32 before anything else uses them
     asm volatile("" : "+v"(lo), "+v"(hi));
-    const float s32 = (hi - lo) / n_lv;
+    const float s32 = div_exact(hi - lo, n_lv, inv_lv);
     const _Float16 s16 = static_cast<_Float16>(s32);
     const _Float16 z16 = static_cast<_Float16>(lo);
     G.sc[g] = static_cast<float>(s16);
@@ -292,28 +304,38 @@ __device__ __forceinline__ void v_halfwords(const uint32_t (&D)[4], uint32_t (&E
   }
 }
 
-// Stores the V half-words E of this lane's token (slot `slot`, pslot that of
-// the neighbouring token of the tile, lane ^ 1) at byte offset `plane` and
-// word stride `rec_stride` of the block: both slots of a word in one 32-bit
-// store where the neighbour holds the other slot of the word (the odd token
-// of the pair stores b = 8 h + 4 .. + 7, the even one b = 8 h .. + 3), else
-// this slot's halves only.
-__device__ __forceinline__ void v_store(uint8_t* block, bool ok, int slot, int pslot, bool tok_odd, int h,
-                                        const uint32_t (&E)[4], int plane, int rec_stride, int word_off) {
+// The V words of the slot pair of this lane's token and its neighbour in the
+// tile (lane ^ 1): the even token of the pair assembles b = 8 h .. 8 h + 3,
+// the odd one b = 8 h + 4 .. 8 h + 7 (W[q] for b0 + q), each word holding the
+// even slot's half-word low; `odd_slot` tells which of the two slots is this
+// lane's.  Every lane takes part (a DPP exchange).
+__device__ __forceinline__ int v_pair(const uint32_t (&E)[4], bool tok_odd, bool odd_slot, int h, uint32_t (&W)[4]) {
   const uint32_t send0 = tok_odd ? E[0] : E[2], send1 = tok_odd ? E[1] : E[3];
   const uint32_t own0 = tok_odd ? E[2] : E[0], own1 = tok_odd ? E[3] : E[1];
   const uint32_t recv0 = dpp_xor1_u32(send0), recv1 = dpp_xor1_u32(send1);
+  const uint32_t s_lo = odd_slot ? 0x01000504u : 0x05040100u;
+  const uint32_t s_hi = odd_slot ? 0x03020706u : 0x07060302u;
+  W[0] = __builtin_amdgcn_perm(recv0, own0, s_lo);
+  W[1] = __builtin_amdgcn_perm(recv0, own0, s_hi);
+  W[2] = __builtin_amdgcn_perm(recv1, own1, s_lo);
+  W[3] = __builtin_amdgcn_perm(recv1, own1, s_hi);
+  return 8 * h + (tok_odd ? 4 : 0);
+}
+
+// Stores the V half-words E of this lane's token (slot `slot`; pslot that of
+// the neighbouring token) into the block's plane at byte offset `plane`,
+// record stride `rec_stride`: the assembled words where the neighbour holds
+// the other slot of each word, else this slot's 16-bit halves only.
+__device__ __forceinline__ void v_store(uint8_t* block, bool ok, int slot, int pslot, bool tok_odd, int h,
+                                        const uint32_t (&E)[4], int plane, int rec_stride) {
+  uint32_t W[4];
+  const int b0 = v_pair(E, tok_odd, (slot & 1) != 0, h, W);
   if (!ok) return;
   const int off = slot & 15;
-  uint8_t* base = block + plane + rec_stride * 16 * (off >> 2) + word_off * ((off & 3) >> 1);
-  if (pslot == (slot ^ 1)) {  // both slots of the words: the low half is the even slot's
-    const uint32_t s_lo = (slot & 1) ? 0x01000504u : 0x05040100u;
-    const uint32_t s_hi = (slot & 1) ? 0x03020706u : 0x07060302u;
-    const int b0 = 8 * h + (tok_odd ? 4 : 0);
-    *reinterpret_cast<uint32_t*>(base + rec_stride * (b0 + 0)) = __builtin_amdgcn_perm(recv0, own0, s_lo);
-    *reinterpret_cast<uint32_t*>(base + rec_stride * (b0 + 1)) = __builtin_amdgcn_perm(recv0, own0, s_hi);
-    *reinterpret_cast<uint32_t*>(base + rec_stride * (b0 + 2)) = __builtin_amdgcn_perm(recv1, own1, s_lo);
-    *reinterpret_cast<uint32_t*>(base + rec_stride * (b0 + 3)) = __builtin_amdgcn_perm(recv1, own1, s_hi);
+  uint8_t* base = block + plane + rec_stride * 16 * (off >> 2) + 4 * ((off & 3) >> 1);
+  if (pslot == (slot ^ 1)) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) *reinterpret_cast<uint32_t*>(base + rec_stride * (b0 + q)) = W[q];
   } else {
     uint8_t* half = base + 2 * (off & 1);
 #pragma unroll
@@ -325,12 +347,16 @@ __device__ __forceinline__ void v_store(uint8_t* block, bool ok, int slot, int p
 }
 
 // Quantize-pack-store one tensor of a 32-token tile from the lane's 64 values
-// c (in units of 1/u).  kT = 0: keys, 1: values.
-template <int kT, bool kWide>
+// c (in units of 1/u).  kT = 0: keys, 1: values; `slot` is the lane's token's
+// slot (-1 past the end).  kImg (2-bit keys and values): the words go to the
+// wave's LDS image `img` of two blocks, token n of the tile at slot n % 16 of
+// image block n / 16, for the caller to copy out; otherwise they are stored
+// slot by slot into the pool.
+template <int kT, bool kWide, bool kImg>
 __device__ __forceinline__ void bulk_store(const float (&c)[64], float u, uint8_t* __restrict__ pool, int num_pages,
-                                           int num_kv_heads, int hd, int n, int n_tokens,
-                                           const int32_t* __restrict__ slots, float* __restrict__ rot_out, float clip,
-                                           int gsize, float* __restrict__ sq_err, int kbits, int vbits, int lane) {
+                                           int num_kv_heads, int hd, int n, int slot, float* __restrict__ rot_out,
+                                           float clip, int gsize, float* __restrict__ sq_err, int kbits, int vbits,
+                                           int lane, uint8_t* img) {
   const int h = lane >> 5;
   const float n_lv = static_cast<float>((1 << (kT == 0 ? kbits : vbits)) - 1);
   const BulkGroups G = bulk_params(c, u, clip, gsize, n_lv);
@@ -370,36 +396,54 @@ __device__ __forceinline__ void bulk_store(const float (&c)[64], float u, uint8_
     run(std::true_type{});
   }
 
-  const int token = n < n_tokens ? n : -1;
-  const int slot = token >= 0 ? slots[token] : -1;
+  const bool tok_odd = (lane & 1) != 0;
   const bool ok = slot >= 0 && slot < num_pages * kPage;
-  const int pslot = static_cast<int>(dpp_xor1_u32(static_cast<uint32_t>(slot)));
-  uint8_t* block =
-      pool + (static_cast<size_t>(ok ? slot >> 4 : 0) * num_kv_heads + hd) * block_bytes(kbits, vbits);
-  const int off = slot & 15;
+  uint32_t E[4], EH[4];
   if (kT == 1) {
-    uint32_t E[4];
     v_halfwords(w, E);
-    v_store(block, ok, slot, pslot, (lane & 1) != 0, h, E, 8, 16, 4);
-    if (kWide) {
-      uint32_t EH[4];
-      v_halfwords(wh, EH);
-      v_store(block, ok, slot, pslot, (lane & 1) != 0, h, EH, v_hi_plane(kbits), 8, 4);
-    }
+    if (kWide) v_halfwords(wh, EH);
   }
-  if (!ok) return;
-  if (kT == 0) {
+  if (kImg) {
+    uint8_t* ib = img + kBlockBytes * ((lane & 31) >> 4);
+    const int io = lane & 15;  // the token's slot in the image
+    if (kT == 0) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      *reinterpret_cast<uint32_t*>(block + 16 * (16 * a + off) + 4 * h) = w[a];
-      if (kWide) *reinterpret_cast<uint32_t*>(block + kKHiPlane + 8 * (16 * a + off) + 4 * h) = wh[a];
+      for (int a = 0; a < 4; ++a) *reinterpret_cast<uint32_t*>(ib + 16 * (16 * a + io) + 4 * h) = w[a];
+    } else {
+      uint32_t W[4];
+      const int b0 = v_pair(E, tok_odd, tok_odd, h, W);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<uint32_t*>(ib + 8 + 16 * (16 * (io >> 2) + b0 + q) + 4 * ((io & 3) >> 1)) = W[q];
     }
-  }
 #pragma unroll
-  for (int g = 0; g < 2; ++g)  // metadata of group 2 h + g: record 4 (2 h + g) + off / 4
-    *reinterpret_cast<uint32_t*>(block + kCodeBytes + kMetaRecordBytes * (4 * (2 * h + g) + (off >> 2)) + 16 * kT +
-                                 4 * (off & 3)) = G.pair[g];
-  const size_t row = (static_cast<size_t>(token) * num_kv_heads + hd) * 2 + kT;
+    for (int g = 0; g < 2; ++g)
+      *reinterpret_cast<uint32_t*>(ib + kCodeBytes + kMetaRecordBytes * (4 * (2 * h + g) + (io >> 2)) + 16 * kT +
+                                   4 * (io & 3)) = G.pair[g];
+    if (!ok) return;
+  } else {
+    const int pslot = static_cast<int>(dpp_xor1_u32(static_cast<uint32_t>(slot)));
+    uint8_t* block =
+        pool + (static_cast<size_t>(ok ? slot >> 4 : 0) * num_kv_heads + hd) * block_bytes(kbits, vbits);
+    const int off = slot & 15;
+    if (kT == 1) {
+      v_store(block, ok, slot, pslot, tok_odd, h, E, 8, 16);
+      if (kWide) v_store(block, ok, slot, pslot, tok_odd, h, EH, v_hi_plane(kbits), 8);
+    }
+    if (!ok) return;
+    if (kT == 0) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        *reinterpret_cast<uint32_t*>(block + 16 * (16 * a + off) + 4 * h) = w[a];
+        if (kWide) *reinterpret_cast<uint32_t*>(block + kKHiPlane + 8 * (16 * a + off) + 4 * h) = wh[a];
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 2; ++g)  // metadata of group 2 h + g: record 4 (2 h + g) + off / 4
+      *reinterpret_cast<uint32_t*>(block + kCodeBytes + kMetaRecordBytes * (4 * (2 * h + g) + (off >> 2)) + 16 * kT +
+                                   4 * (off & 3)) = G.pair[g];
+  }
+  const size_t row = (static_cast<size_t>(n) * num_kv_heads + hd) * 2 + kT;
   if (sq_err != nullptr) sq_err[row * 2 + h] = e_sum;  // channels [64 h, 64 h + 64)
   if (rot_out != nullptr) {
     float* dst = rot_out + row * kHeadDim + 64 * h;
@@ -408,6 +452,19 @@ __device__ __forceinline__ void bulk_store(const float (&c)[64], float u, uint8_
       *reinterpret_cast<float4v*>(dst + 4 * q) =
           float4v{c[4 * q] * u, c[4 * q + 1] * u, c[4 * q + 2] * u, c[4 * q + 3] * u};
   }
+}
+
+typedef uint16_t uint16_v2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16_v2 __attribute__((ext_vector_type(2)));
+
+// One bf16 element of a packed pair (hi selects the upper one) times a power
+// of two given as bf16 bits, by the bf16 dot product with (s, 0) or (0, s)
+// plus 0: the product is exact while it stays a normal fp32, so the dot
+// product's own rounding never acts (its addition is not IEEE-rounded, which
+// is why the key centering is a plain fp32 subtraction instead).
+__device__ __forceinline__ float bf16_pick_scale(uint32_t pair, bool hi, uint32_t scale_bits) {
+  const bf16_v2 sel = __builtin_bit_cast(bf16_v2, hi ? scale_bits << 16 : scale_bits);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16_v2, pair), sel, 0.0f, false);
 }
 
 template <int kIn>
@@ -425,62 +482,78 @@ __device__ __forceinline__ void bulk_load(BulkRaw<kIn>& r, const void* __restric
                       : *reinterpret_cast<const uint4v*>(static_cast<const float*>(src) + base + 4 * q);
 }
 
-// Rotates (and quantizes, packs, stores) one tensor of the lane's token.
-template <int kIn, int kRot, int kT>
+// Rotates (and quantizes, packs, stores) one tensor of the lane's token;
+// next() issues the loads of the next tensor once the rotation is done (the
+// point of fewest live registers that still leaves the quantizer's work to
+// cover their latency).
+template <int kIn, int kRot, int kT, bool kImg, typename Next>
 __device__ __forceinline__ void bulk_tensor(const BulkRaw<kIn>& raw, const half8* op, const float* centre,
                                             const float* sgn, uint8_t* __restrict__ pool, int num_pages,
-                                            int num_kv_heads, int hd, int n, int n_tokens,
-                                            const int32_t* __restrict__ slots, float* __restrict__ rot_out,
+                                            int num_kv_heads, int hd, int n, int slot, float* __restrict__ rot_out,
                                             float clip, int gsize, float* __restrict__ sq_err, int kbits, int vbits,
-                                            int lane) {
+                                            int lane, uint8_t* img, Next&& next) {
   const int h = lane >> 5;
-  float a[64];  // channel 64 h + v of the token, centred for keys
-#pragma unroll
-  for (int q = 0; q < 8; ++q)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int v = 8 * q + e;
-      if (kIn == 0) {
-        const uint32_t word = raw.w[q][e >> 1];
-        a[v] = __uint_as_float((e & 1) ? (word & 0xffff0000u) : (word << 16));
-      } else {
-        a[v] = __uint_as_float(raw.w[2 * q + (e >> 2)][e & 3]);
-      }
-    }
-  if (kT == 0) {  // key centering (fp32)
+  // bf16 values scale exactly into fp16: they need no low part (kvq_rot.h)
+  constexpr bool kBf16Values = kIn == 0 && kT == 1 && kRot == 0;
+  float a[64];  // channel 64 h + v of the token, centred for keys (unused for bf16 values)
+  if (!kBf16Values) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const float4v m4 = *reinterpret_cast<const float4v*>(centre + 64 * h + 4 * q);
+      float4v m4 = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (kT == 0) m4 = *reinterpret_cast<const float4v*>(centre + 64 * h + 4 * q);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) a[4 * q + e] = a[4 * q + e] - m4[e];
+      for (int e = 0; e < 4; ++e) {
+        const int v = 4 * q + e;
+        const uint32_t word = kIn == 0 ? raw.w[v >> 3][(v & 7) >> 1] : raw.w[q][e];
+        const float x = kIn == 0 ? __uint_as_float((v & 1) ? (word & 0xffff0000u) : (word << 16)) : __uint_as_float(word);
+        a[v] = x - m4[e];  // key centering (fp32); values use centre 0
+      }
     }
   }
   float c[64];
   float u = 1.0f;
   if (kRot == 0) {
-    float amax = 0.0f;
+    float amax;
+    if (kBf16Values) {  // the largest magnitude from the bf16 bits (sign cleared, compared as integers)
+      uint16_v2 m2 = {0, 0};
 #pragma unroll
-    for (int v = 0; v < 64; ++v) amax = fmaxf(amax, fabsf(a[v]));
+      for (int q = 0; q < 8; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(uint16_v2, raw.w[q][i] & 0x7fff7fffu));
+      amax = __uint_as_float(static_cast<uint32_t>(m2[0] > m2[1] ? m2[0] : m2[1]) << 16);
+    } else {
+      amax = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 64; ++v) amax = fmaxf(amax, fabsf(a[v]));
+    }
     float p, q;
     swap32(amax, p, q);
     const float rs = row_split_scale(fmaxf(p, q));
     u = 1.0f / (rs * kRotScale);  // a power of two: exact
-    constexpr bool kLo = !(kIn == 0 && kT == 1);  // bf16 values scale exactly into fp16
+    constexpr bool kLo = !kBf16Values;
     half8 b_hi[8], b_lo[8];
+    if (kBf16Values) {
+      // rs as a bf16 in either half: the dot product with it scales one element exactly
+      const uint32_t rs_bits = __float_as_uint(rs) >> 16;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+      for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if (kLo) {
+        for (int e = 0; e < 8; ++e) {
+          b_hi[ks][e] = static_cast<_Float16>(bf16_pick_scale(raw.w[ks][e >> 1], (e & 1) != 0, rs_bits));
+          b_lo[ks][e] = 0;
+        }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
           _Float16 hh, ll;
           split_scaled(a[8 * ks + e], rs, hh, ll);
           b_hi[ks][e] = hh;
           b_lo[ks][e] = ll;
-        } else {
-          b_hi[ks][e] = static_cast<_Float16>(a[8 * ks + e] * rs);
-          b_lo[ks][e] = 0;
         }
-      }
+    }
     float16v acc[4];
     rotate32<kLo>(b_hi, b_lo, op, lane, acc);
 #pragma unroll
@@ -510,15 +583,18 @@ __device__ __forceinline__ void bulk_tensor(const BulkRaw<kIn>& raw, const half8
       c[v] = fmaf(hi, sg, lo) * kInvSqrt128;
     }
   }
-  if ((kT == 0 ? kbits : vbits) > 2)
-    bulk_store<kT, true>(c, u, pool, num_pages, num_kv_heads, hd, n, n_tokens, slots, rot_out, clip, gsize, sq_err,
-                         kbits, vbits, lane);
+  next();
+  if (!kImg && (kT == 0 ? kbits : vbits) > 2)
+    bulk_store<kT, true, false>(c, u, pool, num_pages, num_kv_heads, hd, n, slot, rot_out, clip, gsize, sq_err, kbits,
+                                vbits, lane, img);
   else
-    bulk_store<kT, false>(c, u, pool, num_pages, num_kv_heads, hd, n, n_tokens, slots, rot_out, clip, gsize, sq_err,
-                          kbits, vbits, lane);
+    bulk_store<kT, false, kImg>(c, u, pool, num_pages, num_kv_heads, hd, n, slot, rot_out, clip, gsize, sq_err, kbits,
+                                vbits, lane, img);
 }
 
-template <int kIn, int kRot>  // kIn: 0 = bf16, 1 = fp32; kRot: 0 = dense R, 1 = Hadamard signs
+// kNarrow: 2-bit keys and values (the tile goes through the wave's LDS
+// image); otherwise 3- or 4-bit codes in either tensor, stored slot by slot.
+template <int kIn, int kRot, bool kNarrow>  // kIn: 0 = bf16, 1 = fp32; kRot: 0 = dense R, 1 = Hadamard signs
 __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
     uint8_t* __restrict__ pool, int num_pages, int num_kv_heads, const void* __restrict__ k_in,
     const void* __restrict__ v_in, int n_tokens, const int32_t* __restrict__ slots, const float* __restrict__ mu,
@@ -532,6 +608,10 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
   constexpr int kOps = 32 * 2 * 64;  // half8 operands of one R
   __shared__ half8 s_op[kRot == 0 ? 2 * kOps : 1];  // R_K then R_V, 128 KB (dense R only)
   __shared__ float s_vec[3][kHeadDim];              // key centre; Hadamard signs of K and V
+  constexpr int kImgChunks = kNarrow ? 2 * kBlockBytes / 16 : 1;
+  __shared__ uint4v s_img[kBulkWaves][kImgChunks];  // each wave's image of two 2-bit blocks
+  __shared__ int s_next;                            // the workgroup's next unclaimed tile index j
+  if (tid == 0) s_next = kBulkWaves;
 
   if (kRot == 0) {
     stage_rotation_t(r_k + static_cast<size_t>(hd) * kHeadDim * kHeadDim, s_op, wave, kBulkWaves, lane);
@@ -550,25 +630,109 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
 
   const int n_tiles = (n_tokens + kBulkTok - 1) / kBulkTok;
   const int stride = gridDim.x * kBulkWaves;
-  int tile = blockIdx.x * kBulkWaves + wave;
+  // The workgroup's tiles are blockIdx.x * 8 + (j % 8) + stride * (j / 8),
+  // j = 0, 1, ..; its waves start with j = wave and then claim the next j
+  // from an LDS counter, so a wave that issues less often takes fewer tiles.
+  auto tile_of = [&](int j) { return blockIdx.x * kBulkWaves + j % kBulkWaves + stride * (j / kBulkWaves); };
+  int tile = tile_of(wave);
   if (tile >= n_tiles) return;  // no barrier follows
   const int nl = lane & 31;
-  constexpr bool kPrefetch = kIn == 0;  // fp32 rows are loaded where they are used (registers)
+  uint8_t* img = reinterpret_cast<uint8_t*>(&s_img[wave][0]);
+  // bf16 rows are loaded one tensor ahead (32 registers); fp32 rows, twice
+  // the registers, where they are used.  A tile's slots come with its key
+  // rows, so that no wait for them also waits for stores issued later.
+  constexpr bool kAhead = kIn == 0;
   BulkRaw<kIn> rk, rv;
-  bulk_load<kIn>(rk, k_in, kBulkTok * tile + nl, n_tokens, num_kv_heads, hd, h);
-  for (; tile < n_tiles; tile += stride) {
+  int slot = 0;
+  auto load_keys = [&](int t) {
+    const int n = kBulkTok * t + nl;
+    slot = n < n_tokens ? slots[n] : -1;
+    bulk_load<kIn>(rk, k_in, n, n_tokens, num_kv_heads, hd, h);
+  };
+  if (kAhead) load_keys(tile);
+  // The tile's image is copied out at the top of the next tile (and after the
+  // last), once that tile's rows have arrived: the copy-out's stores then
+  // come after the wait for those loads, and no later wait for loads finds
+  // them still in flight.
+  auto copy_out = [&](int sl) {
+    // the image was written by this wave only: order those LDS writes before
+    // the reads that copy it out
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // Whole pages: the tile's 32 tokens fill two distinct pages in order
+    // (token n at slot 16 page + n % 16); each block is then stored as whole
+    // lines, 16 B per lane (chunks 0..63, then 64..95).
+    const int s0 = __builtin_amdgcn_readlane(sl, 0), s16 = __builtin_amdgcn_readlane(sl, 16);
+    const int page = nl < 16 ? (s0 >> 4) : (s16 >> 4);
+    const bool mine = sl >= 0 && sl < num_pages * kPage && sl == kPage * page + (nl & 15);
+    if ((s0 >> 4) != (s16 >> 4) && __ballot(mine) == ~0ull) {
+      constexpr int kChunks = kBlockBytes / 16;  // 96 per block
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        uint4v* dst = reinterpret_cast<uint4v*>(
+            pool + (static_cast<size_t>((b ? s16 : s0) >> 4) * num_kv_heads + hd) * kBlockBytes);
+        dst[lane] = s_img[wave][b * kChunks + lane];
+        if (lane < kChunks - 64) dst[64 + lane] = s_img[wave][b * kChunks + 64 + lane];
+      }
+    } else if (sl >= 0 && sl < num_pages * kPage) {
+      // Otherwise each token's own bytes go to its slot: lane (h, n) copies
+      // K records 2h, 2h + 1, V half-words b = 8h .. 8h + 7 and the metadata
+      // of groups 2h, 2h + 1 (16-bit V stores keep the other slot of a word).
+      const uint8_t* ib = img + kBlockBytes * (nl >> 4);
+      const int io = nl & 15, off = sl & 15;
+      uint8_t* blk = pool + (static_cast<size_t>(sl >> 4) * num_kv_heads + hd) * kBlockBytes;
+#pragma unroll
+      for (int a = 2 * h; a < 2 * h + 2; ++a)
+        *reinterpret_cast<uint2*>(blk + 16 * (16 * a + off)) = *reinterpret_cast<const uint2*>(ib + 16 * (16 * a + io));
+#pragma unroll
+      for (int b = 8 * h; b < 8 * h + 8; ++b)
+        *reinterpret_cast<uint16_t*>(blk + 16 * (16 * (off >> 2) + b) + 8 + 4 * ((off & 3) >> 1) + 2 * (off & 1)) =
+            *reinterpret_cast<const uint16_t*>(ib + 16 * (16 * (io >> 2) + b) + 8 + 4 * ((io & 3) >> 1) +
+                                               2 * (io & 1));
+#pragma unroll
+      for (int g = 2 * h; g < 2 * h + 2; ++g)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          *reinterpret_cast<uint32_t*>(blk + kCodeBytes + kMetaRecordBytes * (4 * g + (off >> 2)) + 16 * t +
+                                       4 * (off & 3)) =
+              *reinterpret_cast<const uint32_t*>(ib + kCodeBytes + kMetaRecordBytes * (4 * g + (io >> 2)) + 16 * t +
+                                                 4 * (io & 3));
+    }
+    // the next tile's image writes come after these reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  int prev_slot = -1;
+  bool have_prev = false;
+  for (;;) {
     const int n = kBulkTok * tile + nl;
-    if (kPrefetch) bulk_load<kIn>(rv, v_in, n, n_tokens, num_kv_heads, hd, h);
-    bulk_tensor<kIn, kRot, 0>(rk, s_op, s_vec[0], s_vec[1], pool, num_pages, num_kv_heads, hd, n, n_tokens, slots,
-                              rot_out, clip, gsize, sq_err, kbits, vbits, lane);
-    if (!kPrefetch) bulk_load<kIn>(rv, v_in, n, n_tokens, num_kv_heads, hd, h);
-    if (tile + stride < n_tiles && kPrefetch)
-      bulk_load<kIn>(rk, k_in, kBulkTok * (tile + stride) + nl, n_tokens, num_kv_heads, hd, h);
-    bulk_tensor<kIn, kRot, 1>(rv, s_op + kOps, s_vec[0], s_vec[2], pool, num_pages, num_kv_heads, hd, n, n_tokens,
-                              slots, rot_out, clip, gsize, sq_err, kbits, vbits, lane);
-    if (!kPrefetch && tile + stride < n_tiles)
-      bulk_load<kIn>(rk, k_in, kBulkTok * (tile + stride) + nl, n_tokens, num_kv_heads, hd, h);
+    if (!kAhead) load_keys(tile);
+    const int cur_slot = slot;
+    // this tile's rows and slots are here (s_waitcnt vmcnt(0), every other
+    // counter left alone) before the previous tile's stores are issued
+    if (kNarrow) __builtin_amdgcn_s_waitcnt(0x0f70);
+    if (kNarrow && have_prev) copy_out(prev_slot);
+    int next_tile = n_tiles;
+    bulk_tensor<kIn, kRot, 0, kNarrow>(rk, s_op, s_vec[0], s_vec[1], pool, num_pages, num_kv_heads, hd, n, cur_slot,
+                                       rot_out, clip, gsize, sq_err, kbits, vbits, lane, img, [&]() {
+                                         if (kAhead) bulk_load<kIn>(rv, v_in, n, n_tokens, num_kv_heads, hd, h);
+                                       });
+    if (!kAhead) bulk_load<kIn>(rv, v_in, n, n_tokens, num_kv_heads, hd, h);
+    bulk_tensor<kIn, kRot, 1, kNarrow>(rv, s_op + kOps, s_vec[0], s_vec[2], pool, num_pages, num_kv_heads, hd, n,
+                                       cur_slot, rot_out, clip, gsize, sq_err, kbits, vbits, lane, img, [&]() {
+                                         int j = 0;
+                                         if (lane == 0) j = atomicAdd(&s_next, 1);
+                                         next_tile = tile_of(__builtin_amdgcn_readfirstlane(j));
+                                         if (kAhead && next_tile < n_tiles) load_keys(next_tile);
+                                       });
+    prev_slot = cur_slot;
+    have_prev = true;
+    if (next_tile >= n_tiles) break;
+    tile = next_tile;
   }
+  if (kNarrow) copy_out(prev_slot);
 }
 
 hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const void* k, const void* v, int in_kind,
@@ -584,8 +748,11 @@ hipError_t launch_append(uint8_t* pool, int num_pages, int num_kv_heads, const v
     const int per = std::max(1, std::min((n_tiles + kBulkWaves - 1) / kBulkWaves,
                                          (256 + num_kv_heads - 1) / num_kv_heads));
     const dim3 bgrid(per, num_kv_heads);
-    auto kern = in_kind == 0 ? (rot_kind == 0 ? append_bulk_kernel<0, 0> : append_bulk_kernel<0, 1>)
-                             : (rot_kind == 0 ? append_bulk_kernel<1, 0> : append_bulk_kernel<1, 1>);
+    const bool narrow = kbits == 2 && vbits == 2;
+    auto kern = narrow ? (in_kind == 0 ? (rot_kind == 0 ? append_bulk_kernel<0, 0, true> : append_bulk_kernel<0, 1, true>)
+                                       : (rot_kind == 0 ? append_bulk_kernel<1, 0, true> : append_bulk_kernel<1, 1, true>))
+                       : (in_kind == 0 ? (rot_kind == 0 ? append_bulk_kernel<0, 0, false> : append_bulk_kernel<0, 1, false>)
+                                       : (rot_kind == 0 ? append_bulk_kernel<1, 0, false> : append_bulk_kernel<1, 1, false>));
     hipLaunchKernelGGL(kern, bgrid, dim3(kBulkThreads), 0, stream, pool, num_pages, num_kv_heads, k, v, n_tokens, slots,
                        mu, r_k, r_v, rot_out, clip, gsize, sq_err, kbits, vbits);
     return hipGetLastError();
