@@ -679,19 +679,24 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
       // Otherwise each token's own bytes go to its slot: lane (h, n) copies
       // K records 2h, 2h + 1, V half-words b = 8h .. 8h + 7 and the metadata
       // of groups 2h, 2h + 1 (16-bit V stores keep the other slot of a word).
-      const uint8_t* ib = img + kBlockBytes * (nl >> 4);
-      const int io = nl & 15, off = sl & 15;
+      // (addresses formed here from an opaque lane index: hoisted out of the
+      // tile loop they would only take registers from the common path)
+      int lid = lane;
+      asm volatile("" : "+v"(lid));
+      const int hh = lid >> 5, ln = lid & 31;
+      const uint8_t* ib = img + kBlockBytes * (ln >> 4);
+      const int io = ln & 15, off = sl & 15;
       uint8_t* blk = pool + (static_cast<size_t>(sl >> 4) * num_kv_heads + hd) * kBlockBytes;
 #pragma unroll
-      for (int a = 2 * h; a < 2 * h + 2; ++a)
+      for (int a = 2 * hh; a < 2 * hh + 2; ++a)
         *reinterpret_cast<uint2*>(blk + 16 * (16 * a + off)) = *reinterpret_cast<const uint2*>(ib + 16 * (16 * a + io));
 #pragma unroll
-      for (int b = 8 * h; b < 8 * h + 8; ++b)
+      for (int b = 8 * hh; b < 8 * hh + 8; ++b)
         *reinterpret_cast<uint16_t*>(blk + 16 * (16 * (off >> 2) + b) + 8 + 4 * ((off & 3) >> 1) + 2 * (off & 1)) =
             *reinterpret_cast<const uint16_t*>(ib + 16 * (16 * (io >> 2) + b) + 8 + 4 * ((io & 3) >> 1) +
                                                2 * (io & 1));
 #pragma unroll
-      for (int g = 2 * h; g < 2 * h + 2; ++g)
+      for (int g = 2 * hh; g < 2 * hh + 2; ++g)
 #pragma unroll
         for (int t = 0; t < 2; ++t)
           *reinterpret_cast<uint32_t*>(blk + kCodeBytes + kMetaRecordBytes * (4 * g + (off >> 2)) + 16 * t +
