@@ -76,5 +76,34 @@ def build(verbose: bool = False) -> str:
     return _link(SOURCES, LIB, verbose)
 
 
+# A host-sanitized variant for the CPU checks of the C ABI: the host-only source
+# (argument validation, sizes, workspace layout) is compiled with g++ under
+# AddressSanitizer and UndefinedBehaviorSanitizer and linked with the device
+# objects of the last build(); load it with gcc's libasan preloaded.  It is a
+# test artefact, never loaded by the package.
+HOST_SOURCES = ["kvq_api.cpp"]
+SANITIZED_LIB = os.path.join(HERE, "_build", "libkvq_hostsan.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined"]
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """Link _build/libkvq_hostsan.so: sanitized host objects plus build()'s device objects."""
+    obj_dir = os.path.join(HERE, "_build")
+    dev_objs = [os.path.join(obj_dir, os.path.splitext(s)[0] + ".o") for s in SOURCES if s not in HOST_SOURCES]
+    if not all(os.path.exists(o) for o in dev_objs):
+        build(verbose)
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    host_objs = []
+    for src in HOST_SOURCES:
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".hostsan.o")
+        _run(["g++", "-std=c++17", "-O1", "-g", "-fPIC", *SAN_FLAGS, "-D__HIP_PLATFORM_AMD__", "-I",
+              os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-c",
+              os.path.join(CSRC, src), "-o", obj], verbose)
+        host_objs.append(obj)
+    _run(["g++", "-shared", *SAN_FLAGS, *host_objs, *dev_objs, "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+          "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", SANITIZED_LIB], verbose)
+    return SANITIZED_LIB
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

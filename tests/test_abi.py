@@ -24,7 +24,9 @@ def K():
         from rotated_int2_kv_centering_amd import build
 
         build.build()
-    kvq.load()
+    # KVQ_TEST_LIB: another build of the same library (the host-sanitized one, see
+    # test_host_sanitizers.py)
+    kvq.load(os.environ.get("KVQ_TEST_LIB", kvq.LIB_PATH))
     return kvq
 
 
