@@ -271,7 +271,7 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
  *               attended from the window buffer (read only here), the others
  *               from the cache.  The buffer's slots of every window position
  *               must hold that position's key and value (kvq_window_fill,
- *               kvq_decode_step).  Supported for g <= 8.
+ *               kvq_decode_step).  Any g (up to 16, as without a window).
  * Value range: every scale and zero the cache format stores (any finite fp16).
  * The P.V product runs on the matrix cores with the fp16 operand p * s_v (p a
  * softmax weight, s_v a value group's scale); the kernel keeps that operand in

@@ -268,7 +268,6 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
     if (st != KVQ_OK) return st;
     if (window->batch < batch)
       return fail(KVQ_EINVAL, "window holds %d sequences, the call has %d", window->batch, batch);
-    if (g > 8) return fail(KVQ_EUNSUPPORTED, "an exact window needs g <= 8 (g=%d)", g);
   }
   kvq::DecodePlan plan;
   if (!make_plan(batch, cache->num_kv_heads, g, max_seq_len, num_splits, &plan,

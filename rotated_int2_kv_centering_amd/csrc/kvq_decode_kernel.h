@@ -964,16 +964,17 @@ void decode_kernel(const DecodeParams p) {
     }
   }
 
-  // Exact window (g <= 8), on the matrix cores (v_mfma_f32_16x16x32_bf16; the
-  // window rows are exact bf16), computed by the workgroup of the sequence's
-  // last split after its page loop and stored to the workspace before its
-  // ticket (the window row of each query head: acc 128 | max | sum, acc
-  // unnormalised and in the original basis); the merging workgroup loads it
-  // with the split rows.  Rows: n_ws sinks, then positions w_r0 .. T-1,
-  // staged in the upper part of the ring (row-major, 512 B per row: the key,
-  // whose 16-byte chunks are XOR-swizzled by row % 16, then the value), above
-  // the merge's max/sum pairs (at most 2 * kNH * (max splits with a window)
-  // floats); the R_V^T partials later reuse the rows' space.
+  // Exact window, on the matrix cores (v_mfma_f32_16x16x32_bf16; the window
+  // rows are exact bf16), computed by the workgroup of the sequence's last
+  // split after its page loop and stored to the workspace before its ticket
+  // (the window row of each query head: acc 128 | max | sum, acc unnormalised
+  // and in the original basis); the merging workgroup loads it with the split
+  // rows.  Rows: n_ws sinks, then positions w_r0 .. T-1, loaded whole into
+  // registers, then staged in the upper part of the ring 256 B per row: first
+  // the keys (16-byte chunks XOR-swizzled by row % 16) for the logits, then
+  // the values in the same place for the value sums; above the merge's
+  // max/sum pairs (at most 2 * kNH * (max splits with a window) floats); the
+  // R_V^T partials later reuse the rows' space.
   //   logits  C[head][row] = <q_head, k_row> over 16-row tiles: A = q split
   //           into three bf16 parts (truncation; about 21 bits), B = key rows;
   //           <q_head, mu> is taken off in fp32.
@@ -981,7 +982,7 @@ void decode_kernel(const DecodeParams p) {
   //           and 32-row blocks: A = p in two bf16 parts, B = values.
   // Both splits are made once into LDS in operand order.  Rows past n_w read
   // row n_w - 1 (finite) and carry weight 0.
-  constexpr bool kWinOk = kNQ <= 2;
+  constexpr bool kWinOk = true;
   constexpr int kWinMax = 8 + 128;                    // window rows
   constexpr int kWinLd = kWinOk ? (kWinMax * 32 + kThreads - 1) / kThreads : 1;  // 16-byte chunks per thread
   constexpr int kWinRowsPad = 32 * ((kWinMax + 31) / 32);  // 32-row blocks of the value product
@@ -991,7 +992,7 @@ void decode_kernel(const DecodeParams p) {
   constexpr int kRingFloats = static_cast<int>(sizeof(s_ring) / sizeof(float));
   constexpr int kOwOff = kRingFloats - kNH * kHeadDim;  // [kNH][128] window value sums
   constexpr int kWmlOff = kOwOff - 2 * kNH;             // [kNH][2] window max, sum of weights
-  constexpr int kRowsOff = kWmlOff - kWinMax * kHeadDim;  // [kWinMax][2][128] bf16 rows
+  constexpr int kRowsOff = kWmlOff - kWinMax * kHeadDim / 2;  // [kWinMax][128] bf16 rows (keys, then values)
   constexpr int kWpOff = kRowsOff - kNH * kHeadRow;     // [kNH][kHeadRow]
   constexpr int kQpOff = kWpOff - 3 * kNH * kQpStride / 2;  // [3][kNH][kQpStride] bf16 q parts
   constexpr int kWmuOff = kQpOff - kHeadDim - kNH;      // [128] mu, then [kNH] <q, mu>
@@ -1065,15 +1066,15 @@ void decode_kernel(const DecodeParams p) {
     if (tid < kHeadDim && p.win_mu != nullptr) wmu = p.win_mu[h * kHeadDim + tid];
   }
   if (win_wg) __syncthreads();  // the per-wave partials were read; the ring takes the window rows
-  uint4v* const s_rows = reinterpret_cast<uint4v*>(s_post + kRowsOff);  // 32 chunks per row
+  uint4v* const s_rows = reinterpret_cast<uint4v*>(s_post + kRowsOff);  // 16 chunks per row
   float* const s_wp = s_post + kWpOff;
   uint16_t* const s_qp = reinterpret_cast<uint16_t*>(s_post + kQpOff);
   if (win_wg) {
 #pragma unroll
-    for (int u = 0; u < kWinLd; ++u) {
+    for (int u = 0; u < kWinLd; ++u) {  // the keys
       const int idx = tid + u * kThreads;
       const int wi = idx >> 5, j = idx & 31;
-      if (wi < n_w) s_rows[32 * wi + (j < 16 ? (j ^ (wi & 15)) : j)] = wraw[u];
+      if (wi < n_w && j < 16) s_rows[16 * wi + (j ^ (wi & 15))] = wraw[u];
     }
 #pragma unroll
     for (int u = 0; u < kQPerThread; ++u) {  // the query rows as given, and their three bf16 parts
@@ -1111,7 +1112,7 @@ void decode_kernel(const DecodeParams p) {
       float4v C = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const bf16x8 kB = __builtin_bit_cast(bf16x8, s_rows[32 * wi + ((4 * kb + kq) ^ (wi & 15))]);
+        const bf16x8 kB = __builtin_bit_cast(bf16x8, s_rows[16 * wi + ((4 * kb + kq) ^ (wi & 15))]);
 #pragma unroll
         for (int sp = 0; sp < 3; ++sp) {
           const uint4v qa = hq < kNH ? *reinterpret_cast<const uint4v*>(s_qp + (sp * kNH + hq) * kQpStride + 32 * kb +
@@ -1128,6 +1129,13 @@ void decode_kernel(const DecodeParams p) {
       }
     }
     __syncthreads();
+    // the keys were read: the values take their place (the softmax below reads only the logits)
+#pragma unroll
+    for (int u = 0; u < kWinLd; ++u) {
+      const int idx = tid + u * kThreads;
+      const int wi = idx >> 5, j = idx & 31;
+      if (wi < n_w && j >= 16) s_rows[16 * wi + (j - 16)] = wraw[u];
+    }
     // per head (one wave): logits (log2 units) = (<q, k> - <q, mu>) * scale, max, weights
     // exp2(logit - max) split into bf16 hi | lo over the same row (all reads first), their sum
     const int n_wpad = 32 * ((n_w + 31) / 32);
@@ -1164,9 +1172,9 @@ void decode_kernel(const DecodeParams p) {
       }
     }
     __syncthreads();
-    // value sums: wave w < 8 takes channels 16 w .. +16; A = weights (hi, lo), B = values
-    if (wave < kHeadDim / 16) {
-      const uint16_t* vrows = reinterpret_cast<const uint16_t*>(s_rows) + kHeadDim + 16 * wave + hq;
+    // value sums: channels 16 cw .. +16 for cw = wave, wave + kW, ..; A = weights (hi, lo), B = values
+    for (int cw = wave; cw < kHeadDim / 16; cw += kW) {
+      const uint16_t* vrows = reinterpret_cast<const uint16_t*>(s_rows) + 16 * cw + hq;
       const uint16_t* prow = reinterpret_cast<const uint16_t*>(s_wp + (hq < kNH ? hq : 0) * kHeadRow);
       float4v C = {0.0f, 0.0f, 0.0f, 0.0f};
       for (int kb = 0; kb < n_wpad / 32; ++kb) {
@@ -1174,8 +1182,7 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           const int w0 = min(32 * kb + 8 * kq + 2 * e2, n_w - 1), w1 = min(32 * kb + 8 * kq + 2 * e2 + 1, n_w - 1);
-          vv[e2] = static_cast<uint32_t>(vrows[w0 * 2 * kHeadDim]) |
-                   (static_cast<uint32_t>(vrows[w1 * 2 * kHeadDim]) << 16);
+          vv[e2] = static_cast<uint32_t>(vrows[w0 * kHeadDim]) | (static_cast<uint32_t>(vrows[w1 * kHeadDim]) << 16);
         }
         const bool live = hq < g;
         const uint4v ph = live ? *reinterpret_cast<const uint4v*>(prow + 32 * kb + 8 * kq) : uint4v{0u, 0u, 0u, 0u};
@@ -1188,7 +1195,7 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int jh = 4 * kq + i;
-        if (jh < g) s_post[kOwOff + jh * kHeadDim + 16 * wave + hq] = C[i];
+        if (jh < g) s_post[kOwOff + jh * kHeadDim + 16 * cw + hq] = C[i];
       }
     }
     __syncthreads();

@@ -272,7 +272,9 @@ def test_window_bytes_and_host_validation(K):
     assert _decode(K, c, window=W(4, 4, 1, None)) == K.KVQ_EINVAL          # no buffer
     assert _decode(K, c, window=W(4, 4, 1, FAKE + 8)) == K.KVQ_EINVAL      # misaligned buffer
     assert _decode(K, c, batch=2, window=W(4, 4, 1, FAKE)) == K.KVQ_EINVAL  # holds one sequence
-    assert _decode(K, c, hq=16, window=W(4, 4, 1, FAKE)) == K.KVQ_EUNSUPPORTED  # g = 16
+    # g = 16 with a window passes validation (without a GPU the call then stops at
+    # its first HIP runtime query)
+    assert _decode(K, c, hq=16, window=W(4, 4, 1, FAKE)) not in (K.KVQ_EINVAL, K.KVQ_EUNSUPPORTED)
     lib = K.load()
     w = W(4, 4, 2, FAKE)
     fill = lib.kvq_window_fill

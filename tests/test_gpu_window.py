@@ -85,6 +85,10 @@ WSHAPES = [
     (3, 32, 8, [1000, 16, 257], 4, 128),
     (2, 64, 8, [513, 1024], 4, 128),  # g = 8
     (2, 2, 2, [77, 300], 2, 32),      # g = 1
+    (2, 12, 1, [900, 40], 4, 128),    # g = 12
+    (2, 16, 1, [1500, 130], 4, 128),  # g = 16, the largest
+    (1, 64, 4, [2000], 8, 128),       # g = 16 at the largest window
+    (2, 16, 1, [5, 300], 8, 0),       # g = 16, sinks only, a sequence below them
 ]
 
 
@@ -150,15 +154,15 @@ def test_full_size_window_sampled_heads():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("sinks,recent", [(4, 16), (4, 0), (0, 1)])
-def test_step_with_window(dtype, sinks, recent):
+@pytest.mark.parametrize("sinks,recent,hq", [(4, 16, 8), (4, 0, 8), (0, 1, 8), (4, 16, 32)])
+def test_step_with_window(dtype, sinks, recent, hq):
     """kvq_decode_step with a window: the cache bytes equal kvq_quant_append of the
     new tokens, the new token's window slot holds its bf16 rows, and the output
     matches the oracle with every window position exact."""
     from rotated_int2_kv_centering_amd import kvq
     import torch
     dev = require_gpu()
-    case = I.make_case("ws", 80 + sinks + recent, B=3, Hq=8, Hkv=2, seq_lens=[40, 3, 17], dtype=dtype,
+    case = I.make_case("ws", 80 + sinks + recent + hq, B=3, Hq=hq, Hkv=2, seq_lens=[40, 3, 17], dtype=dtype,
                        table_policy="interleaved")
     newest = np.array([np.nonzero(case.tok_seq == b)[0][-1] for b in range(case.B)])
     old = np.setdiff1d(np.arange(case.n_tokens), newest)
@@ -183,7 +187,8 @@ def test_step_with_window(dtype, sinks, recent):
     assert max_abs_rel(got, ref) <= TOL
 
 
-@pytest.mark.parametrize("shape", [(1, 4, 1, [2000], 64), (1, 64, 8, [3000], 40), (2, 32, 8, [900, 1500], 24)],
+@pytest.mark.parametrize("shape", [(1, 4, 1, [2000], 64), (1, 64, 8, [3000], 40), (2, 32, 8, [900, 1500], 24),
+                                   (1, 32, 2, [3000], 40)],
                          ids=lambda s: f"Hq{s[1]}_Hkv{s[2]}_T{'-'.join(map(str, s[3]))}_ns{s[4]}")
 def test_decode_window_many_splits(shape):
     """Enough splits that the merging workgroup cannot stage the partial rows and
