@@ -40,7 +40,8 @@ the design notes of the repository):
 Packed page layout.  The pages fix only that rotation keeps a regular paged
 layout; the byte layout below is this repository's format, stated here in
 full so the oracle can be read without any other file.  One block holds the 16
-token slots of one (page p, KV head h) and starts at byte (p*H_kv + h)*1536:
+token slots of one (page p, KV head h) and starts at byte (p*H_kv + h)*B,
+B the block size below:
 
 * bytes [0, 1024): 64 records of 16 bytes.  Record r = 16*a + b
   (a in 0..3, b in 0..15) is four little-endian uint32 words at byte 16*r:
@@ -50,26 +51,33 @@ token slots of one (page p, KV head h) and starts at byte (p*H_kv + h)*1536:
   - V code of slot s, channel c: t = c // 16, b = c % 16, a = s // 4,
     i = s % 4; record 16*a + b, word V[i // 2], bit 2*t + 16*(i % 2).
   Each code occupies that bit and the one above it (low bit first).
-* bytes [1024, 1536): 16 records of 32 bytes.  Record m = 4*grp + a holds,
-  for the four slots s = 4*a + i (i in 0..3) and channel group grp
-  (channels 32*grp .. 32*grp+31): at byte 1024 + 32*m + 4*i the K pair and at
-  byte 1024 + 32*m + 16 + 4*i the V pair, each pair being the fp16 scale
-  (low two bytes) then the fp16 zero, little-endian.
+* bytes [1024, 1024 + M), M = 128 * (128 / G) (512, 256 or 128 bytes for
+  G = 32, 64, 128): 128 / G * 4 records of 32 bytes.  Record m = 4*grp + a
+  holds, for the four slots s = 4*a + i (i in 0..3) and channel group grp
+  (channels G*grp .. G*grp + G - 1): at byte 1024 + 32*m + 4*i the K pair and
+  at byte 1024 + 32*m + 16 + 4*i the V pair, each pair being the fp16 scale
+  (low two bytes) then the fp16 zero, little-endian.  The base block is
+  1024 + M bytes: 96, 80 or 72 bytes per token and KV head.
 
-With 4-bit keys (key_bits = 4, a K4V2 budget) a block is 2048 bytes; 3-bit
-keys (key_bits = 3, the page's K3V2 budget) use the same block, their high
-part being a single bit.  The 1536 bytes above keep their layout, the K words holding the low
-two bits of each key code (code & 3); bytes [1536, 2048) are 64 records of 8
-bytes, record r = 16*a + s holding words H0, H1 at byte 1536 + 8*r: the high
-two bits (code >> 2) of the key code of slot s, channel c sit in record
-16*a + s, word H[kk // 2], at the same bit as its low bits in K[kk // 2].
+Keys or values of 3 or 4 bits (key_bits, val_bits: the page's K3V2, K3V3 and
+K4V2 budgets) keep the low two bits of each code (code & 3) in the words
+above and the rest in a plane appended to the block, the keys' plane first
+(at P_K = 1024 + M), then the values' (at P_V = P_K + the keys' plane size):
 
-Values of 3 or 4 bits (val_bits; K3V3 is the page's symmetric budget) add
-another 512-byte plane after the keys' plane, at P = 1536 (2-bit keys) or
-P = 2048 (wider keys), so a K3V3 block is 2560 bytes.  Its 64 records of 8
-bytes hold words VH0, VH1 at byte P + 8*r: the high bits of the V code of slot
-s, channel c sit in record 16*a + b, word VH[i // 2], at the same bit as its
-low bits in V[i // 2].
+* 4 bits: a 512-byte plane, 64 records of 8 bytes.  Record r holds words
+  H0, H1 (keys) or VH0, VH1 (values) at byte P + 8*r: the high two bits
+  (code >> 2) of a code sit in the same record and word index as its low
+  bits (record 16*a + s, word H[kk // 2] for the key of slot s, channel c;
+  record 16*a + b, word VH[i // 2] for the value), at the same bit.
+* 3 bits: a 256-byte plane, 64 records of 4 bytes, one word W per record at
+  byte P + 4*r holding the high bit (code >> 2) of every code of the record:
+  keys: the code at bit j of word K[w] (j even) has its high bit at bit
+  j + w of W (the two K words interleaved); values: the code of slot
+  4*a + i, channel 16*t + b (record 16*a + b) has its high bit at bit 8*i + t
+  of W (one byte per slot).
+
+So a K2V2 block is 1536 bytes for G = 32, a K3V3 block 2048 (128 bytes per
+token) and a K4V2 block 2048.
 """
 
 from __future__ import annotations
@@ -80,21 +88,34 @@ HEAD_DIM = 128
 GROUP = 32
 N_GROUPS = HEAD_DIM // GROUP
 PAGE = 16
-BLOCK_BYTES = 1536
 CODE_BYTES = 1024
-HI_PLANE = 1536  # byte offset of the 4-bit keys' high-bit plane
 
 
-def block_bytes(key_bits: int = 2, val_bits: int = 2) -> int:
-    """Bytes of one (page, KV head) block: 1536, plus 512 for 3- or 4-bit keys and
-    512 for 3- or 4-bit values."""
-    assert key_bits in (2, 3, 4) and val_bits in (2, 3, 4), "codes are 2, 3 or 4 bits"
-    return BLOCK_BYTES + 512 * (key_bits > 2) + 512 * (val_bits > 2)
+def meta_bytes(group: int = GROUP) -> int:
+    """Metadata bytes of a block: 16 slots x (K, V) x 4 bytes per group."""
+    assert group in (32, 64, 128), "group size must be 32, 64 or 128"
+    return PAGE * 2 * 4 * (HEAD_DIM // group)
 
 
-def value_plane(key_bits: int = 2) -> int:
-    """Byte offset of the wide values' high-bit plane: after the keys' plane, if any."""
-    return HI_PLANE + 512 * (key_bits > 2)
+def plane_bytes(bits: int) -> int:
+    """Bytes of the high-bit plane of 3- or 4-bit codes (none for 2-bit codes)."""
+    assert bits in (2, 3, 4), "codes are 2, 3 or 4 bits"
+    return {2: 0, 3: 256, 4: 512}[bits]
+
+
+def key_plane(group: int = GROUP) -> int:
+    """Byte offset of the keys' high-bit plane: after codes and metadata."""
+    return CODE_BYTES + meta_bytes(group)
+
+
+def value_plane(key_bits: int = 2, group: int = GROUP) -> int:
+    """Byte offset of the values' high-bit plane: after the keys' plane, if any."""
+    return key_plane(group) + plane_bytes(key_bits)
+
+
+def block_bytes(key_bits: int = 2, val_bits: int = 2, group: int = GROUP) -> int:
+    """Bytes of one (page, KV head) block: codes, metadata, then the planes."""
+    return value_plane(key_bits, group) + plane_bytes(val_bits)
 
 
 # --------------------------------------------------------------------- checks
@@ -215,14 +236,6 @@ def int2_dequantize(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.n
     return lv.reshape(codes.shape)
 
 
-def meta_per_32(a: np.ndarray) -> np.ndarray:
-    """Per-group scales (or zeros) [..., 128/G] spread over the block's four
-    32-channel metadata entries [..., 4]: each entry holds the pair of the group
-    containing its channels (the block layout keeps four pairs for every G)."""
-    a = np.asarray(a)
-    return np.repeat(a, N_GROUPS // a.shape[-1], axis=-1)
-
-
 # ------------------------------------------------------------ pack / unpack
 def _k_position(slot: int, c: int):
     kk, a, e = c // 32, (c % 32) // 8, c % 8
@@ -246,15 +259,36 @@ _K_POS = np.array([[_k_position(s, c) for c in range(HEAD_DIM)] for s in range(P
 _V_POS = np.array([[_v_position(s, c) for c in range(HEAD_DIM)] for s in range(PAGE)], dtype=np.int64)
 
 
+def _set_bits(words, idx, bit, val, width):
+    """words[idx] <- field of ``width`` bits at ``bit`` replaced by val (all arrays flat)."""
+    mask = np.uint32((1 << width) - 1)
+    np.bitwise_and.at(words, idx, ~(mask << bit))
+    np.bitwise_or.at(words, idx, (val & mask) << bit)
+
+
+def _plane_position(pos, bits: int, value: bool):
+    """Plane (word index, bit) of the codes at code-word positions pos [..., (record, word, bit)]:
+    4-bit planes mirror the code words (two words per record, same bit); 3-bit planes hold one
+    word per record, keys' high bits at bit + w (w = 0, 1 the K word), values' at 8 * i + t
+    (slot 4a + i, channel tile t)."""
+    rec, word, bit = pos[..., 0], pos[..., 1] - (2 if value else 0), pos[..., 2]
+    if bits == 4:
+        return rec * 2 + word, bit
+    if not value:
+        return rec, bit + word
+    i = 2 * word + bit // 16
+    return rec, 8 * i + (bit % 16) // 2
+
+
 def pack_block(k_codes, k_s16, k_z16, v_codes, v_s16, v_z16, block: np.ndarray | None = None,
-               slots=None, key_bits: int = 2, val_bits: int = 2) -> np.ndarray:
+               slots=None, key_bits: int = 2, val_bits: int = 2, group: int = GROUP) -> np.ndarray:
     """Write token slots of one (page, KV head) block in the layout above.
 
-    ``k_codes``/``v_codes`` are uint8 [n, 128]; scales/zeros float16 [n, 4];
+    ``k_codes``/``v_codes`` are uint8 [n, 128]; scales/zeros float16 [n, 128/G];
     ``slots`` (default 0..n-1, distinct) are the slot indices inside the page.
     Bits of slots not written are left as they were in ``block``.
     """
-    nb = block_bytes(key_bits, val_bits)
+    nb = block_bytes(key_bits, val_bits, group)
     blk = np.zeros(nb, np.uint8) if block is None else block
     assert blk.shape == (nb,) and blk.dtype == np.uint8
     n = np.asarray(k_codes).shape[0]
@@ -264,34 +298,23 @@ def pack_block(k_codes, k_s16, k_z16, v_codes, v_s16, v_z16, block: np.ndarray |
     k_codes = np.asarray(k_codes, np.uint32)
     v_codes = np.asarray(v_codes, np.uint32)
     assert k_codes.max(initial=0) < (1 << key_bits) and v_codes.max(initial=0) < (1 << val_bits)
-    for codes, table in ((k_codes & 3, _K_POS), (v_codes & 3, _V_POS)):
+    for codes, table in ((k_codes, _K_POS), (v_codes, _V_POS)):
         pos = table[slots]                                      # [n, 128, (record, word, bit)]
-        idx = (pos[..., 0] * 4 + pos[..., 1]).reshape(-1)
-        bit = pos[..., 2].reshape(-1).astype(np.uint32)
-        val = np.asarray(codes, np.uint32).reshape(-1)
-        np.bitwise_and.at(words, idx, ~(np.uint32(3) << bit))
-        np.bitwise_or.at(words, idx, (val & np.uint32(3)) << bit)
-    if key_bits > 2:  # high bits of the key codes: record r at 1536 + 8 r, word H[kk // 2], same bit
-        hi = blk[HI_PLANE:HI_PLANE + 512].view("<u4").reshape(-1)  # 64 records x 2 words
-        pos = _K_POS[slots]
-        idx = (pos[..., 0] * 2 + pos[..., 1]).reshape(-1)
-        bit = pos[..., 2].reshape(-1).astype(np.uint32)
-        val = (k_codes >> np.uint32(2)).reshape(-1)
-        np.bitwise_and.at(hi, idx, ~(np.uint32(3) << bit))
-        np.bitwise_or.at(hi, idx, (val & np.uint32(3)) << bit)
-    if val_bits > 2:  # high bits of the value codes: record r at value_plane + 8 r, word VH[i // 2], same bit
-        vp = value_plane(key_bits)
-        hi = blk[vp:vp + 512].view("<u4").reshape(-1)
-        pos = _V_POS[slots]
-        idx = (pos[..., 0] * 2 + pos[..., 1] - 2).reshape(-1)
-        bit = pos[..., 2].reshape(-1).astype(np.uint32)
-        val = (v_codes >> np.uint32(2)).reshape(-1)
-        np.bitwise_and.at(hi, idx, ~(np.uint32(3) << bit))
-        np.bitwise_or.at(hi, idx, (val & np.uint32(3)) << bit)
-    meta = blk[CODE_BYTES:BLOCK_BYTES].view("<u2").reshape(16, 2, 4, 2)   # [record m][K/V][i][scale/zero]
+        _set_bits(words, (pos[..., 0] * 4 + pos[..., 1]).reshape(-1), pos[..., 2].reshape(-1).astype(np.uint32),
+                  codes.reshape(-1), 2)
+    for bits, codes, table, off, value in ((key_bits, k_codes, _K_POS, key_plane(group), False),
+                                           (val_bits, v_codes, _V_POS, value_plane(key_bits, group), True)):
+        if bits == 2:
+            continue
+        plane = blk[off:off + plane_bytes(bits)].view("<u4").reshape(-1)
+        idx, bit = _plane_position(table[slots], bits, value)
+        _set_bits(plane, idx.reshape(-1), bit.reshape(-1).astype(np.uint32), (codes >> np.uint32(2)).reshape(-1),
+                  bits - 2)
+    n_g = HEAD_DIM // group
+    meta = blk[CODE_BYTES:CODE_BYTES + meta_bytes(group)].view("<u2").reshape(4 * n_g, 2, 4, 2)  # [m][K/V][i][s/z]
     for idx, s in enumerate(slots):
         a, i = int(s) // 4, int(s) % 4
-        for grp in range(N_GROUPS):
+        for grp in range(n_g):
             m = 4 * grp + a
             meta[m, 0, i, 0] = np.asarray(k_s16[idx, grp], np.float16).view(np.uint16)
             meta[m, 0, i, 1] = np.asarray(k_z16[idx, grp], np.float16).view(np.uint16)
@@ -300,49 +323,47 @@ def pack_block(k_codes, k_s16, k_z16, v_codes, v_s16, v_z16, block: np.ndarray |
     return blk
 
 
-def unpack_blocks(blocks: np.ndarray, key_bits: int = 2, val_bits: int = 2):
-    """Inverse of ``pack_block`` for a stack of blocks [n, 1536] (all 16 slots each).
+def unpack_blocks(blocks: np.ndarray, key_bits: int = 2, val_bits: int = 2, group: int = GROUP):
+    """Inverse of ``pack_block`` for a stack of blocks [n, block_bytes] (all 16 slots each).
 
     Returns (k_codes, k_s16, k_z16, v_codes, v_s16, v_z16) with codes uint8
-    [n, 16, 128] and scales/zeros float16 [n, 16, 4].
+    [n, 16, 128] and scales/zeros float16 [n, 16, 128/G].
     """
-    blk = np.ascontiguousarray(blocks, np.uint8).reshape(-1, block_bytes(key_bits, val_bits))
-    words = blk[:, :CODE_BYTES].view("<u4").reshape(-1, 64, 4).astype(np.int64)
-    meta = blk[:, CODE_BYTES:BLOCK_BYTES].view("<f2").reshape(-1, 16, 2, 4, 2)   # [n][record m][K/V][i][scale/zero]
+    blk = np.ascontiguousarray(blocks, np.uint8).reshape(-1, block_bytes(key_bits, val_bits, group))
+    words = blk[:, :CODE_BYTES].view("<u4").reshape(-1, 256).astype(np.int64)
+    n_g = HEAD_DIM // group
+    meta = blk[:, CODE_BYTES:CODE_BYTES + meta_bytes(group)].view("<f2").reshape(-1, 4 * n_g, 2, 4, 2)
 
-    def gather(pos):
-        rec, word, bit = pos[..., 0], pos[..., 1], pos[..., 2]      # [16, 128] each
-        return ((words[:, rec, word] >> bit[None]) & 3).astype(np.uint8)
+    def gather(bits, table, off, value):
+        pos = table                                                  # [16, 128, 3]
+        low = (words[:, pos[..., 0] * 4 + pos[..., 1]] >> pos[..., 2][None]) & 3
+        if bits > 2:
+            plane = blk[:, off:off + plane_bytes(bits)].view("<u4").reshape(blk.shape[0], -1).astype(np.int64)
+            idx, bit = _plane_position(pos, bits, value)
+            low = low + (((plane[:, idx] >> bit[None]) & ((1 << (bits - 2)) - 1)) << 2)
+        return low.astype(np.uint8)
 
     slots = np.arange(PAGE)
-    rec = 4 * np.arange(N_GROUPS)[None, :] + (slots // 4)[:, None]     # [slot, grp] -> record m
+    rec = 4 * np.arange(n_g)[None, :] + (slots // 4)[:, None]          # [slot, grp] -> record m
     i = np.broadcast_to((slots % 4)[:, None], rec.shape)
-    k = gather(_K_POS)
-    if key_bits > 2:
-        hi = blk[:, HI_PLANE:HI_PLANE + 512].view("<u4").reshape(-1, 64, 2).astype(np.int64)
-        r_, w_, b_ = _K_POS[..., 0], _K_POS[..., 1], _K_POS[..., 2]
-        k = k + (((hi[:, r_, w_] >> b_[None]) & 3) << 2).astype(np.uint8)
-    v = gather(_V_POS)
-    if val_bits > 2:
-        vp = value_plane(key_bits)
-        hi = blk[:, vp:vp + 512].view("<u4").reshape(-1, 64, 2).astype(np.int64)
-        r_, w_, b_ = _V_POS[..., 0], _V_POS[..., 1] - 2, _V_POS[..., 2]
-        v = v + (((hi[:, r_, w_] >> b_[None]) & 3) << 2).astype(np.uint8)
+    k = gather(key_bits, _K_POS, key_plane(group), False)
+    v = gather(val_bits, _V_POS, value_plane(key_bits, group), True)
     return (k, meta[:, rec, 0, i, 0], meta[:, rec, 0, i, 1],
             v, meta[:, rec, 1, i, 0], meta[:, rec, 1, i, 1])
 
 
-def unpack_block(block: np.ndarray, key_bits: int = 2, val_bits: int = 2):
-    """``unpack_blocks`` for a single block: codes [16, 128], scales/zeros [16, 4]."""
-    return tuple(x[0] for x in unpack_blocks(np.asarray(block, np.uint8)[None], key_bits, val_bits))
+def unpack_block(block: np.ndarray, key_bits: int = 2, val_bits: int = 2, group: int = GROUP):
+    """``unpack_blocks`` for a single block: codes [16, 128], scales/zeros [16, 128/G]."""
+    return tuple(x[0] for x in unpack_blocks(np.asarray(block, np.uint8)[None], key_bits, val_bits, group))
 
 
-def pool_bytes(num_pages: int, num_kv_heads: int, key_bits: int = 2, val_bits: int = 2) -> int:
-    return int(num_pages) * int(num_kv_heads) * block_bytes(key_bits, val_bits)
+def pool_bytes(num_pages: int, num_kv_heads: int, key_bits: int = 2, val_bits: int = 2, group: int = GROUP) -> int:
+    return int(num_pages) * int(num_kv_heads) * block_bytes(key_bits, val_bits, group)
 
 
-def block_view(pool: np.ndarray, page: int, h: int, num_kv_heads: int, key_bits: int = 2, val_bits: int = 2) -> np.ndarray:
-    nb = block_bytes(key_bits, val_bits)
+def block_view(pool: np.ndarray, page: int, h: int, num_kv_heads: int, key_bits: int = 2, val_bits: int = 2,
+               group: int = GROUP) -> np.ndarray:
+    nb = block_bytes(key_bits, val_bits, group)
     off = (int(page) * num_kv_heads + int(h)) * nb
     return pool[off:off + nb]
 
@@ -358,7 +379,6 @@ def quantize_append(pool: np.ndarray, num_kv_heads: int, slots, x: np.ndarray, w
     """
     kc, ks, kz = int2_quantize(x, clip, group, key_bits)
     vc, vs, vz = int2_quantize(w, clip, group, val_bits)
-    ks, kz, vs, vz = (meta_per_32(a) for a in (ks, kz, vs, vz))
     slots = np.asarray(slots, np.int64)
     assert len(np.unique(slots)) == len(slots), "slots must be distinct"
     pages = slots // PAGE
@@ -367,8 +387,8 @@ def quantize_append(pool: np.ndarray, num_kv_heads: int, slots, x: np.ndarray, w
         offs = slots[sel] % PAGE
         for h in range(num_kv_heads):
             pack_block(kc[sel, h], ks[sel, h], kz[sel, h], vc[sel, h], vs[sel, h], vz[sel, h],
-                       block=block_view(pool, page, h, num_kv_heads, key_bits, val_bits), slots=offs, key_bits=key_bits,
-                       val_bits=val_bits)
+                       block=block_view(pool, page, h, num_kv_heads, key_bits, val_bits, group), slots=offs,
+                       key_bits=key_bits, val_bits=val_bits, group=group)
 
 
 def append_tokens(pool, num_kv_heads, slots, k, v, mu, r_k, r_v, clip: float = 1.0, group: int = GROUP,
@@ -386,7 +406,8 @@ def check_orthogonal_all(r: np.ndarray, tol: float = 1e-6) -> None:
 
 
 # ----------------------------------------------------------- reading the cache
-def gather_sequence(pool, num_kv_heads, table_row, seq_len, h, num_pages=None, key_bits: int = 2, val_bits: int = 2):
+def gather_sequence(pool, num_kv_heads, table_row, seq_len, h, num_pages=None, key_bits: int = 2, val_bits: int = 2,
+                    group: int = GROUP):
     """Dequantized rotated keys x_hat and values w_hat [T', 128] of one sequence and KV head (fp64).
 
     A table entry outside [0, num_pages) marks an absent page: its positions
@@ -397,13 +418,14 @@ def gather_sequence(pool, num_kv_heads, table_row, seq_len, h, num_pages=None, k
     if T == 0:
         return np.zeros((0, HEAD_DIM)), np.zeros((0, HEAD_DIM))
     n_pages = (T + PAGE - 1) // PAGE
+    nb = block_bytes(key_bits, val_bits, group)
     if num_pages is None:
-        num_pages = np.asarray(pool).size // (num_kv_heads * block_bytes(key_bits, val_bits))
+        num_pages = np.asarray(pool).size // (num_kv_heads * nb)
     pages = np.asarray(table_row[:n_pages], np.int64)
     present = (pages >= 0) & (pages < num_pages)
-    offs = (np.where(present, pages, 0) * num_kv_heads + int(h)) * block_bytes(key_bits, val_bits)
-    blocks = np.asarray(pool, np.uint8)[offs[:, None] + np.arange(block_bytes(key_bits, val_bits))[None, :]]
-    kc, ks, kz, vc, vs, vz = unpack_blocks(blocks, key_bits, val_bits)
+    offs = (np.where(present, pages, 0) * num_kv_heads + int(h)) * nb
+    blocks = np.asarray(pool, np.uint8)[offs[:, None] + np.arange(nb)[None, :]]
+    kc, ks, kz, vc, vs, vz = unpack_blocks(blocks, key_bits, val_bits, group)
     keep = np.repeat(present, PAGE)[:T]
     x = int2_dequantize(kc, ks, kz).reshape(-1, HEAD_DIM)[:T][keep]
     w = int2_dequantize(vc, vs, vz).reshape(-1, HEAD_DIM)[:T][keep]
@@ -428,7 +450,8 @@ def softmax_attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray, scale
 
 
 def decode_attention(q, pool, num_kv_heads, page_table, seq_lens, r_k, r_v, sm_scale=None,
-                     heads=None, bypass=None, num_pages=None, key_bits: int = 2, val_bits: int = 2) -> np.ndarray:
+                     heads=None, bypass=None, num_pages=None, key_bits: int = 2, val_bits: int = 2,
+                     group: int = GROUP) -> np.ndarray:
     """Decode attention read from the packed cache (OptR §3.2 Eq. (5), §3.1 Eq. (4)).
 
     For query head j of sequence b, with h = j // g:
@@ -456,7 +479,7 @@ def decode_attention(q, pool, num_kv_heads, page_table, seq_lens, r_k, r_v, sm_s
         if (b, h) not in cache:
             if bypass is None:
                 cache[(b, h)] = gather_sequence(pool, num_kv_heads, page_table[b], seq_lens[b], h, num_pages,
-                                                key_bits, val_bits)
+                                                key_bits, val_bits, group)
             else:
                 x, w, tok_seq = bypass
                 sel = np.asarray(tok_seq) == b
@@ -490,7 +513,7 @@ def window_slot(t: int, sinks: int, recent: int) -> int:
 
 
 def effective_kv_window(pool, num_kv_heads, table_row, seq_len, h, mu_h, r_k_h, r_v_h, k_exact, v_exact,
-                        sinks, recent, num_pages=None, key_bits: int = 2, val_bits: int = 2):
+                        sinks, recent, num_pages=None, key_bits: int = 2, val_bits: int = 2, group: int = GROUP):
     """Keys and values attention uses for one sequence and KV head, in the original basis (fp64).
 
     Window positions (``window_mask``) take k_exact[s], v_exact[s] (the BF16
@@ -505,13 +528,14 @@ def effective_kv_window(pool, num_kv_heads, table_row, seq_len, h, mu_h, r_k_h, 
         return np.zeros((0, HEAD_DIM)), np.zeros((0, HEAD_DIM))
     win = window_mask(T, sinks, recent)
     n_pages = (T + PAGE - 1) // PAGE
+    nb = block_bytes(key_bits, val_bits, group)
     if num_pages is None:
-        num_pages = np.asarray(pool).size // (num_kv_heads * block_bytes(key_bits, val_bits))
+        num_pages = np.asarray(pool).size // (num_kv_heads * nb)
     pages = np.asarray(table_row[:n_pages], np.int64)
     present = (pages >= 0) & (pages < num_pages)
-    offs = (np.where(present, pages, 0) * num_kv_heads + int(h)) * block_bytes(key_bits, val_bits)
-    blocks = np.asarray(pool, np.uint8)[offs[:, None] + np.arange(block_bytes(key_bits, val_bits))[None, :]]
-    kc, ks, kz, vc, vs, vz = unpack_blocks(blocks, key_bits, val_bits)
+    offs = (np.where(present, pages, 0) * num_kv_heads + int(h)) * nb
+    blocks = np.asarray(pool, np.uint8)[offs[:, None] + np.arange(nb)[None, :]]
+    kc, ks, kz, vc, vs, vz = unpack_blocks(blocks, key_bits, val_bits, group)
     x_hat = int2_dequantize(kc, ks, kz).reshape(-1, HEAD_DIM)[:T]
     w_hat = int2_dequantize(vc, vs, vz).reshape(-1, HEAD_DIM)[:T]
     k_int2 = x_hat @ np.asarray(r_k_h, np.float64).T + np.asarray(mu_h, np.float64)
@@ -523,7 +547,8 @@ def effective_kv_window(pool, num_kv_heads, table_row, seq_len, h, mu_h, r_k_h, 
 
 
 def decode_attention_window(q, pool, num_kv_heads, page_table, seq_lens, mu, r_k, r_v, k_seqs, v_seqs,
-                            sinks, recent, sm_scale=None, heads=None, num_pages=None, key_bits: int = 2, val_bits: int = 2) -> np.ndarray:
+                            sinks, recent, sm_scale=None, heads=None, num_pages=None, key_bits: int = 2, val_bits: int = 2,
+                            group: int = GROUP) -> np.ndarray:
     """OptR §3.2 Eq. (5) with the BF16 window: Eq. (1)-(2) attention of query
     head j of sequence b over ``effective_kv_window`` of KV head h = j // g.
 
@@ -544,7 +569,7 @@ def decode_attention_window(q, pool, num_kv_heads, page_table, seq_lens, mu, r_k
         if (b, h) not in cache:
             cache[(b, h)] = effective_kv_window(pool, num_kv_heads, page_table[b], seq_lens[b], h, mu[h], r_k[h],
                                                 r_v[h], np.asarray(k_seqs[b])[:, h], np.asarray(v_seqs[b])[:, h],
-                                                sinks, recent, num_pages, key_bits, val_bits)
+                                                sinks, recent, num_pages, key_bits, val_bits, group)
         k_eff, v_eff = cache[(b, h)]
         out[b, j] = softmax_attention(q[b, j], k_eff, v_eff, sm_scale)
     return out
@@ -620,7 +645,8 @@ def present_positions(table_row, seq_len: int, num_pages: int) -> np.ndarray:
 
 
 def output_error(q, pool, num_kv_heads, page_table, seq_lens, k_seqs, v_seqs, mu, r_k, r_v, w_o,
-                 sm_scale=None, num_pages=None, kv_heads=None, key_bits: int = 2, val_bits: int = 2):
+                 sm_scale=None, num_pages=None, kv_heads=None, key_bits: int = 2, val_bits: int = 2,
+                 group: int = GROUP):
     """OptR §3.2 Eq. (6)-(10) at the decode position of every sequence, from the packed cache (fp64).
 
     Query head j of sequence b (KV head h = j // g) attends positions 0..T_b-1.
@@ -641,7 +667,7 @@ def output_error(q, pool, num_kv_heads, page_table, seq_lens, k_seqs, v_seqs, mu
     w_o = np.asarray(w_o, np.float64)
     d_model = w_o.shape[0]
     if num_pages is None:
-        num_pages = np.asarray(pool).size // (num_kv_heads * block_bytes(key_bits, val_bits))
+        num_pages = np.asarray(pool).size // (num_kv_heads * block_bytes(key_bits, val_bits, group))
     dy_k = np.zeros((B, Hq, d_model))
     dy_v = np.zeros((B, Hq, d_model))
     e_out = np.zeros((B, Hq))
@@ -651,7 +677,7 @@ def output_error(q, pool, num_kv_heads, page_table, seq_lens, k_seqs, v_seqs, mu
         keep = present_positions(page_table[b], T, num_pages)
         for h in (range(num_kv_heads) if kv_heads is None else kv_heads):
             x_hat, w_hat = gather_sequence(pool, num_kv_heads, page_table[b], T, h, num_pages, key_bits,
-                                           val_bits)
+                                           val_bits, group)
             k_eff = x_hat @ np.asarray(r_k[h], np.float64).T + np.asarray(mu[h], np.float64)
             v_eff = w_hat @ np.asarray(r_v[h], np.float64).T
             k_ex = np.asarray(k_seqs[b], np.float64)[:T, h][keep]

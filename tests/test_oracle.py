@@ -171,31 +171,81 @@ def test_block_layout_golden(golden_dir):
     assert n_checked == 10
 
 
-def test_pack_unpack_roundtrip_and_partial_writes():
-    rng = np.random.default_rng(14)
-    kc = rng.integers(0, 4, (16, 128)).astype(np.uint8)
-    vc = rng.integers(0, 4, (16, 128)).astype(np.uint8)
-    f = lambda: rng.standard_normal((16, 4)).astype(np.float16)
+LAYOUTS = [(2, 2, 32), (2, 2, 64), (2, 2, 128), (3, 3, 32), (4, 2, 64), (3, 4, 128), (2, 3, 64)]
+
+
+@pytest.mark.parametrize("kb,vb,g", LAYOUTS)
+def test_pack_unpack_roundtrip_and_partial_writes(kb, vb, g):
+    """Every layout round-trips, and slot-by-slot writes in any order onto a dirty
+    block give the bytes of one whole-block write (no slot's bits touch another's)."""
+    rng = np.random.default_rng(14 + kb + 3 * vb + g)
+    kc = rng.integers(0, 1 << kb, (16, 128)).astype(np.uint8)
+    vc = rng.integers(0, 1 << vb, (16, 128)).astype(np.uint8)
+    f = lambda: rng.standard_normal((16, 128 // g)).astype(np.float16)
     ks, kz, vs, vz = f(), f(), f(), f()
-    full = O.pack_block(kc, ks, kz, vc, vs, vz)
-    got = O.unpack_block(full)
+    full = O.pack_block(kc, ks, kz, vc, vs, vz, key_bits=kb, val_bits=vb, group=g)
+    assert full.size == O.block_bytes(kb, vb, g)
+    got = O.unpack_block(full, kb, vb, g)
     for a, b in zip(got, (kc, ks, kz, vc, vs, vz)):
         np.testing.assert_array_equal(a.view(np.uint8) if a.dtype == np.float16 else a,
                                       b.view(np.uint8) if b.dtype == np.float16 else b)
     # slot-by-slot writes in a scrambled order onto a dirty block give the same bytes
-    blk = rng.integers(0, 256, O.BLOCK_BYTES).astype(np.uint8)
+    blk = rng.integers(0, 256, O.block_bytes(kb, vb, g)).astype(np.uint8)
     for s in rng.permutation(16):
         O.pack_block(kc[s:s + 1], ks[s:s + 1], kz[s:s + 1], vc[s:s + 1], vs[s:s + 1], vz[s:s + 1],
-                     block=blk, slots=[s])
+                     block=blk, slots=[s], key_bits=kb, val_bits=vb, group=g)
     np.testing.assert_array_equal(blk, full)
 
 
 def test_storage_arithmetic():
-    """OptR §1: INT2 codes take 1/8 of BF16 storage; with fp16 scale+zero per 32 the
-    block is 96 bytes per token per KV head (3 bits per element)."""
+    """OptR §1: INT2 codes take 1/8 of BF16 storage; with fp16 scale+zero per group
+    the block is 96, 80 or 72 bytes per token per KV head for G = 32, 64, 128 (3,
+    2.5 and 2.25 bits per element); 3-bit codes add one bit per element, 4-bit two."""
     assert O.CODE_BYTES // 16 // 2 == 128 * 2 // 8            # K (or V) codes per token = bf16 bytes / 8
-    assert O.BLOCK_BYTES // 16 == 96
-    assert O.BLOCK_BYTES * 8 / (16 * 2 * 128) == 3.0
+    for g, per_token in ((32, 96), (64, 80), (128, 72)):
+        assert O.block_bytes(group=g) // 16 == per_token
+        assert O.block_bytes(group=g) * 8 / (16 * 2 * 128) == 2 + 32 / g
+    assert O.block_bytes(3, 3) // 16 == 128                   # K3V3: 4 bits per element
+    assert O.block_bytes(3, 2) * 8 / (16 * 2 * 128) == 3.5
+    assert O.block_bytes(4, 4) // 16 == 160
+
+
+def test_compact_layout_golden(golden_dir):
+    """Hand-derived block sizes, metadata positions for G = 64 and 128, and 3-bit
+    key planes (tests/golden/block_layout_compact.txt)."""
+    with open(os.path.join(golden_dir, "block_layout_compact.txt")) as f:
+        lines = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    n_seen = {"BLOCK": 0, "META": 0, "KEY3": 0}
+    for parts in lines:
+        kind, nums = parts[0], list(map(int, parts[1:]))
+        n_seen[kind] += 1
+        if kind == "BLOCK":
+            kb, vb, g, size = nums
+            assert O.block_bytes(kb, vb, g) == size
+            continue
+        if kind == "META":
+            g, slot, grp, tensor, sbits, zbits, *pairs = nums
+            kb = 2
+            z = np.zeros((1, 128), np.uint8)
+            m0 = np.zeros((1, 128 // g), np.float16)
+            pair = [m0.copy() for _ in range(4)]
+            pair[2 * tensor][0, grp] = np.uint16(sbits).view(np.float16)
+            pair[2 * tensor + 1][0, grp] = np.uint16(zbits).view(np.float16)
+            blk = O.pack_block(z, pair[0], pair[1], z, pair[2], pair[3], slots=[slot], group=g)
+        else:
+            kb, g, slot, ch, code, *pairs = nums
+            kc = np.zeros((1, 128), np.uint8)
+            kc[0, ch] = code
+            z = np.zeros((1, 128), np.uint8)
+            m0 = np.zeros((1, 128 // g), np.float16)
+            blk = O.pack_block(kc, m0, m0, z, m0, m0, slots=[slot], key_bits=kb, group=g)
+        want = dict(zip(pairs[0::2], pairs[1::2]))
+        nz = np.nonzero(blk)[0]
+        assert set(nz) == set(want) and all(blk[b] == v for b, v in want.items()), parts
+        back = O.unpack_block(blk, kb, 2, g)
+        if kind == "KEY3":
+            assert back[0][slot, ch] == code and np.count_nonzero(back[0]) == 1
+    assert n_seen == {"BLOCK": 6, "META": 3, "KEY3": 3}
 
 
 # ---------------------------------------------------- attention pins
@@ -673,8 +723,8 @@ def test_quantizer_group_sizes_hand_derived():
 
 def test_quantizer_group_sizes_nearest_level_and_shared_metadata():
     """For G = 64 and 128: four levels per group, each code the nearest level (brute
-    force), G = 32 the default; a packed block repeats each group's pair over its
-    32-channel metadata entries, and unpacking gives back the same levels."""
+    force), G = 32 the default; a packed block keeps one pair per group, and
+    unpacking gives back the same levels."""
     rng = np.random.default_rng(41)
     x = np.concatenate([_random_rows(rng, 40), _random_rows(rng, 24, 5.0, -1.0)])
     np.testing.assert_array_equal(O.int2_quantize(x)[0], O.int2_quantize(x, group=32)[0])
@@ -687,13 +737,12 @@ def test_quantizer_group_sizes_nearest_level_and_shared_metadata():
         got = np.take_along_axis(dist, codes.reshape(64, 128 // g, g)[..., None].astype(np.int64), -1)[..., 0]
         tol = 4 * np.spacing(np.maximum(s16.astype(np.float32), np.float32(1e-30))).astype(np.float64)[..., None]
         assert np.all(got <= dist.min(-1) + tol + 1e-12), g
-        # pack 16 rows into one block and read it back
-        blk = O.pack_block(codes[:16], O.meta_per_32(s16[:16]), O.meta_per_32(z16[:16]),
-                           codes[16:32], O.meta_per_32(s16[16:32]), O.meta_per_32(z16[16:32]))
-        kc, ks, kz, vc, vs, vz = O.unpack_block(blk)
-        for grp in range(4):
-            np.testing.assert_array_equal(ks[:, grp], s16[:16, grp * 32 // g])
-            np.testing.assert_array_equal(vz[:, grp], z16[16:32, grp * 32 // g])
+        # pack 16 rows into one block (one metadata pair per group) and read it back
+        blk = O.pack_block(codes[:16], s16[:16], z16[:16], codes[16:32], s16[16:32], z16[16:32], group=g)
+        assert blk.size == 1024 + 128 * (128 // g)
+        kc, ks, kz, vc, vs, vz = O.unpack_block(blk, group=g)
+        np.testing.assert_array_equal(ks, s16[:16])
+        np.testing.assert_array_equal(vz, z16[16:32])
         np.testing.assert_array_equal(O.int2_dequantize(kc, ks, kz), O.int2_dequantize(codes[:16], s16[:16], z16[:16]))
         np.testing.assert_array_equal(O.int2_dequantize(vc, vs, vz),
                                       O.int2_dequantize(codes[16:32], s16[16:32], z16[16:32]))
@@ -705,9 +754,9 @@ def test_decode_with_group_size_equals_attention_on_effective_kv():
     c = _tiny(B=2, Hq=8, Hkv=2, seq_lens=[50, 33], table_policy="permuted")
     x, w = O.rotated_inputs(c.k, c.v, c.mu, c.r_k, c.r_v)
     for g in (64, 128):
-        pool = np.zeros(O.pool_bytes(c.num_pages, c.Hkv), np.uint8)
+        pool = np.zeros(O.pool_bytes(c.num_pages, c.Hkv, group=g), np.uint8)
         O.append_tokens(pool, c.Hkv, c.slots, c.k, c.v, c.mu, c.r_k, c.r_v, group=g)
-        got = O.decode_attention(c.q, pool, c.Hkv, c.page_table, c.seq_lens, c.r_k, c.r_v)
+        got = O.decode_attention(c.q, pool, c.Hkv, c.page_table, c.seq_lens, c.r_k, c.r_v, group=g)
         kq = O.int2_dequantize(*O.int2_quantize(x, group=g))
         vq = O.int2_dequantize(*O.int2_quantize(w, group=g))
         for b in range(c.B):
@@ -951,7 +1000,7 @@ def test_quantizer_three_bits_hand_derived_and_nearest():
 def test_wide_value_block_layout_golden(golden_dir):
     """Hand-derived byte positions of wide value codes (low bits in place, high
     bits in the value plane after the keys' plane); keys and metadata are
-    unaffected and the block grows by 512 bytes."""
+    unaffected and the block grows by the planes (256 bytes for 3 bits, 512 for 4)."""
     with open(os.path.join(golden_dir, "block_layout_wide_v.txt")) as f:
         lines = [l.split() for l in f if l.strip() and not l.startswith("#")]
     z = np.zeros((1, 128), np.uint8)
@@ -961,7 +1010,7 @@ def test_wide_value_block_layout_golden(golden_dir):
         vc = z.copy()
         vc[0, ch] = code
         blk = O.pack_block(z, zf, zf, vc, zf, zf, slots=[slot], key_bits=kb, val_bits=vb)
-        assert blk.size == 1536 + 512 * (kb > 2) + 512 * (vb > 2)
+        assert blk.size == 1536 + {2: 0, 3: 256, 4: 512}[kb] + {2: 0, 3: 256, 4: 512}[vb]
         want = dict(zip(pairs[0::2], pairs[1::2]))
         nz = np.nonzero(blk)[0]
         assert set(nz) == set(want) and all(blk[b] == v for b, v in want.items()), parts
