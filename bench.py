@@ -166,7 +166,8 @@ def cpu_workers() -> int:
     return max(1, min(n, 16))
 
 
-def cpu_baseline(case, pool_np, kv_heads_sample: int, window=None, key_bits: int = 2, val_bits: int = 2):
+def cpu_baseline(case, pool_np, kv_heads_sample: int, window=None, key_bits: int = 2, val_bits: int = 2,
+                 group: int = 32):
     """Time the oracle (as it stands) on the step: the append of the newest token,
     then the decode of the query heads (with the exact window (sinks, recent) when
     given), one KV head per task.  Two runs: KV heads [0, kv_heads_sample) on one
@@ -188,7 +189,7 @@ def cpu_baseline(case, pool_np, kv_heads_sample: int, window=None, key_bits: int
     def append():
         pool = pool_np.copy()
         x, w = O.rotated_inputs(case.k[last], case.v[last], case.mu, r_k, r_v)
-        O.quantize_append(pool, case.Hkv, case.slots[last], x, w, key_bits=key_bits, val_bits=val_bits)
+        O.quantize_append(pool, case.Hkv, case.slots[last], x, w, key_bits=key_bits, val_bits=val_bits, group=group)
         return pool
 
     def decode(pool, h):
@@ -196,10 +197,10 @@ def cpu_baseline(case, pool_np, kv_heads_sample: int, window=None, key_bits: int
         if window:
             O.decode_attention_window(case.q, pool, case.Hkv, case.page_table, case.seq_lens, case.mu, r_k, r_v,
                                       k_seqs, v_seqs, window[0], window[1], heads=heads, key_bits=key_bits,
-                                      val_bits=val_bits)
+                                      val_bits=val_bits, group=group)
         else:
             O.decode_attention(case.q, pool, case.Hkv, case.page_table, case.seq_lens, r_k, r_v, heads=heads,
-                               key_bits=key_bits, val_bits=val_bits)
+                               key_bits=key_bits, val_bits=val_bits, group=group)
 
     hs = list(range(min(kv_heads_sample, case.Hkv)))
     tokens = float(case.seq_lens.sum())
@@ -243,7 +244,8 @@ def bench_evaluator(args, torch, I, kvq, dev, desc, case) -> int:
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
     rot_kind = kvq.KVQ_ROT_HADAMARD if args.rotation == "hadamard" else kvq.KVQ_ROT_DENSE
-    pool = torch.zeros(case.num_pages * case.Hkv * 1536, dtype=torch.uint8, device=dev)
+    nbytes = kvq.kvq_pool_bytes(kvq.make_cache(case.Hkv, case.num_pages))
+    pool = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
     cache = kvq.make_cache(case.Hkv, case.num_pages, pool, rotation=rot_kind)
     k, v = B16(case.k_bits), B16(case.v_bits)
     r_k, r_v, mu = T(case.r_k), T(case.r_v), T(case.mu)
@@ -334,9 +336,11 @@ def main() -> int:
                     help="KV heads in the oracle's one-core sample (0 = skip the CPU baseline)")
     ap.add_argument("--window", default="", help="exact bf16 window 'sinks,recent' (e.g. 4,128); default none")
     ap.add_argument("--key-bits", type=int, default=2, choices=[2, 3, 4],
-                    help="bits per key code: 2, or 3 / 4 (K3V2 / K4V2: a 512-byte high-bit plane per block)")
+                    help="bits per key code: 2, or 3 / 4 (K3V2 / K4V2: a 256- or 512-byte high-bit plane per block)")
     ap.add_argument("--val-bits", type=int, default=2, choices=[2, 3, 4],
-                    help="bits per value code: 2, or 3 / 4 (with 3-bit keys, K3V3: another 512-byte plane)")
+                    help="bits per value code: 2, or 3 / 4 (with 3-bit keys, K3V3: another plane)")
+    ap.add_argument("--group", type=int, default=32, choices=[32, 64, 128],
+                    help="Q2's group size G (one metadata pair per G channels: 96, 80 or 72 bytes per token)")
     ap.add_argument("--evaluator", action="store_true",
                     help="time the output-error evaluator (kvq_output_error) instead of the decode step")
     ap.add_argument("--rotation", default="dense", choices=["dense", "hadamard"],
@@ -376,9 +380,11 @@ def main() -> int:
     def B16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
 
-    # per token and KV head: K and V codes, K and V (scale, zero); each 3- or 4-bit tensor adds
-    # the 32 B of its high-bit plane
-    bpt = BYTES_PER_TOKEN_HEAD + (32 if args.key_bits > 2 else 0) + (32 if args.val_bits > 2 else 0)
+    # per token and KV head: K and V codes, K and V (scale, zero) per group; each 3- or 4-bit tensor
+    # adds its high-bit plane (16 or 32 B): the library's block size over the page's 16 tokens
+    bpt = kvq.kvq_pool_bytes(kvq.make_cache(1, 1, group_size=args.group, key_bits=args.key_bits,
+                                            val_bits=args.val_bits)) // PAGE
+    assert bpt > 0
     cache_bytes = int(case.seq_lens.sum()) * case.Hkv * bpt
     pool_bytes = case.num_pages * case.Hkv * PAGE * bpt
     n_rep = args.replicas or max(2, -(-2 * MALL_BYTES // pool_bytes) + 1)
@@ -391,7 +397,7 @@ def main() -> int:
     for r in range(n_rep):
         pools.append(torch.zeros(pool_bytes, dtype=torch.uint8, device=dev))
         caches.append(kvq.make_cache(case.Hkv, case.num_pages, pools[-1], rotation=rot_kind, key_bits=args.key_bits,
-                                     val_bits=args.val_bits))
+                                     val_bits=args.val_bits, group_size=args.group))
         rks.append(T(case.r_k))
         rvs.append(T(case.r_v))
         mus.append(T(case.mu))
@@ -536,7 +542,8 @@ def main() -> int:
     achieved = alg_bytes / (split_avg_ms * 1e-3) / 1e9
     # the committed counter summaries are per workload, without a window and with a dense R
     variant = (("" if args.rotation == "dense" else "_" + args.rotation) + (f"_window{sinks}_{recent}" if n_win_tok else "")
-               + (f"_k{args.key_bits}" if args.key_bits > 2 else "") + (f"_v{args.val_bits}" if args.val_bits > 2 else ""))
+               + (f"_k{args.key_bits}" if args.key_bits > 2 else "") + (f"_v{args.val_bits}" if args.val_bits > 2 else "")
+               + (f"_g{args.group}" if args.group != 32 else ""))
     traffic = counters_for(kernel_source_sha(), args.workload + variant)
 
     cpu = None
@@ -544,7 +551,7 @@ def main() -> int:
         log("[bench] timing the oracle on the CPU ...")
         cpu = cpu_baseline(case, pools[0].cpu().numpy(), args.cpu_kv_heads,
                            window=(sinks, recent) if (sinks or recent) else None, key_bits=args.key_bits,
-                           val_bits=args.val_bits)
+                           val_bits=args.val_bits, group=args.group)
 
     res = {
         "metric": "INT2 decode attention KV-tokens/s + HBM GB/s (% peak), 8B GQA shape @128K",
@@ -563,7 +570,7 @@ def main() -> int:
         "config": {
             "workload": desc,
             "batch": case.B, "num_q_heads": case.Hq, "num_kv_heads": case.Hkv, "head_dim": 128,
-            "context_tokens": int(tokens), "group_size": 32, "page_size": PAGE,
+            "context_tokens": int(tokens), "group_size": args.group, "page_size": PAGE,
             "page_table": "seeded permutation" if case.B == 1 else "seeded interleaved allocator",
             "cache_replicas": n_rep, "num_splits": args.num_splits or "auto",
             "exact_window": {"sinks": sinks, "recent": recent} if (sinks or recent) else None,

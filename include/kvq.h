@@ -22,26 +22,36 @@
  * gets all-zero codes.  The page names Q2(.; c, G) without defining c; both
  * range ends scaled by c is this library's reading.
  *
- * Geometry supported: head_dim 128, group 32, page 16 tokens, query heads per
- * KV head g = num_q_heads / num_kv_heads with 1 <= g <= 16.
+ * Geometry supported: head_dim 128, group G = 32, 64 or 128, page 16 tokens,
+ * query heads per KV head g = num_q_heads / num_kv_heads with 1 <= g <= 16.
  *
  * Cache layout.  One device buffer ("pool") of num_pages * num_kv_heads blocks
- * of 1536 bytes; block (page p, KV head h) starts at (p*num_kv_heads + h)*1536
- * and holds the 16 token slots of that page.  Inside a block:
+ * of B bytes (B below); block (page p, KV head h) starts at
+ * (p*num_kv_heads + h)*B and holds the 16 token slots of that page.  Inside a
+ * block:
  *   [0, 1024)    64 records of 16 bytes, record r = 16a + b (a < 4, b < 16)
  *                = little-endian uint32 words K0, K1, V0, V1.
  *                K code of slot s, channel c (kk = c/32, a = (c%32)/8, e = c%8):
  *                  record 16a + s, word K[kk/2], bits 2*(4*(kk%2) + e/2) + 16*(e%2) (+1).
  *                V code of slot s, channel c (t = c/16, b = c%16, a = s/4, i = s%4):
  *                  record 16a + b, word V[i/2], bits 2*t + 16*(i%2) (+1).
- *   [1024, 1536) 16 records of 32 bytes, record m = 4*grp + a: for slots
- *                s = 4a + i, at +4i the K (fp16 scale, fp16 zero) pair of
- *                channel group grp, at +16+4i the V pair.
- * A slot index is page*16 + offset.  96 bytes per token per KV head.
+ *   [1024, 1024 + M), M = 128*(128/G) (512, 256, 128 bytes for G = 32, 64,
+ *                128): 4*128/G records of 32 bytes, record m = 4*grp + a:
+ *                for slots s = 4a + i, at +4i the K (fp16 scale, fp16 zero)
+ *                pair of channel group grp (channels G*grp .. G*grp + G-1),
+ *                at +16+4i the V pair.
+ * A slot index is page*16 + offset.  96, 80 or 72 bytes per token per KV head.
  * Caches with 3- or 4-bit keys or values (kvq_cache.key_bits, val_bits)
- * append a 512-byte high-bit plane per widened tensor to every block, so the
- * block is 1536, 2048 or 2560 bytes and block (p, h) starts at
- * (p*num_kv_heads + h) * block bytes.
+ * append a high-bit plane per widened tensor, the keys' first (at
+ * P_K = 1024 + M), then the values' (at P_V = P_K + the keys' plane size):
+ *   4 bits: 512 bytes, record r at P + 8r = words H0, H1 (keys) or VH0, VH1
+ *           (values); a code's high two bits sit at the record, word index
+ *           and bit of its low two bits.
+ *   3 bits: 256 bytes, one word W per record at P + 4r.  Keys: the code at
+ *           bit j of word K[w] has its high bit at bit j + w of W; values:
+ *           the code of slot 4a + i, channel 16t + b has it at bit 8i + t.
+ * So B = 1024 + M + the planes: K2V2 1536 / 1280 / 1152 (G = 32 / 64 / 128),
+ * K3V2 1792, K3V3 2048, K4V2 2048, K4V4 2560 (G = 32).
  *
  * Conventions for every call.
  *   - Pointers marked "device" are HIP device (or managed) memory; "host" are
@@ -98,28 +108,20 @@ typedef struct {
   int32_t num_kv_heads; /* H_kv >= 1                                          */
   int32_t head_dim;     /* must be 128                                        */
   int32_t group_size;   /* Q2's group size G: 32, 64 or 128 consecutive rotated
-                           channels.  The block layout is the same for every G:
-                           it keeps one (scale, zero) pair per 32 channels, each
-                           holding the pair of the group containing them       */
+                           channels, one (scale, zero) pair per group and
+                           tensor (the metadata shrinks with G)               */
   int32_t page_size;    /* must be 16                                         */
   int32_t num_pages;    /* pages in the pool                                  */
   void* pool;           /* device, kvq_pool_bytes(cache) bytes, 16-byte aligned */
   float clip_ratio;     /* Q2's clip ratio c in (0, 1]; 0 selects 1 (no clip)  */
   int32_t rotation;     /* kvq_rotation: how r_k and r_v describe R           */
   int32_t key_bits;     /* bits per key code: 2 (or 0, the default), 3 (K3V2)
-                           or 4 (K4V2).  With 3 or 4 the 1536-byte layout holds
-                           each key code's low two bits and a 512-byte plane
-                           at byte 1536 the rest (record r = 16 a + s at
-                           1536 + 8 r, words H0, H1 at the bits of K0, K1; one
-                           bit used for 3-bit keys)                           */
+                           or 4 (K4V2): the code words hold the low two bits,
+                           the keys' plane (256 bytes for 3, 512 for 4) the
+                           rest, as the layout above states                  */
   int32_t val_bits;     /* bits per value code: 2 (or 0, the default), 3 (K3V3
-                           with 3-bit keys) or 4.  With 3 or 4 another 512-byte
-                           plane follows (at byte 1536, or 2048 after a key
-                           plane): record r = 16 a + b at P + 8 r, words VH0,
-                           VH1 at the bits of V0, V1 hold each value code's
-                           high bits.  A block is 1536 bytes plus 512 per
-                           plane: 1536 (K2V2), 2048 (K3V2, K4V2, K2V4) or
-                           2560 (K3V3, K4V4)                                 */
+                           with 3-bit keys) or 4: the low two bits in the code
+                           words, the rest in the values' plane              */
 } kvq_cache;
 
 /*
@@ -153,9 +155,10 @@ typedef struct {
   const float* mu;
 } kvq_window;
 
-/* Bytes of the pool: num_pages * num_kv_heads * block bytes (1536, plus 512
- * for 3- or 4-bit keys and 512 for 3- or 4-bit values).  0 if `cache` is NULL
- * or has non-positive sizes. */
+/* Bytes of the pool: num_pages * num_kv_heads * B, B the block size of the
+ * cache's group size and code widths (1024 + 128*(128/G), plus 256 per 3-bit
+ * and 512 per 4-bit plane).  0 if `cache` is NULL, has non-positive sizes or
+ * an unsupported group size or width. */
 size_t kvq_pool_bytes(const kvq_cache* cache);
 
 /*

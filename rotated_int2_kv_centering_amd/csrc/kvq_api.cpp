@@ -14,6 +14,7 @@
 
 #include "kvq.h"
 #include "kvq_internal.h"
+#include "kvq_layout.h"
 
 namespace {
 
@@ -36,8 +37,6 @@ kvq_status hip_fail(hipError_t e, const char* what) {
 constexpr int kHeadDim = 128;
 constexpr int kGroupMetadata = 32;  // the block keeps one (scale, zero) pair per 32 channels
 constexpr int kPage = 16;
-constexpr size_t kBlockBytes = 1536;
-constexpr size_t kPlaneBytes = 512;  // high-bit plane of 3- or 4-bit key or value codes
 constexpr int kRowStride = 132;  // floats per split partial (acc[128], max, sum, pad)
 constexpr int kMaxGroup = 16;
 constexpr int kMinPagesPerSplit = 8;
@@ -74,9 +73,10 @@ float clip_of(const kvq_cache* c) { return c->clip_ratio == 0.0f ? 1.0f : c->cli
 // Bits per key and per value code (0 selects 2).
 int kbits_of(const kvq_cache* c) { return c->key_bits > 2 ? c->key_bits : 2; }
 int vbits_of(const kvq_cache* c) { return c->val_bits > 2 ? c->val_bits : 2; }
-// Bytes of one (page, KV head) block: one high-bit plane per tensor wider than 2 bits.
+// Bytes of one (page, KV head) block: codes, one metadata pair per group of G
+// channels, one high-bit plane per tensor wider than 2 bits (kvq_layout.h).
 size_t block_bytes_of(const kvq_cache* c) {
-  return kBlockBytes + (kbits_of(c) > 2 ? kPlaneBytes : 0) + (vbits_of(c) > 2 ? kPlaneBytes : 0);
+  return static_cast<size_t>(kvq::block_bytes(kbits_of(c), vbits_of(c), c->group_size));
 }
 
 // Compute units of the current device, cached per device id (256 when no
@@ -372,6 +372,10 @@ extern "C" {
 
 size_t kvq_pool_bytes(const kvq_cache* cache) {
   if (cache == nullptr || cache->num_kv_heads <= 0 || cache->num_pages <= 0) return 0;
+  const int g = cache->group_size, kb = cache->key_bits, vb = cache->val_bits;
+  if (g != 32 && g != 64 && g != 128) return 0;
+  if (kb != 0 && (kb < 2 || kb > 4)) return 0;
+  if (vb != 0 && (vb < 2 || vb > 4)) return 0;
   return static_cast<size_t>(cache->num_pages) * static_cast<size_t>(cache->num_kv_heads) * block_bytes_of(cache);
 }
 
@@ -550,6 +554,7 @@ kvq_status kvq_output_error(const kvq_cache* cache, const void* q, kvq_dtype q_d
   a.r_k = r_k;
   a.r_v = r_v;
   a.rot_kind = cache->rotation;
+  a.gsize = cache->group_size;
   a.kbits = kbits_of(cache);
   a.vbits = vbits_of(cache);
   a.sm_scale = sm_scale == 0.0f ? 1.0f / std::sqrt(static_cast<float>(kHeadDim)) : sm_scale;

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     if (rot_out != nullptr) rot_out[((static_cast<size_t>(n) * num_kv_heads + h) * 2 + tensor) * kHeadDim + j] = xv;
 
     const int page = slot >> 4;
-    uint8_t* block = pool + (static_cast<size_t>(page) * num_kv_heads + h) * block_bytes(kbits, vbits);
+    uint8_t* block = pool + (static_cast<size_t>(page) * num_kv_heads + h) * block_bytes(kbits, vbits, gsize);
     float2 r;
     if (gsize == 128) {
       const float2 a = s_rng[t][0], b = s_rng[t][1];
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
     } else {
       r = q2_wave_range(xv, gsize);
     }
-    const float lvl = q2_pack_channel(xv, j, tensor, block, slot & 15, clip, r.x, r.y, kbits, vbits);
+    const float lvl = q2_pack_channel(xv, j, tensor, block, slot & 15, clip, r.x, r.y, kbits, vbits, gsize);
     if (sq_err != nullptr) {  // squared error over this wave's 64 channels
       float e = (xv - lvl) * (xv - lvl);
 #pragma unroll
@@ -352,13 +352,14 @@ __device__ __forceinline__ void v_store(uint8_t* block, bool ok, int slot, int p
 // wave's LDS image `img` of two blocks, token n of the tile at slot n % 16 of
 // image block n / 16, for the caller to copy out; otherwise they are stored
 // slot by slot into the pool.
-template <int kT, bool kWide, bool kImg>
+template <int kT, int kBits, bool kImg>
 __device__ __forceinline__ void bulk_store(const float (&c)[64], float u, uint8_t* __restrict__ pool, int num_pages,
                                            int num_kv_heads, int hd, int n, int slot, float* __restrict__ rot_out,
                                            float clip, int gsize, float* __restrict__ sq_err, int kbits, int vbits,
                                            int lane, uint8_t* img) {
+  constexpr bool kWide = kBits > 2;
   const int h = lane >> 5;
-  const float n_lv = static_cast<float>((1 << (kT == 0 ? kbits : vbits)) - 1);
+  const float n_lv = static_cast<float>((1 << kBits) - 1);
   const BulkGroups G = bulk_params(c, u, clip, gsize, n_lv);
   // words: K code words a = 0..3 (kWide: + their high bits), or V byte words j = 0..3
   uint32_t w[4], wh[4];
@@ -371,12 +372,16 @@ __device__ __forceinline__ void bulk_store(const float (&c)[64], float u, uint8_
     }
     e_sum = 0.0f;
   };
+  constexpr int bits = kBits;
   auto pack = [&](int v, uint32_t y) {
     const int q = kT == 0 ? kword_of(v) : vword_of(v);
     const int b = kT == 0 ? kbit_of(v) : vbit_of(v);
     if (kWide) {
       w[q] |= (y & 3u) << b;
-      wh[q] |= ((y >> 2) & 3u) << b;
+      if (bits == 4)  // the high bits at the low bits' position
+        wh[q] |= ((y >> 2) & 3u) << b;
+      else  // 3 bits: keys at the position plus the word index h; values: bit 8 (b % 4) + tile of byte b % 4
+        wh[q] |= ((y >> 2) & 1u) << (kT == 0 ? b + h : 8 * (v & 3) + 4 * h + (v >> 4));
     } else {
       w[q] += y << b;
     }
@@ -398,10 +403,19 @@ __device__ __forceinline__ void bulk_store(const float (&c)[64], float u, uint8_
 
   const bool tok_odd = (lane & 1) != 0;
   const bool ok = slot >= 0 && slot < num_pages * kPage;
+  const int shift = meta_shift(gsize);
   uint32_t E[4], EH[4];
   if (kT == 1) {
     v_halfwords(w, E);
-    if (kWide) v_halfwords(wh, EH);
+    if (kWide && bits == 4) v_halfwords(wh, EH);
+  }
+  if (kWide && bits == 3) {  // 3-bit planes: both lane halves' bits of each word
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float p0, p1;
+      swap32(__uint_as_float(wh[q]), p0, p1);
+      wh[q] = __float_as_uint(p0) | __float_as_uint(p1);
+    }
   }
   if (kImg) {
     uint8_t* ib = img + kBlockBytes * ((lane & 31) >> 4);
@@ -417,31 +431,43 @@ __device__ __forceinline__ void bulk_store(const float (&c)[64], float u, uint8_
         *reinterpret_cast<uint32_t*>(ib + 8 + 16 * (16 * (io >> 2) + b0 + q) + 4 * ((io & 3) >> 1)) = W[q];
     }
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
-      *reinterpret_cast<uint32_t*>(ib + kCodeBytes + kMetaRecordBytes * (4 * (2 * h + g) + (io >> 2)) + 16 * kT +
-                                   4 * (io & 3)) = G.pair[g];
+    for (int g = 0; g < 2; ++g)  // 32-channel group 2 h + g: a pair where a group of G channels starts
+      if (((2 * h + g) & ((1 << shift) - 1)) == 0)
+        *reinterpret_cast<uint32_t*>(ib + kCodeBytes + kMetaRecordBytes * (4 * ((2 * h + g) >> shift) + (io >> 2)) +
+                                     16 * kT + 4 * (io & 3)) = G.pair[g];
     if (!ok) return;
   } else {
     const int pslot = static_cast<int>(dpp_xor1_u32(static_cast<uint32_t>(slot)));
     uint8_t* block =
-        pool + (static_cast<size_t>(ok ? slot >> 4 : 0) * num_kv_heads + hd) * block_bytes(kbits, vbits);
+        pool + (static_cast<size_t>(ok ? slot >> 4 : 0) * num_kv_heads + hd) * block_bytes(kbits, vbits, gsize);
     const int off = slot & 15;
     if (kT == 1) {
       v_store(block, ok, slot, pslot, tok_odd, h, E, 8, 16);
-      if (kWide) v_store(block, ok, slot, pslot, tok_odd, h, EH, v_hi_plane(kbits), 8);
+      if (kWide && bits == 4) v_store(block, ok, slot, pslot, tok_odd, h, EH, v_hi_plane(kbits, gsize), 8);
     }
     if (!ok) return;
     if (kT == 0) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         *reinterpret_cast<uint32_t*>(block + 16 * (16 * a + off) + 4 * h) = w[a];
-        if (kWide) *reinterpret_cast<uint32_t*>(block + kKHiPlane + 8 * (16 * a + off) + 4 * h) = wh[a];
+        if (kWide && bits == 4) *reinterpret_cast<uint32_t*>(block + k_hi_plane(gsize) + 8 * (16 * a + off) + 4 * h) = wh[a];
       }
+      if (kWide && bits == 3) {  // the record's plane word (both K words' bits), records 2h, 2h + 1 by this lane
+#pragma unroll
+        for (int a = 2 * h; a < 2 * h + 2; ++a)
+          *reinterpret_cast<uint32_t*>(block + k_hi_plane(gsize) + 4 * (16 * a + off)) = wh[a];
+      }
+    } else if (kWide && bits == 3) {  // byte off % 4 of plane record 16 (off / 4) + b, b = 8h .. 8h + 7 by this lane
+#pragma unroll
+      for (int b = 8 * h; b < 8 * h + 8; ++b)
+        block[v_hi_plane(kbits, gsize) + 4 * (16 * (off >> 2) + b) + (off & 3)] =
+            static_cast<uint8_t>(wh[b >> 2] >> (8 * (b & 3)));
     }
 #pragma unroll
-    for (int g = 0; g < 2; ++g)  // metadata of group 2 h + g: record 4 (2 h + g) + off / 4
-      *reinterpret_cast<uint32_t*>(block + kCodeBytes + kMetaRecordBytes * (4 * (2 * h + g) + (off >> 2)) + 16 * kT +
-                                   4 * (off & 3)) = G.pair[g];
+    for (int g = 0; g < 2; ++g)  // 32-channel group 2 h + g: a pair where a group of G channels starts
+      if (((2 * h + g) & ((1 << shift) - 1)) == 0)
+        *reinterpret_cast<uint32_t*>(block + kCodeBytes + kMetaRecordBytes * (4 * ((2 * h + g) >> shift) + (off >> 2)) +
+                                     16 * kT + 4 * (off & 3)) = G.pair[g];
   }
   const size_t row = (static_cast<size_t>(n) * num_kv_heads + hd) * 2 + kT;
   if (sq_err != nullptr) sq_err[row * 2 + h] = e_sum;  // channels [64 h, 64 h + 64)
@@ -584,12 +610,16 @@ __device__ __forceinline__ void bulk_tensor(const BulkRaw<kIn>& raw, const half8
     }
   }
   next();
-  if (!kImg && (kT == 0 ? kbits : vbits) > 2)
-    bulk_store<kT, true, false>(c, u, pool, num_pages, num_kv_heads, hd, n, slot, rot_out, clip, gsize, sq_err, kbits,
-                                vbits, lane, img);
+  const int bits = kT == 0 ? kbits : vbits;
+  if (!kImg && bits == 4)
+    bulk_store<kT, 4, false>(c, u, pool, num_pages, num_kv_heads, hd, n, slot, rot_out, clip, gsize, sq_err, kbits,
+                             vbits, lane, img);
+  else if (!kImg && bits == 3)
+    bulk_store<kT, 3, false>(c, u, pool, num_pages, num_kv_heads, hd, n, slot, rot_out, clip, gsize, sq_err, kbits,
+                             vbits, lane, img);
   else
-    bulk_store<kT, false, kImg>(c, u, pool, num_pages, num_kv_heads, hd, n, slot, rot_out, clip, gsize, sq_err, kbits,
-                                vbits, lane, img);
+    bulk_store<kT, 2, kImg>(c, u, pool, num_pages, num_kv_heads, hd, n, slot, rot_out, clip, gsize, sq_err, kbits,
+                            vbits, lane, img);
 }
 
 // kNarrow: 2-bit keys and values (the tile goes through the wave's LDS
@@ -667,13 +697,13 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
     const int page = nl < 16 ? (s0 >> 4) : (s16 >> 4);
     const bool mine = sl >= 0 && sl < num_pages * kPage && sl == kPage * page + (nl & 15);
     if ((s0 >> 4) != (s16 >> 4) && __ballot(mine) == ~0ull) {
-      constexpr int kChunks = kBlockBytes / 16;  // 96 per block
+      constexpr int kImgBlk = kBlockBytes / 16;  // image chunks per block (96)
+      const int nb = block_bytes(2, 2, gsize);   // 1536, 1280 or 1152 bytes stored
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        uint4v* dst = reinterpret_cast<uint4v*>(
-            pool + (static_cast<size_t>((b ? s16 : s0) >> 4) * num_kv_heads + hd) * kBlockBytes);
-        dst[lane] = s_img[wave][b * kChunks + lane];
-        if (lane < kChunks - 64) dst[64 + lane] = s_img[wave][b * kChunks + 64 + lane];
+        uint4v* dst = reinterpret_cast<uint4v*>(pool + (static_cast<size_t>((b ? s16 : s0) >> 4) * num_kv_heads + hd) * nb);
+        dst[lane] = s_img[wave][b * kImgBlk + lane];
+        if (lane < nb / 16 - 64) dst[64 + lane] = s_img[wave][b * kImgBlk + 64 + lane];
       }
     } else if (sl >= 0 && sl < num_pages * kPage) {
       // Otherwise each token's own bytes go to its slot: lane (h, n) copies
@@ -686,7 +716,8 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
       const int hh = lid >> 5, ln = lid & 31;
       const uint8_t* ib = img + kBlockBytes * (ln >> 4);
       const int io = ln & 15, off = sl & 15;
-      uint8_t* blk = pool + (static_cast<size_t>(sl >> 4) * num_kv_heads + hd) * kBlockBytes;
+      uint8_t* blk = pool + (static_cast<size_t>(sl >> 4) * num_kv_heads + hd) * block_bytes(2, 2, gsize);
+      const int shift = meta_shift(gsize);
 #pragma unroll
       for (int a = 2 * hh; a < 2 * hh + 2; ++a)
         *reinterpret_cast<uint2*>(blk + 16 * (16 * a + off)) = *reinterpret_cast<const uint2*>(ib + 16 * (16 * a + io));
@@ -696,13 +727,14 @@ __global__ __launch_bounds__(kBulkThreads) void append_bulk_kernel(
             *reinterpret_cast<const uint16_t*>(ib + 16 * (16 * (io >> 2) + b) + 8 + 4 * ((io & 3) >> 1) +
                                                2 * (io & 1));
 #pragma unroll
-      for (int g = 2 * hh; g < 2 * hh + 2; ++g)
+      for (int g = 2 * hh; g < 2 * hh + 2; ++g)  // the pairs of the groups of G channels starting at 32 g
+        if ((g & ((1 << shift) - 1)) == 0)
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-          *reinterpret_cast<uint32_t*>(blk + kCodeBytes + kMetaRecordBytes * (4 * g + (off >> 2)) + 16 * t +
-                                       4 * (off & 3)) =
-              *reinterpret_cast<const uint32_t*>(ib + kCodeBytes + kMetaRecordBytes * (4 * g + (io >> 2)) + 16 * t +
-                                                 4 * (io & 3));
+          for (int t = 0; t < 2; ++t)
+            *reinterpret_cast<uint32_t*>(blk + kCodeBytes + kMetaRecordBytes * (4 * (g >> shift) + (off >> 2)) +
+                                         16 * t + 4 * (off & 3)) =
+                *reinterpret_cast<const uint32_t*>(ib + kCodeBytes + kMetaRecordBytes * (4 * (g >> shift) + (io >> 2)) +
+                                                   16 * t + 4 * (io & 3));
     }
     // the next tile's image writes come after these reads
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -231,8 +231,11 @@ void decode_kernel(const DecodeParams p) {
   // ring parts: codes of page 0, of page 1, metadata, then the keys' and the values' high-bit planes
   constexpr int kRingParts = 3 + kKW + kVW;
   constexpr int kKPart = 3, kVPart = 3 + kKW;
-  constexpr int kBlk = block_bytes(kKW ? 4 : 2, kVW ? 4 : 2);
-  constexpr int kVPlane = v_hi_plane(kKW ? 4 : 2);
+  // the block's size and the offsets of its metadata's end and planes follow
+  // the cache format (G, and 3- or 4-bit codes: kvq_device.h)
+  const int kBlk = block_bytes(p.kbits, p.vbits, p.gsize);
+  const int kKPlane = k_hi_plane(p.gsize);
+  const int kVPlane = v_hi_plane(p.kbits, p.gsize);
   static_assert(kDepth >= 2 && kDmaPerPair * (kDepth - 1) <= 63, "ring depth within the vmcnt range");
   constexpr int kNH = 4 * kNQ;
   constexpr int kThreads = 64 * kW;
@@ -462,7 +465,11 @@ void decode_kernel(const DecodeParams p) {
   const int col = lane & 15;  // MFMA column: 4*grp + jj
   const int grp = col >> 2;
   const int jj = col & 3;
-  const int meta_off = kMetaRecordBytes * (4 * grp + a);  // within a page's metadata
+  // within a page's metadata: the record of the group of G channels holding 32-channel group grp
+  const int meta_off = kMetaRecordBytes * (4 * (grp >> meta_shift(p.gsize)) + a);
+  // 16-byte chunks per page of the metadata and of the planes (fewer lanes load them when compact)
+  const int meta_ch = meta_bytes(p.gsize) / 16;
+  const int kplane_ch = plane_bytes(p.kbits) / 16, vplane_ch = plane_bytes(p.vbits) / 16;
   const uint8_t* pool_h = p.pool + static_cast<size_t>(h) * kBlk;
   const size_t page_stride = static_cast<size_t>(H) * kBlk;
 
@@ -477,22 +484,26 @@ void decode_kernel(const DecodeParams p) {
     uint4v(*r)[64] = ring(slot);
     dma16(blk0, 16 * lane, &r[0][0]);
     dma16(blk1, 16 * lane, &r[1][0]);
-    // metadata: lanes 0..31 take page 0's 512 B, lanes 32..63 page 1's
-    if (lane < 32)
-      dma16(blk0, kCodeBytes + 16 * lane, &r[2][0]);
-    else
-      dma16(blk1, kCodeBytes - 512 + 16 * lane, &r[2][0]);
-    if (kKW) {  // the keys' high-bit planes, page 0 then page 1 (512 B each)
-      if (lane < 32)
-        dma16(blk0, kKHiPlane + 16 * lane, &r[kKPart][0]);
-      else
-        dma16(blk1, kKHiPlane - 512 + 16 * lane, &r[kKPart][0]);
+    // metadata: lanes 0.. take page 0's, lanes 32.. page 1's (512 B apart in
+    // the ring whatever their size)
+    if (lane < 32) {
+      if (lane < meta_ch) dma16(blk0, kCodeBytes + 16 * lane, &r[2][0]);
+    } else {
+      if (lane - 32 < meta_ch) dma16(blk1, kCodeBytes - 512 + 16 * lane, &r[2][0]);
+    }
+    if (kKW) {  // the keys' high-bit planes, page 0 then page 1 (512 B apart)
+      if (lane < 32) {
+        if (lane < kplane_ch) dma16(blk0, kKPlane + 16 * lane, &r[kKPart][0]);
+      } else {
+        if (lane - 32 < kplane_ch) dma16(blk1, kKPlane - 512 + 16 * lane, &r[kKPart][0]);
+      }
     }
     if (kVW) {  // the values' high-bit planes
-      if (lane < 32)
-        dma16(blk0, kVPlane + 16 * lane, &r[kVPart][0]);
-      else
-        dma16(blk1, kVPlane - 512 + 16 * lane, &r[kVPart][0]);
+      if (lane < 32) {
+        if (lane < vplane_ch) dma16(blk0, kVPlane + 16 * lane, &r[kVPart][0]);
+      } else {
+        if (lane - 32 < vplane_ch) dma16(blk1, kVPlane - 512 + 16 * lane, &r[kVPart][0]);
+      }
     }
   };
 
@@ -572,8 +583,8 @@ void decode_kernel(const DecodeParams p) {
       const int tensor = tid / kHeadDim;
       const int pos = T - 1;
       uint8_t* blk = p.pool + (static_cast<size_t>(s_pages[np - 1]) * H + h) * kBlk;
-      s_hat[tensor][rc] =
-          q2_pack_channel(s_nrow[tensor][rc], rc, tensor, blk, pos & (kPage - 1), p.clip, rg.x, rg.y, p.kbits, p.vbits);
+      s_hat[tensor][rc] = q2_pack_channel(s_nrow[tensor][rc], rc, tensor, blk, pos & (kPage - 1), p.clip, rg.x, rg.y,
+                                          p.kbits, p.vbits, p.gsize);
     }
   }
   for (int jh = wave; jh < kNH; jh += kW) {
@@ -666,21 +677,44 @@ void decode_kernel(const DecodeParams p) {
     P.vm0 = *reinterpret_cast<const uint4v*>(meta + meta_off + 16);
     P.km1 = *reinterpret_cast<const uint4v*>(meta + 512 + meta_off);
     P.vm1 = *reinterpret_cast<const uint4v*>(meta + 512 + meta_off + 16);
-    // wide codes: the plane words (H0, H1 or VH0, VH1) of record `lane`, per page
+    // wide codes: the high bits of record `lane`, per page, at the positions of
+    // their low bits in the code words (H0, H1 or VH0, VH1).  4-bit planes hold
+    // them so; a 3-bit key plane word holds both K words' bits interleaved (bit
+    // j + w), a 3-bit value plane word one byte per slot (bit 8 i + t), spread
+    // here to bit 2 t + 16 (i % 2) of word i / 2.
     uint32_t kh[2][2] = {{0u, 0u}, {0u, 0u}}, vh[2][2] = {{0u, 0u}, {0u, 0u}};
     if (kKW) {
       const uint32_t* hp = reinterpret_cast<const uint32_t*>(&r[kKPart][0]);
-      kh[0][0] = hp[2 * lane];
-      kh[0][1] = hp[2 * lane + 1];
-      kh[1][0] = hp[128 + 2 * lane];
-      kh[1][1] = hp[128 + 2 * lane + 1];
+#pragma unroll
+      for (int X = 0; X < 2; ++X) {
+        if (p.kbits == 3) {
+          const uint32_t w = hp[128 * X + lane];
+          kh[X][0] = w & 0x55555555u;
+          kh[X][1] = (w >> 1) & 0x55555555u;
+        } else {
+          kh[X][0] = hp[128 * X + 2 * lane];
+          kh[X][1] = hp[128 * X + 2 * lane + 1];
+        }
+      }
     }
     if (kVW) {
       const uint32_t* hp = reinterpret_cast<const uint32_t*>(&r[kVPart][0]);
-      vh[0][0] = hp[2 * lane];
-      vh[0][1] = hp[2 * lane + 1];
-      vh[1][0] = hp[128 + 2 * lane];
-      vh[1][1] = hp[128 + 2 * lane + 1];
+#pragma unroll
+      for (int X = 0; X < 2; ++X) {
+        if (p.vbits == 3) {
+          const uint32_t w = hp[128 * X + lane];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            uint32_t y = ((w >> (16 * q)) & 0xffu) | (((w >> (16 * q + 8)) & 0xffu) << 16);
+            y = (y | (y << 4)) & 0x0f0f0f0fu;
+            y = (y | (y << 2)) & 0x33333333u;
+            vh[X][q] = (y | (y << 1)) & 0x55555555u;
+          }
+        } else {
+          vh[X][0] = hp[128 * X + 2 * lane];
+          vh[X][1] = hp[128 * X + 2 * lane + 1];
+        }
+      }
     }
     const int i0 = 2 * pair;
     // page ids and the pair's validity are wave-uniform (scalar registers)

@@ -4,25 +4,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kvq_layout.h"
+
 namespace kvq {
 
 // Cache geometry (the only one the kernels implement).
 constexpr int kHeadDim = 128;
 constexpr int kGroup = 32;
 constexpr int kPage = 16;
-constexpr int kBlockBytes = 1536;   // one (page, KV head) block of 2-bit codes
-constexpr int kCodeBytes = 1024;    // 64 records x 16 B of K/V code words
-constexpr int kMetaRecordBytes = 32;
-// 3- and 4-bit codes keep their low two bits in the 2-bit layout and the rest
-// in a 512-byte plane per widened tensor (64 records of 8 B, record r at 8 r,
-// words at the bits of the two K or the two V words of record r): the keys'
-// plane at byte 1536, the values' plane after it (1536 or 2048).
-constexpr int kPlaneBytes = 512;
-constexpr int kKHiPlane = kBlockBytes;
-__host__ __device__ constexpr int block_bytes(int kbits, int vbits) {
-  return kBlockBytes + (kbits > 2 ? kPlaneBytes : 0) + (vbits > 2 ? kPlaneBytes : 0);
-}
-__host__ __device__ constexpr int v_hi_plane(int kbits) { return kBlockBytes + (kbits > 2 ? kPlaneBytes : 0); }
 
 // Decode split limits and the partial-result row stride (floats).
 constexpr int kMaxPagesPerSplit = 2048;

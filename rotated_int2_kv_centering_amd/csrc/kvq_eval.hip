@@ -101,13 +101,17 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   __shared__ float s_qh[kNH][kHeadDim];  // q R_K * c
   __shared__ float s_qs[kNH][4];         // per-32-channel sums of s_qh
   // per-wave page staging, reused by the merges
-  constexpr int kBlk = kBlockBytes + kPlaneBytes * kPlanes;
+  constexpr int kBlk = kBlockBytes + 512 * kPlanes;  // the largest block of this plane count (G = 32, 4 bits)
   constexpr int kBlkWords = kBlk / 4;
-  constexpr int kBlkChunks = kBlk / 16;
+  const int nb = block_bytes(p.kbits, p.vbits, p.gsize);  // this pool's block: its stride and size
+  const int nb_chunks = nb / 16;
+  const int msh = meta_shift(p.gsize);                // metadata record of 32-channel group c: 4 (c >> msh) + slot / 4
   constexpr int kStage = 2 * kPage * kRowPad + kBlkWords + 2 * kNH * kPage + 2 * kNH;
-  const bool kwide = kPlanes > 0 && p.kbits > 2;     // the keys' high-bit plane at byte 1536
+  const bool kwide = kPlanes > 0 && p.kbits > 2;     // the keys' high-bit plane after the metadata
   const bool vwide = kPlanes > 0 && p.vbits > 2;     // the values' plane after it
-  const int vpw = v_hi_plane(p.kbits) / 4;           // word index of the values' plane
+  const bool k3 = p.kbits == 3, v3 = p.vbits == 3;   // 3-bit planes: one word per record
+  const int kpw = k_hi_plane(p.gsize) / 4;           // word index of the keys' plane
+  const int vpw = v_hi_plane(p.kbits, p.gsize) / 4;  // word index of the values' plane
   constexpr int kMergeW = kEvWaves * kNH * (3 * kHeadDim + 4) + kEvWaves;
   constexpr int kBuf = kEvWaves * kStage > kMergeW ? kEvWaves * kStage : kMergeW;
   __shared__ float s_buf[kBuf];
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   float* const st = s_buf + wave * kStage;
   float* const s_k = st;                                   // [16][kRowPad]
   float* const s_v = st + kPage * kRowPad;                 // [16][kRowPad]
-  uint32_t* const s_blk = reinterpret_cast<uint32_t*>(st + 2 * kPage * kRowPad);  // the block: 384, 512 or 640 words
+  uint32_t* const s_blk = reinterpret_cast<uint32_t*>(st + 2 * kPage * kRowPad);  // the block: up to 384, 512 or 640 words
   float* const s_p = st + 2 * kPage * kRowPad + kBlkWords;  // [2][kNH][16]
   float* const s_al = s_p + 2 * kNH * kPage;                      // [2][kNH]
 
@@ -174,11 +178,11 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   };
   auto load_page = [&](int pg, int id, PageRegs<kF32>& r) {
     const int nt = min(kPage, T - kPage * pg);
-    const uint8_t* blk = p.pool + (static_cast<size_t>(id) * H + h) * kBlk;
+    const uint8_t* blk = p.pool + (static_cast<size_t>(id) * H + h) * nb;
 #pragma unroll
     for (int u = 0; u < 3; ++u)
-      r.blk[u] = 64 * u + lane < kBlkChunks ? *reinterpret_cast<const uint4v*>(blk + 16 * (64 * u + lane))
-                                            : uint4v{0u, 0u, 0u, 0u};
+      r.blk[u] = 64 * u + lane < nb_chunks ? *reinterpret_cast<const uint4v*>(blk + 16 * (64 * u + lane))
+                                           : uint4v{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < PageRegs<kF32>::kRowWords; ++u) {
       const int idx = u * 64 + lane;
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   auto stage_page = [&](const PageRegs<kF32>& r) {
 #pragma unroll
     for (int u = 0; u < 3; ++u)
-      if (64 * u + lane < kBlkChunks) reinterpret_cast<uint4v*>(s_blk)[64 * u + lane] = r.blk[u];
+      if (64 * u + lane < nb_chunks) reinterpret_cast<uint4v*>(s_blk)[64 * u + lane] = r.blk[u];
 #pragma unroll
     for (int u = 0; u < PageRegs<kF32>::kRowWords; ++u) {
       const int idx = u * 64 + lane;
@@ -280,9 +284,19 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const uint32_t w01[2] = {s_blk[4 * (16 * a + t_l)], s_blk[4 * (16 * a + t_l) + 1]};
-        // wide keys: the high bits, record 16 a + t_l of the plane at word 384, words H0, H1
-        const uint32_t h01[2] = {kwide ? s_blk[384 + 2 * (16 * a + t_l)] : 0u,
-                                 kwide ? s_blk[384 + 2 * (16 * a + t_l) + 1] : 0u};
+        // wide keys: the high bits of record 16 a + t_l at the positions of their low bits, from the
+        // plane's words H0, H1 (4 bits) or from its one word, H0's bits even and H1's odd (3 bits)
+        uint32_t h01[2] = {0u, 0u};
+        if (kwide) {
+          if (k3) {
+            const uint32_t P = s_blk[kpw + 16 * a + t_l];
+            h01[0] = P & 0x55555555u;
+            h01[1] = (P >> 1) & 0x55555555u;
+          } else {
+            h01[0] = s_blk[kpw + 2 * (16 * a + t_l)];
+            h01[1] = s_blk[kpw + 2 * (16 * a + t_l) + 1];
+          }
+        }
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
           const uint32_t w = w01[kk >> 1], wh = h01[kk >> 1];
@@ -307,7 +321,7 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
         float acc = 0.0f;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-          const uint32_t pr = s_blk[(kCodeBytes + kMetaRecordBytes * (4 * kk + (t_l >> 2))) / 4 + (t_l & 3)];
+          const uint32_t pr = s_blk[(kCodeBytes + kMetaRecordBytes * (4 * (kk >> msh) + (t_l >> 2))) / 4 + (t_l & 3)];
           acc = fmaf(f16_lo(pr), dq[u][kk], fmaf(f16_hi(pr), s_qs[jq + 4 * u][kk], acc));
         }
         eq[u] = acc;
@@ -368,18 +382,24 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
         }
       }
       // V code of slot t, channel c: record 16 (t / 4) + c % 16, word V[(t % 4) / 2], bit 2 (c / 16) + 16 (t % 2);
-      // V (scale, zero) of (group c / 32, slot t): record 4 (c / 32) + t / 4, at +16 + 4 (t % 4)
-      const int tile = c0 >> 4, b0 = c0 & 15, grp = c0 >> 5;
+      // V (scale, zero) of (channel c, slot t): record 4 (c / G) + t / 4, at +16 + 4 (t % 4)
+      const int tile = c0 >> 4, b0 = c0 & 15, grp = (c0 >> 5) >> msh;
       for (int t = 0; t < nt; ++t) {
         const int wsel = 2 + ((t & 3) >> 1);
         const int sh = 2 * tile + 16 * (t & 1);
         const uint32_t w0 = s_blk[4 * (16 * (t >> 2) + b0) + wsel];
         const uint32_t w1 = s_blk[4 * (16 * (t >> 2) + b0 + 1) + wsel];
         uint32_t cv0 = (w0 >> sh) & 3u, cv1 = (w1 >> sh) & 3u;
-        if (vwide) {  // high bits: the same record and bit of the values' plane, word VH[(t % 4) / 2]
-          const int hsel = (t & 3) >> 1;
-          cv0 |= ((s_blk[vpw + 2 * (16 * (t >> 2) + b0) + hsel] >> sh) & 3u) << 2;
-          cv1 |= ((s_blk[vpw + 2 * (16 * (t >> 2) + b0 + 1) + hsel] >> sh) & 3u) << 2;
+        if (vwide) {
+          if (v3) {  // the high bit: bit 8 (t % 4) + c / 16 of the record's plane word
+            const int hb = 8 * (t & 3) + tile;
+            cv0 |= ((s_blk[vpw + 16 * (t >> 2) + b0] >> hb) & 1u) << 2;
+            cv1 |= ((s_blk[vpw + 16 * (t >> 2) + b0 + 1] >> hb) & 1u) << 2;
+          } else {  // the high bits: the same record and bit of the values' plane, word VH[(t % 4) / 2]
+            const int hsel = (t & 3) >> 1;
+            cv0 |= ((s_blk[vpw + 2 * (16 * (t >> 2) + b0) + hsel] >> sh) & 3u) << 2;
+            cv1 |= ((s_blk[vpw + 2 * (16 * (t >> 2) + b0 + 1) + hsel] >> sh) & 3u) << 2;
+          }
         }
         const uint32_t pr = s_blk[(kCodeBytes + kMetaRecordBytes * (4 * grp + (t >> 2)) + 16) / 4 + (t & 3)];
         const float sv = f16_lo(pr), zv = f16_hi(pr);

@@ -98,7 +98,7 @@ struct DecodeParams {
   const float* mu;
   float clip;  // Q2's clip ratio for the appended token
   int gsize;   // Q2's group size G (32, 64 or 128) for the appended token
-  int kbits;   // bits per key code: 2, or 3 / 4 (a high-bit plane at byte 1536)
+  int kbits;   // bits per key code: 2, or 3 / 4 (a high-bit plane after the metadata)
   int vbits;   // bits per value code: 2, or 3 / 4 (a high-bit plane after the keys' one, if any)
   int rot_kind;  // 0: r_k, r_v are dense [H][128][128]; 1: Hadamard, r_k, r_v are signs [H][128]
 };
@@ -138,7 +138,8 @@ struct EvalParams {
   const float* r_k;
   const float* r_v;
   int rot_kind;   // 0 dense [H][128][128], 1 Hadamard signs [H][128]
-  int kbits;      // bits per key code (3 and 4: a high-bit plane at byte 1536)
+  int gsize;      // Q2's group size G (32, 64 or 128): one metadata pair per G channels
+  int kbits;      // bits per key code (3 and 4: a high-bit plane after the metadata)
   int vbits;      // bits per value code (3 and 4: a high-bit plane after the keys' one, if any)
   float sm_scale;
   int n_splits, pages_per_split;

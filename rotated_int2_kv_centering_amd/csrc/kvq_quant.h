@@ -80,28 +80,28 @@ __device__ __forceinline__ float2 q2_wave_range(float xv, int gsize) {
 // out as two whole waves (j = 64 * w2 + lane), with (mn, mx) the unclipped
 // range of channel j's group (q2_wave_range).  `block` is the (page, KV head)
 // block to write, or null to only compute; `off` is the slot within the page
-// (0..15); tensor 0 = K, 1 = V.  The block keeps one metadata pair per 32
-// channels: for G > 32 each holds its group's pair.  kbits (vbits) = 3 or 4
-// quantizes the key (value) to 8 or 16 levels: its low two bits go where a
-// 2-bit code would, the rest to the tensor's plane (kvq_device.h: record r at
-// 8 r, the same word and bit).  Returns the dequantized level of channel j.
+// (0..15); tensor 0 = K, 1 = V.  The block keeps one metadata pair per group
+// of G channels (gsize).  kbits (vbits) = 3 or 4 quantizes the key (value) to
+// 8 or 16 levels: its low two bits go where a 2-bit code would, the rest to
+// the tensor's plane (kvq_device.h).  Returns the dequantized level of channel j.
 //
 // K code of slot s, channel c (kk = c/32, a = (c%32)/8, e = c%8): record
 // 16a + s, word K[kk/2], bit 2(4(kk%2) + e/2) + 16(e%2).  V code (t = c/16,
 // b = c%16, a = s/4, i = s%4): record 16a + b, word V[i/2], bit 2t + 16(i%2).
-// Metadata of slot s, group grp: record 4grp + s/4 at byte 1024 + 32*record,
-// K pair at +4(s%4), V pair at +16 + 4(s%4), each (fp16 scale, fp16 zero).
-// A K code word and a metadata pair belong to one slot (plain stores); a V
-// code word holds codes of two slots, so it is updated with atomic and/or of
-// this slot's bits only, which keeps concurrent writes to other slots intact.
+// Metadata of slot s, group grp (of G channels): record 4grp + s/4 at byte
+// 1024 + 32*record, K pair at +4(s%4), V pair at +16 + 4(s%4), each (fp16
+// scale, fp16 zero).  A K code word and a metadata pair belong to one slot
+// (plain stores); a V code word holds codes of two slots, so it is updated
+// with atomic and/or of this slot's bits only, which keeps concurrent writes
+// to other slots intact; so is a 3-bit plane word, which holds bits of both
+// K words of a record (each wave writes its own alternate bits) or of four
+// value slots.
 __device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, uint8_t* block, int off, float clip,
-                                                float mn, float mx, int kbits = 2, int vbits = 2) {
-  const bool k4 = tensor == 0 && kbits > 2;  // a wide key: high part in the plane
-  const bool v4 = tensor == 1 && vbits > 2;  // a wide value: high part in the values' plane
-  const float n_lv = static_cast<float>((1 << (tensor == 0 ? kbits : vbits)) - 1);
+                                                float mn, float mx, int kbits = 2, int vbits = 2, int gsize = 32) {
+  const int bits = tensor == 0 ? kbits : vbits;
+  const float n_lv = static_cast<float>((1 << bits) - 1);
   const int lane = j & 63;
   const int w2 = j >> 6;
-  const int grp = j >> 5;
   mn *= clip;
   mx *= clip;
   // c*min and c*max are rounded to fp32 before anything else uses them (the
@@ -120,15 +120,17 @@ __device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, ui
   }
 
   if (tensor == 0) {
-    const int kk = grp, a = (j & 31) >> 3, e = j & 7;
+    const int kk = j >> 5, a = (j & 31) >> 3, e = j & 7;
     const int sh = 2 * (4 * (kk & 1) + (e >> 1)) + 16 * (e & 1);
     uint32_t w = (code & 3u) << sh;
-    uint32_t wh = (code >> 2) << sh;  // 4-bit keys: the high bits (0 otherwise)
+    // wide keys: the high bits at the same position (4 bits), or the high bit
+    // at the position plus the word index w2 (3 bits)
+    uint32_t wh = bits == 4 ? (code >> 2) << sh : (code >> 2) << (sh + w2);
     w |= __shfl_xor(w, 1);
     w |= __shfl_xor(w, 2);
     w |= __shfl_xor(w, 4);
     w |= __shfl_xor(w, 32);
-    if (k4) {
+    if (bits > 2) {
       wh |= __shfl_xor(wh, 1);
       wh |= __shfl_xor(wh, 2);
       wh |= __shfl_xor(wh, 4);
@@ -136,16 +138,24 @@ __device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, ui
     }
     if (block != nullptr && (lane & 39) == 0) {  // e == 0, kk even: lanes 0, 8, 16, 24 hold both groups' words
       *reinterpret_cast<uint32_t*>(block + 16 * (16 * a + off) + 4 * w2) = w;
-      if (k4) *reinterpret_cast<uint32_t*>(block + kKHiPlane + 8 * (16 * a + off) + 4 * w2) = wh;
+      if (bits == 4) {
+        *reinterpret_cast<uint32_t*>(block + k_hi_plane(gsize) + 8 * (16 * a + off) + 4 * w2) = wh;
+      } else if (bits == 3) {  // this wave's alternate bits of the record's plane word
+        uint32_t* pw = reinterpret_cast<uint32_t*>(block + k_hi_plane(gsize) + 4 * (16 * a + off));
+        atomicAnd(pw, ~(0x55555555u << w2));
+        atomicOr(pw, wh);
+      }
     }
   } else {
     const int t16 = j >> 4, b = j & 15, a = off >> 2, i = off & 3;
     const int shift = 16 * (i & 1);
     uint32_t w = (code & 3u) << (2 * t16 + shift);
-    uint32_t wh = (code >> 2) << (2 * t16 + shift);  // wide values: the high bits (0 otherwise)
+    // wide values: the high bits at the same position (4 bits), or the high
+    // bit at bit 8 i + t16 of the record's plane word (3 bits)
+    uint32_t wh = bits == 4 ? (code >> 2) << (2 * t16 + shift) : (code >> 2) << (8 * i + t16);
     w |= __shfl_xor(w, 16);
     w |= __shfl_xor(w, 32);
-    if (v4) {
+    if (bits > 2) {
       wh |= __shfl_xor(wh, 16);
       wh |= __shfl_xor(wh, 32);
     }
@@ -154,17 +164,22 @@ __device__ __forceinline__ float q2_pack_channel(float xv, int j, int tensor, ui
       const uint32_t mask = 0xffu << (8 * w2 + shift);  // this wave's four tiles of this slot
       atomicAnd(word, ~mask);
       atomicOr(word, w);
-      if (v4) {  // the plane's words are shared by slots as the V words are
-        uint32_t* hword = reinterpret_cast<uint32_t*>(block + v_hi_plane(kbits) + 8 * (16 * a + b) + 4 * (i >> 1));
+      if (bits == 4) {  // the plane's words are shared by slots as the V words are
+        uint32_t* hword =
+            reinterpret_cast<uint32_t*>(block + v_hi_plane(kbits, gsize) + 8 * (16 * a + b) + 4 * (i >> 1));
         atomicAnd(hword, ~mask);
+        atomicOr(hword, wh);
+      } else if (bits == 3) {  // this wave's four tiles of slot i: a nibble of byte i
+        uint32_t* hword = reinterpret_cast<uint32_t*>(block + v_hi_plane(kbits, gsize) + 4 * (16 * a + b));
+        atomicAnd(hword, ~(0xfu << (8 * i + 4 * w2)));
         atomicOr(hword, wh);
       }
     }
   }
-  if (block != nullptr && (j & 31) == 0) {
+  if (block != nullptr && (j & (gsize - 1)) == 0) {
     const uint32_t pair = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, s16)) |
                           (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, z16)) << 16);
-    const int rec = 4 * grp + (off >> 2);
+    const int rec = 4 * (j / gsize) + (off >> 2);
     *reinterpret_cast<uint32_t*>(block + kCodeBytes + kMetaRecordBytes * rec + 16 * tensor + 4 * (off & 3)) = pair;
   }
   return fmaf(sc, static_cast<float>(code), z);

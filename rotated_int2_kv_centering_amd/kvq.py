@@ -30,7 +30,7 @@ KVQ_ROT_DENSE, KVQ_ROT_HADAMARD = 0, 1
 # kvq_pt_policy
 KVQ_PT_CONTIGUOUS, KVQ_PT_PERMUTED, KVQ_PT_INTERLEAVED, KVQ_PT_VALIDATE = 0, 1, 2, 3
 
-HEAD_DIM, GROUP_SIZE, PAGE_SIZE, BLOCK_BYTES = 128, 32, 16, 1536
+HEAD_DIM, GROUP_SIZE, PAGE_SIZE = 128, 32, 16
 STATUS_NAMES = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_EUNSUPPORTED", 3: "KVQ_ENOSPACE", 4: "KVQ_EHIP"}
 
 

@@ -44,9 +44,11 @@ class DeviceCase:
         self.num_pages = int(num_pages or case.num_pages)
         self.key_bits = key_bits
         self.val_bits = val_bits
-        self.pool = torch.zeros(O.pool_bytes(self.num_pages, case.Hkv, key_bits, val_bits), dtype=torch.uint8,
-                                device=dev)
         self.group_size = group_size
+        # the block layout's parameters, as the oracle's layout functions take them
+        self.layout = dict(key_bits=key_bits, val_bits=val_bits, group=group_size)
+        self.pool = torch.zeros(O.pool_bytes(self.num_pages, case.Hkv, key_bits, val_bits, group_size),
+                                dtype=torch.uint8, device=dev)
         self.cache = kvq.make_cache(case.Hkv, self.num_pages, self.pool, clip_ratio=clip_ratio, group_size=group_size,
                                     key_bits=key_bits, val_bits=val_bits,
                                     rotation=kvq.KVQ_ROT_HADAMARD if case.rotation == "hadamard" else kvq.KVQ_ROT_DENSE)

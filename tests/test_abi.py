@@ -64,6 +64,20 @@ def test_pool_bytes(K):
     assert K.kvq_pool_bytes(K.make_cache(1, 16)) == 16 * 1536
     assert K.kvq_pool_bytes(K.make_cache(0, 16)) == 0
     assert K.kvq_pool_bytes(K.make_cache(8, 0)) == 0
+    # the metadata holds one pair per group: 80 and 72 bytes per token for G = 64 and 128
+    assert K.kvq_pool_bytes(K.make_cache(8, 16, group_size=64)) == 16 * 8 * 1280
+    assert K.kvq_pool_bytes(K.make_cache(8, 16, group_size=128)) == 16 * 8 * 1152
+    assert K.kvq_pool_bytes(K.make_cache(8, 16, group_size=48)) == 0  # unsupported group size
+    assert K.kvq_pool_bytes(K.make_cache(8, 16, key_bits=5)) == 0
+
+
+def test_pool_bytes_agree_with_the_oracle_layout(K):
+    from oracle import kvq_oracle as O
+    for g in (32, 64, 128):
+        for kb in (2, 3, 4):
+            for vb in (2, 3, 4):
+                got = K.kvq_pool_bytes(K.make_cache(3, 5, group_size=g, key_bits=kb, val_bits=vb))
+                assert got == O.pool_bytes(5, 3, kb, vb, g), (g, kb, vb)
 
 
 CTR = 4096 * 4  # the fixed ticket prefix
@@ -298,11 +312,12 @@ def test_cache_clip_ratio_layout_and_validation(K):
     assert K.kvq_pool_bytes(K.make_cache(2, 8, FAKE, key_bits=4)) == 2 * 8 * 2048
     assert K.kvq_pool_bytes(K.make_cache(2, 8, FAKE, key_bits=0)) == 2 * 8 * 1536
     assert _decode(K, K.make_cache(1, 8, FAKE, key_bits=5)) == K.KVQ_EUNSUPPORTED and "key_bits" in K.kvq_last_error()
-    assert K.kvq_pool_bytes(K.make_cache(2, 8, FAKE, key_bits=3)) == 2 * 8 * 2048
-    # 3- and 4-bit values add the values' plane: 2048 alone, 2560 with a keys' plane
+    assert K.kvq_pool_bytes(K.make_cache(2, 8, FAKE, key_bits=3)) == 2 * 8 * 1792
+    # 3- and 4-bit values add the values' plane (256 or 512 bytes)
     assert K.kvq_cache.val_bits.offset == 44
     assert K.kvq_pool_bytes(K.make_cache(2, 8, FAKE, val_bits=4)) == 2 * 8 * 2048
-    assert K.kvq_pool_bytes(K.make_cache(2, 8, FAKE, key_bits=3, val_bits=3)) == 2 * 8 * 2560
+    assert K.kvq_pool_bytes(K.make_cache(2, 8, FAKE, key_bits=3, val_bits=3)) == 2 * 8 * 2048
+    assert K.kvq_pool_bytes(K.make_cache(2, 8, FAKE, key_bits=4, val_bits=4)) == 2 * 8 * 2560
     assert K.kvq_pool_bytes(K.make_cache(2, 8, FAKE, key_bits=4, val_bits=2)) == 2 * 8 * 2048
     assert _decode(K, K.make_cache(1, 8, FAKE, val_bits=1)) == K.KVQ_EUNSUPPORTED and "val_bits" in K.kvq_last_error()
     assert _decode(K, K.make_cache(1, 8, FAKE, rotation=2)) == K.KVQ_EINVAL  # unknown rotation kind

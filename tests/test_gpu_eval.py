@@ -48,13 +48,13 @@ class Evaluated:
     """Append with squared errors, then kvq_output_error; results on the host."""
 
     def __init__(self, case, dev, d_model=96, w_dtype="bf16", table=None, with_err=True, seed=7, key_bits=2,
-                 val_bits=2):
+                 val_bits=2, group=32):
         import torch
         from rotated_int2_kv_centering_amd import kvq
         self.c = c = case
         self.key_bits = key_bits
         self.val_bits = val_bits
-        self.dc = dc = DeviceCase(case, dev, key_bits=key_bits, val_bits=val_bits)
+        self.dc = dc = DeviceCase(case, dev, key_bits=key_bits, val_bits=val_bits, group_size=group)
         n = c.n_tokens
         self.sq_err = torch.zeros((max(n, 1), c.Hkv, 2, 2), dtype=torch.float32, device=dev)
         kvq.kvq_quant_append_err(dc.cache, dc.k, dc.v, dc.in_dtype, n, dc.slots, dc.mu, dc.r_k, dc.r_v, None,
@@ -96,8 +96,7 @@ class Evaluated:
         ks = [c.k[c.tok_seq == b] for b in range(c.B)]
         vs = [c.v[c.tok_seq == b] for b in range(c.B)]
         dy_k, dy_v, e_out, e_rec = O.output_error(c.q, self.dc.pool_np(), c.Hkv, self.table, c.seq_lens, ks, vs, c.mu,
-                                                  r_k, r_v, self.w_o, num_pages=c.num_pages, key_bits=self.key_bits,
-                                                  val_bits=self.val_bits)
+                                                  r_k, r_v, self.w_o, num_pages=c.num_pages, **self.dc.layout)
         return dict(dy_k=dy_k, dy_v=dy_v, e_out=e_out, e_rec=e_rec)
 
 
@@ -195,13 +194,14 @@ def test_full_size_llama8b_t128k():
     _check(ev.run(), ev.oracle())
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits,group", [(3, 32), (4, 32), (3, 128), (4, 64)])
 @pytest.mark.parametrize("shape", [(2, 32, 8, [700, 65]), (1, 64, 8, [400])], ids=lambda s: f"Hq{s[1]}")
-def test_output_error_with_wide_keys(shape, bits):
-    """3- and 4-bit keys (2048-byte blocks): the evaluator reads the high-bit plane."""
+def test_output_error_with_wide_keys(shape, bits, group):
+    """3- and 4-bit keys: the evaluator reads the keys' high-bit plane (one word per record for 3 bits, two
+    for 4) after the metadata, whose size follows the group size."""
     dev = require_gpu()
     B, Hq, Hkv, lens = shape
     case = I.make_case("evk", 240 + sum(lens) + Hq + bits, B=B, Hq=Hq, Hkv=Hkv, seq_lens=lens,
                        table_policy="interleaved")
-    ev = Evaluated(case, dev, key_bits=bits)
+    ev = Evaluated(case, dev, key_bits=bits, group=group)
     _check(ev.run(), ev.oracle())

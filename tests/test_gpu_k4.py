@@ -1,7 +1,8 @@
 """GPU parity of 3- and 4-bit keys (K3V2, K4V2 budgets) through the C ABI.
 
-A cache with key_bits = 3 or 4 holds 2048-byte blocks: the 2-bit layout with
-each key code's low two bits, plus a plane with the rest.  Gates as for 2-bit keys: the
+A cache with key_bits = 3 or 4 holds the 2-bit layout with each key code's low
+two bits, plus a plane with the rest after the metadata (256 bytes for 3 bits,
+512 for 4), for every group size.  Gates as for 2-bit keys: the
 kernel's rotated rows within the fp32 bound of the fp64 rotation and the bytes
 bit-exact to the oracle's 16-level quantizer and packing on those rows (both
 append kernels); the fused step writing the append's bytes; decode within 2e-3
@@ -59,16 +60,16 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("bits", [3, 4])
+@pytest.mark.parametrize("bits,group", [(3, 32), (4, 32), (3, 64), (3, 128), (4, 128)])
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"B{s[0]}_Hq{s[1]}_Hkv{s[2]}_T{'-'.join(map(str, s[3]))}")
-def test_decode_parity(shape, bits):
+def test_decode_parity(shape, bits, group):
     dev = require_gpu()
     B, Hq, Hkv, lens = shape
     case = I.make_case("k4d", 310 + sum(lens) + Hq, B=B, Hq=Hq, Hkv=Hkv, seq_lens=lens, table_policy="interleaved")
-    dc = DeviceCase(case, dev, key_bits=bits)
+    dc = DeviceCase(case, dev, key_bits=bits, group_size=group)
     dc.append(rot_out=False)
     ref = O.decode_attention(case.q, dc.pool_np(), case.Hkv, case.page_table, case.seq_lens, case.r_k, case.r_v,
-                             key_bits=bits)
+                             **dc.layout)
     for ns in (0, 1, 3):
         got = dc.decode("f32", num_splits=ns)
         assert max_abs_rel(got, ref) <= TOL, ns
@@ -79,23 +80,23 @@ def test_decode_parity(shape, bits):
 @pytest.mark.parametrize("shape", [(2, 32, 8, [1000, 17], "bf16"), (2, 64, 8, [513, 16], "f32"),
                                    (1, 16, 1, [300], "bf16"), (3, 8, 2, [0, 5, 100], "bf16")],
                          ids=lambda s: f"Hq{s[1]}_Hkv{s[2]}_{s[4]}")
-@pytest.mark.parametrize("bits", [3, 4])
-def test_step_writes_the_appended_bytes(shape, bits):
+@pytest.mark.parametrize("bits,group", [(3, 32), (4, 32), (3, 128)])
+def test_step_writes_the_appended_bytes(shape, bits, group):
     dev = require_gpu()
     B, Hq, Hkv, lens, dtype = shape
     case = I.make_case("k4s", 320 + sum(lens) + Hq, B=B, Hq=Hq, Hkv=Hkv, seq_lens=lens, dtype=dtype,
                        table_policy="interleaved")
     newest = _newest(case)
-    a = DeviceCase(case, dev, key_bits=bits)
+    a = DeviceCase(case, dev, key_bits=bits, group_size=group)
     _prefill(a, case, newest)
-    b = DeviceCase(case, dev, key_bits=bits)
+    b = DeviceCase(case, dev, key_bits=bits, group_size=group)
     b.pool.copy_(a.pool)
     _append_newest(a, newest)
     k_new, v_new = _new_kv(case, b, newest, dev)
     got = b.step(k_new, v_new, "f32")
     np.testing.assert_array_equal(b.pool_np(), a.pool_np())
     ref = O.decode_attention(case.q, b.pool_np(), Hkv, case.page_table, case.seq_lens, case.r_k, case.r_v,
-                             key_bits=bits)
+                             **b.layout)
     assert max_abs_rel(got, ref) <= TOL
 
 

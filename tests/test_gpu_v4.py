@@ -1,8 +1,8 @@
 """GPU parity of 3- and 4-bit values (K3V3, K2V4, K4V4 budgets) through the C ABI.
 
-A cache with val_bits = 3 or 4 adds a 512-byte plane holding each value code's
-high bits (after the keys' plane when keys are wide too), so blocks are 2048 or
-2560 bytes.  Gates as for 2-bit values: the kernel's rotated rows within the
+A cache with val_bits = 3 or 4 adds a plane holding each value code's high
+bits (256 bytes for 3 bits, 512 for 4; after the keys' plane when keys are wide
+too), for every group size.  Gates as for 2-bit values: the kernel's rotated rows within the
 fp32 bound of the fp64 rotation and the bytes bit-exact to the oracle's
 quantizer and packing on those rows (both append kernels, partial and full
 pages); the fused step writing the append's bytes; decode within 2e-3 of the
@@ -48,7 +48,7 @@ def test_append_bytes_match_the_oracle(dtype, lens, rotation, group, kb, vb):
     O.quantize_append(expect, case.Hkv, case.slots, xg, wg, group=group, key_bits=kb, val_bits=vb)
     np.testing.assert_array_equal(dc.pool_np(), expect)
     if vb > 2:  # the values really use more than four levels
-        _, _, _, vc, _, _ = O.unpack_blocks(dc.pool_np().reshape(-1, O.block_bytes(kb, vb)), kb, vb)
+        _, _, _, vc, _, _ = O.unpack_blocks(dc.pool_np().reshape(-1, O.block_bytes(kb, vb, group)), kb, vb, group)
         assert vc.max() > 3
 
 
@@ -62,17 +62,18 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("kb,vb", BUDGETS, ids=lambda b: str(b))
+@pytest.mark.parametrize("kb,vb,group", [b + (32,) for b in BUDGETS] + [(3, 3, 128), (2, 3, 64), (4, 4, 64)],
+                         ids=lambda b: str(b))
 @pytest.mark.parametrize("shape", SHAPES, ids=lambda s: f"B{s[0]}_Hq{s[1]}_Hkv{s[2]}_T{'-'.join(map(str, s[3]))}")
-def test_decode_parity(shape, kb, vb):
+def test_decode_parity(shape, kb, vb, group):
     dev = require_gpu()
     B, Hq, Hkv, lens = shape
     case = I.make_case("v4d", 410 + sum(lens) + Hq + kb, B=B, Hq=Hq, Hkv=Hkv, seq_lens=lens,
                        table_policy="interleaved")
-    dc = DeviceCase(case, dev, key_bits=kb, val_bits=vb)
+    dc = DeviceCase(case, dev, key_bits=kb, val_bits=vb, group_size=group)
     dc.append(rot_out=False)
     ref = O.decode_attention(case.q, dc.pool_np(), case.Hkv, case.page_table, case.seq_lens, case.r_k, case.r_v,
-                             key_bits=kb, val_bits=vb)
+                             **dc.layout)
     for ns in (0, 1, 3):
         got = dc.decode("f32", num_splits=ns)
         assert max_abs_rel(got, ref) <= TOL, ns
@@ -103,23 +104,23 @@ def test_hadamard_decode_parity(shape, kb, vb):
 @pytest.mark.parametrize("shape", [(2, 32, 8, [1000, 17], "bf16"), (2, 64, 8, [513, 16], "f32"),
                                    (1, 16, 1, [300], "bf16"), (3, 8, 2, [0, 5, 100], "bf16")],
                          ids=lambda s: f"Hq{s[1]}_Hkv{s[2]}_{s[4]}")
-@pytest.mark.parametrize("kb,vb", [(3, 3), (2, 4)], ids=lambda b: str(b))
-def test_step_writes_the_appended_bytes(shape, kb, vb):
+@pytest.mark.parametrize("kb,vb,group", [(3, 3, 32), (2, 4, 32), (3, 3, 64), (2, 3, 128)], ids=lambda b: str(b))
+def test_step_writes_the_appended_bytes(shape, kb, vb, group):
     dev = require_gpu()
     B, Hq, Hkv, lens, dtype = shape
     case = I.make_case("v4s", 420 + sum(lens) + Hq + vb, B=B, Hq=Hq, Hkv=Hkv, seq_lens=lens, dtype=dtype,
                        table_policy="interleaved")
     newest = _newest(case)
-    a = DeviceCase(case, dev, key_bits=kb, val_bits=vb)
+    a = DeviceCase(case, dev, key_bits=kb, val_bits=vb, group_size=group)
     _prefill(a, case, newest)
-    b = DeviceCase(case, dev, key_bits=kb, val_bits=vb)
+    b = DeviceCase(case, dev, key_bits=kb, val_bits=vb, group_size=group)
     b.pool.copy_(a.pool)
     _append_newest(a, newest)
     k_new, v_new = _new_kv(case, b, newest, dev)
     got = b.step(k_new, v_new, "f32")
     np.testing.assert_array_equal(b.pool_np(), a.pool_np())
     ref = O.decode_attention(case.q, b.pool_np(), Hkv, case.page_table, case.seq_lens, case.r_k, case.r_v,
-                             key_bits=kb, val_bits=vb)
+                             **b.layout)
     assert max_abs_rel(got, ref) <= TOL
 
 
@@ -138,13 +139,13 @@ def test_window_with_wide_values(kb, vb):
     assert max_abs_rel(got, ref) <= TOL
 
 
-@pytest.mark.parametrize("kb,vb", [(3, 3), (2, 4)], ids=lambda b: str(b))
-def test_output_error_with_wide_values(kb, vb):
-    """The evaluator reads the values' plane (2048- and 2560-byte blocks)."""
+@pytest.mark.parametrize("kb,vb,group", [(3, 3, 32), (2, 4, 32), (3, 3, 128), (4, 3, 64)], ids=lambda b: str(b))
+def test_output_error_with_wide_values(kb, vb, group):
+    """The evaluator reads the values' plane (256 bytes for 3 bits, 512 for 4) after the keys' one."""
     from tests.test_gpu_eval import Evaluated, _check
     dev = require_gpu()
     case = I.make_case("v4e", 440 + kb + vb, B=2, Hq=32, Hkv=8, seq_lens=[700, 65], table_policy="interleaved")
-    ev = Evaluated(case, dev, key_bits=kb, val_bits=vb)
+    ev = Evaluated(case, dev, key_bits=kb, val_bits=vb, group=group)
     _check(ev.run(), ev.oracle())
 
 
