@@ -82,11 +82,14 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // base + voff (base wave-uniform, in SGPRs) and its bytes land at lds + 16*l
 // (global_load_lds_dwordx4, LDS base in M0).  Issued as inline asm so the
 // compiler adds none of its own (whole-queue) waits for it; every read of a
-// ring slot is preceded by an explicit vmcnt wait instead.
+// ring slot is preceded by an explicit vmcnt wait instead.  The page stream is
+// read once per call, so it carries the non-temporal hint (nt): it displaces
+// less of what the L2 holds for the call's prologue and merge (R, page table,
+// partial rows, code).
 __device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, void* lds) {
   const uint32_t lds_addr =
       __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)(lds))));
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "s"(lds_addr)
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(base), "s"(lds_addr)
                : "memory", "m0");
 }
 
@@ -110,8 +113,7 @@ struct PagePair {
 // Sum of v over the workgroup, returned to every thread (s_red: kW ints).
 template <int kW>
 __device__ __forceinline__ int block_sum(int v, int lane, int wave, int* s_red) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  v = wave_sum_int(v);
   if (lane == 0) s_red[wave] = v;
   __syncthreads();
   int t = 0;
@@ -245,7 +247,7 @@ void decode_kernel(const DecodeParams p) {
   constexpr int kRows = kHeadDim / kParts;
   static_assert(kParts >= 2, "at least two row parts");
   __shared__ int s_pages[kMaxPagesPerSplit];
-  __shared__ float s_q[kNH][kHeadDim];  // q rows -> q_hat -> o_rot
+  __shared__ __align__(16) float s_q[kNH][kHeadDim];  // q rows -> q_hat -> o_rot
   __shared__ float s_f[kNH];
   __shared__ float s_m[kW][kNH];
   __shared__ float s_l[kW][kNH];
@@ -260,11 +262,6 @@ void decode_kernel(const DecodeParams p) {
   // page 0/1, part 2 = 32 x 16 B metadata of page 0 then of page 1; parts 3
   // and on: the high-bit planes of page 0 then of page 1 (keys', values').
   __shared__ uint4v s_ring[kDepth][kW][kRingParts][64];
-  // merge of split partial rows staged whole in the ring: the weight of every
-  // (split, head) row and each head's sum of weights
-  constexpr int kMaxImgRows = static_cast<int>(sizeof(s_ring) / sizeof(float)) / kPartStride;
-  __shared__ float s_wgt[kMaxImgRows];
-  __shared__ float s_wsum[kNH], s_wmax[kNH];
   // Prologue scratch (q_hat partials [kParts][kNH][128], then the new token's
   // partials [2][4][128]) lives in the last ring slot, which no load targets
   // before the main loop, when it fits there.  After the main loop the whole
@@ -588,9 +585,7 @@ void decode_kernel(const DecodeParams p) {
     }
   }
   for (int jh = wave; jh < kNH; jh += kW) {
-    float am = fmaxf(fabsf(s_q[jh][lane]), fabsf(s_q[jh][lane + 64]));
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+    const float am = wave_max_all(fmaxf(fabsf(s_q[jh][lane]), fabsf(s_q[jh][lane + 64])));
     if (lane == 0) {
       int e = 0;
       frexpf(am, &e);  // am in [2^(e-1), 2^e)
@@ -600,9 +595,7 @@ void decode_kernel(const DecodeParams p) {
   __syncthreads();
   if (new_att) {  // logits (log2 units) of the new token: one wave per head
     for (int jh = wave; jh < g; jh += kW) {
-      float d = fmaf(s_q[jh][lane], s_hat[0][lane], s_q[jh][lane + 64] * s_hat[0][lane + 64]);
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+      const float d = wave_sum_all(fmaf(s_q[jh][lane], s_hat[0][lane], s_q[jh][lane + 64] * s_hat[0][lane + 64]));
       if (lane == 0) s_nlog[jh] = d;
     }
   }
@@ -935,17 +928,23 @@ void decode_kernel(const DecodeParams p) {
 
   // ---- per-wave results to LDS: lane (a, b) owns channels 32a + b and
   //      32a + 16 + b (tiles 2a, 2a+1) for the four heads of each quad.
+  // lane values broadcast by readlane (scalar operands), picked by the lane's row a
+  auto lane_val = [](float x, int k) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k)); };
+  auto pick_a = [&](float x, int k0) {  // x at lane k0 + 4 a
+    const float v0 = lane_val(x, k0), v1 = lane_val(x, k0 + 4), v2 = lane_val(x, k0 + 8), v3 = lane_val(x, k0 + 12);
+    return a == 0 ? v0 : (a == 1 ? v1 : (a == 2 ? v2 : v3));
+  };
 #pragma unroll
   for (int Q = 0; Q < kNQ; ++Q) {
     // the sums were kept in units of 2^e_u of the lane's value group: lanes
     // 0..3 (group 0) carry the weight sums, acc rows of group a take group a's unit
     const float unit = ldexpf(1.0f, static_cast<int>(e_u));
-    const float unit_a = __shfl(unit, 4 * a);
+    const float unit_a = pick_a(unit, 0);
     const float lsum = rows_sum(l_run[Q]) * unit;
     const float zsum = rows_sum(z_run[Q]) * unit;  // lane (., grp, jj): sum_s p z_v for (jj, grp)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float zi = __shfl(zsum, 4 * a + i);  // zero part of head i, group a
+      const float zi = pick_a(zsum, i);  // zero part of head i, group a (the rows hold the same sums)
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
         if ((t >> 1) == a)  // undo the tile's code factor 4^(t%4), the 2^-24 code scale and the unit
@@ -1253,16 +1252,27 @@ void decode_kernel(const DecodeParams p) {
   if (tid == 0)
     s_ticket = __hip_atomic_fetch_add(p.counters + b * H + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // R_V rows for the output rotation, requested by every workgroup right after
-  // its ticket (the merging one finds them in flight): thread (row oi, part oq)
-  // takes channels [kRows * oq, +kRows) of row oi
+  // its ticket (the merging one finds them in flight).  Thread (row ri, part
+  // rq), rq in the upper lane bits, takes channels [kRows * rq, +kRows) of
+  // row ri, in 16-byte chunks rotated by rq so that the kParts lanes sharing a
+  // row read different LDS banks of o_rot; the parts are then summed across
+  // lanes.  Hadamard: thread oi holds the sign of output channel oi.
+  constexpr int kOiW = 64 / kParts;          // output rows per wave
+  constexpr int kChunks = kRows / 4;         // 16-byte chunks per part
+  constexpr int kChunkRot = 8 / kParts;      // chunk rotation per part
+  const bool rot_lane = tid < kParts * kHeadDim;  // whole waves
+  const int ri = (tid >> 6) * kOiW + (lane % kOiW);
+  const int rq = lane / kOiW;
   const int oi = tid & (kHeadDim - 1);
-  const int oq = rpart;
-  float4v rr[kRows / 4];
-  float sgv = 0.0f;  // Hadamard: the sign of output channel oi
+  float4v rr[kChunks];
+  float sgv = 0.0f;
   if (!hadamard) {
-    const float* Rrow = p.r_v + (static_cast<size_t>(h) * kHeadDim + oi) * kHeadDim + kRows * oq;
+    if (rot_lane) {
+      const float* Rrow = p.r_v + (static_cast<size_t>(h) * kHeadDim + ri) * kHeadDim + kRows * rq;
 #pragma unroll
-    for (int u = 0; u < kRows / 4; ++u) rr[u] = *reinterpret_cast<const float4v*>(Rrow + 4 * u);
+      for (int u = 0; u < kChunks; ++u)
+        rr[u] = *reinterpret_cast<const float4v*>(Rrow + 4 * ((u + kChunkRot * rq) % kChunks));
+    }
   } else {
     sgv = p.r_v[h * kHeadDim + oi];
   }
@@ -1330,32 +1340,6 @@ void decode_kernel(const DecodeParams p) {
   }
   if (img) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial-row copies have landed
   __syncthreads();
-  // Whole rows in the ring ([split][head][acc 128 | max | sum | pad]): wave jh
-  // takes head jh's rows, lane l the splits l, l + 64, ...: the head's max M,
-  // the weights exp2(max_split - M) into s_wgt and their sum; the output sums
-  // below then read weights and rows with no chain of dependent reads.
-  if (img) {
-    for (int jh = wave; jh < g; jh += kW) {
-      float m = kNegBig;
-      for (int sp = lane; sp < n_valid; sp += 64) m = fmaxf(m, s_post[(sp * g + jh) * kPartStride + 128]);
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-      float l = 0.0f;
-      for (int sp = lane; sp < n_valid; sp += 64) {
-        const float* r = s_post + (sp * g + jh) * kPartStride;
-        const float w = __builtin_amdgcn_exp2f(r[128] - m);
-        s_wgt[sp * g + jh] = w;
-        l = fmaf(w, r[129], l);
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
-      if (lane == 0) {
-        s_wsum[jh] = l;
-        s_wmax[jh] = m;
-      }
-    }
-    __syncthreads();
-  }
 #pragma unroll
   for (int k = 0; k < kIdx; ++k) {
     const int idx = tid + k * kThreads;
@@ -1364,14 +1348,36 @@ void decode_kernel(const DecodeParams p) {
     const int c = idx % kHeadDim;
     float M = kNegBig, l = 0.0f;
     if (img) {
-      const float* col = s_post + jh * kPartStride + c;
-      const float* wv = s_wgt + jh;
+      // Whole rows in the ring ([split][head][acc 128 | max | sum | pad]).  The
+      // 64 lanes of a wave are 64 channels of one head (idx's head is uniform
+      // per wave): lane l forms the weight exp2(max_split - M) of splits l,
+      // l + 64, ... in registers, and each weight reaches the channel sums as a
+      // scalar operand (readlane), with no barrier and no LDS round trip.
+      const float* rows = s_post + jh * kPartStride;
+      float m = kNegBig;
+      for (int sp = lane; sp < n_valid; sp += 64) m = fmaxf(m, rows[sp * g * kPartStride + 128]);
+      m = wave_max_all(m);
       float o = 0.0f;
-#pragma unroll 8
-      for (int sp = 0; sp < n_valid; ++sp) o = fmaf(wv[sp * g], col[sp * g * kPartStride], o);
-      l = s_wsum[jh];
+      for (int s0 = 0; s0 < n_valid; s0 += 64) {
+        const int sl = min(s0 + lane, n_valid - 1);
+        const float w = s0 + lane < n_valid ? __builtin_amdgcn_exp2f(rows[sl * g * kPartStride + 128] - m) : 0.0f;
+        l = fmaf(w, rows[sl * g * kPartStride + 129], l);
+        // 16 splits per batch: their loads are issued together, then the FMAs
+        // in split order (w = 0 past the last split, whose rows read a valid one)
+        const int n = min(64, n_valid - s0);
+        const float* col = rows + s0 * g * kPartStride + c;
+        for (int u0 = 0; u0 < n; u0 += 16) {
+          float x[16];
+#pragma unroll
+          for (int e = 0; e < 16; ++e) x[e] = col[min(u0 + e, n - 1) * g * kPartStride];
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            o = fmaf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), u0 + e)), x[e], o);
+        }
+      }
+      l = wave_sum_all(l);
       if (win_here) {  // the window's part: its weight against the splits' max, value sum added after R_V^T
-        const float m = s_wmax[jh], mx = fmaxf(m, w_m[k]);
+        const float mx = fmaxf(m, w_m[k]);
         const float a = __builtin_amdgcn_exp2f(m - mx), ww = __builtin_amdgcn_exp2f(w_m[k] - mx);
         l = fmaf(a, l, ww * w_l[k]);
         o *= a;
@@ -1422,28 +1428,37 @@ void decode_kernel(const DecodeParams p) {
       if (act && jh < g) store_out(jh, i, y * kInvSqrt128 * sgv);
     }
   } else {
-  // o = o_rot R_V^T: o[i] = sum_c o_rot[c] R_V[i][c]; thread (i, part) sums kRows channels
-  if (tid < kParts * kHeadDim) {
+  // o = o_rot R_V^T: o[i] = sum_c o_rot[c] R_V[i][c]; thread (ri, rq) sums
+  // kRows channels, the kParts lanes of row ri add their sums, and lane part
+  // rq stores heads rq, rq + kParts, ...
+  static_assert(kParts == 2 || kParts == 4, "the parts of a row sit in lane bit 5, or bits 4..5");
+  if (rot_lane) {
     float o[kNH];
 #pragma unroll
     for (int jh = 0; jh < kNH; ++jh) o[jh] = 0.0f;
 #pragma unroll
-    for (int u = 0; u < kRows / 4; ++u)
+    for (int u = 0; u < kChunks; ++u) {
+      const int c0 = kRows * rq + 4 * ((u + kChunkRot * rq) % kChunks);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
+      for (int jh = 0; jh < kNH; ++jh) {
+        const float4v qv = *reinterpret_cast<const float4v*>(&s_q[jh][c0]);
 #pragma unroll
-        for (int jh = 0; jh < kNH; ++jh) o[jh] = fmaf(s_q[jh][kRows * oq + 4 * u + e], rr[u][e], o[jh]);
+        for (int e = 0; e < 4; ++e) o[jh] = fmaf(qv[e], rr[u][e], o[jh]);
+      }
+    }
 #pragma unroll
-    for (int jh = 0; jh < kNH; ++jh) s_post[(oq * kNH + jh) * kHeadDim + oi] = o[jh];
-  }
-  __syncthreads();
-  for (int idx = tid; idx < g * kHeadDim; idx += kThreads) {
-    const int jh = idx / kHeadDim;
-    const int i = idx % kHeadDim;
-    float o = 0.0f;
+    for (int jh = 0; jh < kNH; ++jh) {
+      float x, y;
+      if (kParts == 4) {
+        o[jh] = rows_sum(o[jh]);
+      } else {
+        swap32(o[jh], x, y);
+        o[jh] = x + y;
+      }
+    }
 #pragma unroll
-    for (int u = 0; u < kParts; ++u) o += s_post[(u * kNH + jh) * kHeadDim + i];
-    store_out(jh, i, o);
+    for (int jh = 0; jh < kNH; ++jh)
+      if (jh % kParts == rq && jh < g) store_out(jh, ri, o[jh]);
   }
   }  // dense R
   if (tid == 0) __hip_atomic_store(p.counters + b * H + h, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

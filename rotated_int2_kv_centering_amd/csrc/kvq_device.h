@@ -90,5 +90,31 @@ __device__ __forceinline__ float rows_sum(float x) {
   swap32(x, u, v);
   return u + v;
 }
+// Max / sum over the whole wave, returned to every lane: within each 16-lane
+// row by DPP (quad pairs, then row rotations by 4 and 8), then over the rows.
+__device__ __forceinline__ float wave_max_all(float x) {
+  x = fmaxf(x, dpp_f32<QuadXor1::ctrl>(x));
+  x = fmaxf(x, dpp_f32<QuadXor2::ctrl>(x));
+  x = fmaxf(x, dpp_f32<kDppRowRor4>(x));
+  x = fmaxf(x, dpp_f32<kDppRowRor8>(x));
+  return rows_max(x);
+}
+__device__ __forceinline__ int wave_sum_int(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, QuadXor1::ctrl, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, QuadXor2::ctrl, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowRor4, 0xf, 0xf, false);
+  x += __builtin_amdgcn_update_dpp(0, x, kDppRowRor8, 0xf, 0xf, false);
+  auto r = __builtin_amdgcn_permlane16_swap(static_cast<uint32_t>(x), static_cast<uint32_t>(x), false, false);
+  x = static_cast<int>(r[0] + r[1]);
+  r = __builtin_amdgcn_permlane32_swap(static_cast<uint32_t>(x), static_cast<uint32_t>(x), false, false);
+  return static_cast<int>(r[0] + r[1]);
+}
+__device__ __forceinline__ float wave_sum_all(float x) {
+  x += dpp_f32<QuadXor1::ctrl>(x);
+  x += dpp_f32<QuadXor2::ctrl>(x);
+  x += dpp_f32<kDppRowRor4>(x);
+  x += dpp_f32<kDppRowRor8>(x);
+  return rows_sum(x);
+}
 
 }  // namespace kvq
