@@ -99,6 +99,19 @@ __device__ __forceinline__ float wave_max_all(float x) {
   x = fmaxf(x, dpp_f32<kDppRowRor8>(x));
   return rows_max(x);
 }
+// Max / sum over each 16-lane row (lane bits 0..3), returned to every lane of the row.
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f32<QuadXor1::ctrl>(x));
+  x = fmaxf(x, dpp_f32<QuadXor2::ctrl>(x));
+  x = fmaxf(x, dpp_f32<kDppRowRor4>(x));
+  return fmaxf(x, dpp_f32<kDppRowRor8>(x));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f32<QuadXor1::ctrl>(x);
+  x += dpp_f32<QuadXor2::ctrl>(x);
+  x += dpp_f32<kDppRowRor4>(x);
+  return x + dpp_f32<kDppRowRor8>(x);
+}
 __device__ __forceinline__ int wave_sum_int(int x) {
   x += __builtin_amdgcn_update_dpp(0, x, QuadXor1::ctrl, 0xf, 0xf, false);
   x += __builtin_amdgcn_update_dpp(0, x, QuadXor2::ctrl, 0xf, 0xf, false);

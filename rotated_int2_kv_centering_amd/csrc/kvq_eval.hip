@@ -172,7 +172,9 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
     for (int e = 0; e < 2; ++e) accA[jj][e] = accB[jj][e] = accC[jj][e] = 0.0f;
   float e_acc = 0.0f;
 
+  // page id of page pg of the split (-1: past the split, or not in the pool)
   auto page_of = [&](int pg) -> int {
+    if (pg >= p_end) return -1;
     const int id = p.page_table[static_cast<size_t>(b) * p.max_pages + pg];
     return (id >= 0 && id < p.num_pages) ? id : -1;
   };
@@ -237,21 +239,30 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
     }
   };
 
-  // pages of this wave, skipping absent ones; the next present page is loaded ahead
-  auto next_present = [&](int pg) {
-    while (pg < p_end && page_of(pg) < 0) pg += kEvWaves;
-    return pg;
-  };
-  int pg = next_present(p_first + wave);
+  // Pages pg = p_first + wave, + kEvWaves, ...: the page's data is loaded one
+  // page ahead and its id two pages ahead, so neither latency is waited on
+  // in line; an absent page is skipped after its (masked) turn.
+  int pg = p_first + wave;
+  int id_cur = page_of(pg);
   PageRegs<kF32> cur;
-  if (pg < p_end) load_page(pg, page_of(pg), cur);
-  while (pg < p_end) {
+  if (id_cur >= 0) load_page(pg, id_cur, cur);
+  int id_nxt = page_of(pg + kEvWaves);
+  for (; pg < p_end; pg += kEvWaves) {
     const int nt = min(kPage, T - kPage * pg);
-    const int pg_next = next_present(pg + kEvWaves);
-    stage_page(cur);
-    e_acc += cur.err;
+    const int id_2 = page_of(pg + 2 * kEvWaves);
+    const bool here = id_cur >= 0;
+    if (here) {
+      stage_page(cur);
+      e_acc += cur.err;
+    }
     PageRegs<kF32> nxt;
-    if (pg_next < p_end) load_page(pg_next, page_of(pg_next), nxt);
+    if (id_nxt >= 0) load_page(pg + kEvWaves, id_nxt, nxt);
+    id_cur = id_nxt;
+    id_nxt = id_2;
+    if (!here) {
+      cur = nxt;
+      continue;
+    }
     wave_sync();
 
     // ---- logits: lane (token t_l, head quad jq) forms a and a~ of heads jq + 4 u
@@ -336,32 +347,21 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
     for (int u = 0; u < kHQ; ++u) {
       const int jj = jq + 4 * u;
-      float ma = ea[u], mq = eq[u];
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) {
-        ma = fmaxf(ma, __shfl_xor(ma, o));
-        mq = fmaxf(mq, __shfl_xor(mq, o));
-      }
+      const float ma = row16_max(ea[u]), mq = row16_max(eq[u]);
       const float na = fmaxf(m_a[u], ma), nq = fmaxf(m_q[u], mq);
       const float ala = __builtin_amdgcn_exp2f(m_a[u] - na), alq = __builtin_amdgcn_exp2f(m_q[u] - nq);
       const float pa = __builtin_amdgcn_exp2f(ea[u] - na), pq = __builtin_amdgcn_exp2f(eq[u] - nq);
-      float sa = pa, sq = pq;
-#pragma unroll
-      for (int o = 8; o >= 1; o >>= 1) {
-        sa += __shfl_xor(sa, o);
-        sq += __shfl_xor(sq, o);
-      }
+      const float sa = row16_sum(pa), sq = row16_sum(pq);
       l_a[u] = fmaf(l_a[u], ala, sa);
       l_q[u] = fmaf(l_q[u], alq, sq);
       m_a[u] = na;
       m_q[u] = nq;
-      if (jj < g) {
-        s_p[jj * kPage + t_l] = pa;
-        s_p[(kNH + jj) * kPage + t_l] = pq;
-        if (t_l == 0) {
-          s_al[jj] = ala;
-          s_al[kNH + jj] = alq;
-        }
+      // heads past g weigh nothing (their sums are never stored)
+      s_p[jj * kPage + t_l] = jj < g ? pa : 0.0f;
+      s_p[(kNH + jj) * kPage + t_l] = jj < g ? pq : 0.0f;
+      if (t_l == 0) {
+        s_al[jj] = jj < g ? ala : 1.0f;
+        s_al[kNH + jj] = jj < g ? alq : 1.0f;
       }
     }
     wave_sync();
@@ -371,20 +371,19 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
       const int c0 = 2 * lane;
 #pragma unroll
       for (int jj = 0; jj < kNH; ++jj) {
-        if (jj < g) {
-          const float ala = s_al[jj], alq = s_al[kNH + jj];
+        const float ala = s_al[jj], alq = s_al[kNH + jj];
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            accA[jj][e] *= ala;
-            accB[jj][e] *= alq;
-            accC[jj][e] *= alq;
-          }
+        for (int e = 0; e < 2; ++e) {
+          accA[jj][e] *= ala;
+          accB[jj][e] *= alq;
+          accC[jj][e] *= alq;
         }
       }
       // V code of slot t, channel c: record 16 (t / 4) + c % 16, word V[(t % 4) / 2], bit 2 (c / 16) + 16 (t % 2);
       // V (scale, zero) of (channel c, slot t): record 4 (c / G) + t / 4, at +16 + 4 (t % 4)
+      // (a full page runs four tokens per step, so their LDS reads are issued ahead of their uses)
       const int tile = c0 >> 4, b0 = c0 & 15, grp = (c0 >> 5) >> msh;
-      for (int t = 0; t < nt; ++t) {
+      auto token = [&](int t) {
         const int wsel = 2 + ((t & 3) >> 1);
         const int sh = 2 * tile + 16 * (t & 1);
         const uint32_t w0 = s_blk[4 * (16 * (t >> 2) + b0) + wsel];
@@ -408,20 +407,23 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
         const float v0 = s_v[t * kRowPad + c0], v1 = s_v[t * kRowPad + c0 + 1];
 #pragma unroll
         for (int jj = 0; jj < kNH; ++jj) {
-          if (jj < g) {
-            const float pa = s_p[jj * kPage + t], pq = s_p[(kNH + jj) * kPage + t];
-            accA[jj][0] = fmaf(pa, v0, accA[jj][0]);
-            accA[jj][1] = fmaf(pa, v1, accA[jj][1]);
-            accB[jj][0] = fmaf(pq, v0, accB[jj][0]);
-            accB[jj][1] = fmaf(pq, v1, accB[jj][1]);
-            accC[jj][0] = fmaf(pq, wh0, accC[jj][0]);
-            accC[jj][1] = fmaf(pq, wh1, accC[jj][1]);
-          }
+          const float pa = s_p[jj * kPage + t], pq = s_p[(kNH + jj) * kPage + t];
+          accA[jj][0] = fmaf(pa, v0, accA[jj][0]);
+          accA[jj][1] = fmaf(pa, v1, accA[jj][1]);
+          accB[jj][0] = fmaf(pq, v0, accB[jj][0]);
+          accB[jj][1] = fmaf(pq, v1, accB[jj][1]);
+          accC[jj][0] = fmaf(pq, wh0, accC[jj][0]);
+          accC[jj][1] = fmaf(pq, wh1, accC[jj][1]);
         }
+      };
+      if (nt == kPage) {
+#pragma unroll 4
+        for (int t = 0; t < kPage; ++t) token(t);
+      } else {
+        for (int t = 0; t < nt; ++t) token(t);
       }
     }
     wave_sync();  // staging free for the next page
-    pg = pg_next;
     cur = nxt;
   }
 
