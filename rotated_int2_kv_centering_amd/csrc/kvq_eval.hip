@@ -66,12 +66,19 @@ template <bool kF32>
 struct PageRegs {
   static constexpr int kRowWords = kF32 ? 8 : 4;  // uint4 per lane for 16 rows of k (or v)
   uint4v k[kRowWords], v[kRowWords], blk[3];  // the block as 16-byte chunks lane, 64 + lane, 128 + lane
-  float err;  // this lane's token's squared error (lanes 0..15)
+  float4v err;  // this lane's token's squared errors, K and V (lanes 0..15)
 };
 
-template <int kNH, bool kF32, int kPlanes>  // kPlanes: high-bit planes per block (3- or 4-bit keys, values)
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+
+// kPlanes: high-bit planes per block (3- or 4-bit keys, values); kMfma: the matrix-core page loop (bf16 k and
+// v, 2-bit codes), else the vector-ALU one
+template <int kNH, bool kF32, int kPlanes, bool kMfma>
 __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2))) void eval_attn_kernel(
     const EvalParams p) {
+  static_assert(!kMfma || (!kF32 && kPlanes == 0), "the MFMA page loop reads bf16 rows and 2-bit codes");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -114,7 +121,8 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   const int vpw = v_hi_plane(p.kbits, p.gsize) / 4;  // word index of the values' plane
   constexpr int kMergeW = kEvWaves * kNH * (3 * kHeadDim + 4) + kEvWaves;
   constexpr int kBuf = kEvWaves * kStage > kMergeW ? kEvWaves * kStage : kMergeW;
-  __shared__ float s_buf[kBuf];
+  __shared__ __align__(16) float s_buf[kBuf];
+  __shared__ float s_fq[kNH];  // MFMA path: the INT2 query scale f per head
   __shared__ int s_ticket;
 
   // ---- queries, scaled by c, and their rotation q R_K
@@ -144,6 +152,15 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   }
   __syncthreads();
 
+  const int p_first = split * p.pages_per_split;
+  const int p_end = min(p_first + p.pages_per_split, n_pages);
+  const int64_t row0 = p.row0[b];
+  // the waves' rows for the merge: [wave][head][A | B | C (128 each) | m_a l_a m_q l_q], then [wave] errors
+  constexpr int kWRow = 3 * kHeadDim + 4;
+  float* const s_mw = s_buf;
+  float* const s_merr = s_buf + kEvWaves * kNH * kWRow;
+
+  if constexpr (!kMfma) {
   // ---- this wave's pages: first + wave, + kEvWaves, ...
   float* const st = s_buf + wave * kStage;
   float* const s_k = st;                                   // [16][kRowPad]
@@ -152,9 +169,6 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   float* const s_p = st + 2 * kPage * kRowPad + kBlkWords;  // [2][kNH][16]
   float* const s_al = s_p + 2 * kNH * kPage;                      // [2][kNH]
 
-  const int p_first = split * p.pages_per_split;
-  const int p_end = min(p_first + p.pages_per_split, n_pages);
-  const int64_t row0 = p.row0[b];
   constexpr int kHQ = kNH / 4;  // heads per lane in the logit phase: j = jq + 4 u
   const int t_l = lane & 15, jq = lane >> 4;
   float m_a[kHQ], l_a[kHQ], m_q[kHQ], l_q[kHQ];
@@ -172,12 +186,12 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
     for (int e = 0; e < 2; ++e) accA[jj][e] = accB[jj][e] = accC[jj][e] = 0.0f;
   float e_acc = 0.0f;
 
-  // page id of page pg of the split (-1: past the split, or not in the pool)
+  // the table entry of page pg of the split (-1 past the split), loaded ahead and checked at use
+  // (a check in the loading block would wait for the load there)
   auto page_of = [&](int pg) -> int {
-    if (pg >= p_end) return -1;
-    const int id = p.page_table[static_cast<size_t>(b) * p.max_pages + pg];
-    return (id >= 0 && id < p.num_pages) ? id : -1;
+    return pg < p_end ? p.page_table[static_cast<size_t>(b) * p.max_pages + pg] : -1;
   };
+  auto present = [&](int id) { return id >= 0 && id < p.num_pages; };
   auto load_page = [&](int pg, int id, PageRegs<kF32>& r) {
     const int nt = min(kPage, T - kPage * pg);
     const uint8_t* blk = p.pool + (static_cast<size_t>(id) * H + h) * nb;
@@ -204,12 +218,10 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
         r.v[u] = uint4v{0u, 0u, 0u, 0u};
       }
     }
-    r.err = 0.0f;
-    if (p.sq_err != nullptr && lane < nt) {
-      const float4v e4 =
-          *reinterpret_cast<const float4v*>(p.sq_err + (static_cast<size_t>(row0 + kPage * pg + lane) * H + h) * 4);
-      r.err = (e4[0] + e4[1]) + (e4[2] + e4[3]);
-    }
+    // this lane's token's squared errors (lanes 0..15), summed when the page is consumed
+    r.err = p.sq_err != nullptr && lane < nt
+                ? *reinterpret_cast<const float4v*>(p.sq_err + (static_cast<size_t>(row0 + kPage * pg + lane) * H + h) * 4)
+                : float4v{0.0f, 0.0f, 0.0f, 0.0f};
   };
   auto stage_page = [&](const PageRegs<kF32>& r) {
 #pragma unroll
@@ -245,18 +257,18 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   int pg = p_first + wave;
   int id_cur = page_of(pg);
   PageRegs<kF32> cur;
-  if (id_cur >= 0) load_page(pg, id_cur, cur);
+  if (present(id_cur)) load_page(pg, id_cur, cur);
   int id_nxt = page_of(pg + kEvWaves);
   for (; pg < p_end; pg += kEvWaves) {
     const int nt = min(kPage, T - kPage * pg);
-    const int id_2 = page_of(pg + 2 * kEvWaves);
-    const bool here = id_cur >= 0;
+    const bool here = present(id_cur);
     if (here) {
       stage_page(cur);
-      e_acc += cur.err;
+      e_acc += (cur.err[0] + cur.err[1]) + (cur.err[2] + cur.err[3]);
     }
     PageRegs<kF32> nxt;
-    if (id_nxt >= 0) load_page(pg + kEvWaves, id_nxt, nxt);
+    if (present(id_nxt)) load_page(pg + kEvWaves, id_nxt, nxt);
+    const int id_2 = page_of(pg + 2 * kEvWaves);  // issued last: no wait below covers it
     id_cur = id_nxt;
     id_nxt = id_2;
     if (!here) {
@@ -427,11 +439,8 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
     cur = nxt;
   }
 
-  // ---- merge the waves: [wave][head][A | B | C (128 each) | m_a l_a m_q l_q], then [wave] errors
+  // ---- this wave's rows of s_mw
   __syncthreads();
-  constexpr int kWRow = 3 * kHeadDim + 4;
-  float* const s_mw = s_buf;
-  float* const s_merr = s_buf + kEvWaves * kNH * kWRow;
 #pragma unroll
   for (int jj = 0; jj < kNH; ++jj) {
     if (jj < g) {
@@ -457,6 +466,398 @@ __global__ __launch_bounds__(kEvThreads) __attribute__((amdgpu_waves_per_eu(2)))
   }
   const float e_w = wave_sum(lane < kPage ? e_acc : 0.0f);
   if (lane == 0) s_merr[wave] = e_w;
+  } else {
+    // ---- MFMA path (bf16 k and v, 2-bit codes): lane (a = lane / 16, col = lane % 16).
+    // Every product below is a 16 x 16 tile whose output lane (a, col) holds rows 4a + i:
+    //   exact logits   C[token][head]   = k rows (A, token = col of the A operand) x q in three bf16
+    //                                     parts (B, column = head)                 (16x16x32 bf16)
+    //   INT2 logits    C[token][4grp+j] = key codes as fp16 subnormals x the block-diagonal fp16
+    //                                     hi/lo of q_hat f, as in the decode kernel (16x16x32 f16)
+    //   A, B readouts  C[head][ch]      = p (A: row = head, k = tokens 4a..4a+3 the lane holds)
+    //                                     in two bf16 parts x v (B, tokens x 16 channels)    (16x16x16 bf16)
+    //   C readout      C[4grp+j][ch]    = p~ s_v 2^-e in two fp16 parts x value codes    (16x16x16 f16)
+    // so the weights formed in the logit layout feed the readouts with no transposition.
+    constexpr int kNQ = kNH / 4;
+    constexpr int kQpRow = kHeadDim + 8;   // bf16 per (part, head) row of the q parts (conflict-light B reads)
+    constexpr int kVbRow = kHeadDim + 8;   // bf16 per staged v row
+    constexpr int kQpFloats = 3 * 16 * kQpRow / 2;
+    constexpr int kVbFloats = kPage * kVbRow / 2;
+    constexpr int kQbFloats = kNQ * 4 * 2 * 64 * 4;  // INT2 query operands [quad][kk][hi, lo][lane], one copy
+    static_assert(kQpFloats + kEvWaves * kVbFloats + kQbFloats <= kBuf, "MFMA staging fits the page buffer");
+    uint16_t* const s_qp = reinterpret_cast<uint16_t*>(s_buf);                                    // [3][16][kQpRow]
+    uint16_t* const s_vb = reinterpret_cast<uint16_t*>(s_buf + kQpFloats + wave * kVbFloats);  // [16][kVbRow]
+    uint4v* const s_qb = reinterpret_cast<uint4v*>(s_buf + kQpFloats + kEvWaves * kVbFloats);
+    const int a = lane >> 4, col = lane & 15, grp = col >> 2, jj = col & 3;
+    // the three bf16 parts of q c (truncation; columns past g are zero), and the INT2 scale f per head
+    for (int idx = tid; idx < 16 * kHeadDim; idx += kEvThreads) {
+      const int n = idx / kHeadDim, c = idx % kHeadDim;
+      float r = n < g ? s_q[n][c] : 0.0f;
+#pragma unroll
+      for (int sp = 0; sp < 3; ++sp) {
+        const uint32_t t = __float_as_uint(r) & 0xffff0000u;
+        s_qp[(sp * 16 + n) * kQpRow + c] = static_cast<uint16_t>(t >> 16);
+        r -= __uint_as_float(t);
+      }
+    }
+    for (int jh = wave; jh < kNH; jh += kEvWaves) {
+      const float am = wave_max_all(fmaxf(fabsf(s_qh[jh][lane]), fabsf(s_qh[jh][lane + 64])));
+      if (lane == 0) {
+        int e = 0;
+        frexpf(am, &e);  // am in [2^(e-1), 2^e)
+        s_fq[jh] = am > 0.0f ? ldexpf(1.0f, 14 - e) : 1.0f;
+      }
+    }
+    __syncthreads();
+    // INT2 query operands of quad Q, column 4 grp + jj: head 4 Q + jj on group grp's 32 channels, element
+    // e divided by 4^(e/2) (the factor its key code carries), as fp16 hi + lo of q_hat c f; the lane's
+    // operands (the same in every wave) are kept in LDS by wave 0 and read back per page, so they hold
+    // no registers across the loop
+    float qz[kNQ], c1[kNQ];
+#pragma unroll
+    for (int Q = 0; Q < kNQ; ++Q) {
+      const int jl = 4 * Q + jj;
+      const float f = s_fq[jl];
+      half8 hi, lo;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float sc = s_qh[jl][32 * grp + 8 * a + e] * f * (1.0f / static_cast<float>(1 << (2 * (e >> 1))));
+        const _Float16 hh = static_cast<_Float16>(sc);
+        hi[e] = hh;
+        lo[e] = static_cast<_Float16>(sc - static_cast<float>(hh));
+      }
+      c1[Q] = 16777216.0f / f;  // the code's 2^-24 and f undone
+      qz[Q] = s_qs[jl][grp] / c1[Q];
+      const half8 zero = {};
+      if (wave == 0) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          s_qb[((Q * 4 + kk) * 2 + 0) * 64 + lane] = __builtin_bit_cast(uint4v, grp == kk ? hi : zero);
+          s_qb[((Q * 4 + kk) * 2 + 1) * 64 + lane] = __builtin_bit_cast(uint4v, grp == kk ? lo : zero);
+        }
+      }
+    }
+    __syncthreads();
+
+    // state: exact softmax per head col, INT2 per (quad, head jj); accumulators in the output layouts
+    float m_a = -INFINITY, l_a = 0.0f;
+    float m_q[kNQ], l_q[kNQ], z_run[kNQ];
+    float4v accA[8], accB[8], accC[kNQ][8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) accA[t] = accB[t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int Q = 0; Q < kNQ; ++Q) {
+      m_q[Q] = -INFINITY;
+      l_q[Q] = 0.0f;
+      z_run[Q] = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) accC[Q][t] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    float e_acc = 0.0f;
+    // lane values broadcast by readlane, picked by the lane's row a
+    auto lane_val = [](float x, int k) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), k)); };
+
+    struct PageM {
+      uint4v k[4], v[4];  // k: the A operand of k-step u (token col, channels 32 u + 8 a ..); v: staged rows
+      uint4v rec, km, vm; // this lane's code record, its K and V metadata records
+      float4v err;        // this lane's token's squared errors (lanes 0..15)
+    };
+    auto page_of = [&](int pg) -> int {
+      return pg < p_end ? p.page_table[static_cast<size_t>(b) * p.max_pages + pg] : -1;
+    };
+    auto present = [&](int id) { return id >= 0 && id < p.num_pages; };
+    auto load_page = [&](int pg, int id, PageM& r) {
+      const int nt = min(kPage, T - kPage * pg);
+      const uint16_t* kb = static_cast<const uint16_t*>(p.k);
+      const uint16_t* vb = static_cast<const uint16_t*>(p.v);
+      const size_t rowk = static_cast<size_t>(row0 + kPage * pg + min(col, nt - 1)) * H + h;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) r.k[u] = *reinterpret_cast<const uint4v*>(kb + rowk * kHeadDim + 32 * u + 8 * a);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int idx = u * 64 + lane, t = idx >> 4, part = idx & 15;
+        r.v[u] = t < nt ? *reinterpret_cast<const uint4v*>(
+                              vb + (static_cast<size_t>(row0 + kPage * pg + t) * H + h) * kHeadDim + 8 * part)
+                        : uint4v{0u, 0u, 0u, 0u};
+      }
+      const uint8_t* blk = p.pool + (static_cast<size_t>(id) * H + h) * nb;
+      r.rec = *reinterpret_cast<const uint4v*>(blk + 16 * lane);
+      const uint8_t* meta = blk + kCodeBytes + kMetaRecordBytes * (4 * (grp >> msh) + a);
+      r.km = *reinterpret_cast<const uint4v*>(meta);
+      r.vm = *reinterpret_cast<const uint4v*>(meta + 16);
+      r.err = p.sq_err != nullptr && lane < nt
+                  ? *reinterpret_cast<const float4v*>(p.sq_err +
+                                                      (static_cast<size_t>(row0 + kPage * pg + lane) * H + h) * 4)
+                  : float4v{0.0f, 0.0f, 0.0f, 0.0f};
+    };
+
+    int pg = p_first + wave;
+    int id_cur = page_of(pg);
+    PageM cur;
+    if (present(id_cur)) load_page(pg, id_cur, cur);
+    int id_nxt = page_of(pg + kEvWaves);
+    for (; pg < p_end; pg += kEvWaves) {
+      const int nt = min(kPage, T - kPage * pg);
+      const bool here = present(id_cur);
+      if (here) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int idx = u * 64 + lane;
+          *reinterpret_cast<uint4v*>(s_vb + (idx >> 4) * kVbRow + 8 * (idx & 15)) = cur.v[u];
+        }
+        e_acc += (cur.err[0] + cur.err[1]) + (cur.err[2] + cur.err[3]);
+      }
+      PageM nxt;
+      if (present(id_nxt)) load_page(pg + kEvWaves, id_nxt, nxt);
+      const int id_2 = page_of(pg + 2 * kEvWaves);  // issued last: no wait below covers it
+      id_cur = id_nxt;
+      id_nxt = id_2;
+      if (!here) {
+        cur = nxt;
+        continue;
+      }
+      const PageM& P = cur;
+
+      // ---- logits, lane (a, col): tokens 4a + i
+      float4v E = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bf16x8 kA = __builtin_bit_cast(bf16x8, P.k[u]);
+#pragma unroll
+        for (int sp = 0; sp < 3; ++sp) {
+          const uint4v qb = *reinterpret_cast<const uint4v*>(s_qp + (sp * 16 + col) * kQpRow + 32 * u + 8 * a);
+          E = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kA, __builtin_bit_cast(bf16x8, qb), E, 0, 0, 0);
+        }
+      }
+      // key operands: a code at bits 2q (+16) of a word is the fp16 subnormal code 4^q 2^-24
+      const uint32_t kw[4] = {P.rec[0], P.rec[0] >> 8, P.rec[1], P.rec[1] >> 8};
+      half8 kA2[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        uint4v rr;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rr[q] = kw[kk] & (0x00030003u << (2 * q));
+        kA2[kk] = __builtin_bit_cast(half8, rr);
+      }
+      bool live[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) live[i] = 4 * a + i < nt;
+      float ea[4], eq[kNQ][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ea[i] = live[i] ? E[i] : -INFINITY;
+#pragma unroll
+      for (int Q = 0; Q < kNQ; ++Q) {
+        float4v C = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const half8 qh = __builtin_bit_cast(half8, s_qb[((Q * 4 + kk) * 2 + 0) * 64 + lane]);
+          const half8 ql = __builtin_bit_cast(half8, s_qb[((Q * 4 + kk) * 2 + 1) * 64 + lane]);
+          C = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA2[kk], qh, C, 0, 0, 0);
+          C = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA2[kk], ql, C, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // s_grp <codes, q_hat> + z_grp sum(q_hat), summed over the four groups of the row
+          const float s = fmaf(C[i], f16_lo(P.km[i]), f16_hi(P.km[i]) * qz[Q]);
+          const float lg = row_sum_stride4(s) * c1[Q];
+          eq[Q][i] = live[i] ? lg : -INFINITY;
+        }
+      }
+
+      // ---- online softmax: exact per head col; INT2 per head jj of each quad (the group lanes agree)
+      const float pm = rows_max(fmaxf(fmaxf(ea[0], ea[1]), fmaxf(ea[2], ea[3])));
+      const float na = fmaxf(m_a, pm);
+      const float ala = __builtin_amdgcn_exp2f(m_a - na);
+      float pa[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pa[i] = col < g ? __builtin_amdgcn_exp2f(ea[i] - na) : 0.0f;
+      l_a = fmaf(l_a, ala, rows_sum((pa[0] + pa[1]) + (pa[2] + pa[3])));
+      m_a = na;
+      float pq[kNQ][4], alq[kNQ];
+#pragma unroll
+      for (int Q = 0; Q < kNQ; ++Q) {
+        const float qm = rows_max(fmaxf(fmaxf(eq[Q][0], eq[Q][1]), fmaxf(eq[Q][2], eq[Q][3])));
+        const float nq = fmaxf(m_q[Q], qm);
+        alq[Q] = __builtin_amdgcn_exp2f(m_q[Q] - nq);
+        const bool hq = 4 * Q + jj < g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pq[Q][i] = hq ? __builtin_amdgcn_exp2f(eq[Q][i] - nq) : 0.0f;
+        l_q[Q] = fmaf(l_q[Q], alq[Q], rows_sum((pq[Q][0] + pq[Q][1]) + (pq[Q][2] + pq[Q][3])));
+        m_q[Q] = nq;
+      }
+      // rescale the sums kept against the old maxima (wave-uniform skip when nothing moved)
+      bool moved = ala != 1.0f;
+#pragma unroll
+      for (int Q = 0; Q < kNQ; ++Q) moved = moved || alq[Q] != 1.0f;
+      if (__ballot(moved) != 0) {
+        // accA / accB rows 4a + i are heads 4a + i: their factors come from lane 4a + i (row 0)
+        float fa[4], fb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float xa = 1.0f, xb = 1.0f;
+#pragma unroll
+          for (int Q = 0; Q < kNQ; ++Q) {
+            const float va = lane_val(ala, 4 * Q + i), vb = lane_val(alq[Q], i);
+            xa = a == Q ? va : xa;
+            xb = a == Q ? vb : xb;
+          }
+          fa[i] = xa;
+          fb[i] = xb;
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            accA[t][i] *= fa[i];
+            accB[t][i] *= fb[i];
+          }
+#pragma unroll
+        for (int Q = 0; Q < kNQ; ++Q) {
+          // accC[Q] rows 4 grp + i are head 4 Q + i: the factor of lane i
+          float fc[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) fc[i] = lane_val(alq[Q], i);
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) accC[Q][t][i] *= fc[i];
+          z_run[Q] *= alq[Q];
+        }
+      }
+
+      // ---- readouts A = sum p v, B = sum p~ v (rows = heads), C = sum p~ w_hat (rows 4 grp + j per quad)
+      wave_sync();  // the staged v rows are visible to the whole wave
+      // x = hi + lo + r by truncation, |r| < 2^-16 |x| (the weights are finite and nonnegative)
+      auto split_bf16 = [](const float (&x)[4], short4v& hi, short4v& lo) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t t = __float_as_uint(x[i]) & 0xffff0000u;
+          hi[i] = static_cast<short>(t >> 16);
+          lo[i] = static_cast<short>(__float_as_uint(x[i] - __uint_as_float(t)) >> 16);
+        }
+      };
+      short4v pa_hi, pa_lo, pb_hi, pb_lo;
+      split_bf16(pa, pa_hi, pa_lo);
+      float pbv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = 0.0f;  // row col of the B readout: head col = 4 Q + jj, this lane's jj
+#pragma unroll
+        for (int Q = 0; Q < kNQ; ++Q) x = (col >> 2) == Q ? pq[Q][i] : x;
+        pbv[i] = x;
+      }
+      split_bf16(pbv, pb_hi, pb_lo);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        short4v vB;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vB[i] = static_cast<short>(s_vb[(4 * a + i) * kVbRow + 16 * t + col]);
+        accA[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_hi, vB, accA[t], 0, 0, 0);
+        accA[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa_lo, vB, accA[t], 0, 0, 0);
+        accB[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb_hi, vB, accB[t], 0, 0, 0);
+        accB[t] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pb_lo, vB, accB[t], 0, 0, 0);
+      }
+      // value scales and zeros of the lane's tokens (masked slots: 0, whatever bits they hold);
+      // the page's unit 2^e per group brings its largest scale into [1/2, 1)
+      float sv[4], zv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[i] = live[i] ? f16_lo(P.vm[i]) : 0.0f;
+        zv[i] = live[i] ? f16_hi(P.vm[i]) : 0.0f;
+      }
+      const float smax = rows_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+      int ex = 0;
+      frexpf(smax, &ex);  // smax in [2^(ex-1), 2^ex)
+      if (!(smax > 0.0f)) ex = 0;
+      const float unit_in = ldexpf(1.0f, -ex);
+      // the output rows 4 a + i belong to group a: its unit comes from lane 4 a (group a's lanes agree)
+      float eo = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float v = lane_val(static_cast<float>(ex), 4 * k);
+        eo = a == k ? v : eo;
+      }
+      const float unit_out = ldexpf(16777216.0f, static_cast<int>(eo));  // the codes' 2^-24 and the unit undone
+      // value code operands of tile t: record 16 a + col, words V0 (tokens 4a, 4a + 1) and V1 (4a + 2, 4a + 3),
+      // bits 2 (t % 4) (+16), tiles 4..7 in the upper byte: codes times 4^(t % 4)
+      const uint32_t vw[4] = {P.rec[2], P.rec[3], P.rec[2] >> 8, P.rec[3] >> 8};
+#pragma unroll
+      for (int Q = 0; Q < kNQ; ++Q) {
+        float x[4];
+        half4 xh, xl;
+        float zq = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = pq[Q][i] * sv[i] * unit_in;
+          xh[i] = static_cast<_Float16>(x[i]);
+          xl[i] = static_cast<_Float16>(x[i] - static_cast<float>(xh[i]));
+          zq = fmaf(pq[Q][i], zv[i], zq);
+        }
+        z_run[Q] += rows_sum(zq);  // lane (., grp, jj): sum of p~ z_v over the page for (head 4Q + jj, grp)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          const uint32_t m = 0x00030003u << (2 * (t & 3));
+          uint32_t w2[2] = {vw[2 * (t >> 2)] & m, vw[2 * (t >> 2) + 1] & m};
+          const half4 cB = __builtin_bit_cast(half4, w2);
+          float4v pc = {0.0f, 0.0f, 0.0f, 0.0f};
+          pc = __builtin_amdgcn_mfma_f32_16x16x16f16(xh, cB, pc, 0, 0, 0);
+          pc = __builtin_amdgcn_mfma_f32_16x16x16f16(xl, cB, pc, 0, 0, 0);
+          const float fct = unit_out * (1.0f / static_cast<float>(1 << (2 * (t & 3))));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) accC[Q][t][i] = fmaf(pc[i], fct, accC[Q][t][i]);
+        }
+      }
+      wave_sync();  // staging free for the next page
+      cur = nxt;
+    }
+
+    // ---- this wave's rows of s_mw
+    __syncthreads();  // every wave is done with its staging (s_mw overlays it)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hd = 4 * a + i;  // accA / accB row
+      if (a < kNQ && hd < g) {
+        float* row = s_mw + (wave * kNH + hd) * kWRow;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          row[16 * t + col] = accA[t][i];
+          row[kHeadDim + 16 * t + col] = accB[t][i];
+        }
+      }
+    }
+#pragma unroll
+    for (int Q = 0; Q < kNQ; ++Q) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // zero part of head 4 Q + i, group a: lane 4 a + i
+        float zi = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float v = lane_val(z_run[Q], 4 * k + i);
+          zi = a == k ? v : zi;
+        }
+        const int hd = 4 * Q + i;
+        if (hd < g) {
+          float* row = s_mw + (wave * kNH + hd) * kWRow + 2 * kHeadDim;
+#pragma unroll
+          for (int t = 0; t < 8; ++t)
+            if ((t >> 1) == a) row[16 * t + col] = accC[Q][t][i] + zi;
+        }
+      }
+      if (lane < 4 && 4 * Q + lane < g) {
+        float* row = s_mw + (wave * kNH + 4 * Q + lane) * kWRow + 3 * kHeadDim;
+        row[2] = m_q[Q];
+        row[3] = l_q[Q];
+      }
+    }
+    if (lane < g) {
+      float* row = s_mw + (wave * kNH + lane) * kWRow + 3 * kHeadDim;
+      row[0] = m_a;
+      row[1] = l_a;
+    }
+    const float e_w = wave_sum(lane < kPage ? e_acc : 0.0f);
+    if (lane == 0) s_merr[wave] = e_w;
+  }
+
   __syncthreads();
 
   float* const part_base = p.part + slot * p.n_splits * kEvHeads * kEvPartStride;
@@ -649,9 +1050,11 @@ template <int kNH, int kPlanes>
 hipError_t launch_attn(const EvalParams& p, hipStream_t stream) {
   const dim3 grid(p.num_kv_heads * p.n_splits, p.batch, (p.g + kEvHeads - 1) / kEvHeads);
   if (p.kv_kind == 1)
-    hipLaunchKernelGGL((eval_attn_kernel<kNH, true, kPlanes>), grid, dim3(kEvThreads), 0, stream, p);
+    hipLaunchKernelGGL((eval_attn_kernel<kNH, true, kPlanes, false>), grid, dim3(kEvThreads), 0, stream, p);
+  else if constexpr (kPlanes == 0)
+    hipLaunchKernelGGL((eval_attn_kernel<kNH, false, 0, true>), grid, dim3(kEvThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((eval_attn_kernel<kNH, false, kPlanes>), grid, dim3(kEvThreads), 0, stream, p);
+    hipLaunchKernelGGL((eval_attn_kernel<kNH, false, kPlanes, false>), grid, dim3(kEvThreads), 0, stream, p);
   return hipGetLastError();
 }
 
