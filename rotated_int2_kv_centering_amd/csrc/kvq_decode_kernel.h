@@ -126,12 +126,17 @@ __device__ __forceinline__ int block_sum(int v, int lane, int wave, int* s_red) 
 // Exclusive prefix sum of v in thread order; `total` receives the sum.
 template <int kW>
 __device__ __forceinline__ int block_excl_scan(int v, int lane, int wave, int* s_red, int& total) {
+  // inclusive scan inside each 16-lane row (DPP row shifts; lanes shifted in from outside the row add 0),
+  // then the totals of the rows before the lane's, read from lanes 15, 31, 47
   int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15), r1 = __builtin_amdgcn_readlane(x, 31),
+            r2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = lane >> 4;
+  x += (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
   if (lane == 63) s_red[wave] = x;
   __syncthreads();
   int before = 0, t = 0;
