@@ -112,6 +112,7 @@ def kernel_source_sha() -> str:
         "kvq_decode_g8.hip",
         "kvq_decode_g16.hip",
         "kvq_device.h",
+        "kvq_layout.h",
         "kvq_quant.h",
         "kvq_internal.h",
     ):
