@@ -145,11 +145,14 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(
 //      packs the codes straight into the block's words: a slot's K words are
 //      whole in one lane; its V half-words take one exchange across the lane
 //      halves, and the two slots of a V word one between neighbouring lanes;
-//   4. plain stores: the wave writes the K and the V words of its tile's
-//      records within microseconds of each other, so the lines of a block are
-//      whole in L2 before they leave.  A V word whose other slot is not the
-//      neighbouring token of the same tile is written as this slot's 16-bit
-//      half only.
+//   4. 2-bit codes: the lanes write the tile's two blocks into the wave's LDS
+//      image, which is copied out as whole 16-byte chunks (whole lines) when
+//      the tile fills two pages in order, else slot by slot; 3- and 4-bit
+//      codes are stored slot by slot.  Slot by slot, a V word whose other slot
+//      is not the neighbouring token of the same tile is written as this
+//      slot's 16-bit half only.
+//   Tiles are dealt to the workgroup's waves from an LDS counter, so a wave
+//   that is issued less often takes fewer of them.
 // ---------------------------------------------------------------------------
 constexpr int kBulkThreads = 512;
 constexpr int kBulkWaves = kBulkThreads / 64;
