@@ -218,7 +218,8 @@ kvq_status kvq_quant_append_err(const kvq_cache* cache, const void* k, const voi
 /*
  * kvq_decode_workspace_bytes - device workspace needed by kvq_decode_attn for
  * the same (batch, num_q_heads, num_kv_heads, max_seq_len, num_splits).
- * num_splits 0 selects the automatic split plan.  Returns 0 on invalid input.
+ * num_splits 0 selects the automatic split plan (the size covers either
+ * launch shape the call may take).  Returns 0 on invalid input.
  * The workspace holds per-(sequence, KV head) ticket counters, the split
  * partials and one row per output row for an exact window's part (used when a
  * window is given).  It must be zero-filled before its first use; every completed
@@ -262,9 +263,10 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
  *   num_splits  0 = automatic: the kernel reads the batch's lengths and cuts
  *               every sequence into splits of one common size, the smallest
  *               (found in a few refinement rounds) for which all splits of all
- *               (sequence, KV head) pairs fit in one workgroup per compute
- *               unit, so short sequences take few workgroups and long ones
- *               many.  Otherwise the requested number of splits per
+ *               (sequence, KV head) pairs fit in one round of workgroups (one
+ *               per compute unit; three for a batch of more than one sequence
+ *               with g <= 4, 2-bit codes and no window), so short sequences
+ *               take few workgroups and long ones many.  Otherwise the requested number of splits per
  *               (sequence, KV head), each sized for max_seq_len.  Either way
  *               a split holds at most 2048 pages and a sequence at most 512
  *               splits, so the count used can differ from the request;
@@ -287,7 +289,9 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
  * subnormal operand).  Stale slots past a sequence's end and absent pages may
  * hold any bytes: they weigh nothing.
  * Work decomposition: one kernel launch; one workgroup per compute unit
- * (12 waves for g <= 4, 8 for g <= 8, else 4) streams a split's pages, and
+ * (12 waves for g <= 4, 8 for g <= 8, else 4; for a batch of g <= 4 with
+ * 2-bit codes and no window, three 4-wave workgroups per compute unit, which
+ * cut the sequences into three times as many splits) streams a split's pages, and
  * the last workgroup of each (sequence, KV head) merges the split partials
  * (log-sum-exp), adds the window's part, and applies R_V^T.
  * Limits: max_seq_len <= 16777216 (512 splits x 2048 pages x 16 tokens).

@@ -103,17 +103,21 @@ int device_cu_count() {
   return cache[dev];
 }
 
-// Decode workgroups per compute unit: each workgroup has as many waves as a
-// compute unit holds for its group size (12 for g <= 4, 8 for g <= 8, else 4).
-int workgroups_per_cu(int) { return 1; }
+// Decode workgroups per compute unit: one, with as many waves as a compute unit
+// holds for its group size (12 for g <= 4, 8 for g <= 8, else 4); three 4-wave
+// workgroups in the narrow shape, taken by batches of g <= 4 with 2-bit codes
+// and no window under the balanced plan (finer splits when lengths differ).
+bool narrow_shape(int batch, int g, int kbits, int vbits, bool win) {
+  return batch > 1 && g <= 4 && kbits == 2 && vbits == 2 && !win;
+}
 
 // Splits of one (sequence, KV head) the merging workgroup can stage in LDS
 // next to an exact window (kvq_decode.hip lays the window out in the same
 // LDS; without a window the limit is kMaxSplits).
 int max_splits_with_window(int g) { return g <= 4 ? kMaxSplits : 128; }
 
-bool make_plan(int batch, int num_kv_heads, int g, int max_seq_len, int num_splits, kvq::DecodePlan* plan,
-               int max_splits = kMaxSplits, int extra = 0) {
+bool make_plan(int batch, int num_kv_heads, int max_seq_len, int num_splits, kvq::DecodePlan* plan,
+               int max_splits = kMaxSplits, int extra = 0, bool narrow = false) {
   if (batch < 0 || num_kv_heads < 1 || max_seq_len < 0 || num_splits < 0) return false;
   if (max_seq_len > kMaxContext) return false;
   const int n_pages = (max_seq_len + kPage - 1) / kPage;
@@ -121,8 +125,9 @@ bool make_plan(int batch, int num_kv_heads, int g, int max_seq_len, int num_spli
   plan->n_pages_max = n_pages;
   // no sequence is cut into more than max_splits splits
   const long long pps_floor = (n_pages + max_splits - 1) / max_splits;
-  const long long target = static_cast<long long>(workgroups_per_cu(g)) * device_cu_count();
   plan->balanced = num_splits == 0 && static_cast<long long>(batch) * n1 <= 0x7fffffffLL;
+  plan->narrow = plan->balanced && narrow;
+  const long long target = static_cast<long long>(plan->narrow ? 3 : 1) * device_cu_count();
   if (plan->balanced) {
     // The kernel picks pps in [pps_min, pps_max] from the batch's total pages P:
     // pps >= H P / target, or pps = pps_max.  Sequence b takes max(1, ceil(p_b / pps))
@@ -270,8 +275,9 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
       return fail(KVQ_EINVAL, "window holds %d sequences, the call has %d", window->batch, batch);
   }
   kvq::DecodePlan plan;
-  if (!make_plan(batch, cache->num_kv_heads, g, max_seq_len, num_splits, &plan,
-                 win ? max_splits_with_window(g) : kMaxSplits, static_cast<int>(stepping) + static_cast<int>(win)))
+  if (!make_plan(batch, cache->num_kv_heads, max_seq_len, num_splits, &plan,
+                 win ? max_splits_with_window(g) : kMaxSplits, static_cast<int>(stepping) + static_cast<int>(win),
+                 narrow_shape(batch, g, kbits_of(cache), vbits_of(cache), win)))
     return fail(KVQ_EINVAL, "cannot plan the decode split");
   // the tickets' prefix: the caller workspace's, or a fixed one (static workspace)
   const size_t tickets = ticket_bytes != 0 ? ticket_bytes : counters_bytes(batch, cache->num_kv_heads);
@@ -312,6 +318,7 @@ kvq_status decode_common(const kvq_cache* cache, const void* k_new, const void* 
   a.pps_min = plan.pps_min;
   a.pps_max = plan.pps_max;
   a.target_wgs = plan.target_wgs;
+  a.narrow = plan.narrow ? 1 : 0;
   a.win = win ? static_cast<uint16_t*>(window->buf) : nullptr;
   a.win_sinks = win ? window->sinks : 0;
   a.win_recent = win ? window->recent : 0;
@@ -410,9 +417,15 @@ kvq_status kvq_quant_append_err(const kvq_cache* cache, const void* k, const voi
 size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads, int32_t max_seq_len,
                                   int32_t num_splits) {
   if (batch < 0 || num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0) return 0;
-  kvq::DecodePlan plan;
-  if (!make_plan(batch, num_kv_heads, num_q_heads / num_kv_heads, max_seq_len, num_splits, &plan)) return 0;
-  return workspace_bytes(batch, num_q_heads, num_kv_heads, plan);
+  // the larger of the two shapes' needs (the call's shape depends on the cache and window)
+  kvq::DecodePlan plan, narrow;
+  if (!make_plan(batch, num_kv_heads, max_seq_len, num_splits, &plan)) return 0;
+  size_t bytes = workspace_bytes(batch, num_q_heads, num_kv_heads, plan);
+  if (narrow_shape(batch, num_q_heads / num_kv_heads, 2, 2, false)) {
+    if (!make_plan(batch, num_kv_heads, max_seq_len, num_splits, &narrow, kMaxSplits, 0, true)) return 0;
+    bytes = std::max(bytes, workspace_bytes(batch, num_q_heads, num_kv_heads, narrow));
+  }
+  return bytes;
 }
 
 kvq_status kvq_decode_attn(const kvq_cache* cache, const void* q, kvq_dtype q_dtype, int32_t batch,
@@ -435,8 +448,10 @@ kvq_status kvq_decode_attn_noalloc(const kvq_cache* cache, const void* q, kvq_dt
       num_q_heads % cache->num_kv_heads == 0) {
     kvq::DecodePlan plan;
     const int g = num_q_heads / cache->num_kv_heads;
-    if (make_plan(batch, cache->num_kv_heads, g, max_seq_len, num_splits, &plan,
-                  window_active(window) ? max_splits_with_window(g) : kMaxSplits, window_active(window) ? 1 : 0)) {
+    const bool win = window_active(window);
+    if (make_plan(batch, cache->num_kv_heads, max_seq_len, num_splits, &plan,
+                  win ? max_splits_with_window(g) : kMaxSplits, win ? 1 : 0,
+                  narrow_shape(batch, g, kbits_of(cache), vbits_of(cache), win))) {
       const size_t need = kvq::kStaticTicketBytes + split_rows_bytes(batch, num_q_heads, plan) +
                           sizeof(float) * static_cast<size_t>(batch) * num_q_heads * kRowStride;
       if (need > kvq::kStaticScratchBytes)

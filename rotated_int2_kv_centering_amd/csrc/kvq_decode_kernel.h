@@ -74,6 +74,12 @@ template <bool kKW, bool kVW> struct PairDma { static constexpr int n = 4 + 2 * 
 template <int kNQ, int kParts> struct DecodeShape { static constexpr int waves = 4, depth = kParts == 3 ? 8 : 6; };
 template <int kParts> struct DecodeShape<1, kParts> { static constexpr int waves = kParts <= 4 ? 12 : 8, depth = 3; };
 template <int kParts> struct DecodeShape<2, kParts> { static constexpr int waves = 8, depth = kParts <= 4 ? 4 : 3; };
+// The narrow shape for batches of g <= 4 with 2-bit codes and no window: three
+// 4-wave workgroups per compute unit (the same 3 waves per SIMD and per-wave
+// ring).  Three times the splits per KV head cut each sequence's pages more
+// finely, so the largest split, which sets the kernel's length when lengths
+// differ, sits closer to the mean.
+constexpr int kNarrowWaves = 4, kNarrowDepth = 3, kNarrowWgPerCu = 3;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -231,8 +237,8 @@ __device__ __forceinline__ float ld_agent(const float* p) {
 
 // quads of query heads (g <= 4 * kNQ), waves per workgroup, ring depth, 3- or
 // 4-bit keys, 3- or 4-bit values, Hadamard rotation
-template <int kNQ, int kW, int kDepth, bool kKW, bool kVW, bool kHad>
-__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kW / 4)))
+template <int kNQ, int kW, int kDepth, bool kKW, bool kVW, bool kHad, int kWgPerCu = 1>
+__global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kW / 4 * kWgPerCu)))
 void decode_kernel(const DecodeParams p) {
   constexpr int kDmaPerPair = PairDma<kKW, kVW>::n;
   // ring parts: codes of page 0, of page 1, metadata, then the keys' and the values' high-bit planes
@@ -1020,7 +1026,7 @@ void decode_kernel(const DecodeParams p) {
   //           and 32-row blocks: A = p in two bf16 parts, B = values.
   // Both splits are made once into LDS in operand order.  Rows past n_w read
   // row n_w - 1 (finite) and carry weight 0.
-  constexpr bool kWinOk = true;
+  constexpr bool kWinOk = kWgPerCu == 1;  // the narrow shape's ring cannot stage a window
   constexpr int kWinMax = 8 + 128;                    // window rows
   constexpr int kWinLd = kWinOk ? (kWinMax * 32 + kThreads - 1) / kThreads : 1;  // 16-byte chunks per thread
   constexpr int kWinRowsPad = 32 * ((kWinMax + 31) / 32);  // 32-row blocks of the value product
@@ -1485,6 +1491,15 @@ static hipError_t launch_one(const DecodeParams& prm, hipStream_t stream, hipEve
                             args, 0, stream,
                             ev_begin, ev_end, 0);
 }
+static hipError_t launch_narrow(const DecodeParams& prm, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
+  constexpr int kW = kNarrowWaves, kD = kNarrowDepth, kC = kNarrowWgPerCu;
+  DecodeParams arg = prm;
+  void* args[] = {&arg};
+  const void* kern = prm.rot_kind == 1 ? reinterpret_cast<const void*>(&decode_kernel<1, kW, kD, false, false, true, kC>)
+                                       : reinterpret_cast<const void*>(&decode_kernel<1, kW, kD, false, false, false, kC>);
+  return hipExtLaunchKernel(kern, dim3(prm.num_kv_heads * prm.n_splits), dim3(64 * kW), args, 0, stream, ev_begin,
+                            ev_end, 0);
+}
 
 // The decode kernels of kNQ quads of query heads (g <= 4 kNQ), for every key
 // and value code width and rotation kind; 3- and 4-bit codes of a tensor share
@@ -1493,6 +1508,7 @@ static hipError_t launch_one(const DecodeParams& prm, hipStream_t stream, hipEve
 // kvq_decode_g16.hip), so the three compile in parallel.
 template <int kNQ>
 hipError_t launch_decode_quads(const DecodeParams& prm, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
+  if (kNQ == 1 && prm.narrow) return launch_narrow(prm, stream, ev_begin, ev_end);
   const bool kw = prm.kbits > 2, vw = prm.vbits > 2;
   if (kw)
     return vw ? launch_one<kNQ, true, true>(prm, stream, ev_begin, ev_end)

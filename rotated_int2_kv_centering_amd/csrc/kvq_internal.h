@@ -50,6 +50,7 @@ struct DecodePlan {
                         // balanced: the split size for one sequence of max_seq_len (a guess)
   int n_splits;         // fixed plan: splits per (sequence, KV head); balanced: slots per KV head
   int pps_min, pps_max, target_wgs;  // balanced plan
+  bool narrow;          // the narrow decode shape (three 4-wave workgroups per compute unit)
 };
 
 // Kernel arguments of the fused decode (passed by value).
@@ -80,6 +81,7 @@ struct DecodeParams {
   int pages_per_split;
   int n_splits;
   int pps_min, pps_max, target_wgs;
+  int narrow;  // 1: the narrow shape (three 4-wave workgroups per compute unit; balanced plan, g <= 4)
   // Exact window (win null = none): bf16 [batch'][num_kv_heads][win_sinks +
   // win_recent][2][128]; positions t < win_sinks and t >= T - win_recent are
   // attended from it (logit <q, k - win_mu>), the rest from the pool.  The

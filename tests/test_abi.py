@@ -97,10 +97,11 @@ def test_workspace_bytes_with_explicit_splits(K):
 
 def test_workspace_bytes_automatic_plan(K):
     # Automatic plan, 256 compute units: split slots per KV head
-    # S = min(B * ceil(pages / pps_min), max(ceil(256 / H_kv), ceil(B * pages / 2048)) + B - 1),
+    # S = min(B * ceil(pages / pps_min), max(ceil(W / H_kv), ceil(B * pages / 2048)) + B - 1),
     # pps_min = max(8, ceil(pages / 512)); partial rows = H_q * S; window rows = B * H_q.
+    # W = 256 workgroups, or 768 for a batch of g <= 4 (the narrow shape: three per compute unit).
     assert K.kvq_decode_workspace_bytes(1, 32, 8, 131072, 0) == CTR + 4 * 32 * 32 * 132 + 4 * 32 * 132
-    assert K.kvq_decode_workspace_bytes(16, 32, 8, 65536, 0) == CTR + 4 * 32 * (32 + 15) * 132 + 4 * 16 * 32 * 132
+    assert K.kvq_decode_workspace_bytes(16, 32, 8, 65536, 0) == CTR + 4 * 32 * (96 + 15) * 132 + 4 * 16 * 32 * 132
     # one split per sequence
     assert K.kvq_decode_workspace_bytes(3, 8, 2, 100, 0) == CTR + 4 * 8 * 3 * 132 + 4 * 3 * 8 * 132
     # B = 4, 8192 pages: max(32, ceil(4 * 8192 / 2048) = 16) + 3 = 35 slots
