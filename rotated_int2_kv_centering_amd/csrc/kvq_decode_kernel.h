@@ -44,6 +44,12 @@
 // holds), B = value codes (subnormal bit patterns) of 32 tokens x 16 channels;
 // rows whose group does not own the tile's channels are discarded.  The
 // zero-point part sum_s p_s z_v,s is accumulated in fp32.
+// For g = 5..8 one octet layout replaces the two quads: column (row)
+// n = 8*h + j is head j on the groups h and h + 2.  The logits take two
+// accumulators per page (groups 0-1 and 2-3, half the columns of each
+// product live) summed across the column halves by one DPP rotation, and
+// P.V one A operand per group half (tiles 0-3 and 4-7): 24 products per
+// page pair for eight heads instead of 48.
 
 #pragma once
 
@@ -69,11 +75,14 @@ template <bool kKW, bool kVW> struct PairDma { static constexpr int n = 4 + 2 * 
 // LDS by direct global->LDS loads; depth - 1 pairs are in flight while one is
 // computed).  The g <= 4 kernel fits 3 waves per SIMD, so one 12-wave
 // workgroup fills a compute unit, while its ring fits the LDS (up to one
-// plane); g <= 8 fits 2 (256 registers); the largest runs 1 wave per SIMD and
-// keeps more pairs in flight per wave instead.
+// plane); so does g <= 8 with 2-bit codes (the octet layout's 168 registers),
+// and with a plane 2 per SIMD; the largest runs 1 wave per SIMD and keeps more
+// pairs in flight per wave instead.
 template <int kNQ, int kParts> struct DecodeShape { static constexpr int waves = 4, depth = kParts == 3 ? 8 : 6; };
 template <int kParts> struct DecodeShape<1, kParts> { static constexpr int waves = kParts <= 4 ? 12 : 8, depth = 3; };
-template <int kParts> struct DecodeShape<2, kParts> { static constexpr int waves = 8, depth = kParts <= 4 ? 4 : 3; };
+template <int kParts> struct DecodeShape<2, kParts> {
+  static constexpr int waves = kParts == 3 ? 12 : 8, depth = kParts == 3 ? 3 : (kParts <= 4 ? 4 : 3);
+};
 // The narrow shape for batches of g <= 4 with 2-bit codes and no window: three
 // 4-wave workgroups per compute unit (the same 3 waves per SIMD and per-wave
 // ring).  Three times the splits per KV head cut each sequence's pages more
@@ -475,6 +484,16 @@ void decode_kernel(const DecodeParams p) {
   const int jj = col & 3;
   // within a page's metadata: the record of the group of G channels holding 32-channel group grp
   const int meta_off = kMetaRecordBytes * (4 * (grp >> meta_shift(p.gsize)) + a);
+  // The octet layout (g = 5..8): every product covers all eight heads.  MFMA
+  // column 8 oh + oj is head oj on the groups oh and oh + 2: a logit product
+  // puts group oh (one accumulator) or oh + 2 (another) in the columns of its
+  // half, and the P.V rows 8 oh + oj carry head oj's weights times the values'
+  // scales of group oh (tiles 0-3) or oh + 2 (tiles 4-7).  Half the products
+  // of two quads, and half their accumulators.
+  constexpr bool kOct = kNQ == 2;
+  const int oh = col >> 3, oj = col & 7;
+  const int meta_lo = kMetaRecordBytes * (4 * (oh >> meta_shift(p.gsize)) + a);
+  const int meta_hi = kMetaRecordBytes * (4 * ((oh + 2) >> meta_shift(p.gsize)) + a);
   // 16-byte chunks per page of the metadata and of the planes (fewer lanes load them when compact)
   const int meta_ch = meta_bytes(p.gsize) / 16;
   const int kplane_ch = plane_bytes(p.kbits) / 16, vplane_ch = plane_bytes(p.vbits) / 16;
@@ -614,33 +633,53 @@ void decode_kernel(const DecodeParams p) {
 #pragma unroll
   for (int d = 1; d < kDepth - 1; ++d) issue(d, min(wave + kW * d, npairs - 1));
 
-  // ---- block-diagonal query operands (fp16 hi/lo of q_hat * f)
+  // ---- block-diagonal query operands (fp16 hi/lo of q_hat * f): per quad Q,
+  //      column 4 grp + jj is head 4 Q + jj on group grp; in the octet layout
+  //      (one set), column 8 oh + oj is head oj on groups oh and oh + 2
   half8 qhi[kNQ][4], qlo[kNQ][4];
-  float qz[kNQ], c1[kNQ];
-#pragma unroll
-  for (int Q = 0; Q < kNQ; ++Q) {
-    const int jl = 4 * Q + jj;
-    const float f = s_f[jl];
-    half8 hi, lo;
+  float qz[kNQ], c1[kNQ];  // octet layout: qz[0], qz[1] for groups oh, oh + 2
+  // the hi/lo pair of head jl on 32-channel group gq, and its sum of q_hat over the group
+  auto q_part = [&](int jl, int gq, float f, half8& hi, half8& lo) {
     float qsum = 0.0f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       // element e meets key register e/2, whose codes carry a factor 4^(e/2)
-      const float qv = s_q[jl][32 * grp + 8 * a + e];
+      const float qv = s_q[jl][32 * gq + 8 * a + e];
       const float sc = qv * f * (1.0f / static_cast<float>(1 << (2 * (e >> 1))));
       const _Float16 hh = static_cast<_Float16>(sc);
       hi[e] = hh;
       lo[e] = static_cast<_Float16>(sc - static_cast<float>(hh));
       qsum += qv;
     }
-    qsum = rows_sum(qsum);  // sum of q_hat over group grp's 32 channels
-    c1[Q] = kTwo24 / f;
-    qz[Q] = qsum / c1[Q];
-    const half8 zero = {};
+    return rows_sum(qsum);  // over the group's 32 channels
+  };
+  const half8 zero = {};
+  if constexpr (kOct) {
+    const float f = s_f[oj];
+    half8 hl, ll, hh, lh;
+    const float qs_lo = q_part(oj, oh, f, hl, ll), qs_hi = q_part(oj, oh + 2, f, hh, lh);
+    c1[0] = kTwo24 / f;
+    qz[0] = qs_lo / c1[0];
+    qz[1] = qs_hi / c1[0];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      qhi[Q][kk] = (grp == kk) ? hi : zero;
-      qlo[Q][kk] = (grp == kk) ? lo : zero;
+      qhi[0][kk] = kk == oh ? hl : (kk == oh + 2 ? hh : zero);
+      qlo[0][kk] = kk == oh ? ll : (kk == oh + 2 ? lh : zero);
+    }
+  } else {
+#pragma unroll
+    for (int Q = 0; Q < kNQ; ++Q) {
+      const int jl = 4 * Q + jj;
+      const float f = s_f[jl];
+      half8 hi, lo;
+      const float qsum = q_part(jl, grp, f, hi, lo);
+      c1[Q] = kTwo24 / f;
+      qz[Q] = qsum / c1[Q];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        qhi[Q][kk] = (grp == kk) ? hi : zero;
+        qlo[Q][kk] = (grp == kk) ? lo : zero;
+      }
     }
   }
 
@@ -655,9 +694,14 @@ void decode_kernel(const DecodeParams p) {
   // below 2^15, for every scale the cache format stores, and the group's
   // largest scale gives operands of at least p * 2^-3 (normal down to
   // p = 2^-11).  m_adj = m_run + e_u is the exp2 argument's offset.
+  // The octet layout keeps one state (index 0) for head oj, z_run[0], [1] for
+  // its groups oh and oh + 2, and a unit per group: e_u (oh) and e_u2 (oh + 2);
+  // the weights are formed in units of 2^e_u and scaled by ratio =
+  // 2^(e_u - e_u2) for group oh + 2.
   float m_run[kNQ], l_run[kNQ], z_run[kNQ], m_adj[kNQ], thr[kNQ];
-  float e_u = 0.0f;
+  float e_u = 0.0f, e_u2 = 0.0f, ratio = 1.0f;
   _Float16 u_hi = static_cast<_Float16>(128.0f), u_lo = static_cast<_Float16>(0.125f);  // 2^(e_u+7), 2^(e_u-3)
+  _Float16 u_hi2 = u_hi, u_lo2 = u_lo;                                                 // the same for e_u2
   float4v acc[kNQ][8];
 #pragma unroll
   for (int Q = 0; Q < kNQ; ++Q) {
@@ -728,21 +772,16 @@ void decode_kernel(const DecodeParams p) {
     const bool has1 = ph1 >= 0;
     // no position of the pair masked
     const bool full = ok0 && has1 && (p0 + i0) * kPage >= int2_lo && (p0 + i0 + 2) * kPage <= int2_hi;
-    // logits (log2 units, divided by c1) for both pages
-    float sp[kNQ][2][4];
-#pragma unroll
-    for (int X = 0; X < 2; ++X) {
+    // Key operands of page X: a code at bits 2q (+16) of a word is the fp16
+    // subnormal code * 4^q * 2^-24, so one AND per register; groups 1 and 3 sit
+    // in the upper byte of each half and are shifted down first.  The factor
+    // 4^q is divided out of the query operand.  A wide key's high bits, moved
+    // two bits up, fill bits 2q + 2 and 2q + 3: low | high is the whole code
+    // times 4^q (at most 15 * 64 < 2^10, still a subnormal), one AND-OR more.
+    auto key_ops = [&](int X, half8 (&kA)[4]) {
       const uint4v rec = X ? P.rec1 : P.rec0;
-      const uint4v km = X ? P.km1 : P.km0;
-      // Key operands: a code at bits 2q (+16) of a word is the fp16 subnormal
-      // code * 4^q * 2^-24, so one AND per register; groups 1 and 3 sit in the
-      // upper byte of each half and are shifted down first.  The factor 4^q is
-      // divided out of the query operand.  A wide key's high bits, moved two
-      // bits up, fill bits 2q + 2 and 2q + 3: low | high is the whole code times
-      // 4^q (at most 15 * 64 < 2^10, still a subnormal), one AND-OR more.
       const uint32_t kw[4] = {rec[0], rec[0] >> 8, rec[1], rec[1] >> 8};
       const uint32_t kw2[4] = {kh[X][0] << 2, (kh[X][0] >> 8) << 2, kh[X][1] << 2, (kh[X][1] >> 8) << 2};
-      half8 kA[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         uint4v rr;
@@ -753,6 +792,198 @@ void decode_kernel(const DecodeParams p) {
         }
         kA[kk] = __builtin_bit_cast(half8, rr);
       }
+    };
+    // Value operands: tile t holds channels 16t..16t+15.  Tiles 0-3 sit in the
+    // low byte of each half (bits 2t), tiles 4-7 in the high byte; a register
+    // of tile t holds the codes times 4^(t%4) (divided out of acc at the end).
+    // Wide values: the plane's bits two up, OR-ed in as for the keys.
+    auto value_ops = [&](half8 (&vB)[8]) {
+      const uint32_t vw[8] = {P.rec0[2], P.rec0[3], P.rec1[2], P.rec1[3],
+                              P.rec0[2] >> 8, P.rec0[3] >> 8, P.rec1[2] >> 8, P.rec1[3] >> 8};
+      const uint32_t vw2[8] = {vh[0][0] << 2, vh[0][1] << 2, vh[1][0] << 2, vh[1][1] << 2,
+                               (vh[0][0] >> 8) << 2, (vh[0][1] >> 8) << 2, (vh[1][0] >> 8) << 2,
+                               (vh[1][1] >> 8) << 2};
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const uint32_t m = 0x00030003u << (2 * (t & 3));
+        const int hb = 4 * (t >> 2);
+        uint4v rr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rr[i] = kVW ? ((vw[hb + i] & m) | (vw2[hb + i] & (m << 2))) : (vw[hb + i] & m);
+        vB[t] = __builtin_bit_cast(half8, rr);
+      }
+    };
+    // position i of page X's quad a is attended from the cache
+    auto live = [&](int X, int i) {
+      return (X == 0 ? ok0 : has1) && (p0 + i0 + X) * kPage + 4 * a + i >= int2_lo &&
+             (p0 + i0 + X) * kPage + 4 * a + i < int2_hi;
+    };
+
+    if constexpr (kOct) {
+      // metadata records of the lane's groups oh (L) and oh + 2 (H), pages 0 and 1
+      uint4v kmL[2], kmH[2], vmL[2], vmH[2];
+#pragma unroll
+      for (int X = 0; X < 2; ++X) {
+        kmL[X] = *reinterpret_cast<const uint4v*>(meta + 512 * X + meta_lo);
+        vmL[X] = *reinterpret_cast<const uint4v*>(meta + 512 * X + meta_lo + 16);
+        kmH[X] = *reinterpret_cast<const uint4v*>(meta + 512 * X + meta_hi);
+        vmH[X] = *reinterpret_cast<const uint4v*>(meta + 512 * X + meta_hi + 16);
+      }
+      // logits (log2 units, divided by c1) of head oj, tokens 4 a + i of page X
+      float so[2][4];
+#pragma unroll
+      for (int X = 0; X < 2; ++X) {
+        half8 kA[4];
+        key_ops(X, kA);
+        float4v CL = {0.0f, 0.0f, 0.0f, 0.0f}, CH = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {  // groups 0, 1: column half oh holds group oh
+          CL = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[kk], qhi[0][kk], CL, 0, 0, 0);
+          CL = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[kk], qlo[0][kk], CL, 0, 0, 0);
+        }
+#pragma unroll
+        for (int kk = 2; kk < 4; ++kk) {  // groups 2, 3: group oh + 2
+          CH = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[kk], qhi[0][kk], CH, 0, 0, 0);
+          CH = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[kk], qlo[0][kk], CH, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // the lane's two groups, then the other column half's two (lane col ^ 8)
+          const uint32_t kl = kmL[X][i], kh2 = kmH[X][i];
+          const float s = fmaf(CL[i], f16_lo(kl), fmaf(f16_hi(kl), qz[0], fmaf(CH[i], f16_lo(kh2), f16_hi(kh2) * qz[1])));
+          so[X][i] = s + dpp_f32<kDppRowRor8>(s);
+        }
+        if (!full) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!live(X, i)) {  // weight 0; the value metadata may hold any bits
+              so[X][i] = -INFINITY;
+              vmL[X][i] = 0u;
+              vmH[X][i] = 0u;
+            }
+        }
+      }
+      half8 vB[8];
+      value_ops(vB);
+
+      // the P.V units of groups oh and oh + 2, as in the quad layout below
+      {
+        auto s16 = [](uint32_t w) { return __builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)); };
+        _Float16 mL = s16(vmL[0][0]), mH = s16(vmH[0][0]);
+#pragma unroll
+        for (int X = 0; X < 2; ++X)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            mL = __builtin_fmaxf16(mL, s16(vmL[X][i]));
+            mH = __builtin_fmaxf16(mH, s16(vmH[X][i]));
+          }
+        // bit 8 h of fold(b): some lane of column half h (lanes 16 a + 8 h + j) is set
+        auto fold = [](uint64_t b) {
+          b |= b >> 32;
+          b |= b >> 16;
+          b |= b >> 1;
+          b |= b >> 2;
+          b |= b >> 4;
+          return b & 0x101ull;
+        };
+        const _Float16 z16 = static_cast<_Float16>(0.0f);
+        const uint64_t need = __ballot(mL >= u_hi) | __ballot(mH >= u_hi2) |
+                              (fold(__ballot(mL > z16)) & ~fold(__ballot(mL >= u_lo))) |
+                              (fold(__ballot(mH > z16)) & ~fold(__ballot(mH >= u_lo2)));
+        if (need != 0) {  // rare
+          // a group's largest scale: its column half (8 columns) over the four rows
+          auto group_max = [](float x) {
+            x = fmaxf(x, dpp_f32<QuadXor1::ctrl>(x));
+            x = fmaxf(x, dpp_f32<QuadXor2::ctrl>(x));
+            x = fmaxf(x, __shfl_xor(x, 4));
+            return rows_max(x);
+          };
+          auto new_unit = [](float gs, float e_old, _Float16 uh, _Float16 ul) {
+            int ex = 0;
+            frexpf(gs, &ex);  // gs in [2^(ex-1), 2^ex)
+            const bool move = gs >= static_cast<float>(uh) || (gs < static_cast<float>(ul) && gs > 0.0f);
+            return move ? static_cast<float>(ex - 7) : e_old;
+          };
+          const float nL = new_unit(group_max(static_cast<float>(mL)), e_u, u_hi, u_lo);
+          const float nH = new_unit(group_max(static_cast<float>(mH)), e_u2, u_hi2, u_lo2);
+          const float fL = ldexpf(1.0f, static_cast<int>(e_u - nL));  // old unit / new unit
+          const float fH = ldexpf(1.0f, static_cast<int>(e_u2 - nH));
+          // acc rows 4 a + i belong to group a / 2 (tiles 0-3) and a / 2 + 2 (tiles 4-7)
+          const float faL = __shfl(fL, 8 * (a >> 1)), faH = __shfl(fH, 8 * (a >> 1));
+#pragma unroll
+          for (int t = 0; t < 8; ++t) acc[0][t] *= t < 4 ? faL : faH;
+          l_run[0] *= fL;
+          z_run[0] *= fL;
+          z_run[1] *= fH;
+          e_u = nL;
+          e_u2 = nH;
+          m_adj[0] = m_run[0] + e_u;
+          ratio = ldexpf(1.0f, static_cast<int>(e_u - e_u2));
+          u_hi = static_cast<_Float16>(ldexpf(1.0f, static_cast<int>(e_u) + 7));  // inf past fp16: never reached
+          u_lo = static_cast<_Float16>(ldexpf(1.0f, static_cast<int>(e_u) - 3));  // 0 below fp16: no lower unit
+          u_hi2 = static_cast<_Float16>(ldexpf(1.0f, static_cast<int>(e_u2) + 7));
+          u_lo2 = static_cast<_Float16>(ldexpf(1.0f, static_cast<int>(e_u2) - 3));
+        }
+      }
+
+      // online softmax of head oj (lazy reference, as below)
+      float smax = so[0][0];
+#pragma unroll
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) smax = fmaxf(smax, so[X][i]);
+      if (__ballot(smax > thr[0]) != 0) {
+        const float m_new = fmaxf(m_run[0], rows_max(smax) * c1[0]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[0] - m_new);
+        // acc row 4 a + i is head 4 (a % 2) + i: its factor from lane 4 (a % 2) + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float al = __shfl(alpha, 4 * (a & 1) + i);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) acc[0][t][i] *= al;
+        }
+        l_run[0] *= alpha;
+        z_run[0] *= alpha;
+        z_run[1] *= alpha;
+        m_run[0] = m_new;
+        m_adj[0] = m_new + e_u;
+        thr[0] = (m_new + kLazy) * (1.0f / c1[0]);
+      }
+      half8 pL, pH;  // rows 8 oh + oj: weights times the value scales of group oh / oh + 2
+#pragma unroll
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pr = __builtin_amdgcn_exp2f(fmaf(so[X][i], c1[0], -m_adj[0]));
+          const float prh = pr * ratio;
+          l_run[0] += pr;
+          z_run[0] = fmaf(f16_hi(vmL[X][i]), pr, z_run[0]);
+          z_run[1] = fmaf(f16_hi(vmH[X][i]), prh, z_run[1]);
+          if (kHad) {
+            const float psl = f16_lo(vmL[X][i]) * pr, psh = f16_lo(vmH[X][i]) * prh;
+            const _Float16 hl = static_cast<_Float16>(psl), hh = static_cast<_Float16>(psh);
+            pL[4 * X + i] = hl;
+            pH[4 * X + i] = hh;
+            z_run[0] = fmaf(vmid, psl - static_cast<float>(hl), z_run[0]);
+            z_run[1] = fmaf(vmid, psh - static_cast<float>(hh), z_run[1]);
+          } else {
+            pL[4 * X + i] = static_cast<_Float16>(fmaf(f16_lo(vmL[X][i]), pr, 0.0f));
+            pH[4 * X + i] = static_cast<_Float16>(fmaf(f16_lo(vmH[X][i]), prh, 0.0f));
+          }
+        }
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(t < 4 ? pL : pH, vB[t], acc[0][t], 0, 0, 0);
+      return;
+    }
+
+    // logits (log2 units, divided by c1) for both pages
+    float sp[kNQ][2][4];
+#pragma unroll
+    for (int X = 0; X < 2; ++X) {
+      const uint4v km = X ? P.km1 : P.km0;
+      half8 kA[4];
+      key_ops(X, kA);
       const int pos0 = (p0 + i0 + X) * kPage + 4 * a;
       const bool page_ok = X == 0 ? ok0 : has1;
 #pragma unroll
@@ -790,24 +1021,8 @@ void decode_kernel(const DecodeParams p) {
       }
     }
 
-    // Value operands: tile t holds channels 16t..16t+15.  Tiles 0-3 sit in the
-    // low byte of each half (bits 2t), tiles 4-7 in the high byte; a register
-    // of tile t holds the codes times 4^(t%4) (divided out of acc at the end).
-    // Wide values: the plane's bits two up, OR-ed in as for the keys.
-    const uint32_t vw[8] = {P.rec0[2], P.rec0[3], P.rec1[2], P.rec1[3],
-                            P.rec0[2] >> 8, P.rec0[3] >> 8, P.rec1[2] >> 8, P.rec1[3] >> 8};
-    const uint32_t vw2[8] = {vh[0][0] << 2, vh[0][1] << 2, vh[1][0] << 2, vh[1][1] << 2,
-                             (vh[0][0] >> 8) << 2, (vh[0][1] >> 8) << 2, (vh[1][0] >> 8) << 2, (vh[1][1] >> 8) << 2};
     half8 vB[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint32_t m = 0x00030003u << (2 * (t & 3));
-      const int hb = 4 * (t >> 2);
-      uint4v rr;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rr[i] = kVW ? ((vw[hb + i] & m) | (vw2[hb + i] & (m << 2))) : (vw[hb + i] & m);
-      vB[t] = __builtin_bit_cast(half8, rr);
-    }
+    value_ops(vB);
 
     // The P.V operand's unit per value group, from the pair's value scales
     // (lane: its group's scales of 8 positions; masked ones are 0): any scale
@@ -945,27 +1160,56 @@ void decode_kernel(const DecodeParams p) {
     const float v0 = lane_val(x, k0), v1 = lane_val(x, k0 + 4), v2 = lane_val(x, k0 + 8), v3 = lane_val(x, k0 + 12);
     return a == 0 ? v0 : (a == 1 ? v1 : (a == 2 ? v2 : v3));
   };
-#pragma unroll
-  for (int Q = 0; Q < kNQ; ++Q) {
-    // the sums were kept in units of 2^e_u of the lane's value group: lanes
-    // 0..3 (group 0) carry the weight sums, acc rows of group a take group a's unit
-    const float unit = ldexpf(1.0f, static_cast<int>(e_u));
-    const float unit_a = pick_a(unit, 0);
-    const float lsum = rows_sum(l_run[Q]) * unit;
-    const float zsum = rows_sum(z_run[Q]) * unit;  // lane (., grp, jj): sum_s p z_v for (jj, grp)
+  if constexpr (kOct) {
+    // sums in units of 2^e_u (group oh) and 2^e_u2 (group oh + 2); lanes 0..7
+    // (column half 0) carry head oj's weight sum.  Lane (a, col) holds acc rows
+    // 4 a + i: head 4 (a % 2) + i on group a / 2 (tiles 0-3) or a / 2 + 2
+    // (tiles 4-7), kept where the tile's channels are that group's.
+    const float unit_l = ldexpf(1.0f, static_cast<int>(e_u)), unit_h = ldexpf(1.0f, static_cast<int>(e_u2));
+    const float ua_l = (a >> 1) ? lane_val(unit_l, 8) : lane_val(unit_l, 0);
+    const float ua_h = (a >> 1) ? lane_val(unit_h, 8) : lane_val(unit_h, 0);
+    const float lsum = rows_sum(l_run[0]) * unit_l;
+    // lane (., oh, oj): sum_s p z_v for (oj, group oh) and (oj, group oh + 2)
+    const float zs_l = rows_sum(z_run[0]) * unit_l, zs_h = rows_sum(z_run[1]) * unit_h;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float zi = pick_a(zsum, i);  // zero part of head i, group a (the rows hold the same sums)
+      const int jh = 4 * (a & 1) + i;
+      const float zl = pick_a(zs_l, i), zh = pick_a(zs_h, i);  // lane 4 a + i: head jh, group a / 2 (+ 2)
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        if ((t >> 1) == a)  // undo the tile's code factor 4^(t%4), the 2^-24 code scale and the unit
-          s_post[(wave * kNH + 4 * Q + i) * kHeadDim + 16 * t + col] =
-              acc[Q][t][i] * ((kTwo24 / static_cast<float>(1 << (2 * (t & 3)))) * unit_a) + zi;
+        if (((t >> 1) & 1) == (a >> 1))
+          s_post[(wave * kNH + jh) * kHeadDim + 16 * t + col] =
+              acc[0][t][i] * ((kTwo24 / static_cast<float>(1 << (2 * (t & 3)))) * (t < 4 ? ua_l : ua_h)) +
+              (t < 4 ? zl : zh);
       }
     }
-    if (lane < 4) {
-      s_m[wave][4 * Q + lane] = m_run[Q];
-      s_l[wave][4 * Q + lane] = lsum;
+    if (lane < 8) {
+      s_m[wave][lane] = m_run[0];
+      s_l[wave][lane] = lsum;
+    }
+  } else {
+#pragma unroll
+    for (int Q = 0; Q < kNQ; ++Q) {
+      // the sums were kept in units of 2^e_u of the lane's value group: lanes
+      // 0..3 (group 0) carry the weight sums, acc rows of group a take group a's unit
+      const float unit = ldexpf(1.0f, static_cast<int>(e_u));
+      const float unit_a = pick_a(unit, 0);
+      const float lsum = rows_sum(l_run[Q]) * unit;
+      const float zsum = rows_sum(z_run[Q]) * unit;  // lane (., grp, jj): sum_s p z_v for (jj, grp)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float zi = pick_a(zsum, i);  // zero part of head i, group a (the rows hold the same sums)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          if ((t >> 1) == a)  // undo the tile's code factor 4^(t%4), the 2^-24 code scale and the unit
+            s_post[(wave * kNH + 4 * Q + i) * kHeadDim + 16 * t + col] =
+                acc[Q][t][i] * ((kTwo24 / static_cast<float>(1 << (2 * (t & 3)))) * unit_a) + zi;
+        }
+      }
+      if (lane < 4) {
+        s_m[wave][4 * Q + lane] = m_run[Q];
+        s_l[wave][4 * Q + lane] = lsum;
+      }
     }
   }
   __syncthreads();
@@ -1491,6 +1735,7 @@ static hipError_t launch_one(const DecodeParams& prm, hipStream_t stream, hipEve
                             args, 0, stream,
                             ev_begin, ev_end, 0);
 }
+template <int kNQ>  // instantiated for kNQ = 1 only
 static hipError_t launch_narrow(const DecodeParams& prm, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
   constexpr int kW = kNarrowWaves, kD = kNarrowDepth, kC = kNarrowWgPerCu;
   DecodeParams arg = prm;
@@ -1508,7 +1753,9 @@ static hipError_t launch_narrow(const DecodeParams& prm, hipStream_t stream, hip
 // kvq_decode_g16.hip), so the three compile in parallel.
 template <int kNQ>
 hipError_t launch_decode_quads(const DecodeParams& prm, hipStream_t stream, hipEvent_t ev_begin, hipEvent_t ev_end) {
-  if (kNQ == 1 && prm.narrow) return launch_narrow(prm, stream, ev_begin, ev_end);
+  if constexpr (kNQ == 1) {
+    if (prm.narrow) return launch_narrow<kNQ>(prm, stream, ev_begin, ev_end);
+  }
   const bool kw = prm.kbits > 2, vw = prm.vbits > 2;
   if (kw)
     return vw ? launch_one<kNQ, true, true>(prm, stream, ev_begin, ev_end)

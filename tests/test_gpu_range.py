@@ -92,6 +92,7 @@ CASES = [
     ("big_then_small", 4, 1, [1800]),
     ("per_position", 8, 1, [1200, 517]),
     ("big_then_small", 8, 1, [1024]),
+    ("phases", 8, 2, [2049, 700]),
     ("per_position", 16, 1, [900]),
     ("phases", 16, 1, [1300]),
 ]
