@@ -54,6 +54,8 @@ WORKLOADS = {
                         lambda I, rot: I.batched_case(rotation=rot)),
     "gqa70b_b4_t128k": ("70B-class GQA decode (64 q / 8 kv heads), batch 4, context 131072 each",
                         lambda I, rot: I.seventy_b_case(rotation=rot)),
+    "gqa405b_t128k": ("405B-class GQA decode (128 q / 8 kv heads, group 16), batch 1, context 131072",
+                      lambda I, rot: I.gqa405b_case(rotation=rot)),
 }
 
 

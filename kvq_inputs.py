@@ -277,5 +277,11 @@ def seventy_b_case(T: int = 131072, B: int = 4, seed: int = 5, rotation: str = "
                      n_outliers=3, mu_tokens=2048, table_policy="interleaved", rotation=rotation)
 
 
+def gqa405b_case(T: int = 131072, B: int = 1, seed: int = 6, rotation: str = "dense") -> Case:
+    """128 query / 8 KV heads (group 16, the 405B-class head layout), bf16, interleaved page allocator."""
+    return make_case(f"gqa405b_b{B}_t{T}", seed, B=B, Hq=128, Hkv=8, seq_lens=[T] * B, dtype="bf16",
+                     n_outliers=3, mu_tokens=2048, table_policy="interleaved", rotation=rotation)
+
+
 def list_cases() -> List[str]:
     return ["tiny_t256", "llama8b_t32k", "llama8b_t128k", "llama8b_batch16", "gqa70b_b4_t128k"]

@@ -49,7 +49,10 @@
 // accumulators per page (groups 0-1 and 2-3, half the columns of each
 // product live) summed across the column halves by one DPP rotation, and
 // P.V one A operand per group half (tiles 0-3 and 4-7): 24 products per
-// page pair for eight heads instead of 48.
+// page pair for eight heads instead of 48.  For g = 9..16 the hexadeca
+// layout makes every column a head: four logit accumulators per page (one
+// per group, all columns live) and one P.V operand per group, 24 products
+// per page pair for sixteen heads instead of 96.
 
 #pragma once
 
@@ -76,9 +79,11 @@ template <bool kKW, bool kVW> struct PairDma { static constexpr int n = 4 + 2 * 
 // computed).  The g <= 4 kernel fits 3 waves per SIMD, so one 12-wave
 // workgroup fills a compute unit, while its ring fits the LDS (up to one
 // plane); so does g <= 8 with 2-bit codes (the octet layout's 168 registers),
-// and with a plane 2 per SIMD; the largest runs 1 wave per SIMD and keeps more
-// pairs in flight per wave instead.
-template <int kNQ, int kParts> struct DecodeShape { static constexpr int waves = 4, depth = kParts == 3 ? 8 : 6; };
+// and with a plane 2 per SIMD; g <= 16 with 2-bit codes runs 2 per SIMD (the
+// hexadeca layout), with a plane 1 per SIMD and more pairs in flight per wave.
+template <int kNQ, int kParts> struct DecodeShape {
+  static constexpr int waves = kParts == 3 ? 8 : 4, depth = kParts == 3 ? 4 : 6;
+};
 template <int kParts> struct DecodeShape<1, kParts> { static constexpr int waves = kParts <= 4 ? 12 : 8, depth = 3; };
 template <int kParts> struct DecodeShape<2, kParts> {
   static constexpr int waves = kParts == 3 ? 12 : 8, depth = kParts == 3 ? 3 : (kParts <= 4 ? 4 : 3);
@@ -491,9 +496,17 @@ void decode_kernel(const DecodeParams p) {
   // scales of group oh (tiles 0-3) or oh + 2 (tiles 4-7).  Half the products
   // of two quads, and half their accumulators.
   constexpr bool kOct = kNQ == 2;
+  // The hexadeca layout (g = 9..16): column (and P.V row) n is head n, and each
+  // product is one group's: four logit accumulators per page and one P.V
+  // operand per group, 24 products per page pair instead of four quads' 96.
+  // The units of the P.V operand are then wave-uniform, one per group.
+  constexpr bool kHex = kNQ == 4;
   const int oh = col >> 3, oj = col & 7;
   const int meta_lo = kMetaRecordBytes * (4 * (oh >> meta_shift(p.gsize)) + a);
   const int meta_hi = kMetaRecordBytes * (4 * ((oh + 2) >> meta_shift(p.gsize)) + a);
+  int meta_g[4];  // hexadeca layout: the records of all four groups
+#pragma unroll
+  for (int G = 0; G < 4; ++G) meta_g[G] = kMetaRecordBytes * (4 * (G >> meta_shift(p.gsize)) + a);
   // 16-byte chunks per page of the metadata and of the planes (fewer lanes load them when compact)
   const int meta_ch = meta_bytes(p.gsize) / 16;
   const int kplane_ch = plane_bytes(p.kbits) / 16, vplane_ch = plane_bytes(p.vbits) / 16;
@@ -654,7 +667,12 @@ void decode_kernel(const DecodeParams p) {
     return rows_sum(qsum);  // over the group's 32 channels
   };
   const half8 zero = {};
-  if constexpr (kOct) {
+  if constexpr (kHex) {  // column col is head col; qz[G] for group G
+    const float f = s_f[col];
+    c1[0] = kTwo24 / f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qz[kk] = q_part(col, kk, f, qhi[0][kk], qlo[0][kk]) / c1[0];
+  } else if constexpr (kOct) {
     const float f = s_f[oj];
     half8 hl, ll, hh, lh;
     const float qs_lo = q_part(oj, oh, f, hl, ll), qs_hi = q_part(oj, oh + 2, f, hh, lh);
@@ -698,8 +716,18 @@ void decode_kernel(const DecodeParams p) {
   // its groups oh and oh + 2, and a unit per group: e_u (oh) and e_u2 (oh + 2);
   // the weights are formed in units of 2^e_u and scaled by ratio =
   // 2^(e_u - e_u2) for group oh + 2.
+  // The hexadeca layout keeps one state (index 0) for head col, z_run[G] per
+  // group, and wave-uniform units eg[G]: its weights are formed without a
+  // unit (exp2(logit - m_run) <= 2^kLazy) and scaled by 2^-eg[G] per group.
   float m_run[kNQ], l_run[kNQ], z_run[kNQ], m_adj[kNQ], thr[kNQ];
   float e_u = 0.0f, e_u2 = 0.0f, ratio = 1.0f;
+  float eg[4] = {0.0f, 0.0f, 0.0f, 0.0f}, ug[4] = {1.0f, 1.0f, 1.0f, 1.0f};  // hexadeca: eg, ug = 2^-eg
+  _Float16 uhg[4], ulg[4];  // hexadeca: 2^(eg+7), 2^(eg-3)
+#pragma unroll
+  for (int G = 0; G < 4; ++G) {
+    uhg[G] = static_cast<_Float16>(128.0f);
+    ulg[G] = static_cast<_Float16>(0.125f);
+  }
   _Float16 u_hi = static_cast<_Float16>(128.0f), u_lo = static_cast<_Float16>(0.125f);  // 2^(e_u+7), 2^(e_u-3)
   _Float16 u_hi2 = u_hi, u_lo2 = u_lo;                                                 // the same for e_u2
   float4v acc[kNQ][8];
@@ -818,6 +846,139 @@ void decode_kernel(const DecodeParams p) {
       return (X == 0 ? ok0 : has1) && (p0 + i0 + X) * kPage + 4 * a + i >= int2_lo &&
              (p0 + i0 + X) * kPage + 4 * a + i < int2_hi;
     };
+
+    if constexpr (kHex) {
+      // metadata records of the four groups, tokens 4 a + i of pages 0 and 1
+      uint4v kmg[2][4], vmg[2][4];
+#pragma unroll
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int G = 0; G < 4; ++G) {
+          kmg[X][G] = *reinterpret_cast<const uint4v*>(meta + 512 * X + meta_g[G]);
+          vmg[X][G] = *reinterpret_cast<const uint4v*>(meta + 512 * X + meta_g[G] + 16);
+        }
+      // logits (log2 units, divided by c1) of head col, tokens 4 a + i of page X
+      float sx[2][4];
+#pragma unroll
+      for (int X = 0; X < 2; ++X) {
+        half8 kA[4];
+        key_ops(X, kA);
+        float4v C[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          C[kk] = float4v{0.0f, 0.0f, 0.0f, 0.0f};
+          C[kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[kk], qhi[0][kk], C[kk], 0, 0, 0);
+          C[kk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kA[kk], qlo[0][kk], C[kk], 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float s = 0.0f;
+#pragma unroll
+          for (int G = 0; G < 4; ++G) {
+            const uint32_t km = kmg[X][G][i];
+            s = fmaf(C[G][i], f16_lo(km), fmaf(f16_hi(km), qz[G], s));
+          }
+          sx[X][i] = s;
+        }
+        if (!full) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (!live(X, i)) {  // weight 0; the value metadata may hold any bits
+              sx[X][i] = -INFINITY;
+#pragma unroll
+              for (int G = 0; G < 4; ++G) vmg[X][G][i] = 0u;
+            }
+        }
+      }
+      half8 vB[8];
+      value_ops(vB);
+
+      // the P.V unit of each group (wave-uniform): moved when a scale of the
+      // pair reaches 2^(eg+7), or when the group's nonzero scales all lie below
+      // 2^(eg-3); the sums kept in the old unit are rescaled
+      {
+        auto s16 = [](uint32_t w) { return __builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)); };
+        const _Float16 z16 = static_cast<_Float16>(0.0f);
+        _Float16 mg[4];
+        bool need = false;
+#pragma unroll
+        for (int G = 0; G < 4; ++G) {
+          mg[G] = s16(vmg[0][G][0]);
+#pragma unroll
+          for (int X = 0; X < 2; ++X)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mg[G] = __builtin_fmaxf16(mg[G], s16(vmg[X][G][i]));
+          need = need || __ballot(mg[G] >= uhg[G]) != 0 ||
+                 (__ballot(mg[G] > z16) != 0 && __ballot(mg[G] >= ulg[G]) == 0);
+        }
+        if (need) {  // rare
+#pragma unroll
+          for (int G = 0; G < 4; ++G) {
+            const float gs = wave_max_all(static_cast<float>(mg[G]));
+            int ex = 0;
+            frexpf(gs, &ex);  // gs in [2^(ex-1), 2^ex)
+            const bool move = gs >= static_cast<float>(uhg[G]) || (gs < static_cast<float>(ulg[G]) && gs > 0.0f);
+            const float en = move ? static_cast<float>(ex - 7) : eg[G];
+            const float fl = ldexpf(1.0f, static_cast<int>(eg[G] - en));  // old unit / new unit
+            acc[0][2 * G] *= fl;
+            acc[0][2 * G + 1] *= fl;
+            z_run[G] *= fl;
+            eg[G] = en;
+            ug[G] = ldexpf(1.0f, -static_cast<int>(en));
+            uhg[G] = static_cast<_Float16>(ldexpf(1.0f, static_cast<int>(en) + 7));  // inf past fp16: never reached
+            ulg[G] = static_cast<_Float16>(ldexpf(1.0f, static_cast<int>(en) - 3));  // 0 below fp16: no lower unit
+          }
+        }
+      }
+
+      // online softmax of head col (lazy reference; weights formed without a unit)
+      float smax = sx[0][0];
+#pragma unroll
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) smax = fmaxf(smax, sx[X][i]);
+      if (__ballot(smax > thr[0]) != 0) {
+        const float m_new = fmaxf(m_run[0], rows_max(smax) * c1[0]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[0] - m_new);
+        // acc row 4 a + i is head 4 a + i: its factor from lane 4 a + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float al = __shfl(alpha, 4 * a + i);
+#pragma unroll
+          for (int t = 0; t < 8; ++t) acc[0][t][i] *= al;
+        }
+        l_run[0] *= alpha;
+#pragma unroll
+        for (int G = 0; G < 4; ++G) z_run[G] *= alpha;
+        m_run[0] = m_new;
+        thr[0] = (m_new + kLazy) * (1.0f / c1[0]);
+      }
+      half8 pG[4];  // row col: head col's weights times the value scales of group G, in units of 2^eg
+#pragma unroll
+      for (int X = 0; X < 2; ++X)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float pr = __builtin_amdgcn_exp2f(fmaf(sx[X][i], c1[0], -m_run[0]));
+          l_run[0] += pr;
+#pragma unroll
+          for (int G = 0; G < 4; ++G) {
+            const uint32_t vm = vmg[X][G][i];
+            const float pw = pr * ug[G];
+            z_run[G] = fmaf(f16_hi(vm), pw, z_run[G]);
+            if (kHad) {
+              const float ps = f16_lo(vm) * pw;
+              const _Float16 hi = static_cast<_Float16>(ps);
+              pG[G][4 * X + i] = hi;
+              z_run[G] = fmaf(vmid, ps - static_cast<float>(hi), z_run[G]);
+            } else {
+              pG[G][4 * X + i] = static_cast<_Float16>(fmaf(f16_lo(vm), pw, 0.0f));
+            }
+          }
+        }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) acc[0][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pG[t >> 1], vB[t], acc[0][t], 0, 0, 0);
+      return;
+    }
 
     if constexpr (kOct) {
       // metadata records of the lane's groups oh (L) and oh + 2 (H), pages 0 and 1
@@ -1160,7 +1321,32 @@ void decode_kernel(const DecodeParams p) {
     const float v0 = lane_val(x, k0), v1 = lane_val(x, k0 + 4), v2 = lane_val(x, k0 + 8), v3 = lane_val(x, k0 + 12);
     return a == 0 ? v0 : (a == 1 ? v1 : (a == 2 ? v2 : v3));
   };
-  if constexpr (kOct) {
+  if constexpr (kHex) {
+    // lane (a, col) holds acc rows 4 a + i, head 4 a + i, of every tile; the
+    // sums of tile t are in units of 2^eg[t / 2]; lanes 0..15 carry head col's
+    // weight sum (no unit)
+    const float lsum = rows_sum(l_run[0]);
+    float zs[4];  // lane (., col): sum_s p z_v for (head col, group G)
+#pragma unroll
+    for (int G = 0; G < 4; ++G) zs[G] = rows_sum(z_run[G]) * ldexpf(1.0f, static_cast<int>(eg[G]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int jh = 4 * a + i;
+#pragma unroll
+      for (int G = 0; G < 4; ++G) {
+        const float zi = pick_a(zs[G], i);  // lane 4 a + i: head jh, group G
+        const float ut = ldexpf(1.0f, static_cast<int>(eg[G]));
+#pragma unroll
+        for (int t = 2 * G; t < 2 * G + 2; ++t)
+          s_post[(wave * kNH + jh) * kHeadDim + 16 * t + col] =
+              acc[0][t][i] * ((kTwo24 / static_cast<float>(1 << (2 * (t & 3)))) * ut) + zi;
+      }
+    }
+    if (lane < 16) {
+      s_m[wave][lane] = m_run[0];
+      s_l[wave][lane] = lsum;
+    }
+  } else if constexpr (kOct) {
     // sums in units of 2^e_u (group oh) and 2^e_u2 (group oh + 2); lanes 0..7
     // (column half 0) carry head oj's weight sum.  Lane (a, col) holds acc rows
     // 4 a + i: head 4 (a % 2) + i on group a / 2 (tiles 0-3) or a / 2 + 2

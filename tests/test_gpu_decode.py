@@ -227,6 +227,7 @@ FULL = {
     "llama8b_t128k": lambda: I.llama8b_case(131072),
     "llama8b_batch16": lambda: I.batched_case(),
     "gqa70b_b4_t128k": lambda: I.seventy_b_case(),
+    "gqa405b_t128k": lambda: I.gqa405b_case(),
 }
 
 
