@@ -55,6 +55,10 @@ SHAPES = [
     (1, 6, 1, [150], "permuted"),               # g = 6 (second quad padded)
     (1, 12, 1, [200], "permuted"),              # g = 12 (padded quad)
     (1, 16, 1, [300], "permuted"),              # g = 16
+    (2, 10, 2, [400, 77], "interleaved"),       # g = 5: three padded heads of the octet layout
+    (1, 7, 1, [260], "permuted"),               # g = 7
+    (1, 9, 1, [500], "permuted"),               # g = 9: seven padded heads of the hexadeca layout
+    (2, 30, 2, [333, 1200], "interleaved"),     # g = 15
 ]
 
 

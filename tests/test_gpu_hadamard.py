@@ -48,6 +48,8 @@ SHAPES = [
     (2, 32, 8, [1000, 257]),      # g = 4
     (2, 64, 8, [513, 1024]),      # g = 8
     (1, 16, 1, [300]),            # g = 16
+    (2, 10, 2, [200, 90]),        # g = 5
+    (1, 12, 1, [300]),            # g = 12
     (3, 8, 2, [0, 5, 100]),
 ]
 
