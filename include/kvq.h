@@ -289,9 +289,11 @@ size_t kvq_decode_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t nu
  * subnormal operand).  Stale slots past a sequence's end and absent pages may
  * hold any bytes: they weigh nothing.
  * Work decomposition: one kernel launch; one workgroup per compute unit
- * (12 waves for g <= 4, 8 for g <= 8, else 4; for a batch of g <= 4 with
- * 2-bit codes and no window, three 4-wave workgroups per compute unit, which
- * cut the sequences into three times as many splits) streams a split's pages, and
+ * (with 2-bit codes 12 waves for g <= 8 and 8 for g <= 16; with a high-bit
+ * plane 12 or 8 waves for g <= 4, 8 for g <= 8, else 4; for a batch of g <= 4
+ * with 2-bit codes and no window, three 4-wave workgroups per compute unit,
+ * which cut the sequences into three times as many splits) streams a split's
+ * pages, and
  * the last workgroup of each (sequence, KV head) merges the split partials
  * (log-sum-exp), adds the window's part, and applies R_V^T.
  * Limits: max_seq_len <= 16777216 (512 splits x 2048 pages x 16 tokens).

@@ -249,8 +249,9 @@ __device__ __forceinline__ float ld_agent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// quads of query heads (g <= 4 * kNQ), waves per workgroup, ring depth, 3- or
-// 4-bit keys, 3- or 4-bit values, Hadamard rotation
+// kNQ: g <= 4 * kNQ (1: one quad of heads, 2: the octet layout, 4: the
+// hexadeca layout); waves per workgroup, ring depth, 3- or 4-bit keys, 3- or
+// 4-bit values, Hadamard rotation, workgroups per compute unit
 template <int kNQ, int kW, int kDepth, bool kKW, bool kVW, bool kHad, int kWgPerCu = 1>
 __global__ __launch_bounds__(64 * kW) __attribute__((amdgpu_waves_per_eu(kW / 4 * kWgPerCu)))
 void decode_kernel(const DecodeParams p) {
@@ -1932,7 +1933,7 @@ static hipError_t launch_narrow(const DecodeParams& prm, hipStream_t stream, hip
                             ev_end, 0);
 }
 
-// The decode kernels of kNQ quads of query heads (g <= 4 kNQ), for every key
+// The decode kernels for g <= 4 kNQ query heads per KV head, for every key
 // and value code width and rotation kind; 3- and 4-bit codes of a tensor share
 // one kernel (the plane's unused bit is 0).  Each kNQ is instantiated in a
 // translation unit of its own (kvq_decode.hip, kvq_decode_g8.hip,
